@@ -1,0 +1,230 @@
+"""Pins for oracle O5-O7 (packed block-causal attention, fp64); CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import packing as P
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(T, H, d, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, H, d)), rng.standard_normal((T, H, d)),
+            rng.standard_normal((T, H, d)))
+
+
+def _close(a, b, abs_tol=1e-10, rel=1e-9):
+    """The pages' equivalence tolerance: abs 1e-10 + rel 1e-9 * max|x|."""
+    scale = max(np.abs(a).max(initial=0.0), np.abs(b).max(initial=0.0))
+    return np.abs(a - b).max(initial=0.0) <= abs_tol + rel * scale
+
+
+# ----------------------------------------------------------- O5 vs O7
+
+def test_forward_equals_brute_force_dense_mask():
+    rng = np.random.default_rng(0)
+    for trial in range(20):
+        lengths = rng.integers(0, 7, size=int(rng.integers(1, 6))).tolist()
+        if sum(lengths) == 0:
+            lengths.append(1)
+        T, H, d = sum(lengths), 2, 8
+        q, k, v = _rand(T, H, d, trial)
+        md = P.packed_row_metadata(lengths)
+        o, _ = A.varlen_forward(q, k, v, md["cu"])
+        od = A.dense_masked_forward(q, k, v, md["seg"], md["pos"], np.ones(T, bool))
+        assert _close(o, od), lengths
+
+
+def test_three_representations_agree():
+    """separate per-segment calls == padded rows with validity == packed flat stream."""
+    lengths = [5, 3, 4]
+    T, H, d = 12, 2, 16
+    q, k, v = _rand(T, H, d, 1)
+    cu = P.packed_row_metadata(lengths)["cu"]
+    packed, _ = A.varlen_forward(q, k, v, cu)
+    sep = np.zeros_like(packed)
+    pad = np.zeros_like(packed)
+    W = max(lengths)
+    for b in range(3):
+        s, e = int(cu[b]), int(cu[b + 1])
+        for h in range(H):
+            sep[s:e, h], _ = A.segment_head_forward(q[s:e, h], k[s:e, h], v[s:e, h], 1 / math.sqrt(d))
+        # one right-padded row of width W, junk in the padding
+        qq = np.full((W, H, d), 7.0); kk = np.full((W, H, d), -3.0); vv = np.full((W, H, d), 1e3)
+        qq[:e - s], kk[:e - s], vv[:e - s] = q[s:e], k[s:e], v[s:e]
+        valid = np.arange(W) < (e - s)
+        o_row = A.dense_masked_forward(qq, kk, vv, np.where(valid, 0, -1), np.where(valid, np.arange(W), 0), valid)
+        assert np.all(o_row[~valid] == 0.0)          # inactive queries: zero mixture
+        pad[s:e] = o_row[:e - s]
+    assert _close(packed, sep)
+    assert _close(packed, pad)
+
+
+def test_merged_boundary_changes_only_the_merged_slice():
+    g = json.load(open(os.path.join(GOLD, "worked_5_3_4.json")))
+    q, k, v = _rand(12, 2, 64, 2)
+    o3, _ = A.varlen_forward(q, k, v, g["cu_seqlens"])
+    o2, _ = A.varlen_forward(q, k, v, g["merged_cu_seqlens"])
+    # A is untouched; B's queries come first in B+C, so causality hides C from them
+    assert _close(o3[:8], o2[:8])
+    # C's queries now see B's keys
+    assert np.abs(o3[8:] - o2[8:]).min() > 1e-6
+    # and the three slices are independent attentions
+    for s, e in [(0, 5), (5, 8), (8, 12)]:
+        o_alone, _ = A.varlen_forward(q[s:e], k[s:e], v[s:e], [0, e - s])
+        assert _close(o_alone, o3[s:e])
+
+
+def test_closed_forms():
+    d = 16
+    scale = 1 / math.sqrt(d)
+    q, k, v = _rand(1, 1, d, 3)
+    o, lse = A.varlen_forward(q, k, v, [0, 1])
+    assert np.allclose(o, v, rtol=0, atol=1e-15)                 # L = 1: O = v
+    assert math.isclose(lse[0, 0], scale * float(q[0, 0] @ k[0, 0]), rel_tol=1e-14)
+    # all keys equal: uniform softmax, O_i = prefix mean of v, LSE_i = s + ln(i+1)
+    L = 9
+    qq, _, vv = _rand(L, 1, d, 4)
+    kk = np.repeat(np.random.default_rng(5).standard_normal((1, 1, d)), L, axis=0)
+    o, lse = A.varlen_forward(qq, kk, vv, [0, L])
+    pref = np.cumsum(vv[:, 0], axis=0) / np.arange(1, L + 1)[:, None]
+    assert np.allclose(o[:, 0], pref, rtol=0, atol=1e-13)
+    s = scale * (qq[:, 0] @ kk[0, 0])
+    assert np.allclose(lse[0], s + np.log(np.arange(1, L + 1)), rtol=0, atol=1e-12)
+
+
+def test_matches_torch_sdpa_with_explicit_mask():
+    lengths = [37, 1, 0, 64, 15]
+    T, H, d = sum(lengths), 3, 32
+    q, k, v = _rand(T, H, d, 6)
+    md = P.packed_row_metadata(lengths)
+    o, _ = A.varlen_forward(q, k, v, md["cu"])
+    seg = torch.tensor(md["seg"]); pos = torch.tensor(md["pos"])
+    mask = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    assert np.abs(o - ref.permute(1, 0, 2).numpy()).max() < 1e-12
+
+
+def test_isolation_and_lse_bounds():
+    lengths = [6, 9]
+    q, k, v = _rand(15, 2, 8, 7)
+    o, lse = A.varlen_forward(q, k, v, [0, 6, 15])
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:6] += 5.0; k2[:6] *= -3.0; v2[:6] = 1e6         # perturb segment A only
+    o2, lse2 = A.varlen_forward(q2, k2, v2, [0, 6, 15])
+    assert np.array_equal(o[6:], o2[6:]) and np.array_equal(lse[:, 6:], lse2[:, 6:])
+    # LSE >= max permitted score, and <= max + ln(count)
+    for h in range(2):
+        for t in range(15):
+            s0 = 0 if t < 6 else 6
+            sc = (k[s0:t + 1, h] @ q[t, h]) / math.sqrt(8)
+            assert sc.max() - 1e-12 <= lse[h, t] <= sc.max() + math.log(t - s0 + 1) + 1e-12
+
+
+def test_forward_rows_equals_full_forward():
+    lengths = [13, 0, 40, 7]
+    T = sum(lengths)
+    q, k, v = _rand(T, 2, 16, 8)
+    cu = P.packed_row_metadata(lengths)["cu"]
+    o, lse = A.varlen_forward(q, k, v, cu)
+    rows = [0, 12, 13, 30, 52, 59]
+    heads = [0, 1, 1, 0, 1, 0]
+    orow, lrow = A.forward_rows(q, k, v, cu, rows, heads)
+    for n, (t, h) in enumerate(zip(rows, heads)):
+        assert np.allclose(orow[n], o[t, h], rtol=0, atol=1e-13)
+        assert math.isclose(lrow[n], lse[h, t], rel_tol=0, abs_tol=1e-12)
+
+
+# ----------------------------------------------------------- O6
+
+def _loss(q, k, v, do, cu):
+    o, _ = A.varlen_forward(q, k, v, cu)
+    return float((o * do).sum())
+
+
+def test_backward_finite_differences():
+    lengths = [3, 0, 5, 1]
+    T, H, d = sum(lengths), 2, 4
+    q, k, v = _rand(T, H, d, 9)
+    do = np.random.default_rng(10).standard_normal((T, H, d))
+    cu = P.packed_row_metadata(lengths)["cu"]
+    dq, dk, dv = A.varlen_backward(q, k, v, do, cu)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, cu)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, cu)
+            assert abs((lp - lm) / (2 * eps) - g[idx]) < 1e-7, (name, idx)
+
+
+def test_backward_closed_forms_and_isolation():
+    d = 8
+    q, k, v = _rand(1, 1, d, 11)
+    do = np.random.default_rng(12).standard_normal((1, 1, d))
+    dq, dk, dv = A.varlen_backward(q, k, v, do, [0, 1])
+    assert np.all(dq == 0) and np.all(dk == 0) and np.array_equal(dv, do)
+    # cross-segment derivatives are exactly zero: B's loss does not reach A
+    q, k, v = _rand(10, 2, d, 13)
+    do = np.zeros((10, 2, d)); do[4:] = 1.0
+    dq, dk, dv = A.varlen_backward(q, k, v, do, [0, 4, 10])
+    assert np.all(dq[:4] == 0) and np.all(dk[:4] == 0) and np.all(dv[:4] == 0)
+
+
+def test_backward_matches_torch_autograd():
+    lengths = [20, 1, 33, 0, 9]
+    T, H, d = sum(lengths), 2, 16
+    q, k, v = _rand(T, H, d, 14)
+    do = np.random.default_rng(15).standard_normal((T, H, d))
+    md = P.packed_row_metadata(lengths)
+    dq, dk, dv = A.varlen_backward(q, k, v, do, md["cu"])
+    seg = torch.tensor(md["seg"]); pos = torch.tensor(md["pos"])
+    mask = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous().requires_grad_() for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    out.backward(torch.from_numpy(do).permute(1, 0, 2))
+    for mine, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.abs(mine - ref.grad.permute(1, 0, 2).numpy()).max() < 1e-11
+
+
+# ----------------------------------------------------------- pin sensitivity
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """A plausible slip in O5 (strict causality, a dropped boundary, a wrong
+    scale) must fail the brute-force and library pins above."""
+    lengths = [5, 3, 4]
+    T, H, d = 12, 2, 8
+    q, k, v = _rand(T, H, d, 16)
+    md = P.packed_row_metadata(lengths)
+    ref = A.dense_masked_forward(q, k, v, md["seg"], md["pos"], np.ones(T, bool))
+
+    def strict(qs, ks, vs, scale):       # key j < i instead of j <= i
+        L = qs.shape[0]
+        out = np.zeros_like(qs)
+        for i in range(L):
+            if i == 0:
+                continue
+            sc = scale * (ks[:i] @ qs[i])
+            e = np.exp(sc - sc.max())
+            out[i] = (e / e.sum()) @ vs[:i]
+        return out, np.zeros(L)
+
+    monkeypatch.setattr(A, "segment_head_forward", strict)
+    o, _ = A.varlen_forward(q, k, v, md["cu"])
+    assert not _close(o, ref)
+    monkeypatch.undo()
+    o, _ = A.varlen_forward(q, k, v, [0, 12])          # boundary dropped
+    assert not _close(o, ref)
+    o, _ = A.varlen_forward(q, k, v, md["cu"], scale=1.0)  # scale forgotten
+    assert not _close(o, ref)
