@@ -1,0 +1,195 @@
+/*
+ * pvb.h -- packed, padding-free, block-causal varlen attention for MI355X (gfx950).
+ *
+ * A flat token axis of length T carries several independent sequences back to
+ * back.  cu_seqlens (int32, B+1 entries, cu[0] = 0, cu[B] = T) cuts it into
+ * slices [cu[b], cu[b+1]); attention is causal inside each slice only, so the
+ * whole computation is block-diagonal causal attention and no [T, T] mask is
+ * ever built ("Packing与 FlashAttention Varlen", section 1 and section 3).
+ *
+ * Conventions for every entry point
+ *   - Return value: pvb_status; PVB_OK (0) on success.
+ *   - Host planners run synchronously on the calling thread, validate every
+ *     argument before writing anything, and leave outputs untouched on error.
+ *   - Device entry points validate their scalar arguments on the host, enqueue
+ *     their kernels on `stream` and never synchronise.  Problems that only the
+ *     device can see (a bad device-resident cu_seqlens, lengths that overflow)
+ *     are reported through a caller-provided device status word (int32, written
+ *     by the call: 0 or a pvb_status code); the kernels then write no outputs.
+ *   - Every buffer is allocated and owned by the caller.  The library keeps no
+ *     allocations and no mutable global state; calls are reentrant.  Pointers
+ *     named d_* are device pointers, h_* host pointers.
+ *   - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous [T, H, d] (token-major,
+ *     then head, then feature): element (t, h, c) at offset (t*H + h)*d + c.
+ *     LSE and the backward's D are fp32 [H, T].
+ *   - Self-attention only: one cu_seqlens for queries and keys, H query heads =
+ *     H key/value heads, d in {64, 128}.  The softmax scale is an argument
+ *     (1/sqrt(d) is the usual value).
+ */
+#ifndef PVB_H
+#define PVB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pvb_status {
+  PVB_OK = 0,
+  PVB_E_INVALID_ARG = 1,    /* null pointer, negative size, bad enum, capacity <= 0 */
+  PVB_E_OVERSIZED = 2,      /* a sample longer than the capacity (never split)     */
+  PVB_E_OVERFLOW = 3,       /* a count or offset would not fit int32              */
+  PVB_E_BAD_CU_SEQLENS = 4, /* cu[0] != 0, decreasing, or cu[B] != T             */
+  PVB_E_WORKSPACE = 5,      /* workspace missing or smaller than required         */
+  PVB_E_UNSUPPORTED = 6,    /* head_dim other than 64/128, or a size beyond limits */
+  PVB_E_HIP = 7             /* a HIP runtime call failed (launch error)           */
+} pvb_status;
+
+typedef enum pvb_dtype { PVB_BF16 = 0, PVB_F32 = 1 } pvb_dtype;
+
+/* Precision of the probability operands (P, dS) fed to the matrix cores.
+ * PVB_PREC_BF16: one bf16 rounding.  PVB_PREC_SPLIT: each value is split as
+ * hi = bf16(x), lo = bf16(x - hi) and both parts are multiplied (two MFMAs),
+ * giving about 16 significant bits.  Scores, softmax and accumulation are fp32
+ * in both modes. */
+typedef enum pvb_precision { PVB_PREC_BF16 = 0, PVB_PREC_SPLIT = 1 } pvb_precision;
+
+/* ------------------------------------------------------------------ host planners */
+
+/* Order-preserving next-fit ("Pack sequences without joining their contexts",
+ * "Fill only the current row"; the sequential strategy of "Packing与
+ * FlashAttention Varlen", section 2).  Items are read in order; an item that
+ * does not fit in the room left in the current row starts a new row; rows are
+ * never revisited and items are never split.  A zero-length item is placed in
+ * the current row at its fill level.
+ *   lengths  [n]  item lengths, 0 <= lengths[i] <= capacity   (host)
+ *   row_of   [n]  out: row of item i                          (host)
+ *   start_of [n]  out: offset of item i inside its row        (host)
+ *   n_rows        out: number of rows (0 when n == 0)          (host)
+ * Errors: PVB_E_INVALID_ARG (null pointer with n > 0, n < 0, capacity <= 0,
+ * negative length), PVB_E_OVERSIZED (a length > capacity), PVB_E_OVERFLOW
+ * (n > 2^31, so ordinals would not fit int32). */
+pvb_status pvb_pack_plan_nextfit(const int32_t* lengths, int64_t n, int32_t capacity,
+                                 int32_t* row_of, int32_t* start_of, int64_t* n_rows);
+
+/* Best-fit-decreasing (the default packing strategy named in "Packing与
+ * FlashAttention Varlen", section 2).  Items are taken by decreasing length,
+ * ties by lower index; each goes to the open bin with the least room left that
+ * still fits it (room >= length), ties to the lowest bin number, else to a new
+ * bin.  Bins are numbered in creation order and keep insertion order.
+ *   lengths     [n]    item lengths, 0 <= lengths[i] <= capacity   (host)
+ *   bin_of      [n]    out: bin of item i                          (host)
+ *   start_of    [n]    out: offset of item i inside its bin        (host)
+ *   n_bins             out: number of bins                          (host)
+ *   order       [n]    out: item ids bin by bin, insertion order    (host)
+ *   bin_offsets [n+1]  out: bin j's items are order[bin_offsets[j] .. bin_offsets[j+1]);
+ *                      entries past n_bins are left untouched       (host)
+ * Errors as pvb_pack_plan_nextfit. */
+pvb_status pvb_pack_plan_bfd(const int32_t* lengths, int64_t n, int32_t capacity,
+                             int32_t* bin_of, int32_t* start_of, int64_t* n_bins,
+                             int32_t* order, int64_t* bin_offsets);
+
+/* ------------------------------------------------------------ device packed row */
+
+/* Packed-row metadata by a device prefix scan ("Packing与 FlashAttention
+ * Varlen", sections 1-3: cu_seqlens = running sum of lengths, local
+ * position_ids restart at 0 in every sample; "Pack sequences without joining
+ * their contexts", "Fill only the current row": occurrence segment ids,
+ * padding cells with segment -1 and position 0).
+ *   d_lengths   [n_seg]     segment lengths (>= 0)                        (device)
+ *   n_seg                   number of segments, >= 0
+ *   capacity                cells in the row C (>= sum of lengths; = T for a flat pack)
+ *   segment_base            id of segment 0 (occurrence ordinal offset)
+ *   d_cu        [n_seg+1]   out: cu[0] = 0, cu[b+1] = cu[b] + L_b           (device)
+ *   d_pos       [capacity]  out: t - cu[s(t)] for real cells, 0 for padding (device)
+ *   d_seg       [capacity]  out: segment_base + s(t), -1 for padding        (device)
+ *                           where s(t) = max{ b : cu[b] <= t } (a zero-length
+ *                           segment owns no cell but consumes an id)
+ *   d_max_seqlen [1]        out, nullable: max length                       (device)
+ *   Optional token gather (all four null, or d_tokens/d_tok_off and at least
+ *   one output non-null): segment b is a document whose L_b + 1 tokens start at
+ *   d_tokens[d_tok_off[b]]; cell cu[b] + j gets input tok[j] and target
+ *   tok[j+1] (next-token pairs never cross documents: "Form pairs inside each
+ *   source range"); padding cells get -1 and valid 0.
+ *   d_tokens    [*]         int32 token ids                                 (device)
+ *   d_tok_off   [n_seg]     int64 first-token offsets                       (device)
+ *   d_inputs, d_targets [capacity]  out, nullable                          (device)
+ *   d_valid     [capacity]  out, nullable: 1 real / 0 padding (uint8)       (device)
+ *   d_status    [1]         out: device status word (required)              (device)
+ * Device-detected errors (status word): PVB_E_INVALID_ARG (negative length),
+ * PVB_E_OVERFLOW (cu would exceed int32), PVB_E_OVERSIZED (sum > capacity);
+ * then only d_cu may have been written. */
+pvb_status pvb_build_packed_row(const int32_t* d_lengths, int32_t n_seg, int32_t capacity,
+                                int32_t segment_base, int32_t* d_cu, int32_t* d_pos,
+                                int32_t* d_seg, int32_t* d_max_seqlen,
+                                const int32_t* d_tokens, const int64_t* d_tok_off,
+                                int32_t* d_inputs, int32_t* d_targets, uint8_t* d_valid,
+                                int32_t* d_status, void* stream);
+
+/* ---------------------------------------------------------------- attention */
+
+/* Bytes of device workspace pvb_varlen_attn_fwd (bwd = 0) or
+ * pvb_varlen_attn_bwd (bwd = 1) needs for these sizes.  Returns 0 for
+ * invalid sizes. */
+size_t pvb_varlen_attn_workspace_bytes(int32_t T, int32_t H, int32_t d, int32_t n_seg,
+                                       int32_t bwd, int32_t grad_dtype);
+
+/* Forward block-causal attention over the packed stream.  For every segment b
+ * and head h, query i (cu[b] <= i < cu[b+1]) attends to keys j with
+ * cu[b] <= j <= i:  O_i = sum_j softmax_j(scale * q_i.k_j) v_j and
+ * LSE_i = ln sum_j exp(scale * q_i.k_j) ("Packing与 FlashAttention Varlen",
+ * section 1: independent attentions written back in flat order; section 5:
+ * per-slice base and extent, causal inside the slice, O at Q's offsets).
+ * Zero-length segments are allowed (repeated cu values) and do no work.
+ *   d_q, d_k, d_v  bf16 [T, H, d]                                  (device)
+ *   d_cu           int32 [n_seg+1]                                 (device)
+ *   h_cu           int32 [n_seg+1] host mirror, nullable: when given it is
+ *                  validated on the host and a bad one returns
+ *                  PVB_E_BAD_CU_SEQLENS before anything is enqueued  (host)
+ *   d_o            out [T, H, d], bf16 or fp32 per o_dtype          (device)
+ *   d_lse          out fp32 [H, T] natural-log LSE                   (device)
+ *   workspace      >= pvb_varlen_attn_workspace_bytes(..., 0, ...) bytes  (device)
+ *   d_status       out: device status word (required)               (device)
+ * Device-detected error: PVB_E_BAD_CU_SEQLENS in the status word; then O and
+ * LSE are not written. */
+pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, const void* d_v,
+                               const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                               int32_t T, int32_t H, int32_t d, float softmax_scale,
+                               void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
+                               void* workspace, size_t workspace_bytes, int32_t* d_status,
+                               void* stream);
+
+/* Backward of pvb_varlen_attn_fwd for the loss sum(O * dO): the textbook
+ * softmax-attention gradient restricted to the same slices (the same ranges
+ * drive forward and backward: "Pack sequences without joining their
+ * contexts", "Extend the existing storage and decoder").
+ *   D_i = sum_c dO_ic O_ic;  P_ij = exp(scale q_i.k_j - LSE_i);
+ *   dV_j = sum_i P_ij dO_i;  dS_ij = P_ij (dO_i.v_j - D_i);
+ *   dQ_i = scale sum_j dS_ij k_j;  dK_j = scale sum_i dS_ij q_i.
+ *   d_q, d_k, d_v, d_do  bf16 [T, H, d]                            (device)
+ *   d_o                  forward output, bf16 or fp32 per o_dtype   (device)
+ *   d_lse                fp32 [H, T] from the forward               (device)
+ *   d_dq, d_dk, d_dv     out [T, H, d], bf16 or fp32 per grad_dtype (device)
+ *   other arguments as in pvb_varlen_attn_fwd.
+ * Cross-segment derivatives are exactly zero. */
+pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v,
+                               const void* d_o, int32_t o_dtype, const void* d_do,
+                               const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                               int32_t n_seg, int32_t T, int32_t H, int32_t d,
+                               float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                               int32_t grad_dtype, int32_t precision, void* workspace,
+                               size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* pvb_status_string(int32_t status);
+
+/* Library version string (static). */
+const char* pvb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PVB_H */

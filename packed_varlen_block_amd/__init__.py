@@ -1,0 +1,282 @@
+"""Python binding of libpvb (packed block-causal varlen attention, gfx950).
+
+Argument marshalling only: every step runs in the C-ABI library's host code or
+HIP kernels.  torch supplies device memory (outputs, workspace) and the
+current HIP stream.  There is no fallback: if libpvb.so is missing or a call
+fails, an exception is raised.
+
+Functions (same names as the C entry points without the ``pvb_`` prefix):
+  pack_plan_nextfit, pack_plan_bfd       host planners (numpy in / numpy out)
+  build_packed_row                       device prefix scan -> cu, pos, seg, ...
+  varlen_attn_fwd, varlen_attn_bwd       bf16 MFMA attention kernels
+  workspace_bytes, status_string, check_status
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpvb.so")
+
+PVB_OK = 0
+PVB_BF16, PVB_F32 = 0, 1
+PVB_PREC_BF16, PVB_PREC_SPLIT = 0, 1
+STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "PVB_E_OVERFLOW",
+                4: "PVB_E_BAD_CU_SEQLENS", 5: "PVB_E_WORKSPACE", 6: "PVB_E_UNSUPPORTED", 7: "PVB_E_HIP"}
+
+# every symbol include/pvb.h declares
+EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
+           "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
+           "pvb_status_string", "pvb_version")
+
+
+class PvbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {STATUS_NAMES.get(self.status, self.status)} "
+                         f"({status_string(self.status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpvb.so (built in-tree by packed_varlen_block_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m packed_varlen_block_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        L.pvb_pack_plan_nextfit.argtypes = [P, I64, I32, P, P, P]
+        L.pvb_pack_plan_bfd.argtypes = [P, I64, I32, P, P, P, P, P]
+        L.pvb_build_packed_row.argtypes = [P, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P]
+        L.pvb_varlen_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+        L.pvb_varlen_attn_workspace_bytes.restype = SZ
+        L.pvb_varlen_attn_fwd.argtypes = [P, P, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P, P]
+        L.pvb_varlen_attn_bwd.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, F,
+                                          P, P, P, I32, I32, P, SZ, P, P]
+        for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
+                     "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd"):
+            getattr(L, name).restype = ctypes.c_int
+        L.pvb_status_string.argtypes = [I32]
+        L.pvb_status_string.restype = ctypes.c_char_p
+        L.pvb_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pvb_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().pvb_version().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != PVB_OK:
+        raise PvbError(rc, where)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+# ---------------------------------------------------------------- host planners
+
+def _lengths_array(lengths) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64))
+    if a.size and (a.min() < -2**31 or a.max() > 2**31 - 1):
+        raise PvbError(3, "lengths")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def pack_plan_nextfit(lengths, capacity: int):
+    """Order-preserving next-fit.  Returns (row_of, start_of, n_rows)."""
+    a = _lengths_array(lengths)
+    n = a.size
+    row_of = np.zeros(max(n, 1), np.int32)
+    start_of = np.zeros(max(n, 1), np.int32)
+    n_rows = ctypes.c_int64(0)
+    _check(lib().pvb_pack_plan_nextfit(_ptr(a), n, int(capacity), _ptr(row_of), _ptr(start_of),
+                                       ctypes.addressof(n_rows)), "pack_plan_nextfit")
+    return row_of[:n], start_of[:n], int(n_rows.value)
+
+
+def pack_plan_bfd(lengths, capacity: int):
+    """Best-fit-decreasing.  Returns (bin_of, start_of, n_bins, order, bin_offsets)."""
+    a = _lengths_array(lengths)
+    n = a.size
+    bin_of = np.zeros(max(n, 1), np.int32)
+    start_of = np.zeros(max(n, 1), np.int32)
+    order = np.zeros(max(n, 1), np.int32)
+    offs = np.zeros(n + 1, np.int64)
+    n_bins = ctypes.c_int64(0)
+    _check(lib().pvb_pack_plan_bfd(_ptr(a), n, int(capacity), _ptr(bin_of), _ptr(start_of),
+                                   ctypes.addressof(n_bins), _ptr(order), _ptr(offs)), "pack_plan_bfd")
+    nb = int(n_bins.value)
+    return bin_of[:n], start_of[:n], nb, order[:n], offs[:nb + 1]
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def check_status(status) -> None:
+    """Synchronise on a device status word and raise if it holds an error."""
+    st = int(status.item())
+    if st != PVB_OK:
+        raise PvbError(st, "device status")
+
+
+def build_packed_row(lengths, capacity: int | None = None, segment_base: int = 0,
+                     tokens=None, tok_off=None, status=None):
+    """Device packed-row metadata.  ``lengths`` is an int32 CUDA tensor [B].
+
+    Returns a dict of CUDA tensors: cu [B+1], pos [C], seg [C], max_seqlen [1],
+    status [1]; with ``tokens``/``tok_off`` also inputs, targets [C] and valid [C].
+    Enqueued on the current stream; call check_status(out["status"]) to
+    synchronise and raise on a device-detected error.
+    """
+    torch = _torch()
+    dev = lengths.device
+    if lengths.dtype != torch.int32 or not lengths.is_contiguous():
+        raise PvbError(1, "build_packed_row: lengths must be contiguous int32")
+    B = lengths.numel()
+    if capacity is None:
+        capacity = int(lengths.sum().item())
+    C = int(capacity)
+    out = {"cu": torch.empty(B + 1, dtype=torch.int32, device=dev),
+           "pos": torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C],
+           "seg": torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C],
+           "max_seqlen": torch.zeros(1, dtype=torch.int32, device=dev),
+           "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+    gather = tokens is not None
+    if gather:
+        out["inputs"] = torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C]
+        out["targets"] = torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C]
+        out["valid"] = torch.empty(max(C, 1), dtype=torch.uint8, device=dev)[:C]
+    rc = lib().pvb_build_packed_row(
+        _ptr(lengths), B, C, int(segment_base), _ptr(out["cu"]), _ptr(out["pos"]), _ptr(out["seg"]),
+        _ptr(out["max_seqlen"]), _ptr(tokens) if gather else None, _ptr(tok_off) if gather else None,
+        _ptr(out["inputs"]) if gather else None, _ptr(out["targets"]) if gather else None,
+        _ptr(out["valid"]) if gather else None, _ptr(out["status"]), _stream(dev))
+    _check(rc, "build_packed_row")
+    return out
+
+
+def workspace_bytes(T: int, H: int, d: int, n_seg: int, backward: bool, grad_dtype=PVB_F32) -> int:
+    return int(lib().pvb_varlen_attn_workspace_bytes(T, H, d, n_seg, int(bool(backward)), int(grad_dtype)))
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return PVB_BF16
+    if dt == torch.float32:
+        return PVB_F32
+    raise PvbError(1, f"unsupported dtype {dt}")
+
+
+def _prec_code(p):
+    return {"bf16": PVB_PREC_BF16, "split": PVB_PREC_SPLIT, PVB_PREC_BF16: PVB_PREC_BF16,
+            PVB_PREC_SPLIT: PVB_PREC_SPLIT}[p]
+
+
+def _check_qkv(*ts):
+    torch = _torch()
+    T, H, d = ts[0].shape
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (T, H, d) or not t.is_cuda:
+            raise PvbError(1, "q/k/v/dO must be contiguous bf16 CUDA tensors of one shape [T, H, d]")
+    return T, H, d
+
+
+def varlen_attn_fwd(q, k, v, cu, h_cu=None, softmax_scale=None, o_dtype=None, precision="bf16",
+                    out=None, lse=None, workspace=None, status=None):
+    """Forward packed block-causal attention.  Returns (O [T,H,d], LSE [H,T] fp32, status).
+
+    q, k, v: contiguous bf16 CUDA [T, H, d]; cu: int32 CUDA [B+1]; h_cu: optional
+    host (numpy/list) mirror of cu, validated on the host.
+    """
+    torch = _torch()
+    T, H, d = _check_qkv(q, k, v)
+    if cu.dtype != torch.int32 or not cu.is_cuda:
+        raise PvbError(1, "cu must be an int32 CUDA tensor")
+    n_seg = cu.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o_dtype = torch.bfloat16 if o_dtype is None else o_dtype
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, d), dtype=o_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    nbytes = workspace_bytes(T, H, d, n_seg, False)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    hc = None
+    if h_cu is not None:
+        hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
+        if hc.size != n_seg + 1:
+            raise PvbError(1, "h_cu must have B+1 entries")
+    rc = lib().pvb_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(hc), n_seg, T, H, d, scale,
+                                   _ptr(out), _dtype_code(out.dtype), _ptr(lse), _prec_code(precision),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _ptr(status), _stream(dev))
+    _check(rc, "varlen_attn_fwd")
+    return out, lse, status
+
+
+def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad_dtype=None,
+                    precision="bf16", dq=None, dk=None, dv=None, workspace=None, status=None):
+    """Backward.  Returns (dQ, dK, dV, status); grads are [T, H, d] in grad_dtype."""
+    torch = _torch()
+    T, H, d = _check_qkv(q, k, v, do)
+    if tuple(o.shape) != (T, H, d) or not o.is_contiguous():
+        raise PvbError(1, "o must be contiguous [T, H, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T) or not lse.is_contiguous():
+        raise PvbError(1, "lse must be contiguous fp32 [H, T]")
+    n_seg = cu.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
+    gcode = _dtype_code(grad_dtype)
+    dev = q.device
+    dq = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dq is None else dq
+    dk = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dk is None else dk
+    dv = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dv is None else dv
+    nbytes = workspace_bytes(T, H, d, n_seg, True, gcode)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    hc = None
+    if h_cu is not None:
+        hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
+        if hc.size != n_seg + 1:
+            raise PvbError(1, "h_cu must have B+1 entries")
+    rc = lib().pvb_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o.dtype), _ptr(do),
+                                   _ptr(lse), _ptr(cu), _ptr(hc), n_seg, T, H, d, scale,
+                                   _ptr(dq), _ptr(dk), _ptr(dv), gcode, _prec_code(precision),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _ptr(status), _stream(dev))
+    _check(rc, "varlen_attn_bwd")
+    return dq, dk, dv, status

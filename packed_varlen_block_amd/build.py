@@ -1,0 +1,69 @@
+"""Build libpvb.so (the C-ABI library) in-tree with hipcc for gfx950.
+
+Usage: python -m packed_varlen_block_amd.build [--verbose] [--resource-usage]
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(HERE, "libpvb.so")
+
+SOURCES = ["abi.cpp", "pack_plan.cpp", "packed_row.hip", "attn_common.hip", "attn_fwd.hip", "attn_bwd.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed-fp32 VALU instructions are disabled for every HIP translation unit.
+DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in line and line.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}")
+    return out
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmd = [HIPCC, "-c", path, "-o", obj] + COMMON_FLAGS
+        if src.endswith(".hip"):
+            cmd = [HIPCC, "-x", "hip", "-c", path, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS
+            if resource_usage:
+                cmd += ["-Rpass-analysis=kernel-resource-usage"]
+        out = _run(cmd, verbose)
+        if out and (verbose or resource_usage):
+            print(out)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp"
+    _run([HIPCC, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH], verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--resource-usage", action="store_true")
+    a = ap.parse_args(argv)
+    print(build(a.verbose, a.resource_usage))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

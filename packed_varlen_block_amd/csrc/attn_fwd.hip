@@ -1,0 +1,270 @@
+// Forward block-causal varlen attention on gfx950 matrix cores.
+//
+// What is computed ("Packing与 FlashAttention Varlen", sections 1 and 5;
+// "Pack sequences without joining their contexts", "Permission depends on the
+// example"): for every segment [cu[b], cu[b+1]) and head h, query i attends to
+// keys j of the same segment with j <= i; O and LSE are written at the
+// query's own flat rows.
+//
+// One workgroup = one work item (segment b, query tile m of 128 rows, head h)
+// taken from the planner's heaviest-first list.  Its 4 waves own 32 query rows
+// each.  Per 64-key tile:
+//   * K and V rows of the segment are staged through LDS with 16-byte
+//     coalesced loads (rows past the segment end are zero-filled, never read),
+//   * S^T = K Q^T on 32x32x16 bf16 MFMAs with Q held in registers, so that
+//     each lane owns one query column and the row max/sum of the online
+//     softmax is in-lane plus one half-wave exchange,
+//   * O^T += V^T P^T, where V^T fragments come straight from the row-major V
+//     tile through the LDS transpose read and P never leaves registers.
+// Key tiles wholly above the diagonal are never visited; masking is applied
+// only on tiles that cross the diagonal or the segment end.
+#include "pvb_device.hpp"
+
+namespace pvb {
+namespace {
+
+constexpr int kFwdBM = 128;   // query rows per work item
+constexpr int kFwdBN = 64;    // keys per K/V tile
+constexpr int kFwdThreads = 256;
+
+template <int D, bool SPLIT, typename OutT>
+__global__ void __launch_bounds__(kFwdThreads, 2)
+attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                const bf16* __restrict__ v, const int32_t* __restrict__ cu,
+                const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int H, int T,
+                float scale_log2, OutT* __restrict__ o, float* __restrict__ lse) {
+  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int KP = D + 8;         // K tile pitch (elements): 16-byte reads hit distinct banks
+  constexpr int VP = D + 16;        // V tile pitch (elements)
+  constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
+  constexpr int DBLK = D / 32;      // 32-wide feature blocks of O^T
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int CPT = BN * CPR / kFwdThreads;  // chunks per thread per tile
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 sV[BN * VP];
+
+  const int tau = blockIdx.x / H;
+  const int h = blockIdx.x - tau * H;
+  if (tau >= *n_tiles) return;
+  const int2 tm = tiles[tau];
+  const int seg0 = cu[tm.x];
+  const int L = cu[tm.x + 1] - seg0;
+  const int q0 = tm.y * BM;
+  const int64_t rs = (int64_t)H * D;  // row stride (elements)
+  const int64_t base = ((int64_t)seg0 * H + h) * D;
+  const bf16* qb = q + base;
+  const bf16* kb = k + base;
+  const bf16* vb = v + base;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int qrow = q0 + 32 * w + lq;     // this lane's query (local index)
+  const int wq_first = q0 + 32 * w;
+  const int wq_last = min(wq_first + 31, L - 1);
+  const bool wave_active = wq_first < L;
+
+  bf16x8 qf[KSTEPS];
+  if (qrow < L) {
+    const bf16* p = qb + qrow * rs + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8*)(p + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = bf16x8{};
+  }
+
+  f32x16 oacc[DBLK];
+#pragma unroll
+  for (int j = 0; j < DBLK; ++j) oacc[j] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int q_last = min(q0 + BM, L) - 1;
+  const int nkv = q_last / BN + 1;
+
+  uint4 kr[CPT], vr[CPT];
+  auto load_tile = [&](int n) {
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + kFwdThreads * r;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      const int key = n * BN + row;
+      if (key < L) {
+        kr[r] = *(const uint4*)(kb + key * rs + col);
+        vr[r] = *(const uint4*)(vb + key * rs + col);
+      } else {
+        kr[r] = zero4();
+        vr[r] = zero4();
+      }
+    }
+  };
+
+  load_tile(0);
+  for (int n = 0; n < nkv; ++n) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + kFwdThreads * r;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      *(uint4*)(sK + row * KP + col) = kr[r];
+      *(uint4*)(sV + row * VP + col) = vr[r];
+    }
+    __syncthreads();
+    if (n + 1 < nkv) load_tile(n + 1);
+
+    const int key0 = n * BN;
+    if (!wave_active || key0 > wq_last) continue;  // every key of this tile is in this wave's future
+
+    // S^T = K Q^T: two 32-key blocks
+    f32x16 st[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8 kf = *(const bf16x8*)(sK + (kb2 * 32 + lq) * KP + 16 * s + 8 * g);
+        st[kb2] = mfma32(kf, qf[s], st[kb2]);
+      }
+    }
+    // mask: key > query, or key past the segment end
+    if (key0 + BN - 1 > wq_first || key0 + BN > L) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key > qrow || key >= L) st[kb2][i] = -INFINITY;
+        }
+    }
+    // online softmax for this lane's query column
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb2][i]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float rsum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(st[kb2][i] * scale_log2 - m_use);
+        st[kb2][i] = p;
+        rsum += p;
+      }
+    rsum += swap_halves(rsum);
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < DBLK; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
+
+    // O^T += V^T P^T over four 16-key k-steps.  k-slot 8g+e of this lane holds
+    // key 16kk + 8(e/4) + 4g + e%4, which is where S^T's C layout put it.
+#pragma unroll
+    for (int kk = 0; kk < BN / 16; ++kk) {
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = st[kk >> 1][8 * (kk & 1) + e];
+        ph[e] = (bf16)p;
+        if constexpr (SPLIT) pl[e] = (bf16)(p - (float)ph[e]);
+      }
+      const bf16* vrow = sV + (16 * kk + 4 * g + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) +
+                         4 * (lane & 3);
+#pragma unroll
+      for (int j = 0; j < DBLK; ++j) {
+        const bf16x8 vf = cat(lds_read_tr(vrow + 32 * j), lds_read_tr(vrow + 8 * VP + 32 * j));
+        oacc[j] = mfma32(vf, ph, oacc[j]);
+        if constexpr (SPLIT) oacc[j] = mfma32(vf, pl, oacc[j]);
+      }
+    }
+  }
+
+  if (!wave_active || qrow >= L) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  OutT* op = o + ((int64_t)(seg0 + qrow) * H + h) * D;
+#pragma unroll
+  for (int j = 0; j < DBLK; ++j)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int col = 32 * j + 8 * i4 + 4 * g;
+      if constexpr (sizeof(OutT) == 4) {
+        *(float4*)(op + col) = make_float4(oacc[j][4 * i4] * inv, oacc[j][4 * i4 + 1] * inv,
+                                           oacc[j][4 * i4 + 2] * inv, oacc[j][4 * i4 + 3] * inv);
+      } else {
+        bf16x4 r;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) r[t] = (bf16)(oacc[j][4 * i4 + t] * inv);
+        *(bf16x4*)(op + col) = r;
+      }
+    }
+  if (g == 0) lse[(int64_t)h * T + seg0 + qrow] = (m_run + log2f(l_run)) * kLn2;
+}
+
+template <int D, bool SPLIT, typename OutT>
+hipError_t launch_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
+                      const int2* tiles, const int32_t* count, int H, int T, size_t cap,
+                      float scale_log2, void* o, float* lse, hipStream_t s) {
+  const size_t grid = cap * (size_t)H;
+  if (grid == 0) return hipSuccess;
+  attn_fwd_kernel<D, SPLIT, OutT><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, tiles, count, H, T, scale_log2,
+      (OutT*)o, lse);
+  return hipGetLastError();
+}
+
+size_t fwd_workspace(int32_t T, int32_t n_seg) {
+  return 256 + plan_capacity(T, n_seg, kFwdBM) * sizeof(int2);
+}
+
+}  // namespace
+
+size_t attn_fwd_workspace_bytes(int32_t T, int32_t n_seg) { return fwd_workspace(T, n_seg); }
+
+}  // namespace pvb
+
+extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, const void* d_v,
+                                          const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                          int32_t T, int32_t H, int32_t d, float softmax_scale,
+                                          void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
+                                          void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                          void* stream) {
+  using namespace pvb;
+  if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
+  if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_o == nullptr || d_lse == nullptr))
+    return PVB_E_INVALID_ARG;
+  if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
+  if (precision != PVB_PREC_BF16 && precision != PVB_PREC_SPLIT) return PVB_E_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY)) return PVB_E_INVALID_ARG;
+  if (d != 64 && d != 128) return PVB_E_UNSUPPORTED;
+  if ((int64_t)T * H * d > (int64_t)1 << 40) return PVB_E_UNSUPPORTED;
+  const size_t cap = plan_capacity(T, n_seg, kFwdBM);
+  if (cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < fwd_workspace(T, n_seg)) return PVB_E_WORKSPACE;
+  const pvb_status hs = check_host_cu(h_cu, n_seg, T);
+  if (hs != PVB_OK) return hs;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* count = static_cast<int32_t*>(workspace);
+  int2* tiles = reinterpret_cast<int2*>(static_cast<char*>(workspace) + 256);
+  plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kFwdBM, 0, tiles, count, d_status);
+  if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+
+  const float sl2 = softmax_scale * kLog2e;
+  const bool split = precision == PVB_PREC_SPLIT, f32 = o_dtype == PVB_F32;
+  hipError_t e;
+#define PVB_FWD(D_, S_, T_) \
+  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, tiles, count, H, T, cap, sl2, d_o, d_lse, s)
+  if (d == 128) {
+    if (split) { if (f32) PVB_FWD(128, true, float); else PVB_FWD(128, true, bf16); }
+    else { if (f32) PVB_FWD(128, false, float); else PVB_FWD(128, false, bf16); }
+  } else {
+    if (split) { if (f32) PVB_FWD(64, true, float); else PVB_FWD(64, true, bf16); }
+    else { if (f32) PVB_FWD(64, false, float); else PVB_FWD(64, false, bf16); }
+  }
+#undef PVB_FWD
+  return e == hipSuccess ? PVB_OK : PVB_E_HIP;
+}

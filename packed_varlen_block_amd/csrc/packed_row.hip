@@ -1,0 +1,142 @@
+// Packed-row metadata on the device: cu_seqlens by a prefix scan of the
+// segment lengths, then per-cell local positions and occurrence segment ids
+// ("Packing与 FlashAttention Varlen", sections 1-3; "Pack sequences without
+// joining their contexts", "Fill only the current row"), with an optional
+// next-token gather that keeps every pair inside its own document ("Form pairs
+// inside each source range").
+#include "pvb_device.hpp"
+
+namespace pvb {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kFillThreads = 256;
+
+// One workgroup scans all lengths in chunks of kScanThreads, carrying the sum.
+__global__ void __launch_bounds__(kScanThreads)
+scan_lengths_kernel(const int32_t* __restrict__ lengths, int n, int capacity,
+                    int32_t* __restrict__ cu, int32_t* __restrict__ max_seqlen,
+                    int32_t* __restrict__ status) {
+  __shared__ int64_t s_wsum[kScanThreads / 64];
+  __shared__ int s_flags, s_max;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) {
+    s_flags = 0;
+    s_max = 0;
+  }
+  __syncthreads();
+  int64_t carry = 0;
+  int flags = 0, mx = 0;
+  for (int i0 = 0; i0 < n; i0 += kScanThreads) {
+    const int i = i0 + tid;
+    int64_t x = 0;
+    if (i < n) {
+      const int L = lengths[i];
+      if (L < 0) flags |= 1;
+      else {
+        x = L;
+        mx = max(mx, L);
+      }
+    }
+    // inclusive scan: within the wave, then across waves
+    int64_t y = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int64_t t = __shfl_up(y, off, 64);
+      if (lane >= off) y += t;
+    }
+    if (lane == 63) s_wsum[w] = y;
+    __syncthreads();
+    int64_t before = 0, total = 0;
+    for (int k = 0; k < kScanThreads / 64; ++k) {
+      if (k < w) before += s_wsum[k];
+      total += s_wsum[k];
+    }
+    const int64_t incl = carry + before + y;
+    if (i < n) {
+      if (incl > INT32_MAX) flags |= 2;
+      else cu[i + 1] = (int32_t)incl;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (flags) atomicOr(&s_flags, flags);
+  atomicMax(&s_max, mx);
+  __syncthreads();
+  if (tid == 0) {
+    cu[0] = 0;
+    int st = PVB_OK;
+    if (s_flags & 1) st = PVB_E_INVALID_ARG;
+    else if (s_flags & 2) st = PVB_E_OVERFLOW;
+    else if (carry > capacity) st = PVB_E_OVERSIZED;
+    *status = st;
+    if (max_seqlen != nullptr && st == PVB_OK) *max_seqlen = s_max;
+  }
+}
+
+// One thread per cell: s(t) = max{b : cu[b] <= t} by binary search.
+__global__ void __launch_bounds__(kFillThreads)
+fill_row_kernel(const int32_t* __restrict__ cu, int n, int capacity, int base,
+                int32_t* __restrict__ pos, int32_t* __restrict__ seg,
+                const int32_t* __restrict__ tokens, const int64_t* __restrict__ tok_off,
+                int32_t* __restrict__ inputs, int32_t* __restrict__ targets,
+                uint8_t* __restrict__ valid, const int32_t* __restrict__ status) {
+  const int t = blockIdx.x * kFillThreads + threadIdx.x;
+  if (t >= capacity || *status != PVB_OK) return;
+  const int total = cu[n];
+  if (t < total) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int j = t - cu[lo];
+    pos[t] = j;
+    seg[t] = base + lo;
+    if (tokens != nullptr) {
+      const int64_t off = tok_off[lo] + j;
+      if (inputs != nullptr) inputs[t] = tokens[off];
+      if (targets != nullptr) targets[t] = tokens[off + 1];
+    }
+    if (valid != nullptr) valid[t] = 1;
+  } else {
+    pos[t] = 0;
+    seg[t] = -1;
+    if (inputs != nullptr) inputs[t] = -1;
+    if (targets != nullptr) targets[t] = -1;
+    if (valid != nullptr) valid[t] = 0;
+  }
+}
+
+}  // namespace
+}  // namespace pvb
+
+extern "C" pvb_status pvb_build_packed_row(const int32_t* d_lengths, int32_t n_seg, int32_t capacity,
+                                           int32_t segment_base, int32_t* d_cu, int32_t* d_pos,
+                                           int32_t* d_seg, int32_t* d_max_seqlen,
+                                           const int32_t* d_tokens, const int64_t* d_tok_off,
+                                           int32_t* d_inputs, int32_t* d_targets, uint8_t* d_valid,
+                                           int32_t* d_status, void* stream) {
+  using namespace pvb;
+  if (n_seg < 0 || capacity < 0 || segment_base < 0 || d_cu == nullptr || d_status == nullptr)
+    return PVB_E_INVALID_ARG;
+  if (n_seg > 0 && d_lengths == nullptr) return PVB_E_INVALID_ARG;
+  if (capacity > 0 && (d_pos == nullptr || d_seg == nullptr)) return PVB_E_INVALID_ARG;
+  if ((int64_t)segment_base + n_seg > (int64_t)INT32_MAX + 1) return PVB_E_OVERFLOW;
+  const bool want_tokens = d_inputs != nullptr || d_targets != nullptr;
+  if (want_tokens && (d_tokens == nullptr || d_tok_off == nullptr)) return PVB_E_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  scan_lengths_kernel<<<1, kScanThreads, 0, s>>>(d_lengths, n_seg, capacity, d_cu, d_max_seqlen,
+                                                 d_status);
+  if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  if (capacity > 0) {
+    const int blocks = (capacity + kFillThreads - 1) / kFillThreads;
+    fill_row_kernel<<<blocks, kFillThreads, 0, s>>>(d_cu, n_seg, capacity, segment_base, d_pos,
+                                                    d_seg, want_tokens ? d_tokens : nullptr,
+                                                    d_tok_off, d_inputs, d_targets, d_valid,
+                                                    d_status);
+    if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  }
+  return PVB_OK;
+}

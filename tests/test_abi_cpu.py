@@ -1,0 +1,164 @@
+"""C-ABI library on the CPU: symbols, host planners vs the oracle, host-side errors.
+
+No GPU is touched: the device entry points are only called with arguments
+that their host-side validation rejects before any HIP call.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import packed_varlen_block_amd as pvb
+from oracle import packing as P
+from workloads import raw_lengths_cfg3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+
+def _header_symbols():
+    text = open(os.path.join(ROOT, "include", "pvb.h")).read()
+    return sorted(set(re.findall(r"\b(pvb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pvb.lib()
+    syms = _header_symbols()
+    assert len(syms) >= 8
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(pvb.EXPORTS) == syms
+    assert "gfx950" in pvb.version()
+
+
+def test_status_strings():
+    for code in range(8):
+        assert pvb.status_string(code) and pvb.status_string(code) != "unknown status"
+    assert pvb.status_string(99) == "unknown status"
+
+
+def test_nextfit_fixture_matches_oracle():
+    g = json.load(open(os.path.join(GOLD, "nextfit_capacity6.json")))
+    row_of, start_of, n_rows = pvb.pack_plan_nextfit(g["prediction_lengths"], g["capacity"])
+    o_row, o_start, o_n = P.next_fit(g["prediction_lengths"], g["capacity"])
+    assert row_of.tolist() == o_row == [0, 0, 1]
+    assert start_of.tolist() == o_start == [0, 3, 0]
+    assert n_rows == o_n == 2
+
+
+def test_planners_bit_exact_random():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        cap = int(rng.integers(1, 40))
+        n = int(rng.integers(0, 60))
+        lengths = rng.integers(0, cap + 1, size=n)
+        a = pvb.pack_plan_nextfit(lengths, cap)
+        b = P.next_fit(lengths.tolist(), cap)
+        assert a[0].tolist() == b[0] and a[1].tolist() == b[1] and a[2] == b[2]
+        a = pvb.pack_plan_bfd(lengths, cap)
+        b = P.best_fit_decreasing(lengths.tolist(), cap)
+        assert a[0].tolist() == b[0] and a[1].tolist() == b[1] and a[2] == b[2]
+        assert a[3].tolist() == b[3] and a[4].tolist() == b[4]
+
+
+def test_bfd_cfg3_20000_lengths_bit_exact():
+    L = raw_lengths_cfg3(0)
+    a = pvb.pack_plan_bfd(L, 8192)
+    b = P.best_fit_decreasing(L.tolist(), 8192)
+    assert a[2] == b[2]
+    assert np.array_equal(a[0], np.asarray(b[0])) and np.array_equal(a[1], np.asarray(b[1]))
+    assert np.array_equal(a[3], np.asarray(b[3])) and np.array_equal(a[4], np.asarray(b[4]))
+    first = L[a[3][a[4][0]:a[4][1]]]
+    assert first.tolist() == [8192]
+
+
+def test_planners_large_n_and_capacity_one():
+    L = np.ones(100000, np.int32)
+    row_of, start_of, n_rows = pvb.pack_plan_nextfit(L, 1)
+    assert n_rows == 100000 and row_of[-1] == 99999 and start_of.max() == 0
+    bin_of, start_of, n_bins, order, offs = pvb.pack_plan_bfd(L, 7)
+    assert n_bins == (100000 + 6) // 7 and offs[-1] == 100000
+    assert pvb.pack_plan_nextfit([], 5)[2] == 0
+    assert pvb.pack_plan_bfd([], 5)[2] == 0
+
+
+def test_planner_errors():
+    with pytest.raises(pvb.PvbError) as e:
+        pvb.pack_plan_nextfit([3, 9], 8)
+    assert e.value.status == 2
+    with pytest.raises(pvb.PvbError) as e:
+        pvb.pack_plan_bfd([3, -1], 8)
+    assert e.value.status == 1
+    with pytest.raises(pvb.PvbError) as e:
+        pvb.pack_plan_bfd([1], 0)
+    assert e.value.status == 1
+    # null output pointer
+    L = pvb.lib()
+    a = np.array([1, 2], np.int32)
+    n = ctypes.c_int64(0)
+    assert L.pvb_pack_plan_nextfit(a.ctypes.data, 2, 4, None, None, ctypes.addressof(n)) == 1
+
+
+def test_workspace_sizes():
+    assert pvb.workspace_bytes(8192, 32, 128, 1, False) >= 256 + 64 * 8
+    fwd = pvb.workspace_bytes(4096, 16, 128, 16, False)
+    bwd32 = pvb.workspace_bytes(4096, 16, 128, 16, True, pvb.PVB_F32)
+    bwd16 = pvb.workspace_bytes(4096, 16, 128, 16, True, pvb.PVB_BF16)
+    assert bwd32 >= 16 * 4096 * 4 and bwd16 >= bwd32 + 4096 * 16 * 128 * 4
+    assert fwd > 0
+    assert pvb.workspace_bytes(10, 2, 96, 1, False) == 0
+
+
+FAKE = 0x1000   # a non-null address that host validation never dereferences
+
+
+def _fwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=2, d=64, scale=0.125,
+                o=FAKE, o_dtype=0, lse=FAKE, prec=0, ws=FAKE, ws_bytes=1 << 20, status=FAKE)
+    args.update(kw)
+    return pvb.lib().pvb_varlen_attn_fwd(*args.values(), None)
+
+
+def _bwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, o_dtype=0, do=FAKE, lse=FAKE, cu=FAKE, h_cu=None,
+                n_seg=1, T=8, H=2, d=64, scale=0.125, dq=FAKE, dk=FAKE, dv=FAKE, g=1, prec=0,
+                ws=FAKE, ws_bytes=1 << 24, status=FAKE)
+    args.update(kw)
+    return pvb.lib().pvb_varlen_attn_bwd(*args.values(), None)
+
+
+def test_device_entry_points_reject_bad_arguments_on_host():
+    assert _fwd(d=96) == 6
+    assert _fwd(H=0) == 1
+    assert _fwd(q=None) == 1
+    assert _fwd(status=None) == 1
+    assert _fwd(o_dtype=5) == 1
+    assert _fwd(prec=7) == 1
+    assert _fwd(scale=0.0) == 1
+    assert _fwd(scale=float("nan")) == 1
+    assert _fwd(ws=None) == 5
+    assert _fwd(ws_bytes=16) == 5
+    bad = np.array([0, 9], np.int32)                  # cu[B] != T
+    assert _fwd(h_cu=bad.ctypes.data) == 4
+    dec = np.array([0, 6, 5, 8], np.int32)            # decreasing
+    assert _fwd(h_cu=dec.ctypes.data, n_seg=3) == 4
+    first = np.array([1, 8], np.int32)
+    assert _fwd(h_cu=first.ctypes.data) == 4
+    assert _bwd(d=32) == 6
+    assert _bwd(dv=None) == 1
+    assert _bwd(g=3) == 1
+    assert _bwd(ws_bytes=8) == 5
+    assert _bwd(h_cu=bad.ctypes.data) == 4
+    L = pvb.lib()
+    assert L.pvb_build_packed_row(None, 2, 8, 0, FAKE, FAKE, FAKE, None, None, None, None, None, None,
+                                  FAKE, None) == 1
+    assert L.pvb_build_packed_row(FAKE, 2, 8, -1, FAKE, FAKE, FAKE, None, None, None, None, None, None,
+                                  FAKE, None) == 1
+    assert L.pvb_build_packed_row(FAKE, 2, 8, 2**31 - 1, FAKE, FAKE, FAKE, None, None, None, None,
+                                  None, None, FAKE, None) == 3
+    # token outputs without a token source
+    assert L.pvb_build_packed_row(FAKE, 2, 8, 0, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
+                                  FAKE, None) == 1

@@ -1,0 +1,165 @@
+"""GPU parity of the varlen attention kernels against the fp64 oracle.
+
+Small cases are compared element by element in full; the full-size workloads
+are launched exactly as the benchmark launches them and compared on sampled
+heads, each sampled head in full (every segment, every row).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from tests.parity import (check, compare_bwd, compare_fwd, dev_bf16, dev_cu, gpu_bwd, gpu_fwd,
+                          host_cu, oracle_inputs, say, to64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import packed_varlen_block_amd  # noqa: F401  (fails loudly if libpvb.so is missing)
+
+
+SMALL_LENGTHS = [
+    [1], [2], [63], [64], [65], [127], [128], [129],
+    [5, 3, 4], [0, 0, 7, 0], [200, 1, 0, 130, 64, 65], [300], [17, 129, 0, 1, 256],
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("o_dtype,precision", [("bf16", "bf16"), ("f32", "bf16"), ("f32", "split")])
+def test_forward_small_sweep(d, o_dtype, precision):
+    for i, lengths in enumerate(SMALL_LENGTHS):
+        say(f"fwd small d={d} o={o_dtype} prec={precision} lengths={lengths}")
+        w = W.random_small(100 + i, lengths, H=3, d=d, backward=False)
+        _, o, lse = gpu_fwd(w, o_dtype, precision)
+        compare_fwd(w, o, lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("grad_dtype,precision", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "split")])
+def test_backward_small_sweep(d, grad_dtype, precision):
+    for i, lengths in enumerate(SMALL_LENGTHS):
+        say(f"bwd small d={d} g={grad_dtype} prec={precision} lengths={lengths}")
+        w = W.random_small(200 + i, lengths, H=3, d=d, backward=True)
+        dev, o, lse = gpu_fwd(w, "f32" if precision == "split" else "bf16", precision)
+        dq, dk, dv = gpu_bwd(dev, o, lse, w, grad_dtype, precision)
+        compare_bwd(w, dq, dk, dv)
+
+
+def test_worked_example_and_merged_boundary():
+    say("cfg1: worked example, forward, and the merged boundary [0,5,12]")
+    import packed_varlen_block_amd as pvb
+    import torch
+    w = W.make(1)
+    for od in ("bf16", "f32"):
+        dev, o, lse = gpu_fwd(w, od)
+        compare_fwd(w, o, lse, tag=f"cfg1 {od} ")
+    q, k, v, _ = dev
+    merged = torch.tensor([0, 5, 12], dtype=torch.int32).cuda()
+    om, lm, st = pvb.varlen_attn_fwd(q, k, v, merged, o_dtype=torch.float32)
+    pvb.check_status(st)
+    o3, _, st = pvb.varlen_attn_fwd(q, k, v, dev[3], o_dtype=torch.float32)
+    pvb.check_status(st)
+    qo, ko, vo, _ = oracle_inputs(w)
+    ref_m, _ = A.varlen_forward(qo, ko, vo, [0, 5, 12])
+    check("cfg1 merged O", to64(om), ref_m)
+    # rows of A and B do not change when B and C merge; C's rows do
+    assert torch.allclose(om[:8], o3[:8], atol=1e-6)
+    assert (om[8:] - o3[8:]).abs().max().item() > 1e-3
+
+
+def test_cfg2_forward_full():
+    say("cfg2: T=4096, 16 segments, H=16, d=128, forward, every head")
+    w = W.make(2)
+    _, o, lse = gpu_fwd(w, "bf16")
+    compare_fwd(w, o, lse, tag="cfg2 ")
+
+
+def _cfg3():
+    import packed_varlen_block_amd as pvb
+    raw = W.raw_lengths_cfg3(0)
+    _, _, _, order, offs = pvb.pack_plan_bfd(raw, 8192)
+    return W.make(3, first_pack_lengths=raw[order[offs[0]:offs[1]]])
+
+
+def test_cfg3_forward_backward_sampled_heads():
+    say("cfg3: BFD first pack T=8192, H=32, d=128, fwd+bwd; heads 0, 13, 31 compared")
+    w = _cfg3()
+    assert w.T == 8192 and len(w.lengths) == 1
+    dev, o, lse = gpu_fwd(w, "bf16")
+    dq, dk, dv = gpu_bwd(dev, o, lse, w, "f32")
+    compare_fwd(w, o, lse, heads=[0, 13, 31], tag="cfg3 ")
+    compare_bwd(w, dq, dk, dv, heads=[0, 31], tag="cfg3 ")
+
+
+def test_cfg4_forward_backward_sampled_heads():
+    say("cfg4: T=32768 with a 16384 segment, H=32, d=128, fwd+bwd; head 7 compared")
+    w = W.make(4)
+    dev, o, lse = gpu_fwd(w, "bf16")
+    dq, dk, dv = gpu_bwd(dev, o, lse, w, "f32")
+    compare_fwd(w, o, lse, heads=[7], tag="cfg4 ")
+    compare_bwd(w, dq, dk, dv, heads=[7], tag="cfg4 ")
+
+
+def test_cfg5_forward_backward_split_precision():
+    say("cfg5: T=16384 edge lengths incl. 0, outliers x30, H=16, fwd+bwd split/fp32; heads 0, 9")
+    w = W.make(5)
+    assert (w.lengths == 0).any()
+    dev, o, lse = gpu_fwd(w, "f32", "split")
+    dq, dk, dv = gpu_bwd(dev, o, lse, w, "f32", "split")
+    compare_fwd(w, o, lse, heads=[0, 9], tag="cfg5 ")
+    compare_bwd(w, dq, dk, dv, heads=[0, 9], tag="cfg5 ")
+
+
+def test_isolation_nan_in_other_segment():
+    say("isolation: NaN/Inf in segment A leaves segment B bit-identical and finite")
+    import torch
+    w = W.random_small(7, [70, 150], H=2, d=128, backward=True)
+    dev, o, lse = gpu_fwd(w, "f32")
+    dq, dk, dv = gpu_bwd(dev, o, lse, w, "f32")
+    w2 = W.random_small(7, [70, 150], H=2, d=128, backward=True)
+    for arr in (w2.q, w2.k, w2.v, w2.do):
+        arr[:70] = 0x7FC0            # bf16 NaN
+        arr[3] = 0x7F80              # bf16 +Inf
+    dev2, o2, lse2 = gpu_fwd(w2, "f32")
+    dq2, dk2, dv2 = gpu_bwd(dev2, o2, lse2, w2, "f32")
+    for a, b in ((o, o2), (dk, dk2), (dv, dv2)):
+        assert torch.isfinite(b[70:]).all()
+        assert torch.equal(a[70:], b[70:])
+    assert torch.isfinite(dq2[70:]).all()
+    assert torch.allclose(dq[70:], dq2[70:], atol=1e-6)
+    assert torch.equal(lse[:, 70:], lse2[:, 70:])
+
+
+def test_bad_device_cu_sets_status_and_writes_nothing():
+    say("device-detected bad cu_seqlens")
+    import packed_varlen_block_amd as pvb
+    import torch
+    w = W.random_small(9, [40, 24], H=2, d=64, backward=False)
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    for bad in ([0, 40, 30], [1, 40, 64], [0, 40, 63]):
+        cu = torch.tensor(bad, dtype=torch.int32).cuda()
+        o = torch.full((64, 2, 64), 7.0, dtype=torch.float32).cuda()
+        _, _, st = pvb.varlen_attn_fwd(q, k, v, cu, out=o)
+        with pytest.raises(pvb.PvbError) as e:
+            pvb.check_status(st)
+        assert e.value.status == 4
+        assert (o == 7.0).all()
+    with pytest.raises(pvb.PvbError) as e:
+        pvb.varlen_attn_fwd(q, k, v, torch.tensor([0, 40, 30], dtype=torch.int32).cuda(),
+                            h_cu=[0, 40, 30])
+    assert e.value.status == 4
+
+
+def test_backward_dk_dv_deterministic():
+    say("determinism: dK/dV bitwise repeatable")
+    import torch
+    w = W.random_small(11, [300, 77], H=2, d=128, backward=True)
+    dev, o, lse = gpu_fwd(w, "bf16")
+    a = gpu_bwd(dev, o, lse, w, "f32")
+    b = gpu_bwd(dev, o, lse, w, "f32")
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert torch.allclose(a[0], b[0], atol=1e-5)
