@@ -1,0 +1,258 @@
+"""Benchmark: packed varlen block-causal attention, forward + backward, one MI355X.
+
+Default workload: best-fit-decreasing packing of 20,000 log-normal sample
+lengths (median 600, sigma 1, clipped to [8, 8192]) at budget 8192, then
+attention on the first pack (T = 8192, one 8192-token segment), H = 32,
+head_dim = 128, bf16 Q/K/V ~ N(0,1)*0.5 and dO ~ N(0,1).
+
+One step is one pass of the whole hot path over that batch:
+  host   pack_plan_bfd over the 20,000 lengths; the first pack's lengths are
+         copied to the device (pinned ring buffer, asynchronous),
+  device build_packed_row (cu_seqlens, position_ids, segment_ids),
+         varlen_attn_fwd (O bf16, LSE), varlen_attn_bwd (dQ, dK, dV fp32).
+Host planning of step i+1 overlaps the device work of step i.
+
+Useful work: F = sum over segments of H * 4 * d * L(L+1)/2 for the forward;
+the backward counts 2.5 F (five matrix products over the permitted edges),
+so a step is 3.5 F.  Printed as one JSON line.
+
+python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-hbm-case]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def useful_fwd_flops(lengths, H, d):
+    return float(sum(H * 4.0 * d * L * (L + 1) / 2.0 for L in (int(x) for x in lengths)))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-case", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the fp64 oracle (as it stands) on whole heads of the same workload."""
+    from oracle import attention as A
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    q = W.bf16_bits_to_f64(wl.q)
+    k = W.bf16_bits_to_f64(wl.k)
+    v = W.bf16_bits_to_f64(wl.v)
+    do = W.bf16_bits_to_f64(wl.do)
+    cu = np.concatenate([[0], np.cumsum(wl.lengths)]).astype(np.int64)
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < wl.H and time.perf_counter() - t0 < budget_s:
+        A.varlen_forward(q, k, v, cu, heads=[heads])
+        A.varlen_backward(q, k, v, do, cu, heads=[heads])
+        heads += 1
+    el = time.perf_counter() - t0
+    flops = 3.5 * useful_fwd_flops(wl.lengths, heads, wl.d)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle forward+backward on {heads} of {wl.H} heads of the same "
+                      f"pack, {el:.1f} s; useful causal FLOP counted as on the GPU"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import packed_varlen_block_amd as pvb
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- workload: BFD first pack of the 20,000 lengths
+    raw = W.raw_lengths_cfg3(a.seed)
+    _, _, n_bins, order, offs = pvb.pack_plan_bfd(raw, 8192)
+    first = raw[order[offs[0]:offs[1]]]
+    wl = W.make(3, seed=a.seed, first_pack_lengths=first)
+    T, H, d = wl.T, wl.H, wl.d
+    B = len(wl.lengths)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = up(wl.q), up(wl.k), up(wl.v), up(wl.do)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    ws_f = torch.empty(pvb.workspace_bytes(T, H, d, B, False), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(pvb.workspace_bytes(T, H, d, B, True, pvb.PVB_F32), dtype=torch.uint8, device=dev)
+    st_row = torch.zeros(1, dtype=torch.int32, device=dev)
+    st_f = torch.zeros(1, dtype=torch.int32, device=dev)
+    st_b = torch.zeros(1, dtype=torch.int32, device=dev)
+    ring = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(4)]
+    ring_ev = [None] * 4
+    len_dev = torch.empty(B, dtype=torch.int32, device=dev)
+
+    ev = {name: [] for name in ("row", "fwd", "bwd")}
+
+    def step(i, timed):
+        # host: plan, take the first pack, stage its lengths
+        _, _, _, order_i, offs_i = pvb.pack_plan_bfd(raw, 8192)
+        slot = i % 4
+        if ring_ev[slot] is not None:
+            ring_ev[slot].synchronize()
+        ring[slot].numpy()[:] = raw[order_i[offs_i[0]:offs_i[1]]]
+        len_dev.copy_(ring[slot], non_blocking=True)
+        e = torch.cuda.Event()
+        e.record(stream)
+        ring_ev[slot] = e
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        if timed:
+            marks[0].record(stream)
+        row = pvb.build_packed_row(len_dev, capacity=T, status=st_row)
+        if timed:
+            marks[1].record(stream)
+        pvb.varlen_attn_fwd(q, k, v, row["cu"], out=o, lse=lse, workspace=ws_f, status=st_f)
+        if timed:
+            marks[2].record(stream)
+        pvb.varlen_attn_bwd(q, k, v, o, do, lse, row["cu"], dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                            status=st_b)
+        if timed:
+            marks[3].record(stream)
+            ev["row"].append((marks[0], marks[1]))
+            ev["fwd"].append((marks[1], marks[2]))
+            ev["bwd"].append((marks[2], marks[3]))
+
+    for i in range(a.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    for s in (st_row, st_f, st_b):
+        pvb.check_status(s)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for s in (st_row, st_f, st_b):
+        pvb.check_status(s)
+
+    def avg_ms(name):
+        return float(np.mean([s.elapsed_time(e) for s, e in ev[name]]))
+
+    ms_step = elapsed / a.steps * 1e3
+    F = useful_fwd_flops(wl.lengths, H, d)
+    value = 3.5 * F / (ms_step * 1e-3) / 1e12
+    fwd_ms, bwd_ms, row_ms = avg_ms("fwd"), avg_ms("bwd"), avg_ms("row")
+    bwd_tflops = 2.5 * F / (bwd_ms * 1e-3) / 1e12
+    fwd_tflops = F / (fwd_ms * 1e-3) / 1e12
+    # host planner time alone
+    tp = time.perf_counter()
+    for _ in range(5):
+        pvb.pack_plan_bfd(raw, 8192)
+    plan_ms = (time.perf_counter() - tp) / 5 * 1e3
+
+    out = {
+        "metric": "varlen causal attn fwd+bwd useful TFLOP/s and % bf16 MFMA peak, T=8192 pack",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bfd_first_pack_T8192_H32_d128", "T": T, "H": H, "head_dim": d,
+                   "segments": B, "samples_planned": int(raw.size), "packs": int(n_bins),
+                   "passes": "fwd+bwd", "o_dtype": "bf16", "grad_dtype": "f32",
+                   "precision": "bf16", "seed": a.seed},
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "useful_flop_per_step": 3.5 * F,
+        "breakdown_ms": {"host_bfd_plan": round(plan_ms, 4), "build_packed_row": round(row_ms, 4),
+                         "varlen_attn_fwd": round(fwd_ms, 4), "varlen_attn_bwd": round(bwd_ms, 4)},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "roofline": {"kernel": "varlen_attn_bwd", "bound": "mfma", "achieved": round(bwd_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+
+    if not a.no_hbm_case:
+        out["short_pack_fwd"] = short_pack_forward(torch, pvb, W, dev, stream, a.seed)
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def short_pack_forward(torch, pvb, W, dev, stream, seed, n_sets=8, reps=40):
+    """The short-segment pack (T=4096, 16 segments in [64,512], H=16, d=128,
+    forward, O bf16): achieved HBM GB/s of algorithmic bytes.  n_sets input
+    sets (> 256 MB in total) rotate so that each call starts cold in the caches."""
+    w = W.make(2, seed=seed)
+    T, H, d = w.T, w.H, w.d
+    B = len(w.lengths)
+    sets = []
+    for s in range(n_sets):
+        ws = W.random_small(seed * 100 + s, w.lengths, H, d, scale=0.5, backward=False, cfg_tag=2)
+        up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+        sets.append((up(ws.q), up(ws.k), up(ws.v), torch.empty((T, H, d), dtype=torch.bfloat16, device=dev),
+                     torch.empty((H, T), dtype=torch.float32, device=dev)))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(w.lengths)]).astype(np.int32), device=dev)
+    wsp = torch.empty(pvb.workspace_bytes(T, H, d, B, False), dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    for i in range(10):
+        q, k, v, o, l = sets[i % n_sets]
+        pvb.varlen_attn_fwd(q, k, v, cu, out=o, lse=l, workspace=wsp, status=st)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps):
+        q, k, v, o, l = sets[i % n_sets]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pvb.varlen_attn_fwd(q, k, v, cu, out=o, lse=l, workspace=wsp, status=st)
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    pvb.check_status(st)
+    ms = np.array([a.elapsed_time(b) for a, b in times])
+    byts = 3 * T * H * d * 2 + T * H * d * 2 + 4 * T * H + 4 * (B + 1)
+    F = useful_fwd_flops(w.lengths, H, d)
+    med = float(np.median(ms))
+    return {"workload": "pack_T4096_16seg_H16_d128", "pass": "fwd", "median_us": round(med * 1e3, 2),
+            "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2),
+            "algorithmic_bytes": byts, "achieved_GBs": round(byts / (med * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "useful_tflops": round(F / (med * 1e-3) / 1e12, 2)}
+
+
+if __name__ == "__main__":
+    main()

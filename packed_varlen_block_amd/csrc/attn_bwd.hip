@@ -19,8 +19,11 @@
 //               P, dS in registers (lane = key column),
 //               dV += P^T dO and dK += dS^T Q with dO/Q fragments read
 //               transposed from LDS,
-//               dS -> LDS, then dQ_tile = dS K split over the waves by output
-//               block and added into the fp32 accumulator with atomics.
+//               dS^T -> LDS, then dQ_tile = dS K split over the waves by
+//               output block and added into the fp32 accumulator with atomics.
+//             The next query tile is prefetched into registers during the
+//             current one and lands in the other half of a double-buffered
+//             LDS tile; barriers order LDS only, so atomics stay in flight.
 //   bwd_dq    dQ accumulator -> bf16 (only for bf16 gradients).
 #include "pvb_device.hpp"
 
@@ -79,17 +82,18 @@ bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                 GradT* __restrict__ dk, GradT* __restrict__ dv) {
   constexpr int BN = kBwdBN, BM = kBwdBM;
   constexpr int QP = D + 8;         // pitch of the Q / dO / K tiles (elements)
-  constexpr int SP = BN + 8;        // pitch of the dS tile
+  constexpr int TP = BM + 8;        // pitch of the dS^T tile [key][query]
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int QCH = BM * CPR / kBwdThreads;  // chunks per thread per Q (or dO) tile
   constexpr int NSPLIT = SPLIT ? 2 : 1;
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BM * QP];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[BM * QP];
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2][BM * QP];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[2][BM * QP];
   __shared__ __attribute__((aligned(16))) bf16 sK[BN * QP];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[NSPLIT][BM * SP];
-  __shared__ float sLse[BM], sDel[BM];
+  __shared__ __attribute__((aligned(16))) bf16 sdST[NSPLIT][BN * TP];
+  __shared__ float sLse[2][BM], sDel[2][BM];
 
   const int tau = blockIdx.x / H;
   const int h = blockIdx.x - tau * H;
@@ -104,6 +108,9 @@ bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int kw0 = k0 + 32 * w;          // first key of this wave
   const int kcol = kw0 + lq;            // this lane's key column (local index)
+  // transpose-read lane offsets: row (lane&15)>>2 of a 4-row group, column 16((lane>>4)&1) + 4(lane&3)
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // K and V fragments (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kf[KSTEPS], vf[KSTEPS];
@@ -126,42 +133,69 @@ bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     *(uint4*)(sK + row * QP + col) = key < L ? *(const uint4*)(k + base + key * rs + col) : zero4();
   }
 
+  // next query tile, prefetched into registers while the current one is used
+  uint4 pq[QCH], pd[QCH];
+  float plse = INFINITY, pdel = 0.f;
+  auto fetch = [&](int jq) {
+    const int qt0 = jq * BM;
+#pragma unroll
+    for (int r = 0; r < QCH; ++r) {
+      const int c = tid + kBwdThreads * r;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      const int qi = qt0 + row;
+      if (qi < L) {
+        pq[r] = *(const uint4*)(q + base + qi * rs + col);
+        pd[r] = *(const uint4*)(dout + base + qi * rs + col);
+      } else {
+        pq[r] = zero4();
+        pd[r] = zero4();
+      }
+    }
+    if (tid < BM) {
+      const int qi = qt0 + tid;
+      plse = qi < L ? lse[(int64_t)h * T + seg0 + qi] * kLog2e : INFINITY;
+      pdel = qi < L ? delta[(int64_t)h * T + seg0 + qi] : 0.f;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < QCH; ++r) {
+      const int c = tid + kBwdThreads * r;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      *(uint4*)(sQ[buf] + row * QP + col) = pq[r];
+      *(uint4*)(sdO[buf] + row * QP + col) = pd[r];
+    }
+    if (tid < BM) {
+      sLse[buf][tid] = plse;
+      sDel[buf][tid] = pdel;
+    }
+  };
+
   f32x16 dkacc[DBLK], dvacc[DBLK];
 #pragma unroll
   for (int j = 0; j < DBLK; ++j) dkacc[j] = dvacc[j] = f32x16{};
 
+  const int jq0 = k0 / BM;
   const int jq_end = (L + BM - 1) / BM;
-  for (int jq = k0 / BM; jq < jq_end; ++jq) {
+  fetch(jq0);
+  stash(0);
+  lds_barrier();
+  for (int jq = jq0; jq < jq_end; ++jq) {
+    const int buf = (jq - jq0) & 1;
     const int qt0 = jq * BM;
     const int qt_last = min(qt0 + BM, L) - 1;
-    __syncthreads();
-    for (int c = tid; c < BM * CPR; c += kBwdThreads) {
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int qi = qt0 + row;
-      uint4 a = zero4(), b = zero4();
-      if (qi < L) {
-        a = *(const uint4*)(q + base + qi * rs + col);
-        b = *(const uint4*)(dout + base + qi * rs + col);
-      }
-      *(uint4*)(sQ + row * QP + col) = a;
-      *(uint4*)(sdO + row * QP + col) = b;
-    }
-    if (tid < BM) {
-      const int qi = qt0 + tid;
-      sLse[tid] = qi < L ? lse[(int64_t)h * T + seg0 + qi] * kLog2e : INFINITY;
-      sDel[tid] = qi < L ? delta[(int64_t)h * T + seg0 + qi] : 0.f;
-    }
-    __syncthreads();
+    if (jq + 1 < jq_end) fetch(jq + 1);
+    const bf16* cQ = sQ[buf];
+    const bf16* cdO = sdO[buf];
 
-    const bool wave_idle = kw0 > qt_last;   // all of this wave's keys are later than all queries
-    if (!wave_idle) {
+    if (kw0 <= qt_last) {   // otherwise every key of this wave is later than every query
       f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const bf16x8 qa = *(const bf16x8*)(sQ + (32 * qb + lq) * QP + 16 * s + 8 * g);
-          const bf16x8 da = *(const bf16x8*)(sdO + (32 * qb + lq) * QP + 16 * s + 8 * g);
+          const bf16x8 qa = *(const bf16x8*)(cQ + (32 * qb + lq) * QP + 16 * s + 8 * g);
+          const bf16x8 da = *(const bf16x8*)(cdO + (32 * qb + lq) * QP + 16 * s + 8 * g);
           sacc[qb] = mfma32(qa, kf[s], sacc[qb]);
           pacc[qb] = mfma32(da, vf[s], pacc[qb]);
         }
@@ -173,10 +207,10 @@ bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int ql = 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
-          float p = exp2f(sacc[qb][i] * scale_log2 - sLse[ql]);
+          float p = fast_exp2(sacc[qb][i] * scale_log2 - sLse[buf][ql]);
           if (need_mask && (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L)) p = 0.f;
           sacc[qb][i] = p;
-          pacc[qb][i] = p * (pacc[qb][i] - sDel[ql]);
+          pacc[qb][i] = p * (pacc[qb][i] - sDel[buf][ql]);
         }
       // dV += P^T dO and dK += dS^T Q.  k-slot 8g+e holds query 16kk + 8(e/4) + 4g + e%4.
 #pragma unroll
@@ -193,12 +227,11 @@ bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
             sl[e] = (bf16)(ds - (float)sh[e]);
           }
         }
-        const int roff = (16 * kk + 4 * g + ((lane & 15) >> 2)) * QP + 16 * ((lane >> 4) & 1) +
-                         4 * (lane & 3);
+        const int roff = (16 * kk + 4 * g + tr_row) * QP + tr_col;
 #pragma unroll
         for (int j = 0; j < DBLK; ++j) {
-          const bf16x8 dof = cat(lds_read_tr(sdO + roff + 32 * j), lds_read_tr(sdO + roff + 8 * QP + 32 * j));
-          const bf16x8 qtf = cat(lds_read_tr(sQ + roff + 32 * j), lds_read_tr(sQ + roff + 8 * QP + 32 * j));
+          const bf16x8 dof = cat(lds_read_tr(cdO + roff + 32 * j), lds_read_tr(cdO + roff + 8 * QP + 32 * j));
+          const bf16x8 qtf = cat(lds_read_tr(cQ + roff + 32 * j), lds_read_tr(cQ + roff + 8 * QP + 32 * j));
           dvacc[j] = mfma32(ph, dof, dvacc[j]);
           dkacc[j] = mfma32(sh, qtf, dkacc[j]);
           if constexpr (SPLIT) {
@@ -207,47 +240,50 @@ bwd_main_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
           }
         }
       }
-      // dS -> LDS as [query][key]
+      // dS^T -> LDS: row = this lane's key, four consecutive queries per store
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
-          const float ds = pacc[qb][i];
-          const bf16 hi = (bf16)ds;
-          sdS[0][ql * SP + 32 * w + lq] = hi;
-          if constexpr (SPLIT) sdS[1][ql * SP + 32 * w + lq] = (bf16)(ds - (float)hi);
-        }
-    } else {
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 hi, lo;
 #pragma unroll
-      for (int p = 0; p < NSPLIT; ++p)
-        for (int ql = 0; ql < BM; ++ql)
-          if (g == 0) sdS[p][ql * SP + 32 * w + lq] = (bf16)0.f;
+          for (int t = 0; t < 4; ++t) {
+            const float ds = pacc[qb][4 * i4 + t];
+            hi[t] = (bf16)ds;
+            if constexpr (SPLIT) lo[t] = (bf16)(ds - (float)hi[t]);
+          }
+          const int off = (32 * w + lq) * TP + 32 * qb + 8 * i4 + 4 * g;
+          *(bf16x4*)(&sdST[0][off]) = hi;
+          if constexpr (SPLIT) *(bf16x4*)(&sdST[1][off]) = lo;
+        }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // dQ tile = dS K over the item's keys, one 32x32 output block at a time
-    const int n_ks = min(BN / 16, (qt_last - k0) / 16 + 1);   // key steps that can be non-zero
+    // dQ tile = dS K, one 32x32 output block at a time; only key steps that
+    // belong to waves with work are visited
+    const int n_ks = min(BN / 16, (qt_last - k0) / 16 + 1);
     for (int blk = w; blk < 2 * DBLK; blk += 4) {
       const int qb = blk & 1, j = blk >> 1;
       f32x16 acc = f32x16{};
       for (int ks = 0; ks < n_ks; ++ks) {
-        const bf16* kaddr = sK + (16 * ks + 8 * g + ((lane & 15) >> 2)) * QP + 32 * j +
-                            16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int r0 = 16 * ks + 8 * g + tr_row;
+        const bf16* kaddr = sK + r0 * QP + 32 * j + tr_col;
         const bf16x8 bk = cat(lds_read_tr(kaddr), lds_read_tr(kaddr + 4 * QP));
 #pragma unroll
         for (int p = 0; p < NSPLIT; ++p) {
-          const bf16x8 a = *(const bf16x8*)(&sdS[p][(32 * qb + lq) * SP + 16 * ks + 8 * g]);
+          const bf16* saddr = &sdST[p][r0 * TP + 32 * qb + tr_col];
+          const bf16x8 a = cat(lds_read_tr(saddr), lds_read_tr(saddr + 4 * TP));
           acc = mfma32(a, bk, acc);
         }
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = qt0 + 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (qi < L)
-          unsafeAtomicAdd(dq_acc + base + qi * rs + 32 * j + lq, acc[i] * scale);
+        if (qi < L) unsafeAtomicAdd(dq_acc + base + qi * rs + 32 * j + lq, acc[i] * scale);
       }
     }
+    if (jq + 1 < jq_end) stash(buf ^ 1);
+    lds_barrier();
   }
 
   // dK (scaled) and dV rows of this wave's keys

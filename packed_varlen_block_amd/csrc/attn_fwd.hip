@@ -100,7 +100,7 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   load_tile(0);
   for (int n = 0; n < nkv; ++n) {
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + kFwdThreads * r;
@@ -108,7 +108,7 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       *(uint4*)(sK + row * KP + col) = kr[r];
       *(uint4*)(sV + row * VP + col) = vr[r];
     }
-    __syncthreads();
+    lds_barrier();
     if (n + 1 < nkv) load_tile(n + 1);
 
     const int key0 = n * BN;
@@ -143,13 +143,13 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     mx = fmaxf(mx, swap_halves(mx));
     const float m_new = fmaxf(m_run, mx * scale_log2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = fast_exp2(m_run - m_use);
     float rsum = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(st[kb2][i] * scale_log2 - m_use);
+        const float p = fast_exp2(st[kb2][i] * scale_log2 - m_use);
         st[kb2][i] = p;
         rsum += p;
       }

@@ -50,6 +50,15 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// 2^x on the transcendental unit (results below 2^-126 flush to 0; -inf -> 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
+// not for its outstanding global loads, stores or atomics.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T out_cast(float x);
 template <>
