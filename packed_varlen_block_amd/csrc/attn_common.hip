@@ -42,7 +42,7 @@ __device__ int block_inclusive_scan(int x, int* wsum, int* total) {
 }  // namespace
 
 __global__ void __launch_bounds__(kPlanThreads)
-plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile, int backward,
+plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
                   int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status) {
   __shared__ int s_nt[kPlanChunk];
   __shared__ int s_off[kPlanMaxM];  // counts per group, then their exclusive offsets
@@ -120,7 +120,7 @@ plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile, in
       if (m < M) {
         for (int i = 0; i < nc; ++i) {
           const int nt = s_nt[i];
-          if (nt > m) tiles[pos++] = make_int2(c0 + i, backward ? nt - 1 - m : m);
+          if (nt > m) tiles[pos++] = make_int2(c0 + i, m);
         }
       }
     }

@@ -9,15 +9,17 @@
 // One workgroup = one work item (segment b, query tile m of 128 rows, head h)
 // taken from the planner's heaviest-first list.  Its 4 waves own 32 query rows
 // each.  Per 64-key tile:
-//   * K and V rows of the segment are staged through LDS with 16-byte
-//     coalesced loads (rows past the segment end are zero-filled, never read),
+//   * K and V rows of the segment are copied global -> LDS asynchronously
+//     (16-byte copies into a double-buffered, XOR-swizzled tile: the copy of
+//     tile n+1 overlaps the math on tile n),
 //   * S^T = K Q^T on 32x32x16 bf16 MFMAs with Q held in registers, so that
 //     each lane owns one query column and the row max/sum of the online
 //     softmax is in-lane plus one half-wave exchange,
 //   * O^T += V^T P^T, where V^T fragments come straight from the row-major V
 //     tile through the LDS transpose read and P never leaves registers.
 // Key tiles wholly above the diagonal are never visited; masking is applied
-// only on tiles that cross the diagonal or the segment end.
+// only on tiles that cross the diagonal or the segment end.  The running max
+// is raised lazily (see kSlack), so most tiles skip the rescale of O.
 #include "pvb_device.hpp"
 
 namespace pvb {
@@ -34,15 +36,15 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int H, int T,
                 float scale_log2, OutT* __restrict__ o, float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int KP = D + 8;         // K tile pitch (elements): 16-byte reads hit distinct banks
-  constexpr int VP = D + 16;        // V tile pitch (elements)
   constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;      // 32-wide feature blocks of O^T
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int CPT = BN * CPR / kFwdThreads;  // chunks per thread per tile
+  // The running max used for the exponentials is raised only when a tile's
+  // max exceeds it by more than kSlack (log2 units), so most tiles skip the
+  // rescale of O and the row sum; probabilities stay below 2^kSlack.
+  constexpr float kSlack = 8.f;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BN * VP];
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * D];
 
   const int tau = blockIdx.x / H;
   const int h = blockIdx.x - tau * H;
@@ -51,23 +53,24 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int q0 = tm.y * BM;
-  const int64_t rs = (int64_t)H * D;  // row stride (elements)
+  const int rs = H * D;  // row stride (elements)
   const int64_t base = ((int64_t)seg0 * H + h) * D;
-  const bf16* qb = q + base;
-  const bf16* kb = k + base;
-  const bf16* vb = v + base;
+  const bf16* qs = q + base;
+  const bf16* ks = k + base;
+  const bf16* vs = v + base;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int qrow = q0 + 32 * w + lq;     // this lane's query (local index)
   const int wq_first = q0 + 32 * w;
   const int wq_last = min(wq_first + 31, L - 1);
   const bool wave_active = wq_first < L;
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   bf16x8 qf[KSTEPS];
   if (qrow < L) {
-    const bf16* p = qb + qrow * rs + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8*)(p + 16 * s);
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8*)(qs + qrow * rs + 16 * s + 8 * g);
   } else {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = bf16x8{};
@@ -81,111 +84,98 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int q_last = min(q0 + BM, L) - 1;
   const int nkv = q_last / BN + 1;
 
-  uint4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int n) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + kFwdThreads * r;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int key = n * BN + row;
-      if (key < L) {
-        kr[r] = *(const uint4*)(kb + key * rs + col);
-        vr[r] = *(const uint4*)(vb + key * rs + col);
-      } else {
-        kr[r] = zero4();
-        vr[r] = zero4();
-      }
-    }
-  };
-
-  load_tile(0);
+  stage_rows<D, BN>(ks, rs, 0, L, sK[0], w, lane);
+  stage_rows<D, BN>(vs, rs, 0, L, sV[0], w, lane);
+  wait_vmcnt<0>();              // Q fragments and this wave's copies of tile 0
   for (int n = 0; n < nkv; ++n) {
+    const int b = n & 1;
+    // every wave's copies of tile n have landed, and every wave is done with
+    // buffer b^1 (tile n-1), which now receives tile n+1
     lds_barrier();
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + kFwdThreads * r;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *(uint4*)(sK + row * KP + col) = kr[r];
-      *(uint4*)(sV + row * VP + col) = vr[r];
+    if (n + 1 < nkv) {
+      stage_rows<D, BN>(ks, rs, (n + 1) * BN, L, sK[b ^ 1], w, lane);
+      stage_rows<D, BN>(vs, rs, (n + 1) * BN, L, sV[b ^ 1], w, lane);
     }
-    lds_barrier();
-    if (n + 1 < nkv) load_tile(n + 1);
-
+    const bf16* cK = sK[b];
+    const bf16* cV = sV[b];
     const int key0 = n * BN;
-    if (!wave_active || key0 > wq_last) continue;  // every key of this tile is in this wave's future
-
-    // S^T = K Q^T: two 32-key blocks
-    f32x16 st[2] = {f32x16{}, f32x16{}};
+    if (wave_active && key0 <= wq_last) {
+      // S^T = K Q^T: two 32-key blocks
+      f32x16 st[2];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        st[kb2] = mfma32(*(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 8 * g)), qf[0], f32x16{});
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 kf = *(const bf16x8*)(sK + (kb2 * 32 + lq) * KP + 16 * s + 8 * g);
-        st[kb2] = mfma32(kf, qf[s], st[kb2]);
+      for (int s = 1; s < KSTEPS; ++s)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+          st[kb2] = mfma32(*(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g)), qf[s], st[kb2]);
+      // mask: key > query, or key past the segment end
+      if (key0 + BN - 1 > wq_first || key0 + BN > L) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key > qrow || key >= L) st[kb2][i] = -INFINITY;
+          }
       }
-    }
-    // mask: key > query, or key past the segment end
-    if (key0 + BN - 1 > wq_first || key0 + BN > L) {
+      // online softmax for this lane's query column (in log2 units)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb2][i]);
+      mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int j = 0; j < DBLK; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float rsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key > qrow || key >= L) st[kb2][i] = -INFINITY;
+          const float p = fast_exp2(st[kb2][i] * scale_log2 - m_use);
+          st[kb2][i] = p;
+          rsum += p;
         }
-    }
-    // online softmax for this lane's query column
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb2][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rsum = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(st[kb2][i] * scale_log2 - m_use);
-        st[kb2][i] = p;
-        rsum += p;
-      }
-    rsum += swap_halves(rsum);
-    l_run = l_run * alpha + rsum;
-    m_run = m_new;
-#pragma unroll
-    for (int j = 0; j < DBLK; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
+      l_run += rsum + swap_halves(rsum);
 
-    // O^T += V^T P^T over four 16-key k-steps.  k-slot 8g+e of this lane holds
-    // key 16kk + 8(e/4) + 4g + e%4, which is where S^T's C layout put it.
+      // O^T += V^T P^T over four 16-key k-steps.  k-slot 8g+e of this lane holds
+      // key 16kk + 8(e/4) + 4g + e%4, which is where S^T's C layout put it.
 #pragma unroll
-    for (int kk = 0; kk < BN / 16; ++kk) {
-      bf16x8 ph, pl;
+      for (int kk = 0; kk < BN / 16; ++kk) {
+        bf16x8 ph, pl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = st[kk >> 1][8 * (kk & 1) + e];
-        ph[e] = (bf16)p;
-        if constexpr (SPLIT) pl[e] = (bf16)(p - (float)ph[e]);
-      }
-      const bf16* vrow = sV + (16 * kk + 4 * g + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) +
-                         4 * (lane & 3);
+        for (int e = 0; e < 8; ++e) {
+          const float p = st[kk >> 1][8 * (kk & 1) + e];
+          ph[e] = (bf16)p;
+          if constexpr (SPLIT) pl[e] = (bf16)(p - (float)ph[e]);
+        }
+        const int r0 = 16 * kk + 4 * g + tr_row;
 #pragma unroll
-      for (int j = 0; j < DBLK; ++j) {
-        const bf16x8 vf = cat(lds_read_tr(vrow + 32 * j), lds_read_tr(vrow + 8 * VP + 32 * j));
-        oacc[j] = mfma32(vf, ph, oacc[j]);
-        if constexpr (SPLIT) oacc[j] = mfma32(vf, pl, oacc[j]);
+        for (int j = 0; j < DBLK; ++j) {
+          const int c = 32 * j + tr_col;
+          const bf16x8 vf = cat(lds_read_tr(cV + swz<D>(r0, c)), lds_read_tr(cV + swz<D>(r0 + 8, c)));
+          oacc[j] = mfma32(vf, ph, oacc[j]);
+          if constexpr (SPLIT) oacc[j] = mfma32(vf, pl, oacc[j]);
+        }
       }
     }
+    if (n + 1 < nkv) wait_vmcnt<0>();   // this wave's copies of tile n+1
   }
 
   if (!wave_active || qrow >= L) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  OutT* op = o + ((int64_t)(seg0 + qrow) * H + h) * D;
+  OutT* op = o + base + (int64_t)qrow * rs;
 #pragma unroll
   for (int j = 0; j < DBLK; ++j)
 #pragma unroll
@@ -240,7 +230,7 @@ extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, cons
   if (precision != PVB_PREC_BF16 && precision != PVB_PREC_SPLIT) return PVB_E_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != 64 && d != 128) return PVB_E_UNSUPPORTED;
-  if ((int64_t)T * H * d > (int64_t)1 << 40) return PVB_E_UNSUPPORTED;
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31)) return PVB_E_UNSUPPORTED;
   const size_t cap = plan_capacity(T, n_seg, kFwdBM);
   if (cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fwd_workspace(T, n_seg)) return PVB_E_WORKSPACE;
@@ -250,7 +240,7 @@ extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* count = static_cast<int32_t*>(workspace);
   int2* tiles = reinterpret_cast<int2*>(static_cast<char*>(workspace) + 256);
-  plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kFwdBM, 0, tiles, count, d_status);
+  plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kFwdBM, tiles, count, d_status);
   if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
 
   const float sl2 = softmax_scale * kLog2e;

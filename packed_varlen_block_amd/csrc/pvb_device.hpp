@@ -59,6 +59,79 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Element offset of (row, col) in an LDS tile [rows][D] of bf16 whose 16-byte
+// chunks are XOR-swizzled per row.  For D = 128 (16 chunks per 256-byte row,
+// 64 banks of 4 bytes) the swizzle f(r) = 4(r%4) + (r/4)%4 makes three access
+// patterns bank-conflict free: 16 lanes reading 16 bytes each from 16
+// consecutive rows, 32 lanes doing transposed 8-byte reads from 4 consecutive
+// rows (r%4 == 0) x 64 bytes, and 16 lanes writing one whole row.
+template <int D>
+__device__ __forceinline__ int swzf(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * D + ((((col >> 3) ^ swzf<D>(row))) << 3) + (col & 7);
+}
+
+// Asynchronous 16-byte copy global -> LDS: global_load_lds_dwordx4.  The
+// wave's 64 lanes write 64 consecutive 16-byte chunks starting at LDS byte
+// address `lds_wave_base` (wave-uniform; lane l at chunk l), reading from
+// `gbase + voff` (gbase wave-uniform, voff a per-lane byte offset).
+// Completion is tracked by vmcnt only.  The copy is issued from inline
+// assembly so that the compiler, which cannot tell which LDS buffer it writes,
+// does not add a conservative wait for it before every later LDS read; the
+// kernels wait for it explicitly (wait_vmcnt) before a barrier.
+__device__ __forceinline__ void copy_to_lds16(const void* gbase, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_wave_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// Same, 4 bytes per lane (global_load_lds_dword): 64 consecutive dwords.
+__device__ __forceinline__ void copy_to_lds4(const void* gbase, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_wave_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+// Stage rows [row0, row0 + ROWS) of a segment-relative [L, D] tensor (row
+// stride rs elements) into a swizzled LDS tile [ROWS][D] with 16-byte
+// global->LDS copies spread over the 4 waves of a 256-thread workgroup.  Rows
+// at or past L are clamped to row L-1 of the same segment, so every staged
+// value is finite whenever the segment itself is; callers mask those rows.
+// Issues ROWS * D / 8 / 256 copies per thread.
+template <int D, int ROWS>
+__device__ __forceinline__ void stage_rows(const bf16* src, int rs, int row0, int L, bf16* tile, int w,
+                                           int lane) {
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;        // rows covered by one wave-wide copy
+  constexpr int NI = ROWS / RPI / 4;   // copies per wave
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t tile_base = lds_addr(tile);
+#pragma unroll
+  for (int r = 0; r < NI; ++r) {
+    const int grp = 4 * r + wu;
+    const int row = grp * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swzf<D>(row);   // logical chunk that lands in this lane's slot
+    const int srow = min(row0 + row, L - 1);
+    copy_to_lds16(src, (uint32_t)(srow * rs + c * 8) * 2u, tile_base + (uint32_t)(grp * RPI * D * 2));
+  }
+}
+
+// s_waitcnt with only the vector-memory counter restricted: vmcnt <= n.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <typename T>
 __device__ __forceinline__ T out_cast(float x);
 template <>
@@ -71,10 +144,10 @@ __device__ __forceinline__ bf16 out_cast<bf16>(float x) { return (bf16)x; }
 //
 // A "tile" is (segment b, tile index m) with m < ceil(L_b / TILE); zero-length
 // segments have none.  The planner validates cu_seqlens, then writes all tiles
-// ordered heaviest first: by m descending when `ascending_work` is false (the
-// forward, where q-tile m reads m+1 key tiles) or by (ntiles_b - 1 - m)
-// descending when it is true (the backward, where key tile m of segment b
-// visits ntiles_b - m query tiles), segments in order within a group.  Items
+// ordered by m descending, segments in order within a group.  That is heaviest
+// first for query tiles (query tile m visits m+1 key tiles); a kernel that
+// walks key tiles reads entry (b, m) as key tile ntiles_b - 1 - m, which visits
+// m+1 query tiles, so the same list is heaviest first for it too.  Items
 // are tile-major with the head fastest, so with H a multiple of 8 every item of
 // one head lands on the same XCD (workgroups are dealt to the 8 XCDs round
 // robin) and the key/value rows it re-reads stay in that XCD's L2.
@@ -90,7 +163,7 @@ struct PlanOut {
 };
 
 __global__ void __launch_bounds__(kPlanThreads)
-plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile, int backward,
+plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
                   int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status);
 
 // Host helpers (defined in attn_common.hip).
