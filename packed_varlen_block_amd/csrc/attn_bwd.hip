@@ -79,7 +79,12 @@ bwd_pre_kernel(const OT* __restrict__ o, const bf16* __restrict__ dout, const fl
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, typename GradT>
+// MODE selects what one launch accumulates: kBoth (dK and dV), kOnlyV or
+// kOnlyK.  Splitting trades one extra product (S is recomputed by both
+// passes) for register budgets that fit two waves per SIMD at d = 128.
+constexpr int kBoth = 0, kOnlyV = 1, kOnlyK = 2;
+
+template <int D, bool SPLIT, typename GradT, int MODE>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                const bf16* __restrict__ dout, const float2* __restrict__ ld,
@@ -89,10 +94,19 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   constexpr int BN = kTile, BM = kKvBM;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
+  constexpr int PB = (D + 8) * 2;                // padded row pitch (bytes)
+  constexpr int CP = D / 8 + 1;                  // 16-byte chunks per padded row
+  constexpr int CPT = (BM * CP + 63) / 64;       // wave-wide copies per tile
+  constexpr int NI = (2 * CPT + 3) / 4;          // copies per wave per stage (Q, dO, spare)
+  constexpr int TILE_BYTES = CPT * 1024;
+  constexpr int STAGE_BYTES = 4 * NI * 1024;
+  // NST-deep ring of query tiles: the copy of step t + NST - 1 is issued
+  // while step t is being used.
+  constexpr int NST = 2;
+  constexpr int COPIES = NI + 1;                 // + the {LSE, D} record copy
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][BM * D];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[2][BM * D];
-  __shared__ __attribute__((aligned(16))) float2 sLD[2][BM];
+  __shared__ __attribute__((aligned(1024))) char ring[NST][STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float2 sLD[NST][BM];
 
   const int tau = blockIdx.x / H;
   const int h = blockIdx.x - tau * H;
@@ -110,99 +124,150 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   const float2* lds_h = ld + (int64_t)h * T + seg0;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int kw0 = k0 + 32 * w;          // first key of this wave
   const int kcol = kw0 + lq;            // this lane's key column (local index)
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // per-lane byte offsets into a padded tile: row reads and transposed reads
+  const int a_off = pi32(lq) * PB + 16 * g;
+  const int t_off = (g + 4 * ((lane & 15) >> 2)) * PB + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
+  constexpr bool kWantK = MODE != kOnlyV, kWantV = MODE != kOnlyK;
   // K and V fragments (B operands of S = Q K^T and dP = dO V^T)
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  bf16x8 kf[KSTEPS], vf[kWantK ? KSTEPS : 1];
   if (kcol < L) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       kf[s] = *(const bf16x8*)(ks + kcol * rs + 16 * s + 8 * g);
-      vf[s] = *(const bf16x8*)(vs + kcol * rs + 16 * s + 8 * g);
+      if constexpr (kWantK) vf[s] = *(const bf16x8*)(vs + kcol * rs + 16 * s + 8 * g);
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) kf[s] = vf[s] = bf16x8{};
+    for (int s = 0; s < KSTEPS; ++s) {
+      kf[s] = bf16x8{};
+      if constexpr (kWantK) vf[s] = bf16x8{};
+    }
   }
 
-  // query tile jq -> buffer b: Q and dO rows plus their {LSE log2e, D} records
+  // the fragment loads must not be left in flight: the compiler would wait for
+  // them inside the loop with counts that also cover the asynchronous copies
+  wait_vmcnt<0>();
+
+  // where this lane's slot of each copy lands: tile row and 16-byte chunk
+  int c_row[NI], c_col[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = 4 * i + wu;                     // wave-wide copy index within the stage
+    const int p = 64 * (c % CPT) + lane;          // chunk within its tile
+    c_row[i] = min(p / CP, BM - 1);               // spare slots re-read a valid row
+    c_col[i] = min(p % CP, D / 8 - 1);            // the pad chunk of a row gets a copy of its last chunk
+  }
+  // query tile jq -> ring slot b: Q and dO rows plus their {LSE log2e, D}
+  // records; every wave issues COPIES copies (it moves a quarter of the records)
   auto stage = [&](int jq, int b) {
     const int qt0 = jq * BM;
-    stage_rows<D, BM>(qs, rs, qt0, L, sQ[b], w, lane);
-    stage_rows<D, BM>(gs, rs, qt0, L, sdO[b], w, lane);
-    if (w == 0)   // 64 dwords = BM records; rows past L are clamped like the tiles
-      copy_to_lds4(lds_h, (uint32_t)(min(qt0 + (lane >> 1), L - 1) * 8 + (lane & 1) * 4),
-                   lds_addr(sLD[b]));
+    const uint32_t sb = lds_addr(ring[b]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = 4 * i + wu;
+      const bf16* src = c >= CPT && c < 2 * CPT ? gs : qs;
+      const int grow = min(qt0 + c_row[i], L - 1);
+      copy_to_lds16(src, (uint32_t)(grow * rs + c_col[i] * 8) * 2u, sb + (uint32_t)c * 1024u);
+    }
+    if (lane < 2 * BM / 4) {
+      // records are stored in C-layout order: slot 16g + i holds the record
+      // of tile row crow32(i, g), so a lane's 16 records are contiguous
+      const int rec = (2 * BM / 4) * w + lane;   // dword index of the record block
+      const int slot = rec >> 1;
+      const int row = crow32(slot & 15, slot >> 4);
+      copy_to_lds4(lds_h, (uint32_t)(min(qt0 + row, L - 1) * 8 + (rec & 1) * 4),
+                   lds_addr(sLD[b]) + (uint32_t)(wu * (2 * BM / 4) * 4));
+    }
   };
 
-  f32x16 dkacc[DBLK], dvacc[DBLK];
+  f32x16 dkacc[kWantK ? DBLK : 1], dvacc[kWantV ? DBLK : 1];
 #pragma unroll
-  for (int j = 0; j < DBLK; ++j) dkacc[j] = dvacc[j] = f32x16{};
+  for (int j = 0; j < DBLK; ++j) {
+    if constexpr (kWantK) dkacc[j] = f32x16{};
+    if constexpr (kWantV) dvacc[j] = f32x16{};
+  }
 
-  const int jq0 = k0 / BM;
-  const int jq_end = (L + BM - 1) / BM;
-  stage(jq0, 0);
-  wait_vmcnt<0>();
-  for (int jq = jq0; jq < jq_end; ++jq) {
-    const int b = (jq - jq0) & 1;
-    const int qt0 = jq * BM;
+  const int jq_lo = k0 / BM;
+  const int n_steps = (L + BM - 1) / BM - jq_lo;
+  const int jq_hi = jq_lo + n_steps - 1;
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < n_steps) stage(jq_lo + i, i);
+  for (int t = 0; t < n_steps; ++t) {
+    const int b = t % NST;
+    const int qt0 = (jq_lo + t) * BM;
+    // this wave's copies of step t are done once at most the later steps' remain
+    if (t + NST - 2 < n_steps) wait_vmcnt<(NST - 2) * COPIES>();
+    else wait_vmcnt<0>();
+    // every wave's copies of step t have landed, and every wave is done with
+    // the slot of step t - 1, which now receives step t + NST - 1
     lds_barrier();
-    if (jq + 1 < jq_end) stage(jq + 1, b ^ 1);
-    const bf16* cQ = sQ[b];
-    const bf16* cdO = sdO[b];
+    if (t + NST - 1 < n_steps) stage(jq_lo + (t + NST - 1), (t + NST - 1) % NST);
+    const char* cQ = ring[b];
+    const char* cdO = ring[b] + TILE_BYTES;
     const float2* cLD = sLD[b];
 
-    // S = Q K^T and dP = dO V^T; element i is query qt0 + 8(i/4) + 4g + i%4
-    f32x16 sacc = mfma32(*(const bf16x8*)(cQ + swz<D>(lq, 8 * g)), kf[0], f32x16{});
-    f32x16 pacc = mfma32(*(const bf16x8*)(cdO + swz<D>(lq, 8 * g)), vf[0], f32x16{});
+    // S = Q K^T and dP = dO V^T; element i is query qt0 + crow32(i, g)
+    f32x16 sacc = mfma32(*(const bf16x8*)(cQ + a_off), kf[0], f32x16{});
+    f32x16 pacc;
+    if constexpr (kWantK) pacc = mfma32(*(const bf16x8*)(cdO + a_off), vf[0], f32x16{});
 #pragma unroll
     for (int s = 1; s < KSTEPS; ++s) {
-      sacc = mfma32(*(const bf16x8*)(cQ + swz<D>(lq, 16 * s + 8 * g)), kf[s], sacc);
-      pacc = mfma32(*(const bf16x8*)(cdO + swz<D>(lq, 16 * s + 8 * g)), vf[s], pacc);
+      sacc = mfma32(*(const bf16x8*)(cQ + a_off + 32 * s), kf[s], sacc);
+      if constexpr (kWantK) pacc = mfma32(*(const bf16x8*)(cdO + a_off + 32 * s), vf[s], pacc);
     }
     const bool need_mask = qt0 < kw0 + 31 || qt0 + BM > L || kw0 + 32 > L;
+    float4 rec[8];   // {LSE log2e, D} of the 16 queries of this lane's elements
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rec[k] = *(const float4*)(cLD + 16 * g + 2 * k);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int ql = 8 * (i >> 2) + 4 * g + (i & 3);
-      const float2 r = cLD[ql];
+      const int ql = crow32(i, g);
+      const float2 r = (i & 1) ? make_float2(rec[i >> 1].z, rec[i >> 1].w)
+                               : make_float2(rec[i >> 1].x, rec[i >> 1].y);
       float p = fast_exp2(sacc[i] * scale_log2 - r.x);
       if (need_mask && (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L)) p = 0.f;
       sacc[i] = p;
-      pacc[i] = p * (pacc[i] - r.y);
+      if constexpr (kWantK) pacc[i] = p * (pacc[i] - r.y);
     }
-    // dV += P^T dO and dK += dS^T Q.  k-slot 8g+e holds query 16kk + 8(e/4) + 4g + e%4.
+    // dV += P^T dO and dK += dS^T Q; k-slot 8g+e of step kk is tile row
+    // 16kk + 4(e&3) + 2(e>>2) + g, which the transposed reads fetch
 #pragma unroll
     for (int kk = 0; kk < BM / 16; ++kk) {
       bf16x8 ph, pl, sh, sl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = sacc[8 * kk + e];
-        const float ds = pacc[8 * kk + e];
-        ph[e] = (bf16)p;
-        sh[e] = (bf16)ds;
-        if constexpr (SPLIT) {
-          pl[e] = (bf16)(p - (float)ph[e]);
-          sl[e] = (bf16)(ds - (float)sh[e]);
+        if constexpr (kWantV) {
+          const float p = sacc[8 * kk + e];
+          ph[e] = (bf16)p;
+          if constexpr (SPLIT) pl[e] = (bf16)(p - (float)ph[e]);
+        }
+        if constexpr (kWantK) {
+          const float ds = pacc[8 * kk + e];
+          sh[e] = (bf16)ds;
+          if constexpr (SPLIT) sl[e] = (bf16)(ds - (float)sh[e]);
         }
       }
-      const int r0 = 16 * kk + 4 * g + tr_row;
 #pragma unroll
       for (int j = 0; j < DBLK; ++j) {
-        const int c = 32 * j + tr_col;
-        const bf16x8 dof = cat(lds_read_tr(cdO + swz<D>(r0, c)), lds_read_tr(cdO + swz<D>(r0 + 8, c)));
-        const bf16x8 qtf = cat(lds_read_tr(cQ + swz<D>(r0, c)), lds_read_tr(cQ + swz<D>(r0 + 8, c)));
-        dvacc[j] = mfma32(ph, dof, dvacc[j]);
-        dkacc[j] = mfma32(sh, qtf, dkacc[j]);
-        if constexpr (SPLIT) {
-          dvacc[j] = mfma32(pl, dof, dvacc[j]);
-          dkacc[j] = mfma32(sl, qtf, dkacc[j]);
+        const int o0 = t_off + 16 * kk * PB + 64 * j;
+        const int o1 = o0 + 2 * PB;
+        if constexpr (kWantV) {
+          const bf16x8 dof = cat(lds_read_tr((const bf16*)(cdO + o0)), lds_read_tr((const bf16*)(cdO + o1)));
+          dvacc[j] = mfma32(ph, dof, dvacc[j]);
+          if constexpr (SPLIT) dvacc[j] = mfma32(pl, dof, dvacc[j]);
+        }
+        if constexpr (kWantK) {
+          const bf16x8 qtf = cat(lds_read_tr((const bf16*)(cQ + o0)), lds_read_tr((const bf16*)(cQ + o1)));
+          dkacc[j] = mfma32(sh, qtf, dkacc[j]);
+          if constexpr (SPLIT) dkacc[j] = mfma32(sl, qtf, dkacc[j]);
         }
       }
     }
-    if (jq + 1 < jq_end) wait_vmcnt<0>();
   }
 
   // dK (scaled) and dV rows of this wave's keys
@@ -213,8 +278,8 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
       const int key = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
       if (key < L) {
         const int64_t off = base + (int64_t)key * rs + 32 * j + lq;
-        dk[off] = out_cast<GradT>(dkacc[j][i] * scale);
-        dv[off] = out_cast<GradT>(dvacc[j][i]);
+        if constexpr (kWantK) dk[off] = out_cast<GradT>(dkacc[j][i] * scale);
+        if constexpr (kWantV) dv[off] = out_cast<GradT>(dvacc[j][i]);
       }
     }
 }
@@ -386,9 +451,18 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   }
   const size_t grid = cap * (size_t)H;
   if (grid > 0) {
-    bwd_dkv_kernel<D, SPLIT, GradT><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count, H,
-        T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
+    if constexpr (D == 128) {
+      bwd_dkv_kernel<D, SPLIT, GradT, kOnlyV><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
+          H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
+      bwd_dkv_kernel<D, SPLIT, GradT, kOnlyK><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
+          H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
+    } else {
+      bwd_dkv_kernel<D, SPLIT, GradT, kBoth><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
+          H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
+    }
     bwd_dq_kernel<D, SPLIT, GradT><<<dim3((unsigned)grid), kThreads, 0, s>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count, H,
         T, scale, scale * kLog2e, (GradT*)dq);

@@ -125,6 +125,22 @@ __device__ __forceinline__ void stage_rows(const bf16* src, int rs, int row0, in
   }
 }
 
+// Padded LDS tiles.  Rows hold D + 8 bf16 (an odd number of 16-byte chunks),
+// and within every 32-row block the rows of an MFMA operand are permuted by
+// pi (row-index bits r4 r3 r2 r1 r0 -> r4 r1 r0 r3 r2).  With this layout
+//  * 16-byte row reads by 16 lanes from rows pi(0..15) (or pi(16..31)), and
+//  * transposed 8-byte reads by 32 lanes from rows b, b+4, b+8, b+12 (64 bytes each)
+// are free of bank conflicts, and every address is a per-lane base plus a
+// compile-time offset.  C-layout row r of a 32x32 MFMA result computed from
+// operand rows pi(0..31) is tile row pi(r), so element i of lane (g, .) sits
+// on tile row 16(i>>3) + 4(i&3) + 2((i>>2)&1) + g of its block, and the
+// k-slot 8g+e of a 16-deep step kk over those rows is tile row
+// 16kk + 4(e&3) + 2(e>>2) + g.
+__device__ __forceinline__ int pi32(int r) { return (r & 16) | ((r & 3) << 2) | ((r >> 2) & 3); }
+__host__ __device__ constexpr int crow32(int i, int g) {
+  return 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + g;
+}
+
 // s_waitcnt with only the vector-memory counter restricted: vmcnt <= n.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
