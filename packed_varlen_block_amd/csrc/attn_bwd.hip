@@ -106,7 +106,8 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   constexpr int COPIES = NI + 1;                 // + the {LSE, D} record copy
 
   __shared__ __attribute__((aligned(1024))) char ring[NST][STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) float2 sLD[NST][BM];
+  // per ring slot: LSE log2e of the BM rows, then their D, both in C-layout order
+  __shared__ __attribute__((aligned(16))) float sLD[NST][2 * BM];
 
   const int tau = blockIdx.x / H;
   const int h = blockIdx.x - tau * H;
@@ -125,7 +126,7 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int kw0 = k0 + 32 * w;          // first key of this wave
+  const int kw0 = k0 + 32 * wu;         // first key of this wave (wave-uniform)
   const int kcol = kw0 + lq;            // this lane's key column (local index)
   // per-lane byte offsets into a padded tile: row reads and transposed reads
   const int a_off = pi32(lq) * PB + 16 * g;
@@ -153,34 +154,52 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   wait_vmcnt<0>();
 
   // where this lane's slot of each copy lands: tile row and 16-byte chunk
-  int c_row[NI], c_col[NI];
+  int c_row[NI];
+  uint32_t c_off[NI];                             // byte offset of the slot's chunk in a full tile
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int c = 4 * i + wu;                     // wave-wide copy index within the stage
     const int p = 64 * (c % CPT) + lane;          // chunk within its tile
     c_row[i] = min(p / CP, BM - 1);               // spare slots re-read a valid row
-    c_col[i] = min(p % CP, D / 8 - 1);            // the pad chunk of a row gets a copy of its last chunk
+    const int col = min(p % CP, D / 8 - 1);       // the pad chunk of a row gets a copy of its last chunk
+    c_off[i] = (uint32_t)(c_row[i] * rs + col * 8) * 2u;
   }
+  // records are stored in C-layout order: dword j < BM holds the LSE of tile
+  // row crow32(j & 15, j >> 4), dword BM + j its D, so a lane's 16 values of
+  // either kind are contiguous
+  const int rec = (2 * BM / 4) * w + lane;        // dword index within the slot
+  const int rec_kind = rec >= BM ? 1 : 0;
+  const int rec_slot = rec - BM * rec_kind;
+  const int rec_row = crow32(rec_slot & 15, rec_slot >> 4);
+  const uint32_t rec_off = (uint32_t)(rec_row * 8 + rec_kind * 4);
   // query tile jq -> ring slot b: Q and dO rows plus their {LSE log2e, D}
   // records; every wave issues COPIES copies (it moves a quarter of the records)
   auto stage = [&](int jq, int b) {
     const int qt0 = jq * BM;
     const uint32_t sb = lds_addr(ring[b]);
+    const uint32_t lb = lds_addr(sLD[b]) + (uint32_t)(wu * (2 * BM / 4) * 4);
+    if (qt0 + BM <= L) {
+      // every row inside the segment: fixed per-lane offsets from a moving base
+      const bf16* q0p = qs + (int64_t)qt0 * rs;
+      const bf16* g0p = gs + (int64_t)qt0 * rs;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int c = 4 * i + wu;
-      const bf16* src = c >= CPT && c < 2 * CPT ? gs : qs;
-      const int grow = min(qt0 + c_row[i], L - 1);
-      copy_to_lds16(src, (uint32_t)(grow * rs + c_col[i] * 8) * 2u, sb + (uint32_t)c * 1024u);
-    }
-    if (lane < 2 * BM / 4) {
-      // records are stored in C-layout order: slot 16g + i holds the record
-      // of tile row crow32(i, g), so a lane's 16 records are contiguous
-      const int rec = (2 * BM / 4) * w + lane;   // dword index of the record block
-      const int slot = rec >> 1;
-      const int row = crow32(slot & 15, slot >> 4);
-      copy_to_lds4(lds_h, (uint32_t)(min(qt0 + row, L - 1) * 8 + (rec & 1) * 4),
-                   lds_addr(sLD[b]) + (uint32_t)(wu * (2 * BM / 4) * 4));
+      for (int i = 0; i < NI; ++i) {
+        const int c = 4 * i + wu;
+        copy_to_lds16(c >= CPT && c < 2 * CPT ? g0p : q0p, c_off[i], sb + (uint32_t)c * 1024u);
+      }
+      if (lane < 2 * BM / 4) copy_to_lds4(lds_h + qt0, rec_off, lb);
+    } else {
+      // ragged last tile: rows past the end re-read the segment's last row
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = 4 * i + wu;
+        const bf16* src = c >= CPT && c < 2 * CPT ? gs : qs;
+        const int grow = min(qt0 + c_row[i], L - 1);
+        const uint32_t col_bytes = c_off[i] - (uint32_t)(c_row[i] * rs) * 2u;
+        copy_to_lds16(src, (uint32_t)(grow * rs) * 2u + col_bytes, sb + (uint32_t)c * 1024u);
+      }
+      if (lane < 2 * BM / 4)
+        copy_to_lds4(lds_h, (uint32_t)(min(qt0 + rec_row, L - 1) * 8 + rec_kind * 4), lb);
     }
   };
 
@@ -209,30 +228,63 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     if (t + NST - 1 < n_steps) stage(jq_lo + (t + NST - 1), (t + NST - 1) % NST);
     const char* cQ = ring[b];
     const char* cdO = ring[b] + TILE_BYTES;
-    const float2* cLD = sLD[b];
+    const float* cLD = sLD[b];
 
-    // S = Q K^T and dP = dO V^T; element i is query qt0 + crow32(i, g)
-    f32x16 sacc = mfma32(*(const bf16x8*)(cQ + a_off), kf[0], f32x16{});
+    // S = Q K^T and dP = dO V^T; element i is query qt0 + crow32(i, g).
+    // The Q / dO operands are read kPf k-steps ahead of their MFMAs.
+    constexpr int R = kWantK ? 2 : 1;      // LDS operand reads per k-step
+    constexpr int kPf = 2;
+    bf16x8 qa[KSTEPS], ga[kWantK ? KSTEPS : 1];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      qa[s] = *(const bf16x8*)(cQ + a_off + 32 * s);
+      if constexpr (kWantK) ga[s] = *(const bf16x8*)(cdO + a_off + 32 * s);
+    }
+    float4 lsev[4], dv4[kWantK ? 4 : 1];   // LSE log2e and D of this lane's 16 queries
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lsev[k] = *(const float4*)(cLD + 16 * g + 4 * k);
+    if constexpr (kWantK) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dv4[k] = *(const float4*)(cLD + BM + 16 * g + 4 * k);
+    }
+    f32x16 sacc = mfma32(qa[0], kf[0], f32x16{});
     f32x16 pacc;
-    if constexpr (kWantK) pacc = mfma32(*(const bf16x8*)(cdO + a_off), vf[0], f32x16{});
+    if constexpr (kWantK) pacc = mfma32(ga[0], vf[0], f32x16{});
 #pragma unroll
     for (int s = 1; s < KSTEPS; ++s) {
-      sacc = mfma32(*(const bf16x8*)(cQ + a_off + 32 * s), kf[s], sacc);
-      if constexpr (kWantK) pacc = mfma32(*(const bf16x8*)(cdO + a_off + 32 * s), vf[s], pacc);
+      sacc = mfma32(qa[s], kf[s], sacc);
+      if constexpr (kWantK) pacc = mfma32(ga[s], vf[s], pacc);
     }
-    const bool need_mask = qt0 < kw0 + 31 || qt0 + BM > L || kw0 + 32 > L;
-    float4 rec[8];   // {LSE log2e, D} of the 16 queries of this lane's elements
+    // issue order: reads of steps 0..kPf, then per step its MFMAs followed by
+    // the reads of step s + kPf + 1; the record reads go in after step 3
+    __builtin_amdgcn_sched_group_barrier(0x100, R * (kPf + 1), 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) rec[k] = *(const float4*)(cLD + 16 * g + 2 * k);
+    for (int s = 0; s < KSTEPS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
+      if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+      if (s == 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (kWantK && s == 5) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    // wave-uniform: only tiles that cross the diagonal or an end are masked
+    const bool need_mask = qt0 < kw0 + 31 || qt0 + BM > L || kw0 + 32 > L;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int ql = crow32(i, g);
-      const float2 r = (i & 1) ? make_float2(rec[i >> 1].z, rec[i >> 1].w)
-                               : make_float2(rec[i >> 1].x, rec[i >> 1].y);
-      float p = fast_exp2(sacc[i] * scale_log2 - r.x);
-      if (need_mask && (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L)) p = 0.f;
-      sacc[i] = p;
-      if constexpr (kWantK) pacc[i] = p * (pacc[i] - r.y);
+      const float lse2 = lsev[i >> 2][i & 3];
+      sacc[i] = fast_exp2(sacc[i] * scale_log2 - lse2);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ql = crow32(i, g);
+        if (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L) sacc[i] = 0.f;
+      }
+    }
+    if constexpr (kWantK) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float dd = dv4[i >> 2][i & 3];
+        pacc[i] = sacc[i] * (pacc[i] - dd);
+      }
     }
     // dV += P^T dO and dK += dS^T Q; k-slot 8g+e of step kk is tile row
     // 16kk + 4(e&3) + 2(e>>2) + g, which the transposed reads fetch
@@ -315,9 +367,10 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
   const bf16* vs = v + base;
   const bf16* gs = dout + base;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qrow = q0 + 32 * w + lq;
-  const int wq_first = q0 + 32 * w;
+  const int wq_first = q0 + 32 * w;     // wave-uniform
   const int wq_last = min(wq_first + 31, L - 1);
   const bool wave_active = wq_first < L;
   const int tr_row = (lane & 15) >> 2;
@@ -343,46 +396,76 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 
   const int q_last = min(q0 + BM, L) - 1;
   const int nkv = q_last / BN + 1;
-  stage_rows<D, BN>(ks, rs, 0, L, sK[0], w, lane);
-  stage_rows<D, BN>(vs, rs, 0, L, sV[0], w, lane);
+  FullTileCopy<D, BN> full;
+  full.init(rs, w, lane);
+  auto stage = [&](int row0, int b) {
+    if (row0 + BN <= L) {
+      full.issue(ks, rs, row0, sK[b]);
+      full.issue(vs, rs, row0, sV[b]);
+    } else {
+      stage_rows<D, BN>(ks, rs, row0, L, sK[b], w, lane);
+      stage_rows<D, BN>(vs, rs, row0, L, sV[b], w, lane);
+    }
+  };
+  stage(0, 0);
   wait_vmcnt<0>();
   for (int n = 0; n < nkv; ++n) {
     const int b = n & 1;
     lds_barrier();
-    if (n + 1 < nkv) {
-      stage_rows<D, BN>(ks, rs, (n + 1) * BN, L, sK[b ^ 1], w, lane);
-      stage_rows<D, BN>(vs, rs, (n + 1) * BN, L, sV[b ^ 1], w, lane);
-    }
+    if (n + 1 < nkv) stage((n + 1) * BN, b ^ 1);
     const bf16* cK = sK[b];
     const bf16* cV = sV[b];
     const int key0 = n * BN;
     if (wave_active && key0 <= wq_last) {
-      // S^T = K Q^T and dP^T = V dO^T: each lane owns one query column
+      // S^T = K Q^T and dP^T = V dO^T: each lane owns one query column.  The
+      // K and V operands are read kPf k-steps ahead of their MFMAs.
+      constexpr int kPf = 1;
+      bf16x8 ka[KSTEPS][2], va[KSTEPS][2];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          ka[s][kb2] = *(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g));
+          va[s][kb2] = *(const bf16x8*)(cV + swz<D>(32 * kb2 + lq, 16 * s + 8 * g));
+        }
       f32x16 st[2], dpt[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        st[kb2] = mfma32(*(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 8 * g)), qf[0], f32x16{});
-        dpt[kb2] = mfma32(*(const bf16x8*)(cV + swz<D>(32 * kb2 + lq, 8 * g)), gf[0], f32x16{});
+        st[kb2] = mfma32(ka[0][kb2], qf[0], f32x16{});
+        dpt[kb2] = mfma32(va[0][kb2], gf[0], f32x16{});
       }
 #pragma unroll
       for (int s = 1; s < KSTEPS; ++s)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          st[kb2] = mfma32(*(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g)), qf[s], st[kb2]);
-          dpt[kb2] = mfma32(*(const bf16x8*)(cV + swz<D>(32 * kb2 + lq, 16 * s + 8 * g)), gf[s], dpt[kb2]);
+          st[kb2] = mfma32(ka[s][kb2], qf[s], st[kb2]);
+          dpt[kb2] = mfma32(va[s][kb2], gf[s], dpt[kb2]);
         }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * (kPf + 1), 0);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      // wave-uniform: only tiles that cross the diagonal or the end are masked
       const bool need_mask = key0 + BN - 1 > wq_first || key0 + BN > L;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(st[kb2][i] * scale_log2 - rl.x);
-          if (need_mask) {
+        for (int i = 0; i < 16; ++i) st[kb2][i] = fast_exp2(st[kb2][i] * scale_log2 - rl.x);
+      if (need_mask) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > qrow || key >= L) p = 0.f;
+            if (key > qrow || key >= L) st[kb2][i] = 0.f;
           }
-          st[kb2][i] = p * (dpt[kb2][i] - rl.y);
-        }
+      }
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kb2][i] *= dpt[kb2][i] - rl.y;
       // dQ^T += K^T dS^T.  k-slot 8g+e holds key 16kk + 8(e/4) + 4g + e%4.
 #pragma unroll
       for (int kk = 0; kk < BN / 16; ++kk) {

@@ -59,9 +59,10 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bf16* ks = k + base;
   const bf16* vs = v + base;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qrow = q0 + 32 * w + lq;     // this lane's query (local index)
-  const int wq_first = q0 + 32 * w;
+  const int wq_first = q0 + 32 * w;      // wave-uniform
   const int wq_last = min(wq_first + 31, L - 1);
   const bool wave_active = wq_first < L;
   const int tr_row = (lane & 15) >> 2;
@@ -84,32 +85,50 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int q_last = min(q0 + BM, L) - 1;
   const int nkv = q_last / BN + 1;
 
-  stage_rows<D, BN>(ks, rs, 0, L, sK[0], w, lane);
-  stage_rows<D, BN>(vs, rs, 0, L, sV[0], w, lane);
+  FullTileCopy<D, BN> full;
+  full.init(rs, w, lane);
+  auto stage = [&](int row0, int b) {
+    if (row0 + BN <= L) {
+      full.issue(ks, rs, row0, sK[b]);
+      full.issue(vs, rs, row0, sV[b]);
+    } else {
+      stage_rows<D, BN>(ks, rs, row0, L, sK[b], w, lane);
+      stage_rows<D, BN>(vs, rs, row0, L, sV[b], w, lane);
+    }
+  };
+  stage(0, 0);
   wait_vmcnt<0>();              // Q fragments and this wave's copies of tile 0
   for (int n = 0; n < nkv; ++n) {
     const int b = n & 1;
     // every wave's copies of tile n have landed, and every wave is done with
     // buffer b^1 (tile n-1), which now receives tile n+1
     lds_barrier();
-    if (n + 1 < nkv) {
-      stage_rows<D, BN>(ks, rs, (n + 1) * BN, L, sK[b ^ 1], w, lane);
-      stage_rows<D, BN>(vs, rs, (n + 1) * BN, L, sV[b ^ 1], w, lane);
-    }
+    if (n + 1 < nkv) stage((n + 1) * BN, b ^ 1);
     const bf16* cK = sK[b];
     const bf16* cV = sV[b];
     const int key0 = n * BN;
     if (wave_active && key0 <= wq_last) {
-      // S^T = K Q^T: two 32-key blocks
+      // S^T = K Q^T: two 32-key blocks.  The K operands are read kPf k-steps
+      // ahead of their MFMAs.
+      constexpr int kPf = 2;
+      bf16x8 ka[KSTEPS][2];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) ka[s][kb2] = *(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g));
       f32x16 st[2];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-        st[kb2] = mfma32(*(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 8 * g)), qf[0], f32x16{});
+      for (int kb2 = 0; kb2 < 2; ++kb2) st[kb2] = mfma32(ka[0][kb2], qf[0], f32x16{});
 #pragma unroll
       for (int s = 1; s < KSTEPS; ++s)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-          st[kb2] = mfma32(*(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g)), qf[s], st[kb2]);
+        for (int kb2 = 0; kb2 < 2; ++kb2) st[kb2] = mfma32(ka[s][kb2], qf[s], st[kb2]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kPf + 1), 0);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
       // mask: key > query, or key past the segment end
       if (key0 + BN - 1 > wq_first || key0 + BN > L) {
 #pragma unroll

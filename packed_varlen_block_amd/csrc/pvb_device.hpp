@@ -125,6 +125,35 @@ __device__ __forceinline__ void stage_rows(const bf16* src, int rs, int row0, in
   }
 }
 
+// The same copy pattern for a tile whose rows all lie inside the segment:
+// the per-lane byte offsets are computed once (init) and each call only moves
+// the wave-uniform source pointer, so a call costs no vector ALU work.
+template <int D, int ROWS>
+struct FullTileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int NI = ROWS / RPI / 4;
+  uint32_t voff[NI];
+  int wu;
+  __device__ __forceinline__ void init(int rs, int w, int lane) {
+    wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      const int row = (4 * r + wu) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swzf<D>(row);
+      voff[r] = (uint32_t)(row * rs + c * 8) * 2u;
+    }
+  }
+  // rows [row0, row0 + ROWS) of src (row stride rs), all < L
+  __device__ __forceinline__ void issue(const bf16* src, int rs, int row0, bf16* tile) const {
+    const bf16* s0 = src + (int64_t)row0 * rs;
+    const uint32_t tile_base = lds_addr(tile);
+#pragma unroll
+    for (int r = 0; r < NI; ++r)
+      copy_to_lds16(s0, voff[r], tile_base + (uint32_t)((4 * r + wu) * RPI * D * 2));
+  }
+};
+
 // Padded LDS tiles.  Rows hold D + 8 bf16 (an odd number of 16-byte chunks),
 // and within every 32-row block the rows of an MFMA operand are permuted by
 // pi (row-index bits r4 r3 r2 r1 r0 -> r4 r1 r0 r3 r2).  With this layout
