@@ -11,14 +11,14 @@
 //
 // Kernels (one planner list of 128-row tiles serves both main kernels):
 //   bwd_pre  {LSE log2(e), D = rowsum(dO * O)} per (token, head).
-//   bwd_dkv  one workgroup per (segment, 128-key tile, head).  Its 4 waves own
-//            32 keys each, with K and V fragments and the dK/dV accumulators in
-//            registers, and walk the 32-row query tiles from the diagonal to
-//            the segment end: S = Q K^T and dP = dO V^T (Q, dO copied
-//            global -> LDS into a double-buffered tile, the next one in flight
-//            during the math on the current one), P and dS in registers, then
-//            dV += P^T dO and dK += dS^T Q with the dO / Q fragments read
-//            transposed from LDS.
+//   bwd_kv_pair  one workgroup per (segment, 64-key half of a planner tile,
+//            head).  Wave pairs own 32 keys each and walk the 32-row query
+//            tiles from the diagonal to the segment end (Q, dO copied
+//            global -> LDS into a double-buffered ring, the next tile in flight
+//            during the math on the current one).  In a pair one wave forms
+//            S, P and dV += P^T dO, the other dP, dS = P (dP - D) with P
+//            handed over through LDS, and dK += dS^T Q; the second operands
+//            are read transposed from LDS.
 //   bwd_dq   one workgroup per (segment, 128-query tile, head), shaped like the
 //            forward: Q and dO fragments in registers, K and V tiles copied
 //            global -> LDS (double-buffered); S^T, dP^T and dS^T with each lane owning one query
@@ -33,8 +33,8 @@
 namespace pvb {
 namespace {
 
-constexpr int kTile = 128;       // rows per planner tile (keys for dkv, queries for dq)
-constexpr int kKvBM = 32;        // query rows per dkv step
+constexpr int kTile = 128;       // rows per planner tile (two 64-key halves for dK/dV, queries for dQ)
+constexpr int kKvBM = 32;        // query rows per dK/dV step
 constexpr int kDqBN = 64;        // keys per dq step
 constexpr int kThreads = 256;
 constexpr int kPreThreads = 256;
@@ -77,21 +77,25 @@ bwd_pre_kernel(const OT* __restrict__ o, const bf16* __restrict__ dout, const fl
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV
+// dK, dV with wave pairs
 // ---------------------------------------------------------------------------
-// MODE selects what one launch accumulates: kBoth (dK and dV), kOnlyV or
-// kOnlyK.  Splitting trades one extra product (S is recomputed by both
-// passes) for register budgets that fit two waves per SIMD at d = 128.
-constexpr int kBoth = 0, kOnlyV = 1, kOnlyK = 2;
-
-template <int D, bool SPLIT, typename GradT, int MODE>
-__global__ void __launch_bounds__(kThreads, 2)
-bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-               const bf16* __restrict__ dout, const float2* __restrict__ ld,
-               const int32_t* __restrict__ cu, const int2* __restrict__ tiles,
-               const int32_t* __restrict__ n_tiles, int H, int T, float scale, float scale_log2,
-               GradT* __restrict__ dk, GradT* __restrict__ dv) {
-  constexpr int BN = kTile, BM = kKvBM;
+// One workgroup per (segment, 64-key tile, head); waves 2p and 2p+1 form pair
+// p, owning keys k0 + 32p .. +31.  Per 32-row query step the even wave computes
+// S = Q K^T, P = exp2(S scale log2e - LSE log2e) and dV += P^T dO; the odd wave
+// computes dP = dO V^T, takes P from its partner through LDS, forms
+// dS = P (dP - D) and accumulates dK += dS^T Q.  Each matrix product over the
+// permitted (query, key) pairs is done once: S, dP, dV and dK, 16 MFMAs per
+// wave and step.  Both roles run the same instruction stream up to role
+// selects: first product A x (K or V fragment in registers) with A = Q or dO
+// rows from LDS, then (P or dS) x (dO or Q, read transposed from LDS).
+template <int D, bool SPLIT, typename GradT>
+__global__ void __launch_bounds__(kThreads, 3)
+bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                   const bf16* __restrict__ dout, const float2* __restrict__ ld,
+                   const int32_t* __restrict__ cu, const int2* __restrict__ tiles,
+                   const int32_t* __restrict__ n_tiles, int H, int T, float scale, float scale_log2,
+                   GradT* __restrict__ dk, GradT* __restrict__ dv) {
+  constexpr int BN = kTile / 2, BM = kKvBM;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int PB = (D + 8) * 2;                // padded row pitch (bytes)
@@ -100,86 +104,77 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   constexpr int NI = (2 * CPT + 3) / 4;          // copies per wave per stage (Q, dO, spare)
   constexpr int TILE_BYTES = CPT * 1024;
   constexpr int STAGE_BYTES = 4 * NI * 1024;
-  // NST-deep ring of query tiles: the copy of step t + NST - 1 is issued
-  // while step t is being used.
-  constexpr int NST = 2;
+  constexpr int NST = 2;                         // ring of query tiles
   constexpr int COPIES = NI + 1;                 // + the {LSE, D} record copy
 
   __shared__ __attribute__((aligned(1024))) char ring[NST][STAGE_BYTES];
   // per ring slot: LSE log2e of the BM rows, then their D, both in C-layout order
   __shared__ __attribute__((aligned(16))) float sLD[NST][2 * BM];
+  // P handed from the even to the odd wave of a pair: chunk j of lane l holds
+  // its elements 4j .. 4j+3 (same lane, same C-layout position in both waves)
+  __shared__ __attribute__((aligned(16))) float4 xbuf[2][4][64];
 
-  const int tau = blockIdx.x / H;
-  const int h = blockIdx.x - tau * H;
+  // work item: 128-key planner tile tau, its 64-key half, head h
+  const int tau = blockIdx.x / (2 * H);
+  const int rem = blockIdx.x - tau * 2 * H;
+  const int half = rem >= H ? 1 : 0;
+  const int h = rem - half * H;
   if (tau >= *n_tiles) return;
   const int2 tm = tiles[tau];
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
-  const int k0 = ((L + BN - 1) / BN - 1 - tm.y) * BN;   // key tiles mirror the query-tile list
+  const int k0 = ((L + kTile - 1) / kTile - 1 - tm.y) * kTile + BN * half;
+  if (k0 >= L) return;                                 // empty half of a ragged last tile
   const int rs = H * D;                                // row stride (elements)
   const int64_t base = ((int64_t)seg0 * H + h) * D;
   const bf16* qs = q + base;
-  const bf16* ks = k + base;
-  const bf16* vs = v + base;
   const bf16* gs = dout + base;
   const float2* lds_h = ld + (int64_t)h * T + seg0;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int kw0 = k0 + 32 * wu;         // first key of this wave (wave-uniform)
-  const int kcol = kw0 + lq;            // this lane's key column (local index)
-  // per-lane byte offsets into a padded tile: row reads and transposed reads
+  const int pair = wu >> 1, role = wu & 1;             // role 0: S, P, dV; role 1: dP, dS, dK
+  const int kw0 = k0 + 32 * pair;                      // first key of this pair (wave-uniform)
+  const int kcol = kw0 + lq;                           // this lane's key column (local index)
   const int a_off = pi32(lq) * PB + 16 * g;
   const int t_off = (g + 4 * ((lane & 15) >> 2)) * PB + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-  constexpr bool kWantK = MODE != kOnlyV, kWantV = MODE != kOnlyK;
-  // K and V fragments (B operands of S = Q K^T and dP = dO V^T)
-  bf16x8 kf[KSTEPS], vf[kWantK ? KSTEPS : 1];
+  // B operand of the first product: K rows (role 0) or V rows (role 1)
+  const bf16* fs = (role ? v : k) + base;
+  bf16x8 frag[KSTEPS];
   if (kcol < L) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      kf[s] = *(const bf16x8*)(ks + kcol * rs + 16 * s + 8 * g);
-      if constexpr (kWantK) vf[s] = *(const bf16x8*)(vs + kcol * rs + 16 * s + 8 * g);
-    }
+    for (int s = 0; s < KSTEPS; ++s) frag[s] = *(const bf16x8*)(fs + kcol * rs + 16 * s + 8 * g);
   } else {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      kf[s] = bf16x8{};
-      if constexpr (kWantK) vf[s] = bf16x8{};
-    }
+    for (int s = 0; s < KSTEPS; ++s) frag[s] = bf16x8{};
   }
-
   // the fragment loads must not be left in flight: the compiler would wait for
   // them inside the loop with counts that also cover the asynchronous copies
   wait_vmcnt<0>();
 
   // where this lane's slot of each copy lands: tile row and 16-byte chunk
-  int c_row[NI];
+  // (spare slots re-read a valid row; the pad chunk of a row gets a copy of
+  // its last chunk)
+  auto c_row = [&](int i) { return min((64 * ((4 * i + wu) % CPT) + lane) / CP, BM - 1); };
+  auto c_col = [&](int i) { return min((64 * ((4 * i + wu) % CPT) + lane) % CP, D / 8 - 1); };
   uint32_t c_off[NI];                             // byte offset of the slot's chunk in a full tile
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = 4 * i + wu;                     // wave-wide copy index within the stage
-    const int p = 64 * (c % CPT) + lane;          // chunk within its tile
-    c_row[i] = min(p / CP, BM - 1);               // spare slots re-read a valid row
-    const int col = min(p % CP, D / 8 - 1);       // the pad chunk of a row gets a copy of its last chunk
-    c_off[i] = (uint32_t)(c_row[i] * rs + col * 8) * 2u;
-  }
-  // records are stored in C-layout order: dword j < BM holds the LSE of tile
-  // row crow32(j & 15, j >> 4), dword BM + j its D, so a lane's 16 values of
-  // either kind are contiguous
-  const int rec = (2 * BM / 4) * w + lane;        // dword index within the slot
-  const int rec_kind = rec >= BM ? 1 : 0;
-  const int rec_slot = rec - BM * rec_kind;
-  const int rec_row = crow32(rec_slot & 15, rec_slot >> 4);
-  const uint32_t rec_off = (uint32_t)(rec_row * 8 + rec_kind * 4);
-  // query tile jq -> ring slot b: Q and dO rows plus their {LSE log2e, D}
-  // records; every wave issues COPIES copies (it moves a quarter of the records)
+  for (int i = 0; i < NI; ++i) c_off[i] = (uint32_t)(c_row(i) * rs + c_col(i) * 8) * 2u;
+  // records in C-layout order: dword j < BM holds the LSE of tile row
+  // crow32(j & 15, j >> 4), dword BM + j its D
+  auto rec_row = [&]() {
+    const int rec = (2 * BM / 4) * w + lane;
+    const int slot = rec - (rec >= BM ? BM : 0);
+    return crow32(slot & 15, slot >> 4);
+  };
+  const int rec_kind = (2 * BM / 4) * w + lane >= BM ? 1 : 0;
+  const uint32_t rec_off = (uint32_t)(rec_row() * 8 + rec_kind * 4);
   auto stage = [&](int jq, int b) {
     const int qt0 = jq * BM;
     const uint32_t sb = lds_addr(ring[b]);
     const uint32_t lb = lds_addr(sLD[b]) + (uint32_t)(wu * (2 * BM / 4) * 4);
     if (qt0 + BM <= L) {
-      // every row inside the segment: fixed per-lane offsets from a moving base
       const bf16* q0p = qs + (int64_t)qt0 * rs;
       const bf16* g0p = gs + (int64_t)qt0 * rs;
 #pragma unroll
@@ -194,145 +189,116 @@ bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
       for (int i = 0; i < NI; ++i) {
         const int c = 4 * i + wu;
         const bf16* src = c >= CPT && c < 2 * CPT ? gs : qs;
-        const int grow = min(qt0 + c_row[i], L - 1);
-        const uint32_t col_bytes = c_off[i] - (uint32_t)(c_row[i] * rs) * 2u;
-        copy_to_lds16(src, (uint32_t)(grow * rs) * 2u + col_bytes, sb + (uint32_t)c * 1024u);
+        const int grow = min(qt0 + c_row(i), L - 1);
+        copy_to_lds16(src, (uint32_t)(grow * rs + c_col(i) * 8) * 2u, sb + (uint32_t)c * 1024u);
       }
       if (lane < 2 * BM / 4)
-        copy_to_lds4(lds_h, (uint32_t)(min(qt0 + rec_row, L - 1) * 8 + rec_kind * 4), lb);
+        copy_to_lds4(lds_h, (uint32_t)(min(qt0 + rec_row(), L - 1) * 8 + rec_kind * 4), lb);
     }
   };
 
-  f32x16 dkacc[kWantK ? DBLK : 1], dvacc[kWantV ? DBLK : 1];
+  f32x16 acc2[DBLK];
 #pragma unroll
-  for (int j = 0; j < DBLK; ++j) {
-    if constexpr (kWantK) dkacc[j] = f32x16{};
-    if constexpr (kWantV) dvacc[j] = f32x16{};
-  }
+  for (int j = 0; j < DBLK; ++j) acc2[j] = f32x16{};
+  float4* xb = xbuf[pair][0];
 
   const int jq_lo = k0 / BM;
   const int n_steps = (L + BM - 1) / BM - jq_lo;
-  const int jq_hi = jq_lo + n_steps - 1;
 #pragma unroll
   for (int i = 0; i < NST - 1; ++i)
     if (i < n_steps) stage(jq_lo + i, i);
   for (int t = 0; t < n_steps; ++t) {
     const int b = t % NST;
     const int qt0 = (jq_lo + t) * BM;
-    // this wave's copies of step t are done once at most the later steps' remain
     if (t + NST - 2 < n_steps) wait_vmcnt<(NST - 2) * COPIES>();
     else wait_vmcnt<0>();
-    // every wave's copies of step t have landed, and every wave is done with
-    // the slot of step t - 1, which now receives step t + NST - 1
+    // every wave's copies of step t have landed, every wave is done with the
+    // slot of step t - 1 (which now receives step t + NST - 1), and the odd
+    // waves are done reading the P of step t - 1
     lds_barrier();
     if (t + NST - 1 < n_steps) stage(jq_lo + (t + NST - 1), (t + NST - 1) % NST);
     const char* cQ = ring[b];
     const char* cdO = ring[b] + TILE_BYTES;
-    const float* cLD = sLD[b];
+    const char* a_src = role ? cdO : cQ;         // rows of the first product
+    const char* t_src = role ? cQ : cdO;         // transposed operand of the second
+    const float* cLD = sLD[b] + role * BM;       // LSE (role 0) or D (role 1)
 
-    // S = Q K^T and dP = dO V^T; element i is query qt0 + crow32(i, g).
-    // The Q / dO operands are read kPf k-steps ahead of their MFMAs.
-    constexpr int R = kWantK ? 2 : 1;      // LDS operand reads per k-step
-    constexpr int kPf = 2;
-    bf16x8 qa[KSTEPS], ga[kWantK ? KSTEPS : 1];
+    // S (role 0) or dP (role 1); element i is query qt0 + crow32(i, g).
+    // Operands are read three k-steps ahead of their MFMAs.
+    bf16x8 aa[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) aa[s] = *(const bf16x8*)(a_src + a_off + 32 * s);
+    f32x16 acc = mfma32(aa[0], frag[0], f32x16{});
+#pragma unroll
+    for (int s = 1; s < KSTEPS; ++s) acc = mfma32(aa[s], frag[s], acc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      qa[s] = *(const bf16x8*)(cQ + a_off + 32 * s);
-      if constexpr (kWantK) ga[s] = *(const bf16x8*)(cdO + a_off + 32 * s);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s + 3 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    float4 lsev[4], dv4[kWantK ? 4 : 1];   // LSE log2e and D of this lane's 16 queries
+    float4 rv[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) lsev[k] = *(const float4*)(cLD + 16 * g + 4 * k);
-    if constexpr (kWantK) {
+    for (int kq = 0; kq < 4; ++kq) rv[kq] = *(const float4*)(cLD + 16 * g + 4 * kq);
+
+    if (role == 0) {
+      // P, zero outside the causal ranges; handed to the partner
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dv4[k] = *(const float4*)(cLD + BM + 16 * g + 4 * k);
+      for (int i = 0; i < 16; ++i) acc[i] = fast_exp2(acc[i] * scale_log2 - rv[i >> 2][i & 3]);
+      // wave-uniform: only tiles that cross the diagonal or an end are masked
+      if (qt0 < kw0 + 31 || qt0 + BM > L || kw0 + 32 > L) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = crow32(i, g);
+          if (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L) acc[i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xb[64 * j + lane] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
     }
-    f32x16 sacc = mfma32(qa[0], kf[0], f32x16{});
-    f32x16 pacc;
-    if constexpr (kWantK) pacc = mfma32(ga[0], vf[0], f32x16{});
+    lds_barrier();                               // P of this step is visible to the odd waves
+    if (role == 1) {
+      // dS = P (dP - D)
 #pragma unroll
-    for (int s = 1; s < KSTEPS; ++s) {
-      sacc = mfma32(qa[s], kf[s], sacc);
-      if constexpr (kWantK) pacc = mfma32(ga[s], vf[s], pacc);
-    }
-    // issue order: reads of steps 0..kPf, then per step its MFMAs followed by
-    // the reads of step s + kPf + 1; the record reads go in after step 3
-    __builtin_amdgcn_sched_group_barrier(0x100, R * (kPf + 1), 0);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
-      if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-      if (s == 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      if (kWantK && s == 5) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    }
-    // wave-uniform: only tiles that cross the diagonal or an end are masked
-    const bool need_mask = qt0 < kw0 + 31 || qt0 + BM > L || kw0 + 32 > L;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float lse2 = lsev[i >> 2][i & 3];
-      sacc[i] = fast_exp2(sacc[i] * scale_log2 - lse2);
-    }
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ql = crow32(i, g);
-        if (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L) sacc[i] = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const float4 p4 = xb[64 * j + lane];
+        acc[4 * j] = p4.x * (acc[4 * j] - rv[j].x);
+        acc[4 * j + 1] = p4.y * (acc[4 * j + 1] - rv[j].y);
+        acc[4 * j + 2] = p4.z * (acc[4 * j + 2] - rv[j].z);
+        acc[4 * j + 3] = p4.w * (acc[4 * j + 3] - rv[j].w);
       }
     }
-    if constexpr (kWantK) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float dd = dv4[i >> 2][i & 3];
-        pacc[i] = sacc[i] * (pacc[i] - dd);
-      }
-    }
-    // dV += P^T dO and dK += dS^T Q; k-slot 8g+e of step kk is tile row
-    // 16kk + 4(e&3) + 2(e>>2) + g, which the transposed reads fetch
+    // dV += P^T dO (role 0) or dK += dS^T Q (role 1); k-slot 8g+e of step kk
+    // is tile row 16kk + 4(e&3) + 2(e>>2) + g, which the transposed reads fetch
 #pragma unroll
     for (int kk = 0; kk < BM / 16; ++kk) {
-      bf16x8 ph, pl, sh, sl;
+      bf16x8 xh, xl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if constexpr (kWantV) {
-          const float p = sacc[8 * kk + e];
-          ph[e] = (bf16)p;
-          if constexpr (SPLIT) pl[e] = (bf16)(p - (float)ph[e]);
-        }
-        if constexpr (kWantK) {
-          const float ds = pacc[8 * kk + e];
-          sh[e] = (bf16)ds;
-          if constexpr (SPLIT) sl[e] = (bf16)(ds - (float)sh[e]);
-        }
+        const float x = acc[8 * kk + e];
+        xh[e] = (bf16)x;
+        if constexpr (SPLIT) xl[e] = (bf16)(x - (float)xh[e]);
       }
 #pragma unroll
       for (int j = 0; j < DBLK; ++j) {
         const int o0 = t_off + 16 * kk * PB + 64 * j;
-        const int o1 = o0 + 2 * PB;
-        if constexpr (kWantV) {
-          const bf16x8 dof = cat(lds_read_tr((const bf16*)(cdO + o0)), lds_read_tr((const bf16*)(cdO + o1)));
-          dvacc[j] = mfma32(ph, dof, dvacc[j]);
-          if constexpr (SPLIT) dvacc[j] = mfma32(pl, dof, dvacc[j]);
-        }
-        if constexpr (kWantK) {
-          const bf16x8 qtf = cat(lds_read_tr((const bf16*)(cQ + o0)), lds_read_tr((const bf16*)(cQ + o1)));
-          dkacc[j] = mfma32(sh, qtf, dkacc[j]);
-          if constexpr (SPLIT) dkacc[j] = mfma32(sl, qtf, dkacc[j]);
-        }
+        const bf16x8 tf = cat(lds_read_tr((const bf16*)(t_src + o0)), lds_read_tr((const bf16*)(t_src + o0 + 2 * PB)));
+        acc2[j] = mfma32(xh, tf, acc2[j]);
+        if constexpr (SPLIT) acc2[j] = mfma32(xl, tf, acc2[j]);
       }
     }
   }
 
-  // dK (scaled) and dV rows of this wave's keys
+  // dV (role 0) or scaled dK (role 1) rows of this pair's keys
+  GradT* outp = role ? dk : dv;
+  const float oscale = role ? scale : 1.f;
 #pragma unroll
   for (int j = 0; j < DBLK; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key < L) {
-        const int64_t off = base + (int64_t)key * rs + 32 * j + lq;
-        if constexpr (kWantK) dk[off] = out_cast<GradT>(dkacc[j][i] * scale);
-        if constexpr (kWantV) dv[off] = out_cast<GradT>(dvacc[j][i]);
-      }
+      if (key < L) outp[base + (int64_t)key * rs + 32 * j + lq] = out_cast<GradT>(acc2[j][i] * oscale);
     }
 }
 
@@ -534,18 +500,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   }
   const size_t grid = cap * (size_t)H;
   if (grid > 0) {
-    if constexpr (D == 128) {
-      bwd_dkv_kernel<D, SPLIT, GradT, kOnlyV><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
-          H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
-      bwd_dkv_kernel<D, SPLIT, GradT, kOnlyK><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
-          H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
-    } else {
-      bwd_dkv_kernel<D, SPLIT, GradT, kBoth><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
-          H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
-    }
+    bwd_kv_pair_kernel<D, SPLIT, GradT><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
+        H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
     bwd_dq_kernel<D, SPLIT, GradT><<<dim3((unsigned)grid), kThreads, 0, s>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count, H,
         T, scale, scale * kLog2e, (GradT*)dq);
@@ -583,7 +540,7 @@ extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, cons
   if (d != 64 && d != 128) return PVB_E_UNSUPPORTED;
   if ((int64_t)T * H * d >= ((int64_t)1 << 31)) return PVB_E_UNSUPPORTED;
   const size_t cap = plan_capacity(T, n_seg, kTile);
-  if (cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
+  if (2 * cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
   const BwdLayout lay = bwd_layout(T, H, n_seg);
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
