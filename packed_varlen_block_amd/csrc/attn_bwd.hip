@@ -45,7 +45,7 @@ template <int D, typename OT>
 __global__ void __launch_bounds__(kPreThreads)
 bwd_pre_kernel(const OT* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
                int rows, int H, int T, float2* __restrict__ ld, const int32_t* __restrict__ status) {
-  if (*status != PVB_OK) return;
+  if (status != nullptr && *status != PVB_OK) return;
   constexpr int TPR = D / 8;                     // threads per (token, head) row
   constexpr int RPB = kPreThreads / TPR;         // rows per block
   const int r = blockIdx.x * RPB + threadIdx.x / TPR;
@@ -88,13 +88,12 @@ bwd_pre_kernel(const OT* __restrict__ o, const bf16* __restrict__ dout, const fl
 // wave and step.  Both roles run the same instruction stream up to role
 // selects: first product A x (K or V fragment in registers) with A = Q or dO
 // rows from LDS, then (P or dS) x (dO or Q, read transposed from LDS).
-template <int D, bool SPLIT, typename GradT>
+template <int D, bool SPLIT, typename GradT, bool DECODE>
 __global__ void __launch_bounds__(kThreads, 3)
 bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const bf16* __restrict__ dout, const float2* __restrict__ ld,
-                   const int32_t* __restrict__ cu, const int2* __restrict__ tiles,
-                   const int32_t* __restrict__ n_tiles, int H, int T, float scale, float scale_log2,
-                   GradT* __restrict__ dk, GradT* __restrict__ dv) {
+                   const int32_t* __restrict__ cu, const WorkList wl, int H, int T, float scale,
+                   float scale_log2, GradT* __restrict__ dk, GradT* __restrict__ dv) {
   constexpr int BN = kTile / 2, BM = kKvBM;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -119,8 +118,8 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   const int rem = blockIdx.x - tau * 2 * H;
   const int half = rem >= H ? 1 : 0;
   const int h = rem - half * H;
-  if (tau >= *n_tiles) return;
-  const int2 tm = tiles[tau];
+  int2 tm;
+  if (!work_item<kTile, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int k0 = ((L + kTile - 1) / kTile - 1 - tm.y) * kTile + BN * half;
@@ -305,13 +304,12 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, typename GradT>
+template <int D, bool SPLIT, typename GradT, bool DECODE>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const float2* __restrict__ ld,
-              const int32_t* __restrict__ cu, const int2* __restrict__ tiles,
-              const int32_t* __restrict__ n_tiles, int H, int T, float scale, float scale_log2,
-              GradT* __restrict__ dq) {
+              const int32_t* __restrict__ cu, const WorkList wl, int H, int T, float scale,
+              float scale_log2, GradT* __restrict__ dq) {
   constexpr int BM = kTile, BN = kDqBN;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -321,8 +319,8 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 
   const int tau = blockIdx.x / H;
   const int h = blockIdx.x - tau * H;
-  if (tau >= *n_tiles) return;
-  const int2 tm = tiles[tau];
+  int2 tm;
+  if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int q0 = tm.y * BM;
@@ -489,23 +487,32 @@ BwdLayout bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
 
 template <int D, bool SPLIT, typename GradT, typename OT>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, const int32_t* cu, const int2* tiles, const int32_t* count,
-                      int H, int T, size_t cap, float scale, float2* ld, void* dq, void* dk,
-                      void* dv, const int32_t* status, hipStream_t s) {
+                      const float* lse, const int32_t* cu, const WorkList& wl, int H, int T,
+                      size_t cap, float scale, float2* ld, void* dq, void* dk, void* dv,
+                      hipStream_t s) {
   const int rows = T * H;
   if (rows > 0) {
     constexpr int RPB = kPreThreads / (D / 8);
     bwd_pre_kernel<D, OT><<<(rows + RPB - 1) / RPB, kPreThreads, 0, s>>>(
-        (const OT*)o, (const bf16*)dout, lse, rows, H, T, ld, status);
+        (const OT*)o, (const bf16*)dout, lse, rows, H, T, ld, wl.tiles != nullptr ? wl.status : nullptr);
   }
   const size_t grid = cap * (size_t)H;
   if (grid > 0) {
-    bwd_kv_pair_kernel<D, SPLIT, GradT><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count,
-        H, T, scale, scale * kLog2e, (GradT*)dk, (GradT*)dv);
-    bwd_dq_kernel<D, SPLIT, GradT><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, tiles, count, H,
-        T, scale, scale * kLog2e, (GradT*)dq);
+    if (wl.tiles == nullptr) {
+      bwd_kv_pair_kernel<D, SPLIT, GradT, true><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
+          scale * kLog2e, (GradT*)dk, (GradT*)dv);
+      bwd_dq_kernel<D, SPLIT, GradT, true><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
+          scale * kLog2e, (GradT*)dq);
+    } else {
+      bwd_kv_pair_kernel<D, SPLIT, GradT, false><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
+          scale * kLog2e, (GradT*)dk, (GradT*)dv);
+      bwd_dq_kernel<D, SPLIT, GradT, false><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
+          scale * kLog2e, (GradT*)dq);
+    }
   }
   return hipGetLastError();
 }
@@ -551,14 +558,20 @@ extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, cons
   int32_t* count = reinterpret_cast<int32_t*>(ws);
   int2* tiles = reinterpret_cast<int2*>(ws + lay.tiles_off);
   float2* ld = reinterpret_cast<float2*>(ws + lay.ld_off);
-  plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kTile, tiles, count, d_status);
-  if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  // small packs: the main kernels decode their items themselves (and write the
+  // status); otherwise the planner writes the list and the status first
+  const bool dec = decode_in_kernel(T, n_seg, kTile, cap * (size_t)H);
+  if (!dec) {
+    plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kTile, tiles, count, d_status);
+    if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  }
+  const WorkList wl{dec ? nullptr : tiles, count, n_seg, d_status};
 
   const bool split = precision == PVB_PREC_SPLIT, gf32 = grad_dtype == PVB_F32, of32 = o_dtype == PVB_F32;
   hipError_t e = hipSuccess;
 #define PVB_BWD(D_, S_, G_, O_)                                                                    \
-  e = launch_bwd<D_, S_, G_, O_>(d_q, d_k, d_v, d_o, d_do, d_lse, d_cu, tiles, count, H, T, cap, \
-                                 softmax_scale, ld, d_dq, d_dk, d_dv, d_status, s)
+  e = launch_bwd<D_, S_, G_, O_>(d_q, d_k, d_v, d_o, d_do, d_lse, d_cu, wl, H, T, cap,          \
+                                 softmax_scale, ld, d_dq, d_dk, d_dv, s)
 #define PVB_BWD_O(D_, S_, G_) \
   if (of32) PVB_BWD(D_, S_, G_, float); else PVB_BWD(D_, S_, G_, bf16)
 #define PVB_BWD_G(D_, S_) \

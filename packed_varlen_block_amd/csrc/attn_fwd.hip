@@ -29,11 +29,11 @@ constexpr int kFwdBM = 128;   // query rows per work item
 constexpr int kFwdBN = 64;    // keys per K/V tile
 constexpr int kFwdThreads = 256;
 
-template <int D, bool SPLIT, typename OutT>
+template <int D, bool SPLIT, typename OutT, bool DECODE>
 __global__ void __launch_bounds__(kFwdThreads, 2)
 attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const bf16* __restrict__ v, const int32_t* __restrict__ cu,
-                const int2* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int H, int T,
+                const WorkList wl, int H, int T,
                 float scale_log2, OutT* __restrict__ o, float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
@@ -48,8 +48,8 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const int tau = blockIdx.x / H;
   const int h = blockIdx.x - tau * H;
-  if (tau >= *n_tiles) return;
-  const int2 tm = tiles[tau];
+  int2 tm;
+  if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int q0 = tm.y * BM;
@@ -215,13 +215,16 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
-                      const int2* tiles, const int32_t* count, int H, int T, size_t cap,
-                      float scale_log2, void* o, float* lse, hipStream_t s) {
+                      const WorkList& wl, int H, int T, size_t cap, float scale_log2, void* o,
+                      float* lse, hipStream_t s) {
   const size_t grid = cap * (size_t)H;
   if (grid == 0) return hipSuccess;
-  attn_fwd_kernel<D, SPLIT, OutT><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, tiles, count, H, T, scale_log2,
-      (OutT*)o, lse);
+  if (wl.tiles == nullptr)
+    attn_fwd_kernel<D, SPLIT, OutT, true><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
+  else
+    attn_fwd_kernel<D, SPLIT, OutT, false><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
   return hipGetLastError();
 }
 
@@ -259,14 +262,20 @@ extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* count = static_cast<int32_t*>(workspace);
   int2* tiles = reinterpret_cast<int2*>(static_cast<char*>(workspace) + 256);
-  plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kFwdBM, tiles, count, d_status);
-  if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  // small packs: the attention kernel decodes its items itself; otherwise
+  // the planner writes the list (and the status) first
+  const bool dec = decode_in_kernel(T, n_seg, kFwdBM, cap * (size_t)H);
+  if (!dec) {
+    plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kFwdBM, tiles, count, d_status);
+    if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  }
+  const WorkList wl{dec ? nullptr : tiles, count, n_seg, d_status};
 
   const float sl2 = softmax_scale * kLog2e;
   const bool split = precision == PVB_PREC_SPLIT, f32 = o_dtype == PVB_F32;
   hipError_t e;
 #define PVB_FWD(D_, S_, T_) \
-  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, tiles, count, H, T, cap, sl2, d_o, d_lse, s)
+  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, T, cap, sl2, d_o, d_lse, s)
   if (d == 128) {
     if (split) { if (f32) PVB_FWD(128, true, float); else PVB_FWD(128, true, bf16); }
     else { if (f32) PVB_FWD(128, false, float); else PVB_FWD(128, false, bf16); }

@@ -215,4 +215,125 @@ plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
 size_t plan_capacity(int32_t T, int32_t n_seg, int32_t tile);
 pvb_status check_host_cu(const int32_t* h_cu, int32_t n_seg, int32_t T);
 
+// ---------------------------------------------------------------------------
+// In-kernel work-item decode.
+//
+// For packs of at most kDecodeMaxSeg segments of at most kDecodeMaxM tiles,
+// every wave derives its workgroup's item of the planner's list (same order:
+// tile index descending, segments in order) straight from cu_seqlens, which
+// saves the planner launch and the dependency on it.  The waves of a
+// workgroup compute the same result independently, with no LDS and no
+// barrier.  With nt_b the tile count of segment b, the items of tile index
+// m' >= m number S(m) = sum_b max(0, nt_b - m), so the group of item r is the
+// largest m with S(m) > r (binary search), and within it the item is the
+// (r - S(m+1))-th segment, in order, with nt_b > m.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeMaxM = 256;
+constexpr int kDecodeMaxSeg = 256;
+
+// Work list handed to the attention kernels: the planner's output, or
+// tiles == nullptr when each workgroup decodes its item.
+struct WorkList {
+  const int2* tiles;
+  const int32_t* count;
+  int32_t n_seg;
+  int32_t* status;
+};
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+// Item r of the heavy-first list of (segment, TILE-row tile) pairs.  The
+// result is wave-uniform and the same in every wave.  Returns false when there
+// is no item r or cu_seqlens is invalid; workgroup 0 then, and on success,
+// writes the status word.
+template <int TILE>
+__device__ bool decode_work_item(const int32_t* __restrict__ cu, int n_seg, int T, int r, int2* item,
+                                 int32_t* __restrict__ status) {
+  constexpr int J = kDecodeMaxSeg / 64;       // segments per lane
+  const int lane = threadIdx.x & 63;
+  int nt[J];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int b = 64 * j + lane;
+    nt[j] = 0;
+    if (b < n_seg) {
+      const int a = cu[b], c = cu[b + 1];
+      if (c < a) bad = true;
+      else nt[j] = (int)min(((int64_t)c - a + TILE - 1) / TILE, (int64_t)kDecodeMaxM + 1);
+    }
+  }
+  if (lane == 0 && (cu[0] != 0 || cu[n_seg] != T)) bad = true;
+  int M = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) M = max(M, nt[j]);
+  M = __builtin_amdgcn_readfirstlane(wave_max(M));
+  const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    *status = any_bad ? PVB_E_BAD_CU_SEQLENS : M > kDecodeMaxM ? PVB_E_UNSUPPORTED : PVB_OK;
+  if (any_bad || M > kDecodeMaxM) return false;
+  auto S = [&](int m) {
+    int x = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) x += max(0, nt[j] - m);
+    return __builtin_amdgcn_readfirstlane(wave_sum(x));
+  };
+  if (r >= S(0)) return false;
+  int lo = 0, hi = M - 1;                       // S(lo) > r holds throughout
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S(mid) > r) lo = mid;
+    else hi = mid - 1;
+  }
+  int k = r - S(lo + 1);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(nt[j] > lo);
+    const int cnt = __builtin_popcountll(mask);
+    if (k < cnt) {
+      uint64_t mm = mask;
+      for (int i = 0; i < k; ++i) mm &= mm - 1;   // drop the k lowest set bits
+      // the values are the same in every lane; say so to the compiler, so
+      // that what derives from them stays in scalar registers
+      *item = make_int2(__builtin_amdgcn_readfirstlane(64 * j + __builtin_ctzll(mm)),
+                        __builtin_amdgcn_readfirstlane(lo));
+      return true;
+    }
+    k -= cnt;
+  }
+  return false;                                  // not reached
+}
+
+// The item of workgroup tau: from the planner list, or decoded in place.
+template <int TILE, bool DECODE>
+__device__ __forceinline__ bool work_item(const WorkList& wl, const int32_t* __restrict__ cu, int T, int tau,
+                                          int2* item) {
+  if constexpr (DECODE) {
+    return decode_work_item<TILE>(cu, wl.n_seg, T, tau, item, wl.status);
+  } else {
+    if (tau >= *wl.count) return false;
+    *item = wl.tiles[tau];
+    return true;
+  }
+}
+
+// Whether a launch of this shape decodes its items in place: only small
+// launches, where the planner's launch and the dependency on it are a
+// noticeable share of the call (measured: 20 us of a 60 us short-pack call,
+// against 1% extra on a 2048-workgroup launch).
+constexpr size_t kDecodeMaxGrid = 1024;
+inline bool decode_in_kernel(int32_t T, int32_t n_seg, int32_t tile, size_t grid) {
+  return grid > 0 && grid <= kDecodeMaxGrid && n_seg <= kDecodeMaxSeg &&
+         ((int64_t)T + tile - 1) / tile <= kDecodeMaxM;
+}
+
 }  // namespace pvb

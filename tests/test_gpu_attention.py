@@ -163,3 +163,46 @@ def test_backward_dk_dv_deterministic():
     b = gpu_bwd(dev, o, lse, w, "f32")
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
     assert torch.allclose(a[0], b[0], atol=1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_planner_path_many_segments(d):
+    # More than 1024 segments: the work list comes from the one-workgroup
+    # planner instead of the in-kernel decode used for smaller packs.
+    rng = np.random.default_rng(1234 + d)
+    lengths = rng.integers(0, 25, size=1100).tolist()
+    lengths[5] = 300                      # one segment spanning several tiles
+    say(f"planner path: {len(lengths)} segments, T={sum(lengths)}, d={d}")
+    w = W.random_small(13, lengths, H=2, d=d, backward=True)
+    dev, o, lse = gpu_fwd(w, "bf16")
+    compare_fwd(w, o, lse, tag="planner path ")
+    dq, dk, dv = gpu_bwd(dev, o, lse, w, "f32")
+    compare_bwd(w, dq, dk, dv, tag="planner path ")
+
+
+def test_bad_device_cu_backward_and_planner_path():
+    say("device-detected bad cu_seqlens: backward, and the planner path")
+    import packed_varlen_block_amd as pvb
+    import torch
+    w = W.random_small(9, [40, 24], H=2, d=64, backward=True)
+    dev, o, lse = gpu_fwd(w, "bf16")
+    q, k, v, _ = dev
+    do = dev_bf16(w.do)
+    bad = torch.tensor([0, 40, 30], dtype=torch.int32).cuda()
+    grads = [torch.full((64, 2, 64), 7.0, dtype=torch.float32).cuda() for _ in range(3)]
+    st = pvb.varlen_attn_bwd(q, k, v, o, do, lse, bad, dq=grads[0], dk=grads[1], dv=grads[2])[3]
+    with pytest.raises(pvb.PvbError) as e:
+        pvb.check_status(st)
+    assert e.value.status == 4
+    assert all((g == 7.0).all() for g in grads)
+    # 1100 segments (planner path), one decreasing entry
+    cu = np.arange(1101, dtype=np.int32)
+    cu[500] = 700
+    T = 1100
+    qq = torch.zeros((T, 2, 64), dtype=torch.bfloat16).cuda()
+    out = torch.full((T, 2, 64), 7.0, dtype=torch.float32).cuda()
+    _, _, st = pvb.varlen_attn_fwd(qq, qq, qq, torch.from_numpy(cu).cuda(), out=out)
+    with pytest.raises(pvb.PvbError) as e:
+        pvb.check_status(st)
+    assert e.value.status == 4
+    assert (out == 7.0).all()
