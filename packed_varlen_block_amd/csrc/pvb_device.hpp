@@ -103,21 +103,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Stage rows [row0, row0 + ROWS) of a segment-relative [L, D] tensor (row
 // stride rs elements) into a swizzled LDS tile [ROWS][D] with 16-byte
-// global->LDS copies spread over the 4 waves of a 256-thread workgroup.  Rows
-// at or past L are clamped to row L-1 of the same segment, so every staged
-// value is finite whenever the segment itself is; callers mask those rows.
-// Issues ROWS * D / 8 / 256 copies per thread.
-template <int D, int ROWS>
+// global->LDS copies spread over the NW waves of the workgroup.  Rows at or
+// past L are clamped to row L-1 of the same segment, so every staged value is
+// finite whenever the segment itself is; callers mask those rows.  Issues
+// ROWS * D / 8 / (64 NW) copies per thread.
+template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void stage_rows(const bf16* src, int rs, int row0, int L, bf16* tile, int w,
                                            int lane) {
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;        // rows covered by one wave-wide copy
-  constexpr int NI = ROWS / RPI / 4;   // copies per wave
+  constexpr int NI = ROWS / RPI / NW;  // copies per wave
+  static_assert(NI * RPI * NW == ROWS, "tile rows must split evenly over the waves");
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t tile_base = lds_addr(tile);
 #pragma unroll
   for (int r = 0; r < NI; ++r) {
-    const int grp = 4 * r + wu;
+    const int grp = NW * r + wu;
     const int row = grp * RPI + lane / CPR;
     const int c = (lane % CPR) ^ swzf<D>(row);   // logical chunk that lands in this lane's slot
     const int srow = min(row0 + row, L - 1);
@@ -128,18 +129,18 @@ __device__ __forceinline__ void stage_rows(const bf16* src, int rs, int row0, in
 // The same copy pattern for a tile whose rows all lie inside the segment:
 // the per-lane byte offsets are computed once (init) and each call only moves
 // the wave-uniform source pointer, so a call costs no vector ALU work.
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = 4>
 struct FullTileCopy {
   static constexpr int CPR = D / 8;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int NI = ROWS / RPI / 4;
+  static constexpr int NI = ROWS / RPI / NW;
   uint32_t voff[NI];
   int wu;
   __device__ __forceinline__ void init(int rs, int w, int lane) {
     wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
     for (int r = 0; r < NI; ++r) {
-      const int row = (4 * r + wu) * RPI + lane / CPR;
+      const int row = (NW * r + wu) * RPI + lane / CPR;
       const int c = (lane % CPR) ^ swzf<D>(row);
       voff[r] = (uint32_t)(row * rs + c * 8) * 2u;
     }
@@ -150,7 +151,7 @@ struct FullTileCopy {
     const uint32_t tile_base = lds_addr(tile);
 #pragma unroll
     for (int r = 0; r < NI; ++r)
-      copy_to_lds16(s0, voff[r], tile_base + (uint32_t)((4 * r + wu) * RPI * D * 2));
+      copy_to_lds16(s0, voff[r], tile_base + (uint32_t)((NW * r + wu) * RPI * D * 2));
   }
 };
 

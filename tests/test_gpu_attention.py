@@ -38,6 +38,19 @@ def test_forward_small_sweep(d, o_dtype, precision):
         compare_fwd(w, o, lse)
 
 
+# long segments (many key tiles per query tile, ragged ends) at d = 128
+LONG_LENGTHS = [[512], [513], [700], [1030], [1300, 1], [255, 1800], [2048], [0, 1111, 0]]
+
+
+@pytest.mark.parametrize("o_dtype", ["bf16", "f32"])
+def test_forward_long_segments(o_dtype):
+    for i, lengths in enumerate(LONG_LENGTHS):
+        say(f"fwd long d=128 o={o_dtype} lengths={lengths}")
+        w = W.random_small(300 + i, lengths, H=2, d=128, backward=False)
+        _, o, lse = gpu_fwd(w, o_dtype, "bf16")
+        compare_fwd(w, o, lse)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("grad_dtype,precision", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "split")])
 def test_backward_small_sweep(d, grad_dtype, precision):
