@@ -8,7 +8,7 @@
 //
 // One workgroup = one work item (segment b, query tile m of 128 rows, head h)
 // taken from the planner's heaviest-first list.  Its 4 waves own 32 query rows
-// each.  Per 64-key tile:
+// each.  Per K/V tile (64 keys; 32 when segments are short on average):
 //   * K and V rows of the segment are copied global -> LDS asynchronously
 //     (16-byte copies into a double-buffered, XOR-swizzled tile: the copy of
 //     tile n+1 overlaps the math on tile n),
@@ -26,16 +26,18 @@ namespace pvb {
 namespace {
 
 constexpr int kFwdBM = 128;   // query rows per work item
-constexpr int kFwdBN = 64;    // keys per K/V tile
 constexpr int kFwdThreads = 256;
 
-template <int D, bool SPLIT, typename OutT, bool DECODE>
-__global__ void __launch_bounds__(kFwdThreads, 2)
+// BN keys per K/V tile: 64 for long segments; 32 for short ones, where the
+// smaller register and LDS footprint lets three workgroups share a CU.
+template <int D, bool SPLIT, typename OutT, bool DECODE, int BN>
+__global__ void __launch_bounds__(kFwdThreads, BN == 32 ? 3 : 2)
 attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const bf16* __restrict__ v, const int32_t* __restrict__ cu,
                 const WorkList wl, int H, int T,
                 float scale_log2, OutT* __restrict__ o, float* __restrict__ lse) {
-  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int BM = kFwdBM;
+  constexpr int NB = BN / 32;    // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;      // 32-wide feature blocks of O^T
   // The running max used for the exponentials is raised only when a tile's
@@ -108,31 +110,31 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bf16* cV = sV[b];
     const int key0 = n * BN;
     if (wave_active && key0 <= wq_last) {
-      // S^T = K Q^T: two 32-key blocks.  The K operands are read kPf k-steps
+      // S^T = K Q^T: NB 32-key blocks.  The K operands are read kPf k-steps
       // ahead of their MFMAs.
       constexpr int kPf = 2;
-      bf16x8 ka[KSTEPS][2];
+      bf16x8 ka[KSTEPS][NB];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) ka[s][kb2] = *(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g));
-      f32x16 st[2];
+        for (int kb2 = 0; kb2 < NB; ++kb2) ka[s][kb2] = *(const bf16x8*)(cK + swz<D>(32 * kb2 + lq, 16 * s + 8 * g));
+      f32x16 st[NB];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) st[kb2] = mfma32(ka[0][kb2], qf[0], f32x16{});
+      for (int kb2 = 0; kb2 < NB; ++kb2) st[kb2] = mfma32(ka[0][kb2], qf[0], f32x16{});
 #pragma unroll
       for (int s = 1; s < KSTEPS; ++s)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) st[kb2] = mfma32(ka[s][kb2], qf[s], st[kb2]);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kPf + 1), 0);
+        for (int kb2 = 0; kb2 < NB; ++kb2) st[kb2] = mfma32(ka[s][kb2], qf[s], st[kb2]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NB * (kPf + 1), 0);
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+        if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
       }
       // mask: key > query, or key past the segment end
       if (key0 + BN - 1 > wq_first || key0 + BN > L) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NB; ++kb2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -142,7 +144,7 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // online softmax for this lane's query column (in log2 units)
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < NB; ++kb2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb2][i]);
       mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
@@ -159,7 +161,7 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float rsum = 0.f;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < NB; ++kb2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = fast_exp2(st[kb2][i] * scale_log2 - m_use);
@@ -213,18 +215,25 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   if (g == 0) lse[(int64_t)h * T + seg0 + qrow] = (m_run + log2f(l_run)) * kLn2;
 }
 
+template <int D, bool SPLIT, typename OutT, int BN>
+void launch_fwd_bn(const void* q, const void* k, const void* v, const int32_t* cu, const WorkList& wl,
+                   int H, int T, size_t grid, float scale_log2, void* o, float* lse, hipStream_t s) {
+  if (wl.tiles == nullptr)
+    attn_fwd_kernel<D, SPLIT, OutT, true, BN><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
+  else
+    attn_fwd_kernel<D, SPLIT, OutT, false, BN><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
+}
+
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
                       const WorkList& wl, int H, int T, size_t cap, float scale_log2, void* o,
-                      float* lse, hipStream_t s) {
+                      float* lse, bool short_keys, hipStream_t s) {
   const size_t grid = cap * (size_t)H;
   if (grid == 0) return hipSuccess;
-  if (wl.tiles == nullptr)
-    attn_fwd_kernel<D, SPLIT, OutT, true><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
-  else
-    attn_fwd_kernel<D, SPLIT, OutT, false><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
+  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, T, grid, scale_log2, o, lse, s);
+  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, T, grid, scale_log2, o, lse, s);
   return hipGetLastError();
 }
 
@@ -270,12 +279,14 @@ extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, cons
     if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
   }
   const WorkList wl{dec ? nullptr : tiles, count, n_seg, d_status};
+  // segments shorter than 512 on average: 32-key tiles, three workgroups per CU
+  const bool short_keys = (int64_t)T < 512 * (int64_t)n_seg;
 
   const float sl2 = softmax_scale * kLog2e;
   const bool split = precision == PVB_PREC_SPLIT, f32 = o_dtype == PVB_F32;
   hipError_t e;
 #define PVB_FWD(D_, S_, T_) \
-  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, T, cap, sl2, d_o, d_lse, s)
+  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, T, cap, sl2, d_o, d_lse, short_keys, s)
   if (d == 128) {
     if (split) { if (f32) PVB_FWD(128, true, float); else PVB_FWD(128, true, bf16); }
     else { if (f32) PVB_FWD(128, false, float); else PVB_FWD(128, false, bf16); }
