@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-case", action="store_true")
+    ap.add_argument("--no-long-case", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -244,6 +245,8 @@ def main():
 
     if not a.no_hbm_case:
         out["short_pack_fwd"] = short_pack_forward(torch, pvb, W, dev, stream, a.seed)
+    if not a.no_long_case:
+        out["long_mixed_pack"] = long_mixed_pack(torch, pvb, W, dev, stream, a.seed)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -290,6 +293,44 @@ def short_pack_forward(torch, pvb, W, dev, stream, seed, n_sets=8, reps=40):
             "algorithmic_bytes": byts, "achieved_GBs": round(byts / (med * 1e-3) / 1e9, 1),
             "hbm_frac": round(byts / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "useful_tflops": round(F / (med * 1e-3) / 1e12, 2)}
+
+
+def long_mixed_pack(torch, pvb, W, dev, stream, seed, reps=5):
+    """The long mixed pack (T=32768: one 16384-token segment, then segments of
+    16-1024, H=32, d=128), forward and backward as in the main step (O bf16,
+    fp32 gradients, bf16 P/dS): useful TFLOP/s per call, median of reps."""
+    w = W.make(4, seed=seed)
+    T, H, d = w.T, w.H, w.d
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, do = up(w.q), up(w.k), up(w.v), up(w.do)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(w.lengths)]).astype(np.int32), device=dev)
+    B = len(w.lengths)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    grads = [torch.empty((T, H, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    wf = torch.empty(pvb.workspace_bytes(T, H, d, B, False), dtype=torch.uint8, device=dev)
+    wb = torch.empty(pvb.workspace_bytes(T, H, d, B, True, pvb.PVB_F32), dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = []
+    for i in range(2 + reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        pvb.varlen_attn_fwd(q, k, v, cu, out=o, lse=lse, workspace=wf, status=st)
+        e[1].record(stream)
+        pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, dq=grads[0], dk=grads[1], dv=grads[2],
+                            workspace=wb, status=st)
+        e[2].record(stream)
+        if i >= 2:
+            ev.append(e)
+    torch.cuda.synchronize()
+    pvb.check_status(st)
+    fwd = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+    F = useful_fwd_flops(w.lengths, H, d)
+    both = 3.5 * F / ((fwd + bwd) * 1e-3) / 1e12
+    return {"workload": "long_mixed_T32768_H32_d128", "segments": B, "pass": "fwd+bwd",
+            "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "fwd_bwd_ms": round(fwd + bwd, 4),
+            "useful_tflops": round(both, 2), "pct_bf16_mfma_peak": round(100.0 * both / PEAK_BF16_TFLOPS, 2)}
 
 
 if __name__ == "__main__":
