@@ -9,8 +9,14 @@
 //   dS_ij = P_ij (dP_ij - D_i),  dV_j = sum_i P_ij dO_i,
 //   dK_j = scale sum_i dS_ij q_i, dQ_i = scale sum_j dS_ij k_j.
 //
-// Kernels (one planner list of 128-row tiles serves both main kernels):
-//   bwd_pre  {LSE log2(e), D = rowsum(dO * O)} per (token, head).
+// Kernels (one planner list of 128-row tiles serves both):
+//   bwd_dq   (runs first) one workgroup per (segment, 128-query tile, head);
+//            forms {LSE log2(e), D = rowsum(dO * O)} of its rows for the
+//            dK/dV kernel, and is shaped like the forward: Q and dO fragments
+//            in registers, K and V tiles copied global -> LDS
+//            (double-buffered); S^T, dP^T and dS^T with each lane owning one
+//            query column, and dQ^T += K^T dS^T with K^T read transposed from
+//            LDS.
 //   bwd_kv_pair  one workgroup per (segment, 64-key half of a planner tile,
 //            head).  Wave pairs own 32 keys each and walk the 32-row query
 //            tiles from the diagonal to the segment end (Q, dO copied
@@ -19,10 +25,6 @@
 //            S, P and dV += P^T dO, the other dP, dS = P (dP - D) with P
 //            handed over through LDS, and dK += dS^T Q; the second operands
 //            are read transposed from LDS.
-//   bwd_dq   one workgroup per (segment, 128-query tile, head), shaped like the
-//            forward: Q and dO fragments in registers, K and V tiles copied
-//            global -> LDS (double-buffered); S^T, dP^T and dS^T with each lane owning one query
-//            column, and dQ^T += K^T dS^T with K^T read transposed from LDS.
 // dQ is recomputed rather than accumulated across key tiles with atomics:
 // device-scope float atomics are resolved past the per-XCD L2, and their
 // traffic (about 4 bytes per permitted edge at 128-key tiles) costs more than
@@ -37,44 +39,6 @@ constexpr int kTile = 128;       // rows per planner tile (two 64-key halves for
 constexpr int kKvBM = 32;        // query rows per dK/dV step
 constexpr int kDqBN = 64;        // keys per dq step
 constexpr int kThreads = 256;
-constexpr int kPreThreads = 256;
-
-// Per (head, token): {LSE * log2(e), D = dO . O}, the two row statistics the
-// main kernels need, in one 8-byte record.
-template <int D, typename OT>
-__global__ void __launch_bounds__(kPreThreads)
-bwd_pre_kernel(const OT* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
-               int rows, int H, int T, float2* __restrict__ ld, const int32_t* __restrict__ status) {
-  if (status != nullptr && *status != PVB_OK) return;
-  constexpr int TPR = D / 8;                     // threads per (token, head) row
-  constexpr int RPB = kPreThreads / TPR;         // rows per block
-  const int r = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c = (threadIdx.x % TPR) * 8;
-  float acc = 0.f;
-  if (r < rows) {
-    const int64_t off = (int64_t)r * D + c;
-    const bf16x8 g = *(const bf16x8*)(dout + off);
-    float ov[8];
-    if constexpr (sizeof(OT) == 4) {
-      const float4 a = *(const float4*)(o + off), b = *(const float4*)(o + off + 4);
-      ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
-      ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
-    } else {
-      const bf16x8 a = *(const bf16x8*)(o + off);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ov[e] = (float)a[e];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)g[e] * ov[e];
-  }
-#pragma unroll
-  for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (r < rows && threadIdx.x % TPR == 0) {
-    const int t = r / H, h = r - t * H;
-    const int64_t i = (int64_t)h * T + t;
-    ld[i] = make_float2(lse[i] * kLog2e, acc);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK, dV with wave pairs
@@ -304,12 +268,14 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, typename GradT, bool DECODE>
+// Also forms the per-row statistics {LSE log2e, D = dO . O} of its queries and
+// writes them for the dK/dV kernel, which runs after it.
+template <int D, bool SPLIT, typename GradT, bool DECODE, typename OT>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-              const bf16* __restrict__ dout, const float2* __restrict__ ld,
-              const int32_t* __restrict__ cu, const WorkList wl, int H, int T, float scale,
-              float scale_log2, GradT* __restrict__ dq) {
+              const bf16* __restrict__ dout, const OT* __restrict__ o, const float* __restrict__ lse,
+              float2* __restrict__ ld, const int32_t* __restrict__ cu, const WorkList wl, int H, int T,
+              float scale, float scale_log2, GradT* __restrict__ dq) {
   constexpr int BM = kTile, BN = kDqBN;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -342,17 +308,37 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 
   bf16x8 qf[KSTEPS], gf[KSTEPS];
   float2 rl = make_float2(INFINITY, 0.f);   // {LSE log2e, D} of this lane's query
+  float dpart = 0.f;                        // this lane's half of dO . O
   if (qrow < L) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       qf[s] = *(const bf16x8*)(qs + qrow * rs + 16 * s + 8 * g);
       gf[s] = *(const bf16x8*)(gs + qrow * rs + 16 * s + 8 * g);
     }
-    rl = ld[(int64_t)h * T + seg0 + qrow];
+    const OT* orow = o + base + (int64_t)qrow * rs;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      float ov[8];
+      if constexpr (sizeof(OT) == 4) {
+        const float4 a = *(const float4*)(orow + 16 * s + 8 * g), b = *(const float4*)(orow + 16 * s + 8 * g + 4);
+        ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+        ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+      } else {
+        const bf16x8 a = *(const bf16x8*)(orow + 16 * s + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = (float)a[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += (float)gf[s][e] * ov[e];
+    }
+    rl.x = lse[(int64_t)h * T + seg0 + qrow] * kLog2e;
   } else {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = gf[s] = bf16x8{};
   }
+  // lanes l and l^32 hold the two halves of one query row
+  rl.y = dpart + swap_halves(dpart);
+  if (g == 0 && qrow < L) ld[(int64_t)h * T + seg0 + qrow] = rl;
 
   f32x16 dqacc[DBLK];
 #pragma unroll
@@ -485,34 +471,33 @@ BwdLayout bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   return l;
 }
 
+template <int D, bool SPLIT, typename GradT, typename OT, bool DECODE>
+void launch_bwd_kernels(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, const int32_t* cu, const WorkList& wl, int H, int T,
+                        size_t grid, float scale, float2* ld, void* dq, void* dk, void* dv,
+                        hipStream_t s) {
+  // dQ first: it also writes the {LSE log2e, D} records the dK/dV kernel reads
+  bwd_dq_kernel<D, SPLIT, GradT, DECODE, OT><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const OT*)o, lse, ld, cu, wl,
+      H, T, scale, scale * kLog2e, (GradT*)dq);
+  bwd_kv_pair_kernel<D, SPLIT, GradT, DECODE><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
+      scale * kLog2e, (GradT*)dk, (GradT*)dv);
+}
+
 template <int D, bool SPLIT, typename GradT, typename OT>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, const int32_t* cu, const WorkList& wl, int H, int T,
                       size_t cap, float scale, float2* ld, void* dq, void* dk, void* dv,
                       hipStream_t s) {
-  const int rows = T * H;
-  if (rows > 0) {
-    constexpr int RPB = kPreThreads / (D / 8);
-    bwd_pre_kernel<D, OT><<<(rows + RPB - 1) / RPB, kPreThreads, 0, s>>>(
-        (const OT*)o, (const bf16*)dout, lse, rows, H, T, ld, wl.tiles != nullptr ? wl.status : nullptr);
-  }
   const size_t grid = cap * (size_t)H;
   if (grid > 0) {
-    if (wl.tiles == nullptr) {
-      bwd_kv_pair_kernel<D, SPLIT, GradT, true><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
-          scale * kLog2e, (GradT*)dk, (GradT*)dv);
-      bwd_dq_kernel<D, SPLIT, GradT, true><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
-          scale * kLog2e, (GradT*)dq);
-    } else {
-      bwd_kv_pair_kernel<D, SPLIT, GradT, false><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
-          scale * kLog2e, (GradT*)dk, (GradT*)dv);
-      bwd_dq_kernel<D, SPLIT, GradT, false><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
-          scale * kLog2e, (GradT*)dq);
-    }
+    if (wl.tiles == nullptr)
+      launch_bwd_kernels<D, SPLIT, GradT, OT, true>(q, k, v, o, dout, lse, cu, wl, H, T, grid, scale, ld,
+                                                    dq, dk, dv, s);
+    else
+      launch_bwd_kernels<D, SPLIT, GradT, OT, false>(q, k, v, o, dout, lse, cu, wl, H, T, grid, scale, ld,
+                                                     dq, dk, dv, s);
   }
   return hipGetLastError();
 }
