@@ -62,6 +62,39 @@ def test_backward_small_sweep(d, grad_dtype, precision):
         compare_bwd(w, dq, dk, dv)
 
 
+# long segments through the backward: many query steps per key tile in the
+# dK/dV kernel, many key tiles per query tile in the dQ kernel, ragged ends
+LONG_BWD_LENGTHS = [[513], [1030], [1300, 1], [255, 1800], [0, 1111, 0]]
+
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+def test_backward_long_segments(grad_dtype):
+    for i, lengths in enumerate(LONG_BWD_LENGTHS):
+        say(f"bwd long d=128 g={grad_dtype} lengths={lengths}")
+        w = W.random_small(400 + i, lengths, H=2, d=128, backward=True)
+        dev, o, lse = gpu_fwd(w, "bf16", "bf16")
+        dq, dk, dv = gpu_bwd(dev, o, lse, w, grad_dtype, "bf16")
+        compare_bwd(w, dq, dk, dv)
+
+
+def test_empty_pack():
+    """T = 0 (no segments, or only empty ones): every call succeeds and
+    returns empty outputs."""
+    import torch
+    import packed_varlen_block_amd as pvb
+    H, d = 2, 128
+    for lengths in ([], [0], [0, 0, 0]):
+        say(f"empty pack lengths={lengths}")
+        cu = torch.tensor(host_cu(lengths), dtype=torch.int32).cuda()
+        z = torch.empty((0, H, d), dtype=torch.bfloat16, device="cuda")
+        o, lse, st = pvb.varlen_attn_fwd(z, z, z, cu)
+        pvb.check_status(st)
+        assert tuple(o.shape) == (0, H, d) and tuple(lse.shape) == (H, 0)
+        dq, dk, dv, st = pvb.varlen_attn_bwd(z, z, z, o, z, lse, cu)
+        pvb.check_status(st)
+        assert all(tuple(g.shape) == (0, H, d) for g in (dq, dk, dv))
+
+
 def test_worked_example_and_merged_boundary():
     say("cfg1: worked example, forward, and the merged boundary [0,5,12]")
     import packed_varlen_block_amd as pvb
