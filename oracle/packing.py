@@ -20,6 +20,17 @@ O3  best-fit-decreasing
 O4  next-token pair forming inside each document
     "Pack sequences without joining their contexts", "Form pairs inside each
     source range".
+O9  boundaries compiled back from position_ids
+    "Packing与 FlashAttention Varlen" section 3: the reset points of the
+    sample-local positions (position == 0, or position == the smallest
+    position for the general path), followed by the total token count, are
+    cu_seqlens; max_seqlen is the largest difference.  Section 6: when the
+    positions are multimodal rotary coordinates that repeat inside a sample,
+    the boundary is read from a separate strictly increasing text-position
+    plane instead.  Readings: the first token must be a reset point (else
+    cu[0] would not be 0 and the contract of section 3 fails: an error); an
+    empty stream gives cu = [0] and max_seqlen = 0; zero-length segments
+    cannot be represented and vanish.
 """
 from __future__ import annotations
 
@@ -242,3 +253,33 @@ def packed_rows(documents, capacity: int):
     return {"inputs": inputs, "targets": targets, "segments": segments,
             "positions": positions, "valid": valid, "lengths": lengths,
             "row_of": row_of, "start_of": start_of}
+
+
+# ---------------------------------------------------------------------------
+# O9
+# ---------------------------------------------------------------------------
+
+def boundaries_from_positions(position_ids, sentinel: str = "zero"):
+    """O9.  Returns (cu, max_seqlen) for a flat position stream.
+
+    sentinel "zero": a token starts a segment when its position is 0;
+    sentinel "min": when its position equals the smallest position.
+    """
+    pos = [int(x) for x in np.asarray(position_ids).reshape(-1)]
+    T = len(pos)
+    if T == 0:
+        return np.zeros(1, dtype=np.int32), 0
+    if sentinel == "zero":
+        s = 0
+    elif sentinel == "min":
+        s = min(pos)
+    else:
+        raise ValueError("sentinel must be 'zero' or 'min'")
+    starts = [t for t in range(T) if pos[t] == s]
+    if not starts or starts[0] != 0:
+        raise PackingError("the first token is not a segment start")
+    if T > INT32_MAX:
+        raise PackingError("token count overflows int32")
+    cu = starts + [T]
+    max_seqlen = max(cu[b + 1] - cu[b] for b in range(len(cu) - 1))
+    return np.asarray(cu, dtype=np.int32), max_seqlen

@@ -204,3 +204,70 @@ def test_bfd_errors():
         P.best_fit_decreasing([9], 8)
     with pytest.raises(P.PackingError):
         P.best_fit_decreasing([1], 0)
+
+
+# ---------------------------------------------------------------- O9
+
+def test_boundaries_from_positions_worked_example():
+    """Section 3's table: resets at 0, 5, 8; the total 12 appended."""
+    g = _gold("worked_5_3_4.json")
+    cu, mx = P.boundaries_from_positions(g["position_ids"])
+    assert cu.tolist() == g["cu_seqlens"] and mx == g["max_seqlen"]
+    cu2, mx2 = P.boundaries_from_positions(g["position_ids"], "min")
+    assert cu2.tolist() == g["cu_seqlens"] and mx2 == g["max_seqlen"]
+
+
+def test_boundaries_round_trip_and_zero_length_loss():
+    """lengths -> positions (O1) -> boundaries gives the lengths back, except
+    that zero-length segments vanish."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        B = int(rng.integers(1, 12))
+        lengths = rng.integers(0, 9, size=B).tolist()
+        if sum(lengths) == 0:
+            continue
+        md = P.packed_row_metadata(lengths)
+        cu, mx = P.boundaries_from_positions(md["pos"])
+        kept = [L for L in lengths if L > 0]
+        assert cu.tolist() == P.cu_seqlens_from_lengths(kept)
+        assert mx == max(kept)
+
+
+def test_boundaries_min_sentinel_offset_positions():
+    """Positions that start at 1 (or any c): the min path still finds the
+    starts; the zero path has no start at token 0 and is an error."""
+    md = P.packed_row_metadata([4, 2, 5])
+    for c in (1, 7, -3):
+        cu, mx = P.boundaries_from_positions(md["pos"] + c, "min")
+        assert cu.tolist() == [0, 4, 6, 11] and mx == 5
+    with pytest.raises(P.PackingError):
+        P.boundaries_from_positions(md["pos"] + 1, "zero")
+
+
+def test_boundaries_from_text_plane_not_rotary_planes():
+    """Section 6: rotary coordinates repeat inside a sample (several tokens of
+    an image grid share a temporal, height or width coordinate, and several
+    of them are 0), so reset points read from those planes over-split a
+    sample; the text plane (0, 1, 2, ... per sample) gives the true
+    boundaries."""
+    # sample A: a 2x3 image grid whose coordinates start at 0, then 2 text
+    # tokens continuing after the grid; sample B: 3 text tokens
+    temporal = np.array([0, 0, 0, 0, 0, 0, 3, 4] + [0, 1, 2])
+    height = np.array([0, 0, 0, 1, 1, 1, 3, 4] + [0, 1, 2])
+    width = np.array([0, 1, 2, 0, 1, 2, 3, 4] + [0, 1, 2])
+    text = np.array(list(range(8)) + list(range(3)))
+    cu, mx = P.boundaries_from_positions(text)
+    assert cu.tolist() == [0, 8, 11] and mx == 8
+    for plane in (temporal, height, width):
+        assert len(P.boundaries_from_positions(plane)[0]) > len(cu)   # over-split
+
+
+def test_boundaries_edge_cases():
+    cu, mx = P.boundaries_from_positions([])
+    assert cu.tolist() == [0] and mx == 0
+    cu, mx = P.boundaries_from_positions([0])
+    assert cu.tolist() == [0, 1] and mx == 1
+    cu, mx = P.boundaries_from_positions([0, 0, 0])
+    assert cu.tolist() == [0, 1, 2, 3] and mx == 1
+    with pytest.raises(P.PackingError):
+        P.boundaries_from_positions([1, 0, 1])
