@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-case", action="store_true")
     ap.add_argument("--no-long-case", action="store_true")
+    ap.add_argument("--no-meta-case", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -247,6 +248,8 @@ def main():
         out["short_pack_fwd"] = short_pack_forward(torch, pvb, W, dev, stream, a.seed)
     if not a.no_long_case:
         out["long_mixed_pack"] = long_mixed_pack(torch, pvb, W, dev, stream, a.seed)
+    if not a.no_meta_case:
+        out["boundaries_from_positions"] = boundary_compilation(torch, pvb, W, dev, stream, a.seed)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -331,6 +334,39 @@ def long_mixed_pack(torch, pvb, W, dev, stream, seed, reps=5):
     return {"workload": "long_mixed_T32768_H32_d128", "segments": B, "pass": "fwd+bwd",
             "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "fwd_bwd_ms": round(fwd + bwd, 4),
             "useful_tflops": round(both, 2), "pct_bf16_mfma_peak": round(100.0 * both / PEAK_BF16_TFLOPS, 2)}
+
+
+def boundary_compilation(torch, pvb, W, dev, stream, seed, reps=50):
+    """cu_seqlens compiled back from the long mixed pack's position stream
+    (T=32768, one 16384-token segment then segments of 16-1024): one
+    single-workgroup launch; median call time (it is launch- and latency-bound:
+    128 KB of positions)."""
+    w = W.make(4, seed=seed)
+    T = w.T
+    L = torch.tensor(np.asarray(w.lengths, dtype=np.int32), device=dev)
+    row = pvb.build_packed_row(L, capacity=T)
+    pvb.check_status(row["status"])
+    pos = row["pos"]
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        out = pvb.boundaries_from_positions(pos, "zero", status=st)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = pvb.boundaries_from_positions(pos, "zero", status=st)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    pvb.check_status(st)
+    n = int(out["n_seg"].item())
+    if out["cu"][:n + 1].cpu().tolist() != [0] + np.cumsum(w.lengths).tolist():
+        raise RuntimeError("boundaries_from_positions: wrong cu_seqlens")
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"workload": "positions_T32768_long_mixed", "segments": n,
+            "median_us": round(float(np.median(ms)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2)}
 
 
 if __name__ == "__main__":

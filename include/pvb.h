@@ -128,6 +128,38 @@ pvb_status pvb_build_packed_row(const int32_t* d_lengths, int32_t n_seg, int32_t
                                 int32_t* d_inputs, int32_t* d_targets, uint8_t* d_valid,
                                 int32_t* d_status, void* stream);
 
+/* The reverse direction: segment boundaries compiled back from a flat
+ * position stream ("Packing与 FlashAttention Varlen", section 3: the tokens
+ * whose sample-local position restarts are the segment starts; appending the
+ * token count gives cu_seqlens, and the largest difference is max_seqlen).
+ * PVB_SENTINEL_ZERO takes position == 0 as a start; PVB_SENTINEL_MIN takes
+ * position == the smallest position in the stream (the general path of
+ * section 3, for encodings whose first position is not 0).  When the model's
+ * positions are rotary coordinates that repeat inside a sample, pass the
+ * separate text-position plane that restarts per sample (section 6) -- for a
+ * [P, T] position tensor, the pointer to that plane's row.  Zero-length
+ * segments cannot be represented in a position stream and do not appear.
+ *   d_pos        int32 [T] positions                                   (device)
+ *   T            tokens, >= 0
+ *   sentinel     PVB_SENTINEL_ZERO or PVB_SENTINEL_MIN
+ *   d_cu         out int32 [cu_capacity]: cu[0..n_seg], cu[0] = 0, cu[n_seg] = T
+ *                                                                      (device)
+ *   cu_capacity  entries d_cu can hold (T + 1 always suffices), >= 1
+ *   d_n_seg      out int32 [1]: number of segments n_seg                (device)
+ *   d_max_seqlen out int32 [1], nullable: largest segment length (0 if T = 0)
+ *                                                                      (device)
+ *   d_status     out: device status word (required)                     (device)
+ * Device-detected errors (status word; then d_cu, d_n_seg and d_max_seqlen
+ * are not written): PVB_E_BAD_CU_SEQLENS (T > 0 and the first token does not
+ * start a segment, so cu[0] could not be 0), PVB_E_OVERSIZED (n_seg + 1 >
+ * cu_capacity).  Host-detected: PVB_E_INVALID_ARG, PVB_E_OVERFLOW
+ * (T = 2^31 - 1). */
+typedef enum pvb_sentinel { PVB_SENTINEL_ZERO = 0, PVB_SENTINEL_MIN = 1 } pvb_sentinel;
+pvb_status pvb_boundaries_from_positions(const int32_t* d_pos, int32_t T, int32_t sentinel,
+                                         int32_t* d_cu, int32_t cu_capacity,
+                                         int32_t* d_n_seg, int32_t* d_max_seqlen,
+                                         int32_t* d_status, void* stream);
+
 /* ---------------------------------------------------------------- attention */
 
 /* Bytes of device workspace pvb_varlen_attn_fwd (bwd = 0) or

@@ -25,11 +25,12 @@ LIB_PATH = os.path.join(_HERE, "libpvb.so")
 PVB_OK = 0
 PVB_BF16, PVB_F32 = 0, 1
 PVB_PREC_BF16, PVB_PREC_SPLIT = 0, 1
+PVB_SENTINEL_ZERO, PVB_SENTINEL_MIN = 0, 1
 STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "PVB_E_OVERFLOW",
                 4: "PVB_E_BAD_CU_SEQLENS", 5: "PVB_E_WORKSPACE", 6: "PVB_E_UNSUPPORTED", 7: "PVB_E_HIP"}
 
 # every symbol include/pvb.h declares
-EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
+EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_status_string", "pvb_version")
 
@@ -55,13 +56,14 @@ def lib() -> ctypes.CDLL:
         L.pvb_pack_plan_nextfit.argtypes = [P, I64, I32, P, P, P]
         L.pvb_pack_plan_bfd.argtypes = [P, I64, I32, P, P, P, P, P]
         L.pvb_build_packed_row.argtypes = [P, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P]
+        L.pvb_boundaries_from_positions.argtypes = [P, I32, I32, P, I32, P, P, P, P]
         L.pvb_varlen_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
         L.pvb_varlen_attn_workspace_bytes.restype = SZ
         L.pvb_varlen_attn_fwd.argtypes = [P, P, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P, P]
         L.pvb_varlen_attn_bwd.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, F,
                                           P, P, P, I32, I32, P, SZ, P, P]
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
-                     "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd"):
+                     "pvb_boundaries_from_positions", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
         L.pvb_status_string.restype = ctypes.c_char_p
@@ -179,6 +181,35 @@ def build_packed_row(lengths, capacity: int | None = None, segment_base: int = 0
         _ptr(out["inputs"]) if gather else None, _ptr(out["targets"]) if gather else None,
         _ptr(out["valid"]) if gather else None, _ptr(out["status"]), _stream(dev))
     _check(rc, "build_packed_row")
+    return out
+
+
+def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None = None, status=None):
+    """cu_seqlens compiled back from a flat int32 CUDA position stream [T].
+
+    ``sentinel`` "zero" (a segment starts where the position is 0) or "min"
+    (where it equals the smallest position).  Returns a dict of CUDA tensors:
+    cu [capacity] (entries 0..n_seg valid), n_seg [1], max_seqlen [1],
+    status [1].  ``capacity`` defaults to T + 1.  Enqueued on the current
+    stream; call check_status(out["status"]) to synchronise and raise.
+    """
+    torch = _torch()
+    dev = pos.device
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 1:
+        raise PvbError(1, "boundaries_from_positions: pos must be a contiguous int32 vector")
+    if sentinel not in ("zero", "min"):
+        raise PvbError(1, "boundaries_from_positions: sentinel must be 'zero' or 'min'")
+    T = pos.numel()
+    cap = T + 1 if capacity is None else int(capacity)
+    out = {"cu": torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+           "n_seg": torch.zeros(1, dtype=torch.int32, device=dev),
+           "max_seqlen": torch.zeros(1, dtype=torch.int32, device=dev),
+           "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+    rc = lib().pvb_boundaries_from_positions(
+        _ptr(pos) if T > 0 else None, T, PVB_SENTINEL_MIN if sentinel == "min" else PVB_SENTINEL_ZERO,
+        _ptr(out["cu"]), cap, _ptr(out["n_seg"]), _ptr(out["max_seqlen"]), _ptr(out["status"]),
+        _stream(dev))
+    _check(rc, "boundaries_from_positions")
     return out
 
 

@@ -163,3 +163,17 @@ def test_device_entry_points_reject_bad_arguments_on_host():
     # token outputs without a token source
     assert L.pvb_build_packed_row(FAKE, 2, 8, 0, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None,
                                   FAKE, None) == 1
+
+
+def test_boundaries_host_side_errors():
+    L = pvb.lib()
+    FAKE = 1 << 40
+    Z, M = pvb.PVB_SENTINEL_ZERO, pvb.PVB_SENTINEL_MIN
+    assert L.pvb_boundaries_from_positions(None, 4, Z, FAKE, 5, FAKE, None, FAKE, None) == 1   # null positions
+    assert L.pvb_boundaries_from_positions(FAKE, -1, Z, FAKE, 5, FAKE, None, FAKE, None) == 1  # negative T
+    assert L.pvb_boundaries_from_positions(FAKE, 4, 2, FAKE, 5, FAKE, None, FAKE, None) == 1   # bad sentinel
+    assert L.pvb_boundaries_from_positions(FAKE, 4, M, FAKE, 0, FAKE, None, FAKE, None) == 1   # no room for cu
+    assert L.pvb_boundaries_from_positions(FAKE, 4, M, None, 5, FAKE, None, FAKE, None) == 1   # null cu
+    assert L.pvb_boundaries_from_positions(FAKE, 4, M, FAKE, 5, None, None, FAKE, None) == 1   # null n_seg
+    assert L.pvb_boundaries_from_positions(FAKE, 4, M, FAKE, 5, FAKE, None, None, None) == 1   # null status
+    assert L.pvb_boundaries_from_positions(FAKE, 2**31 - 1, Z, FAKE, 5, FAKE, None, FAKE, None) == 3

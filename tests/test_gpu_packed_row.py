@@ -89,3 +89,85 @@ def test_device_detected_errors():
         with pytest.raises(pvb.PvbError) as e:
             pvb.check_status(out["status"])
         assert e.value.status == code
+
+
+# ------------------------------------------------ boundaries from positions (O9)
+
+def _bounds(pos, sentinel="zero", capacity=None):
+    import packed_varlen_block_amd as pvb
+    torch = _torch()
+    p = torch.tensor(np.asarray(pos, dtype=np.int32), dtype=torch.int32).cuda()
+    out = pvb.boundaries_from_positions(p, sentinel, capacity)
+    return out
+
+
+def _check_bounds(pos, sentinel="zero"):
+    import packed_varlen_block_amd as pvb
+    out = _bounds(pos, sentinel)
+    pvb.check_status(out["status"])
+    cu, mx = P.boundaries_from_positions(pos, sentinel)
+    n = out["n_seg"].item()
+    assert n == len(cu) - 1
+    assert np.array_equal(out["cu"].cpu().numpy()[:n + 1], cu)
+    assert out["max_seqlen"].item() == mx
+
+
+def test_boundaries_worked_example():
+    say("boundaries: worked example table")
+    g = json.load(open(os.path.join(GOLD, "worked_5_3_4.json")))
+    for sentinel in ("zero", "min"):
+        out = _bounds(g["position_ids"], sentinel)
+        import packed_varlen_block_amd as pvb
+        pvb.check_status(out["status"])
+        assert out["n_seg"].item() == 3
+        assert out["cu"].cpu().tolist()[:4] == g["cu_seqlens"]
+        assert out["max_seqlen"].item() == g["max_seqlen"]
+
+
+def test_boundaries_round_trip_device_rows():
+    """lengths -> device packed row -> its positions -> device boundaries,
+    compared with oracle O9 on the same positions (bit-exact); streams span
+    several 1024-token chunks of the scan."""
+    rng = np.random.default_rng(21)
+    cases = [[8192], [16384] + [int(x) for x in rng.integers(16, 1025, size=40)], [1] * 3000,
+             [0, 5, 0, 0, 7], [1023, 1, 1024, 1025]]
+    for _ in range(12):
+        B = int(rng.integers(1, 60))
+        cases.append([int(x) for x in rng.integers(0, 300, size=B)])
+    for lengths in cases:
+        if sum(lengths) == 0:
+            continue
+        say(f"boundaries: round trip B={len(lengths)} T={sum(lengths)}")
+        row = _row(lengths)
+        import packed_varlen_block_amd as pvb
+        pvb.check_status(row["status"])
+        pos = row["pos"].cpu().numpy()
+        _check_bounds(pos, "zero")
+        _check_bounds(pos + 3, "min")
+        kept = [L for L in lengths if L > 0]
+        out = _bounds(pos)
+        n = out["n_seg"].item()
+        assert out["cu"].cpu().tolist()[:n + 1] == P.cu_seqlens_from_lengths(kept)
+
+
+def test_boundaries_edge_cases_and_errors():
+    import packed_varlen_block_amd as pvb
+    torch = _torch()
+    say("boundaries: empty stream, all starts, errors")
+    _check_bounds([], "zero")
+    _check_bounds([], "min")
+    _check_bounds([0] * 2500, "zero")
+    _check_bounds([5] * 1500, "min")
+    for pos, sentinel, cap, code in (([1, 0, 1], "zero", None, 4), ([0, 1, 0, 1], "zero", 2, 2),
+                                     ([3, 2, 2], "min", None, 4)):
+        p = torch.tensor(pos, dtype=torch.int32).cuda()
+        cu = torch.full((max(cap or len(pos) + 1, 1),), 7, dtype=torch.int32, device="cuda")
+        out = {"n_seg": torch.full((1,), 7, dtype=torch.int32, device="cuda")}
+        st = torch.empty(1, dtype=torch.int32, device="cuda")
+        rc = pvb.lib().pvb_boundaries_from_positions(
+            p.data_ptr(), len(pos), 1 if sentinel == "min" else 0, cu.data_ptr(), cu.numel(),
+            out["n_seg"].data_ptr(), None, st.data_ptr(), None)
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert st.item() == code
+        assert (cu == 7).all() and out["n_seg"].item() == 7
