@@ -54,3 +54,73 @@ def test_zero_eligible_is_an_error():
     rows, z, _ = _setup()
     with pytest.raises(ValueError):
         LP.token_weighted_nll(z, rows["targets"], np.zeros_like(rows["valid"]))
+
+
+# ---------------------------------------------------------------- O10
+
+def test_packed_nll_matches_probe_on_flat_cells():
+    """The probe's twelve cells laid flat: the same sum, count and mean."""
+    rows, z, lp = _setup()
+    C = z.shape[0] * z.shape[1]
+    flat = z.reshape(C, -1)
+    tg = np.where(rows["valid"].reshape(-1), rows["targets"].reshape(-1), -1)
+    row, s, n, m = LP.packed_nll(flat, tg)
+    assert n == 9
+    assert round(s, 6) == lp["loss_sum_printed"] and round(m, 6) == lp["loss_mean_printed"]
+    assert np.all(row[tg < 0] == 0.0)
+
+
+def test_packed_nll_grad_by_finite_differences():
+    rng = np.random.default_rng(5)
+    C, V = 7, 11
+    z = rng.normal(size=(C, V)) * 2
+    tg = rng.integers(0, V, size=C)
+    tg[[1, 4]] = -1                          # two cells without a target
+    mask = np.ones(C, dtype=np.uint8)
+    mask[5] = 0                              # one target not supervised
+    g = LP.packed_nll_grad(z, tg, mask)
+    h = 1e-6
+    for c in range(C):
+        for v in range(V):
+            zp, zm = z.copy(), z.copy()
+            zp[c, v] += h
+            zm[c, v] -= h
+            fd = (LP.packed_nll(zp, tg, mask)[3] - LP.packed_nll(zm, tg, mask)[3]) / (2 * h)
+            assert abs(fd - g[c, v]) < 1e-8, (c, v)
+    assert np.all(g[[1, 4, 5]] == 0.0)
+    assert np.allclose(g.sum(axis=1), 0.0, atol=1e-15)
+
+
+def test_excluded_cells_are_skipped_not_multiplied():
+    """NaN/Inf logits in excluded cells change nothing (x0 would give NaN)."""
+    rng = np.random.default_rng(6)
+    z = rng.normal(size=(5, 9))
+    tg = np.array([3, -1, 2, -100, 8])
+    base = LP.packed_nll(z, tg)
+    gb = LP.packed_nll_grad(z, tg)
+    z[1, :] = np.nan
+    z[3, 2] = np.inf
+    after = LP.packed_nll(z, tg)
+    assert after[1] == base[1] and after[2] == base[2]
+    ga = LP.packed_nll_grad(z, tg)
+    assert np.array_equal(ga, gb)
+
+
+def test_zero_eligible_and_bad_target_are_errors():
+    z = np.zeros((3, 4))
+    with pytest.raises(ValueError):
+        LP.packed_nll(z, np.array([-1, -100, -1]))
+    with pytest.raises(ValueError):
+        LP.packed_nll(z, np.array([0, 1, 2]), mask=np.zeros(3))
+    with pytest.raises(ValueError):
+        LP.packed_nll(z, np.array([0, 4, 1]))
+
+
+def test_shifted_targets_page_figure():
+    """Section 2's figure: A0 A1 A2 | B0 B1 -> A1 A2 -1 | B1 -1; A's last
+    logit never supervises B's first token."""
+    ids = np.array([10, 11, 12, 20, 21])
+    t = LP.shifted_targets(ids, [0, 3, 5])
+    assert t.tolist() == [11, 12, -100, 21, -100]
+    t2 = LP.shifted_targets(ids, [0, 5])             # one sample: a plain shift
+    assert t2.tolist() == [11, 12, 20, 21, -100]
