@@ -44,7 +44,8 @@ typedef enum pvb_status {
   PVB_E_BAD_CU_SEQLENS = 4, /* cu[0] != 0, decreasing, or cu[B] != T             */
   PVB_E_WORKSPACE = 5,      /* workspace missing or smaller than required         */
   PVB_E_UNSUPPORTED = 6,    /* head_dim other than 64/128, or a size beyond limits */
-  PVB_E_HIP = 7             /* a HIP runtime call failed (launch error)           */
+  PVB_E_HIP = 7,            /* a HIP runtime call failed (launch error)           */
+  PVB_E_NO_TARGETS = 8      /* a mean loss over zero eligible targets              */
 } pvb_status;
 
 typedef enum pvb_dtype { PVB_BF16 = 0, PVB_F32 = 1 } pvb_dtype;
@@ -213,6 +214,40 @@ pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v
                                float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
                                int32_t grad_dtype, int32_t precision, void* workspace,
                                size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* ---------------------------------------------------------------- packed loss */
+
+/* Token-weighted negative log-likelihood over packed cells and its logit
+ * gradient ("Pack sequences without joining their contexts", "Keep the same
+ * nine-target objective").  Cell c is eligible when targets[c] >= 0 and, if a
+ * mask is given, mask[c] != 0 (so PAD_CELL = -1 and the ignore label -100 are
+ * never supervised).  With N eligible cells:
+ *   row_nll[c] = logsumexp(logits[c, :]) - logits[c, targets[c]]  (eligible),
+ *                0 (excluded);
+ *   loss[0] = sum of row_nll (float64, fixed summation order), loss[1] = loss[0] / N;
+ *   grad[c, v] = (softmax(logits[c, :])_v - 1[v = targets[c]]) / N  (eligible),
+ *                0 (excluded).
+ * Excluded cells are skipped before any arithmetic: NaN or Inf logits there
+ * change nothing.  Targets must already be sample-local (for next-token
+ * training: shifted inside each sample, the last cell of a sample ignored,
+ * "Packing与 FlashAttention Varlen", section 2).
+ *   d_logits     [C, V] bf16 or fp32 per logits_dtype (row-major)      (device)
+ *   C, V         cells (>= 0) and vocabulary size (> 0)
+ *   d_targets    int32 [C]                                             (device)
+ *   d_mask       uint8 [C], nullable: loss eligibility                 (device)
+ *   d_row_nll    out fp32 [C] (required when C > 0)                    (device)
+ *   d_loss       out float64 [2]: sum, mean                            (device)
+ *   d_count      out int32 [1]: N                                      (device)
+ *   d_grad       out [C, V] per grad_dtype, nullable (no gradient)     (device)
+ *   d_status     out: device status word (required)                   (device)
+ * Device-detected errors (status word; then d_row_nll, d_loss and d_grad are
+ * not written): PVB_E_NO_TARGETS (N = 0), PVB_E_INVALID_ARG (an eligible
+ * target >= V).  Host-detected: PVB_E_INVALID_ARG, PVB_E_UNSUPPORTED
+ * (C >= 2^31). */
+pvb_status pvb_packed_nll(const void* d_logits, int32_t logits_dtype, int64_t C, int32_t V,
+                          const int32_t* d_targets, const uint8_t* d_mask, float* d_row_nll,
+                          double* d_loss, int32_t* d_count, void* d_grad, int32_t grad_dtype,
+                          int32_t* d_status, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);

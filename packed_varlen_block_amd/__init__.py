@@ -27,10 +27,12 @@ PVB_BF16, PVB_F32 = 0, 1
 PVB_PREC_BF16, PVB_PREC_SPLIT = 0, 1
 PVB_SENTINEL_ZERO, PVB_SENTINEL_MIN = 0, 1
 STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "PVB_E_OVERFLOW",
-                4: "PVB_E_BAD_CU_SEQLENS", 5: "PVB_E_WORKSPACE", 6: "PVB_E_UNSUPPORTED", 7: "PVB_E_HIP"}
+                4: "PVB_E_BAD_CU_SEQLENS", 5: "PVB_E_WORKSPACE", 6: "PVB_E_UNSUPPORTED", 7: "PVB_E_HIP",
+                8: "PVB_E_NO_TARGETS"}
 
 # every symbol include/pvb.h declares
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
+           "pvb_packed_nll",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_status_string", "pvb_version")
 
@@ -57,13 +59,15 @@ def lib() -> ctypes.CDLL:
         L.pvb_pack_plan_bfd.argtypes = [P, I64, I32, P, P, P, P, P]
         L.pvb_build_packed_row.argtypes = [P, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P]
         L.pvb_boundaries_from_positions.argtypes = [P, I32, I32, P, I32, P, P, P, P]
+        L.pvb_packed_nll.argtypes = [P, I32, I64, I32, P, P, P, P, P, P, I32, P, P]
         L.pvb_varlen_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
         L.pvb_varlen_attn_workspace_bytes.restype = SZ
         L.pvb_varlen_attn_fwd.argtypes = [P, P, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P, P]
         L.pvb_varlen_attn_bwd.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, F,
                                           P, P, P, I32, I32, P, SZ, P, P]
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
-                     "pvb_boundaries_from_positions", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd"):
+                     "pvb_boundaries_from_positions", "pvb_packed_nll", "pvb_varlen_attn_fwd",
+                     "pvb_varlen_attn_bwd"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
         L.pvb_status_string.restype = ctypes.c_char_p
@@ -210,6 +214,39 @@ def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None 
         _ptr(out["cu"]), cap, _ptr(out["n_seg"]), _ptr(out["max_seqlen"]), _ptr(out["status"]),
         _stream(dev))
     _check(rc, "boundaries_from_positions")
+    return out
+
+
+def packed_nll(logits, targets, mask=None, grad=True, grad_dtype=None, status=None):
+    """Token-weighted NLL over packed cells.  ``logits`` is a CUDA [C, V]
+    bf16/fp32 tensor, ``targets`` int32 [C] (cells with a negative target are
+    excluded), ``mask`` optional uint8 [C] loss eligibility.  Returns a dict of
+    CUDA tensors: row_nll [C], loss [2] (float64 sum, mean), count [1],
+    status [1], and grad [C, V] (logits' dtype unless ``grad_dtype``) when
+    ``grad``.  Enqueued on the current stream; call check_status(out["status"])
+    to synchronise and raise on a device-detected error."""
+    torch = _torch()
+    dev = logits.device
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise PvbError(1, "packed_nll: logits must be contiguous [C, V]")
+    C, V = logits.shape
+    if targets.dtype != torch.int32 or tuple(targets.shape) != (C,) or not targets.is_contiguous():
+        raise PvbError(1, "packed_nll: targets must be contiguous int32 [C]")
+    if mask is not None and (mask.dtype != torch.uint8 or tuple(mask.shape) != (C,) or not mask.is_contiguous()):
+        raise PvbError(1, "packed_nll: mask must be contiguous uint8 [C]")
+    gdt = logits.dtype if grad_dtype is None else grad_dtype
+    out = {"row_nll": torch.empty(max(C, 1), dtype=torch.float32, device=dev)[:C],
+           "loss": torch.zeros(2, dtype=torch.float64, device=dev),
+           "count": torch.zeros(1, dtype=torch.int32, device=dev),
+           "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+    if grad:
+        out["grad"] = torch.empty((C, V), dtype=gdt, device=dev)
+    rc = lib().pvb_packed_nll(
+        _ptr(logits) if C > 0 else None, _dtype_code(logits.dtype), C, V, _ptr(targets) if C > 0 else None,
+        _ptr(mask) if mask is not None else None, _ptr(out["row_nll"]) if C > 0 else None, _ptr(out["loss"]),
+        _ptr(out["count"]), _ptr(out["grad"]) if grad and C > 0 else None, _dtype_code(gdt),
+        _ptr(out["status"]), _stream(dev))
+    _check(rc, "packed_nll")
     return out
 
 

@@ -29,6 +29,7 @@ extern "C" const char* pvb_status_string(int32_t status) {
     case PVB_E_WORKSPACE: return "workspace missing or too small";
     case PVB_E_UNSUPPORTED: return "unsupported size or head dimension";
     case PVB_E_HIP: return "HIP runtime error";
+    case PVB_E_NO_TARGETS: return "no eligible targets (the mean has no denominator)";
     default: return "unknown status";
   }
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert pvb.status_string(code) and pvb.status_string(code) != "unknown status"
     assert pvb.status_string(99) == "unknown status"
 
@@ -177,3 +177,26 @@ def test_boundaries_host_side_errors():
     assert L.pvb_boundaries_from_positions(FAKE, 4, M, FAKE, 5, None, None, FAKE, None) == 1   # null n_seg
     assert L.pvb_boundaries_from_positions(FAKE, 4, M, FAKE, 5, FAKE, None, None, None) == 1   # null status
     assert L.pvb_boundaries_from_positions(FAKE, 2**31 - 1, Z, FAKE, 5, FAKE, None, FAKE, None) == 3
+
+
+def test_packed_nll_host_side_errors():
+    L = pvb.lib()
+    FAKE = 1 << 40
+    B, F32 = pvb.PVB_BF16, pvb.PVB_F32
+    ok = dict(l=FAKE, ld=B, C=4, V=10, t=FAKE, m=None, r=FAKE, loss=FAKE, n=FAKE, g=None, gd=F32, st=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.pvb_packed_nll(a["l"], a["ld"], a["C"], a["V"], a["t"], a["m"], a["r"], a["loss"], a["n"],
+                                a["g"], a["gd"], a["st"], None)
+    assert call(C=-1) == 1
+    assert call(V=0) == 1
+    assert call(l=None) == 1
+    assert call(t=None) == 1
+    assert call(r=None) == 1
+    assert call(loss=None) == 1
+    assert call(n=None) == 1
+    assert call(st=None) == 1
+    assert call(ld=2) == 1
+    assert call(g=FAKE, gd=3) == 1
+    assert call(C=2**31) == 6
