@@ -12,8 +12,10 @@
 //   nll_count_kernel  one workgroup: N and the target checks (status word);
 //   nll_row_kernel    one workgroup per cell: the row's log-sum-exp in one
 //                     pass (per-thread running max and rescaled sum, combined
-//                     across the workgroup), its NLL, then the gradient row in
-//                     a second pass over the (L2-resident) logits;
+//                     across the workgroup), its NLL, then the gradient row.
+//                     Rows of up to kHeld 16-byte vectors per thread stay in
+//                     registers between the two passes (the logits are read
+//                     from HBM once); longer or unaligned rows are read again;
 //   nll_sum_kernel    one workgroup: the loss sum in float64 in a fixed order
 //                     (deterministic), and the mean.
 #include "pvb_device.hpp"
@@ -66,8 +68,10 @@ template <typename T>
 __device__ __forceinline__ float load_f(const T* p) { return (float)*p; }
 
 // One workgroup per cell.  VEC elements per load (16 bytes when the row is
-// aligned for it, else 1).
-template <typename LT, typename GT, int VEC>
+// aligned for it, else 1); HELD: the row is held in registers (VEC > 1 and
+// V <= kHeld * VEC * kRowThreads).
+constexpr int kHeld = 16;
+template <typename LT, typename GT, int VEC, bool HELD>
 __global__ void __launch_bounds__(kRowThreads)
 nll_row_kernel(const LT* __restrict__ logits, int V, const int32_t* __restrict__ targets,
                const uint8_t* __restrict__ mask, const int32_t* __restrict__ count,
@@ -98,17 +102,44 @@ nll_row_kernel(const LT* __restrict__ logits, int V, const int32_t* __restrict__
     }
   };
   const int nv = V / VEC;
-  for (int i = tid; i < nv; i += kRowThreads) {
-    if constexpr (VEC == 1) {
-      add(load_f(row + i));
-    } else {
-      typedef __attribute__((__vector_size__(VEC * sizeof(LT)))) LT vec_t;
-      const vec_t x = *(const vec_t*)(row + (int64_t)i * VEC);
+  typedef __attribute__((__vector_size__(VEC * sizeof(LT)))) LT vec_t;
+  vec_t held[HELD ? kHeld : 1];
+  if constexpr (HELD) {
+    // every load in flight at once, then the pass over registers
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) add((float)x[e]);
+    for (int k = 0; k < kHeld; ++k) {
+      const int i = tid + k * kRowThreads;
+      if (i < nv) held[k] = *(const vec_t*)(row + (int64_t)i * VEC);
     }
+    // the thread's max, then its sum of exp2(x log2e - max): no rescaling
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k)
+      if (tid + k * kRowThreads < nv) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) mx = fmaxf(mx, (float)held[k][e]);
+      }
+    if (mx > -INFINITY) {
+      m = mx * kLog2e;
+#pragma unroll
+      for (int k = 0; k < kHeld; ++k)
+        if (tid + k * kRowThreads < nv) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s += fast_exp2((float)held[k][e] * kLog2e - m);
+        }
+    }
+  } else {
+    for (int i = tid; i < nv; i += kRowThreads) {
+      if constexpr (VEC == 1) {
+        add(load_f(row + i));
+      } else {
+        const vec_t x = *(const vec_t*)(row + (int64_t)i * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) add((float)x[e]);
+      }
+    }
+    for (int v = nv * VEC + tid; v < V; v += kRowThreads) add(load_f(row + v));
   }
-  for (int v = nv * VEC + tid; v < V; v += kRowThreads) add(load_f(row + v));
   // combine (m, s) pairs: over the wave, then over the waves
   auto merge = [](float& m1, float& s1, float m2, float s2) {
     const float mm = fmaxf(m1, m2);
@@ -133,12 +164,29 @@ nll_row_kernel(const LT* __restrict__ logits, int V, const int32_t* __restrict__
   const double lse = ((double)m + log2((double)s)) * (double)kLn2;
   if (tid == 0) row_nll[c] = (float)(lse - (double)load_f(row + y));
   if (grow == nullptr) return;
-  // pass 2: (p - 1[v = y]) / N
+  // pass 2: (p - 1[v = y]) / N, with 1/N folded into the exponent
   const float inv_n = 1.f / (float)*count;
   const float lse2 = (float)(lse * (double)kLog2e);
-  for (int v = tid; v < V; v += kRowThreads) {
-    const float p = fast_exp2(load_f(row + v) * kLog2e - lse2);
-    grow[v] = (GT)((p - (v == y ? 1.f : 0.f)) * inv_n);
+  const float lse2n = (float)(lse * (double)kLog2e + log2((double)*count));
+  if constexpr (HELD) {
+    typedef __attribute__((__vector_size__(VEC * sizeof(GT)))) GT gvec_t;
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+      const int i = tid + k * kRowThreads;
+      if (i < nv) {
+        gvec_t gv;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) gv[e] = (GT)fast_exp2((float)held[k][e] * kLog2e - lse2n);
+        if ((unsigned)(y - i * VEC) < (unsigned)VEC)      // this vector holds the target class
+          gv[y - i * VEC] = (GT)(fast_exp2((float)held[k][y - i * VEC] * kLog2e - lse2n) - inv_n);
+        *(gvec_t*)(grow + (int64_t)i * VEC) = gv;
+      }
+    }
+  } else {
+    for (int v = tid; v < V; v += kRowThreads) {
+      const float p = fast_exp2(load_f(row + v) * kLog2e - lse2);
+      grow[v] = (GT)((p - (v == y ? 1.f : 0.f)) * inv_n);
+    }
   }
 }
 
@@ -165,12 +213,18 @@ nll_sum_kernel(const float* __restrict__ row_nll, int64_t C, const int32_t* __re
 template <typename LT, typename GT>
 void launch_rows(const void* logits, int64_t C, int V, const int32_t* targets, const uint8_t* mask,
                  const int32_t* count, const int32_t* status, float* row_nll, void* grad, hipStream_t s) {
-  const bool vec = (V * sizeof(LT)) % 16 == 0 && ((uintptr_t)logits & 15) == 0;
-  if (vec)
-    nll_row_kernel<LT, GT, 16 / sizeof(LT)><<<dim3((unsigned)C), kRowThreads, 0, s>>>(
+  constexpr int VEC = 16 / sizeof(LT);
+  const bool vec = (V * sizeof(LT)) % 16 == 0 && ((uintptr_t)logits & 15) == 0 &&
+                   (grad == nullptr || ((uintptr_t)grad & 15) == 0);
+  const bool held = vec && V <= kHeld * VEC * kRowThreads;
+  if (held)
+    nll_row_kernel<LT, GT, VEC, true><<<dim3((unsigned)C), kRowThreads, 0, s>>>(
+        (const LT*)logits, V, targets, mask, count, status, row_nll, (GT*)grad);
+  else if (vec)
+    nll_row_kernel<LT, GT, VEC, false><<<dim3((unsigned)C), kRowThreads, 0, s>>>(
         (const LT*)logits, V, targets, mask, count, status, row_nll, (GT*)grad);
   else
-    nll_row_kernel<LT, GT, 1><<<dim3((unsigned)C), kRowThreads, 0, s>>>(
+    nll_row_kernel<LT, GT, 1, false><<<dim3((unsigned)C), kRowThreads, 0, s>>>(
         (const LT*)logits, V, targets, mask, count, status, row_nll, (GT*)grad);
 }
 
