@@ -17,7 +17,14 @@ O7 brute force -- the dense [T, T] permission matrix of "Permission depends on
    masked softmax over whole rows; rows with no permitted key give a zero
    mixture.  Tiny inputs only.
 
-All arrays are float64 numpy; inputs are [T, H, d].  LSE is natural-log,
+Grouped key/value heads ("Packing与 FlashAttention Varlen" section 5: the
+key/value view has h_k heads beside the query view's h): K and V may carry
+H_k heads with H a multiple of H_k; query head h reads key/value head
+h // (H / H_k) (consecutive query heads share a group -- a reading, the page
+gives only the shapes), and the gradient of a key/value head is the sum over
+its group's query heads.
+
+All arrays are float64 numpy; inputs are [T, H, d] (K, V: [T, H_k, d]).  LSE is natural-log,
 layout [H, T].  No blocking beyond a plain split of query rows into chunks
 (which changes no arithmetic inside a row).
 """
@@ -88,6 +95,13 @@ def segment_head_backward(q, k, v, do, scale):
     return dq, dk, dv
 
 
+def _group(q, k):
+    H, Hk = q.shape[1], k.shape[1]
+    if Hk <= 0 or H % Hk != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    return H // Hk
+
+
 def varlen_forward(q, k, v, cu, scale=None, heads=None):
     """O5 over the whole packed stream.  Returns (O [T,H,d], LSE [H,T]).
 
@@ -95,6 +109,7 @@ def varlen_forward(q, k, v, cu, scale=None, heads=None):
     left zero) so that large workloads can be checked on a sample.
     """
     T, H, d = q.shape
+    G = _group(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if int(cu[0]) != 0 or int(cu[-1]) != T:
@@ -106,29 +121,32 @@ def varlen_forward(q, k, v, cu, scale=None, heads=None):
         if e == s:
             continue
         for h in hs:
-            o, l = segment_head_forward(q[s:e, h], k[s:e, h], v[s:e, h], scale)
+            o, l = segment_head_forward(q[s:e, h], k[s:e, h // G], v[s:e, h // G], scale)
             out[s:e, h] = o
             lse[h, s:e] = l
     return out, lse
 
 
 def varlen_backward(q, k, v, do, cu, scale=None, heads=None):
-    """O6 over the whole packed stream.  Returns (dQ, dK, dV), each [T,H,d]."""
+    """O6 over the whole packed stream.  Returns (dQ [T,H,d], dK, dV [T,H_k,d]).
+
+    With ``heads``, dK and dV hold only those query heads' contributions."""
     T, H, d = q.shape
+    G = _group(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = np.zeros((T, H, d))
-    dk = np.zeros((T, H, d))
-    dv = np.zeros((T, H, d))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
     hs = range(H) if heads is None else heads
     for s, e in _segments(cu):
         if e == s:
             continue
         for h in hs:
-            a, b, c = segment_head_backward(q[s:e, h], k[s:e, h], v[s:e, h], do[s:e, h], scale)
+            a, b, c = segment_head_backward(q[s:e, h], k[s:e, h // G], v[s:e, h // G], do[s:e, h], scale)
             dq[s:e, h] = a
-            dk[s:e, h] = b
-            dv[s:e, h] = c
+            dk[s:e, h // G] += b
+            dv[s:e, h // G] += c
     return dq, dk, dv
 
 

@@ -228,3 +228,64 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert not _close(o, ref)
     o, _ = A.varlen_forward(q, k, v, md["cu"], scale=1.0)  # scale forgotten
     assert not _close(o, ref)
+
+
+# ------------------------------------------------ grouped key/value heads
+
+def _gqa_inputs(lengths, H, Hk, d, seed):
+    rng = np.random.default_rng(seed)
+    T = sum(lengths)
+    q = rng.standard_normal((T, H, d))
+    k = rng.standard_normal((T, Hk, d))
+    v = rng.standard_normal((T, Hk, d))
+    do = rng.standard_normal((T, H, d))
+    return q, k, v, do
+
+
+def test_grouped_heads_match_torch_with_repeated_kv():
+    """H = 6 query heads over H_k = 2 key/value heads: torch fp64 SDPA on K/V
+    repeated per query head (repeat_interleave), with autograd summing the
+    key/value gradients over each group."""
+    lengths = [17, 0, 30, 1, 12]
+    H, Hk, d = 6, 2, 16
+    q, k, v, do = _gqa_inputs(lengths, H, Hk, d, 41)
+    md = P.packed_row_metadata(lengths)
+    o, _ = A.varlen_forward(q, k, v, md["cu"])
+    dq, dk, dv = A.varlen_backward(q, k, v, do, md["cu"])
+    assert dk.shape == k.shape and dv.shape == v.shape
+    seg = torch.tensor(md["seg"]); pos = torch.tensor(md["pos"])
+    mask = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous().requires_grad_() for x in (q, k, v))
+    G = H // Hk
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, dim=0), tv.repeat_interleave(G, dim=0), attn_mask=mask)
+    assert np.abs(o - out.detach().permute(1, 0, 2).numpy()).max() < 1e-12
+    out.backward(torch.from_numpy(do).permute(1, 0, 2))
+    for mine, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.abs(mine - ref.grad.permute(1, 0, 2).numpy()).max() < 1e-11
+
+
+def test_grouped_heads_finite_differences_on_shared_kv():
+    """dK of a shared head by central differences of sum(O * dO) (tiny case)."""
+    lengths = [4, 3]
+    H, Hk, d = 4, 2, 3
+    q, k, v, do = _gqa_inputs(lengths, H, Hk, d, 42)
+    cu = P.cu_seqlens_from_lengths(lengths)
+    _, dk, dv = A.varlen_backward(q, k, v, do, cu)
+    f = lambda kk, vv: float((A.varlen_forward(q, kk, vv, cu)[0] * do).sum())
+    h = 1e-6
+    for idx in [(0, 0, 0), (2, 1, 2), (5, 0, 1), (6, 1, 0)]:
+        kp, km = k.copy(), k.copy()
+        kp[idx] += h
+        km[idx] -= h
+        assert abs((f(kp, v) - f(km, v)) / (2 * h) - dk[idx]) < 1e-7
+        vp, vm = v.copy(), v.copy()
+        vp[idx] += h
+        vm[idx] -= h
+        assert abs((f(k, vp) - f(k, vm)) / (2 * h) - dv[idx]) < 1e-7
+
+
+def test_grouped_heads_reject_uneven_groups():
+    q, k, v, _ = _gqa_inputs([5], 3, 2, 4, 43)
+    with pytest.raises(ValueError):
+        A.varlen_forward(q, k, v, [0, 5])
