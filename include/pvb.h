@@ -22,9 +22,10 @@
  *   - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous [T, H, d] (token-major,
  *     then head, then feature): element (t, h, c) at offset (t*H + h)*d + c.
  *     LSE and the backward's D are fp32 [H, T].
- *   - Self-attention only: one cu_seqlens for queries and keys, H query heads =
- *     H key/value heads, d in {64, 128}.  The softmax scale is an argument
- *     (1/sqrt(d) is the usual value).
+ *   - Self-attention only: one cu_seqlens for queries and keys; d in {64, 128}.
+ *     H query heads = H key/value heads, or grouped key/value heads through
+ *     the *_gqa entry points.  The softmax scale is an argument (1/sqrt(d) is
+ *     the usual value).
  */
 #ifndef PVB_H
 #define PVB_H
@@ -248,6 +249,29 @@ pvb_status pvb_packed_nll(const void* d_logits, int32_t logits_dtype, int64_t C,
                           const int32_t* d_targets, const uint8_t* d_mask, float* d_row_nll,
                           double* d_loss, int32_t* d_count, void* d_grad, int32_t grad_dtype,
                           int32_t* d_status, void* stream);
+
+/* Grouped key/value heads ("Packing与 FlashAttention Varlen", section 5: the
+ * key view carries h_k heads beside the query view's h).  As
+ * pvb_varlen_attn_fwd / pvb_varlen_attn_bwd, with K and V (and dK, dV)
+ * [T, H_kv, d], H a multiple of H_kv: query head h reads key/value head
+ * h / (H / H_kv), and dK, dV of a key/value head sum the contributions of its
+ * H / H_kv query heads (each written once; no atomics).  Q, O, dO, dQ stay
+ * [T, H, d] and LSE [H, T]; the workspace size is that of the H-head call.
+ * H_kv = H is exactly the plain call.  Extra error: PVB_E_INVALID_ARG when
+ * H_kv <= 0 or H is not a multiple of H_kv. */
+pvb_status pvb_varlen_attn_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                   const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                   int32_t T, int32_t H, int32_t H_kv, int32_t d, float softmax_scale,
+                                   void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
+                                   void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                   void* stream);
+pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                   const void* d_o, int32_t o_dtype, const void* d_do,
+                                   const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                                   int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                   float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                   int32_t grad_dtype, int32_t precision, void* workspace,
+                                   size_t workspace_bytes, int32_t* d_status, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);

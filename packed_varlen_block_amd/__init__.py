@@ -32,7 +32,7 @@ STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "P
 
 # every symbol include/pvb.h declares
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
-           "pvb_packed_nll",
+           "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_status_string", "pvb_version")
 
@@ -65,9 +65,13 @@ def lib() -> ctypes.CDLL:
         L.pvb_varlen_attn_fwd.argtypes = [P, P, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P, P]
         L.pvb_varlen_attn_bwd.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, F,
                                           P, P, P, I32, I32, P, SZ, P, P]
+        L.pvb_varlen_attn_fwd_gqa.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ,
+                                              P, P]
+        L.pvb_varlen_attn_bwd_gqa.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
+                                              P, P, P, I32, I32, P, SZ, P, P]
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
                      "pvb_boundaries_from_positions", "pvb_packed_nll", "pvb_varlen_attn_fwd",
-                     "pvb_varlen_attn_bwd"):
+                     "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
         L.pvb_status_string.restype = ctypes.c_char_p
@@ -268,24 +272,29 @@ def _prec_code(p):
             PVB_PREC_SPLIT: PVB_PREC_SPLIT}[p]
 
 
-def _check_qkv(*ts):
+def _check_qkv(q, k, v, *rest):
+    """q (and dO) [T, H, d]; k, v [T, H_kv, d] with H a multiple of H_kv."""
     torch = _torch()
-    T, H, d = ts[0].shape
-    for t in ts:
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (T, H, d) or not t.is_cuda:
-            raise PvbError(1, "q/k/v/dO must be contiguous bf16 CUDA tensors of one shape [T, H, d]")
-    return T, H, d
+    T, H, d = q.shape
+    Hk = k.shape[1] if k.dim() == 3 else -1
+    for t, shape in [(q, (T, H, d)), (k, (T, Hk, d)), (v, (T, Hk, d))] + [(t, (T, H, d)) for t in rest]:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda:
+            raise PvbError(1, "q/dO [T, H, d] and k/v [T, H_kv, d] must be contiguous bf16 CUDA tensors")
+    if Hk <= 0 or H % Hk != 0:
+        raise PvbError(1, "the query heads must be a multiple of the key/value heads")
+    return T, H, Hk, d
 
 
 def varlen_attn_fwd(q, k, v, cu, h_cu=None, softmax_scale=None, o_dtype=None, precision="bf16",
                     out=None, lse=None, workspace=None, status=None):
     """Forward packed block-causal attention.  Returns (O [T,H,d], LSE [H,T] fp32, status).
 
-    q, k, v: contiguous bf16 CUDA [T, H, d]; cu: int32 CUDA [B+1]; h_cu: optional
-    host (numpy/list) mirror of cu, validated on the host.
+    q: contiguous bf16 CUDA [T, H, d]; k, v: [T, H_kv, d] (grouped heads when
+    H_kv < H: query head h reads key/value head h // (H / H_kv)); cu: int32
+    CUDA [B+1]; h_cu: optional host (numpy/list) mirror of cu, validated on the host.
     """
     torch = _torch()
-    T, H, d = _check_qkv(q, k, v)
+    T, H, Hk, d = _check_qkv(q, k, v)
     if cu.dtype != torch.int32 or not cu.is_cuda:
         raise PvbError(1, "cu must be an int32 CUDA tensor")
     n_seg = cu.numel() - 1
@@ -306,19 +315,21 @@ def varlen_attn_fwd(q, k, v, cu, h_cu=None, softmax_scale=None, o_dtype=None, pr
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
         if hc.size != n_seg + 1:
             raise PvbError(1, "h_cu must have B+1 entries")
-    rc = lib().pvb_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(hc), n_seg, T, H, d, scale,
-                                   _ptr(out), _dtype_code(out.dtype), _ptr(lse), _prec_code(precision),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _ptr(status), _stream(dev))
+    rc = lib().pvb_varlen_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(hc), n_seg, T, H, Hk, d,
+                                       scale, _ptr(out), _dtype_code(out.dtype), _ptr(lse),
+                                       _prec_code(precision), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(status),
+                                       _stream(dev))
     _check(rc, "varlen_attn_fwd")
     return out, lse, status
 
 
 def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad_dtype=None,
                     precision="bf16", dq=None, dk=None, dv=None, workspace=None, status=None):
-    """Backward.  Returns (dQ, dK, dV, status); grads are [T, H, d] in grad_dtype."""
+    """Backward.  Returns (dQ, dK, dV, status) in grad_dtype: dQ [T, H, d],
+    dK and dV [T, H_kv, d] (summed over each group's query heads)."""
     torch = _torch()
-    T, H, d = _check_qkv(q, k, v, do)
+    T, H, Hk, d = _check_qkv(q, k, v, do)
     if tuple(o.shape) != (T, H, d) or not o.is_contiguous():
         raise PvbError(1, "o must be contiguous [T, H, d]")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T) or not lse.is_contiguous():
@@ -329,8 +340,8 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad
     gcode = _dtype_code(grad_dtype)
     dev = q.device
     dq = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dq is None else dq
-    dk = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dk is None else dk
-    dv = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dv is None else dv
+    dk = torch.empty((T, Hk, d), dtype=grad_dtype, device=dev) if dk is None else dk
+    dv = torch.empty((T, Hk, d), dtype=grad_dtype, device=dev) if dv is None else dv
     nbytes = workspace_bytes(T, H, d, n_seg, True, gcode)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -341,10 +352,10 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
         if hc.size != n_seg + 1:
             raise PvbError(1, "h_cu must have B+1 entries")
-    rc = lib().pvb_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o.dtype), _ptr(do),
-                                   _ptr(lse), _ptr(cu), _ptr(hc), n_seg, T, H, d, scale,
-                                   _ptr(dq), _ptr(dk), _ptr(dv), gcode, _prec_code(precision),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _ptr(status), _stream(dev))
+    rc = lib().pvb_varlen_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o.dtype), _ptr(do),
+                                       _ptr(lse), _ptr(cu), _ptr(hc), n_seg, T, H, Hk, d, scale,
+                                       _ptr(dq), _ptr(dk), _ptr(dv), gcode, _prec_code(precision),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _ptr(status), _stream(dev))
     _check(rc, "varlen_attn_bwd")
     return dq, dk, dv, status

@@ -56,7 +56,7 @@ template <int D, bool SPLIT, typename GradT, bool DECODE>
 __global__ void __launch_bounds__(kThreads, 3)
 bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const bf16* __restrict__ dout, const float2* __restrict__ ld,
-                   const int32_t* __restrict__ cu, const WorkList wl, int H, int T, float scale,
+                   const int32_t* __restrict__ cu, const WorkList wl, int H, int Hk, int T, float scale,
                    float scale_log2, GradT* __restrict__ dk, GradT* __restrict__ dv) {
   constexpr int BN = kTile / 2, BM = kKvBM;
   constexpr int KSTEPS = D / 16;
@@ -77,22 +77,22 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   // its elements 4j .. 4j+3 (same lane, same C-layout position in both waves)
   __shared__ __attribute__((aligned(16))) float4 xbuf[2][4][64];
 
-  // work item: 128-key planner tile tau, its 64-key half, head h
-  const int tau = blockIdx.x / (2 * H);
-  const int rem = blockIdx.x - tau * 2 * H;
-  const int half = rem >= H ? 1 : 0;
-  const int h = rem - half * H;
+  // work item: 128-key planner tile tau, its 64-key half, key/value head hk;
+  // the walk covers the query tiles of each of the group's G query heads
+  const int tau = blockIdx.x / (2 * Hk);
+  const int rem = blockIdx.x - tau * 2 * Hk;
+  const int half = rem >= Hk ? 1 : 0;
+  const int hk = rem - half * Hk;
+  const int G = H / Hk;
   int2 tm;
   if (!work_item<kTile, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int k0 = ((L + kTile - 1) / kTile - 1 - tm.y) * kTile + BN * half;
   if (k0 >= L) return;                                 // empty half of a ragged last tile
-  const int rs = H * D;                                // row stride (elements)
-  const int64_t base = ((int64_t)seg0 * H + h) * D;
-  const bf16* qs = q + base;
-  const bf16* gs = dout + base;
-  const float2* lds_h = ld + (int64_t)h * T + seg0;
+  const int rs = H * D;                                // row stride of Q, dO (elements)
+  const int rs_kv = Hk * D;                            // row stride of K, V, dK, dV
+  const int64_t base_kv = ((int64_t)seg0 * Hk + hk) * D;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -103,11 +103,11 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   const int t_off = (g + 4 * ((lane & 15) >> 2)) * PB + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   // B operand of the first product: K rows (role 0) or V rows (role 1)
-  const bf16* fs = (role ? v : k) + base;
+  const bf16* fs = (role ? v : k) + base_kv;
   bf16x8 frag[KSTEPS];
   if (kcol < L) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) frag[s] = *(const bf16x8*)(fs + kcol * rs + 16 * s + 8 * g);
+    for (int s = 0; s < KSTEPS; ++s) frag[s] = *(const bf16x8*)(fs + kcol * rs_kv + 16 * s + 8 * g);
   } else {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) frag[s] = bf16x8{};
@@ -133,8 +133,22 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   };
   const int rec_kind = (2 * BM / 4) * w + lane >= BM ? 1 : 0;
   const uint32_t rec_off = (uint32_t)(rec_row() * 8 + rec_kind * 4);
-  auto stage = [&](int jq, int b) {
-    const int qt0 = jq * BM;
+  const int jq_lo = k0 / BM;
+  const int n_steps = (L + BM - 1) / BM - jq_lo;      // query tiles per query head
+  // The walk visits query tiles jq_lo.. of query head hk G, then of hk G + 1,
+  // and so on.  Staging runs ahead of the math, so it keeps its own cursor
+  // (query head sh, tile st), advanced one tile per call.
+  int sh = hk * G, st = jq_lo;
+  auto stage = [&](int b) {
+    const int qt0 = st * BM;
+    const int64_t base = ((int64_t)seg0 * H + sh) * D;
+    const bf16* qs = q + base;
+    const bf16* gs = dout + base;
+    const float2* lds_h = ld + (int64_t)sh * T + seg0;
+    if (++st * BM >= L) {
+      st = jq_lo;
+      ++sh;
+    }
     const uint32_t sb = lds_addr(ring[b]);
     const uint32_t lb = lds_addr(sLD[b]) + (uint32_t)(wu * (2 * BM / 4) * 4);
     if (qt0 + BM <= L) {
@@ -165,21 +179,22 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   for (int j = 0; j < DBLK; ++j) acc2[j] = f32x16{};
   float4* xb = xbuf[pair][0];
 
-  const int jq_lo = k0 / BM;
-  const int n_steps = (L + BM - 1) / BM - jq_lo;
+  const int n_walk = G * n_steps;
 #pragma unroll
   for (int i = 0; i < NST - 1; ++i)
-    if (i < n_steps) stage(jq_lo + i, i);
-  for (int t = 0; t < n_steps; ++t) {
+    if (i < n_walk) stage(i);
+  int tq = jq_lo;                                      // query tile of step t
+  for (int t = 0; t < n_walk; ++t) {
     const int b = t % NST;
-    const int qt0 = (jq_lo + t) * BM;
-    if (t + NST - 2 < n_steps) wait_vmcnt<(NST - 2) * COPIES>();
+    const int qt0 = tq * BM;
+    if (++tq * BM >= L) tq = jq_lo;
+    if (t + NST - 2 < n_walk) wait_vmcnt<(NST - 2) * COPIES>();
     else wait_vmcnt<0>();
     // every wave's copies of step t have landed, every wave is done with the
     // slot of step t - 1 (which now receives step t + NST - 1), and the odd
     // waves are done reading the P of step t - 1
     lds_barrier();
-    if (t + NST - 1 < n_steps) stage(jq_lo + (t + NST - 1), (t + NST - 1) % NST);
+    if (t + NST - 1 < n_walk) stage((t + NST - 1) % NST);
     const char* cQ = ring[b];
     const char* cdO = ring[b] + TILE_BYTES;
     const char* a_src = role ? cdO : cQ;         // rows of the first product
@@ -261,7 +276,7 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key < L) outp[base + (int64_t)key * rs + 32 * j + lq] = out_cast<GradT>(acc2[j][i] * oscale);
+      if (key < L) outp[base_kv + (int64_t)key * rs_kv + 32 * j + lq] = out_cast<GradT>(acc2[j][i] * oscale);
     }
 }
 
@@ -274,7 +289,7 @@ template <int D, bool SPLIT, typename GradT, bool DECODE, typename OT>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const OT* __restrict__ o, const float* __restrict__ lse,
-              float2* __restrict__ ld, const int32_t* __restrict__ cu, const WorkList wl, int H, int T,
+              float2* __restrict__ ld, const int32_t* __restrict__ cu, const WorkList wl, int H, int Hk, int T,
               float scale, float scale_log2, GradT* __restrict__ dq) {
   constexpr int BM = kTile, BN = kDqBN;
   constexpr int KSTEPS = D / 16;
@@ -284,17 +299,20 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
   __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * D];
 
   const int tau = blockIdx.x / H;
-  const int h = blockIdx.x - tau * H;
+  const HeadPair hp = head_of_slot(blockIdx.x - tau * H, H, Hk);
+  const int h = hp.h;
   int2 tm;
   if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int q0 = tm.y * BM;
-  const int rs = H * D;
+  const int rs = H * D;       // row stride of Q, dO, O, dQ (elements)
+  const int rs_kv = Hk * D;   // row stride of K, V
   const int64_t base = ((int64_t)seg0 * H + h) * D;
+  const int64_t base_kv = ((int64_t)seg0 * Hk + hp.hk) * D;
   const bf16* qs = q + base;
-  const bf16* ks = k + base;
-  const bf16* vs = v + base;
+  const bf16* ks = k + base_kv;
+  const bf16* vs = v + base_kv;
   const bf16* gs = dout + base;
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
@@ -347,14 +365,14 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
   const int q_last = min(q0 + BM, L) - 1;
   const int nkv = q_last / BN + 1;
   FullTileCopy<D, BN> full;
-  full.init(rs, w, lane);
+  full.init(rs_kv, w, lane);
   auto stage = [&](int row0, int b) {
     if (row0 + BN <= L) {
-      full.issue(ks, rs, row0, sK[b]);
-      full.issue(vs, rs, row0, sV[b]);
+      full.issue(ks, rs_kv, row0, sK[b]);
+      full.issue(vs, rs_kv, row0, sV[b]);
     } else {
-      stage_rows<D, BN>(ks, rs, row0, L, sK[b], w, lane);
-      stage_rows<D, BN>(vs, rs, row0, L, sV[b], w, lane);
+      stage_rows<D, BN>(ks, rs_kv, row0, L, sK[b], w, lane);
+      stage_rows<D, BN>(vs, rs_kv, row0, L, sV[b], w, lane);
     }
   };
   stage(0, 0);
@@ -473,30 +491,31 @@ BwdLayout bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
 
 template <int D, bool SPLIT, typename GradT, typename OT, bool DECODE>
 void launch_bwd_kernels(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const int32_t* cu, const WorkList& wl, int H, int T,
-                        size_t grid, float scale, float2* ld, void* dq, void* dk, void* dv,
+                        const float* lse, const int32_t* cu, const WorkList& wl, int H, int Hk, int T,
+                        size_t cap, float scale, float2* ld, void* dq, void* dk, void* dv,
                         hipStream_t s) {
   // dQ first: it also writes the {LSE log2e, D} records the dK/dV kernel reads
-  bwd_dq_kernel<D, SPLIT, GradT, DECODE, OT><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+  // one dQ workgroup per (tile, query head); one dK/dV workgroup per (64-key
+  // half tile, key/value head), walking the query tiles of the group's heads
+  bwd_dq_kernel<D, SPLIT, GradT, DECODE, OT><<<dim3((unsigned)(cap * H)), kThreads, 0, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const OT*)o, lse, ld, cu, wl,
-      H, T, scale, scale * kLog2e, (GradT*)dq);
-  bwd_kv_pair_kernel<D, SPLIT, GradT, DECODE><<<dim3((unsigned)(2 * grid)), kThreads, 0, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, T, scale,
+      H, Hk, T, scale, scale * kLog2e, (GradT*)dq);
+  bwd_kv_pair_kernel<D, SPLIT, GradT, DECODE><<<dim3((unsigned)(2 * cap * Hk)), kThreads, 0, s>>>(
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, Hk, T, scale,
       scale * kLog2e, (GradT*)dk, (GradT*)dv);
 }
 
 template <int D, bool SPLIT, typename GradT, typename OT>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, const int32_t* cu, const WorkList& wl, int H, int T,
+                      const float* lse, const int32_t* cu, const WorkList& wl, int H, int Hk, int T,
                       size_t cap, float scale, float2* ld, void* dq, void* dk, void* dv,
                       hipStream_t s) {
-  const size_t grid = cap * (size_t)H;
-  if (grid > 0) {
+  if (cap > 0) {
     if (wl.tiles == nullptr)
-      launch_bwd_kernels<D, SPLIT, GradT, OT, true>(q, k, v, o, dout, lse, cu, wl, H, T, grid, scale, ld,
+      launch_bwd_kernels<D, SPLIT, GradT, OT, true>(q, k, v, o, dout, lse, cu, wl, H, Hk, T, cap, scale, ld,
                                                     dq, dk, dv, s);
     else
-      launch_bwd_kernels<D, SPLIT, GradT, OT, false>(q, k, v, o, dout, lse, cu, wl, H, T, grid, scale, ld,
+      launch_bwd_kernels<D, SPLIT, GradT, OT, false>(q, k, v, o, dout, lse, cu, wl, H, Hk, T, cap, scale, ld,
                                                      dq, dk, dv, s);
   }
   return hipGetLastError();
@@ -512,15 +531,16 @@ size_t attn_bwd_workspace_bytes(int32_t T, int32_t H, int32_t d, int32_t n_seg, 
 
 }  // namespace pvb
 
-extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v,
-                                          const void* d_o, int32_t o_dtype, const void* d_do,
-                                          const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
-                                          int32_t n_seg, int32_t T, int32_t H, int32_t d,
-                                          float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
-                                          int32_t grad_dtype, int32_t precision, void* workspace,
-                                          size_t workspace_bytes, int32_t* d_status, void* stream) {
+extern "C" pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                              const void* d_o, int32_t o_dtype, const void* d_do,
+                                              const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                                              int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                              float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                              int32_t grad_dtype, int32_t precision, void* workspace,
+                                              size_t workspace_bytes, int32_t* d_status, void* stream) {
   using namespace pvb;
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
+  if (H_kv <= 0 || H % H_kv != 0) return PVB_E_INVALID_ARG;
   if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_o == nullptr ||
                 d_do == nullptr || d_lse == nullptr || d_dq == nullptr || d_dk == nullptr ||
                 d_dv == nullptr))
@@ -555,7 +575,7 @@ extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, cons
   const bool split = precision == PVB_PREC_SPLIT, gf32 = grad_dtype == PVB_F32, of32 = o_dtype == PVB_F32;
   hipError_t e = hipSuccess;
 #define PVB_BWD(D_, S_, G_, O_)                                                                    \
-  e = launch_bwd<D_, S_, G_, O_>(d_q, d_k, d_v, d_o, d_do, d_lse, d_cu, wl, H, T, cap,          \
+  e = launch_bwd<D_, S_, G_, O_>(d_q, d_k, d_v, d_o, d_do, d_lse, d_cu, wl, H, H_kv, T, cap,    \
                                  softmax_scale, ld, d_dq, d_dk, d_dv, s)
 #define PVB_BWD_O(D_, S_, G_) \
   if (of32) PVB_BWD(D_, S_, G_, float); else PVB_BWD(D_, S_, G_, bf16)
@@ -570,4 +590,16 @@ extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, cons
 #undef PVB_BWD_O
 #undef PVB_BWD
   return e == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+
+extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v,
+                                          const void* d_o, int32_t o_dtype, const void* d_do,
+                                          const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                                          int32_t n_seg, int32_t T, int32_t H, int32_t d,
+                                          float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                          int32_t grad_dtype, int32_t precision, void* workspace,
+                                          size_t workspace_bytes, int32_t* d_status, void* stream) {
+  return pvb_varlen_attn_bwd_gqa(d_q, d_k, d_v, d_o, o_dtype, d_do, d_lse, d_cu, h_cu, n_seg, T, H, H, d,
+                                 softmax_scale, d_dq, d_dk, d_dv, grad_dtype, precision, workspace,
+                                 workspace_bytes, d_status, stream);
 }

@@ -34,7 +34,7 @@ template <int D, bool SPLIT, typename OutT, bool DECODE, int BN>
 __global__ void __launch_bounds__(kFwdThreads, BN == 32 ? 3 : 2)
 attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const bf16* __restrict__ v, const int32_t* __restrict__ cu,
-                const WorkList wl, int H, int T,
+                const WorkList wl, int H, int Hk, int T,
                 float scale_log2, OutT* __restrict__ o, float* __restrict__ lse) {
   constexpr int BM = kFwdBM;
   constexpr int NB = BN / 32;    // 32-key blocks per tile
@@ -49,17 +49,20 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * D];
 
   const int tau = blockIdx.x / H;
-  const int h = blockIdx.x - tau * H;
+  const HeadPair hp = head_of_slot(blockIdx.x - tau * H, H, Hk);
+  const int h = hp.h;
   int2 tm;
   if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
   const int L = cu[tm.x + 1] - seg0;
   const int q0 = tm.y * BM;
-  const int rs = H * D;  // row stride (elements)
+  const int rs = H * D;      // row stride of Q and O (elements)
+  const int rs_kv = Hk * D;  // row stride of K and V
   const int64_t base = ((int64_t)seg0 * H + h) * D;
+  const int64_t base_kv = ((int64_t)seg0 * Hk + hp.hk) * D;
   const bf16* qs = q + base;
-  const bf16* ks = k + base;
-  const bf16* vs = v + base;
+  const bf16* ks = k + base_kv;
+  const bf16* vs = v + base_kv;
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -88,14 +91,14 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int nkv = q_last / BN + 1;
 
   FullTileCopy<D, BN> full;
-  full.init(rs, w, lane);
+  full.init(rs_kv, w, lane);
   auto stage = [&](int row0, int b) {
     if (row0 + BN <= L) {
-      full.issue(ks, rs, row0, sK[b]);
-      full.issue(vs, rs, row0, sV[b]);
+      full.issue(ks, rs_kv, row0, sK[b]);
+      full.issue(vs, rs_kv, row0, sV[b]);
     } else {
-      stage_rows<D, BN>(ks, rs, row0, L, sK[b], w, lane);
-      stage_rows<D, BN>(vs, rs, row0, L, sV[b], w, lane);
+      stage_rows<D, BN>(ks, rs_kv, row0, L, sK[b], w, lane);
+      stage_rows<D, BN>(vs, rs_kv, row0, L, sV[b], w, lane);
     }
   };
   stage(0, 0);
@@ -217,23 +220,23 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <int D, bool SPLIT, typename OutT, int BN>
 void launch_fwd_bn(const void* q, const void* k, const void* v, const int32_t* cu, const WorkList& wl,
-                   int H, int T, size_t grid, float scale_log2, void* o, float* lse, hipStream_t s) {
+                   int H, int Hk, int T, size_t grid, float scale_log2, void* o, float* lse, hipStream_t s) {
   if (wl.tiles == nullptr)
     attn_fwd_kernel<D, SPLIT, OutT, true, BN><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse);
   else
     attn_fwd_kernel<D, SPLIT, OutT, false, BN><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, T, scale_log2, (OutT*)o, lse);
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse);
 }
 
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
-                      const WorkList& wl, int H, int T, size_t cap, float scale_log2, void* o,
+                      const WorkList& wl, int H, int Hk, int T, size_t cap, float scale_log2, void* o,
                       float* lse, bool short_keys, hipStream_t s) {
   const size_t grid = cap * (size_t)H;
   if (grid == 0) return hipSuccess;
-  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, T, grid, scale_log2, o, lse, s);
-  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, T, grid, scale_log2, o, lse, s);
+  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, s);
+  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, s);
   return hipGetLastError();
 }
 
@@ -247,14 +250,15 @@ size_t attn_fwd_workspace_bytes(int32_t T, int32_t n_seg) { return fwd_workspace
 
 }  // namespace pvb
 
-extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, const void* d_v,
-                                          const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
-                                          int32_t T, int32_t H, int32_t d, float softmax_scale,
-                                          void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
-                                          void* workspace, size_t workspace_bytes, int32_t* d_status,
-                                          void* stream) {
+extern "C" pvb_status pvb_varlen_attn_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                              const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                              int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                              float softmax_scale, void* d_o, int32_t o_dtype, float* d_lse,
+                                              int32_t precision, void* workspace, size_t workspace_bytes,
+                                              int32_t* d_status, void* stream) {
   using namespace pvb;
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
+  if (H_kv <= 0 || H % H_kv != 0) return PVB_E_INVALID_ARG;
   if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_o == nullptr || d_lse == nullptr))
     return PVB_E_INVALID_ARG;
   if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
@@ -286,7 +290,7 @@ extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, cons
   const bool split = precision == PVB_PREC_SPLIT, f32 = o_dtype == PVB_F32;
   hipError_t e;
 #define PVB_FWD(D_, S_, T_) \
-  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, T, cap, sl2, d_o, d_lse, short_keys, s)
+  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, H_kv, T, cap, sl2, d_o, d_lse, short_keys, s)
   if (d == 128) {
     if (split) { if (f32) PVB_FWD(128, true, float); else PVB_FWD(128, true, bf16); }
     else { if (f32) PVB_FWD(128, false, float); else PVB_FWD(128, false, bf16); }
@@ -296,4 +300,14 @@ extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, cons
   }
 #undef PVB_FWD
   return e == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+
+extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, const void* d_v,
+                                          const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                          int32_t T, int32_t H, int32_t d, float softmax_scale,
+                                          void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
+                                          void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                          void* stream) {
+  return pvb_varlen_attn_fwd_gqa(d_q, d_k, d_v, d_cu, h_cu, n_seg, T, H, H, d, softmax_scale, d_o, o_dtype,
+                                 d_lse, precision, workspace, workspace_bytes, d_status, stream);
 }

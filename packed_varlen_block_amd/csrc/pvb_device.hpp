@@ -314,6 +314,20 @@ __device__ bool decode_work_item(const int32_t* __restrict__ cu, int n_seg, int 
   return false;                                  // not reached
 }
 
+// Query head h and key/value head hk of head slot r in [0, H) (grouped heads:
+// query head h reads key/value head h / (H / Hk)).  Slot r = gi Hk + hk puts
+// the query heads of one group Hk slots apart, so with Hk a multiple of 8 a
+// group's workgroups land on one XCD (and share its L2) under the
+// round-robin dispatch of workgroups over the XCDs.  Hk = H gives h = r.
+struct HeadPair {
+  int h, hk;
+};
+__device__ __forceinline__ HeadPair head_of_slot(int r, int H, int Hk) {
+  if (Hk == H) return {r, r};   // one query head per key/value head: no division
+  const int hk = r % Hk;
+  return {hk * (H / Hk) + r / Hk, hk};
+}
+
 // The item of workgroup tau: from the planner list, or decoded in place.
 template <int TILE, bool DECODE>
 __device__ __forceinline__ bool work_item(const WorkList& wl, const int32_t* __restrict__ cu, int T, int tau,

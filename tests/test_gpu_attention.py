@@ -252,3 +252,50 @@ def test_bad_device_cu_backward_and_planner_path():
         pvb.check_status(st)
     assert e.value.status == 4
     assert (out == 7.0).all()
+
+
+# ------------------------------------------------ grouped key/value heads
+
+GQA_CASES = [([5, 3, 4], 4, 2, 64), ([200, 1, 0, 130, 64, 65], 6, 1, 128), ([1030], 8, 2, 128),
+             ([255, 1800], 4, 1, 128), ([300, 77], 8, 8, 128)]
+
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+def test_grouped_heads_forward_backward(grad_dtype):
+    import packed_varlen_block_amd as pvb
+    for i, (lengths, H, Hk, d) in enumerate(GQA_CASES):
+        say(f"gqa lengths={lengths} H={H} H_kv={Hk} d={d} g={grad_dtype}")
+        w = W.random_small(500 + i, lengths, H=H, d=d, backward=True)
+        kb = np.ascontiguousarray(w.k[:, :Hk])
+        vb = np.ascontiguousarray(w.v[:, :Hk])
+        q, k, v, do = dev_bf16(w.q), dev_bf16(kb), dev_bf16(vb), dev_bf16(w.do)
+        cu = dev_cu(w.lengths)
+        o, lse, st = pvb.varlen_attn_fwd(q, k, v, cu)
+        pvb.check_status(st)
+        gd = __import__("torch").float32 if grad_dtype == "f32" else __import__("torch").bfloat16
+        dq, dk, dv, st = pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, grad_dtype=gd)
+        pvb.check_status(st)
+        assert tuple(dk.shape) == tuple(dv.shape) == (w.T, Hk, d)
+        qo, ko, vo, doo = (W.bf16_bits_to_f64(x) for x in (w.q, kb, vb, w.do))
+        cuh = host_cu(w.lengths)
+        ro, rl = A.varlen_forward(qo, ko, vo, cuh)
+        check("O", to64(o), ro)
+        check("LSE", lse.double().cpu().numpy(), rl, max_abs=1e-3, mean_abs=1e-4)
+        rq, rk, rv = A.varlen_backward(qo, ko, vo, doo, cuh)
+        check("dQ", to64(dq), rq)
+        # dK, dV sum H / H_kv query heads, so they grow with the group; stored
+        # in bf16 they carry one rounding of up to 2^-9 of their magnitude on
+        # top of the bar
+        for name, got, ref in (("dK", dk, rk), ("dV", dv, rv)):
+            extra = 2.0 ** -9 * float(np.abs(ref).max()) if grad_dtype == "bf16" else 0.0
+            check(name, to64(got), ref, max_abs=2e-2 + extra)
+
+
+def test_grouped_heads_rejects_uneven_groups():
+    import packed_varlen_block_amd as pvb
+    import torch
+    q = torch.zeros((8, 3, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((8, 2, 64), dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, 8], dtype=torch.int32, device="cuda")
+    with pytest.raises(pvb.PvbError):
+        pvb.varlen_attn_fwd(q, k, k, cu)
