@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-long-case", action="store_true")
     ap.add_argument("--no-meta-case", action="store_true")
     ap.add_argument("--no-loss-case", action="store_true")
+    ap.add_argument("--no-gqa-case", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -253,6 +254,8 @@ def main():
         out["boundaries_from_positions"] = boundary_compilation(torch, pvb, W, dev, stream, a.seed)
     if not a.no_loss_case:
         out["packed_loss"] = packed_loss(torch, pvb, dev, stream, a.seed)
+    if not a.no_gqa_case:
+        out["grouped_heads"] = grouped_heads(torch, pvb, dev, stream, a.seed)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -370,6 +373,41 @@ def boundary_compilation(torch, pvb, W, dev, stream, seed, reps=50):
     return {"workload": "positions_T32768_long_mixed", "segments": n,
             "median_us": round(float(np.median(ms)) * 1e3, 2),
             "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+
+
+def grouped_heads(torch, pvb, dev, stream, seed, T=8192, H=32, Hk=8, d=128, reps=5):
+    """The T=8192 pack (one segment) with 32 query heads over 8 key/value heads
+    (grouped heads; the pages give no grouped configuration, this ratio is a
+    common one): forward and backward as in the main step (O bf16, fp32
+    gradients), useful TFLOP/s counted on the query heads, median of reps."""
+    g = torch.Generator(device=dev).manual_seed(seed + 7)
+    rnd = lambda *shape: (torch.randn(shape, generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    q, k, v, do = rnd(T, H, d), rnd(T, Hk, d), rnd(T, Hk, d), (torch.randn((T, H, d), generator=g, device=dev)).to(torch.bfloat16)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    dk, dv = (torch.empty((T, Hk, d), dtype=torch.float32, device=dev) for _ in range(2))
+    wf = torch.empty(pvb.workspace_bytes(T, H, d, 1, False), dtype=torch.uint8, device=dev)
+    wb = torch.empty(pvb.workspace_bytes(T, H, d, 1, True, pvb.PVB_F32), dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = []
+    for i in range(2 + reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        pvb.varlen_attn_fwd(q, k, v, cu, out=o, lse=lse, workspace=wf, status=st)
+        e[1].record(stream)
+        pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, dq=dq, dk=dk, dv=dv, workspace=wb, status=st)
+        e[2].record(stream)
+        if i >= 2:
+            ev.append(e)
+    torch.cuda.synchronize()
+    pvb.check_status(st)
+    fwd = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+    F = useful_fwd_flops([T], H, d)
+    return {"workload": "gqa_T8192_H32_Hkv8_d128", "pass": "fwd+bwd", "fwd_ms": round(fwd, 4),
+            "bwd_ms": round(bwd, 4), "useful_tflops": round(3.5 * F / ((fwd + bwd) * 1e-3) / 1e12, 2)}
 
 
 def packed_loss(torch, pvb, dev, stream, seed, C=8192, V=32768, reps=20):
