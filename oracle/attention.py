@@ -24,6 +24,16 @@ h // (H / H_k) (consecutive query heads share a group -- a reading, the page
 gives only the shapes), and the gradient of a key/value head is the sum over
 its group's query heads.
 
+Separate query and key boundaries and local windows (first page, section 5:
+cu_seqlens_q and cu_seqlens_k give each slice its own query and key extents,
+L_q and L_k; the causal clamp is aligned to the bottom right by L_k - L_q and
+widened by a right window; a local window also bounds it on the left).
+Reading, with delta = L_k - L_q: query i (local) may use key j (local) when
+0 <= j < L_k, j <= i + delta + window_right (window_right >= 0; -1 = no
+bound) and j >= i + delta - window_left (window_left >= 0; -1 = no bound).
+Causal self-attention is window (-1, 0) with cu_k = cu_q.  A query with no
+permitted key gets a zero output and LSE = -inf, and passes no gradient.
+
 All arrays are float64 numpy; inputs are [T, H, d] (K, V: [T, H_k, d]).  LSE is natural-log,
 layout [H, T].  No blocking beyond a plain split of query rows into chunks
 (which changes no arithmetic inside a row).
@@ -206,3 +216,115 @@ def dense_masked_forward(q, k, v, seg, pos, valid, scale=None):
             e = np.exp(row - m)
             out[i, h] = (e / e.sum()) @ v[:, h]
     return out
+
+
+# ---------------------------------------------------------------------------
+# separate query/key extents and local windows
+# ---------------------------------------------------------------------------
+
+def band_allowed(Lq, Lk, window_left=-1, window_right=0):
+    """[Lq, Lk] permission of query i to key j (local indices)."""
+    delta = Lk - Lq
+    i = np.arange(Lq)[:, None]
+    j = np.arange(Lk)[None, :]
+    ok = np.ones((Lq, Lk), dtype=bool)
+    if window_right >= 0:
+        ok &= j <= i + delta + window_right
+    if window_left >= 0:
+        ok &= j >= i + delta - window_left
+    return ok
+
+
+def segment_head_forward_band(q, k, v, scale, window_left=-1, window_right=0):
+    """One segment and head with extents L_q = len(q), L_k = len(k).
+    Returns (O [L_q, d], LSE [L_q])."""
+    Lq, Lk = q.shape[0], k.shape[0]
+    out = np.zeros((Lq, v.shape[1]))
+    lse = np.full(Lq, -np.inf)
+    if Lq == 0 or Lk == 0:
+        return out, lse
+    ok = band_allowed(Lq, Lk, window_left, window_right)
+    for r0 in range(0, Lq, ROW_CHUNK):
+        r1 = min(Lq, r0 + ROW_CHUNK)
+        s = np.where(ok[r0:r1], scale * (q[r0:r1] @ k.T), -np.inf)
+        for r in range(r1 - r0):
+            row = s[r]
+            if not ok[r0 + r].any():
+                continue                                   # no permitted key
+            m = row.max()
+            e = np.exp(row - m)
+            z = e.sum()
+            out[r0 + r] = (e / z) @ v
+            lse[r0 + r] = m + math.log(z)
+    return out, lse
+
+
+def segment_head_backward_band(q, k, v, do, scale, window_left=-1, window_right=0):
+    """Gradients of sum(O * dO) for one segment and head; returns (dq, dk, dv)."""
+    Lq, Lk = q.shape[0], k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if Lq == 0 or Lk == 0:
+        return dq, dk, dv
+    ok = band_allowed(Lq, Lk, window_left, window_right)
+    for i in range(Lq):
+        if not ok[i].any():
+            continue
+        s = np.where(ok[i], scale * (k @ q[i]), -np.inf)
+        m = s.max()
+        e = np.exp(s - m)
+        p = e / e.sum()
+        dp = v @ do[i]
+        ds = p * (dp - (p * dp).sum())
+        dv += np.outer(p, do[i])
+        dq[i] = scale * (ds @ k)
+        dk += scale * np.outer(ds, q[i])
+    return dq, dk, dv
+
+
+def _check_cu(cu, T, what):
+    if int(cu[0]) != 0 or int(cu[-1]) != T:
+        raise ValueError(f"{what} must start at 0 and end at the token count")
+
+
+def varlen_cross_forward(q, k, v, cu_q, cu_k, scale=None, window=(-1, 0), heads=None):
+    """Forward over a packed stream with separate query/key boundaries (same
+    number of slices).  Returns (O [T_q,H,d], LSE [H,T_q])."""
+    Tq, H, d = q.shape
+    G = _group(q, k)
+    if len(cu_q) != len(cu_k):
+        raise ValueError("query and key boundaries must have the same number of slices")
+    _check_cu(cu_q, Tq, "cu_q")
+    _check_cu(cu_k, k.shape[0], "cu_k")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((Tq, H, d))
+    lse = np.full((H, Tq), -np.inf)
+    hs = range(H) if heads is None else heads
+    for (qs, qe), (ks, ke) in zip(_segments(cu_q), _segments(cu_k)):
+        for h in hs:
+            o, l = segment_head_forward_band(q[qs:qe, h], k[ks:ke, h // G], v[ks:ke, h // G], scale, *window)
+            out[qs:qe, h] = o
+            lse[h, qs:qe] = l
+    return out, lse
+
+
+def varlen_cross_backward(q, k, v, do, cu_q, cu_k, scale=None, window=(-1, 0), heads=None):
+    """Backward of varlen_cross_forward: (dQ [T_q,H,d], dK, dV [T_k,H_k,d])."""
+    Tq, H, d = q.shape
+    G = _group(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((Tq, H, d))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    hs = range(H) if heads is None else heads
+    for (qs, qe), (ks, ke) in zip(_segments(cu_q), _segments(cu_k)):
+        for h in hs:
+            a, b, c = segment_head_backward_band(q[qs:qe, h], k[ks:ke, h // G], v[ks:ke, h // G],
+                                                 do[qs:qe, h], scale, *window)
+            dq[qs:qe, h] = a
+            dk[ks:ke, h // G] += b
+            dv[ks:ke, h // G] += c
+    return dq, dk, dv

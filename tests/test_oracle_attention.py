@@ -289,3 +289,106 @@ def test_grouped_heads_reject_uneven_groups():
     q, k, v, _ = _gqa_inputs([5], 3, 2, 4, 43)
     with pytest.raises(ValueError):
         A.varlen_forward(q, k, v, [0, 5])
+
+
+# ------------------------------------- separate query/key extents, windows
+
+def _cross_inputs(lq, lk, H, Hk, d, seed):
+    rng = np.random.default_rng(seed)
+    Tq, Tk = sum(lq), sum(lk)
+    return (rng.standard_normal((Tq, H, d)), rng.standard_normal((Tk, Hk, d)),
+            rng.standard_normal((Tk, Hk, d)), rng.standard_normal((Tq, H, d)))
+
+
+def test_band_self_causal_equals_causal_oracle():
+    lengths = [37, 1, 0, 64, 15]
+    q, k, v, do = _cross_inputs(lengths, lengths, 3, 3, 16, 51)
+    cu = P.cu_seqlens_from_lengths(lengths)
+    o1, l1 = A.varlen_forward(q, k, v, cu)
+    o2, l2 = A.varlen_cross_forward(q, k, v, cu, cu)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-12
+    g1 = A.varlen_backward(q, k, v, do, cu)
+    g2 = A.varlen_cross_backward(q, k, v, do, cu, cu)
+    for a, b in zip(g1, g2):
+        assert np.abs(a - b).max() < 1e-11
+
+
+def _torch_band_mask(lq, lk, wl, wr):
+    """The permission written with torch index ops, per slice, as a dense
+    block-diagonal [T_q, T_k] mask."""
+    Tq, Tk = sum(lq), sum(lk)
+    mask = torch.zeros((Tq, Tk), dtype=torch.bool)
+    q0 = k0 = 0
+    for a, b in zip(lq, lk):
+        i = torch.arange(a)[:, None]
+        j = torch.arange(b)[None, :]
+        m = torch.ones((a, b), dtype=torch.bool)
+        if wr >= 0:
+            m &= j - i <= (b - a) + wr
+        if wl >= 0:
+            m &= j - i >= (b - a) - wl
+        mask[q0:q0 + a, k0:k0 + b] = m
+        q0 += a
+        k0 += b
+    return mask
+
+
+@pytest.mark.parametrize("lq,lk,window", [
+    ([9, 20, 5, 0], [20, 9, 5, 3], (-1, 0)),      # cross, causal aligned bottom-right
+    ([9, 20, 5], [20, 9, 5], (-1, -1)),           # cross, no clamp
+    ([30, 17], [30, 17], (4, 0)),                 # self, sliding window of 4 back
+    ([12, 25], [25, 12], (3, 2)),                 # cross, two-sided local window
+])
+def test_band_matches_torch_sdpa_and_autograd(lq, lk, window):
+    H, Hk, d = 4, 2, 8
+    q, k, v, do = _cross_inputs(lq, lk, H, Hk, d, 52)
+    cq, ck = P.cu_seqlens_from_lengths(lq), P.cu_seqlens_from_lengths(lk)
+    o, lse = A.varlen_cross_forward(q, k, v, cq, ck, window=window)
+    dq, dk, dv = A.varlen_cross_backward(q, k, v, do, cq, ck, window=window)
+    mask = _torch_band_mask(lq, lk, *window)
+    rows = mask.any(dim=1)                          # queries with a permitted key
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).contiguous().requires_grad_() for x in (q, k, v))
+    G = H // Hk
+    kk, vv = tk.repeat_interleave(G, dim=0), tv.repeat_interleave(G, dim=0)
+    out = torch.nn.functional.scaled_dot_product_attention(tq[:, rows], kk, vv, attn_mask=mask[rows])
+    ref = out.detach().permute(1, 0, 2).numpy()
+    assert np.abs(o[rows.numpy()] - ref).max() < 1e-12
+    assert np.all(o[~rows.numpy()] == 0) and np.all(np.isneginf(lse[:, ~rows.numpy()]))
+    out.backward(torch.from_numpy(do[rows.numpy()]).permute(1, 0, 2))
+    for mine, ref_t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.abs(mine - ref_t.grad.permute(1, 0, 2).numpy()).max() < 1e-11
+
+
+def test_band_closed_form_single_key_window():
+    """window (0, 0): query i sees exactly key i + L_k - L_q, so O_i = v of that
+    key and LSE_i = scale q_i . k; queries with no such key get zeros."""
+    lq, lk = [6, 4], [4, 7]
+    q, k, v, _ = _cross_inputs(lq, lk, 2, 2, 5, 53)
+    cq, ck = P.cu_seqlens_from_lengths(lq), P.cu_seqlens_from_lengths(lk)
+    o, lse = A.varlen_cross_forward(q, k, v, cq, ck, window=(0, 0))
+    s = 1 / math.sqrt(5)
+    for b in range(2):
+        for i in range(lq[b]):
+            j = i + lk[b] - lq[b]
+            t = cq[b] + i
+            if 0 <= j < lk[b]:
+                assert np.allclose(o[t], v[ck[b] + j]) and np.allclose(lse[:, t], s * (q[t] * k[ck[b] + j]).sum(-1))
+            else:
+                assert np.all(o[t] == 0) and np.all(np.isneginf(lse[:, t]))
+
+
+def test_band_finite_differences():
+    lq, lk = [5, 3], [3, 6]
+    q, k, v, do = _cross_inputs(lq, lk, 2, 1, 3, 54)
+    cq, ck = P.cu_seqlens_from_lengths(lq), P.cu_seqlens_from_lengths(lk)
+    w = (2, 1)
+    dq, dk, dv = A.varlen_cross_backward(q, k, v, do, cq, ck, window=w)
+    f = lambda qq, kk, vv: float((A.varlen_cross_forward(qq, kk, vv, cq, ck, window=w)[0] * do).sum())
+    h = 1e-6
+    for arr, grad, idx in ((q, dq, (1, 1, 2)), (q, dq, (6, 0, 0)), (k, dk, (4, 0, 1)), (v, dv, (7, 0, 2))):
+        ap, am = arr.copy(), arr.copy()
+        ap[idx] += h
+        am[idx] -= h
+        args_p = [ap if x is arr else x for x in (q, k, v)]
+        args_m = [am if x is arr else x for x in (q, k, v)]
+        assert abs((f(*args_p) - f(*args_m)) / (2 * h) - grad[idx]) < 1e-7
