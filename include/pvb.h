@@ -22,10 +22,11 @@
  *   - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous [T, H, d] (token-major,
  *     then head, then feature): element (t, h, c) at offset (t*H + h)*d + c.
  *     LSE and the backward's D are fp32 [H, T].
- *   - Self-attention only: one cu_seqlens for queries and keys; d in {64, 128}.
- *     H query heads = H key/value heads, or grouped key/value heads through
- *     the *_gqa entry points.  The softmax scale is an argument (1/sqrt(d) is
- *     the usual value).
+ *   - d in {64, 128}.  Causal self-attention takes one cu_seqlens for queries
+ *     and keys; the *_cross_* entry points take separate query and key
+ *     boundaries and a local window.  H query heads = H key/value heads, or
+ *     grouped key/value heads through the *_gqa and *_cross_* entry points.
+ *     The softmax scale is an argument (1/sqrt(d) is the usual value).
  */
 #ifndef PVB_H
 #define PVB_H
@@ -272,6 +273,54 @@ pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, const void*
                                    float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
                                    int32_t grad_dtype, int32_t precision, void* workspace,
                                    size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* ------------------------------------------------- cross attention, local windows */
+
+/* Separate query and key boundaries with a local window ("Packing与
+ * FlashAttention Varlen", section 5: cu_seqlens_q / cu_seqlens_k, the key
+ * extent L_k of a slice, the causal clamp moved by L_k - L_q and widened by
+ * window_right, and the per-row key range of a sliding window).  Segment b
+ * pairs queries [cu_q[b], cu_q[b+1]) with keys [cu_k[b], cu_k[b+1]); with
+ * L_q, L_k its extents and delta = L_k - L_q, local query row r may use local
+ * keys j with
+ *   max(0, r + delta - window_left) <= j <= min(L_k - 1, r + delta + window_right),
+ * a negative window_left (window_right) leaving that side unbounded.
+ * (window_left, window_right) = (-1, 0) is causal attention aligned to the
+ * bottom right of the slice (the last query sees every key); (-1, -1) is full
+ * bidirectional attention inside the slice; (w, 0) is a causal window of
+ * w + 1 keys.  With cu_k = cu_q and (-1, 0) it is exactly the causal
+ * self-attention call.  A query row with no key (possible when L_k < L_q or
+ * with a window) gets O = 0 and LSE = -inf, and contributes no gradient.
+ *   Q, O, dO, dQ  [T_q, H, d];  K, V, dK, dV  [T_k, H_kv, d];  LSE fp32 [H, T_q]
+ *   d_cu_q, h_cu_q  query boundaries, device and host mirror, int32 [n_seg+1]
+ *   d_cu_k, h_cu_k  key boundaries, device and host mirror, int32 [n_seg+1]
+ *   window_left, window_right   >= -1
+ *   workspace  >= pvb_varlen_cross_attn_workspace_bytes(...) bytes   (device)
+ * Both host mirrors are required here and are validated on the host
+ * (PVB_E_BAD_CU_SEQLENS); the device copies must hold the same values.  The
+ * kernels still clip every key range to [0, T_k), so a device copy that
+ * differs gives wrong values but no access outside the buffers.  Other
+ * arguments, dtypes and errors as in the *_gqa calls; a window below -1 is
+ * PVB_E_INVALID_ARG. */
+size_t pvb_varlen_cross_attn_workspace_bytes(int32_t T_q, int32_t T_k, int32_t H, int32_t d,
+                                             int32_t n_seg, int32_t bwd, int32_t grad_dtype);
+pvb_status pvb_varlen_cross_attn_fwd(const void* d_q, const void* d_k, const void* d_v,
+                                     const int32_t* d_cu_q, const int32_t* h_cu_q,
+                                     const int32_t* d_cu_k, const int32_t* h_cu_k, int32_t n_seg,
+                                     int32_t T_q, int32_t T_k, int32_t H, int32_t H_kv, int32_t d,
+                                     int32_t window_left, int32_t window_right, float softmax_scale,
+                                     void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
+                                     void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                     void* stream);
+pvb_status pvb_varlen_cross_attn_bwd(const void* d_q, const void* d_k, const void* d_v,
+                                     const void* d_o, int32_t o_dtype, const void* d_do,
+                                     const float* d_lse, const int32_t* d_cu_q, const int32_t* h_cu_q,
+                                     const int32_t* d_cu_k, const int32_t* h_cu_k, int32_t n_seg,
+                                     int32_t T_q, int32_t T_k, int32_t H, int32_t H_kv, int32_t d,
+                                     int32_t window_left, int32_t window_right, float softmax_scale,
+                                     void* d_dq, void* d_dk, void* d_dv, int32_t grad_dtype,
+                                     int32_t precision, void* workspace, size_t workspace_bytes,
+                                     int32_t* d_status, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);

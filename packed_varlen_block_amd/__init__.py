@@ -33,6 +33,7 @@ STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "P
 # every symbol include/pvb.h declares
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
            "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
+           "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_status_string", "pvb_version")
 
@@ -69,9 +70,16 @@ def lib() -> ctypes.CDLL:
                                               P, P]
         L.pvb_varlen_attn_bwd_gqa.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
                                               P, P, P, I32, I32, P, SZ, P, P]
+        L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+        L.pvb_varlen_cross_attn_workspace_bytes.restype = SZ
+        L.pvb_varlen_cross_attn_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F,
+                                                P, I32, P, I32, P, SZ, P, P]
+        L.pvb_varlen_cross_attn_bwd.argtypes = [P, P, P, P, I32, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                                I32, I32, F, P, P, P, I32, I32, P, SZ, P, P]
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
                      "pvb_boundaries_from_positions", "pvb_packed_nll", "pvb_varlen_attn_fwd",
-                     "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa"):
+                     "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
+                     "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
         L.pvb_status_string.restype = ctypes.c_char_p
@@ -358,4 +366,101 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _ptr(status), _stream(dev))
     _check(rc, "varlen_attn_bwd")
+    return dq, dk, dv, status
+
+
+def cross_workspace_bytes(T_q: int, T_k: int, H: int, d: int, n_seg: int, backward: bool,
+                          grad_dtype=PVB_F32) -> int:
+    return int(lib().pvb_varlen_cross_attn_workspace_bytes(T_q, T_k, H, d, n_seg, int(bool(backward)),
+                                                           int(grad_dtype)))
+
+
+def _check_cross(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k, *rest):
+    """q (and dO) [T_q, H, d]; k, v [T_k, H_kv, d]; device cu_q, cu_k int32 [B+1]
+    with their host mirrors (both required)."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3:
+        raise PvbError(1, "q and k must be 3-d")
+    T_q, H, d = q.shape
+    T_k, Hk = k.shape[0], k.shape[1]
+    for t, shape in [(q, (T_q, H, d)), (k, (T_k, Hk, d)), (v, (T_k, Hk, d))] + [(t, (T_q, H, d)) for t in rest]:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda:
+            raise PvbError(1, "q/dO [T_q, H, d] and k/v [T_k, H_kv, d] must be contiguous bf16 CUDA tensors")
+    if Hk <= 0 or H % Hk != 0:
+        raise PvbError(1, "the query heads must be a multiple of the key/value heads")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or not c.is_cuda or c.dim() != 1:
+            raise PvbError(1, "cu_q and cu_k must be 1-d int32 CUDA tensors")
+    n_seg = cu_q.numel() - 1
+    if cu_k.numel() != n_seg + 1:
+        raise PvbError(1, "cu_q and cu_k must have the same number of segments")
+    if h_cu_q is None or h_cu_k is None:
+        raise PvbError(1, "the cross form needs the host mirrors h_cu_q and h_cu_k")
+    hq = np.ascontiguousarray(np.asarray(h_cu_q, dtype=np.int32))
+    hk = np.ascontiguousarray(np.asarray(h_cu_k, dtype=np.int32))
+    if hq.size != n_seg + 1 or hk.size != n_seg + 1:
+        raise PvbError(1, "h_cu_q and h_cu_k must have B+1 entries")
+    return T_q, T_k, H, Hk, d, n_seg, hq, hk
+
+
+def varlen_cross_attn_fwd(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k, window=(-1, 0), softmax_scale=None,
+                          o_dtype=None, precision="bf16", out=None, lse=None, workspace=None, status=None):
+    """Forward attention with separate query and key boundaries and a local
+    window (window_left, window_right; -1 leaves a side unbounded; (-1, 0) is
+    causal aligned to the bottom right).  Returns (O [T_q,H,d], LSE [H,T_q], status);
+    rows with no key get O = 0 and LSE = -inf."""
+    torch = _torch()
+    T_q, T_k, H, Hk, d, n_seg, hq, hk = _check_cross(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k)
+    wl, wr = int(window[0]), int(window[1])
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o_dtype = torch.bfloat16 if o_dtype is None else o_dtype
+    dev = q.device
+    if out is None:
+        out = torch.empty((T_q, H, d), dtype=o_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
+    nbytes = cross_workspace_bytes(T_q, T_k, H, d, n_seg, False)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    rc = lib().pvb_varlen_cross_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(hq), _ptr(cu_k), _ptr(hk),
+                                         n_seg, T_q, T_k, H, Hk, d, wl, wr, scale, _ptr(out),
+                                         _dtype_code(out.dtype), _ptr(lse), _prec_code(precision),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _ptr(status), _stream(dev))
+    _check(rc, "varlen_cross_attn_fwd")
+    return out, lse, status
+
+
+def varlen_cross_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, h_cu_q, h_cu_k, window=(-1, 0),
+                          softmax_scale=None, grad_dtype=None, precision="bf16", dq=None, dk=None, dv=None,
+                          workspace=None, status=None):
+    """Backward of varlen_cross_attn_fwd.  Returns (dQ [T_q,H,d], dK, dV [T_k,H_kv,d], status)."""
+    torch = _torch()
+    T_q, T_k, H, Hk, d, n_seg, hq, hk = _check_cross(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k, do)
+    if tuple(o.shape) != (T_q, H, d) or not o.is_contiguous():
+        raise PvbError(1, "o must be contiguous [T_q, H, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T_q) or not lse.is_contiguous():
+        raise PvbError(1, "lse must be contiguous fp32 [H, T_q]")
+    wl, wr = int(window[0]), int(window[1])
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
+    gcode = _dtype_code(grad_dtype)
+    dev = q.device
+    dq = torch.empty((T_q, H, d), dtype=grad_dtype, device=dev) if dq is None else dq
+    dk = torch.empty((T_k, Hk, d), dtype=grad_dtype, device=dev) if dk is None else dk
+    dv = torch.empty((T_k, Hk, d), dtype=grad_dtype, device=dev) if dv is None else dv
+    nbytes = cross_workspace_bytes(T_q, T_k, H, d, n_seg, True, gcode)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    rc = lib().pvb_varlen_cross_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o.dtype), _ptr(do),
+                                         _ptr(lse), _ptr(cu_q), _ptr(hq), _ptr(cu_k), _ptr(hk), n_seg, T_q, T_k,
+                                         H, Hk, d, wl, wr, scale, _ptr(dq), _ptr(dk), _ptr(dv), gcode,
+                                         _prec_code(precision), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(status),
+                                         _stream(dev))
+    _check(rc, "varlen_cross_attn_bwd")
     return dq, dk, dv, status

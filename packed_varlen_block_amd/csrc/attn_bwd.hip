@@ -52,12 +52,16 @@ constexpr int kThreads = 256;
 // wave and step.  Both roles run the same instruction stream up to role
 // selects: first product A x (K or V fragment in registers) with A = Q or dO
 // rows from LDS, then (P or dS) x (dO or Q, read transposed from LDS).
-template <int D, bool SPLIT, typename GradT, bool DECODE>
+// Work items come from the key-side list (cu, T, wl); with BAND the query
+// extents come from cu_q (T_q queries) and each key sees the query rows whose
+// band holds it.
+template <int D, bool SPLIT, typename GradT, bool DECODE, bool BAND>
 __global__ void __launch_bounds__(kThreads, 3)
 bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const bf16* __restrict__ dout, const float2* __restrict__ ld,
                    const int32_t* __restrict__ cu, const WorkList wl, int H, int Hk, int T, float scale,
-                   float scale_log2, GradT* __restrict__ dk, GradT* __restrict__ dv) {
+                   float scale_log2, GradT* __restrict__ dk, GradT* __restrict__ dv,
+                   const int32_t* __restrict__ cu_q, int T_q, int win_left, int win_right) {
   constexpr int BN = kTile / 2, BM = kKvBM;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -86,13 +90,19 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   const int G = H / Hk;
   int2 tm;
   if (!work_item<kTile, DECODE>(wl, cu, T, tau, &tm)) return;
-  const int seg0 = cu[tm.x];
-  const int L = cu[tm.x + 1] - seg0;
-  const int k0 = ((L + kTile - 1) / kTile - 1 - tm.y) * kTile + BN * half;
-  if (k0 >= L) return;                                 // empty half of a ragged last tile
+  const int seg0k = cu[tm.x];
+  const int Lk = cu[tm.x + 1] - seg0k;                 // keys of the slice
+  int seg0 = seg0k, Lq = Lk;                           // its query rows (clipped to [0, T_q])
+  if constexpr (BAND) {
+    seg0 = min(max(cu_q[tm.x], 0), T_q);
+    Lq = min(max(cu_q[tm.x + 1] - seg0, 0), T_q - seg0);
+  }
+  const KeyBand<BAND> band{Lk, Lk - Lq, win_left, win_right};
+  const int k0 = ((Lk + kTile - 1) / kTile - 1 - tm.y) * kTile + BN * half;
+  if (k0 >= Lk) return;                                // empty half of a ragged last tile
   const int rs = H * D;                                // row stride of Q, dO (elements)
   const int rs_kv = Hk * D;                            // row stride of K, V, dK, dV
-  const int64_t base_kv = ((int64_t)seg0 * Hk + hk) * D;
+  const int64_t base_kv = ((int64_t)seg0k * Hk + hk) * D;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -105,7 +115,7 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   // B operand of the first product: K rows (role 0) or V rows (role 1)
   const bf16* fs = (role ? v : k) + base_kv;
   bf16x8 frag[KSTEPS];
-  if (kcol < L) {
+  if (kcol < Lk) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) frag[s] = *(const bf16x8*)(fs + kcol * rs_kv + 16 * s + 8 * g);
   } else {
@@ -133,8 +143,17 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   };
   const int rec_kind = (2 * BM / 4) * w + lane >= BM ? 1 : 0;
   const uint32_t rec_off = (uint32_t)(rec_row() * 8 + rec_kind * 4);
-  const int jq_lo = k0 / BM;
-  const int n_steps = (L + BM - 1) / BM - jq_lo;      // query tiles per query head
+  // query rows whose band holds one of this workgroup's keys [k0, k_last]:
+  // from the first row whose band reaches k0 to the last whose band starts by k_last
+  int jq_lo = k0 / BM, jq_end = (Lq + BM - 1) / BM;
+  if constexpr (BAND) {
+    const int k_last = min(k0 + BN, Lk) - 1;
+    const int q_first = win_right < 0 ? 0 : max(0, k0 - band.delta - win_right);
+    const int q_last = win_left < 0 ? Lq - 1 : min(Lq - 1, k_last - band.delta + win_left);
+    jq_lo = q_first / BM;
+    jq_end = q_last >= q_first ? q_last / BM + 1 : jq_lo;
+  }
+  const int n_steps = jq_end - jq_lo;                  // query tiles per query head
   // The walk visits query tiles jq_lo.. of query head hk G, then of hk G + 1,
   // and so on.  Staging runs ahead of the math, so it keeps its own cursor
   // (query head sh, tile st), advanced one tile per call.
@@ -144,14 +163,14 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
     const int64_t base = ((int64_t)seg0 * H + sh) * D;
     const bf16* qs = q + base;
     const bf16* gs = dout + base;
-    const float2* lds_h = ld + (int64_t)sh * T + seg0;
-    if (++st * BM >= L) {
+    const float2* lds_h = ld + (int64_t)sh * T_q + seg0;
+    if (++st >= jq_end) {
       st = jq_lo;
       ++sh;
     }
     const uint32_t sb = lds_addr(ring[b]);
     const uint32_t lb = lds_addr(sLD[b]) + (uint32_t)(wu * (2 * BM / 4) * 4);
-    if (qt0 + BM <= L) {
+    if (qt0 + BM <= Lq) {
       const bf16* q0p = qs + (int64_t)qt0 * rs;
       const bf16* g0p = gs + (int64_t)qt0 * rs;
 #pragma unroll
@@ -166,11 +185,11 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
       for (int i = 0; i < NI; ++i) {
         const int c = 4 * i + wu;
         const bf16* src = c >= CPT && c < 2 * CPT ? gs : qs;
-        const int grow = min(qt0 + c_row(i), L - 1);
+        const int grow = min(qt0 + c_row(i), Lq - 1);
         copy_to_lds16(src, (uint32_t)(grow * rs + c_col(i) * 8) * 2u, sb + (uint32_t)c * 1024u);
       }
       if (lane < 2 * BM / 4)
-        copy_to_lds4(lds_h, (uint32_t)(min(qt0 + rec_row(), L - 1) * 8 + rec_kind * 4), lb);
+        copy_to_lds4(lds_h, (uint32_t)(min(qt0 + rec_row(), Lq - 1) * 8 + rec_kind * 4), lb);
     }
   };
 
@@ -187,7 +206,7 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   for (int t = 0; t < n_walk; ++t) {
     const int b = t % NST;
     const int qt0 = tq * BM;
-    if (++tq * BM >= L) tq = jq_lo;
+    if (++tq >= jq_end) tq = jq_lo;
     if (t + NST - 2 < n_walk) wait_vmcnt<(NST - 2) * COPIES>();
     else wait_vmcnt<0>();
     // every wave's copies of step t have landed, every wave is done with the
@@ -224,11 +243,11 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = fast_exp2(acc[i] * scale_log2 - rv[i >> 2][i & 3]);
       // wave-uniform: only tiles that cross the diagonal or an end are masked
-      if (qt0 < kw0 + 31 || qt0 + BM > L || kw0 + 32 > L) {
+      if (!(band.hi(qt0) >= kw0 + 31 && band.lo(qt0 + BM - 1) <= kw0 && qt0 + BM <= Lq && kw0 + 32 <= Lk)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int ql = crow32(i, g);
-          if (kcol > qt0 + ql || qt0 + ql >= L || kcol >= L) acc[i] = 0.f;
+          const int qr = qt0 + crow32(i, g);
+          if (kcol > band.hi(qr) || kcol < band.lo(qr) || qr >= Lq || kcol >= Lk) acc[i] = 0.f;
         }
       }
 #pragma unroll
@@ -276,7 +295,7 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key < L) outp[base_kv + (int64_t)key * rs_kv + 32 * j + lq] = out_cast<GradT>(acc2[j][i] * oscale);
+      if (key < Lk) outp[base_kv + (int64_t)key * rs_kv + 32 * j + lq] = out_cast<GradT>(acc2[j][i] * oscale);
     }
 }
 
@@ -285,12 +304,13 @@ bwd_kv_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 // ---------------------------------------------------------------------------
 // Also forms the per-row statistics {LSE log2e, D = dO . O} of its queries and
 // writes them for the dK/dV kernel, which runs after it.
-template <int D, bool SPLIT, typename GradT, bool DECODE, typename OT>
+template <int D, bool SPLIT, typename GradT, bool DECODE, typename OT, bool BAND>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
               const bf16* __restrict__ dout, const OT* __restrict__ o, const float* __restrict__ lse,
               float2* __restrict__ ld, const int32_t* __restrict__ cu, const WorkList wl, int H, int Hk, int T,
-              float scale, float scale_log2, GradT* __restrict__ dq) {
+              float scale, float scale_log2, GradT* __restrict__ dq,
+              const int32_t* __restrict__ cu_k, int T_k, int win_left, int win_right) {
   constexpr int BM = kTile, BN = kDqBN;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -304,12 +324,18 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
   int2 tm;
   if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
-  const int L = cu[tm.x + 1] - seg0;
+  const int L = cu[tm.x + 1] - seg0;           // query rows of the slice
+  int seg0k = seg0, Lk = L;                    // its keys (clipped to [0, T_k])
+  if constexpr (BAND) {
+    seg0k = min(max(cu_k[tm.x], 0), T_k);
+    Lk = min(max(cu_k[tm.x + 1] - seg0k, 0), T_k - seg0k);
+  }
+  const KeyBand<BAND> band{Lk, Lk - L, win_left, win_right};
   const int q0 = tm.y * BM;
   const int rs = H * D;       // row stride of Q, dO, O, dQ (elements)
   const int rs_kv = Hk * D;   // row stride of K, V
   const int64_t base = ((int64_t)seg0 * H + h) * D;
-  const int64_t base_kv = ((int64_t)seg0 * Hk + hp.hk) * D;
+  const int64_t base_kv = ((int64_t)seg0k * Hk + hp.hk) * D;
   const bf16* qs = q + base;
   const bf16* ks = k + base_kv;
   const bf16* vs = v + base_kv;
@@ -350,6 +376,9 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
       for (int e = 0; e < 8; ++e) dpart += (float)gf[s][e] * ov[e];
     }
     rl.x = lse[(int64_t)h * T + seg0 + qrow] * kLog2e;
+    // a row with no key (LSE = -inf) takes +inf, so that every P of the row,
+    // masked scores included, is exp2(-inf) = 0 rather than NaN
+    if constexpr (BAND) rl.x = rl.x == -INFINITY ? INFINITY : rl.x;
   } else {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = gf[s] = bf16x8{};
@@ -363,28 +392,34 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
   for (int j = 0; j < DBLK; ++j) dqacc[j] = f32x16{};
 
   const int q_last = min(q0 + BM, L) - 1;
-  const int nkv = q_last / BN + 1;
+  // key tiles holding a key that some row of the tile may use
+  int n_lo = 0, n_end = q_last / BN + 1;
+  if constexpr (BAND) {
+    const int klo = band.lo(q0), khi = band.hi(q_last);
+    n_lo = klo / BN;
+    n_end = khi >= klo ? khi / BN + 1 : n_lo;
+  }
   FullTileCopy<D, BN> full;
   full.init(rs_kv, w, lane);
   auto stage = [&](int row0, int b) {
-    if (row0 + BN <= L) {
+    if (row0 + BN <= Lk) {
       full.issue(ks, rs_kv, row0, sK[b]);
       full.issue(vs, rs_kv, row0, sV[b]);
     } else {
-      stage_rows<D, BN>(ks, rs_kv, row0, L, sK[b], w, lane);
-      stage_rows<D, BN>(vs, rs_kv, row0, L, sV[b], w, lane);
+      stage_rows<D, BN>(ks, rs_kv, row0, Lk, sK[b], w, lane);
+      stage_rows<D, BN>(vs, rs_kv, row0, Lk, sV[b], w, lane);
     }
   };
-  stage(0, 0);
+  if (n_end > n_lo) stage(n_lo * BN, 0);
   wait_vmcnt<0>();
-  for (int n = 0; n < nkv; ++n) {
-    const int b = n & 1;
+  for (int n = n_lo; n < n_end; ++n) {
+    const int b = (n - n_lo) & 1;
     lds_barrier();
-    if (n + 1 < nkv) stage((n + 1) * BN, b ^ 1);
+    if (n + 1 < n_end) stage((n + 1) * BN, b ^ 1);
     const bf16* cK = sK[b];
     const bf16* cV = sV[b];
     const int key0 = n * BN;
-    if (wave_active && key0 <= wq_last) {
+    if (wave_active && key0 <= band.hi(wq_last) && key0 + BN - 1 >= band.lo(wq_first)) {
       // S^T = K Q^T and dP^T = V dO^T: each lane owns one query column.  The
       // K and V operands are read kPf k-steps ahead of their MFMAs.
       constexpr int kPf = 1;
@@ -415,8 +450,9 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
-      // wave-uniform: only tiles that cross the diagonal or the end are masked
-      const bool need_mask = key0 + BN - 1 > wq_first || key0 + BN > L;
+      // wave-uniform: only tiles that cross a band edge (the diagonal when
+      // causal) or the end of the keys are masked
+      const bool need_mask = !(key0 >= band.lo(wq_last) && key0 + BN - 1 <= band.hi(wq_first) && key0 + BN <= Lk);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -427,7 +463,7 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > qrow || key >= L) st[kb2][i] = 0.f;
+            if (key > band.hi(qrow) || key < band.lo(qrow) || key >= Lk) st[kb2][i] = 0.f;
           }
       }
 #pragma unroll
@@ -454,7 +490,7 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
         }
       }
     }
-    if (n + 1 < nkv) wait_vmcnt<0>();
+    if (n + 1 < n_end) wait_vmcnt<0>();
   }
 
   if (!wave_active || qrow >= L) return;
@@ -477,106 +513,137 @@ bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16
 }
 
 struct BwdLayout {
-  size_t tiles_off, ld_off, total;
+  size_t tiles_off, tiles_k_off, ld_off, total;
 };
 
-BwdLayout bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
+// Workspace: list counts in [0, 256) (query list at 0, key list at 128), the
+// query tile list, the key tile list (cross form only; otherwise the query
+// list serves both kernels), then the {LSE log2e, D} records [H][T].
+BwdLayout bwd_layout(int32_t T, int32_t H, int32_t n_seg, int32_t T_k = -1) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdLayout l;
   l.tiles_off = 256;
-  l.ld_off = up(l.tiles_off + plan_capacity(T, n_seg, kTile) * sizeof(int2));
+  size_t end = up(l.tiles_off + plan_capacity(T, n_seg, kTile) * sizeof(int2));
+  l.tiles_k_off = l.tiles_off;
+  if (T_k >= 0) {
+    l.tiles_k_off = end;
+    end = up(end + plan_capacity(T_k, n_seg, kTile) * sizeof(int2));
+  }
+  l.ld_off = end;
   l.total = l.ld_off + (size_t)H * T * sizeof(float2);
   return l;
 }
 
-template <int D, bool SPLIT, typename GradT, typename OT, bool DECODE>
+template <int D, bool SPLIT, typename GradT, typename OT, bool BAND>
 void launch_bwd_kernels(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const int32_t* cu, const WorkList& wl, int H, int Hk, int T,
-                        size_t cap, float scale, float2* ld, void* dq, void* dk, void* dv,
+                        const float* lse, const int32_t* cu, const WorkList& wl, const int32_t* cu_kl,
+                        const WorkList& wl_k, int H, int Hk, int T, int T_kl, size_t cap, size_t cap_k,
+                        float scale, float2* ld, void* dq, void* dk, void* dv, const BandArgs& bd,
                         hipStream_t s) {
-  // dQ first: it also writes the {LSE log2e, D} records the dK/dV kernel reads
-  // one dQ workgroup per (tile, query head); one dK/dV workgroup per (64-key
-  // half tile, key/value head), walking the query tiles of the group's heads
-  bwd_dq_kernel<D, SPLIT, GradT, DECODE, OT><<<dim3((unsigned)(cap * H)), kThreads, 0, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const OT*)o, lse, ld, cu, wl,
-      H, Hk, T, scale, scale * kLog2e, (GradT*)dq);
-  bwd_kv_pair_kernel<D, SPLIT, GradT, DECODE><<<dim3((unsigned)(2 * cap * Hk)), kThreads, 0, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu, wl, H, Hk, T, scale,
-      scale * kLog2e, (GradT*)dk, (GradT*)dv);
+  // dQ first: it also writes the {LSE log2e, D} records the dK/dV kernel reads.
+  // One dQ workgroup per (query tile, query head); one dK/dV workgroup per
+  // (64-key half tile, key/value head), walking the query tiles of the
+  // group's heads.
+  const unsigned gq = (unsigned)(cap * H), gk = (unsigned)(2 * cap_k * Hk);
+  if (gq > 0) {
+    if (wl.tiles == nullptr)
+      bwd_dq_kernel<D, SPLIT, GradT, true, OT, BAND><<<dim3(gq), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const OT*)o, lse, ld, cu, wl,
+          H, Hk, T, scale, scale * kLog2e, (GradT*)dq, bd.cu_k, bd.T_k, bd.wl, bd.wr);
+    else
+      bwd_dq_kernel<D, SPLIT, GradT, false, OT, BAND><<<dim3(gq), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, (const OT*)o, lse, ld, cu, wl,
+          H, Hk, T, scale, scale * kLog2e, (GradT*)dq, bd.cu_k, bd.T_k, bd.wl, bd.wr);
+  }
+  if (gk > 0) {
+    if (wl_k.tiles == nullptr)
+      bwd_kv_pair_kernel<D, SPLIT, GradT, true, BAND><<<dim3(gk), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu_kl, wl_k, H, Hk, T_kl,
+          scale, scale * kLog2e, (GradT*)dk, (GradT*)dv, cu, T, bd.wl, bd.wr);
+    else
+      bwd_kv_pair_kernel<D, SPLIT, GradT, false, BAND><<<dim3(gk), kThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, ld, cu_kl, wl_k, H, Hk, T_kl,
+          scale, scale * kLog2e, (GradT*)dk, (GradT*)dv, cu, T, bd.wl, bd.wr);
+  }
 }
 
 template <int D, bool SPLIT, typename GradT, typename OT>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, const int32_t* cu, const WorkList& wl, int H, int Hk, int T,
-                      size_t cap, float scale, float2* ld, void* dq, void* dk, void* dv,
+                      const float* lse, const int32_t* cu, const WorkList& wl, const int32_t* cu_kl,
+                      const WorkList& wl_k, int H, int Hk, int T, int T_kl, size_t cap, size_t cap_k,
+                      float scale, float2* ld, void* dq, void* dk, void* dv, const BandArgs& bd,
                       hipStream_t s) {
-  if (cap > 0) {
-    if (wl.tiles == nullptr)
-      launch_bwd_kernels<D, SPLIT, GradT, OT, true>(q, k, v, o, dout, lse, cu, wl, H, Hk, T, cap, scale, ld,
-                                                    dq, dk, dv, s);
-    else
-      launch_bwd_kernels<D, SPLIT, GradT, OT, false>(q, k, v, o, dout, lse, cu, wl, H, Hk, T, cap, scale, ld,
-                                                     dq, dk, dv, s);
-  }
+  if (bd.on)
+    launch_bwd_kernels<D, SPLIT, GradT, OT, true>(q, k, v, o, dout, lse, cu, wl, cu_kl, wl_k, H, Hk, T, T_kl,
+                                                  cap, cap_k, scale, ld, dq, dk, dv, bd, s);
+  else
+    launch_bwd_kernels<D, SPLIT, GradT, OT, false>(q, k, v, o, dout, lse, cu, wl, cu_kl, wl_k, H, Hk, T, T_kl,
+                                                   cap, cap_k, scale, ld, dq, dk, dv, bd, s);
   return hipGetLastError();
 }
 
-}  // namespace
-
-size_t attn_bwd_workspace_bytes(int32_t T, int32_t H, int32_t d, int32_t n_seg, int32_t grad_dtype) {
-  (void)d;
-  (void)grad_dtype;
-  return bwd_layout(T, H, n_seg).total;
-}
-
-}  // namespace pvb
-
-extern "C" pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, const void* d_v,
-                                              const void* d_o, int32_t o_dtype, const void* d_do,
-                                              const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
-                                              int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
-                                              float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
-                                              int32_t grad_dtype, int32_t precision, void* workspace,
-                                              size_t workspace_bytes, int32_t* d_status, void* stream) {
-  using namespace pvb;
+pvb_status bwd_call(const void* d_q, const void* d_k, const void* d_v, const void* d_o, int32_t o_dtype,
+                    const void* d_do, const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                    int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d, float softmax_scale,
+                    void* d_dq, void* d_dk, void* d_dv, int32_t grad_dtype, int32_t precision,
+                    void* workspace, size_t workspace_bytes, int32_t* d_status, const BandArgs& bd,
+                    void* stream) {
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
   if (H_kv <= 0 || H % H_kv != 0) return PVB_E_INVALID_ARG;
-  if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_o == nullptr ||
-                d_do == nullptr || d_lse == nullptr || d_dq == nullptr || d_dk == nullptr ||
-                d_dv == nullptr))
+  const int32_t T_k = bd.on ? bd.T_k : T;
+  if ((T > 0 && (d_q == nullptr || d_o == nullptr || d_do == nullptr || d_lse == nullptr || d_dq == nullptr)) ||
+      (T_k > 0 && (d_k == nullptr || d_v == nullptr || d_dk == nullptr || d_dv == nullptr)))
     return PVB_E_INVALID_ARG;
   if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
   if (grad_dtype != PVB_BF16 && grad_dtype != PVB_F32) return PVB_E_INVALID_ARG;
   if (precision != PVB_PREC_BF16 && precision != PVB_PREC_SPLIT) return PVB_E_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != 64 && d != 128) return PVB_E_UNSUPPORTED;
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31)) return PVB_E_UNSUPPORTED;
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || (int64_t)T_k * H_kv * d >= ((int64_t)1 << 31))
+    return PVB_E_UNSUPPORTED;
   const size_t cap = plan_capacity(T, n_seg, kTile);
-  if (2 * cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
-  const BwdLayout lay = bwd_layout(T, H, n_seg);
+  const size_t cap_k = bd.on ? plan_capacity(T_k, n_seg, kTile) : cap;
+  if (cap * (size_t)H > 0x7fffffffULL || 2 * cap_k * (size_t)H_kv > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
+  const BwdLayout lay = bwd_layout(T, H, n_seg, bd.on ? T_k : -1);
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
   if (hs != PVB_OK) return hs;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  int32_t* count = reinterpret_cast<int32_t*>(ws);
-  int2* tiles = reinterpret_cast<int2*>(ws + lay.tiles_off);
   float2* ld = reinterpret_cast<float2*>(ws + lay.ld_off);
-  // small packs: the main kernels decode their items themselves (and write the
-  // status); otherwise the planner writes the list and the status first
-  const bool dec = decode_in_kernel(T, n_seg, kTile, cap * (size_t)H);
-  if (!dec) {
-    plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kTile, tiles, count, d_status);
-    if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
+  // Small launches decode their items in the kernels (which then write the
+  // status); otherwise the planner writes the list and the status first.  The
+  // cross form takes one mode for both lists, so that the query list's writer
+  // comes first in stream order and the key list's writes only errors.
+  bool dec = decode_in_kernel(T, n_seg, kTile, cap * (size_t)H);
+  if (bd.on) dec = dec && decode_in_kernel(T_k, n_seg, kTile, 2 * cap_k * (size_t)H_kv);
+  auto make_list = [&](const int32_t* c, int32_t Tn, size_t toff, size_t coff, bool first,
+                       WorkList* out) -> bool {
+    int32_t* count = reinterpret_cast<int32_t*>(ws + coff);
+    int2* tiles = reinterpret_cast<int2*>(ws + toff);
+    if (!dec) {
+      plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(c, n_seg, Tn, kTile, tiles, count, d_status, first ? 1 : 0);
+      if (hipGetLastError() != hipSuccess) return false;
+    }
+    *out = WorkList{dec ? nullptr : tiles, count, n_seg, d_status, first};
+    return true;
+  };
+  WorkList wl, wl_k;
+  if (!make_list(d_cu, T, lay.tiles_off, 0, true, &wl)) return PVB_E_HIP;
+  const int32_t* cu_kl = d_cu;
+  if (bd.on) {
+    cu_kl = bd.cu_k;
+    if (!make_list(bd.cu_k, T_k, lay.tiles_k_off, 128, false, &wl_k)) return PVB_E_HIP;
+  } else {
+    wl_k = wl;
   }
-  const WorkList wl{dec ? nullptr : tiles, count, n_seg, d_status};
 
   const bool split = precision == PVB_PREC_SPLIT, gf32 = grad_dtype == PVB_F32, of32 = o_dtype == PVB_F32;
   hipError_t e = hipSuccess;
-#define PVB_BWD(D_, S_, G_, O_)                                                                    \
-  e = launch_bwd<D_, S_, G_, O_>(d_q, d_k, d_v, d_o, d_do, d_lse, d_cu, wl, H, H_kv, T, cap,    \
-                                 softmax_scale, ld, d_dq, d_dk, d_dv, s)
+#define PVB_BWD(D_, S_, G_, O_)                                                                        \
+  e = launch_bwd<D_, S_, G_, O_>(d_q, d_k, d_v, d_o, d_do, d_lse, d_cu, wl, cu_kl, wl_k, H, H_kv, T, T_k, \
+                                 cap, cap_k, softmax_scale, ld, d_dq, d_dk, d_dv, bd, s)
 #define PVB_BWD_O(D_, S_, G_) \
   if (of32) PVB_BWD(D_, S_, G_, float); else PVB_BWD(D_, S_, G_, bf16)
 #define PVB_BWD_G(D_, S_) \
@@ -592,6 +659,32 @@ extern "C" pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, 
   return e == hipSuccess ? PVB_OK : PVB_E_HIP;
 }
 
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int32_t T, int32_t H, int32_t d, int32_t n_seg, int32_t grad_dtype) {
+  (void)d;
+  (void)grad_dtype;
+  return bwd_layout(T, H, n_seg).total;
+}
+
+size_t cross_bwd_workspace_bytes(int32_t T_q, int32_t T_k, int32_t H, int32_t n_seg) {
+  return bwd_layout(T_q, H, n_seg, T_k).total;
+}
+
+}  // namespace pvb
+
+extern "C" pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                              const void* d_o, int32_t o_dtype, const void* d_do,
+                                              const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                                              int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                              float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                              int32_t grad_dtype, int32_t precision, void* workspace,
+                                              size_t workspace_bytes, int32_t* d_status, void* stream) {
+  return pvb::bwd_call(d_q, d_k, d_v, d_o, o_dtype, d_do, d_lse, d_cu, h_cu, n_seg, T, H, H_kv, d,
+                       softmax_scale, d_dq, d_dk, d_dv, grad_dtype, precision, workspace, workspace_bytes,
+                       d_status, pvb::BandArgs{}, stream);
+}
+
 extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v,
                                           const void* d_o, int32_t o_dtype, const void* d_do,
                                           const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
@@ -602,4 +695,23 @@ extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, cons
   return pvb_varlen_attn_bwd_gqa(d_q, d_k, d_v, d_o, o_dtype, d_do, d_lse, d_cu, h_cu, n_seg, T, H, H, d,
                                  softmax_scale, d_dq, d_dk, d_dv, grad_dtype, precision, workspace,
                                  workspace_bytes, d_status, stream);
+}
+
+extern "C" pvb_status pvb_varlen_cross_attn_bwd(const void* d_q, const void* d_k, const void* d_v,
+                                                const void* d_o, int32_t o_dtype, const void* d_do,
+                                                const float* d_lse, const int32_t* d_cu_q,
+                                                const int32_t* h_cu_q, const int32_t* d_cu_k,
+                                                const int32_t* h_cu_k, int32_t n_seg, int32_t T_q,
+                                                int32_t T_k, int32_t H, int32_t H_kv, int32_t d,
+                                                int32_t window_left, int32_t window_right,
+                                                float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                                int32_t grad_dtype, int32_t precision, void* workspace,
+                                                size_t workspace_bytes, int32_t* d_status, void* stream) {
+  using namespace pvb;
+  const pvb_status hs = check_cross_args(h_cu_q, d_cu_k, h_cu_k, n_seg, T_q, T_k, window_left, window_right);
+  if (hs != PVB_OK) return hs;
+  const BandArgs bd{true, d_cu_k, T_k, window_left, window_right};
+  return bwd_call(d_q, d_k, d_v, d_o, o_dtype, d_do, d_lse, d_cu_q, h_cu_q, n_seg, T_q, H, H_kv, d,
+                  softmax_scale, d_dq, d_dk, d_dv, grad_dtype, precision, workspace, workspace_bytes, d_status,
+                  bd, stream);
 }

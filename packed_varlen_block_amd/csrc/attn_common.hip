@@ -43,7 +43,8 @@ __device__ int block_inclusive_scan(int x, int* wsum, int* total) {
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
-                  int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status) {
+                  int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status,
+                  int report_ok) {
   __shared__ int s_nt[kPlanChunk];
   __shared__ int s_off[kPlanMaxM];  // counts per group, then their exclusive offsets
   __shared__ int s_wsum[kPlanThreads / 64];
@@ -104,7 +105,7 @@ plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
   __syncthreads();
   if (tid == 0) {
     *count = carry;
-    *status = PVB_OK;
+    if (report_ok) *status = PVB_OK;
   }
 
   // 4. emit: inside group m, segments in order
@@ -130,6 +131,16 @@ plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
 size_t plan_capacity(int32_t T, int32_t n_seg, int32_t tile) {
   // sum_b ceil(L_b / tile) <= (T + n_seg * (tile - 1)) / tile
   return (size_t)(((int64_t)T + (int64_t)n_seg * (tile - 1)) / tile);
+}
+
+pvb_status check_cross_args(const int32_t* h_cu_q, const int32_t* d_cu_k, const int32_t* h_cu_k,
+                            int32_t n_seg, int32_t T_q, int32_t T_k, int32_t wl, int32_t wr) {
+  if (h_cu_q == nullptr || h_cu_k == nullptr || d_cu_k == nullptr || T_k < 0 || T_q < 0 || n_seg < 0 ||
+      wl < -1 || wr < -1)
+    return PVB_E_INVALID_ARG;
+  const pvb_status sq = check_host_cu(h_cu_q, n_seg, T_q);
+  if (sq != PVB_OK) return sq;
+  return check_host_cu(h_cu_k, n_seg, T_k);
 }
 
 pvb_status check_host_cu(const int32_t* h_cu, int32_t n_seg, int32_t T) {

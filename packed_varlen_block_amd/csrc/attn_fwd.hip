@@ -30,12 +30,16 @@ constexpr int kFwdThreads = 256;
 
 // BN keys per K/V tile: 64 for long segments; 32 for short ones, where the
 // smaller register and LDS footprint lets three workgroups share a CU.
-template <int D, bool SPLIT, typename OutT, bool DECODE, int BN>
+// BAND: separate key boundaries cu_k (T_k keys) and a key band per query row
+// (bottom-right causal alignment and local windows, see KeyBand); without it,
+// causal self-attention over cu.
+template <int D, bool SPLIT, typename OutT, bool DECODE, int BN, bool BAND>
 __global__ void __launch_bounds__(kFwdThreads, BN == 32 ? 3 : 2)
 attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const bf16* __restrict__ v, const int32_t* __restrict__ cu,
                 const WorkList wl, int H, int Hk, int T,
-                float scale_log2, OutT* __restrict__ o, float* __restrict__ lse) {
+                float scale_log2, OutT* __restrict__ o, float* __restrict__ lse,
+                const int32_t* __restrict__ cu_k, int T_k, int win_left, int win_right) {
   constexpr int BM = kFwdBM;
   constexpr int NB = BN / 32;    // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
@@ -54,12 +58,20 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   int2 tm;
   if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
   const int seg0 = cu[tm.x];
-  const int L = cu[tm.x + 1] - seg0;
+  const int L = cu[tm.x + 1] - seg0;           // query rows of the slice
+  int seg0k = seg0, Lk = L;                    // its keys
+  if constexpr (BAND) {
+    // clipped to [0, T_k] so that no access leaves the key tensors (cu_k is
+    // validated on the host)
+    seg0k = min(max(cu_k[tm.x], 0), T_k);
+    Lk = min(max(cu_k[tm.x + 1] - seg0k, 0), T_k - seg0k);
+  }
+  const KeyBand<BAND> band{Lk, Lk - L, win_left, win_right};
   const int q0 = tm.y * BM;
   const int rs = H * D;      // row stride of Q and O (elements)
   const int rs_kv = Hk * D;  // row stride of K and V
   const int64_t base = ((int64_t)seg0 * H + h) * D;
-  const int64_t base_kv = ((int64_t)seg0 * Hk + hp.hk) * D;
+  const int64_t base_kv = ((int64_t)seg0k * Hk + hp.hk) * D;
   const bf16* qs = q + base;
   const bf16* ks = k + base_kv;
   const bf16* vs = v + base_kv;
@@ -88,31 +100,38 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   float m_run = -INFINITY, l_run = 0.f;
 
   const int q_last = min(q0 + BM, L) - 1;
-  const int nkv = q_last / BN + 1;
+  // key tiles holding a key that some row of the tile may use
+  int n_lo = 0, n_end = q_last / BN + 1;
+  if constexpr (BAND) {
+    const int klo = band.lo(q0), khi = band.hi(q_last);
+    n_lo = klo / BN;
+    n_end = khi >= klo ? khi / BN + 1 : n_lo;
+  }
+  const int nkv = n_end - n_lo;
 
   FullTileCopy<D, BN> full;
   full.init(rs_kv, w, lane);
   auto stage = [&](int row0, int b) {
-    if (row0 + BN <= L) {
+    if (row0 + BN <= Lk) {
       full.issue(ks, rs_kv, row0, sK[b]);
       full.issue(vs, rs_kv, row0, sV[b]);
     } else {
-      stage_rows<D, BN>(ks, rs_kv, row0, L, sK[b], w, lane);
-      stage_rows<D, BN>(vs, rs_kv, row0, L, sV[b], w, lane);
+      stage_rows<D, BN>(ks, rs_kv, row0, Lk, sK[b], w, lane);
+      stage_rows<D, BN>(vs, rs_kv, row0, Lk, sV[b], w, lane);
     }
   };
-  stage(0, 0);
-  wait_vmcnt<0>();              // Q fragments and this wave's copies of tile 0
-  for (int n = 0; n < nkv; ++n) {
-    const int b = n & 1;
+  if (nkv > 0) stage(n_lo * BN, 0);
+  wait_vmcnt<0>();              // Q fragments and this wave's copies of the first tile
+  for (int n = n_lo; n < n_end; ++n) {
+    const int b = (n - n_lo) & 1;
     // every wave's copies of tile n have landed, and every wave is done with
     // buffer b^1 (tile n-1), which now receives tile n+1
     lds_barrier();
-    if (n + 1 < nkv) stage((n + 1) * BN, b ^ 1);
+    if (n + 1 < n_end) stage((n + 1) * BN, b ^ 1);
     const bf16* cK = sK[b];
     const bf16* cV = sV[b];
     const int key0 = n * BN;
-    if (wave_active && key0 <= wq_last) {
+    if (wave_active && key0 <= band.hi(wq_last) && key0 + BN - 1 >= band.lo(wq_first)) {
       // S^T = K Q^T: NB 32-key blocks.  The K operands are read kPf k-steps
       // ahead of their MFMAs.
       constexpr int kPf = 2;
@@ -134,14 +153,16 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
         if (s + kPf + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
       }
-      // mask: key > query, or key past the segment end
-      if (key0 + BN - 1 > wq_first || key0 + BN > L) {
+      // mask keys outside the row's band (later than the query when causal)
+      // or past the slice's keys; only tiles that cross a band edge or the end
+      if (!(key0 >= band.lo(wq_last) && key0 + BN - 1 <= band.hi(wq_first) && key0 + BN <= Lk)) {
+        const int khi = band.hi(qrow), klo = band.lo(qrow);
 #pragma unroll
         for (int kb2 = 0; kb2 < NB; ++kb2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kb2 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > qrow || key >= L) st[kb2][i] = -INFINITY;
+            if (key > khi || key < klo || key >= Lk) st[kb2][i] = -INFINITY;
           }
       }
       // online softmax for this lane's query column (in log2 units)
@@ -153,7 +174,10 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        // a row with no key so far in a wave that rescales: -inf - -inf would
+        // make alpha NaN (only rows of a band can have none)
+        float alpha = fast_exp2(m_run - m_new);
+        if constexpr (BAND) alpha = m_new == -INFINITY ? 1.f : alpha;
         l_run *= alpha;
 #pragma unroll
         for (int j = 0; j < DBLK; ++j)
@@ -194,7 +218,7 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
       }
     }
-    if (n + 1 < nkv) wait_vmcnt<0>();   // this wave's copies of tile n+1
+    if (n + 1 < n_end) wait_vmcnt<0>();   // this wave's copies of tile n+1
   }
 
   if (!wave_active || qrow >= L) return;
@@ -218,25 +242,36 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   if (g == 0) lse[(int64_t)h * T + seg0 + qrow] = (m_run + log2f(l_run)) * kLn2;
 }
 
+template <int D, bool SPLIT, typename OutT, int BN, bool BAND>
+void launch_fwd_bb(const void* q, const void* k, const void* v, const int32_t* cu, const WorkList& wl,
+                   int H, int Hk, int T, size_t grid, float scale_log2, void* o, float* lse,
+                   const BandArgs& bd, hipStream_t s) {
+  if (wl.tiles == nullptr)
+    attn_fwd_kernel<D, SPLIT, OutT, true, BN, BAND><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse,
+        bd.cu_k, bd.T_k, bd.wl, bd.wr);
+  else
+    attn_fwd_kernel<D, SPLIT, OutT, false, BN, BAND><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse,
+        bd.cu_k, bd.T_k, bd.wl, bd.wr);
+}
+
 template <int D, bool SPLIT, typename OutT, int BN>
 void launch_fwd_bn(const void* q, const void* k, const void* v, const int32_t* cu, const WorkList& wl,
-                   int H, int Hk, int T, size_t grid, float scale_log2, void* o, float* lse, hipStream_t s) {
-  if (wl.tiles == nullptr)
-    attn_fwd_kernel<D, SPLIT, OutT, true, BN><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse);
-  else
-    attn_fwd_kernel<D, SPLIT, OutT, false, BN><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse);
+                   int H, int Hk, int T, size_t grid, float scale_log2, void* o, float* lse,
+                   const BandArgs& bd, hipStream_t s) {
+  if (bd.on) launch_fwd_bb<D, SPLIT, OutT, BN, true>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
+  else launch_fwd_bb<D, SPLIT, OutT, BN, false>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
 }
 
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
                       const WorkList& wl, int H, int Hk, int T, size_t cap, float scale_log2, void* o,
-                      float* lse, bool short_keys, hipStream_t s) {
+                      float* lse, bool short_keys, const BandArgs& bd, hipStream_t s) {
   const size_t grid = cap * (size_t)H;
   if (grid == 0) return hipSuccess;
-  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, s);
-  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, s);
+  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
+  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
   return hipGetLastError();
 }
 
@@ -250,22 +285,25 @@ size_t attn_fwd_workspace_bytes(int32_t T, int32_t n_seg) { return fwd_workspace
 
 }  // namespace pvb
 
-extern "C" pvb_status pvb_varlen_attn_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
-                                              const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
-                                              int32_t T, int32_t H, int32_t H_kv, int32_t d,
-                                              float softmax_scale, void* d_o, int32_t o_dtype, float* d_lse,
-                                              int32_t precision, void* workspace, size_t workspace_bytes,
-                                              int32_t* d_status, void* stream) {
-  using namespace pvb;
+namespace pvb {
+namespace {
+pvb_status fwd_call(const void* d_q, const void* d_k, const void* d_v, const int32_t* d_cu,
+                    const int32_t* h_cu, int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                    float softmax_scale, void* d_o, int32_t o_dtype, float* d_lse, int32_t precision,
+                    void* workspace, size_t workspace_bytes, int32_t* d_status, const BandArgs& bd,
+                    void* stream) {
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
   if (H_kv <= 0 || H % H_kv != 0) return PVB_E_INVALID_ARG;
-  if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_o == nullptr || d_lse == nullptr))
+  const int32_t T_k = bd.on ? bd.T_k : T;
+  if ((T > 0 && (d_q == nullptr || d_o == nullptr || d_lse == nullptr)) ||
+      (T_k > 0 && (d_k == nullptr || d_v == nullptr)))
     return PVB_E_INVALID_ARG;
   if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
   if (precision != PVB_PREC_BF16 && precision != PVB_PREC_SPLIT) return PVB_E_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != 64 && d != 128) return PVB_E_UNSUPPORTED;
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31)) return PVB_E_UNSUPPORTED;
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || (int64_t)T_k * H_kv * d >= ((int64_t)1 << 31))
+    return PVB_E_UNSUPPORTED;
   const size_t cap = plan_capacity(T, n_seg, kFwdBM);
   if (cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fwd_workspace(T, n_seg)) return PVB_E_WORKSPACE;
@@ -283,14 +321,14 @@ extern "C" pvb_status pvb_varlen_attn_fwd_gqa(const void* d_q, const void* d_k, 
     if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
   }
   const WorkList wl{dec ? nullptr : tiles, count, n_seg, d_status};
-  // segments shorter than 512 on average: 32-key tiles, three workgroups per CU
-  const bool short_keys = (int64_t)T < 512 * (int64_t)n_seg;
+  // key extents shorter than 512 on average: 32-key tiles, three workgroups per CU
+  const bool short_keys = (int64_t)T_k < 512 * (int64_t)n_seg;
 
   const float sl2 = softmax_scale * kLog2e;
   const bool split = precision == PVB_PREC_SPLIT, f32 = o_dtype == PVB_F32;
   hipError_t e;
 #define PVB_FWD(D_, S_, T_) \
-  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, H_kv, T, cap, sl2, d_o, d_lse, short_keys, s)
+  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, H_kv, T, cap, sl2, d_o, d_lse, short_keys, bd, s)
   if (d == 128) {
     if (split) { if (f32) PVB_FWD(128, true, float); else PVB_FWD(128, true, bf16); }
     else { if (f32) PVB_FWD(128, false, float); else PVB_FWD(128, false, bf16); }
@@ -300,6 +338,34 @@ extern "C" pvb_status pvb_varlen_attn_fwd_gqa(const void* d_q, const void* d_k, 
   }
 #undef PVB_FWD
   return e == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+}  // namespace
+}  // namespace pvb
+
+extern "C" pvb_status pvb_varlen_attn_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                              const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                              int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                              float softmax_scale, void* d_o, int32_t o_dtype, float* d_lse,
+                                              int32_t precision, void* workspace, size_t workspace_bytes,
+                                              int32_t* d_status, void* stream) {
+  return pvb::fwd_call(d_q, d_k, d_v, d_cu, h_cu, n_seg, T, H, H_kv, d, softmax_scale, d_o, o_dtype, d_lse,
+                       precision, workspace, workspace_bytes, d_status, pvb::BandArgs{}, stream);
+}
+
+extern "C" pvb_status pvb_varlen_cross_attn_fwd(const void* d_q, const void* d_k, const void* d_v,
+                                                const int32_t* d_cu_q, const int32_t* h_cu_q,
+                                                const int32_t* d_cu_k, const int32_t* h_cu_k, int32_t n_seg,
+                                                int32_t T_q, int32_t T_k, int32_t H, int32_t H_kv, int32_t d,
+                                                int32_t window_left, int32_t window_right,
+                                                float softmax_scale, void* d_o, int32_t o_dtype, float* d_lse,
+                                                int32_t precision, void* workspace, size_t workspace_bytes,
+                                                int32_t* d_status, void* stream) {
+  using namespace pvb;
+  const pvb_status hs = check_cross_args(h_cu_q, d_cu_k, h_cu_k, n_seg, T_q, T_k, window_left, window_right);
+  if (hs != PVB_OK) return hs;
+  const BandArgs bd{true, d_cu_k, T_k, window_left, window_right};
+  return fwd_call(d_q, d_k, d_v, d_cu_q, h_cu_q, n_seg, T_q, H, H_kv, d, softmax_scale, d_o, o_dtype, d_lse,
+                  precision, workspace, workspace_bytes, d_status, bd, stream);
 }
 
 extern "C" pvb_status pvb_varlen_attn_fwd(const void* d_q, const void* d_k, const void* d_v,

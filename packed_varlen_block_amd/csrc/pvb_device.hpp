@@ -210,11 +210,25 @@ struct PlanOut {
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
-                  int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status);
+                  int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status,
+                  int report_ok = 1);
 
 // Host helpers (defined in attn_common.hip).
 size_t plan_capacity(int32_t T, int32_t n_seg, int32_t tile);
 pvb_status check_host_cu(const int32_t* h_cu, int32_t n_seg, int32_t T);
+
+// Separate key boundaries cu_k (T_k keys) and the key band of each query row
+// (see KeyBand): the cross-attention / local-window form of the attention
+// entry points.  on = false is causal self-attention over one cu.
+struct BandArgs {
+  bool on = false;
+  const int32_t* cu_k = nullptr;
+  int T_k = 0, wl = -1, wr = 0;
+};
+// Host checks of the cross form: both host mirrors are required (the key
+// extents are read by the kernels without a device check), and validated.
+pvb_status check_cross_args(const int32_t* h_cu_q, const int32_t* d_cu_k, const int32_t* h_cu_k,
+                            int32_t n_seg, int32_t T_q, int32_t T_k, int32_t wl, int32_t wr);
 
 // ---------------------------------------------------------------------------
 // In-kernel work-item decode.
@@ -233,12 +247,15 @@ constexpr int kDecodeMaxM = 256;
 constexpr int kDecodeMaxSeg = 256;
 
 // Work list handed to the attention kernels: the planner's output, or
-// tiles == nullptr when each workgroup decodes its item.
+// tiles == nullptr when each workgroup decodes its item.  report_ok = false
+// (a second list of one call, written after the first) writes the status word
+// only on an error, so that it cannot clear the first list's error.
 struct WorkList {
   const int2* tiles;
   const int32_t* count;
   int32_t n_seg;
   int32_t* status;
+  bool report_ok = true;
 };
 
 __device__ __forceinline__ int wave_sum(int x) {
@@ -254,11 +271,11 @@ __device__ __forceinline__ int wave_max(int x) {
 
 // Item r of the heavy-first list of (segment, TILE-row tile) pairs.  The
 // result is wave-uniform and the same in every wave.  Returns false when there
-// is no item r or cu_seqlens is invalid; workgroup 0 then, and on success,
-// writes the status word.
+// is no item r or cu_seqlens is invalid; workgroup 0 then, and on success
+// when report_ok, writes the status word.
 template <int TILE>
 __device__ bool decode_work_item(const int32_t* __restrict__ cu, int n_seg, int T, int r, int2* item,
-                                 int32_t* __restrict__ status) {
+                                 int32_t* __restrict__ status, bool report_ok) {
   constexpr int J = kDecodeMaxSeg / 64;       // segments per lane
   const int lane = threadIdx.x & 63;
   int nt[J];
@@ -279,7 +296,7 @@ __device__ bool decode_work_item(const int32_t* __restrict__ cu, int n_seg, int 
   for (int j = 0; j < J; ++j) M = max(M, nt[j]);
   M = __builtin_amdgcn_readfirstlane(wave_max(M));
   const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0)
+  if (blockIdx.x == 0 && threadIdx.x == 0 && (report_ok || any_bad || M > kDecodeMaxM))
     *status = any_bad ? PVB_E_BAD_CU_SEQLENS : M > kDecodeMaxM ? PVB_E_UNSUPPORTED : PVB_OK;
   if (any_bad || M > kDecodeMaxM) return false;
   auto S = [&](int m) {
@@ -328,12 +345,31 @@ __device__ __forceinline__ HeadPair head_of_slot(int r, int H, int Hk) {
   return {hk * (H / Hk) + r / Hk, hk};
 }
 
+// The keys that query row r (local) of a slice may use: [lo(r), hi(r)],
+// clipped to [0, Lk) when BAND (empty when lo > hi).  delta = Lk - Lq aligns
+// the causal clamp to the bottom right; wl / wr < 0 leave that side
+// unbounded ("Packing与 FlashAttention Varlen", section 5: the key-block clamp
+// (m+1) BM + L_k - L_q + window_right).  Without BAND it is causal
+// self-attention, [0, r]; callers still bound keys by Lk themselves.
+template <bool BAND>
+struct KeyBand {
+  int Lk, delta, wl, wr;
+  __device__ __forceinline__ int hi(int r) const {
+    if constexpr (BAND) return wr < 0 ? Lk - 1 : min(Lk - 1, r + delta + wr);
+    else return r;
+  }
+  __device__ __forceinline__ int lo(int r) const {
+    if constexpr (BAND) return wl < 0 ? 0 : max(0, r + delta - wl);
+    else return 0;
+  }
+};
+
 // The item of workgroup tau: from the planner list, or decoded in place.
 template <int TILE, bool DECODE>
 __device__ __forceinline__ bool work_item(const WorkList& wl, const int32_t* __restrict__ cu, int T, int tau,
                                           int2* item) {
   if constexpr (DECODE) {
-    return decode_work_item<TILE>(cu, wl.n_seg, T, tau, item, wl.status);
+    return decode_work_item<TILE>(cu, wl.n_seg, T, tau, item, wl.status, wl.report_ok);
   } else {
     if (tau >= *wl.count) return false;
     *item = wl.tiles[tau];

@@ -200,3 +200,59 @@ def test_packed_nll_host_side_errors():
     assert call(ld=2) == 1
     assert call(g=FAKE, gd=3) == 1
     assert call(C=2**31) == 6
+
+
+def _xfwd(**kw):
+    cq = np.array([0, 8], np.int32)
+    ck = np.array([0, 12], np.int32)
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, h_cu_q=cq.ctypes.data, cu_k=FAKE, h_cu_k=ck.ctypes.data,
+                n_seg=1, T_q=8, T_k=12, H=4, H_kv=2, d=64, wl=-1, wr=0, scale=0.125, o=FAKE, o_dtype=0,
+                lse=FAKE, prec=0, ws=FAKE, ws_bytes=16, status=FAKE)
+    args.update(kw)
+    return pvb.lib().pvb_varlen_cross_attn_fwd(*args.values(), None)
+
+
+def _xbwd(**kw):
+    cq = np.array([0, 8], np.int32)
+    ck = np.array([0, 12], np.int32)
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, o_dtype=0, do=FAKE, lse=FAKE, cu_q=FAKE,
+                h_cu_q=cq.ctypes.data, cu_k=FAKE, h_cu_k=ck.ctypes.data, n_seg=1, T_q=8, T_k=12, H=4, H_kv=2,
+                d=64, wl=-1, wr=0, scale=0.125, dq=FAKE, dk=FAKE, dv=FAKE, g=1, prec=0, ws=FAKE, ws_bytes=16,
+                status=FAKE)
+    args.update(kw)
+    return pvb.lib().pvb_varlen_cross_attn_bwd(*args.values(), None)
+
+
+def test_cross_entry_points_reject_bad_arguments_on_host():
+    """Every case fails host validation; the valid ones stop at the (too small) workspace."""
+    assert _xfwd() == 5 and _xbwd() == 5
+    for call in (_xfwd, _xbwd):
+        assert call(h_cu_q=None) == 1                 # the host mirrors are required
+        assert call(h_cu_k=None) == 1
+        assert call(cu_k=None) == 1
+        assert call(wl=-2) == 1
+        assert call(wr=-5) == 1
+        assert call(T_k=-1) == 1
+        assert call(H_kv=3) == 1                      # 4 query heads over 3 key/value heads
+        assert call(d=96) == 6
+        assert call(k=None) == 1
+        assert call(T_k=13) == 4                      # h_cu_k[B] != T_k
+        assert call(T_q=9) == 4                       # h_cu_q[B] != T_q
+        dec = np.array([0, 9, 8, 12], np.int32)
+        ok3 = np.array([0, 2, 4, 8], np.int32)
+        assert call(n_seg=3, h_cu_k=dec.ctypes.data, h_cu_q=ok3.ctypes.data) == 4
+        assert call(scale=0.0) == 1
+    assert _xbwd(g=5) == 1
+    assert _xbwd(dk=None) == 1
+    # no keys at all: k, v (and dK, dV) may be null
+    assert _xfwd(k=None, v=None, T_k=0, h_cu_k=np.array([0, 0], np.int32).ctypes.data) == 5
+
+
+def test_cross_workspace_sizes():
+    W = pvb.cross_workspace_bytes
+    # the forward needs only the query tile list: the self-attention size for T_q
+    assert W(4096, 9000, 16, 128, 16, False) == pvb.workspace_bytes(4096, 16, 128, 16, False)
+    # the backward adds the key tile list to the self-attention size for T_q
+    assert W(4096, 4096, 16, 128, 16, True) > pvb.workspace_bytes(4096, 16, 128, 16, True)
+    assert W(4096, 64000, 16, 128, 16, True) >= 16 * 4096 * 8 + 64000 // 128 * 8
+    assert W(10, 10, 2, 96, 1, False) == 0 and W(10, -1, 2, 64, 1, True) == 0

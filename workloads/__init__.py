@@ -226,3 +226,16 @@ def random_small(seed: int, lengths, H: int, d: int, scale: float = 1.0,
     T = int(lengths.sum())
     q, k, v, do = tensors(seed, cfg_tag, T, H, d, scale, backward, outlier_frac, outlier_scale)
     return Workload(cfg_tag, f"small_{cfg_tag}", lengths, H, d, q, k, v, do, backward, seed)
+
+
+def random_cross(seed: int, lengths_q, lengths_k, H: int, Hk: int, d: int, scale: float = 1.0,
+                 backward: bool = True, cfg_tag: int = 98):
+    """Inputs with separate query and key segment lengths (cross attention,
+    local windows): q, dO bf16 bits [T_q, H, d]; k, v [T_k, Hk, d]."""
+    Tq = int(np.sum(np.asarray(lengths_q, dtype=np.int64)))
+    Tk = int(np.sum(np.asarray(lengths_k, dtype=np.int64)))
+    q = normal_bf16(seed, cfg_tag, STREAM_Q, (Tq, H, d), scale)
+    k = normal_bf16(seed, cfg_tag, STREAM_K, (Tk, Hk, d), scale)
+    v = normal_bf16(seed, cfg_tag, STREAM_V, (Tk, Hk, d), scale)
+    do = normal_bf16(seed, cfg_tag, STREAM_DO, (Tq, H, d), 1.0) if backward else None
+    return q, k, v, do
