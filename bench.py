@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--no-meta-case", action="store_true")
     ap.add_argument("--no-loss-case", action="store_true")
     ap.add_argument("--no-gqa-case", action="store_true")
+    ap.add_argument("--no-band-case", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -256,6 +257,8 @@ def main():
         out["packed_loss"] = packed_loss(torch, pvb, dev, stream, a.seed)
     if not a.no_gqa_case:
         out["grouped_heads"] = grouped_heads(torch, pvb, dev, stream, a.seed)
+    if not a.no_band_case:
+        out["cross_and_window"] = cross_and_window(torch, pvb, dev, stream, a.seed)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -408,6 +411,65 @@ def grouped_heads(torch, pvb, dev, stream, seed, T=8192, H=32, Hk=8, d=128, reps
     F = useful_fwd_flops([T], H, d)
     return {"workload": "gqa_T8192_H32_Hkv8_d128", "pass": "fwd+bwd", "fwd_ms": round(fwd, 4),
             "bwd_ms": round(bwd, 4), "useful_tflops": round(3.5 * F / ((fwd + bwd) * 1e-3) / 1e12, 2)}
+
+
+def band_pairs(Lq, Lk, wl, wr):
+    """(query, key) pairs a slice of Lq queries over Lk keys uses: query r takes
+    keys max(0, r + Lk - Lq - wl) .. min(Lk - 1, r + Lk - Lq + wr), a negative
+    bound being open."""
+    r = np.arange(Lq, dtype=np.int64)
+    hi = np.full(Lq, Lk - 1) if wr < 0 else np.minimum(Lk - 1, r + Lk - Lq + wr)
+    lo = np.zeros(Lq, dtype=np.int64) if wl < 0 else np.maximum(0, r + Lk - Lq - wl)
+    return float(np.maximum(hi - lo + 1, 0).sum())
+
+
+def cross_and_window(torch, pvb, dev, stream, seed, H=32, d=128, reps=5):
+    """Two band shapes at H=32, d=128 (O bf16, fp32 gradients), forward and
+    backward, useful TFLOP/s from the (query, key) pairs each uses (4 d flops
+    per pair forward, 2.5 times that backward), median of reps:
+      - local causal window of 1024 keys over the T=8192 single-segment pack
+        (window (1023, 0), keys = queries);
+      - chunked prefill: 4 slices whose last 2048 queries attend to all 8192 of
+        their keys with the causal clamp aligned to the bottom right."""
+    g = torch.Generator(device=dev).manual_seed(seed + 9)
+    res = {}
+    for name, lq, lk, win in (("window1024_T8192", [8192], [8192], (1023, 0)),
+                              ("prefill_q2048_k8192_x4", [2048] * 4, [8192] * 4, (-1, 0))):
+        Tq, Tk = sum(lq), sum(lk)
+        rnd = lambda *shape: (torch.randn(shape, generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        q, k, v, do = rnd(Tq, H, d), rnd(Tk, H, d), rnd(Tk, H, d), rnd(Tq, H, d) * 2
+        hq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+        hk = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        cq, ck = torch.from_numpy(hq).to(dev), torch.from_numpy(hk).to(dev)
+        o = torch.empty((Tq, H, d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=dev)
+        dq = torch.empty((Tq, H, d), dtype=torch.float32, device=dev)
+        dk, dv = (torch.empty((Tk, H, d), dtype=torch.float32, device=dev) for _ in range(2))
+        n = len(lq)
+        wf = torch.empty(pvb.cross_workspace_bytes(Tq, Tk, H, d, n, False), dtype=torch.uint8, device=dev)
+        wb = torch.empty(pvb.cross_workspace_bytes(Tq, Tk, H, d, n, True), dtype=torch.uint8, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        ev = []
+        for i in range(2 + reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            pvb.varlen_cross_attn_fwd(q, k, v, cq, ck, hq, hk, window=win, out=o, lse=lse, workspace=wf, status=st)
+            e[1].record(stream)
+            pvb.varlen_cross_attn_bwd(q, k, v, o, do, lse, cq, ck, hq, hk, window=win, dq=dq, dk=dk, dv=dv,
+                                      workspace=wb, status=st)
+            e[2].record(stream)
+            if i >= 2:
+                ev.append(e)
+        torch.cuda.synchronize()
+        pvb.check_status(st)
+        fwd = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+        bwd = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+        F = sum(band_pairs(a, b, *win) for a, b in zip(lq, lk)) * 4.0 * d * H
+        res[name] = {"window": list(win), "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+                     "fwd_tflops": round(F / (fwd * 1e-3) / 1e12, 2),
+                     "bwd_tflops": round(2.5 * F / (bwd * 1e-3) / 1e12, 2),
+                     "useful_tflops": round(3.5 * F / ((fwd + bwd) * 1e-3) / 1e12, 2)}
+    return res
 
 
 def packed_loss(torch, pvb, dev, stream, seed, C=8192, V=32768, reps=20):
