@@ -200,14 +200,26 @@ def build_packed_row(lengths, capacity: int | None = None, segment_base: int = 0
     return out
 
 
-def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None = None, status=None):
+def _reuse(out, name, shape, dtype, dev):
+    """An output tensor taken from a caller's dict (no allocation), checked."""
+    t = out[name]
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or not t.is_contiguous():
+        raise PvbError(1, f"out[{name!r}] must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
+    return t
+
+
+def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None = None, status=None,
+                              out=None):
     """cu_seqlens compiled back from a flat int32 CUDA position stream [T].
 
     ``sentinel`` "zero" (a segment starts where the position is 0) or "min"
     (where it equals the smallest position).  Returns a dict of CUDA tensors:
     cu [capacity] (entries 0..n_seg valid), n_seg [1], max_seqlen [1],
-    status [1].  ``capacity`` defaults to T + 1.  Enqueued on the current
-    stream; call check_status(out["status"]) to synchronise and raise.
+    status [1].  ``capacity`` defaults to T + 1.  ``out``: a dict returned by an
+    earlier call, whose tensors are written again (nothing is allocated; its
+    values are those of the last call until the kernel writes them).  Enqueued
+    on the current stream; call check_status(out["status"]) to synchronise and
+    raise.
     """
     torch = _torch()
     dev = pos.device
@@ -217,10 +229,16 @@ def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None 
         raise PvbError(1, "boundaries_from_positions: sentinel must be 'zero' or 'min'")
     T = pos.numel()
     cap = T + 1 if capacity is None else int(capacity)
-    out = {"cu": torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-           "n_seg": torch.zeros(1, dtype=torch.int32, device=dev),
-           "max_seqlen": torch.zeros(1, dtype=torch.int32, device=dev),
-           "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+    if out is not None:
+        out = {"cu": _reuse(out, "cu", (max(cap, 1),), torch.int32, dev),
+               "n_seg": _reuse(out, "n_seg", (1,), torch.int32, dev),
+               "max_seqlen": _reuse(out, "max_seqlen", (1,), torch.int32, dev),
+               "status": status if status is not None else _reuse(out, "status", (1,), torch.int32, dev)}
+    else:
+        out = {"cu": torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+               "n_seg": torch.zeros(1, dtype=torch.int32, device=dev),
+               "max_seqlen": torch.zeros(1, dtype=torch.int32, device=dev),
+               "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
     rc = lib().pvb_boundaries_from_positions(
         _ptr(pos) if T > 0 else None, T, PVB_SENTINEL_MIN if sentinel == "min" else PVB_SENTINEL_ZERO,
         _ptr(out["cu"]), cap, _ptr(out["n_seg"]), _ptr(out["max_seqlen"]), _ptr(out["status"]),
@@ -229,14 +247,16 @@ def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None 
     return out
 
 
-def packed_nll(logits, targets, mask=None, grad=True, grad_dtype=None, status=None):
+def packed_nll(logits, targets, mask=None, grad=True, grad_dtype=None, status=None, out=None):
     """Token-weighted NLL over packed cells.  ``logits`` is a CUDA [C, V]
     bf16/fp32 tensor, ``targets`` int32 [C] (cells with a negative target are
     excluded), ``mask`` optional uint8 [C] loss eligibility.  Returns a dict of
     CUDA tensors: row_nll [C], loss [2] (float64 sum, mean), count [1],
     status [1], and grad [C, V] (logits' dtype unless ``grad_dtype``) when
-    ``grad``.  Enqueued on the current stream; call check_status(out["status"])
-    to synchronise and raise on a device-detected error."""
+    ``grad``.  ``out``: a dict returned by an earlier call of the same shapes,
+    whose tensors are written again (nothing is allocated).  Enqueued on the
+    current stream; call check_status(out["status"]) to synchronise and raise
+    on a device-detected error."""
     torch = _torch()
     dev = logits.device
     if logits.dim() != 2 or not logits.is_contiguous():
@@ -247,12 +267,21 @@ def packed_nll(logits, targets, mask=None, grad=True, grad_dtype=None, status=No
     if mask is not None and (mask.dtype != torch.uint8 or tuple(mask.shape) != (C,) or not mask.is_contiguous()):
         raise PvbError(1, "packed_nll: mask must be contiguous uint8 [C]")
     gdt = logits.dtype if grad_dtype is None else grad_dtype
-    out = {"row_nll": torch.empty(max(C, 1), dtype=torch.float32, device=dev)[:C],
-           "loss": torch.zeros(2, dtype=torch.float64, device=dev),
-           "count": torch.zeros(1, dtype=torch.int32, device=dev),
-           "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
-    if grad:
-        out["grad"] = torch.empty((C, V), dtype=gdt, device=dev)
+    if out is not None:
+        prev = out
+        out = {"row_nll": _reuse(prev, "row_nll", (C,), torch.float32, dev),
+               "loss": _reuse(prev, "loss", (2,), torch.float64, dev),
+               "count": _reuse(prev, "count", (1,), torch.int32, dev),
+               "status": status if status is not None else _reuse(prev, "status", (1,), torch.int32, dev)}
+        if grad:
+            out["grad"] = _reuse(prev, "grad", (C, V), gdt, dev)
+    else:
+        out = {"row_nll": torch.empty(max(C, 1), dtype=torch.float32, device=dev)[:C],
+               "loss": torch.zeros(2, dtype=torch.float64, device=dev),
+               "count": torch.zeros(1, dtype=torch.int32, device=dev),
+               "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+        if grad:
+            out["grad"] = torch.empty((C, V), dtype=gdt, device=dev)
     rc = lib().pvb_packed_nll(
         _ptr(logits) if C > 0 else None, _dtype_code(logits.dtype), C, V, _ptr(targets) if C > 0 else None,
         _ptr(mask) if mask is not None else None, _ptr(out["row_nll"]) if C > 0 else None, _ptr(out["loss"]),
