@@ -16,7 +16,8 @@ loops, one segment and one head at a time, written from the pages
 Modules
   packing     -- O1 metadata, O2 next-fit, O3 best-fit-decreasing, O4 pair forming
   attention   -- O5 forward, O6 backward, O7 brute-force dense masked attention
-  loss_probe  -- O8 the constructed loss probe
+  loss_probe  -- O8 the constructed loss probe, O10 the packed-row loss
+  linear_attention -- O11 the gated delta rule with its state reset at every boundary
 
 Parity status: every function here is pinned by tests under ``tests/``
 (``-m "not gpu"``) against values the pages print, closed forms, brute force
