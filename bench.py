@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-loss-case", action="store_true")
     ap.add_argument("--no-gqa-case", action="store_true")
     ap.add_argument("--no-band-case", action="store_true")
+    ap.add_argument("--no-gdn-case", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -259,6 +260,8 @@ def main():
         out["grouped_heads"] = grouped_heads(torch, pvb, dev, stream, a.seed)
     if not a.no_band_case:
         out["cross_and_window"] = cross_and_window(torch, pvb, dev, stream, a.seed)
+    if not a.no_gdn_case:
+        out["gated_delta"] = gated_delta(torch, pvb, W, dev, stream, a.seed)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -488,6 +491,51 @@ def cross_and_window(torch, pvb, dev, stream, seed, H=32, d=128, reps=5):
                      "bwd_tflops": round(2.5 * F / (bwd * 1e-3) / 1e12, 2),
                      "useful_tflops": round(3.5 * F / ((fwd + bwd) * 1e-3) / 1e12, 2)}
     return res
+
+
+def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
+    """Gated delta rule over the long mixed pack (T=32768: one 16384-token
+    slice, then slices of 16-1024), H=32, d=128, bf16 O and fp32 final states,
+    the state reset at every boundary; g ~ U(-0.1, 0), beta ~ U(0.05, 1), unit
+    q and k.  Each (slice, head) is a chain of 64-token chunks, so the time is
+    set by the longest slice: reported per chunk of that chain, beside the
+    HBM rate of the algorithmic bytes (q, k, v, g, beta read once, O and the
+    final states written once).  Median of reps."""
+    lengths = W.lengths_cfg4(seed)
+    T, B = int(lengths.sum()), len(lengths)
+    g = torch.Generator(device=dev).manual_seed(seed + 11)
+
+    def unit(*shape):
+        x = torch.randn(shape, generator=g, device=dev)
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    q, k = unit(T, H, d), unit(T, H, d)
+    v = torch.randn((T, H, d), generator=g, device=dev).to(torch.bfloat16)
+    gg = torch.rand((T, H), generator=g, device=dev) * -0.1
+    bb = torch.rand((T, H), generator=g, device=dev) * 0.95 + 0.05
+    hc = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cu = torch.from_numpy(hc).to(dev)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, status=st)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, status=st)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    pvb.check_status(st)
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    byts = 4 * T * H * d * 2 + 2 * T * H * 4 + B * H * d * d * 4
+    chain = int(-(-int(lengths.max()) // 64))
+    return {"workload": "gdn_long_mixed_T32768_H32_d128", "segments": B, "ms": round(ms, 4),
+            "longest_chain_chunks": chain, "us_per_chunk": round(ms * 1e3 / chain, 3),
+            "algorithmic_bytes": byts, "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def packed_loss(torch, pvb, dev, stream, seed, C=8192, V=32768, reps=20):

@@ -322,6 +322,36 @@ pvb_status pvb_varlen_cross_attn_bwd(const void* d_q, const void* d_k, const voi
                                      int32_t precision, void* workspace, size_t workspace_bytes,
                                      int32_t* d_status, void* stream);
 
+/* ------------------------------------------- linear attention: gated delta rule */
+
+/* Gated delta rule over the packed stream with its recurrent state reset at
+ * every boundary ("Packing与 FlashAttention Varlen", section 6: the
+ * linear-attention layers take the same cumulative boundaries, which keep
+ * one sample's recurrent state out of the next).  The recurrence is the
+ * published gated delta rule: for slice b and head h, with a [d, d] state S
+ * (key dims x value dims) starting at h0[b, h] (zero when d_h0 is null), for
+ * each token t of the slice in order:
+ *   S <- exp(g_t) S;  u_t = beta_t (v_t - S^T k_t);  S <- S + k_t u_t^T;
+ *   o_t = scale S^T q_t;
+ * and ht[b, h] = the slice's final S.  Zero-length slices give ht = h0.
+ *   d_q, d_k, d_v  bf16 [T, H, d] (normalise q and k beforehand if wanted)  (device)
+ *   d_g            fp32 [T, H] log gates, expected <= 0                      (device)
+ *   d_beta         fp32 [T, H] write strengths                               (device)
+ *   d_cu, h_cu     as in pvb_varlen_attn_fwd (h_cu nullable)
+ *   d_h0           fp32 [n_seg, H, d, d] initial states, nullable            (device)
+ *   d_o            out [T, H, d], bf16 or fp32 per o_dtype                   (device)
+ *   d_ht           out fp32 [n_seg, H, d, d] final states, nullable          (device)
+ *   d_status       out: device status word (required)                       (device)
+ * d = 128 (else PVB_E_UNSUPPORTED).  No workspace.  The slices are computed in
+ * chunks of 64 tokens (UT transform) in fp32 with matrix-core products whose
+ * fp32 operands are split into two bf16 parts.  Device-detected error:
+ * PVB_E_BAD_CU_SEQLENS (then O and ht are not written). */
+pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                               const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                               int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
+                               const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
+                               int32_t* d_status, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);
 

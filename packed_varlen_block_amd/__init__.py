@@ -34,6 +34,7 @@ STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "P
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
            "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
            "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
+           "pvb_gated_delta_fwd",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_status_string", "pvb_version")
 
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
                                               P, P]
         L.pvb_varlen_attn_bwd_gqa.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
                                               P, P, P, I32, I32, P, SZ, P, P]
+        L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, P]
         L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
         L.pvb_varlen_cross_attn_workspace_bytes.restype = SZ
         L.pvb_varlen_cross_attn_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F,
@@ -79,7 +81,7 @@ def lib() -> ctypes.CDLL:
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
                      "pvb_boundaries_from_positions", "pvb_packed_nll", "pvb_varlen_attn_fwd",
                      "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
-                     "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd"):
+                     "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd", "pvb_gated_delta_fwd"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
         L.pvb_status_string.restype = ctypes.c_char_p
@@ -493,3 +495,49 @@ def varlen_cross_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, h_cu_q, h_cu_k, windo
                                          _stream(dev))
     _check(rc, "varlen_cross_attn_bwd")
     return dq, dk, dv, status
+
+
+def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=None, final_state=True,
+                    o_dtype=None, out=None, state_out=None, status=None):
+    """Gated delta rule over the packed stream, the state reset at every
+    boundary of ``cu``.  q, k, v: contiguous bf16 CUDA [T, H, 128]; g, beta:
+    fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].  Returns
+    (O [T, H, 128], final states [B, H, 128, 128] fp32 or None, status)."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise PvbError(1, "q must be [T, H, d]")
+    T, H, d = q.shape
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (T, H, d) or not t.is_cuda:
+            raise PvbError(1, "q, k, v must be contiguous bf16 CUDA tensors of one shape [T, H, d]")
+    for t in (g, beta):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (T, H) or not t.is_cuda:
+            raise PvbError(1, "g and beta must be contiguous fp32 CUDA tensors [T, H]")
+    if cu.dtype != torch.int32 or not cu.is_cuda:
+        raise PvbError(1, "cu must be an int32 CUDA tensor")
+    n_seg = cu.numel() - 1
+    dev = q.device
+    if initial_state is not None and (initial_state.dtype != torch.float32 or not initial_state.is_contiguous()
+                                      or tuple(initial_state.shape) != (n_seg, H, d, d)):
+        raise PvbError(1, "initial_state must be contiguous fp32 [B, H, d, d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o_dtype = torch.bfloat16 if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((T, H, d), dtype=o_dtype, device=dev)
+    ht = None
+    if final_state:
+        ht = state_out if state_out is not None else torch.empty((max(n_seg, 0), H, d, d), dtype=torch.float32,
+                                                                   device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    hc = None
+    if h_cu is not None:
+        hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
+        if hc.size != n_seg + 1:
+            raise PvbError(1, "h_cu must have B+1 entries")
+    rc = lib().pvb_gated_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg, T,
+                                   H, d, scale, _ptr(initial_state), _ptr(out), _dtype_code(out.dtype),
+                                   _ptr(ht) if ht is not None and ht.numel() > 0 else None, _ptr(status),
+                                   _stream(dev))
+    _check(rc, "gated_delta_fwd")
+    return out, ht, status

@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpvb.so")
 
 SOURCES = ["abi.cpp", "pack_plan.cpp", "packed_row.hip", "packed_loss.hip", "attn_common.hip", "attn_fwd.hip",
-           "attn_bwd.hip"]
+           "attn_bwd.hip", "gated_delta.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

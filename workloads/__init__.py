@@ -239,3 +239,28 @@ def random_cross(seed: int, lengths_q, lengths_k, H: int, Hk: int, d: int, scale
     v = normal_bf16(seed, cfg_tag, STREAM_V, (Tk, Hk, d), scale)
     do = normal_bf16(seed, cfg_tag, STREAM_DO, (Tq, H, d), 1.0) if backward else None
     return q, k, v, do
+
+
+def random_gated_delta(seed: int, lengths, H: int, d: int = 128, g_range=(-0.1, 0.0),
+                       beta_range=(0.05, 1.0), initial_state: bool = False, cfg_tag: int = 97):
+    """Inputs of the gated delta rule over a packed stream: q, k bf16 bits of
+    unit-norm rows (normalised in float32, then rounded), v bf16 bits of
+    N(0,1), log gates g ~ U(g_range) and write strengths beta ~ U(beta_range)
+    as float32 [T, H], and optionally float32 initial states N(0,1)*0.1
+    [B, H, d, d].  Returned as a dict."""
+    lengths = np.asarray(lengths, dtype=np.int32)
+    T = int(lengths.sum())
+    r = _rng(seed, cfg_tag, STREAM_Q)
+    qf = r.standard_normal((T, H, d), dtype=np.float32)
+    kf = _rng(seed, cfg_tag, STREAM_K).standard_normal((T, H, d), dtype=np.float32)
+    qf /= np.maximum(np.linalg.norm(qf, axis=-1, keepdims=True), np.float32(1e-6))
+    kf /= np.maximum(np.linalg.norm(kf, axis=-1, keepdims=True), np.float32(1e-6))
+    out = {"lengths": lengths, "q": f32_to_bf16_bits(qf), "k": f32_to_bf16_bits(kf),
+           "v": normal_bf16(seed, cfg_tag, STREAM_V, (T, H, d), 1.0)}
+    rg = _rng(seed, cfg_tag, STREAM_DO)
+    out["g"] = rg.uniform(g_range[0], g_range[1], size=(T, H)).astype(np.float32)
+    out["beta"] = rg.uniform(beta_range[0], beta_range[1], size=(T, H)).astype(np.float32)
+    if initial_state:
+        out["h0"] = (_rng(seed, cfg_tag, STREAM_OUTLIER).standard_normal((len(lengths), H, d, d), dtype=np.float32)
+                     * np.float32(0.1))
+    return out
