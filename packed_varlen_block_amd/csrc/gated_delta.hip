@@ -23,6 +23,8 @@
 // One workgroup of 4 waves per (slice, head); the slices are independent.
 // Wave w owns value columns [32w, 32w + 32) of the state, which stays in its
 // registers (C layout of four 32x32 blocks) across the chunks of the slice.
+#include <type_traits>
+
 #include "pvb_device.hpp"
 
 namespace pvb {
@@ -32,22 +34,29 @@ constexpr int kGdD = 128;            // d_k = d_v
 constexpr int kGdC = 64;             // chunk length
 constexpr int kGdThreads = 256;
 constexpr int kKP = kGdD + 8;        // bf16 row pitch of the Q, K, V tiles
-constexpr int kTP = kGdC + 8;        // bf16 row pitch of K^T
-constexpr int kFP = kGdC + 4;        // fp32 row pitch of A^T, P and U^T
+constexpr int kFP = kGdC + 4;        // fp32 row pitch of A^T and P
 
 struct GdSmem {
   alignas(16) bf16 q[kGdC][kKP];
   alignas(16) bf16 k[kGdC][kKP];
   alignas(16) bf16 v[kGdC][kKP];
-  alignas(16) bf16 kt[kGdD][kTP];    // K^T: kt[c][pos]
   alignas(16) float at[kGdC][kFP];   // A^T: at[j][i] = A[i][j]
   alignas(16) float p[kGdC][kFP];    // P (row i, column j)
-  alignas(16) float ut[kGdD][kFP];   // U, transposed: ut[n][pos]
-  alignas(16) float gam[kGdC];       // gamma_i
+  // A operands shared by the four waves, split once per chunk, in fragment
+  // order [..][lane]: the gated keys for the state update (key-dim block r,
+  // position step s) and P (row block rb, position step s; rb = 0 stops at
+  // s = 2).  Positions inside a step are in the order of the C layout's rows.
+  alignas(16) bf16x8 kth[4][4][64], ktl[4][4][64];
+  alignas(16) bf16x8 ph[6][64], pl[6][64];
+  alignas(16) float gl[kGdC];        // gamma_i log2(e)
   alignas(16) float eg[kGdC];        // exp(gamma_i)
   alignas(16) float dec[kGdC];       // exp(gamma_63 - gamma_i)
   alignas(16) float beta[kGdC];
 };
+
+// Position of element e of a k-step s fragment whose k order follows the C
+// layout's rows (lane half hg): 16s + 8(e/4) + 4hg + e%4.
+__device__ __forceinline__ int kpos(int s, int e, int hg) { return 16 * s + 8 * (e >> 2) + 4 * hg + (e & 3); }
 
 // hi = bf16(x), lo = bf16(x - hi): hi + lo carries about 16 significant bits.
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
@@ -96,80 +105,125 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
     for (int i = 0; i < 16; ++i)
       S[r][i] = h0 ? h0[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
 
-  for (int c0 = 0; c0 < L; c0 += kGdC) {
-    const int nv = min(kGdC, L - c0);
-    __syncthreads();                                  // the previous chunk's reads are done
-
-    // ---- stage Q, K, V (zero past the slice's end), K^T, and the gates
+  // The inputs of chunk c + 1 are loaded into registers while chunk c is
+  // computed (and before its outputs are stored, so that waiting for them
+  // never waits for those stores).
+  uint4 pq[4], pk[4], pv[4];
+  float pg = 0.f, pb = 0.f;
+  auto fetch = [&](int cc0) {
+    const int nvv = min(kGdC, L - cc0);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int ch = tid + kGdThreads * it;           // 16-byte chunk: row ch/16, columns 8(ch%16)..
       const int row = ch >> 4, col = (ch & 15) * 8;
-      uint4 xq = zero4(), xk = zero4(), xv = zero4();
-      if (row < nv) {
-        const size_t off = ((size_t)(seg0 + c0 + row) * H + h) * kGdD + col;
-        xq = *(const uint4*)(q + off);
-        xk = *(const uint4*)(k + off);
-        xv = *(const uint4*)(v + off);
+      pq[it] = pk[it] = pv[it] = zero4();
+      if (row < nvv) {
+        const size_t off = ((size_t)(seg0 + cc0 + row) * H + h) * kGdD + col;
+        pq[it] = *(const uint4*)(q + off);
+        pk[it] = *(const uint4*)(k + off);
+        pv[it] = *(const uint4*)(v + off);
       }
-      *(uint4*)&sm.q[row][col] = xq;
-      *(uint4*)&sm.k[row][col] = xk;
-      *(uint4*)&sm.v[row][col] = xv;
-      const bf16x8 kk = __builtin_bit_cast(bf16x8, xk);
+    }
+    pg = pb = 0.f;
+    if (w == 0 && lane < nvv) {
+      const size_t idx = (size_t)(seg0 + cc0 + lane) * H + h;
+      pg = g[idx];
+      pb = beta[idx];
+    }
+  };
+  if (L > 0) fetch(0);
+
+  for (int c0 = 0; c0 < L; c0 += kGdC) {
+    const int nv = min(kGdC, L - c0);
+    __syncthreads();                                  // the previous chunk's reads are done
+
+    // ---- stage Q, K, V (zero past the slice's end) and the gates
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.kt[col + e][row] = kk[e];
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + kGdThreads * it;
+      const int row = ch >> 4, col = (ch & 15) * 8;
+      *(uint4*)&sm.q[row][col] = pq[it];
+      *(uint4*)&sm.k[row][col] = pk[it];
+      *(uint4*)&sm.v[row][col] = pv[it];
     }
     if (w == 0) {
-      float gg = 0.f, bb = 0.f;
-      if (lane < nv) {
-        const size_t idx = (size_t)(seg0 + c0 + lane) * H + h;
-        gg = g[idx];
-        bb = beta[idx];
-      }
-      float x = gg;                                   // inclusive sum over the chunk
+      float x = pg;                                   // inclusive sum over the chunk
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
       }
+      x *= kLog2e;
       const float last = __shfl(x, 63, 64);
-      sm.gam[lane] = x;
-      sm.eg[lane] = expf(x);
-      sm.dec[lane] = expf(last - x);
-      sm.beta[lane] = bb;
+      sm.gl[lane] = x;
+      sm.eg[lane] = fast_exp2(x);
+      sm.dec[lane] = fast_exp2(last - x);
+      sm.beta[lane] = pb;
     }
+    if (c0 + kGdC < L) fetch(c0 + kGdC);
     __syncthreads();
 
     // ---- A (for the solve, stored transposed) and P: the lower 32x32 blocks
-    // (0,0), (1,0), (1,1) of K K^T and Q K^T; block (0,1) is never read
-    for (int item = w; item < 6; item += 4) {
-      const bool isq = item >= 3;
-      const int blk = isq ? item - 3 : item;
-      const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
+    // (0,0), (1,0), (1,1) of K K^T and Q K^T (block (0,1) is never read), two
+    // blocks for waves 0 and 1, one for waves 2 and 3
+    auto block = [&](auto isq_tag, int bi, int bj) {
+      constexpr bool ISQ = decltype(isq_tag)::value;
       f32x16 acc = {};
 #pragma unroll
       for (int s = 0; s < kGdD / 16; ++s) {
-        const bf16x8 a = isq ? *(const bf16x8*)&sm.q[32 * bi + c][16 * s + 8 * hg]
+        const bf16x8 a = ISQ ? *(const bf16x8*)&sm.q[32 * bi + c][16 * s + 8 * hg]
                              : *(const bf16x8*)&sm.k[32 * bi + c][16 * s + 8 * hg];
         const bf16x8 bk = *(const bf16x8*)&sm.k[32 * bj + c][16 * s + 8 * hg];
         acc = mfma32(a, bk, acc);
       }
       const int pj = 32 * bj + c;
-      const float gj = sm.gam[pj];
+      const float gj = sm.gl[pj];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int pi = 32 * bi + crow(i, hg);
-        const float dcy = pj <= pi ? expf(sm.gam[pi] - gj) : 0.f;
-        if (isq) sm.p[pi][pj] = acc[i] * dcy;
-        else sm.at[pj][pi] = pj < pi ? sm.beta[pi] * acc[i] * dcy : 0.f;
+      for (int m = 0; m < 4; ++m) {
+        const int p0 = 32 * bi + 8 * m + 4 * hg;      // rows p0 .. p0 + 3
+        const float4 gi = *(const float4*)&sm.gl[p0];
+        const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
+        float bv[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (!ISQ) {
+          const float4 b4 = *(const float4*)&sm.beta[p0];
+          bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pi = p0 + e;
+          const float dcy = fast_exp2(fminf(gv[e] - gj, 0.f));
+          if constexpr (ISQ) sm.p[pi][pj] = pj <= pi ? acc[4 * m + e] * dcy : 0.f;
+          else sm.at[pj][pi] = pj < pi ? bv[e] * acc[4 * m + e] * dcy : 0.f;
+        }
       }
+    };
+    using KK = std::integral_constant<bool, false>;
+    using QK = std::integral_constant<bool, true>;
+    if (w == 0) { block(KK{}, 1, 0); block(QK{}, 0, 0); }
+    else if (w == 1) { block(QK{}, 1, 0); block(KK{}, 0, 0); }
+    else if (w == 2) block(KK{}, 1, 1);
+    else block(QK{}, 1, 1);
+
+    // ---- the gated keys (diag(G_63 / G) K)^T as split A fragments, once for
+    // the four waves: fragment f = (r, s, lane) of a thread
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int f = tid + kGdThreads * it;
+      const int r = f >> 8, s = (f >> 6) & 3, fl = f & 63, fc = fl & 31, fh = fl >> 5;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = kpos(s, e, fh);
+        x[e] = (float)sm.k[pos][32 * r + fc] * sm.dec[pos];
+      }
+      split8(x, sm.kth[r][s][fl], sm.ktl[r][s][fl]);
     }
 
-    // ---- K S0 for this wave's columns.  The state is the B operand straight
-    // from its C layout: k-step s takes elements 8(s%2) + e of block s/2, i.e.
-    // key dims 16s + 8(e/4) + 4hg + e%4, so the K rows are read in that order
-    // (two 8-byte pieces).
-    f32x16 ks[2] = {};
+    // ---- K S0 and Q S0 for this wave's columns.  The state is the B operand
+    // straight from its C layout: k-step s takes elements 8(s%2) + e of block
+    // s/2, i.e. key dims kpos(s, e, hg), so the K and Q rows are read in that
+    // order (two 8-byte pieces).
+    f32x16 ks[2] = {}, oacc[2] = {};
 #pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
       float sv[8];
@@ -180,29 +234,47 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const bf16* kr = &sm.k[32 * rb + c][16 * s + 4 * hg];
+        const bf16* qr = &sm.q[32 * rb + c][16 * s + 4 * hg];
         const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
+        const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
         ks[rb] = mfma32(ka, shi, ks[rb]);
         ks[rb] = mfma32(ka, slo, ks[rb]);
+        oacc[rb] = mfma32(qa, shi, oacc[rb]);
+        oacc[rb] = mfma32(qa, slo, oacc[rb]);
       }
     }
 
-    // ---- right-hand side, in place: rows pos = 32 rb + crow(i, hg)
+    // ---- right-hand side, in place (rows pos = 32 rb + crow(i, hg)); the
+    // state's part of O takes its gate
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int pos = 32 * rb + crow(i, hg);
-        ks[rb][i] = sm.beta[pos] * ((float)sm.v[pos][n0] - sm.eg[pos] * ks[rb][i]);
+        const float egp = sm.eg[pos];
+        ks[rb][i] = sm.beta[pos] * ((float)sm.v[pos][n0] - egp * ks[rb][i]);
+        oacc[rb][i] *= egp;
       }
-    __syncthreads();                                  // A is complete
+    __syncthreads();                                  // A and P are complete
+
+    // ---- P as split A fragments, once for the four waves (read after the
+    // next barrier): fragment f = (rb, s, lane), rb = 0 with s < 2 only
+    for (int f = tid; f < 6 * 64; f += kGdThreads) {
+      const int fi = f >> 6, fl = f & 63, fc = fl & 31, fh = fl >> 5;
+      const int rb = fi < 2 ? 0 : 1, s = fi < 2 ? fi : fi - 2;
+      const float* src = &sm.p[32 * rb + fc][16 * s + 4 * fh];
+      const float4 a4 = *(const float4*)src, b4 = *(const float4*)(src + 8);
+      const float x[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+      split8(x, sm.ph[fi][fl], sm.pl[fi][fl]);
+    }
 
     // ---- (I + A) U = rhs in the C layout: lanes c and c + 32 hold column
     // n0, each in groups of four rows (rows 8m + 4hg .. + 3 of each 32-row
     // block).  Step j: the lane holding row j (final by then) hands u_j to its
     // partner, and every row group that may lie below row j subtracts its
     // A[row][j] multiple.  A is zero on and above the diagonal, so the rows
-    // of row j's own group that are not below it are left as they are.
-    // The A values of step j + 1 are read while step j computes.
+    // of row j's own group that are not below it are left as they are.  The
+    // A values of step j + 1 are read while step j computes.
     float4 acur[2][4], anext[2][4];
     auto load_a = [&](int j, float4 (&buf)[2][4]) {
 #pragma unroll
@@ -212,7 +284,8 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
           if (32 * rb + 8 * m + 7 > j) buf[rb][m] = *(const float4*)&sm.at[j][32 * rb + 8 * m + 4 * hg];
     };
     load_a(0, acur);
-#pragma unroll
+    // fully unrolled: every register index below must be a constant
+#pragma clang loop unroll(full)
     for (int j = 0; j < kGdC - 1; ++j) {
       if (j + 1 < kGdC - 1) load_a(j + 1, anext);
       const int rbj = j >> 5, jj = j & 31;
@@ -237,62 +310,47 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 #pragma unroll
         for (int m = 0; m < 4; ++m) acur[rb][m] = anext[rb][m];
     }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.ut[n0][32 * rb + crow(i, hg)] = ks[rb][i];
 
-    // ---- Q S0 (the state's part of O), after the solve to keep it short
-    f32x16 oacc[2] = {};
-#pragma unroll
-    for (int s = 0; s < kGdD / 16; ++s) {
-      float sv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = S[s >> 1][8 * (s & 1) + e];
-      bf16x8 shi, slo;
-      split8(sv, shi, slo);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16* qr = &sm.q[32 * rb + c][16 * s + 4 * hg];
-        const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
-        oacc[rb] = mfma32(qa, shi, oacc[rb]);
-        oacc[rb] = mfma32(qa, slo, oacc[rb]);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[rb][i] *= sm.eg[32 * rb + crow(i, hg)];
-
-    // ---- U as the B operand (k = position), split; reused by both products
+    // ---- U as the B operand straight from its C layout (k-step s: elements
+    // 8(s%2) + e of row block s/2, positions kpos(s, e, hg)), split
     bf16x8 uh[4], ul[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float* src = &sm.ut[n0][16 * s + 8 * hg];
-      const float4 a4 = *(const float4*)src, b4 = *(const float4*)(src + 4);
-      const float x[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = ks[s >> 1][8 * (s & 1) + e];
       split8(x, uh[s], ul[s]);
     }
+    __syncthreads();                                  // the P and key fragments are complete
 
-    // ---- O = scale (diag(G) Q S0 + P U); row block 0 has no key past 31
+    // ---- O = scale (diag(G) Q S0 + P U); row block 0 has no key past 31.
+    // The wave's 64 x 32 block is staged in the Q/K tiles (free by now) and
+    // written with 16-byte stores.
+    OutT* stg = reinterpret_cast<OutT*>(&sm.q[0][0]) + w * (kGdC * 32);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (rb == 0 && s >= 2) continue;
-        const float* src = &sm.p[32 * rb + c][16 * s + 8 * hg];
-        const float4 a4 = *(const float4*)src, b4 = *(const float4*)(src + 4);
-        const float x[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
-        bf16x8 ph, pl;
-        split8(x, ph, pl);
-        oacc[rb] = mfma32(ph, uh[s], oacc[rb]);
-        oacc[rb] = mfma32(ph, ul[s], oacc[rb]);
-        oacc[rb] = mfma32(pl, uh[s], oacc[rb]);
+        const int fi = rb == 0 ? s : 2 + s;
+        const bf16x8 a_hi = sm.ph[fi][lane], a_lo = sm.pl[fi][lane];
+        oacc[rb] = mfma32(a_hi, uh[s], oacc[rb]);
+        oacc[rb] = mfma32(a_hi, ul[s], oacc[rb]);
+        oacc[rb] = mfma32(a_lo, uh[s], oacc[rb]);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int pos = 32 * rb + crow(i, hg);
-        if (pos < nv) o[((size_t)(seg0 + c0 + pos) * H + h) * kGdD + n0] = out_cast<OutT>(scale * oacc[rb][i]);
+      for (int i = 0; i < 16; ++i) stg[(32 * rb + crow(i, hg)) * 32 + c] = out_cast<OutT>(scale * oacc[rb][i]);
+    }
+    {
+      constexpr int kPer = 16 / sizeof(OutT);         // elements per 16-byte piece
+      constexpr int kRowPieces = 32 / kPer;           // pieces per 32-column row
+#pragma unroll
+      for (int it = 0; it < kGdC * kRowPieces / 64; ++it) {
+        const int piece = lane + 64 * it;
+        const int row = piece / kRowPieces, cp = piece % kRowPieces;
+        if (row < nv)
+          *(uint4*)(o + ((size_t)(seg0 + c0 + row) * H + h) * kGdD + 32 * w + cp * kPer) =
+              *(const uint4*)(stg + row * 32 + cp * kPer);
       }
     }
 
@@ -304,15 +362,10 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
       for (int i = 0; i < 16; ++i) S[r][i] *= glast;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 k8 = *(const bf16x8*)&sm.kt[32 * r + c][16 * s + 8 * hg];
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)k8[e] * sm.dec[16 * s + 8 * hg + e];
-        bf16x8 kh, kl;
-        split8(x, kh, kl);
-        S[r] = mfma32(kh, uh[s], S[r]);
-        S[r] = mfma32(kh, ul[s], S[r]);
-        S[r] = mfma32(kl, uh[s], S[r]);
+        const bf16x8 a_hi = sm.kth[r][s][lane], a_lo = sm.ktl[r][s][lane];
+        S[r] = mfma32(a_hi, uh[s], S[r]);
+        S[r] = mfma32(a_hi, ul[s], S[r]);
+        S[r] = mfma32(a_lo, uh[s], S[r]);
       }
     }
   }
