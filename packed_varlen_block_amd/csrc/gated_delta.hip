@@ -268,59 +268,72 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
       split8(x, sm.ph[fi][fl], sm.pl[fi][fl]);
     }
 
-    // ---- (I + A) U = rhs in the C layout: lanes c and c + 32 hold column
-    // n0, each in groups of four rows (rows 8m + 4hg .. + 3 of each 32-row
-    // block).  Step j: the lane holding row j (final by then) hands u_j to its
+    // ---- (I + A) U = rhs, blocked by 32 rows: U_top = solve(A11, R_top);
+    // R_bot -= A21 U_top on the matrix cores; U_bot = solve(A22, R_bot).
+    // Each triangle is solved in the C layout: lanes c and c + 32 hold
+    // column n0 of the block, each in groups of four rows (rows 8m + 4hg ..
+    // + 3).  Step j: the lane holding row j (final by then) hands u_j to its
     // partner, and every row group that may lie below row j subtracts its
-    // A[row][j] multiple.  A is zero on and above the diagonal, so the rows
-    // of row j's own group that are not below it are left as they are.  The
-    // A values of step j + 1 are read while step j computes.
-    float4 acur[2][4], anext[2][4];
-    auto load_a = [&](int j, float4 (&buf)[2][4]) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+    // A[row][j] multiple.  A is zero on and above the diagonal, so the rows of
+    // row j's own group that are not below it are left as they are.  The A
+    // values of step j + 1 are read while step j computes.
+    auto triangle = [&](auto rb_tag) {
+      constexpr int RB = decltype(rb_tag)::value;
+      float4 acur[4], anext[4];
+      auto load_a = [&](int jj, float4 (&buf)[4]) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          if (32 * rb + 8 * m + 7 > j) buf[rb][m] = *(const float4*)&sm.at[j][32 * rb + 8 * m + 4 * hg];
-    };
-    load_a(0, acur);
-    // fully unrolled: every register index below must be a constant
+          if (8 * m + 7 > jj) buf[m] = *(const float4*)&sm.at[32 * RB + jj][32 * RB + 8 * m + 4 * hg];
+      };
+      load_a(0, acur);
+      // fully unrolled: every register index below must be a constant
 #pragma clang loop unroll(full)
-    for (int j = 0; j < kGdC - 1; ++j) {
-      if (j + 1 < kGdC - 1) load_a(j + 1, anext);
-      const int rbj = j >> 5, jj = j & 31;
-      const int ij = 4 * (jj >> 3) + (jj & 3);        // element index of row j
-      const bool own = ((jj >> 2) & 1) == hg;
-      const float x = ks[rbj][ij];
-      const float other = swap_halves(x);
-      const float uj = own ? x : other;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int jj = 0; jj < 31; ++jj) {
+        if (jj + 1 < 31) load_a(jj + 1, anext);
+        const int ij = 4 * (jj >> 3) + (jj & 3);      // element index of row jj
+        const bool own = ((jj >> 2) & 1) == hg;
+        const float x = ks[RB][ij];
+        const float other = swap_halves(x);
+        const float uj = own ? x : other;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          if (32 * rb + 8 * m + 7 <= j) continue;      // the whole group is at or above row j
-          const float4 a4 = acur[rb][m];
-          ks[rb][4 * m] -= a4.x * uj;
-          ks[rb][4 * m + 1] -= a4.y * uj;
-          ks[rb][4 * m + 2] -= a4.z * uj;
-          ks[rb][4 * m + 3] -= a4.w * uj;
+          if (8 * m + 7 <= jj) continue;              // the whole group is at or above row jj
+          const float4 a4 = acur[m];
+          ks[RB][4 * m] -= a4.x * uj;
+          ks[RB][4 * m + 1] -= a4.y * uj;
+          ks[RB][4 * m + 2] -= a4.z * uj;
+          ks[RB][4 * m + 3] -= a4.w * uj;
         }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acur[rb][m] = anext[rb][m];
-    }
-
-    // ---- U as the B operand straight from its C layout (k-step s: elements
+        for (int m = 0; m < 4; ++m) acur[m] = anext[m];
+      }
+    };
+    // U as the B operand straight from its C layout (k-step s: elements
     // 8(s%2) + e of row block s/2, positions kpos(s, e, hg)), split
     bf16x8 uh[4], ul[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    auto split_u = [&](int s) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = ks[s >> 1][8 * (s & 1) + e];
       split8(x, uh[s], ul[s]);
+    };
+    triangle(std::integral_constant<int, 0>{});
+    split_u(0);
+    split_u(1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float x[8];                                     // -A21 at row 32 + c, positions kpos(s, e, hg)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = -sm.at[kpos(s, e, hg)][32 + c];
+      bf16x8 ah, al;
+      split8(x, ah, al);
+      ks[1] = mfma32(ah, uh[s], ks[1]);
+      ks[1] = mfma32(ah, ul[s], ks[1]);
+      ks[1] = mfma32(al, uh[s], ks[1]);
     }
+    triangle(std::integral_constant<int, 1>{});
+    split_u(2);
+    split_u(3);
     __syncthreads();                                  // the P and key fragments are complete
 
     // ---- O = scale (diag(G) Q S0 + P U); row block 0 has no key past 31.
