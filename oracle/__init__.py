@@ -14,7 +14,8 @@ loops, one segment and one head at a time, written from the pages
   example, the block-causal permission rule and the constructed loss probe.
 
 Modules
-  packing     -- O1 metadata, O2 next-fit, O3 best-fit-decreasing, O4 pair forming
+  packing     -- O1 metadata, O2 next-fit, O3 best-fit-decreasing, O4 pair forming,
+                 O9 boundaries compiled back from position ids
   attention   -- O5 forward, O6 backward, O7 brute-force dense masked attention
   loss_probe  -- O8 the constructed loss probe, O10 the packed-row loss
   linear_attention -- O11 the gated delta rule with its state reset at every boundary
