@@ -256,3 +256,29 @@ def test_cross_workspace_sizes():
     assert W(4096, 4096, 16, 128, 16, True) > pvb.workspace_bytes(4096, 16, 128, 16, True)
     assert W(4096, 64000, 16, 128, 16, True) >= 16 * 4096 * 8 + 64000 // 128 * 8
     assert W(10, 10, 2, 96, 1, False) == 0 and W(10, -1, 2, 64, 1, True) == 0
+
+
+def test_gated_delta_host_side_errors():
+    L = pvb.lib()
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=2, d=128,
+              scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, status=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.pvb_gated_delta_fwd(*a.values(), None)
+    assert call(d=64) == 6                            # only d = 128 is built
+    assert call(H=0) == 1
+    assert call(T=-1) == 1
+    assert call(n_seg=-1) == 1
+    assert call(cu=None) == 1
+    assert call(status=None) == 1
+    for name in ("q", "k", "v", "g", "b", "o"):
+        assert call(**{name: None}) == 1, name
+    assert call(o_dtype=3) == 1
+    assert call(scale=0.0) == 1
+    assert call(scale=float("inf")) == 1
+    assert call(T=2**24, H=2**7) == 6                 # T H d reaches 2^31
+    bad = np.array([0, 9], np.int32)                  # h_cu[B] != T
+    assert call(h_cu=bad.ctypes.data) == 4
+    dec = np.array([0, 6, 5, 8], np.int32)
+    assert call(h_cu=dec.ctypes.data, n_seg=3) == 4
