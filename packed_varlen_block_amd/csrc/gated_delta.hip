@@ -336,12 +336,12 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
     split_u(3);
     __syncthreads();                                  // the P and key fragments are complete
 
-    // ---- O = scale (diag(G) Q S0 + P U); row block 0 has no key past 31.
-    // The wave's 64 x 32 block is staged in the Q/K tiles (free by now) and
+    // ---- O = scale (diag(G) Q S0 + P U) (row block 0 has no key past 31)
+    // and S = G_63 S0 + (diag(G_63 / G) K)^T U: the matrix-core work of both
+    // is issued first, then O is staged in the Q/K tiles (free by now) and
     // written with 16-byte stores.
-    OutT* stg = reinterpret_cast<OutT*>(&sm.q[0][0]) + w * (kGdC * 32);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (rb == 0 && s >= 2) continue;
@@ -351,23 +351,6 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
         oacc[rb] = mfma32(a_hi, ul[s], oacc[rb]);
         oacc[rb] = mfma32(a_lo, uh[s], oacc[rb]);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) stg[(32 * rb + crow(i, hg)) * 32 + c] = out_cast<OutT>(scale * oacc[rb][i]);
-    }
-    {
-      constexpr int kPer = 16 / sizeof(OutT);         // elements per 16-byte piece
-      constexpr int kRowPieces = 32 / kPer;           // pieces per 32-column row
-#pragma unroll
-      for (int it = 0; it < kGdC * kRowPieces / 64; ++it) {
-        const int piece = lane + 64 * it;
-        const int row = piece / kRowPieces, cp = piece % kRowPieces;
-        if (row < nv)
-          *(uint4*)(o + ((size_t)(seg0 + c0 + row) * H + h) * kGdD + 32 * w + cp * kPer) =
-              *(const uint4*)(stg + row * 32 + cp * kPer);
-      }
-    }
-
-    // ---- S = G_63 S0 + (diag(G_63 / G) K)^T U
     const float glast = sm.eg[kGdC - 1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -379,6 +362,23 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
         S[r] = mfma32(a_hi, uh[s], S[r]);
         S[r] = mfma32(a_hi, ul[s], S[r]);
         S[r] = mfma32(a_lo, uh[s], S[r]);
+      }
+    }
+    OutT* stg = reinterpret_cast<OutT*>(&sm.q[0][0]) + w * (kGdC * 32);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) stg[(32 * rb + crow(i, hg)) * 32 + c] = out_cast<OutT>(scale * oacc[rb][i]);
+    {
+      constexpr int kPer = 16 / sizeof(OutT);         // elements per 16-byte piece
+      constexpr int kRowPieces = 32 / kPer;           // pieces per 32-column row
+#pragma unroll
+      for (int it = 0; it < kGdC * kRowPieces / 64; ++it) {
+        const int piece = lane + 64 * it;
+        const int row = piece / kRowPieces, cp = piece % kRowPieces;
+        if (row < nv)
+          *(uint4*)(o + ((size_t)(seg0 + c0 + row) * H + h) * kGdD + 32 * w + cp * kPer) =
+              *(const uint4*)(stg + row * 32 + cp * kPer);
       }
     }
   }
