@@ -115,8 +115,8 @@ def test_self_window_equals_cross_with_same_boundaries():
         assert (a == b).all()
 
 
-def test_cross_no_keys_at_all():
-    """T_k = 0: every row is empty (O = 0, LSE = -inf, dQ = 0)."""
+def test_cross_no_keys_or_no_queries():
+    """T_k = 0: every row is empty (O = 0, LSE = -inf, dQ = 0); T_q = 0: dK = dV = 0."""
     import packed_varlen_block_amd as pvb
     import torch
     say("cross T_k = 0")
@@ -130,6 +130,17 @@ def test_cross_no_keys_at_all():
     dq, dk, dv, st = pvb.varlen_cross_attn_bwd(q, k, k, o, do, lse, _dev_cu(hq), _dev_cu(hk), hq, hk)
     pvb.check_status(st)
     assert (dq == 0).all() and dk.numel() == 0
+    # T_q = 0: no queries at all; the key-side kernel writes zero gradients
+    say("cross T_q = 0")
+    q0 = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    k2 = torch.randn((20, 2, 64), device="cuda").bfloat16()
+    hq, hk = np.array([0, 0, 0], np.int32), np.array([0, 12, 20], np.int32)
+    o, lse, st = pvb.varlen_cross_attn_fwd(q0, k2, k2, _dev_cu(hq), _dev_cu(hk), hq, hk)
+    pvb.check_status(st)
+    assert o.numel() == 0 and lse.numel() == 0
+    dq, dk, dv, st = pvb.varlen_cross_attn_bwd(q0, k2, k2, o, q0, lse, _dev_cu(hq), _dev_cu(hk), hq, hk)
+    pvb.check_status(st)
+    assert dq.numel() == 0 and (dk == 0).all() and (dv == 0).all()
 
 
 def test_cross_planner_path():
