@@ -26,8 +26,11 @@ starts from S0[b] whatever the previous slice ended with.  Zero-length slices
 return their initial state.  Any l2 normalisation of q and k is the caller's
 (the pages do not say); the scale is an argument.
 
-Arrays: q, k [T, H, d_k]; v [T, H, d_v]; g, beta [T, H]; S0 and the final
-states [B, H, d_k, d_v].  A token loop per slice and head, nothing else.
+Arrays: q, k [T, H_k, d_k]; v [T, H, d_v]; g, beta [T, H]; S0 and the final
+states [B, H, d_k, d_v].  H is a multiple of H_k: value head h reads query/key
+head h // (H / H_k) (consecutive value heads share one, a reading: the pages
+give no head layout for these layers).  A token loop per slice and head,
+nothing else.
 """
 from __future__ import annotations
 
@@ -60,8 +63,11 @@ def gated_delta_varlen(q, k, v, g, beta, cu, scale, initial_state=None):
     """The packed stream: every slice [cu[b], cu[b+1]) and head runs the
     recurrence from its own initial state.  Returns (O [T, H, d_v],
     final states [B, H, d_k, d_v])."""
-    T, H, dk = q.shape
-    dv = v.shape[2]
+    T, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    if k.shape != q.shape or H % Hk != 0:
+        raise ValueError("q and k share a shape [T, H_k, d_k], and H is a multiple of H_k")
+    G = H // Hk
     cu = _check_cu(cu, T)
     B = len(cu) - 1
     o = np.zeros((T, H, dv))
@@ -70,7 +76,8 @@ def gated_delta_varlen(q, k, v, g, beta, cu, scale, initial_state=None):
         a, e = cu[b], cu[b + 1]
         for h in range(H):
             s0 = None if initial_state is None else initial_state[b, h]
-            ob, sb = gated_delta_segment(q[a:e, h], k[a:e, h], v[a:e, h], g[a:e, h], beta[a:e, h], scale, s0)
+            ob, sb = gated_delta_segment(q[a:e, h // G], k[a:e, h // G], v[a:e, h], g[a:e, h], beta[a:e, h],
+                                         scale, s0)
             o[a:e, h] = ob
             fin[b, h] = sb
     return o, fin

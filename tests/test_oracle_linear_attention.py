@@ -232,3 +232,18 @@ def test_planted_missing_reset_fails_isolation(monkeypatch):
     monkeypatch.setattr(LA, "gated_delta_segment", leaky)
     with pytest.raises(AssertionError):
         test_slices_are_isolated_and_reset()
+
+
+def test_grouped_heads_equal_repeated_heads():
+    """H value heads over H_k query/key heads: the same as repeating each
+    query/key head for its group (consecutive value heads share one)."""
+    lengths = [9, 0, 14]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, Hk, G, dk, dv = int(cu[-1]), 2, 3, 5, 4
+    q, k, _, _, _ = _rand(12, T, Hk, dk, dv)
+    _, _, v, g, beta = _rand(13, T, Hk * G, dk, dv)
+    o, fin = LA.gated_delta_varlen(q, k, v, g, beta, cu, 0.4)
+    o2, fin2 = LA.gated_delta_varlen(np.repeat(q, G, axis=1), np.repeat(k, G, axis=1), v, g, beta, cu, 0.4)
+    assert np.array_equal(o, o2) and np.array_equal(fin, fin2)
+    with pytest.raises(ValueError):
+        LA.gated_delta_varlen(q, k, v[:, :5], g[:, :5], beta[:, :5], cu, 0.4)
