@@ -351,6 +351,17 @@ pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v
                                int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
                                const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
                                int32_t* d_status, void* stream);
+/* The same with grouped query/key heads: q and k are [T, H_k, d], v, g, beta,
+ * O and the states carry H value heads, H a multiple of H_k, and value head h
+ * reads query/key head h / (H / H_k) (the published Gated DeltaNet layers use
+ * fewer query/key heads than value heads; the pages give no layout).  H_k = H
+ * is exactly pvb_gated_delta_fwd.  Extra error: PVB_E_INVALID_ARG when
+ * H_k <= 0 or H is not a multiple of H_k. */
+pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                   const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                                   int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d,
+                                   float scale, const float* d_h0, void* d_o, int32_t o_dtype,
+                                   float* d_ht, int32_t* d_status, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);

@@ -34,7 +34,7 @@ STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "P
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
            "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
            "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
-           "pvb_gated_delta_fwd",
+           "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_status_string", "pvb_version")
 
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.pvb_varlen_attn_bwd_gqa.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
                                               P, P, P, I32, I32, P, SZ, P, P]
         L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, P]
+        L.pvb_gated_delta_fwd_gqa.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, I32, P, P, P]
         L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
         L.pvb_varlen_cross_attn_workspace_bytes.restype = SZ
         L.pvb_varlen_cross_attn_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F,
@@ -81,7 +82,8 @@ def lib() -> ctypes.CDLL:
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
                      "pvb_boundaries_from_positions", "pvb_packed_nll", "pvb_varlen_attn_fwd",
                      "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
-                     "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd", "pvb_gated_delta_fwd"):
+                     "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd", "pvb_gated_delta_fwd",
+                     "pvb_gated_delta_fwd_gqa"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
         L.pvb_status_string.restype = ctypes.c_char_p
@@ -500,16 +502,20 @@ def varlen_cross_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, h_cu_q, h_cu_k, windo
 def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=None, final_state=True,
                     o_dtype=None, out=None, state_out=None, status=None):
     """Gated delta rule over the packed stream, the state reset at every
-    boundary of ``cu``.  q, k, v: contiguous bf16 CUDA [T, H, 128]; g, beta:
-    fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].  Returns
-    (O [T, H, 128], final states [B, H, 128, 128] fp32 or None, status)."""
+    boundary of ``cu``.  q, k: contiguous bf16 CUDA [T, H_k, 128]; v: [T, H, 128]
+    with H a multiple of H_k (value head h reads query/key head h // (H / H_k));
+    g, beta: fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].
+    Returns (O [T, H, 128], final states [B, H, 128, 128] fp32 or None, status)."""
     torch = _torch()
-    if q.dim() != 3:
-        raise PvbError(1, "q must be [T, H, d]")
-    T, H, d = q.shape
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (T, H, d) or not t.is_cuda:
-            raise PvbError(1, "q, k, v must be contiguous bf16 CUDA tensors of one shape [T, H, d]")
+    if q.dim() != 3 or v.dim() != 3:
+        raise PvbError(1, "q, k, v must be [T, heads, d]")
+    T, Hk, d = q.shape
+    H = v.shape[1]
+    for t, shape in ((q, (T, Hk, d)), (k, (T, Hk, d)), (v, (T, H, d))):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda:
+            raise PvbError(1, "q, k [T, H_k, d] and v [T, H, d] must be contiguous bf16 CUDA tensors")
+    if H % Hk != 0:
+        raise PvbError(1, "the value heads must be a multiple of the query/key heads")
     for t in (g, beta):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (T, H) or not t.is_cuda:
             raise PvbError(1, "g and beta must be contiguous fp32 CUDA tensors [T, H]")
@@ -535,9 +541,9 @@ def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=N
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
         if hc.size != n_seg + 1:
             raise PvbError(1, "h_cu must have B+1 entries")
-    rc = lib().pvb_gated_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg, T,
-                                   H, d, scale, _ptr(initial_state), _ptr(out), _dtype_code(out.dtype),
-                                   _ptr(ht) if ht is not None and ht.numel() > 0 else None, _ptr(status),
-                                   _stream(dev))
+    rc = lib().pvb_gated_delta_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg,
+                                       T, H, Hk, d, scale, _ptr(initial_state), _ptr(out), _dtype_code(out.dtype),
+                                       _ptr(ht) if ht is not None and ht.numel() > 0 else None, _ptr(status),
+                                       _stream(dev))
     _check(rc, "gated_delta_fwd")
     return out, ht, status

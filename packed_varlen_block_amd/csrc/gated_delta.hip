@@ -74,7 +74,7 @@ template <typename OutT>
 __global__ void __launch_bounds__(kGdThreads, 1)
 gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const float* __restrict__ g, const float* __restrict__ beta,
-                   const int32_t* __restrict__ cu, int n_seg, int T, int H, float scale,
+                   const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
                    const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
                    int32_t* __restrict__ status) {
   __shared__ GdSmem sm;
@@ -93,6 +93,7 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   if (s_bad || (int)blockIdx.x >= n_seg * H) return;
 
   const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int hk = h / (H / Hk);                        // the query/key head of value head h
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
   const int n0 = 32 * w + c;                          // this lane's value column
   const size_t st_base = (size_t)(b * H + h) * kGdD * kGdD;
@@ -118,10 +119,11 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
       const int row = ch >> 4, col = (ch & 15) * 8;
       pq[it] = pk[it] = pv[it] = zero4();
       if (row < nvv) {
-        const size_t off = ((size_t)(seg0 + cc0 + row) * H + h) * kGdD + col;
-        pq[it] = *(const uint4*)(q + off);
-        pk[it] = *(const uint4*)(k + off);
-        pv[it] = *(const uint4*)(v + off);
+        const size_t off_qk = ((size_t)(seg0 + cc0 + row) * Hk + hk) * kGdD + col;
+        const size_t off_v = ((size_t)(seg0 + cc0 + row) * H + h) * kGdD + col;
+        pq[it] = *(const uint4*)(q + off_qk);
+        pk[it] = *(const uint4*)(k + off_qk);
+        pv[it] = *(const uint4*)(v + off_v);
       }
     }
     pg = pb = 0.f;
@@ -394,13 +396,14 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 }  // namespace
 }  // namespace pvb
 
-extern "C" pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
-                                          const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
-                                          int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
-                                          const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
-                                          int32_t* d_status, void* stream) {
-  using namespace pvb;
+namespace pvb {
+namespace {
+pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                            const float* d_beta, const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                            int32_t T, int32_t H, int32_t H_k, int32_t d, float scale, const float* d_h0,
+                            void* d_o, int32_t o_dtype, float* d_ht, int32_t* d_status, void* stream) {
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
+  if (H_k <= 0 || H % H_k != 0) return PVB_E_INVALID_ARG;
   if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_g == nullptr || d_beta == nullptr ||
                 d_o == nullptr))
     return PVB_E_INVALID_ARG;
@@ -417,11 +420,32 @@ extern "C" pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, cons
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
   if (o_dtype == PVB_F32)
     gated_delta_kernel<float><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, scale, d_h0,
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
         (float*)d_o, d_ht, d_status);
   else
     gated_delta_kernel<bf16><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, scale, d_h0,
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
         (bf16*)d_o, d_ht, d_status);
   return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+}  // namespace
+}  // namespace pvb
+
+extern "C" pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                          const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                                          int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
+                                          const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
+                                          int32_t* d_status, void* stream) {
+  return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H, d, scale, d_h0, d_o,
+                               o_dtype, d_ht, d_status, stream);
+}
+
+extern "C" pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                              const float* d_g, const float* d_beta, const int32_t* d_cu,
+                                              const int32_t* h_cu, int32_t n_seg, int32_t T, int32_t H,
+                                              int32_t H_k, int32_t d, float scale, const float* d_h0,
+                                              void* d_o, int32_t o_dtype, float* d_ht, int32_t* d_status,
+                                              void* stream) {
+  return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_o,
+                               o_dtype, d_ht, d_status, stream);
 }

@@ -282,3 +282,14 @@ def test_gated_delta_host_side_errors():
     assert call(h_cu=bad.ctypes.data) == 4
     dec = np.array([0, 6, 5, 8], np.int32)
     assert call(h_cu=dec.ctypes.data, n_seg=3) == 4
+
+
+def test_gated_delta_grouped_heads_host_side_errors():
+    L = pvb.lib()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=6, H_k=4, d=128,
+                scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, status=FAKE)
+    assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 1          # 6 value heads over 4
+    args.update(H_k=0)
+    assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 1
+    args.update(H_k=3, d=64)
+    assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 6

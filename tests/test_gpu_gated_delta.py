@@ -43,7 +43,7 @@ def _check(name, got, ref, tol):
 def _run(w, o_dtype="f32", heads=None, scale=None, check=True):
     import packed_varlen_block_amd as pvb
     import torch
-    T, H, d = w["q"].shape
+    T, H, d = w["v"].shape
     hc = host_cu(w["lengths"])
     cu = _dev(hc)
     h0 = _dev(w["h0"]) if "h0" in w else None
@@ -55,7 +55,14 @@ def _run(w, o_dtype="f32", heads=None, scale=None, check=True):
         return o, ht
     hs = list(range(H)) if heads is None else list(heads)
     sc = 1.0 / np.sqrt(d) if scale is None else scale
-    q, k, v = (W.bf16_bits_to_f64(w[x])[:, hs] for x in ("q", "k", "v"))
+    G = H // w["q"].shape[1]
+    hq = sorted({h // G for h in hs})               # the query/key heads the sampled heads read
+    q, k = (W.bf16_bits_to_f64(w[x])[:, hq] for x in ("q", "k"))
+    if G > 1:                                       # one query/key head per sampled value head
+        q, k = (np.ascontiguousarray(x[:, [hq.index(h // G) for h in hs]]) for x in (q, k))
+    else:
+        q, k = (W.bf16_bits_to_f64(w[x])[:, hs] for x in ("q", "k"))
+    v = W.bf16_bits_to_f64(w["v"])[:, hs]
     g, b = w["g"].astype(np.float64)[:, hs], w["beta"].astype(np.float64)[:, hs]
     s0 = w["h0"].astype(np.float64)[:, hs] if "h0" in w else None
     ro, rs = LA.gated_delta_varlen(q, k, v, g, b, hc, sc, s0)
@@ -106,6 +113,21 @@ def test_long_mixed_pack_sampled_heads():
     say(f"gated delta T={int(lengths.sum())} segments={len(lengths)} H=32 (heads 0 and 21)")
     w = W.random_gated_delta(950, lengths, H=32, g_range=(-0.1, 0.0))
     _run(w, "bf16", heads=[0, 21])
+
+
+@pytest.mark.parametrize("H,Hk", [(4, 2), (6, 1), (8, 8)])
+def test_grouped_query_key_heads(H, Hk):
+    say(f"gated delta grouped heads H={H} H_k={Hk}")
+    w = W.random_gated_delta(990, [130, 0, 64, 257], H=H, Hk=Hk, initial_state=True)
+    _run(w, "f32")
+
+
+def test_grouped_heads_long_mixed_pack():
+    """The long mixed pack with 32 value heads over 16 query/key heads."""
+    lengths = W.lengths_cfg4(0)
+    say("gated delta long mixed pack H=32 H_k=16 (heads 1 and 30)")
+    w = W.random_gated_delta(995, lengths, H=32, Hk=16, g_range=(-0.1, 0.0))
+    _run(w, "bf16", heads=[1, 30])
 
 
 def test_scale_argument_and_isolation():

@@ -242,17 +242,19 @@ def random_cross(seed: int, lengths_q, lengths_k, H: int, Hk: int, d: int, scale
 
 
 def random_gated_delta(seed: int, lengths, H: int, d: int = 128, g_range=(-0.1, 0.0),
-                       beta_range=(0.05, 1.0), initial_state: bool = False, cfg_tag: int = 97):
+                       beta_range=(0.05, 1.0), initial_state: bool = False, cfg_tag: int = 97,
+                       Hk: int | None = None):
     """Inputs of the gated delta rule over a packed stream: q, k bf16 bits of
-    unit-norm rows (normalised in float32, then rounded), v bf16 bits of
-    N(0,1), log gates g ~ U(g_range) and write strengths beta ~ U(beta_range)
-    as float32 [T, H], and optionally float32 initial states N(0,1)*0.1
-    [B, H, d, d].  Returned as a dict."""
+    unit-norm rows (normalised in float32, then rounded) with Hk heads (H when
+    None), v bf16 bits of N(0,1) with H heads, log gates g ~ U(g_range) and
+    write strengths beta ~ U(beta_range) as float32 [T, H], and optionally
+    float32 initial states N(0,1)*0.1 [B, H, d, d].  Returned as a dict."""
     lengths = np.asarray(lengths, dtype=np.int32)
     T = int(lengths.sum())
+    Hk = H if Hk is None else Hk
     r = _rng(seed, cfg_tag, STREAM_Q)
-    qf = r.standard_normal((T, H, d), dtype=np.float32)
-    kf = _rng(seed, cfg_tag, STREAM_K).standard_normal((T, H, d), dtype=np.float32)
+    qf = r.standard_normal((T, Hk, d), dtype=np.float32)
+    kf = _rng(seed, cfg_tag, STREAM_K).standard_normal((T, Hk, d), dtype=np.float32)
     qf /= np.maximum(np.linalg.norm(qf, axis=-1, keepdims=True), np.float32(1e-6))
     kf /= np.maximum(np.linalg.norm(kf, axis=-1, keepdims=True), np.float32(1e-6))
     out = {"lengths": lengths, "q": f32_to_bf16_bits(qf), "k": f32_to_bf16_bits(kf),
