@@ -262,6 +262,7 @@ def main():
         out["cross_and_window"] = cross_and_window(torch, pvb, dev, stream, a.seed)
     if not a.no_gdn_case:
         out["gated_delta"] = gated_delta(torch, pvb, W, dev, stream, a.seed)
+        out["gated_delta_grouped"] = gated_delta(torch, pvb, W, dev, stream, a.seed, Hk=16)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -493,11 +494,12 @@ def cross_and_window(torch, pvb, dev, stream, seed, H=32, d=128, reps=5):
     return res
 
 
-def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
+def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5, Hk=None):
     """Gated delta rule over the long mixed pack (T=32768: one 16384-token
     slice, then slices of 16-1024), H=32, d=128, bf16 O and fp32 final states,
     the state reset at every boundary; g ~ U(-0.1, 0), beta ~ U(0.05, 1), unit
-    q and k.  Each (slice, head) is a chain of 64-token chunks, so the time is
+    q and k (Hk query/key heads: H when None, else value heads share them in
+    groups).  Each (slice, head) is a chain of 64-token chunks, so the time is
     set by the longest slice: reported per chunk of that chain, beside the
     HBM rate of the algorithmic bytes (q, k, v, g, beta read once, O and the
     final states written once).  Median of reps."""
@@ -508,7 +510,8 @@ def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
     def unit(*shape):
         x = torch.randn(shape, generator=g, device=dev)
         return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
-    q, k = unit(T, H, d), unit(T, H, d)
+    Hk = H if Hk is None else Hk
+    q, k = unit(T, Hk, d), unit(T, Hk, d)
     v = torch.randn((T, H, d), generator=g, device=dev).to(torch.bfloat16)
     gg = torch.rand((T, H), generator=g, device=dev) * -0.1
     bb = torch.rand((T, H), generator=g, device=dev) * 0.95 + 0.05
@@ -530,9 +533,10 @@ def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
     torch.cuda.synchronize()
     pvb.check_status(st)
     ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
-    byts = 4 * T * H * d * 2 + 2 * T * H * 4 + B * H * d * d * 4
+    byts = (2 * Hk + 2 * H) * T * d * 2 + 2 * T * H * 4 + B * H * d * d * 4
     chain = int(-(-int(lengths.max()) // 64))
-    return {"workload": "gdn_long_mixed_T32768_H32_d128", "segments": B, "ms": round(ms, 4),
+    name = "gdn_long_mixed_T32768_H32_d128" if Hk == H else f"gdn_long_mixed_T32768_H32_Hk{Hk}_d128"
+    return {"workload": name, "segments": B, "ms": round(ms, 4),
             "longest_chain_chunks": chain, "us_per_chunk": round(ms * 1e3 / chain, 3),
             "algorithmic_bytes": byts, "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
