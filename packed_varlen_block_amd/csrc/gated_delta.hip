@@ -17,12 +17,14 @@
 //   O = scale (diag(G) Q S0 + P U),               P_ij = (G_i/G_j) q_i.k_j       (j <= i),
 //   S_end = G_63 S0 + (diag(G_63/G) K)^T U.
 // The chunk products run on the matrix cores; every fp32 operand (the state,
-// P, U, the gated keys) is split into bf16 hi + lo parts, so the products keep
-// about 16 significant bits; the triangular solve is fp32 on the vector unit.
+// P, U, the gated keys, A's off-diagonal block) is split into bf16 hi + lo
+// parts, so the products keep about 16 significant bits; the two 32-row
+// triangles of the solve are fp32 on the vector unit.
 //
-// One workgroup of 4 waves per (slice, head); the slices are independent.
-// Wave w owns value columns [32w, 32w + 32) of the state, which stays in its
-// registers (C layout of four 32x32 blocks) across the chunks of the slice.
+// One workgroup of 4 waves per (slice, value head); the slices are
+// independent.  Value head h reads query/key head h / (H / H_k).  Wave w owns
+// value columns [32w, 32w + 32) of the state, which stays in its registers (C
+// layout of four 32x32 blocks) across the chunks of the slice.
 #include <type_traits>
 
 #include "pvb_device.hpp"
