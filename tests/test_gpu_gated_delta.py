@@ -99,6 +99,14 @@ def test_gate_ranges(g_range, beta_range):
     _run(w, "f32")
 
 
+def test_many_short_slices():
+    """600 slices of 0-20 tokens (the cu_seqlens check strides over them)."""
+    lengths = np.random.default_rng(985).integers(0, 21, size=600)
+    say(f"gated delta {len(lengths)} slices, T={int(lengths.sum())}")
+    w = W.random_gated_delta(986, lengths, H=2, initial_state=True)
+    _run(w, "f32")
+
+
 def test_long_slices():
     for i, lengths in enumerate(([1030], [2100, 5], [700, 0, 1500])):
         say(f"gated delta long lengths={lengths}")
