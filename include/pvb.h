@@ -19,6 +19,12 @@
  *   - Every buffer is allocated and owned by the caller.  The library keeps no
  *     allocations and no mutable global state; calls are reentrant.  Pointers
  *     named d_* are device pointers, h_* host pointers.
+ *   - A device entry point only launches kernels on `stream` (no allocation,
+ *     memset, copy or synchronisation), so it can be recorded into a HIP graph.
+ *     Called without the optional host mirror of cu_seqlens, it plans its work
+ *     on the device from the device cu_seqlens, so a recorded call stays valid
+ *     when the boundaries (and the data) change in place between replays, as
+ *     long as T, B and the other scalar arguments do not.
  *   - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous [T, H, d] (token-major,
  *     then head, then feature): element (t, h, c) at offset (t*H + h)*d + c.
  *     LSE and the backward's D are fp32 [H, T].
