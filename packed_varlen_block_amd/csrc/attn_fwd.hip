@@ -19,7 +19,8 @@
 //     tile through the LDS transpose read and P never leaves registers.
 // Key tiles wholly above the diagonal are never visited; masking is applied
 // only on tiles that cross the diagonal or the segment end.  The running max
-// is raised lazily (see kSlack), so most tiles skip the rescale of O.
+// is raised lazily (see kSlack), so most tiles skip the rescale of O.  A bf16 O
+// is staged through LDS and stored as whole rows.
 #include "pvb_device.hpp"
 
 namespace pvb {
@@ -221,6 +222,39 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (n + 1 < n_end) wait_vmcnt<0>();   // this wave's copies of tile n+1
   }
 
+  if constexpr (sizeof(OutT) == 2) {
+    // bf16 O leaves through LDS: each wave stages its 32 rows (waves 0 and 1
+    // in the K buffers, 2 and 3 in the V buffers, which every wave is done
+    // with after the barrier) and then stores whole rows, 16 bytes per lane,
+    // marked non-temporal.  Whole-row stores stream out during the kernel;
+    // stored straight from the C layout (16-byte pieces of 32 rows per
+    // instruction) O would wait in L2 for the kernel's end.
+    lds_barrier();
+    bf16* stg = (w < 2 ? &sK[0][0] : &sV[0][0]) + (w & 1) * 32 * D;
+    if (!wave_active) return;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int j = 0; j < DBLK; ++j)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 r;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) r[t] = (bf16)(oacc[j][4 * i4 + t] * inv);
+        *(bf16x4*)(stg + swz<D>(lq, 32 * j + 8 * i4 + 4 * g)) = r;
+      }
+    constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per wave-wide store
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int rr = it * RPI + lane / CPR, c = lane % CPR;
+      const bf16x8 x = *(const bf16x8*)(stg + swz<D>(rr, 8 * c));
+      if (wq_first + rr < L)
+        __builtin_nontemporal_store(__builtin_bit_cast(f32x4, x),
+                                    (f32x4*)(o + base + (int64_t)(wq_first + rr) * rs + 8 * c));
+    }
+    if (g == 0 && qrow < L) lse[(int64_t)h * T + seg0 + qrow] = (m_run + log2f(l_run)) * kLn2;
+    return;
+  }
+  // fp32 O (its rows would not fit the 32-key kernel's LDS): straight from the C layout
   if (!wave_active || qrow >= L) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   OutT* op = o + base + (int64_t)qrow * rs;
@@ -229,15 +263,8 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int col = 32 * j + 8 * i4 + 4 * g;
-      if constexpr (sizeof(OutT) == 4) {
-        *(float4*)(op + col) = make_float4(oacc[j][4 * i4] * inv, oacc[j][4 * i4 + 1] * inv,
-                                           oacc[j][4 * i4 + 2] * inv, oacc[j][4 * i4 + 3] * inv);
-      } else {
-        bf16x4 r;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) r[t] = (bf16)(oacc[j][4 * i4 + t] * inv);
-        *(bf16x4*)(op + col) = r;
-      }
+      *(float4*)(op + col) = make_float4(oacc[j][4 * i4] * inv, oacc[j][4 * i4 + 1] * inv,
+                                         oacc[j][4 * i4 + 2] * inv, oacc[j][4 * i4 + 3] * inv);
     }
   if (g == 0) lse[(int64_t)h * T + seg0 + qrow] = (m_run + log2f(l_run)) * kLn2;
 }
