@@ -105,11 +105,15 @@ nll_row_kernel(const LT* __restrict__ logits, int V, const int32_t* __restrict__
   typedef __attribute__((__vector_size__(VEC * sizeof(LT)))) LT vec_t;
   vec_t held[HELD ? kHeld : 1];
   if constexpr (HELD) {
-    // every load in flight at once, then the pass over registers
+    // every load in flight at once, then the pass over registers.  Each logit
+    // and each gradient element is touched once: loads and stores are marked
+    // non-temporal.
+    typedef int ivec_t __attribute__((vector_size(sizeof(vec_t))));
 #pragma unroll
     for (int k = 0; k < kHeld; ++k) {
       const int i = tid + k * kRowThreads;
-      if (i < nv) held[k] = *(const vec_t*)(row + (int64_t)i * VEC);
+      if (i < nv)
+        held[k] = __builtin_bit_cast(vec_t, __builtin_nontemporal_load((const ivec_t*)(row + (int64_t)i * VEC)));
     }
     // the thread's max, then its sum of exp2(x log2e - max): no rescaling
     float mx = -INFINITY;
@@ -179,7 +183,8 @@ nll_row_kernel(const LT* __restrict__ logits, int V, const int32_t* __restrict__
         for (int e = 0; e < VEC; ++e) gv[e] = (GT)fast_exp2((float)held[k][e] * kLog2e - lse2n);
         if ((unsigned)(y - i * VEC) < (unsigned)VEC)      // this vector holds the target class
           gv[y - i * VEC] = (GT)(fast_exp2((float)held[k][y - i * VEC] * kLog2e - lse2n) - inv_n);
-        *(gvec_t*)(grow + (int64_t)i * VEC) = gv;
+        typedef int givec_t __attribute__((vector_size(sizeof(gvec_t))));
+        __builtin_nontemporal_store(__builtin_bit_cast(givec_t, gv), (givec_t*)(grow + (int64_t)i * VEC));
       }
     }
   } else {
