@@ -74,7 +74,20 @@ def errors(got: np.ndarray, ref: np.ndarray):
     return float(d.max(initial=0.0)), float(d.mean()) if d.size else 0.0
 
 
-def check(name: str, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+def bf16_half_ulp(ref: np.ndarray) -> float:
+    """Half a bf16 ulp at the largest magnitude of ``ref``: how far rounding to
+    the bf16 output format alone can move a value of that size (8 significant
+    bits, so the ulp on [2^e, 2^(e+1)) is 2^(e-7))."""
+    m = float(np.abs(ref).max(initial=0.0))
+    return 0.0 if m == 0.0 else float(2.0 ** (np.floor(np.log2(m)) - 8))
+
+
+def check(name: str, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, mean_abs=MEAN_ABS, bf16_out=False):
+    """Per-tensor max-abs / mean-abs comparison.  With ``bf16_out`` the output
+    tensor is stored in bf16 and the max-abs bar also admits that format's own
+    rounding of the largest values (half an ulp of max|ref|)."""
+    if bf16_out:
+        max_abs = max_abs + bf16_half_ulp(ref)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     mx, mn = errors(got, ref)

@@ -1,0 +1,90 @@
+"""Seeded random packs through the forward and backward entry points, every
+head against the fp64 oracle (O5, O6).
+
+Each case draws its own pack: up to eight segments whose lengths sit on and
+next to the 32-, 64- and 128-row tile edges, or anywhere in [1, 400), with
+zero-length segments mixed in; 1-3 key/value heads shared by 1, 2 or 4 query
+heads; d in {64, 128}; bf16 or fp32 O and gradients; one or two bf16 roundings
+of P and dS (always two when the logits are spread wider than the pages'
+workloads); the default softmax scale or another one; with or without the
+host mirror of cu_seqlens.  The bars are those of the other parity tests; a
+tensor stored in bf16 also gets that format's own rounding of its largest
+values (half an ulp of max|ref|), which for the summed dV of four query heads
+per key/value head (|dV| near 10) is above the absolute bar by itself."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from tests.parity import check, dev_bf16, host_cu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+EDGES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import packed_varlen_block_amd  # noqa: F401  (fails loudly if libpvb.so is missing)
+
+
+def _draw(case):
+    r = np.random.default_rng(3000 + case)
+    n = int(r.integers(1, 9))
+    lengths = []
+    for _ in range(n):
+        u = r.random()
+        lengths.append(0 if u < 0.12 else int(r.choice(EDGES)) if u < 0.55 else int(r.integers(1, 400)))
+    if sum(lengths) == 0:
+        lengths[-1] = int(r.choice(EDGES))
+    Hk = int(r.integers(1, 4))
+    G = int(r.choice([1, 2, 4]))
+    d = int(r.choice([64, 128]))
+    precision = "split" if r.random() < 0.25 else "bf16"
+    o_f32, g_bf16 = r.random() < 0.4, r.random() < 0.4
+    softmax_scale = [None, 0.05, 0.25][int(r.integers(0, 3))]
+    input_scale = [0.5, 1.0][int(r.integers(0, 2))]
+    # logit spread: q.k of N(0, s^2) rows has standard deviation sqrt(d) s^2.
+    # Above 1.5 one bf16 rounding of P and dS alone moves dQ and dK by a few
+    # 1e-2, so such draws run with the two-part rounding.
+    spread = (softmax_scale or d ** -0.5) * d ** 0.5 * input_scale ** 2
+    if spread > 1.5:
+        precision = "split"
+    return dict(lengths=lengths, d=d, H=Hk * G, Hk=Hk,
+                o_dtype="f32" if precision == "split" or o_f32 else "bf16",
+                grad_dtype="bf16" if g_bf16 else "f32", precision=precision,
+                softmax_scale=softmax_scale, use_h_cu=bool(r.random() < 0.5), input_scale=input_scale,
+                spread=round(spread, 2))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_pack(case):
+    import packed_varlen_block_amd as pvb
+    import torch
+    c = _draw(case)
+    L, d, H, Hk = c["lengths"], c["d"], c["H"], c["Hk"]
+    say(f"random pack {case}: {c}")
+    qb, kb, vb, db = W.random_cross(3100 + case, L, L, H, Hk, d, scale=c["input_scale"])
+    q, k, v, do = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(db)
+    hc = host_cu(L)
+    cu = torch.tensor(hc).cuda()
+    h_cu = hc if c["use_h_cu"] else None
+    od = torch.float32 if c["o_dtype"] == "f32" else torch.bfloat16
+    gd = torch.float32 if c["grad_dtype"] == "f32" else torch.bfloat16
+    o, lse, st = pvb.varlen_attn_fwd(q, k, v, cu, h_cu=h_cu, softmax_scale=c["softmax_scale"], o_dtype=od,
+                                     precision=c["precision"])
+    pvb.check_status(st)
+    dq, dk, dv, st = pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=h_cu, softmax_scale=c["softmax_scale"],
+                                         grad_dtype=gd, precision=c["precision"])
+    pvb.check_status(st)
+    qo, ko, vo, doo = (W.bf16_bits_to_f64(x) for x in (qb, kb, vb, db))
+    ro, rl = A.varlen_forward(qo, ko, vo, hc, scale=c["softmax_scale"])
+    ob, gb = c["o_dtype"] == "bf16", c["grad_dtype"] == "bf16"
+    check("O", to64(o), ro, bf16_out=ob)
+    check("LSE", lse.double().cpu().numpy(), rl, max_abs=1e-3, mean_abs=1e-4)
+    rq, rk, rv = A.varlen_backward(qo, ko, vo, doo, hc, scale=c["softmax_scale"])
+    check("dQ", to64(dq), rq, bf16_out=gb)
+    check("dK", to64(dk), rk, bf16_out=gb)
+    check("dV", to64(dv), rv, bf16_out=gb)
