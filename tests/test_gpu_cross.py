@@ -49,10 +49,10 @@ def _run(seed, lq, lk, H, Hk, d, window, grad_dtype="f32", precision="bf16", bac
                                                grad_dtype=gd, precision=precision)
     pvb.check_status(st)
     rq, rk, rv = A.varlen_cross_backward(qo, ko, vo, W.bf16_bits_to_f64(db), hq, hk, window=window)
-    check("dQ", to64(dq), rq)
-    for name, got, ref in (("dK", dk, rk), ("dV", dv, rv)):
-        extra = 2.0 ** -9 * float(np.abs(ref).max()) if grad_dtype == "bf16" else 0.0
-        check(name, to64(got), ref, max_abs=2e-2 + extra)
+    # bf16 gradients: the bar also admits the format's own rounding of the
+    # largest values (half an ulp of max|ref|)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(name, to64(got), ref, bf16_out=grad_dtype == "bf16")
 
 
 # (query lengths, key lengths): longer and shorter key extents than query
@@ -168,3 +168,31 @@ def test_cross_bad_device_cu_k_reported_by_the_key_list():
     pvb.varlen_cross_attn_bwd(q, k, v, o, do, lse, _dev_cu(hq), bad_k, hq, hk, status=st)
     torch.cuda.synchronize()
     assert st.item() == 4
+
+
+# seeded random draws: per-segment query and key lengths (on and next to the
+# tile edges, anywhere below 300, or zero on either side), a window from
+# unbounded to tight on both sides, grouped heads, both head sizes
+EDGES = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_cross_random(case):
+    r = np.random.default_rng(4000 + case)
+    n = int(r.integers(1, 7))
+
+    def length():
+        u = r.random()
+        return 0 if u < 0.12 else int(r.choice(EDGES)) if u < 0.5 else int(r.integers(1, 300))
+
+    lq = [length() for _ in range(n)]
+    lk = [length() for _ in range(n)]
+    window = (int(r.choice([-1, 0, 3, 16, 40, 100])), int(r.choice([-1, 0, 0, 5])))
+    Hk = int(r.integers(1, 4))
+    H = Hk * int(r.choice([1, 2, 4]))
+    d = int(r.choice([64, 128]))
+    grad_dtype = "bf16" if r.random() < 0.4 else "f32"
+    precision = "split" if r.random() < 0.25 else "bf16"
+    say(f"cross random {case}: lq={lq} lk={lk} window={window} H={H} H_kv={Hk} d={d} "
+        f"grad={grad_dtype} precision={precision}")
+    _run(4100 + case, lq, lk, H, Hk, d, window, grad_dtype, precision)
