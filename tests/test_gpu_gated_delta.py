@@ -185,3 +185,29 @@ def test_bad_device_cu_writes_nothing():
     torch.cuda.synchronize()
     assert st.item() == 4
     assert (o == 7.0).all() and (ht == 7.0).all()
+
+
+# seeded random draws: slice lengths on and next to the 64-token chunk edges,
+# anywhere below 300, or zero; grouped query/key heads; gate and write-strength
+# ranges; with or without initial states; fp32 or bf16 O; two scales
+CHUNK_EDGES = [1, 63, 64, 65, 127, 128, 129, 192]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_draws(case):
+    r = np.random.default_rng(5000 + case)
+    n = int(r.integers(1, 7))
+    lengths = [0 if (u := r.random()) < 0.12 else int(r.choice(CHUNK_EDGES)) if u < 0.5 else int(r.integers(1, 300))
+               for _ in range(n)]
+    Hk = int(r.integers(1, 4))
+    H = Hk * int(r.choice([1, 2, 4]))
+    g_range = [(0.0, 0.0), (-0.1, 0.0), (-1.0, 0.0), (-6.0, -2.0)][int(r.integers(0, 4))]
+    beta_range = [(0.05, 1.0), (0.9, 1.0), (0.0, 0.3)][int(r.integers(0, 3))]
+    init = bool(r.random() < 0.5)
+    o_dtype = "bf16" if r.random() < 0.4 else "f32"
+    scale = None if r.random() < 0.6 else 0.3
+    say(f"gated delta random {case}: lengths={lengths} H={H} H_k={Hk} g={g_range} beta={beta_range} "
+        f"init={init} o={o_dtype} scale={scale}")
+    w = W.random_gated_delta(5100 + case, lengths, H=H, Hk=Hk, g_range=g_range, beta_range=beta_range,
+                             initial_state=init)
+    _run(w, o_dtype, scale=scale)
