@@ -33,6 +33,14 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
+T_START = time.perf_counter()
+
+
+def note(msg):
+    """One progress line on stderr (stdout carries only the JSON result)."""
+    print(f"bench: {msg} ({time.perf_counter() - T_START:.1f} s)", file=sys.stderr, flush=True)
+
+
 def useful_fwd_flops(lengths, H, d):
     return float(sum(H * 4.0 * d * L * (L + 1) / 2.0 for L in (int(x) for x in lengths)))
 
@@ -248,24 +256,33 @@ def main():
                      "traffic": measured_traffic("varlen_attn_bwd")},
     }
 
+    note(f"main step: {ms_step:.3f} ms per step over {a.steps} steps")
     if not a.no_hbm_case:
         out["short_pack_fwd"] = short_pack_forward(torch, pvb, W, dev, stream, a.seed)
+        note("short pack done")
     if not a.no_long_case:
         out["long_mixed_pack"] = long_mixed_pack(torch, pvb, W, dev, stream, a.seed)
+        note("long mixed pack done")
     if not a.no_meta_case:
         out["boundaries_from_positions"] = boundary_compilation(torch, pvb, W, dev, stream, a.seed)
+        note("boundaries from positions done")
     if not a.no_loss_case:
         out["packed_loss"] = packed_loss(torch, pvb, dev, stream, a.seed)
+        note("packed loss done")
     if not a.no_gqa_case:
         out["grouped_heads"] = grouped_heads(torch, pvb, dev, stream, a.seed)
+        note("grouped heads done")
     if not a.no_band_case:
         out["cross_and_window"] = cross_and_window(torch, pvb, dev, stream, a.seed)
+        note("cross and window done")
     if not a.no_gdn_case:
         out["gated_delta"] = gated_delta(torch, pvb, W, dev, stream, a.seed)
         out["gated_delta_grouped"] = gated_delta(torch, pvb, W, dev, stream, a.seed, Hk=16)
+        note("gated delta done")
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+        note("cpu baseline done")
     print(json.dumps(out), flush=True)
 
 
