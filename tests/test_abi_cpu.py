@@ -148,6 +148,12 @@ def test_device_entry_points_reject_bad_arguments_on_host():
     assert _fwd(h_cu=dec.ctypes.data, n_seg=3) == 4
     first = np.array([1, 8], np.int32)
     assert _fwd(h_cu=first.ctypes.data) == 4
+    # the element limit: T·H·d = 2^31 is refused; one row less passes that check
+    # (and stops at the too-small workspace, before any launch)
+    assert _fwd(T=2 ** 24, H=1, d=128) == 6
+    assert _fwd(T=2 ** 24 - 1, H=1, d=128, ws_bytes=16) == 5
+    assert _bwd(T=2 ** 24, H=1, d=128) == 6
+    assert _bwd(T=2 ** 24 - 1, H=1, d=128, ws_bytes=8) == 5
     assert _bwd(d=32) == 6
     assert _bwd(dv=None) == 1
     assert _bwd(g=3) == 1

@@ -1,0 +1,47 @@
+"""Forward and backward at the largest size the entry points accept: T·H·d
+one token row short of 2^31 elements per tensor (T = 262143, H = 64, d = 128),
+so byte offsets into Q, K, V, O, dO and the gradients pass 4 GB.  2047
+segments of 128 tokens and a ragged last one of 127 keep the products cheap;
+the segments at the start, in the middle and at the very end of the stream are
+compared with the oracle on three heads.  O and the gradients are bf16 (about
+35 GB of device memory in all)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from tests.parity import check, host_cu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_forward_backward_at_the_element_limit():
+    import packed_varlen_block_amd as pvb
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    T, H, d = 262143, 64, 128
+    assert T * H * d < 2 ** 31 <= (T + 1) * H * d
+    lengths = [128] * 2047 + [127]
+    hc = host_cu(lengths)
+    dev = torch.device("cuda:0")
+    say(f"max size: T={T} H={H} d={d} ({T * H * d} elements per tensor), {len(lengths)} segments")
+    q, k, v, do = (W.device_normal_bf16((T, H, d), 7001 + i, 0.5, dev) for i in range(4))
+    cu = torch.tensor(hc).to(dev)
+    o, lse, st = pvb.varlen_attn_fwd(q, k, v, cu)
+    pvb.check_status(st)
+    dq, dk, dv, st = pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, grad_dtype=torch.bfloat16)
+    pvb.check_status(st)
+    heads = [0, 37, 63]
+    for b in (0, 1023, len(lengths) - 1):
+        a, e = int(hc[b]), int(hc[b + 1])
+        say(f"  segment {b}: rows [{a}, {e})")
+        take = lambda t: t[a:e][:, heads].double().cpu().numpy()
+        qo, ko, vo, doo = take(q), take(k), take(v), take(do)
+        ro, rl = A.varlen_forward(qo, ko, vo, [0, e - a])
+        check("O", take(o), ro, bf16_out=True)
+        check("LSE", lse[heads][:, a:e].double().cpu().numpy(), rl, max_abs=1e-3, mean_abs=1e-4)
+        rq, rk, rv = A.varlen_backward(qo, ko, vo, doo, [0, e - a])
+        for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            check(name, take(got), ref, bf16_out=True)
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()

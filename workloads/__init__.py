@@ -266,3 +266,14 @@ def random_gated_delta(seed: int, lengths, H: int, d: int = 128, g_range=(-0.1, 
         out["h0"] = (_rng(seed, cfg_tag, STREAM_OUTLIER).standard_normal((len(lengths), H, d, d), dtype=np.float32)
                      * np.float32(0.1))
     return out
+
+
+def device_normal_bf16(shape, seed: int, scale: float, device):
+    """N(0,1)·scale rounded to bf16, drawn on the device by torch's seeded
+    generator: for tensors too large to draw on the host.  The same values
+    feed the kernels and, copied back in samples, the oracle.  ``scale`` should
+    be a power of two, so that scaling in bf16 is exact."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=g, device=device, dtype=torch.bfloat16).mul_(scale)
