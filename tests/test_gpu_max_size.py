@@ -45,3 +45,36 @@ def test_forward_backward_at_the_element_limit():
             check(name, take(got), ref, bf16_out=True)
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+def test_packed_loss_past_2_to_the_32_elements():
+    """C = 140000 cells over a 32768 vocabulary: 4.6e9 logits (9.2 GB of bf16,
+    the same again for the gradient), so row offsets pass 2^32 elements.  Rows
+    at the start and the end of the matrix are compared with O10."""
+    import packed_varlen_block_amd as pvb
+    import torch
+    from oracle import loss_probe as LP
+    C, V = 140000, 32768
+    assert C * V > 2 ** 32
+    dev = torch.device("cuda:0")
+    say(f"loss C={C} V={V} ({C * V} logits)")
+    z = W.device_normal_bf16((C, V), 7101, 2.0, dev)
+    r = np.random.default_rng(7102)
+    tg = r.integers(0, V, size=C).astype(np.int32)
+    tg[r.random(C) < 0.01] = -100
+    out = pvb.packed_nll(z, torch.tensor(tg).to(dev))
+    pvb.check_status(out["status"])
+    n = int(LP.eligible_cells(tg, None).sum())
+    assert out["count"].item() == n
+    rows = np.r_[0:8, C // 2:C // 2 + 8, C - 16:C]
+    zs = z[torch.tensor(rows).to(dev)].double().cpu().numpy()
+    rrow, _, ns, _ = LP.packed_nll(zs, tg[rows], None)
+    got_row = out["row_nll"].double().cpu().numpy()
+    assert np.abs(got_row[rows] - rrow).max() <= 2e-5 * max(1.0, np.abs(rrow).max())
+    rg = LP.packed_nll_grad(zs, tg[rows], None) * (ns / n)
+    gg = out["grad"][torch.tensor(rows).to(dev)].double().cpu().numpy()
+    assert np.abs(gg - rg).max() <= 4e-3 / n
+    total = float(np.sum(got_row))
+    assert abs(float(out["loss"][0].item()) - total) <= 1e-6 * abs(total)
+    del z, out
+    torch.cuda.empty_cache()
