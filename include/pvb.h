@@ -56,6 +56,12 @@ typedef enum pvb_status {
   PVB_E_NO_TARGETS = 8      /* a mean loss over zero eligible targets              */
 } pvb_status;
 
+/* The largest count a caller may pass to a device entry point (token counts T
+ * and capacity, segment counts B and n_seg, the vocabulary V): 2^31 - 65536, so
+ * that no kernel's stride loop over such a count steps past INT32_MAX.  A larger
+ * count returns PVB_E_OVERFLOW before anything is enqueued. */
+#define PVB_MAX_COUNT (2147483647 - 65535)
+
 typedef enum pvb_dtype { PVB_BF16 = 0, PVB_F32 = 1 } pvb_dtype;
 
 /* Precision of the probability operands (P, dS) fed to the matrix cores.

@@ -23,6 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpvb.so")
 
 PVB_OK = 0
+PVB_MAX_COUNT = 2 ** 31 - 65536   # largest T, capacity, B, n_seg or V a device entry point accepts
 PVB_BF16, PVB_F32 = 0, 1
 PVB_PREC_BF16, PVB_PREC_SPLIT = 0, 1
 PVB_SENTINEL_ZERO, PVB_SENTINEL_MIN = 0, 1

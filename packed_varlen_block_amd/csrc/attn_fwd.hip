@@ -321,6 +321,7 @@ pvb_status fwd_call(const void* d_q, const void* d_k, const void* d_v, const int
                     void* stream) {
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
   if (H_kv <= 0 || H % H_kv != 0) return PVB_E_INVALID_ARG;
+  if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
   const int32_t T_k = bd.on ? bd.T_k : T;
   if ((T > 0 && (d_q == nullptr || d_o == nullptr || d_lse == nullptr)) ||
       (T_k > 0 && (d_k == nullptr || d_v == nullptr)))

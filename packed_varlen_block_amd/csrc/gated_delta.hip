@@ -406,6 +406,7 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
                             void* d_o, int32_t o_dtype, float* d_ht, int32_t* d_status, void* stream) {
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
   if (H_k <= 0 || H % H_k != 0) return PVB_E_INVALID_ARG;
+  if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
   if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_g == nullptr || d_beta == nullptr ||
                 d_o == nullptr))
     return PVB_E_INVALID_ARG;

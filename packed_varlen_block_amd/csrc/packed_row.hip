@@ -263,6 +263,7 @@ extern "C" pvb_status pvb_build_packed_row(const int32_t* d_lengths, int32_t n_s
     return PVB_E_INVALID_ARG;
   if (n_seg > 0 && d_lengths == nullptr) return PVB_E_INVALID_ARG;
   if (capacity > 0 && (d_pos == nullptr || d_seg == nullptr)) return PVB_E_INVALID_ARG;
+  if (n_seg > PVB_MAX_COUNT || capacity > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
   if ((int64_t)segment_base + n_seg > (int64_t)INT32_MAX + 1) return PVB_E_OVERFLOW;
   const bool want_tokens = d_inputs != nullptr || d_targets != nullptr;
   if (want_tokens && (d_tokens == nullptr || d_tok_off == nullptr)) return PVB_E_INVALID_ARG;
@@ -290,7 +291,7 @@ extern "C" pvb_status pvb_boundaries_from_positions(const int32_t* d_pos, int32_
       d_n_seg == nullptr || d_status == nullptr)
     return PVB_E_INVALID_ARG;
   if (sentinel != PVB_SENTINEL_ZERO && sentinel != PVB_SENTINEL_MIN) return PVB_E_INVALID_ARG;
-  if (T == INT32_MAX) return PVB_E_OVERFLOW;   // T + 1 boundaries would not fit int32 counts
+  if (T > PVB_MAX_COUNT) return PVB_E_OVERFLOW;   // also keeps T + 1 boundaries within int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   boundaries_kernel<<<1, kScanThreads, 0, s>>>(d_pos, T, sentinel == PVB_SENTINEL_MIN ? 1 : 0, d_cu,
                                                cu_capacity, d_n_seg, d_max_seqlen, d_status);

@@ -299,3 +299,21 @@ def test_gated_delta_grouped_heads_host_side_errors():
     assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 1
     args.update(H_k=3, d=64)
     assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 6
+
+
+def test_counts_above_the_documented_maximum_are_refused_on_host():
+    """PVB_MAX_COUNT (2^31 - 65536) bounds every count a device entry point
+    takes, so that no kernel's stride loop can step past INT32_MAX; one more
+    returns PVB_E_OVERFLOW (3) before anything is enqueued."""
+    big = pvb.PVB_MAX_COUNT + 1
+    L = pvb.lib()
+    assert _fwd(n_seg=big) == 3
+    assert _bwd(n_seg=big) == 3
+    assert L.pvb_build_packed_row(FAKE, big, 8, 0, FAKE, FAKE, FAKE, None, None, None, None, None, None,
+                                  FAKE, None) == 3
+    assert L.pvb_build_packed_row(FAKE, 2, big, 0, FAKE, FAKE, FAKE, None, None, None, None, None, None,
+                                  FAKE, None) == 3
+    assert L.pvb_boundaries_from_positions(FAKE, big, 0, FAKE, 8, FAKE, None, FAKE, None) == 3
+    assert L.pvb_packed_nll(FAKE, 0, 4, big, FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, None) == 3
+    assert L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, big, 8, 1, 1, 128, 0.1, None,
+                                     FAKE, 1, None, FAKE, None) == 3
