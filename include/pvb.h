@@ -59,7 +59,12 @@ typedef enum pvb_status {
 /* The largest count a caller may pass to a device entry point (token counts T
  * and capacity, segment counts B and n_seg, the vocabulary V): 2^31 - 65536, so
  * that no kernel's stride loop over such a count steps past INT32_MAX.  A larger
- * count returns PVB_E_OVERFLOW before anything is enqueued. */
+ * count returns PVB_E_OVERFLOW before anything is enqueued.
+ * A launch also holds fewer than 2^32 work-items (the dispatch's grid size is
+ * a 32-bit count): an attention call whose work list would need 2^24 or more
+ * workgroups of 256 (about (T / 128 + min(B, T)) * H of them), a gated delta
+ * call with B * H >= 2^24, or a loss over C >= 2^24 cells returns
+ * PVB_E_UNSUPPORTED, again before anything is enqueued. */
 #define PVB_MAX_COUNT (2147483647 - 65535)
 
 typedef enum pvb_dtype { PVB_BF16 = 0, PVB_F32 = 1 } pvb_dtype;
@@ -168,7 +173,7 @@ pvb_status pvb_build_packed_row(const int32_t* d_lengths, int32_t n_seg, int32_t
  * are not written): PVB_E_BAD_CU_SEQLENS (T > 0 and the first token does not
  * start a segment, so cu[0] could not be 0), PVB_E_OVERSIZED (n_seg + 1 >
  * cu_capacity).  Host-detected: PVB_E_INVALID_ARG, PVB_E_OVERFLOW
- * (T = 2^31 - 1). */
+ * (T > PVB_MAX_COUNT). */
 typedef enum pvb_sentinel { PVB_SENTINEL_ZERO = 0, PVB_SENTINEL_MIN = 1 } pvb_sentinel;
 pvb_status pvb_boundaries_from_positions(const int32_t* d_pos, int32_t T, int32_t sentinel,
                                          int32_t* d_cu, int32_t cu_capacity,
@@ -256,8 +261,9 @@ pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v
  *   d_status     out: device status word (required)                   (device)
  * Device-detected errors (status word; then d_row_nll, d_loss and d_grad are
  * not written): PVB_E_NO_TARGETS (N = 0), PVB_E_INVALID_ARG (an eligible
- * target >= V).  Host-detected: PVB_E_INVALID_ARG, PVB_E_UNSUPPORTED
- * (C >= 2^31). */
+ * target >= V).  Host-detected: PVB_E_INVALID_ARG, PVB_E_OVERFLOW
+ * (V > PVB_MAX_COUNT), PVB_E_UNSUPPORTED (C >= 2^24: one workgroup of 256
+ * work-items per cell, and a launch holds fewer than 2^32 work-items). */
 pvb_status pvb_packed_nll(const void* d_logits, int32_t logits_dtype, int64_t C, int32_t V,
                           const int32_t* d_targets, const uint8_t* d_mask, float* d_row_nll,
                           double* d_loss, int32_t* d_count, void* d_grad, int32_t grad_dtype,

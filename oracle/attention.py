@@ -163,10 +163,12 @@ def varlen_backward(q, k, v, do, cu, scale=None, heads=None):
 def forward_rows(q, k, v, cu, rows, heads, scale=None):
     """O5 for chosen (row, head) pairs only: each output row is computed alone.
 
-    rows, heads: equal-length integer sequences of flat token index and head.
-    Returns (O [n, d], LSE [n]).
+    rows, heads: equal-length integer sequences of flat token index and query
+    head; K and V may carry fewer heads (query head h reads key/value head
+    h // (H / H_k), as in varlen_forward).  Returns (O [n, d], LSE [n]).
     """
     T, H, d = q.shape
+    G = _group(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     cu = [int(x) for x in cu]
@@ -178,11 +180,12 @@ def forward_rows(q, k, v, cu, rows, heads, scale=None):
             raise ValueError("row outside the token axis")
         # t's segment starts at the last boundary at or below t
         start = max(c for c in cu[:-1] if c <= t)
-        sc = scale * (k[start:t + 1, h] @ q[t, h])
+        hk = h // G                       # the key/value head query head h reads
+        sc = scale * (k[start:t + 1, hk] @ q[t, h])
         m = sc.max()
         e = np.exp(sc - m)
         z = e.sum()
-        out[n] = (e / z) @ v[start:t + 1, h]
+        out[n] = (e / z) @ v[start:t + 1, hk]
         lse[n] = m + math.log(z)
     return out, lse
 

@@ -43,8 +43,7 @@ EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
 class PvbError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = int(status)
-        super().__init__(f"{where}: {STATUS_NAMES.get(self.status, self.status)} "
-                         f"({status_string(self.status)})")
+        super().__init__(f"{where}: {STATUS_NAMES.get(self.status, self.status)}")
 
 
 _lib = None
@@ -162,6 +161,44 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _need(t, name, dtype=None, shape=None, dev=None, dim=None):
+    """Check one device argument before anything is enqueued: a torch tensor of
+    the given dtype and shape, contiguous, on a CUDA device (the same one as
+    the call's other tensors when ``dev`` is given).  A host tensor, or a
+    mismatched dtype or shape, would hand the kernels a wrong address or
+    reinterpret its bytes; it raises PvbError(PVB_E_INVALID_ARG) instead."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise PvbError(1, f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise PvbError(1, f"{name} must be {dtype}, not {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise PvbError(1, f"{name} must be {dim}-d, not of shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise PvbError(1, f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise PvbError(1, f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise PvbError(1, f"{name} must be a CUDA tensor")
+    if dev is not None and t.device != dev:
+        raise PvbError(1, f"{name} is on {t.device}, the call's other tensors on {dev}")
+    return t
+
+
+def _status_arg(status, dev):
+    torch = _torch()
+    if status is None:
+        return torch.empty(1, dtype=torch.int32, device=dev)
+    return _need(status, "status", torch.int32, (1,), dev)
+
+
+def _workspace_arg(workspace, nbytes, dev):
+    torch = _torch()
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    return _need(workspace, "workspace", dev=dev)
+
+
 def check_status(status) -> None:
     """Synchronise on a device status word and raise if it holds an error."""
     st = int(status.item())
@@ -179,10 +216,15 @@ def build_packed_row(lengths, capacity: int | None = None, segment_base: int = 0
     synchronise and raise on a device-detected error.
     """
     torch = _torch()
+    _need(lengths, "build_packed_row: lengths", torch.int32, dim=1)
     dev = lengths.device
-    if lengths.dtype != torch.int32 or not lengths.is_contiguous():
-        raise PvbError(1, "build_packed_row: lengths must be contiguous int32")
     B = lengths.numel()
+    gather = tokens is not None
+    if gather or tok_off is not None:
+        if tokens is None or tok_off is None:
+            raise PvbError(1, "build_packed_row: tokens and tok_off go together")
+        _need(tokens, "build_packed_row: tokens", torch.int32, dim=1, dev=dev)
+        _need(tok_off, "build_packed_row: tok_off", torch.int64, (B,), dev)
     if capacity is None:
         capacity = int(lengths.sum().item())
     C = int(capacity)
@@ -190,8 +232,7 @@ def build_packed_row(lengths, capacity: int | None = None, segment_base: int = 0
            "pos": torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C],
            "seg": torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C],
            "max_seqlen": torch.zeros(1, dtype=torch.int32, device=dev),
-           "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
-    gather = tokens is not None
+           "status": _status_arg(status, dev)}
     if gather:
         out["inputs"] = torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C]
         out["targets"] = torch.empty(max(C, 1), dtype=torch.int32, device=dev)[:C]
@@ -207,10 +248,7 @@ def build_packed_row(lengths, capacity: int | None = None, segment_base: int = 0
 
 def _reuse(out, name, shape, dtype, dev):
     """An output tensor taken from a caller's dict (no allocation), checked."""
-    t = out[name]
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or not t.is_contiguous():
-        raise PvbError(1, f"out[{name!r}] must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
-    return t
+    return _need(out[name], f"out[{name!r}]", dtype, shape, dev)
 
 
 def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None = None, status=None,
@@ -227,9 +265,8 @@ def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None 
     raise.
     """
     torch = _torch()
+    _need(pos, "boundaries_from_positions: pos", torch.int32, dim=1)
     dev = pos.device
-    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 1:
-        raise PvbError(1, "boundaries_from_positions: pos must be a contiguous int32 vector")
     if sentinel not in ("zero", "min"):
         raise PvbError(1, "boundaries_from_positions: sentinel must be 'zero' or 'min'")
     T = pos.numel()
@@ -238,12 +275,13 @@ def boundaries_from_positions(pos, sentinel: str = "zero", capacity: int | None 
         out = {"cu": _reuse(out, "cu", (max(cap, 1),), torch.int32, dev),
                "n_seg": _reuse(out, "n_seg", (1,), torch.int32, dev),
                "max_seqlen": _reuse(out, "max_seqlen", (1,), torch.int32, dev),
-               "status": status if status is not None else _reuse(out, "status", (1,), torch.int32, dev)}
+               "status": _status_arg(status, dev) if status is not None
+               else _reuse(out, "status", (1,), torch.int32, dev)}
     else:
         out = {"cu": torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
                "n_seg": torch.zeros(1, dtype=torch.int32, device=dev),
                "max_seqlen": torch.zeros(1, dtype=torch.int32, device=dev),
-               "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+               "status": _status_arg(status, dev)}
     rc = lib().pvb_boundaries_from_positions(
         _ptr(pos) if T > 0 else None, T, PVB_SENTINEL_MIN if sentinel == "min" else PVB_SENTINEL_ZERO,
         _ptr(out["cu"]), cap, _ptr(out["n_seg"]), _ptr(out["max_seqlen"]), _ptr(out["status"]),
@@ -263,28 +301,29 @@ def packed_nll(logits, targets, mask=None, grad=True, grad_dtype=None, status=No
     current stream; call check_status(out["status"]) to synchronise and raise
     on a device-detected error."""
     torch = _torch()
+    _need(logits, "packed_nll: logits", dim=2)
+    _dtype_code(logits.dtype)
     dev = logits.device
-    if logits.dim() != 2 or not logits.is_contiguous():
-        raise PvbError(1, "packed_nll: logits must be contiguous [C, V]")
     C, V = logits.shape
-    if targets.dtype != torch.int32 or tuple(targets.shape) != (C,) or not targets.is_contiguous():
-        raise PvbError(1, "packed_nll: targets must be contiguous int32 [C]")
-    if mask is not None and (mask.dtype != torch.uint8 or tuple(mask.shape) != (C,) or not mask.is_contiguous()):
-        raise PvbError(1, "packed_nll: mask must be contiguous uint8 [C]")
+    _need(targets, "packed_nll: targets", torch.int32, (C,), dev)
+    if mask is not None:
+        _need(mask, "packed_nll: mask", torch.uint8, (C,), dev)
     gdt = logits.dtype if grad_dtype is None else grad_dtype
+    _dtype_code(gdt)
     if out is not None:
         prev = out
         out = {"row_nll": _reuse(prev, "row_nll", (C,), torch.float32, dev),
                "loss": _reuse(prev, "loss", (2,), torch.float64, dev),
                "count": _reuse(prev, "count", (1,), torch.int32, dev),
-               "status": status if status is not None else _reuse(prev, "status", (1,), torch.int32, dev)}
+               "status": _status_arg(status, dev) if status is not None
+               else _reuse(prev, "status", (1,), torch.int32, dev)}
         if grad:
             out["grad"] = _reuse(prev, "grad", (C, V), gdt, dev)
     else:
         out = {"row_nll": torch.empty(max(C, 1), dtype=torch.float32, device=dev)[:C],
                "loss": torch.zeros(2, dtype=torch.float64, device=dev),
                "count": torch.zeros(1, dtype=torch.int32, device=dev),
-               "status": status if status is not None else torch.empty(1, dtype=torch.int32, device=dev)}
+               "status": _status_arg(status, dev)}
         if grad:
             out["grad"] = torch.empty((C, V), dtype=gdt, device=dev)
     rc = lib().pvb_packed_nll(
@@ -317,14 +356,26 @@ def _prec_code(p):
 def _check_qkv(q, k, v, *rest):
     """q (and dO) [T, H, d]; k, v [T, H_kv, d] with H a multiple of H_kv."""
     torch = _torch()
+    _need(q, "q", torch.bfloat16, dim=3)
+    _need(k, "k", torch.bfloat16, dim=3)
     T, H, d = q.shape
-    Hk = k.shape[1] if k.dim() == 3 else -1
-    for t, shape in [(q, (T, H, d)), (k, (T, Hk, d)), (v, (T, Hk, d))] + [(t, (T, H, d)) for t in rest]:
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda:
-            raise PvbError(1, "q/dO [T, H, d] and k/v [T, H_kv, d] must be contiguous bf16 CUDA tensors")
+    Hk = k.shape[1]
+    dev = q.device
+    _need(k, "k", shape=(T, Hk, d), dev=dev)
+    _need(v, "v", torch.bfloat16, (T, Hk, d), dev)
+    for t in rest:
+        _need(t, "dO", torch.bfloat16, (T, H, d), dev)
     if Hk <= 0 or H % Hk != 0:
         raise PvbError(1, "the query heads must be a multiple of the key/value heads")
     return T, H, Hk, d
+
+
+def _cu_arg(cu, name, dev):
+    torch = _torch()
+    _need(cu, name, torch.int32, dim=1, dev=dev)
+    if cu.numel() < 1:
+        raise PvbError(1, f"{name} needs at least one entry")
+    return cu.numel() - 1
 
 
 def varlen_attn_fwd(q, k, v, cu, h_cu=None, softmax_scale=None, o_dtype=None, precision="bf16",
@@ -337,21 +388,21 @@ def varlen_attn_fwd(q, k, v, cu, h_cu=None, softmax_scale=None, o_dtype=None, pr
     """
     torch = _torch()
     T, H, Hk, d = _check_qkv(q, k, v)
-    if cu.dtype != torch.int32 or not cu.is_cuda:
-        raise PvbError(1, "cu must be an int32 CUDA tensor")
-    n_seg = cu.numel() - 1
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    o_dtype = torch.bfloat16 if o_dtype is None else o_dtype
     dev = q.device
+    n_seg = _cu_arg(cu, "cu", dev)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o_dtype is None:
+        o_dtype = out.dtype if out is not None else torch.bfloat16
+    _dtype_code(o_dtype)
     if out is None:
         out = torch.empty((T, H, d), dtype=o_dtype, device=dev)
+    _need(out, "out", o_dtype, (T, H, d), dev)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    _need(lse, "lse", torch.float32, (H, T), dev)
     nbytes = workspace_bytes(T, H, d, n_seg, False)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace_arg(workspace, nbytes, dev)
+    status = _status_arg(status, dev)
     hc = None
     if h_cu is not None:
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
@@ -372,23 +423,23 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad
     dK and dV [T, H_kv, d] (summed over each group's query heads)."""
     torch = _torch()
     T, H, Hk, d = _check_qkv(q, k, v, do)
-    if tuple(o.shape) != (T, H, d) or not o.is_contiguous():
-        raise PvbError(1, "o must be contiguous [T, H, d]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T) or not lse.is_contiguous():
-        raise PvbError(1, "lse must be contiguous fp32 [H, T]")
-    n_seg = cu.numel() - 1
+    dev = q.device
+    _need(o, "o", shape=(T, H, d), dev=dev)
+    _dtype_code(o.dtype)
+    _need(lse, "lse", torch.float32, (H, T), dev)
+    n_seg = _cu_arg(cu, "cu", dev)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
     gcode = _dtype_code(grad_dtype)
-    dev = q.device
     dq = torch.empty((T, H, d), dtype=grad_dtype, device=dev) if dq is None else dq
     dk = torch.empty((T, Hk, d), dtype=grad_dtype, device=dev) if dk is None else dk
     dv = torch.empty((T, Hk, d), dtype=grad_dtype, device=dev) if dv is None else dv
+    _need(dq, "dq", grad_dtype, (T, H, d), dev)
+    _need(dk, "dk", grad_dtype, (T, Hk, d), dev)
+    _need(dv, "dv", grad_dtype, (T, Hk, d), dev)
     nbytes = workspace_bytes(T, H, d, n_seg, True, gcode)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace_arg(workspace, nbytes, dev)
+    status = _status_arg(status, dev)
     hc = None
     if h_cu is not None:
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
@@ -413,19 +464,19 @@ def _check_cross(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k, *rest):
     """q (and dO) [T_q, H, d]; k, v [T_k, H_kv, d]; device cu_q, cu_k int32 [B+1]
     with their host mirrors (both required)."""
     torch = _torch()
-    if q.dim() != 3 or k.dim() != 3:
-        raise PvbError(1, "q and k must be 3-d")
+    _need(q, "q", torch.bfloat16, dim=3)
+    _need(k, "k", torch.bfloat16, dim=3)
     T_q, H, d = q.shape
     T_k, Hk = k.shape[0], k.shape[1]
-    for t, shape in [(q, (T_q, H, d)), (k, (T_k, Hk, d)), (v, (T_k, Hk, d))] + [(t, (T_q, H, d)) for t in rest]:
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda:
-            raise PvbError(1, "q/dO [T_q, H, d] and k/v [T_k, H_kv, d] must be contiguous bf16 CUDA tensors")
+    dev = q.device
+    _need(k, "k", shape=(T_k, Hk, d), dev=dev)
+    _need(v, "v", torch.bfloat16, (T_k, Hk, d), dev)
+    for t in rest:
+        _need(t, "dO", torch.bfloat16, (T_q, H, d), dev)
     if Hk <= 0 or H % Hk != 0:
         raise PvbError(1, "the query heads must be a multiple of the key/value heads")
-    for c in (cu_q, cu_k):
-        if c.dtype != torch.int32 or not c.is_cuda or c.dim() != 1:
-            raise PvbError(1, "cu_q and cu_k must be 1-d int32 CUDA tensors")
-    n_seg = cu_q.numel() - 1
+    n_seg = _cu_arg(cu_q, "cu_q", dev)
+    _cu_arg(cu_k, "cu_k", dev)
     if cu_k.numel() != n_seg + 1:
         raise PvbError(1, "cu_q and cu_k must have the same number of segments")
     if h_cu_q is None or h_cu_k is None:
@@ -447,17 +498,19 @@ def varlen_cross_attn_fwd(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k, window=(-1, 0), s
     T_q, T_k, H, Hk, d, n_seg, hq, hk = _check_cross(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k)
     wl, wr = int(window[0]), int(window[1])
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    o_dtype = torch.bfloat16 if o_dtype is None else o_dtype
     dev = q.device
+    if o_dtype is None:
+        o_dtype = out.dtype if out is not None else torch.bfloat16
+    _dtype_code(o_dtype)
     if out is None:
         out = torch.empty((T_q, H, d), dtype=o_dtype, device=dev)
+    _need(out, "out", o_dtype, (T_q, H, d), dev)
     if lse is None:
         lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
+    _need(lse, "lse", torch.float32, (H, T_q), dev)
     nbytes = cross_workspace_bytes(T_q, T_k, H, d, n_seg, False)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace_arg(workspace, nbytes, dev)
+    status = _status_arg(status, dev)
     rc = lib().pvb_varlen_cross_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(hq), _ptr(cu_k), _ptr(hk),
                                          n_seg, T_q, T_k, H, Hk, d, wl, wr, scale, _ptr(out),
                                          _dtype_code(out.dtype), _ptr(lse), _prec_code(precision),
@@ -473,23 +526,23 @@ def varlen_cross_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, h_cu_q, h_cu_k, windo
     """Backward of varlen_cross_attn_fwd.  Returns (dQ [T_q,H,d], dK, dV [T_k,H_kv,d], status)."""
     torch = _torch()
     T_q, T_k, H, Hk, d, n_seg, hq, hk = _check_cross(q, k, v, cu_q, cu_k, h_cu_q, h_cu_k, do)
-    if tuple(o.shape) != (T_q, H, d) or not o.is_contiguous():
-        raise PvbError(1, "o must be contiguous [T_q, H, d]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T_q) or not lse.is_contiguous():
-        raise PvbError(1, "lse must be contiguous fp32 [H, T_q]")
+    dev = q.device
+    _need(o, "o", shape=(T_q, H, d), dev=dev)
+    _dtype_code(o.dtype)
+    _need(lse, "lse", torch.float32, (H, T_q), dev)
     wl, wr = int(window[0]), int(window[1])
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
     gcode = _dtype_code(grad_dtype)
-    dev = q.device
     dq = torch.empty((T_q, H, d), dtype=grad_dtype, device=dev) if dq is None else dq
     dk = torch.empty((T_k, Hk, d), dtype=grad_dtype, device=dev) if dk is None else dk
     dv = torch.empty((T_k, Hk, d), dtype=grad_dtype, device=dev) if dv is None else dv
+    _need(dq, "dq", grad_dtype, (T_q, H, d), dev)
+    _need(dk, "dk", grad_dtype, (T_k, Hk, d), dev)
+    _need(dv, "dv", grad_dtype, (T_k, Hk, d), dev)
     nbytes = cross_workspace_bytes(T_q, T_k, H, d, n_seg, True, gcode)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+    workspace = _workspace_arg(workspace, nbytes, dev)
+    status = _status_arg(status, dev)
     rc = lib().pvb_varlen_cross_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o.dtype), _ptr(do),
                                          _ptr(lse), _ptr(cu_q), _ptr(hq), _ptr(cu_k), _ptr(hk), n_seg, T_q, T_k,
                                          H, Hk, d, wl, wr, scale, _ptr(dq), _ptr(dk), _ptr(dv), gcode,
@@ -508,35 +561,33 @@ def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=N
     g, beta: fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].
     Returns (O [T, H, 128], final states [B, H, 128, 128] fp32 or None, status)."""
     torch = _torch()
-    if q.dim() != 3 or v.dim() != 3:
-        raise PvbError(1, "q, k, v must be [T, heads, d]")
+    _need(q, "q", torch.bfloat16, dim=3)
+    _need(v, "v", torch.bfloat16, dim=3)
     T, Hk, d = q.shape
     H = v.shape[1]
-    for t, shape in ((q, (T, Hk, d)), (k, (T, Hk, d)), (v, (T, H, d))):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda:
-            raise PvbError(1, "q, k [T, H_k, d] and v [T, H, d] must be contiguous bf16 CUDA tensors")
-    if H % Hk != 0:
-        raise PvbError(1, "the value heads must be a multiple of the query/key heads")
-    for t in (g, beta):
-        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (T, H) or not t.is_cuda:
-            raise PvbError(1, "g and beta must be contiguous fp32 CUDA tensors [T, H]")
-    if cu.dtype != torch.int32 or not cu.is_cuda:
-        raise PvbError(1, "cu must be an int32 CUDA tensor")
-    n_seg = cu.numel() - 1
     dev = q.device
-    if initial_state is not None and (initial_state.dtype != torch.float32 or not initial_state.is_contiguous()
-                                      or tuple(initial_state.shape) != (n_seg, H, d, d)):
-        raise PvbError(1, "initial_state must be contiguous fp32 [B, H, d, d]")
+    _need(k, "k", torch.bfloat16, (T, Hk, d), dev)
+    _need(v, "v", shape=(T, H, d), dev=dev)
+    if Hk <= 0 or H % Hk != 0:
+        raise PvbError(1, "the value heads must be a multiple of the query/key heads")
+    _need(g, "g", torch.float32, (T, H), dev)
+    _need(beta, "beta", torch.float32, (T, H), dev)
+    n_seg = _cu_arg(cu, "cu", dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n_seg, H, d, d), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o_dtype = torch.bfloat16 if o_dtype is None else o_dtype
+    if o_dtype is None:
+        o_dtype = out.dtype if out is not None else torch.bfloat16
+    _dtype_code(o_dtype)
     if out is None:
         out = torch.empty((T, H, d), dtype=o_dtype, device=dev)
+    _need(out, "out", o_dtype, (T, H, d), dev)
     ht = None
     if final_state:
         ht = state_out if state_out is not None else torch.empty((max(n_seg, 0), H, d, d), dtype=torch.float32,
                                                                    device=dev)
-    if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+        _need(ht, "state_out", torch.float32, (n_seg, H, d, d), dev)
+    status = _status_arg(status, dev)
     hc = None
     if h_cu is not None:
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))

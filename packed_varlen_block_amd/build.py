@@ -5,6 +5,7 @@ Usage: python -m packed_varlen_block_amd.build [--verbose] [--resource-usage]
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -37,9 +38,9 @@ def _run(cmd, verbose):
     return out
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
+def build(verbose: bool = False, resource_usage: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(BUILD_DIR, src + ".o")
@@ -48,10 +49,14 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             cmd = [HIPCC, "-x", "hip", "-c", path, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS
             if resource_usage:
                 cmd += ["-Rpass-analysis=kernel-resource-usage"]
-        out = _run(cmd, verbose)
-        if out and (verbose or resource_usage):
-            print(out)
+        cmds.append(cmd)
         objs.append(obj)
+    # one compiler process per source, at most `jobs` at a time
+    n = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+        for out in ex.map(lambda c: _run(c, verbose), cmds):
+            if out and (verbose or resource_usage):
+                print(out)
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH], verbose)
     os.replace(tmp, LIB_PATH)

@@ -604,7 +604,8 @@ pvb_status bwd_call(const void* d_q, const void* d_k, const void* d_v, const voi
     return PVB_E_UNSUPPORTED;
   const size_t cap = plan_capacity(T, n_seg, kTile);
   const size_t cap_k = bd.on ? plan_capacity(T_k, n_seg, kTile) : cap;
-  if (cap * (size_t)H > 0x7fffffffULL || 2 * cap_k * (size_t)H_kv > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
+  if (!grid_fits(cap * (uint64_t)H, kThreads) || !grid_fits(2 * cap_k * (uint64_t)H_kv, kThreads))
+    return PVB_E_UNSUPPORTED;
   const BwdLayout lay = bwd_layout(T, H, n_seg, bd.on ? T_k : -1);
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);

@@ -6,6 +6,8 @@
 // work, heaviest first, so that no workgroup is spent on a tile past the end
 // of a short segment (in contrast to a grid sized by the longest segment whose
 // surplus blocks exit, as in "Packing与 FlashAttention Varlen", section 5).
+#include <algorithm>
+
 #include "pvb_device.hpp"
 
 namespace pvb {
@@ -129,8 +131,11 @@ plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
 }
 
 size_t plan_capacity(int32_t T, int32_t n_seg, int32_t tile) {
-  // sum_b ceil(L_b / tile) <= (T + n_seg * (tile - 1)) / tile
-  return (size_t)(((int64_t)T + (int64_t)n_seg * (tile - 1)) / tile);
+  // sum_b ceil(L_b / tile) <= (T + n_b * (tile - 1)) / tile over the n_b
+  // non-empty segments, and n_b <= min(n_seg, T): zero-length segments add
+  // no tiles
+  const int64_t nb = std::min<int64_t>(n_seg, T);
+  return (size_t)(((int64_t)T + nb * (tile - 1)) / tile);
 }
 
 pvb_status check_cross_args(const int32_t* h_cu_q, const int32_t* d_cu_k, const int32_t* h_cu_k,

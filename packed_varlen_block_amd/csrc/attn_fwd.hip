@@ -333,7 +333,7 @@ pvb_status fwd_call(const void* d_q, const void* d_k, const void* d_v, const int
   if ((int64_t)T * H * d >= ((int64_t)1 << 31) || (int64_t)T_k * H_kv * d >= ((int64_t)1 << 31))
     return PVB_E_UNSUPPORTED;
   const size_t cap = plan_capacity(T, n_seg, kFwdBM);
-  if (cap * (size_t)H > 0x7fffffffULL) return PVB_E_UNSUPPORTED;
+  if (!grid_fits(cap * (uint64_t)H, kFwdThreads)) return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < fwd_workspace(T, n_seg)) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
   if (hs != PVB_OK) return hs;

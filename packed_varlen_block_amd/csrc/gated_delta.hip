@@ -413,7 +413,7 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
   if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
   if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != kGdD) return PVB_E_UNSUPPORTED;
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || (int64_t)n_seg * H >= ((int64_t)1 << 31) - 1)
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads))
     return PVB_E_UNSUPPORTED;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
   if (hs != PVB_OK) return hs;

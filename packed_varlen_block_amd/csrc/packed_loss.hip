@@ -245,7 +245,7 @@ extern "C" pvb_status pvb_packed_nll(const void* d_logits, int32_t logits_dtype,
   if (C > 0 && (d_logits == nullptr || d_targets == nullptr || d_row_nll == nullptr)) return PVB_E_INVALID_ARG;
   if (logits_dtype != PVB_BF16 && logits_dtype != PVB_F32) return PVB_E_INVALID_ARG;
   if (d_grad != nullptr && grad_dtype != PVB_BF16 && grad_dtype != PVB_F32) return PVB_E_INVALID_ARG;
-  if (C > 0x7fffffffLL) return PVB_E_UNSUPPORTED;   // one workgroup per cell
+  if (!grid_fits((uint64_t)C, kRowThreads)) return PVB_E_UNSUPPORTED;   // one workgroup per cell
   if (V > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
   hipStream_t s = static_cast<hipStream_t>(stream);
   nll_count_kernel<<<1, kCountThreads, 0, s>>>(d_targets, d_mask, C, V, d_count, d_status);

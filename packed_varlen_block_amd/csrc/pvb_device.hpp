@@ -213,6 +213,13 @@ plan_tiles_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int tile,
                   int2* __restrict__ tiles, int32_t* __restrict__ count, int32_t* __restrict__ status,
                   int report_ok = 1);
 
+// A dispatch packet carries the grid size in work-items as a 32-bit count, so
+// a launch of `blocks` workgroups of `threads` work-items must keep the product
+// below 2^32; the entry points check this on the host before enqueuing
+// anything (PVB_E_UNSUPPORTED), so that no launch fails after an earlier
+// kernel of the same call has written PVB_OK to the status word.
+inline bool grid_fits(uint64_t blocks, uint32_t threads) { return blocks * threads <= 0xffffffffULL; }
+
 // Host helpers (defined in attn_common.hip).
 size_t plan_capacity(int32_t T, int32_t n_seg, int32_t tile);
 pvb_status check_host_cu(const int32_t* h_cu, int32_t n_seg, int32_t T);

@@ -317,3 +317,22 @@ def test_counts_above_the_documented_maximum_are_refused_on_host():
     assert L.pvb_packed_nll(FAKE, 0, 4, big, FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, None) == 3
     assert L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, big, 8, 1, 1, 128, 0.1, None,
                                      FAKE, 1, None, FAKE, None) == 3
+
+
+def test_grids_of_2_to_the_32_work_items_are_refused_on_host():
+    """A dispatch carries its grid size in work-items as a 32-bit count; a call
+    whose launch would need 2^32 or more is refused with PVB_E_UNSUPPORTED (6)
+    before anything is enqueued, and one workgroup fewer passes that check
+    (stopping at the too-small workspace, 5)."""
+    L = pvb.lib()
+    # 2^16 tokens in 2^16 one-token segments: 2^16 tiles per head
+    assert _fwd(T=2 ** 16, n_seg=2 ** 16, H=256, d=64) == 6
+    assert _fwd(T=2 ** 16, n_seg=2 ** 16, H=255, d=64, ws_bytes=16) == 5
+    # the dK/dV launch has two workgroups per tile and key/value head
+    assert _bwd(T=2 ** 16, n_seg=2 ** 16, H=128, d=64) == 6
+    assert _bwd(T=2 ** 16, n_seg=2 ** 16, H=127, d=64, ws_bytes=8) == 5
+    # zero-length segments add no tiles: 2^16 empty segments and T = 128
+    assert _fwd(T=128, n_seg=2 ** 16, H=256, d=64, ws_bytes=16) == 5
+    assert L.pvb_packed_nll(FAKE, 0, 2 ** 24, 8, FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, None) == 6
+    assert L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2 ** 16, 8, 256, 256, 128, 0.1,
+                                     None, FAKE, 1, None, FAKE, None) == 6

@@ -142,6 +142,35 @@ def test_forward_rows_equals_full_forward():
         assert math.isclose(lrow[n], lse[h, t], rel_tol=0, abs_tol=1e-12)
 
 
+def test_forward_rows_grouped_heads():
+    """Grouped key/value heads (first page, section 5: the key view carries
+    h_k heads): query head h of forward_rows reads key/value head h // (H / H_k),
+    as varlen_forward does; a planted mutant that reads the query head's own
+    index fails."""
+    lengths = [9, 0, 17, 5]
+    T, H, Hk, d = sum(lengths), 6, 2, 8
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((T, H, d))
+    k = rng.standard_normal((T, Hk, d))
+    v = rng.standard_normal((T, Hk, d))
+    cu = P.packed_row_metadata(lengths)["cu"]
+    o, lse = A.varlen_forward(q, k, v, cu)
+    rows = [0, 8, 9, 20, 25, 30, 26, 3]
+    heads = [0, 5, 1, 2, 3, 4, 5, 2]
+    orow, lrow = A.forward_rows(q, k, v, cu, rows, heads)
+    for n, (t, h) in enumerate(zip(rows, heads)):
+        assert np.allclose(orow[n], o[t, h], rtol=0, atol=1e-13)
+        assert math.isclose(lrow[n], lse[h, t], rel_tol=0, abs_tol=1e-12)
+
+    # mutant: K/V indexed by the query head modulo H_k (a plausible slip)
+    def wrong(t, h):
+        start = max(c for c in [int(x) for x in cu[:-1]] if c <= t)
+        sc = (k[start:t + 1, h % Hk] @ q[t, h]) / math.sqrt(d)
+        e = np.exp(sc - sc.max())
+        return (e / e.sum()) @ v[start:t + 1, h % Hk]
+    assert any(not np.allclose(wrong(t, h), o[t, h], rtol=0, atol=1e-6) for t, h in zip(rows, heads))
+
+
 # ----------------------------------------------------------- O6
 
 def _loss(q, k, v, do, cu):
