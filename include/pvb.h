@@ -234,6 +234,30 @@ pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v
                                int32_t grad_dtype, int32_t precision, void* workspace,
                                size_t workspace_bytes, int32_t* d_status, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid allocation): pvb_varlen_attn_bwd_gqa
+ * without a workspace argument.  Its scratch (the work list and the per-row
+ * {LSE, D} records) is a fixed device array inside the library of
+ * PVB_STATIC_SCRATCH_BYTES (64 MiB), held by every GPU the library runs on
+ * until the process ends; the call itself allocates nothing.  It serves sizes
+ * whose workspace, pvb_varlen_attn_workspace_bytes(T, H, d, n_seg, 1, ...),
+ * fits that array (8 bytes per token and head plus 8 per 128-row tile:
+ * T = 131072 at H = 32 fits, T = 262144 at H = 32 does not); larger ones
+ * return PVB_E_WORKSPACE before anything is enqueued.  All calls on one
+ * GPU share the array, so calls that overlap on that GPU (other streams,
+ * other threads) race and give wrong gradients: serialise them.  Arguments,
+ * outputs and other errors as pvb_varlen_attn_bwd_gqa; the results are the
+ * same bit for bit.  PVB_E_HIP when the array's device address cannot be
+ * obtained on the current device. */
+#define PVB_STATIC_SCRATCH_BYTES (64u << 20)
+pvb_status pvb_varlen_attn_bwd_noalloc(const void* d_q, const void* d_k, const void* d_v,
+                                       const void* d_o, int32_t o_dtype, const void* d_do,
+                                       const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                                       int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                       float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                       int32_t grad_dtype, int32_t precision, int32_t* d_status,
+                                       void* stream);
+
 /* ---------------------------------------------------------------- packed loss */
 
 /* Token-weighted negative log-likelihood over packed cells and its logit

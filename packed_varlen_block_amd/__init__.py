@@ -37,7 +37,8 @@ EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
            "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
            "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
-           "pvb_status_string", "pvb_version")
+           "pvb_varlen_attn_bwd_noalloc", "pvb_status_string", "pvb_version")
+PVB_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of pvb_varlen_attn_bwd_noalloc
 
 
 class PvbError(RuntimeError):
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
                                               P, P]
         L.pvb_varlen_attn_bwd_gqa.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
                                               P, P, P, I32, I32, P, SZ, P, P]
+        L.pvb_varlen_attn_bwd_noalloc.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
+                                                  P, P, P, I32, I32, P, P]
         L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, P]
         L.pvb_gated_delta_fwd_gqa.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, I32, P, P, P]
         L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
@@ -82,6 +85,7 @@ def lib() -> ctypes.CDLL:
         for name in ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
                      "pvb_boundaries_from_positions", "pvb_packed_nll", "pvb_varlen_attn_fwd",
                      "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
+                     "pvb_varlen_attn_bwd_noalloc",
                      "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd", "pvb_gated_delta_fwd",
                      "pvb_gated_delta_fwd_gqa"):
             getattr(L, name).restype = ctypes.c_int
@@ -451,6 +455,40 @@ def varlen_attn_bwd(q, k, v, o, do, lse, cu, h_cu=None, softmax_scale=None, grad
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _ptr(status), _stream(dev))
     _check(rc, "varlen_attn_bwd")
+    return dq, dk, dv, status
+
+
+def varlen_attn_bwd_noalloc(q, k, v, o, do, lse, cu, dq, dk, dv, status, h_cu=None, softmax_scale=None,
+                            precision="bf16"):
+    """The backward through pvb_varlen_attn_bwd_noalloc: no workspace argument
+    (the library's fixed scratch array serves), and every output passed in,
+    so that neither the binding nor the library allocates device memory.
+    dQ [T, H, d], dK and dV [T, H_kv, d] share one dtype (bf16 or fp32),
+    status int32 [1].  Calls that overlap on one GPU share the scratch and
+    race.  Returns (dq, dk, dv, status)."""
+    torch = _torch()
+    T, H, Hk, d = _check_qkv(q, k, v, do)
+    dev = q.device
+    _need(o, "o", shape=(T, H, d), dev=dev)
+    _dtype_code(o.dtype)
+    _need(lse, "lse", torch.float32, (H, T), dev)
+    n_seg = _cu_arg(cu, "cu", dev)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _need(dq, "dq", None, (T, H, d), dev)
+    gcode = _dtype_code(dq.dtype)
+    _need(dk, "dk", dq.dtype, (T, Hk, d), dev)
+    _need(dv, "dv", dq.dtype, (T, Hk, d), dev)
+    _need(status, "status", torch.int32, (1,), dev)
+    hc = None
+    if h_cu is not None:
+        hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
+        if hc.size != n_seg + 1:
+            raise PvbError(1, "h_cu must have B+1 entries")
+    rc = lib().pvb_varlen_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o.dtype), _ptr(do),
+                                           _ptr(lse), _ptr(cu), _ptr(hc), n_seg, T, H, Hk, d, scale,
+                                           _ptr(dq), _ptr(dk), _ptr(dv), gcode, _prec_code(precision),
+                                           _ptr(status), _stream(dev))
+    _check(rc, "varlen_attn_bwd_noalloc")
     return dq, dk, dv, status
 
 

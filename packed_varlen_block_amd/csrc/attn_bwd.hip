@@ -30,6 +30,8 @@
 // traffic (about 4 bytes per permitted edge at 128-key tiles) costs more than
 // the two extra matrix products.  Every gradient element is written once, so
 // the backward is deterministic.
+#include <mutex>
+
 #include "pvb_device.hpp"
 
 namespace pvb {
@@ -685,6 +687,57 @@ extern "C" pvb_status pvb_varlen_attn_bwd_gqa(const void* d_q, const void* d_k, 
   return pvb::bwd_call(d_q, d_k, d_v, d_o, o_dtype, d_do, d_lse, d_cu, h_cu, n_seg, T, H, H_kv, d,
                        softmax_scale, d_dq, d_dk, d_dv, grad_dtype, precision, workspace, workspace_bytes,
                        d_status, pvb::BandArgs{}, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The backward without a caller workspace.  Its scratch (the planner's tile
+// list and the {LSE log2e, D} records) lives in one fixed device array of the
+// library, `scratch`; each GPU holds its own copy of it, at an address taken
+// once per device with hipGetSymbolAddress (the array's name on the host is
+// only a stand-in and is never passed to a kernel).  Nothing in it has to
+// start at zero: the planner writes its count and list, and the dQ kernel
+// writes every record, before anything reads them.
+// ---------------------------------------------------------------------------
+namespace pvb {
+namespace {
+static __device__ __align__(256) char scratch[PVB_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace pvb
+
+extern "C" pvb_status pvb_varlen_attn_bwd_noalloc(const void* d_q, const void* d_k, const void* d_v,
+                                                  const void* d_o, int32_t o_dtype, const void* d_do,
+                                                  const float* d_lse, const int32_t* d_cu, const int32_t* h_cu,
+                                                  int32_t n_seg, int32_t T, int32_t H, int32_t H_kv, int32_t d,
+                                                  float softmax_scale, void* d_dq, void* d_dk, void* d_dv,
+                                                  int32_t grad_dtype, int32_t precision, int32_t* d_status,
+                                                  void* stream) {
+  using namespace pvb;
+  if (n_seg < 0 || T < 0 || H <= 0) return PVB_E_INVALID_ARG;
+  if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
+  // the sizes the scratch can hold, checked before any HIP call
+  if (bwd_layout(T, H, n_seg).total > (size_t)PVB_STATIC_SCRATCH_BYTES) return PVB_E_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return PVB_E_HIP;
+  return bwd_call(d_q, d_k, d_v, d_o, o_dtype, d_do, d_lse, d_cu, h_cu, n_seg, T, H, H_kv, d, softmax_scale,
+                  d_dq, d_dk, d_dv, grad_dtype, precision, ws, (size_t)PVB_STATIC_SCRATCH_BYTES, d_status,
+                  BandArgs{}, stream);
 }
 
 extern "C" pvb_status pvb_varlen_attn_bwd(const void* d_q, const void* d_k, const void* d_v,

@@ -336,3 +336,25 @@ def test_grids_of_2_to_the_32_work_items_are_refused_on_host():
     assert L.pvb_packed_nll(FAKE, 0, 2 ** 24, 8, FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, None) == 6
     assert L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2 ** 16, 8, 256, 256, 128, 0.1,
                                      None, FAKE, 1, None, FAKE, None) == 6
+
+
+def test_noalloc_backward_refuses_sizes_beyond_its_scratch_on_host():
+    """pvb_varlen_attn_bwd_noalloc serves sizes whose workspace fits its fixed
+    scratch (PVB_STATIC_SCRATCH_BYTES); larger ones return PVB_E_WORKSPACE (5)
+    before any HIP call, bad sizes PVB_E_INVALID_ARG (1) or PVB_E_OVERFLOW (3)."""
+    L = pvb.lib()
+    cap = pvb.PVB_STATIC_SCRATCH_BYTES
+
+    def call(T, H, n_seg=1):
+        return L.pvb_varlen_attn_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, n_seg, T, H, H,
+                                             128, 0.088, FAKE, FAKE, FAKE, 1, 0, FAKE, None)
+    assert pvb.workspace_bytes(262144, 33, 128, 1, True) > cap
+    assert call(262144, 33) == 5
+    assert pvb.workspace_bytes(2 ** 20, 32, 128, 1, True) > cap
+    assert call(2 ** 20, 32) == 5
+    assert call(-1, 4) == 1
+    assert call(8, 0) == 1
+    assert call(8, 4, n_seg=-1) == 1
+    assert call(8, 4, n_seg=pvb.PVB_MAX_COUNT + 1) == 3
+    assert call(262144, 32) == 5                                       # the documented examples
+    assert pvb.workspace_bytes(131072, 32, 128, 1, True) <= cap
