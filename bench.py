@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-gqa-case", action="store_true")
     ap.add_argument("--no-band-case", action="store_true")
     ap.add_argument("--no-gdn-case", action="store_true")
+    ap.add_argument("--no-calls-case", action="store_true")
+    ap.add_argument("--no-edge-case", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -92,15 +94,82 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_info():
+    """(library, threads) of numpy's BLAS as threadpoolctl reports it."""
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                return f"{p.get('internal_api')} ({os.path.basename(p.get('filepath', ''))})", int(p["num_threads"])
+    except Exception:
+        pass
+    return "unknown", 0
+
+
+def oracle_per_config(seed, raw, first, budget_s=10.0):
+    """The fp64 oracle's wall time per workload, on one head of each (the
+    head count is scaled out: full = one head x H, every head costing the
+    same), forward for the forward-only workloads and forward + backward for
+    the others; with the useful GFLOP/s on the same count as the GPU's."""
+    from oracle import attention as A
+    import workloads as W
+    res = {}
+    t_all = time.perf_counter()
+    for cfg in (1, 2, 3, 5, 4):
+        if cfg == 4 and time.perf_counter() - t_all > budget_s:
+            res[f"cfg{cfg}"] = {"skipped": "time budget"}
+            continue
+        H_full = W.HEADS[cfg]
+        w1 = W.make(cfg, seed=seed, first_pack_lengths=first if cfg == 3 else None, H=1)
+        f = W.bf16_bits_to_f64
+        q, k, v = f(w1.q), f(w1.k), f(w1.v)
+        cu = np.concatenate([[0], np.cumsum(w1.lengths)]).astype(np.int64)
+        t0 = time.perf_counter()
+        A.varlen_forward(q, k, v, cu)
+        t_f = time.perf_counter() - t0
+        rec = {"T": int(w1.T), "H": H_full, "head_dim": w1.d, "heads_timed": 1,
+               "fwd_s_per_head": round(t_f, 4), "fwd_s_full": round(t_f * H_full, 3)}
+        F1 = useful_fwd_flops(w1.lengths, 1, w1.d)
+        if w1.backward:
+            t0 = time.perf_counter()
+            A.varlen_backward(q, k, v, f(w1.do), cu)
+            t_b = time.perf_counter() - t0
+            rec.update({"bwd_s_per_head": round(t_b, 4), "fwd_bwd_s_full": round((t_f + t_b) * H_full, 3),
+                        "useful_gflops": round(3.5 * F1 / (t_f + t_b) / 1e9, 2)})
+        else:
+            rec["useful_gflops"] = round(F1 / t_f / 1e9, 2)
+        res[f"cfg{cfg}"] = rec
+    # host planners at n = 20,000: the oracle's BFD against the library's
+    from oracle import packing as P
+    import packed_varlen_block_amd as pvb
+    t0 = time.perf_counter()
+    P.best_fit_decreasing(raw.tolist(), 8192)
+    t_py = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(10):
+        pvb.pack_plan_bfd(raw, 8192)
+    t_c = (time.perf_counter() - t0) / 10
+    res["bfd_n20000"] = {"oracle_python_ms": round(t_py * 1e3, 2), "library_cpp_ms": round(t_c * 1e3, 3)}
+    return res
+
+
 def cpu_baseline(wl, budget_s):
     """Time the fp64 oracle (as it stands) on whole heads of the same workload."""
     from oracle import attention as A
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = len(os.sched_getaffinity(0))
+    blas, blas_threads = blas_info()
     q = W.bf16_bits_to_f64(wl.q)
     k = W.bf16_bits_to_f64(wl.k)
     v = W.bf16_bits_to_f64(wl.v)
@@ -116,7 +185,8 @@ def cpu_baseline(wl, budget_s):
     flops = 3.5 * useful_fwd_flops(wl.lengths, heads, wl.d)
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"fp64 numpy oracle forward+backward on {heads} of {wl.H} heads of the same "
-                      f"pack, {el:.1f} s; useful causal FLOP counted as on the GPU"}
+                      f"pack, {el:.1f} s; useful causal FLOP counted as on the GPU",
+            "cpu_model": cpu_model(), "blas": blas, "blas_threads": blas_threads}
 
 
 def main():
@@ -257,6 +327,19 @@ def main():
     }
 
     note(f"main step: {ms_step:.3f} ms per step over {a.steps} steps")
+    if not a.no_calls_case:
+        c3 = attn_calls(torch, pvb, W, dev, stream, wl, torch.bfloat16, torch.float32, "bf16")
+        c3.update({"workload": "bfd_first_pack_T8192_H32_d128", "o_dtype": "bf16", "grad_dtype": "f32",
+                   "precision": "bf16"})
+        out["first_pack_calls"] = c3
+        note("first pack calls done")
+    if not a.no_edge_case:
+        w5 = W.make(5, seed=a.seed)
+        c5 = attn_calls(torch, pvb, W, dev, stream, w5, torch.float32, torch.float32, "split")
+        c5.update({"workload": "edge_case_T16384_H16_d128", "seed_used": int(w5.extra["seed_used"]),
+                   "o_dtype": "f32", "grad_dtype": "f32", "precision": "split"})
+        out["edge_case_pack"] = c5
+        note("edge-case pack done")
     if not a.no_hbm_case:
         out["short_pack_fwd"] = short_pack_forward(torch, pvb, W, dev, stream, a.seed)
         note("short pack done")
@@ -282,6 +365,7 @@ def main():
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+        out["cpu_baseline"]["per_config"] = oracle_per_config(a.seed, raw, first)
         note("cpu baseline done")
     print(json.dumps(out), flush=True)
 
@@ -328,42 +412,17 @@ def short_pack_forward(torch, pvb, W, dev, stream, seed, n_sets=8, reps=40):
             "useful_tflops": round(F / (med * 1e-3) / 1e12, 2)}
 
 
-def long_mixed_pack(torch, pvb, W, dev, stream, seed, reps=5):
+def long_mixed_pack(torch, pvb, W, dev, stream, seed, reps=50):
     """The long mixed pack (T=32768: one 16384-token segment, then segments of
     16-1024, H=32, d=128), forward and backward as in the main step (O bf16,
-    fp32 gradients, bf16 P/dS): useful TFLOP/s per call, median of reps."""
+    fp32 gradients, bf16 P/dS): median, p10 and p90 over reps calls, useful
+    TFLOP/s at the medians."""
     w = W.make(4, seed=seed)
-    T, H, d = w.T, w.H, w.d
-    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
-    q, k, v, do = up(w.q), up(w.k), up(w.v), up(w.do)
-    cu = torch.tensor(np.concatenate([[0], np.cumsum(w.lengths)]).astype(np.int32), device=dev)
-    B = len(w.lengths)
-    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
-    grads = [torch.empty((T, H, d), dtype=torch.float32, device=dev) for _ in range(3)]
-    wf = torch.empty(pvb.workspace_bytes(T, H, d, B, False), dtype=torch.uint8, device=dev)
-    wb = torch.empty(pvb.workspace_bytes(T, H, d, B, True, pvb.PVB_F32), dtype=torch.uint8, device=dev)
-    st = torch.zeros(1, dtype=torch.int32, device=dev)
-    ev = []
-    for i in range(2 + reps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record(stream)
-        pvb.varlen_attn_fwd(q, k, v, cu, out=o, lse=lse, workspace=wf, status=st)
-        e[1].record(stream)
-        pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, dq=grads[0], dk=grads[1], dv=grads[2],
-                            workspace=wb, status=st)
-        e[2].record(stream)
-        if i >= 2:
-            ev.append(e)
-    torch.cuda.synchronize()
-    pvb.check_status(st)
-    fwd = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
-    bwd = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
-    F = useful_fwd_flops(w.lengths, H, d)
-    both = 3.5 * F / ((fwd + bwd) * 1e-3) / 1e12
-    return {"workload": "long_mixed_T32768_H32_d128", "segments": B, "pass": "fwd+bwd",
-            "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "fwd_bwd_ms": round(fwd + bwd, 4),
-            "useful_tflops": round(both, 2), "pct_bf16_mfma_peak": round(100.0 * both / PEAK_BF16_TFLOPS, 2)}
+    r = attn_calls(torch, pvb, W, dev, stream, w, torch.bfloat16, torch.float32, "bf16", reps=reps)
+    r.update({"workload": "long_mixed_T32768_H32_d128", "pass": "fwd+bwd",
+              "fwd_ms": r["fwd"]["median_ms"], "bwd_ms": r["bwd"]["median_ms"],
+              "fwd_bwd_ms": r["fwd_bwd"]["median_ms"]})
+    return r
 
 
 def queued_us(torch, stream, fn, reps):
@@ -379,6 +438,67 @@ def queued_us(torch, stream, fn, reps):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def timed_calls(torch, stream, parts, warmup=10, reps=50):
+    """Median, p10 and p90 (ms) of each part of a call sequence over reps timed
+    repetitions after warmup untimed ones; parts is a list of (name, fn), the
+    parts run back to back and each is bracketed by HIP events on the launch
+    stream."""
+    for _ in range(warmup):
+        for _, fn in parts:
+            fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+        marks[0].record(stream)
+        for i, (_, fn) in enumerate(parts):
+            fn()
+            marks[i + 1].record(stream)
+        ev.append(marks)
+    torch.cuda.synchronize()
+    out = {}
+    for i, (name, _) in enumerate(parts):
+        ms = np.array([m[i].elapsed_time(m[i + 1]) for m in ev])
+        out[name] = ms
+    out["total"] = np.array([m[0].elapsed_time(m[-1]) for m in ev])
+    return out
+
+
+def pct(ms):
+    return {"median_ms": round(float(np.median(ms)), 4), "p10_ms": round(float(np.percentile(ms, 10)), 4),
+            "p90_ms": round(float(np.percentile(ms, 90)), 4)}
+
+
+def attn_calls(torch, pvb, W, dev, stream, w, o_dtype, g_dtype, precision, reps=50):
+    """One workload's forward and backward calls timed alone: median, p10 and
+    p90 over reps calls after 10 warmups, and useful TFLOP/s at the medians."""
+    T, H, d = w.T, w.H, w.d
+    B = len(w.lengths)
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, do = up(w.q), up(w.k), up(w.v), up(w.do)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(w.lengths)]).astype(np.int32), device=dev)
+    o = torch.empty((T, H, d), dtype=o_dtype, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    grads = [torch.empty((T, H, d), dtype=g_dtype, device=dev) for _ in range(3)]
+    gcode = pvb.PVB_F32 if g_dtype == torch.float32 else pvb.PVB_BF16
+    wf = torch.empty(pvb.workspace_bytes(T, H, d, B, False), dtype=torch.uint8, device=dev)
+    wb = torch.empty(pvb.workspace_bytes(T, H, d, B, True, gcode), dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    r = timed_calls(torch, stream, [
+        ("fwd", lambda: pvb.varlen_attn_fwd(q, k, v, cu, out=o, lse=lse, workspace=wf, status=st,
+                                            precision=precision)),
+        ("bwd", lambda: pvb.varlen_attn_bwd(q, k, v, o, do, lse, cu, dq=grads[0], dk=grads[1], dv=grads[2],
+                                            workspace=wb, status=st, precision=precision))], reps=reps)
+    pvb.check_status(st)
+    F = useful_fwd_flops(w.lengths, H, d)
+    fwd, bwd, tot = (float(np.median(r[n])) for n in ("fwd", "bwd", "total"))
+    return {"segments": B, "T": T, "H": H, "head_dim": d, "calls": reps,
+            "fwd": pct(r["fwd"]), "bwd": pct(r["bwd"]), "fwd_bwd": pct(r["total"]),
+            "fwd_tflops": round(F / (fwd * 1e-3) / 1e12, 2), "bwd_tflops": round(2.5 * F / (bwd * 1e-3) / 1e12, 2),
+            "useful_tflops": round(3.5 * F / (tot * 1e-3) / 1e12, 2),
+            "pct_bf16_mfma_peak": round(100.0 * 3.5 * F / (tot * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
 def boundary_compilation(torch, pvb, W, dev, stream, seed, reps=50):

@@ -20,7 +20,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpvb.so")
+# PVB_LIB_PATH selects another build of the same library (the CPU sanitizer
+# build, libpvb_san.so); there is no other implementation to fall back to.
+LIB_PATH = os.environ.get("PVB_LIB_PATH") or os.path.join(_HERE, "libpvb.so")
 
 PVB_OK = 0
 PVB_MAX_COUNT = 2 ** 31 - 65536   # largest T, capacity, B, n_seg or V a device entry point accepts

@@ -1,6 +1,6 @@
 """Build libpvb.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: python -m packed_varlen_block_amd.build [--verbose] [--resource-usage]
+Usage: python -m packed_varlen_block_amd.build [--verbose] [--resource-usage] [--sanitize]
 """
 from __future__ import annotations
 
@@ -38,15 +38,27 @@ def _run(cmd, verbose):
     return out
 
 
-def build(verbose: bool = False, resource_usage: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# The CPU sanitizer build (libpvb_san.so): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (the planners, the ABI's
+# argument checks, the launch set-up); the device code is built as usual.
+# Every sanitizer flag is given to the host compilation alone.
+SAN_LIB_PATH = os.path.join(HERE, "libpvb_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, resource_usage: bool = False, jobs: int | None = None,
+          sanitize: bool = False) -> str:
+    bdir = BUILD_DIR + ("_san" if sanitize else "")
+    os.makedirs(bdir, exist_ok=True)
     cmds, objs = [], []
+    extra = SAN_FLAGS if sanitize else []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD_DIR, src + ".o")
-        cmd = [HIPCC, "-c", path, "-o", obj] + COMMON_FLAGS
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [HIPCC, "-c", path, "-o", obj] + COMMON_FLAGS + extra
         if src.endswith(".hip"):
-            cmd = [HIPCC, "-x", "hip", "-c", path, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS
+            cmd = [HIPCC, "-x", "hip", "-c", path, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS + extra
             if resource_usage:
                 cmd += ["-Rpass-analysis=kernel-resource-usage"]
         cmds.append(cmd)
@@ -57,18 +69,21 @@ def build(verbose: bool = False, resource_usage: bool = False, jobs: int | None 
         for out in ex.map(lambda c: _run(c, verbose), cmds):
             if out and (verbose or resource_usage):
                 print(out)
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    lib_path = SAN_LIB_PATH if sanitize else LIB_PATH
+    tmp = lib_path + ".tmp"
+    _run([HIPCC, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH] + extra, verbose)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="build libpvb_san.so with host AddressSanitizer and UBSan (CPU checks)")
     a = ap.parse_args(argv)
-    print(build(a.verbose, a.resource_usage))
+    print(build(a.verbose, a.resource_usage, sanitize=a.sanitize))
 
 
 if __name__ == "__main__":

@@ -178,6 +178,10 @@ def tensors(seed: int, cfg: int, T: int, H: int, d: int, scale: float,
     return q, k, v, do
 
 
+# head counts of the five workloads
+HEADS = {1: 2, 2: 16, 3: 32, 4: 32, 5: 16}
+
+
 def make(cfg: int, seed: int = 0, first_pack_lengths=None, H=None, backward=None) -> Workload:
     """Build workload ``cfg`` (1..5).
 
@@ -186,26 +190,27 @@ def make(cfg: int, seed: int = 0, first_pack_lengths=None, H=None, backward=None
     ``H`` overrides the head count (used to cut a bounded sample of a workload).
     """
     extra = {}
+    if cfg not in HEADS:
+        raise ValueError(f"unknown workload {cfg}")
+    h = HEADS[cfg]
     if cfg == 1:
         lengths = np.asarray(WORKED_LENGTHS, dtype=np.int32)
-        h, d, scale, bwd = 2, 64, 1.0, False
+        d, scale, bwd = 64, 1.0, False
     elif cfg == 2:
         lengths = lengths_cfg2(seed)
-        h, d, scale, bwd = 16, 128, 0.5, False
+        d, scale, bwd = 128, 0.5, False
     elif cfg == 3:
         if first_pack_lengths is None:
             raise ValueError("cfg 3 needs the first pack's lengths from a BFD packer")
         lengths = np.asarray(first_pack_lengths, dtype=np.int32)
-        h, d, scale, bwd = 32, 128, 0.5, True
+        d, scale, bwd = 128, 0.5, True
     elif cfg == 4:
         lengths = lengths_cfg4(seed)
-        h, d, scale, bwd = 32, 128, 0.5, True
-    elif cfg == 5:
+        d, scale, bwd = 128, 0.5, True
+    else:
         lengths, used = lengths_cfg5(seed)
         extra["seed_used"] = used
-        h, d, scale, bwd = 16, 128, 1.0, True
-    else:
-        raise ValueError(f"unknown workload {cfg}")
+        d, scale, bwd = 128, 1.0, True
     if H is not None:
         h = int(H)
     if backward is not None:
