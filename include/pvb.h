@@ -211,7 +211,11 @@ size_t pvb_varlen_attn_workspace_bytes(int32_t T, int32_t H, int32_t d, int32_t 
  *   d_cu           int32 [n_seg+1]                                 (device)
  *   h_cu           int32 [n_seg+1] host mirror, nullable: when given it is
  *                  validated on the host and a bad one returns
- *                  PVB_E_BAD_CU_SEQLENS before anything is enqueued  (host)
+ *                  PVB_E_BAD_CU_SEQLENS before anything is enqueued; for a
+ *                  small pack (at most 256 segments, 448 tiles of 128 rows,
+ *                  32768 tokens per segment) the forward then lists its work
+ *                  on the host and passes it with the launch, and does not
+ *                  read d_cu (which must hold the same values)  (host)
  *   d_o            out [T, H, d], bf16 or fp32 per o_dtype          (device)
  *   d_lse          out fp32 [H, T] natural-log LSE                   (device)
  *   workspace      >= pvb_varlen_attn_workspace_bytes(..., 0, ...) bytes  (device)

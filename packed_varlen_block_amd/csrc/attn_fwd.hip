@@ -21,6 +21,9 @@
 // only on tiles that cross the diagonal or the segment end.  The running max
 // is raised lazily (see kSlack), so most tiles skip the rescale of O.  A bf16 O
 // is staged through LDS and stored as whole rows.
+#include <algorithm>
+#include <type_traits>
+
 #include "pvb_device.hpp"
 
 namespace pvb {
@@ -34,13 +37,16 @@ constexpr int kFwdThreads = 256;
 // BAND: separate key boundaries cu_k (T_k keys) and a key band per query row
 // (bottom-right causal alignment and local windows, see KeyBand); without it,
 // causal self-attention over cu.
-template <int D, bool SPLIT, typename OutT, bool DECODE, int BN, bool BAND>
+// MODE: 0 the planner's list, 1 items decoded in the kernel, 2 items listed
+// on the host and passed in `hi` (self-attention only).
+template <int D, bool SPLIT, typename OutT, int MODE, int BN, bool BAND>
 __global__ void __launch_bounds__(kFwdThreads, BN == 32 ? 3 : 2)
 attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const bf16* __restrict__ v, const int32_t* __restrict__ cu,
                 const WorkList wl, int H, int Hk, int T,
                 float scale_log2, OutT* __restrict__ o, float* __restrict__ lse,
-                const int32_t* __restrict__ cu_k, int T_k, int win_left, int win_right) {
+                const int32_t* __restrict__ cu_k, int T_k, int win_left, int win_right,
+                const std::conditional_t<MODE == 2, HostItems, NoHostItems> hi) {
   constexpr int BM = kFwdBM;
   constexpr int NB = BN / 32;    // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
@@ -56,19 +62,31 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tau = blockIdx.x / H;
   const HeadPair hp = head_of_slot(blockIdx.x - tau * H, H, Hk);
   const int h = hp.h;
-  int2 tm;
-  if (!work_item<BM, DECODE>(wl, cu, T, tau, &tm)) return;
-  const int seg0 = cu[tm.x];
-  const int L = cu[tm.x + 1] - seg0;           // query rows of the slice
+  int seg0, L, m_tile, sidx = 0;
+  if constexpr (MODE == 2) {
+    // the launch holds exactly the listed items; the mirror was checked on the host
+    if (blockIdx.x == 0 && threadIdx.x == 0) *wl.status = PVB_OK;
+    seg0 = hi.seg0[tau];
+    L = hi.len_m[tau] >> 8;
+    m_tile = hi.len_m[tau] & 255;
+  } else {
+    int2 tm;
+    if (!work_item<BM, MODE == 1>(wl, cu, T, tau, &tm)) return;
+    sidx = tm.x;
+    seg0 = cu[sidx];
+    L = cu[sidx + 1] - seg0;                   // query rows of the slice
+    m_tile = tm.y;
+  }
   int seg0k = seg0, Lk = L;                    // its keys
   if constexpr (BAND) {
+    static_assert(MODE != 2, "host-listed items are for self-attention");
     // clipped to [0, T_k] so that no access leaves the key tensors (cu_k is
     // validated on the host)
-    seg0k = min(max(cu_k[tm.x], 0), T_k);
-    Lk = min(max(cu_k[tm.x + 1] - seg0k, 0), T_k - seg0k);
+    seg0k = min(max(cu_k[sidx], 0), T_k);
+    Lk = min(max(cu_k[sidx + 1] - seg0k, 0), T_k - seg0k);
   }
   const KeyBand<BAND> band{Lk, Lk - L, win_left, win_right};
-  const int q0 = tm.y * BM;
+  const int q0 = m_tile * BM;
   const int rs = H * D;      // row stride of Q and O (elements)
   const int rs_kv = Hk * D;  // row stride of K and V
   const int64_t base = ((int64_t)seg0 * H + h) * D;
@@ -272,34 +290,68 @@ attn_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 template <int D, bool SPLIT, typename OutT, int BN, bool BAND>
 void launch_fwd_bb(const void* q, const void* k, const void* v, const int32_t* cu, const WorkList& wl,
                    int H, int Hk, int T, size_t grid, float scale_log2, void* o, float* lse,
-                   const BandArgs& bd, hipStream_t s) {
+                   const BandArgs& bd, const HostItems* hi, hipStream_t s) {
+  if constexpr (!BAND) {
+    if (hi != nullptr) {
+      attn_fwd_kernel<D, SPLIT, OutT, 2, BN, false><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse,
+          bd.cu_k, bd.T_k, bd.wl, bd.wr, *hi);
+      return;
+    }
+  }
   if (wl.tiles == nullptr)
-    attn_fwd_kernel<D, SPLIT, OutT, true, BN, BAND><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+    attn_fwd_kernel<D, SPLIT, OutT, 1, BN, BAND><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse,
-        bd.cu_k, bd.T_k, bd.wl, bd.wr);
+        bd.cu_k, bd.T_k, bd.wl, bd.wr, NoHostItems{});
   else
-    attn_fwd_kernel<D, SPLIT, OutT, false, BN, BAND><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
+    attn_fwd_kernel<D, SPLIT, OutT, 0, BN, BAND><<<dim3((unsigned)grid), kFwdThreads, 0, s>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, cu, wl, H, Hk, T, scale_log2, (OutT*)o, lse,
-        bd.cu_k, bd.T_k, bd.wl, bd.wr);
+        bd.cu_k, bd.T_k, bd.wl, bd.wr, NoHostItems{});
 }
 
 template <int D, bool SPLIT, typename OutT, int BN>
 void launch_fwd_bn(const void* q, const void* k, const void* v, const int32_t* cu, const WorkList& wl,
                    int H, int Hk, int T, size_t grid, float scale_log2, void* o, float* lse,
-                   const BandArgs& bd, hipStream_t s) {
-  if (bd.on) launch_fwd_bb<D, SPLIT, OutT, BN, true>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
-  else launch_fwd_bb<D, SPLIT, OutT, BN, false>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
+                   const BandArgs& bd, const HostItems* hi, hipStream_t s) {
+  if (bd.on) launch_fwd_bb<D, SPLIT, OutT, BN, true>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, hi, s);
+  else launch_fwd_bb<D, SPLIT, OutT, BN, false>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, hi, s);
 }
 
 template <int D, bool SPLIT, typename OutT>
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
                       const WorkList& wl, int H, int Hk, int T, size_t cap, float scale_log2, void* o,
-                      float* lse, bool short_keys, const BandArgs& bd, hipStream_t s) {
-  const size_t grid = cap * (size_t)H;
+                      float* lse, bool short_keys, const BandArgs& bd, const HostItems* hi, hipStream_t s) {
+  // host-listed items: exactly one workgroup per (item, head)
+  const size_t grid = (hi != nullptr ? (size_t)hi->n : cap) * (size_t)H;
   if (grid == 0) return hipSuccess;
-  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
-  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, s);
+  if (short_keys) launch_fwd_bn<D, SPLIT, OutT, 32>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, hi, s);
+  else launch_fwd_bn<D, SPLIT, OutT, 64>(q, k, v, cu, wl, H, Hk, T, grid, scale_log2, o, lse, bd, hi, s);
   return hipGetLastError();
+}
+
+// The work list of a small self-attention launch, from the validated host
+// mirror of cu_seqlens, in the planner's order (tile index descending,
+// segments in order within a tile index).  False when it does not fit
+// HostItems (then the device plans).
+bool list_items_on_host(const int32_t* h_cu, int32_t n_seg, int tile, HostItems* out) {
+  int mmax = 0;
+  for (int32_t b = 0; b < n_seg; ++b) {
+    const int32_t L = h_cu[b + 1] - h_cu[b];
+    if (L > 32768) return false;
+    mmax = std::max(mmax, (L + tile - 1) / tile);
+  }
+  int n = 0;
+  for (int m = mmax - 1; m >= 0; --m)
+    for (int32_t b = 0; b < n_seg; ++b) {
+      const int32_t L = h_cu[b + 1] - h_cu[b];
+      if ((L + tile - 1) / tile <= m) continue;
+      if (n >= kHostItemsMax) return false;
+      out->seg0[n] = h_cu[b];
+      out->len_m[n] = (L << 8) | m;
+      ++n;
+    }
+  out->n = n;
+  return true;
 }
 
 size_t fwd_workspace(int32_t T, int32_t n_seg) {
@@ -341,9 +393,14 @@ pvb_status fwd_call(const void* d_q, const void* d_k, const void* d_v, const int
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* count = static_cast<int32_t*>(workspace);
   int2* tiles = reinterpret_cast<int2*>(static_cast<char*>(workspace) + 256);
-  // small packs: the attention kernel decodes its items itself; otherwise
-  // the planner writes the list (and the status) first
-  const bool dec = decode_in_kernel(T, n_seg, kFwdBM, cap * (size_t)H);
+  // small self-attention packs with the host mirror: the items are listed on
+  // the host and passed with the launch; otherwise small packs decode their
+  // items in the kernel, and larger ones take the planner's list (the planner
+  // writes the list and the status first)
+  HostItems hitems;
+  const bool host_list = h_cu != nullptr && !bd.on && n_seg <= kDecodeMaxSeg &&
+                         list_items_on_host(h_cu, n_seg, kFwdBM, &hitems);
+  const bool dec = host_list || decode_in_kernel(T, n_seg, kFwdBM, cap * (size_t)H);
   if (!dec) {
     plan_tiles_kernel<<<1, kPlanThreads, 0, s>>>(d_cu, n_seg, T, kFwdBM, tiles, count, d_status);
     if (hipGetLastError() != hipSuccess) return PVB_E_HIP;
@@ -356,7 +413,8 @@ pvb_status fwd_call(const void* d_q, const void* d_k, const void* d_v, const int
   const bool split = precision == PVB_PREC_SPLIT, f32 = o_dtype == PVB_F32;
   hipError_t e;
 #define PVB_FWD(D_, S_, T_) \
-  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, H_kv, T, cap, sl2, d_o, d_lse, short_keys, bd, s)
+  e = launch_fwd<D_, S_, T_>(d_q, d_k, d_v, d_cu, wl, H, H_kv, T, cap, sl2, d_o, d_lse, short_keys, bd, \
+                            host_list ? &hitems : nullptr, s)
   if (d == 128) {
     if (split) { if (f32) PVB_FWD(128, true, float); else PVB_FWD(128, true, bf16); }
     else { if (f32) PVB_FWD(128, false, float); else PVB_FWD(128, false, bf16); }

@@ -371,6 +371,20 @@ struct KeyBand {
   }
 };
 
+// Work items listed on the host from the host mirror of cu_seqlens and
+// handed to the kernel with its launch arguments (read through the scalar
+// cache, no dependent memory round trip): item r is the tile m[r] of the
+// segment that starts at token seg0[r] and holds len[r] tokens, in the
+// planner's order.  Used for small self-attention launches when the mirror is
+// given; the kernel then does not read cu_seqlens.
+constexpr int kHostItemsMax = 448;
+struct HostItems {
+  int32_t n;
+  int32_t seg0[kHostItemsMax];
+  int32_t len_m[kHostItemsMax];   // len << 8 | m  (len <= 32768, m < 256)
+};
+struct NoHostItems {};
+
 // The item of workgroup tau: from the planner list, or decoded in place.
 template <int TILE, bool DECODE>
 __device__ __forceinline__ bool work_item(const WorkList& wl, const int32_t* __restrict__ cu, int T, int tau,

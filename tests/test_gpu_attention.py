@@ -299,3 +299,31 @@ def test_grouped_heads_rejects_uneven_groups():
     cu = torch.tensor([0, 8], dtype=torch.int32, device="cuda")
     with pytest.raises(pvb.PvbError):
         pvb.varlen_attn_fwd(q, k, k, cu)
+
+
+@pytest.mark.parametrize("lengths", [
+    [5, 3, 4],                              # host-listed items
+    [84, 0, 99, 460, 487, 1, 129],          # host-listed, zeros and tile edges
+    [130] * 240,                            # 480 tiles: more than the host list holds, device plan
+    [40000, 100],                           # a segment past 32768 tokens: device plan
+])
+def test_host_mirror_gives_the_same_forward(lengths):
+    """With the host mirror of cu_seqlens a small self-attention forward lists
+    its items on the host and passes them with the launch; O and LSE equal the
+    device-planned call bit for bit, and the oracle on one head."""
+    import torch
+
+    import packed_varlen_block_amd as pvb
+    say(f"fwd with/without the host mirror: {len(lengths)} segments, T {sum(lengths)}")
+    H, d = 2, 128
+    w = W.random_small(777, lengths, H=H, d=d, backward=False)
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    hc = host_cu(lengths)
+    cu = torch.tensor(hc).cuda()
+    o1, l1, s1 = pvb.varlen_attn_fwd(q, k, v, cu, h_cu=hc)
+    o2, l2, s2 = pvb.varlen_attn_fwd(q, k, v, cu)
+    pvb.check_status(s1)
+    pvb.check_status(s2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if sum(lengths) <= 20000:
+        compare_fwd(w, o1, l1, heads=[1])
