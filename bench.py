@@ -423,6 +423,7 @@ def short_pack_forward(torch, pvb, W, dev, stream, seed, n_sets=8, reps=200):
             "algorithmic_bytes": byts, "achieved_GBs": round(byts / (med * 1e-6) / 1e9, 1),
             "hbm_frac": round(byts / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "useful_tflops": round(F / (med * 1e-6) / 1e12, 2),
+            "traffic": measured_traffic("short_pack_fwd"),
             "device_planned": {"median_us": round(float(np.median(us_dev)), 2),
                                "p10_us": round(float(np.percentile(us_dev, 10)), 2),
                                "p90_us": round(float(np.percentile(us_dev, 90)), 2)}}
