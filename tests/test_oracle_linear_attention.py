@@ -247,3 +247,177 @@ def test_grouped_heads_equal_repeated_heads():
     assert np.array_equal(o, o2) and np.array_equal(fin, fin2)
     with pytest.raises(ValueError):
         LA.gated_delta_varlen(q, k, v[:, :5], g[:, :5], beta[:, :5], cu, 0.4)
+
+
+# ----------------------------------------------------------- O12 (backward)
+
+def _loss_seg(q, k, v, g, beta, scale, do, s0, dsf):
+    o, s = LA.gated_delta_segment(q, k, v, g, beta, scale, s0)
+    return float(np.sum(o * do) + np.sum(s * dsf))
+
+
+def _bwd_case(seed, L=6, dk=4, dv=3, gmin=-0.5):
+    r = np.random.default_rng(seed)
+    q = r.normal(size=(L, dk))
+    k = r.normal(size=(L, dk)) / np.sqrt(dk)
+    v = r.normal(size=(L, dv))
+    g = r.uniform(gmin, 0.0, size=L)
+    beta = r.uniform(0.1, 1.0, size=L)
+    s0 = r.normal(size=(dk, dv)) * 0.5
+    do = r.normal(size=(L, dv))
+    dsf = r.normal(size=(dk, dv))
+    return q, k, v, g, beta, s0, do, dsf
+
+
+def _finite_differences(args, scale, h=1e-6):
+    """Central differences of the loss for every entry of q, k, v, g, beta, s0."""
+    q, k, v, g, beta, s0, do, dsf = args
+    out = []
+    for idx in range(6):
+        base = [q, k, v, g, beta, s0]
+        x = base[idx]
+        grad = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            bp, bm = list(base), list(base)
+            bp[idx], bm[idx] = xp, xm
+            lp = _loss_seg(bp[0], bp[1], bp[2], bp[3], bp[4], scale, do, bp[5], dsf)
+            lm = _loss_seg(bm[0], bm[1], bm[2], bm[3], bm[4], scale, do, bm[5], dsf)
+            grad[pos] = (lp - lm) / (2 * h)
+        out.append(grad)
+    return out
+
+
+def _order(r):
+    """(dq, dk, dv, dg, dbeta, ds0) -> the input order q, k, v, g, beta, s0."""
+    return [r[0], r[1], r[2], r[3], r[4], r[5]]
+
+
+def test_backward_matches_finite_differences():
+    for seed in range(3):
+        args = _bwd_case(10 + seed)
+        q, k, v, g, beta, s0, do, dsf = args
+        got = _order(LA.gated_delta_segment_backward(q, k, v, g, beta, 0.6, do, s0, dsf))
+        fd = _finite_differences(args, 0.6)
+        for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), got, fd):
+            assert np.abs(a - b).max() <= 1e-7 * max(1.0, np.abs(b).max()), name
+
+
+def test_backward_matches_torch_autograd():
+    """torch fp64 autograd through the token loop (a library differentiation
+    of the forward, not of the backward's formulas)."""
+    torch = pytest.importorskip("torch")
+    args = _bwd_case(20, L=17, dk=8, dv=5)
+    q, k, v, g, beta, s0, do, dsf = args
+    T = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, g, beta, s0)]
+    tq, tk, tv, tg, tb, ts0 = T
+    S = ts0
+    loss = torch.zeros((), dtype=torch.float64)
+    for t in range(q.shape[0]):
+        S = torch.exp(tg[t]) * S
+        u = tb[t] * (tv[t] - S.T @ tk[t])
+        S = S + torch.outer(tk[t], u)
+        loss = loss + (0.3 * (S.T @ tq[t])) @ torch.tensor(do[t])
+    loss = loss + (S * torch.tensor(dsf)).sum()
+    loss.backward()
+    got = _order(LA.gated_delta_segment_backward(q, k, v, g, beta, 0.3, do, s0, dsf))
+    for name, a, t in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), got, T):
+        assert np.allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-12), name
+
+
+def test_backward_pure_decay_closed_forms():
+    """beta = 0: o_t = scale e^{c_t} S0^T q_t with c_t = g_0 + .. + g_t and the
+    final state e^{c_L} S0, so dq_t = scale e^{c_t} S0 do_t, dv = 0, dk = 0,
+    dS0 = sum_t scale e^{c_t} q_t do_t^T + e^{c_L} dS_final and
+    dg_t = sum_{t' >= t} scale e^{c_t'} (S0^T q_t').do_t' + e^{c_L} <S0, dS_final>."""
+    q, k, v, g, _, s0, do, dsf = _bwd_case(30, L=7)
+    L = q.shape[0]
+    dq, dk, dv, dg, dbeta, ds0 = LA.gated_delta_segment_backward(q, k, v, g, np.zeros(L), 0.5, do, s0, dsf)
+    c = np.cumsum(g)
+    for t in range(L):
+        assert np.allclose(dq[t], 0.5 * np.exp(c[t]) * s0 @ do[t], rtol=1e-12, atol=1e-14)
+    assert not dv.any() and np.abs(dk).max() == 0.0
+    want_ds0 = sum(0.5 * np.exp(c[t]) * np.outer(q[t], do[t]) for t in range(L)) + np.exp(c[-1]) * dsf
+    assert np.allclose(ds0, want_ds0, rtol=1e-12, atol=1e-14)
+    term = [0.5 * np.exp(c[t]) * (s0.T @ q[t]) @ do[t] for t in range(L)]
+    for t in range(L):
+        want = sum(term[t:]) + np.exp(c[-1]) * np.sum(s0 * dsf)
+        assert np.isclose(dg[t], want, rtol=1e-12, atol=1e-13)
+    # dbeta_t = (dS_t^T k_t) . (v_t - e^{c_t} S0^T k_t), dS_t the gradient of S_t
+    for t in range(L):
+        dSt = sum(0.5 * np.exp(c[u] - c[t]) * np.outer(q[u], do[u]) for u in range(t, L)) \
+            + np.exp(c[-1] - c[t]) * dsf
+        assert np.isclose(dbeta[t], (dSt.T @ k[t]) @ (v[t] - np.exp(c[t]) * s0.T @ k[t]), rtol=1e-11, atol=1e-13)
+
+
+def test_backward_planted_mistakes_fail():
+    """Three plausible slips in the backward, each caught by finite differences."""
+    args = _bwd_case(40)
+    q, k, v, g, beta, s0, do, dsf = args
+    fd = _finite_differences(args, 0.6)
+
+    def mutant(kind):
+        L, dk_ = k.shape
+        S = s0.copy()
+        keep = []
+        for t in range(L):
+            Sd = np.exp(g[t]) * S
+            pred = Sd.T @ k[t]
+            u = beta[t] * (v[t] - pred)
+            keep.append((S, Sd, pred, u, Sd + np.outer(k[t], u)))
+            S = keep[-1][4]
+        dq, dk = np.zeros_like(q), np.zeros_like(k)
+        dS = dsf.copy()
+        for t in range(L - 1, -1, -1):
+            Sp, Sd, pred, u, St = keep[t]
+            dS = dS + 0.6 * np.outer(q[t], do[t])
+            dq[t] = 0.6 * ((Sp if kind == "read_before_write" else St) @ do[t])
+            du = dS.T @ k[t]
+            dk[t] = dS @ u
+            dpred = -beta[t] * du
+            dSd = dS + np.outer(k[t], dpred)
+            if kind != "no_pred_term":
+                dk[t] += Sd @ dpred
+            dS = dSd if kind == "no_decay" else np.exp(g[t]) * dSd
+        return dq, dk
+    for kind in ("read_before_write", "no_pred_term", "no_decay"):
+        mq, mk = mutant(kind)
+        bad = np.abs(mq - fd[0]).max() > 1e-5 or np.abs(mk - fd[1]).max() > 1e-5
+        assert bad, kind
+
+
+def test_backward_varlen_isolation_empty_slices_and_grouped_heads():
+    """Slices are independent (NaN in one slice leaves the others' gradients
+    exact), an empty slice passes its final-state gradient through to its
+    initial state, and grouped heads equal the call with repeated query/key
+    heads, summed over each group."""
+    r = np.random.default_rng(50)
+    lengths = [5, 0, 7, 3]
+    T, H, Hk, dk, dv = sum(lengths), 4, 2, 4, 3
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q = r.normal(size=(T, Hk, dk))
+    k = r.normal(size=(T, Hk, dk)) / 2
+    v = r.normal(size=(T, H, dv))
+    g = r.uniform(-0.4, 0, size=(T, H))
+    beta = r.uniform(0.1, 1, size=(T, H))
+    h0 = r.normal(size=(4, H, dk, dv))
+    do = r.normal(size=(T, H, dv))
+    dht = r.normal(size=(4, H, dk, dv))
+    dq, dk_, dv_, dg, db, dh0 = LA.gated_delta_varlen_backward(q, k, v, g, beta, cu, 0.5, do, h0, dht)
+    assert np.array_equal(dh0[1], dht[1])                       # the empty slice
+    # repeated heads, summed per group
+    G = H // Hk
+    qr, kr = np.repeat(q, G, axis=1), np.repeat(k, G, axis=1)
+    rq, rk, rv, rg, rb, rh = LA.gated_delta_varlen_backward(qr, kr, v, g, beta, cu, 0.5, do, h0, dht)
+    assert np.allclose(dq, rq.reshape(T, Hk, G, dk).sum(2), rtol=1e-13, atol=1e-13)
+    assert np.allclose(dk_, rk.reshape(T, Hk, G, dk).sum(2), rtol=1e-13, atol=1e-13)
+    assert np.array_equal(dv_, rv) and np.array_equal(dg, rg) and np.array_equal(dh0, rh)
+    # NaN in slice 2 (tokens 5..11) changes nothing in slices 0 and 3
+    v2 = v.copy()
+    v2[6, :, 0] = np.nan
+    n = LA.gated_delta_varlen_backward(q, k, v2, g, beta, cu, 0.5, do, h0, dht)
+    for a, b in zip(n, (dq, dk_, dv_, dg, db)):
+        assert np.array_equal(a[:5], b[:5]) and np.array_equal(a[12:], b[12:])
+    assert np.array_equal(n[5][[0, 1, 3]], dh0[[0, 1, 3]])
