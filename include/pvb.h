@@ -421,6 +421,40 @@ pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void*
                                    float scale, const float* d_h0, void* d_o, int32_t o_dtype,
                                    float* d_ht, int32_t* d_status, void* stream);
 
+/* Backward of pvb_gated_delta_fwd_gqa: the gradients of
+ *   sum_t o_t . dO_t + sum_b <ht[b], dht[b]>
+ * with respect to q, k, v, g, beta and the initial states, slice by slice
+ * (nothing crosses a boundary; "Packing与 FlashAttention Varlen", section 6).
+ * Exact in exact arithmetic: reverse-mode differentiation of the recurrence of
+ * pvb_gated_delta_fwd.  The call first recomputes the forward, storing each
+ * 64-token chunk's starting state and solved update in the workspace, then
+ * walks every (slice, value head) back from its last chunk, carrying the
+ * gradient of the state.
+ *   d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0
+ *                  as in pvb_gated_delta_fwd_gqa (d_h0 nullable)
+ *   d_dout         bf16 [T, H, d] gradient of O                         (device)
+ *   d_dht          fp32 [n_seg, H, d, d] gradient of the final states, nullable
+ *                  (zero)                                              (device)
+ *   d_dq, d_dk     out fp32 [T, H_k, d]; a query/key head shared by several
+ *                  value heads gets the sum (then the call clears them first
+ *                  and adds with atomics, so their summation order varies)
+ *   d_dv           out [T, H, d], bf16 or fp32 per grad_dtype
+ *   d_dg, d_dbeta  out fp32 [T, H]
+ *   d_dh0          out fp32 [n_seg, H, d, d], nullable
+ *   workspace      >= pvb_gated_delta_bwd_workspace_bytes(T, H, n_seg) bytes
+ *                  (checkpoints: 96 KB per 64-token chunk and head; scratch:
+ *                  288 KB per slice and head)                          (device)
+ * d = 128.  Device-detected error: PVB_E_BAD_CU_SEQLENS (then no gradient is
+ * written). */
+size_t pvb_gated_delta_bwd_workspace_bytes(int32_t T, int32_t H, int32_t n_seg);
+pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                               const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                               int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d, float scale,
+                               const float* d_h0, const void* d_dout, const float* d_dht, float* d_dq,
+                               float* d_dk, void* d_dv, float* d_dg, float* d_dbeta, float* d_dh0,
+                               int32_t grad_dtype, void* workspace, size_t workspace_bytes,
+                               int32_t* d_status, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);
 

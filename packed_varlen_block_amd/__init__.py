@@ -37,7 +37,8 @@ STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "P
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
            "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
            "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
-           "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa",
+           "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa", "pvb_gated_delta_bwd",
+           "pvb_gated_delta_bwd_workspace_bytes",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_varlen_attn_bwd_noalloc", "pvb_status_string", "pvb_version")
 PVB_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of pvb_varlen_attn_bwd_noalloc
@@ -76,6 +77,10 @@ def lib() -> ctypes.CDLL:
                                               P, P, P, I32, I32, P, SZ, P, P]
         L.pvb_varlen_attn_bwd_noalloc.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, F,
                                                   P, P, P, I32, I32, P, P]
+        L.pvb_gated_delta_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, P, P, P, P, P,
+                                          P, P, I32, P, SZ, P, P]
+        L.pvb_gated_delta_bwd_workspace_bytes.argtypes = [I32, I32, I32]
+        L.pvb_gated_delta_bwd_workspace_bytes.restype = SZ
         L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, P]
         L.pvb_gated_delta_fwd_gqa.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, I32, P, P, P]
         L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
@@ -89,6 +94,7 @@ def lib() -> ctypes.CDLL:
                      "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
                      "pvb_varlen_attn_bwd_noalloc",
                      "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd", "pvb_gated_delta_fwd",
+                     "pvb_gated_delta_bwd",
                      "pvb_gated_delta_fwd_gqa"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
@@ -639,3 +645,57 @@ def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=N
                                        _stream(dev))
     _check(rc, "gated_delta_fwd")
     return out, ht, status
+
+
+def gated_delta_bwd_workspace_bytes(T: int, H: int, n_seg: int) -> int:
+    return int(lib().pvb_gated_delta_bwd_workspace_bytes(T, H, n_seg))
+
+
+def gated_delta_bwd(q, k, v, g, beta, cu, do, h_cu=None, scale=None, initial_state=None, dht=None,
+                    grad_dtype=None, dh0=True, workspace=None, status=None):
+    """Backward of gated_delta_fwd: the gradients of sum(O * do) + sum(ht * dht)
+    (dht: gradient of the final states, optional).  Returns (dq, dk [T, H_k, 128]
+    fp32, dv [T, H, 128] in grad_dtype (fp32 by default), dg, dbeta [T, H] fp32,
+    dh0 [B, H, 128, 128] fp32 or None, status)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, dim=3)
+    _need(v, "v", torch.bfloat16, dim=3)
+    T, Hk, d = q.shape
+    H = v.shape[1]
+    dev = q.device
+    _need(k, "k", torch.bfloat16, (T, Hk, d), dev)
+    _need(v, "v", shape=(T, H, d), dev=dev)
+    _need(do, "do", torch.bfloat16, (T, H, d), dev)
+    if Hk <= 0 or H % Hk != 0:
+        raise PvbError(1, "the value heads must be a multiple of the query/key heads")
+    _need(g, "g", torch.float32, (T, H), dev)
+    _need(beta, "beta", torch.float32, (T, H), dev)
+    n_seg = _cu_arg(cu, "cu", dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n_seg, H, d, d), dev)
+    if dht is not None:
+        _need(dht, "dht", torch.float32, (n_seg, H, d, d), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
+    gcode = _dtype_code(grad_dtype)
+    dq = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((T, H, d), dtype=grad_dtype, device=dev)
+    dg = torch.empty((T, H), dtype=torch.float32, device=dev)
+    db = torch.empty((T, H), dtype=torch.float32, device=dev)
+    dh = torch.empty((max(n_seg, 0), H, d, d), dtype=torch.float32, device=dev) if dh0 else None
+    nbytes = gated_delta_bwd_workspace_bytes(T, H, n_seg)
+    workspace = _workspace_arg(workspace, nbytes, dev)
+    status = _status_arg(status, dev)
+    hc = None
+    if h_cu is not None:
+        hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
+        if hc.size != n_seg + 1:
+            raise PvbError(1, "h_cu must have B+1 entries")
+    rc = lib().pvb_gated_delta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg, T, H,
+                                   Hk, d, scale, _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh) if dh is not None and dh.numel() else None,
+                                   gcode, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _ptr(status), _stream(dev))
+    _check(rc, "gated_delta_bwd")
+    return dq, dk, dv, dg, db, dh, status

@@ -358,3 +358,27 @@ def test_noalloc_backward_refuses_sizes_beyond_its_scratch_on_host():
     assert call(8, 4, n_seg=pvb.PVB_MAX_COUNT + 1) == 3
     assert call(262144, 32) == 5                                       # the documented examples
     assert pvb.workspace_bytes(131072, 32, 128, 1, True) <= cap
+
+
+def test_gated_delta_backward_host_side_errors():
+    L = pvb.lib()
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=2, H_k=2, d=128,
+              scale=0.125, h0=None, do=FAKE, dht=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, db=FAKE, dh0=None,
+              gd=1, ws=FAKE, ws_bytes=16, status=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.pvb_gated_delta_bwd(*a.values(), None)
+    assert call() == 5                                # the workspace is too small
+    assert call(d=64) == 6
+    assert call(H=0) == 1
+    assert call(H_k=3) == 1
+    assert call(gd=4) == 1
+    assert call(scale=0.0) == 1
+    for name in ("q", "k", "v", "g", "b", "do", "dq", "dk", "dv", "dg", "db", "cu", "status"):
+        assert call(**{name: None}) == 1, name
+    assert call(n_seg=pvb.PVB_MAX_COUNT + 1) == 3
+    assert call(T=2 ** 24, H=2 ** 7, H_k=2 ** 7) == 6
+    bad = np.array([0, 9], np.int32)
+    assert call(h_cu=bad.ctypes.data, ws_bytes=1 << 40) == 4
+    assert pvb.gated_delta_bwd_workspace_bytes(8, 2, 1) > 0 and pvb.gated_delta_bwd_workspace_bytes(-1, 2, 1) == 0

@@ -1,0 +1,112 @@
+"""GPU parity of the gated delta rule's backward (pvb_gated_delta_bwd) against
+the fp64 oracle O12: dq, dk, dv, dg, dbeta and the initial-state gradient."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import linear_attention as LA
+from tests.parity import host_cu, say
+
+pytestmark = pytest.mark.gpu
+
+# Bar (per tensor, absolute, against fp64): the kernels work in fp32 with
+# matrix-core products of two-part bf16 operands (about 16 significant bits),
+# as the forward does, so the bar is the forward's: 1e-3 of the tensor's
+# largest magnitude (at least 1e-3).  A bf16 dv also carries its own rounding,
+# half an ulp of its largest value.
+TOL = 1e-3
+BF16_ULP = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import packed_varlen_block_amd  # noqa: F401  (fails loudly if libpvb.so is missing)
+
+
+def _dev(x):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _check(name, got, ref, extra=0.0):
+    tol = TOL * max(1.0, float(np.abs(ref).max(initial=0.0))) + extra
+    err = np.abs(got - ref)
+    mx = float(err.max(initial=0.0))
+    say(f"  {name}: max-abs {mx:.3e}  (bar {tol:.2e}, max|ref| {float(np.abs(ref).max(initial=0.0)):.2e})")
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    assert mx <= tol, f"{name}: max-abs {mx:.3e} > {tol:.3e}"
+
+
+def _case(seed, lengths, H, Hk=None, g_range=(-0.1, 0.0), beta_range=(0.05, 1.0), h0=False, dht=False,
+          grad_dtype="f32", scale=None):
+    import torch
+
+    import packed_varlen_block_amd as pvb
+    w = W.random_gated_delta(seed, lengths, H, g_range=g_range, beta_range=beta_range, initial_state=h0, Hk=Hk)
+    T, d = int(np.sum(lengths)), 128
+    Hk = H if Hk is None else Hk
+    r = np.random.default_rng(seed + 1)
+    do = W.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32))
+    dsf = (r.standard_normal((len(lengths), H, d, d)) * 0.1).astype(np.float32) if dht else None
+    hc = host_cu(lengths)
+    gd = torch.float32 if grad_dtype == "f32" else torch.bfloat16
+    dq, dk, dv, dg, db, dh0, st = pvb.gated_delta_bwd(
+        _dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]), _dev(w["beta"]), _dev(hc), _dev(do), h_cu=hc,
+        scale=scale, initial_state=_dev(w["h0"]) if h0 else None, dht=_dev(dsf) if dht else None, grad_dtype=gd)
+    pvb.check_status(st)
+    f = W.bf16_bits_to_f64
+    sc = 1.0 / np.sqrt(d) if scale is None else scale
+    ref = LA.gated_delta_varlen_backward(f(w["q"]), f(w["k"]), f(w["v"]), w["g"].astype(np.float64),
+                                         w["beta"].astype(np.float64), hc, sc, f(do),
+                                         w["h0"].astype(np.float64) if h0 else None,
+                                         dsf.astype(np.float64) if dht else None)
+    got = [x.double().cpu().numpy() for x in (dq, dk, dv, dg, db)]
+    for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta"), got, ref[:5]):
+        extra = BF16_ULP * float(np.abs(b).max(initial=0.0)) if (name == "dv" and grad_dtype == "bf16") else 0.0
+        _check(name, a, b, extra)
+    _check("dh0", dh0.double().cpu().numpy(), ref[5])
+
+
+@pytest.mark.parametrize("lengths", [[1], [5], [63], [64], [65], [130, 0, 64, 7], [200]])
+def test_backward_small(lengths):
+    say(f"gated delta bwd: lengths {lengths}")
+    _case(400 + len(lengths) + sum(lengths), lengths, H=2)
+
+
+def test_backward_states_and_grouped_heads():
+    say("gated delta bwd: initial states, final-state gradient, 4 value heads over 2 query/key heads")
+    _case(501, [70, 0, 129, 3], H=4, Hk=2, h0=True, dht=True)
+
+
+@pytest.mark.parametrize("g_range,beta_range", [((0.0, 0.0), (0.05, 1.0)), ((-1.0, 0.0), (0.9, 1.0)),
+                                                ((-8.0, -4.0), (0.05, 0.2))])
+def test_backward_gate_ranges(g_range, beta_range):
+    say(f"gated delta bwd: gates {g_range}, beta {beta_range}")
+    _case(502, [150, 40], H=2, g_range=g_range, beta_range=beta_range, h0=True, dht=True)
+
+
+def test_backward_bf16_dv_and_scale():
+    say("gated delta bwd: bf16 dv, scale 0.3")
+    _case(503, [100, 28], H=2, grad_dtype="bf16", scale=0.3, dht=True)
+
+
+def test_backward_long_slice_grouped():
+    say("gated delta bwd: a 2100-token slice beside short ones, 4 value heads over 2, states")
+    _case(504, [2100, 300, 0, 65], H=4, Hk=2, h0=True, dht=True)
+
+
+def test_backward_bad_cu_writes_nothing():
+    import torch
+
+    import packed_varlen_block_amd as pvb
+    say("gated delta bwd: a bad device cu_seqlens sets the status and writes no gradient")
+    w = W.random_gated_delta(505, [10, 6], 2)
+    bad = torch.tensor([0, 12, 9], dtype=torch.int32).cuda()      # decreasing
+    do = _dev(W.f32_to_bf16_bits(np.ones((16, 2, 128), np.float32)))
+    dq, dk, dv, dg, db, dh0, st = pvb.gated_delta_bwd(_dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]),
+                                                      _dev(w["beta"]), bad, do)
+    assert int(st.item()) == 4                                     # PVB_E_BAD_CU_SEQLENS
