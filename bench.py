@@ -362,6 +362,8 @@ def main():
         out["gated_delta"] = gated_delta(torch, pvb, W, dev, stream, a.seed)
         out["gated_delta_grouped"] = gated_delta(torch, pvb, W, dev, stream, a.seed, Hk=16)
         note("gated delta done")
+        out["gated_delta_backward"] = gated_delta_backward(torch, pvb, W, dev, stream, a.seed)
+        note("gated delta backward done")
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
@@ -694,6 +696,48 @@ def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5, Hk=None):
             "longest_chain_chunks": chain, "us_per_chunk": round(ms * 1e3 / chain, 3),
             "algorithmic_bytes": byts, "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def gated_delta_backward(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
+    """Backward of the gated delta rule over the long mixed pack (T=32768: one
+    16384-token slice, then slices of 16-1024), H=32, d=128, fp32 gradients,
+    dO ~ N(0,1) bf16 and a final-state gradient; inputs as in gated_delta.  One
+    call recomputes the forward (storing chunk checkpoints) and walks the
+    chunks back; reported per chunk of the longest slice's chain, median of reps."""
+    lengths = W.lengths_cfg4(seed)
+    T, B = int(lengths.sum()), len(lengths)
+    g = torch.Generator(device=dev).manual_seed(seed + 13)
+
+    def unit(*shape):
+        x = torch.randn(shape, generator=g, device=dev)
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    q, k = unit(T, H, d), unit(T, H, d)
+    v = torch.randn((T, H, d), generator=g, device=dev).to(torch.bfloat16)
+    gg = torch.rand((T, H), generator=g, device=dev) * -0.1
+    bb = torch.rand((T, H), generator=g, device=dev) * 0.95 + 0.05
+    do = torch.randn((T, H, d), generator=g, device=dev).to(torch.bfloat16)
+    dht = torch.randn((B, H, d, d), generator=g, device=dev) * 0.1
+    hc = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cu = torch.from_numpy(hc).to(dev)
+    ws = torch.empty(pvb.gated_delta_bwd_workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pvb.gated_delta_bwd(q, k, v, gg, bb, cu, do, dht=dht, workspace=ws, status=st)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pvb.gated_delta_bwd(q, k, v, gg, bb, cu, do, dht=dht, workspace=ws, status=st)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    pvb.check_status(st)
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    chain = int(-(-int(lengths.max()) // 64))
+    return {"workload": "gdn_bwd_long_mixed_T32768_H32_d128", "segments": B, "ms": round(ms, 4),
+            "longest_chain_chunks": chain, "us_per_chunk": round(ms * 1e3 / chain, 3),
+            "workspace_bytes": int(ws.numel())}
 
 
 def packed_loss(torch, pvb, dev, stream, seed, C=8192, V=32768, reps=20):

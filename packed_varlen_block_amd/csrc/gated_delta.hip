@@ -568,9 +568,10 @@ struct exact_bf16<HView> : std::true_type {};
 // acc += the 32x32 block (m0, n0) of A B over k < K (a multiple of 16): lane
 // l holds A[m0 + l%32][k0 + 8(l/32) + e] and B[k0 + 8(l/32) + e][n0 + l%32];
 // result element i of lane l is row m0 + crow(i, l/32), column n0 + l%32.
-template <typename VA, typename VB>
-__device__ __forceinline__ f32x16 gd_block_product(const VA& a, const VB& b, int m0, int n0, int K, f32x16 acc) {
+template <int K, typename VA, typename VB>
+__device__ __forceinline__ f32x16 gd_block_product(const VA& a, const VB& b, int m0, int n0, f32x16 acc) {
   const int lane = threadIdx.x & 63, c = lane & 31, hg = lane >> 5;
+#pragma unroll 2
   for (int k0 = 0; k0 < K; k0 += 16) {
     float xa[8], xb[8];
 #pragma unroll
@@ -687,8 +688,8 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
         const int bi = jb == 0 ? 0 : (jb == 3 ? 0 : 1), bj = jb == 1 ? 0 : (jb == 3 ? 1 : bi);
         float (*dst)[kLP] = isq ? sm.p : sm.ah;
         f32x16 acc = {};
-        if (jb != 3) acc = isq ? gd_block_product(Qv, KTv, 32 * bi, 32 * bj, kGdD, acc)
-                               : gd_block_product(Kv, KTv, 32 * bi, 32 * bj, kGdD, acc);
+        if (jb != 3) acc = isq ? gd_block_product<kGdD>(Qv, KTv, 32 * bi, 32 * bj, acc)
+                               : gd_block_product<kGdD>(Kv, KTv, 32 * bi, 32 * bj, acc);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 32 * bi + crow(i, hg), cc = 32 * bj + c;
@@ -699,8 +700,8 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
       } else {
         const int jj = job - 8, isq = jj >= 8, blk = jj & 7, rb = blk >> 2, cb = blk & 3;
         f32x16 acc = {};
-        acc = isq ? gd_block_product(Qv, S0v, 32 * rb, 32 * cb, kGdD, acc)
-                  : gd_block_product(Kv, S0v, 32 * rb, 32 * cb, kGdD, acc);
+        acc = isq ? gd_block_product<kGdD>(Qv, S0v, 32 * rb, 32 * cb, acc)
+                  : gd_block_product<kGdD>(Kv, S0v, 32 * rb, 32 * cb, acc);
         float* dst = isq ? s_QS : s_KS;
 #pragma unroll
         for (int i = 0; i < 16; ++i) dst[(32 * rb + crow(i, hg)) * kGdD + 32 * cb + c] = acc[i];
@@ -714,49 +715,75 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
       for (int cc = c0; cc < c0 + 32; ++cc)
         s_X[r * kGdD + cc] = r < n ? (float)Vp[(size_t)r * H * kGdD + cc] - sm.eg[r] * s_KS[r * kGdD + cc] : 0.f;
     }
+    // dU in registers: wave w holds the two 32-row blocks of its 32 columns in
+    // the C layout (rows 32 rb + crow(i, hg), column 32 w + c)
+    f32x16 du[2];
     {
       const FView PTv{&sm.p[0][0], 1, kLP, kGdC, kGdC};                 // P^T
-      for (int job = w; job < 8; job += 4) {
-        const int rb = job >> 2, cb = job & 3;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
         f32x16 a1 = {}, a2 = {};
-        a1 = gd_block_product(PTv, dOv, 32 * rb, 32 * cb, kGdC, a1);
-        a2 = gd_block_product(Kv, dSv, 32 * rb, 32 * cb, kGdD, a2);
+        a1 = gd_block_product<kGdC>(PTv, dOv, 32 * rb, 32 * w, a1);
+        a2 = gd_block_product<kGdD>(Kv, dSv, 32 * rb, 32 * w, a2);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * rb + crow(i, hg);
-          s_dR[r * kGdD + 32 * cb + c] = scale * a1[i] + sm.dec[r] * a2[i];
-        }
+        for (int i = 0; i < 16; ++i) du[rb][i] = scale * a1[i] + sm.dec[32 * rb + crow(i, hg)] * a2[i];
       }
     }
-    __syncthreads();
 
-    // ---- dR = (I + A)^-T dU, A = diag(beta) Ah: wave w holds columns 32w + c,
-    // lane half hg rows 32hg .. 32hg + 31; row j is final when reached from
-    // the bottom, and every row above it subtracts A_ji dR_j
-    {
-      const int col = 32 * w + c;
-      float x[32];
+    // ---- dR = (I + A)^-T dU, A = diag(beta) Ah, in the C layout, blocked by
+    // 32 rows from the bottom: the lower block's triangle, the upper block's
+    // update by the matrix cores, the upper block's triangle.  Inside a block,
+    // row jj is final when reached from the block's end; the lane holding it
+    // hands it across the half-waves and every row above it subtracts A_(jj, row)
+    // times it.
+    auto triangle_t = [&](auto rb_tag) {
+      constexpr int RB = decltype(rb_tag)::value;
 #pragma unroll
-      for (int r = 0; r < 32; ++r) x[r] = s_dR[(32 * hg + r) * kGdD + col];
-#pragma clang loop unroll(full)
-      for (int j = kGdC - 1; j > 0; --j) {
-        const int jh = j >> 5, jr = j & 31;
-        const float mine = x[jr];
-        const float other = swap_halves(mine);
-        const float rj = jh == hg ? mine : other;
-        const float bj = sm.beta[j];
-        if (hg < jh) {
+      for (int jj = 31; jj > 0; --jj) {
+        const int ij = 4 * (jj >> 3) + (jj & 3);    // element index of row jj
+        const bool own = ((jj >> 2) & 1) == hg;
+        const float x = du[RB][ij];
+        const float other = swap_halves(x);
+        const float rj = (own ? x : other) * sm.beta[32 * RB + jj];
 #pragma unroll
-          for (int r = 0; r < 32; ++r) x[r] -= bj * sm.ah[j][r] * rj;
-        } else if (hg == jh) {
-#pragma unroll
-          for (int r = 0; r < 32; ++r)
-            if (r < jr) x[r] -= bj * sm.ah[j][32 * hg + r] * rj;
+        for (int m = 0; m < 4; ++m) {
+          if (8 * m >= jj) continue;                  // every row of the group is at or below jj
+          const float4 a4 = *(const float4*)&sm.ah[32 * RB + jj][32 * RB + 8 * m + 4 * hg];
+          const int r0 = 8 * m + 4 * hg;
+          if (r0 + 0 < jj) du[RB][4 * m + 0] -= a4.x * rj;
+          if (r0 + 1 < jj) du[RB][4 * m + 1] -= a4.y * rj;
+          if (r0 + 2 < jj) du[RB][4 * m + 2] -= a4.z * rj;
+          if (r0 + 3 < jj) du[RB][4 * m + 3] -= a4.w * rj;
         }
       }
+    };
+    triangle_t(std::integral_constant<int, 1>{});
+    {
+      // upper rows i: dU_i -= sum_{j in the lower block} A_ji dR_j; the lower
+      // block is the B operand straight from its C layout (k-step s: elements
+      // 8s + e, rows 32 + kpos(s, e, hg)), A_ji read in that order
 #pragma unroll
-      for (int r = 0; r < 32; ++r) s_dR[(32 * hg + r) * kGdD + col] = x[r];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float xa[8], xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 + kpos(s2, e, hg);
+          xa[e] = -sm.beta[j] * sm.ah[j][c];
+          xb[e] = du[1][8 * s2 + e];
+        }
+        bf16x8 ah, al, bh, bl;
+        split8(xa, ah, al);
+        split8(xb, bh, bl);
+        du[0] = mfma32(ah, bh, du[0]);
+        du[0] = mfma32(ah, bl, du[0]);
+        du[0] = mfma32(al, bh, du[0]);
+      }
     }
+    triangle_t(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_dR[(32 * rb + crow(i, hg)) * kGdD + 32 * w + c] = du[rb][i];
     __syncthreads();
 
     // ---- dV = diag(beta) dR (stored), dKS = -diag(G) dV, and the per-row sums
@@ -800,15 +827,15 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
         if (job < 8) {
           const int rb = job >> 2, cb = job & 3;
           f32x16 acc = {};
-          acc = gd_block_product(Uv, dSTv, 32 * rb, 32 * cb, kGdD, acc);
+          acc = gd_block_product<kGdD>(Uv, dSTv, 32 * rb, 32 * cb, acc);
 #pragma unroll
           for (int i = 0; i < 16; ++i) s_dKt[(32 * rb + crow(i, hg)) * kGdD + 32 * cb + c] = acc[i];
         } else {
           const int jj = job - 8, isp = jj >= 4, jb = jj & 3;
           const int bi = jb == 0 ? 0 : (jb == 3 ? 0 : 1), bj = jb == 1 ? 0 : (jb == 3 ? 1 : bi);
           f32x16 acc = {};
-          if (jb != 3) acc = isp ? gd_block_product(dOv, UTv, 32 * bi, 32 * bj, kGdD, acc)
-                                 : gd_block_product(dRv, UTv, 32 * bi, 32 * bj, kGdD, acc);
+          if (jb != 3) acc = isp ? gd_block_product<kGdD>(dOv, UTv, 32 * bi, 32 * bj, acc)
+                                 : gd_block_product<kGdD>(dRv, UTv, 32 * bi, 32 * bj, acc);
           float* dst = isp ? s_dP : s_dA;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -830,8 +857,8 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
       for (int job = w; job < 16; job += 4) {
         const int rb = job >> 2, cb = job & 3;
         f32x16 a1 = {}, a2 = {};
-        a1 = gd_block_product(KTv, dKSv, 32 * rb, 32 * cb, kGdC, a1);
-        a2 = gd_block_product(QTv, GdOv, 32 * rb, 32 * cb, kGdC, a2);
+        a1 = gd_block_product<kGdC>(KTv, dKSv, 32 * rb, 32 * cb, a1);
+        a2 = gd_block_product<kGdC>(QTv, GdOv, 32 * rb, 32 * cb, a2);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int e = (32 * rb + crow(i, hg)) * kGdD + 32 * cb + c;
@@ -899,13 +926,13 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
         const int rb = (job & 7) >> 2, cb = job & 3;
         f32x16 a1 = {}, a2 = {};
         if (isq) {
-          a1 = gd_block_product(dOv, S0Tv, 32 * rb, 32 * cb, kGdD, a1);
-          a2 = gd_block_product(Nv, Kv, 32 * rb, 32 * cb, kGdC, a2);
+          a1 = gd_block_product<kGdD>(dOv, S0Tv, 32 * rb, 32 * cb, a1);
+          a2 = gd_block_product<kGdC>(Nv, Kv, 32 * rb, 32 * cb, a2);
         } else {
-          a1 = gd_block_product(dKSv, S0Tv, 32 * rb, 32 * cb, kGdD, a1);
-          a2 = gd_block_product(NTv, Qv, 32 * rb, 32 * cb, kGdC, a2);
-          a2 = gd_block_product(Mv, Kv, 32 * rb, 32 * cb, kGdC, a2);
-          a2 = gd_block_product(MTv, Kv, 32 * rb, 32 * cb, kGdC, a2);
+          a1 = gd_block_product<kGdD>(dKSv, S0Tv, 32 * rb, 32 * cb, a1);
+          a2 = gd_block_product<kGdC>(NTv, Qv, 32 * rb, 32 * cb, a2);
+          a2 = gd_block_product<kGdC>(Mv, Kv, 32 * rb, 32 * cb, a2);
+          a2 = gd_block_product<kGdC>(MTv, Kv, 32 * rb, 32 * cb, a2);
         }
         float* outp = isq ? dq : dk;
 #pragma unroll

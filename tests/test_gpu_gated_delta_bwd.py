@@ -110,3 +110,42 @@ def test_backward_bad_cu_writes_nothing():
     dq, dk, dv, dg, db, dh0, st = pvb.gated_delta_bwd(_dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]),
                                                       _dev(w["beta"]), bad, do)
     assert int(st.item()) == 4                                     # PVB_E_BAD_CU_SEQLENS
+
+
+def test_backward_long_mixed_pack_sampled_head():
+    """The long mixed pack (T=32768: a 16384-token slice, then slices of
+    16-1024) at 32 heads, launched as the bench launches it (fp32 gradients,
+    a final-state gradient); value head 5 compared in full, every slice, with
+    the oracle run slice by slice on that head."""
+    import torch
+
+    import packed_varlen_block_amd as pvb
+    lengths = W.lengths_cfg4(0)
+    H, d = 32, 128
+    say(f"gated delta bwd: long mixed pack T={int(lengths.sum())}, H={H}, head 5 against the oracle")
+    w = W.random_gated_delta(506, lengths, H)
+    T = int(lengths.sum())
+    r = np.random.default_rng(507)
+    do = W.f32_to_bf16_bits(r.standard_normal((T, H, d), dtype=np.float32))
+    dsf = (r.standard_normal((len(lengths), H, d, d), dtype=np.float32) * np.float32(0.1))
+    hc = host_cu(lengths)
+    dq, dk, dv, dg, db, dh0, st = pvb.gated_delta_bwd(_dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]),
+                                                      _dev(w["beta"]), _dev(hc), _dev(do), dht=_dev(dsf))
+    pvb.check_status(st)
+    h = 5
+    f = W.bf16_bits_to_f64
+    q, k, v, dof = f(w["q"][:, h]), f(w["k"][:, h]), f(w["v"][:, h]), f(do[:, h])
+    g, b = w["g"][:, h].astype(np.float64), w["beta"][:, h].astype(np.float64)
+    ref = [np.zeros((T, d)), np.zeros((T, d)), np.zeros((T, d)), np.zeros(T), np.zeros(T)]
+    ref_h0 = np.zeros((len(lengths), d, d))
+    for s in range(len(lengths)):
+        a, e = int(hc[s]), int(hc[s + 1])
+        out = LA.gated_delta_segment_backward(q[a:e], k[a:e], v[a:e], g[a:e], b[a:e], d ** -0.5, dof[a:e],
+                                              None, dsf[s, h].astype(np.float64))
+        for i in range(5):
+            ref[i][a:e] = out[i]
+        ref_h0[s] = out[5]
+    got = [dq[:, h], dk[:, h], dv[:, h], dg[:, h], db[:, h]]
+    for name, a, bref in zip(("dq", "dk", "dv", "dg", "dbeta"), got, ref):
+        _check(name, a.double().cpu().numpy(), bref)
+    _check("dh0", dh0[:, h].double().cpu().numpy(), ref_h0)
