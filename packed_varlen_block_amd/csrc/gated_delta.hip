@@ -373,8 +373,7 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int pos = 32 * rb + crow(i, hg);
-          if (pos < nv) cuu[(size_t)pos * kGdD + n0] = ks[rb][i];
+          cuu[(size_t)(32 * rb + crow(i, hg)) * kGdD + n0] = ks[rb][i];   // zero past the end
         }
     }
     __syncthreads();                                  // the P and key fragments are complete
@@ -503,239 +502,313 @@ namespace {
 //
 // The gradients of  sum_t o_t . dO_t + <S_final, dS_final>  with respect to
 // q, k, v, g, beta and the initial states, slice by slice (nothing crosses a
-// boundary), by reverse-mode differentiation of the chunked form above.  A
-// recomputation pass (gated_delta_kernel in CKPT mode) stores each chunk's
-// starting state S0 and its U; the backward then walks the chunks of every
-// (slice, value head) from the last to the first, carrying dS, the gradient
-// with respect to the state at the chunk's end.  With n positions in the
-// chunk, gamma the chunk-local cumulative gate, G = exp(gamma), G_L its last
-// value, Gam_ij = G_i / G_j, Ah = strict_lower(Gam o K K^T) (so A = diag(beta)
-// Ah), P = lower(Gam o Q K^T), X = V - diag(G) K S0 and Kt = diag(G_L / G) K:
+// boundary), by reverse-mode differentiation of the chunked form above.  With
+// n positions in a chunk, gamma the chunk-local cumulative gate, G = exp(gamma),
+// G_L its last value, Gam_ij = G_i / G_j, Ah = strict_lower(Gam o K K^T) (so
+// A = diag(beta) Ah), P = lower(Gam o Q K^T), S0 the state at the chunk's
+// start, U the chunk's solved update, X = V - diag(G) K S0, Kt = diag(G_L / G) K
+// and dS the gradient with respect to the state at the chunk's end:
 //   dU  = scale P^T dO + Kt dS               dR = (I + A)^-T dU
 //   dV  = diag(beta) dR                      dKS = -diag(G) dV
+//   dS (for the previous chunk) = K^T dKS + scale Q^T diag(G) dO + G_L dS
 //   dA  = -strict_lower(dR U^T)              dP = scale lower(dO U^T)
 //   dKt = U dS^T
 //   dbeta_i = sum_c dR_ic X_ic + sum_j dA_ij Ah_ij
 //   dG_i = -sum_c dV_ic (K S0)_ic + scale sum_c dO_ic (Q S0)_ic
 //   M = diag(beta) (Gam o dA),  N = Gam o dP
-//   dK = dKS S0^T + N^T Q + M K + M^T K + diag(G_L / G) dKt
+//   dK = dKS S0^T + N^T Q + (M + M^T) K + diag(G_L / G) dKt
 //   dQ = scale diag(G) dO S0^T + N K
 //   dgamma = rowsum(dP o P) - colsum(dP o P) + rowsum(dA o A) - colsum(dA o A)
 //            + G o dG - rowsum(dKt o Kt);  dgamma_last += sum(dKt o Kt) + G_L <dS, S0>
-//   dg_t = sum_{i >= t} dgamma_i;   dS (for the previous chunk) = K^T dKS + scale Q^T diag(G) dO + G_L dS
-// Every product runs on the matrix cores as 32x32 blocks (gd_block_product),
-// fp32 operands split into bf16 hi + lo; the chunk's matrices live in a
-// per-workgroup global scratch (and Ah, P, M, N in LDS), one wave per output
-// block.  dQ and dK of a query/key head shared by several value heads are
-// summed with fp32 atomic adds into buffers cleared first.
+//   dg_t = sum_{i >= t} dgamma_i  (inside the chunk).
+// Only the first three lines form a chain from chunk to chunk, and that chain
+// needs neither S0 nor U.  So the call runs three passes:
+//   1. the forward in its recomputation mode (gated_delta_kernel, CKPT): S0
+//      and U of every chunk into checkpoint slots;
+//   2. the state-gradient chain (gd_bwd_chain_kernel), one workgroup per
+//      (slice, value head) walking the chunks back: dS at every chunk's end
+//      and every chunk's dR into checkpoint slots, dV, and dh0;
+//   3. the chunk-parallel pass (gd_bwd_chunk_kernel), one workgroup per
+//      (chunk, value head): everything else, from the four checkpoints.
+// The products run on the matrix cores with fp32 operands split into bf16
+// hi + lo parts (about 16 significant bits); the transposed solve is fp32 on
+// the vector unit.  dQ and dK of a query/key head shared by several value
+// heads are summed with fp32 atomic adds into buffers cleared first.
 
-// Read-only matrix views: element (r, c) at p[r * rs + c * cs], zero outside
-// [0, nr) x [0, nc).  FView is fp32 (split into two bf16 parts for the matrix
-// cores), HView bf16 (taken as it is), HSView bf16 times a per-row scale.
-struct FView {
-  const float* p;
-  int64_t rs;
-  int64_t cs;
-  int nr, nc;
-  __device__ __forceinline__ float get(int r, int c) const {
-    return (r < nr && c < nc) ? p[r * rs + c * cs] : 0.f;
-  }
-};
-struct HView {
-  const bf16* p;
-  int64_t rs;
-  int64_t cs;
-  int nr, nc;
-  __device__ __forceinline__ float get(int r, int c) const {
-    return (r < nr && c < nc) ? (float)p[r * rs + c * cs] : 0.f;
-  }
-};
-struct HSView {
-  const bf16* p;
-  int64_t rs;
-  int64_t cs;
-  int nr, nc;
-  const float* rsc;
-  __device__ __forceinline__ float get(int r, int c) const {
-    return (r < nr && c < nc) ? rsc[r] * (float)p[r * rs + c * cs] : 0.f;
-  }
-};
-template <typename V>
-struct exact_bf16 : std::false_type {};
-template <>
-struct exact_bf16<HView> : std::true_type {};
+// Checkpoint layouts, per slot and value head, row-major fp32: S0 and dS
+// [d_k][d_v], U and dR [64][d_v] (all 64 rows written; rows past the chunk's
+// end are zero).
+constexpr size_t kGdStateFloats = (size_t)kGdD * kGdD;
+constexpr size_t kGdChunkFloats = (size_t)kGdC * kGdD;
 
-// acc += the 32x32 block (m0, n0) of A B over k < K (a multiple of 16): lane
-// l holds A[m0 + l%32][k0 + 8(l/32) + e] and B[k0 + 8(l/32) + e][n0 + l%32];
-// result element i of lane l is row m0 + crow(i, l/32), column n0 + l%32.
-template <int K, typename VA, typename VB>
-__device__ __forceinline__ f32x16 gd_block_product(const VA& a, const VB& b, int m0, int n0, f32x16 acc) {
-  const int lane = threadIdx.x & 63, c = lane & 31, hg = lane >> 5;
-#pragma unroll 2
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    float xa[8], xb[8];
+// Sum over the 32 lanes of a half-wave of each of the 16 C-layout values of
+// a lane (rows crow(i, hg) of one 32-column block): a halving exchange, 16
+// shuffles.  Lane c of half hg returns the sum of row crow(idx, hg) with
+// idx = 8 b4 + 4 b3 + 2 b2 + b1 (b_k bit k of c); lanes c and c ^ 1 agree.
+__device__ __forceinline__ float row_sum16(const float (&v)[16], int c, int& idx) {
+  float a[8];
+  const bool b4 = c & 16, b3 = c & 8, b2 = c & 4, b1 = c & 2;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      xa[e] = a.get(m0 + c, k0 + 8 * hg + e);
-      xb[e] = b.get(k0 + 8 * hg + e, n0 + c);
-    }
-    bf16x8 ah, al, bh, bl;
-    split8(xa, ah, al);
-    split8(xb, bh, bl);
-    acc = mfma32(ah, bh, acc);
-    if constexpr (!exact_bf16<VB>::value) acc = mfma32(ah, bl, acc);
-    if constexpr (!exact_bf16<VA>::value) acc = mfma32(al, bh, acc);
-  }
-  return acc;
+  for (int j = 0; j < 8; ++j) a[j] = (b4 ? v[j + 8] : v[j]) + __shfl_xor(b4 ? v[j] : v[j + 8], 16, 64);
+  float b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = (b3 ? a[j + 4] : a[j]) + __shfl_xor(b3 ? a[j] : a[j + 4], 8, 64);
+  float d2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) d2[j] = (b2 ? b[j + 2] : b[j]) + __shfl_xor(b2 ? b[j] : b[j + 2], 4, 64);
+  float e = (b1 ? d2[1] : d2[0]) + __shfl_xor(b1 ? d2[0] : d2[1], 2, 64);
+  e += __shfl_xor(e, 1, 64);
+  idx = 8 * b4 + 4 * b3 + 2 * b2 + b1;
+  return e;
 }
 
-constexpr int kGdBwdScratch = kGdD * kGdD + 6 * kGdC * kGdD + 2 * kGdC * kGdC;   // floats per workgroup
-constexpr int kLP = kGdC + 1;                                                   // LDS row pitch
+// Two 16-byte reads of 8 consecutive fp32 values.
+__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
 
-struct GdBwdSmem {
-  float ah[kGdC][kLP];     // Ah (then M)
-  float p[kGdC][kLP];      // P (then N)
-  float gl[kGdC], eg[kGdC], dec[kGdC], beta[kGdC];
-  float dbeta[kGdC], dG[kGdC], dgam[kGdC];
-  float red[kGdThreads / 64];
+// Shared by the two backward kernels: the chunk's gates (wave 0) and the
+// lower 32x32 blocks of Ah and P (block (0, 1) is not formed), from Q and K
+// staged in LDS.  Job j of 6: KK (1,0), QK (0,0), QK (1,0), KK (0,0), KK (1,1),
+// QK (1,1), handed out as the forward does.
+struct GdTiles {
+  alignas(16) bf16 q[kGdC][kKP];
+  alignas(16) bf16 k[kGdC][kKP];
+  alignas(16) bf16 dO[kGdC][kKP];
+  alignas(16) float ah[kGdC][kFP];   // Ah (no beta)
+  alignas(16) float p[kGdC][kFP];    // P
+  alignas(16) float gl[kGdC];        // gamma_i log2(e)
+  alignas(16) float eg[kGdC];        // G_i
+  alignas(16) float dec[kGdC];       // G_L / G_i
+  alignas(16) float beta[kGdC];
 };
 
+__device__ __forceinline__ void gd_gates(GdTiles& t, float gx, float bx, int lane) {
+  float x = gx;                                       // inclusive sum (zero past the chunk's end)
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  x *= kLog2e;
+  const float last = __shfl(x, 63, 64);               // flat past the end: the last position's sum
+  t.gl[lane] = x;
+  t.eg[lane] = fast_exp2(x);
+  t.dec[lane] = fast_exp2(last - x);
+  t.beta[lane] = bx;
+}
+
+__device__ __forceinline__ void gd_ah_p_block(GdTiles& t, bool isq, int bi, int bj, int c, int hg) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < kGdD / 16; ++s) {
+    const bf16x8 a = isq ? *(const bf16x8*)&t.q[32 * bi + c][16 * s + 8 * hg]
+                         : *(const bf16x8*)&t.k[32 * bi + c][16 * s + 8 * hg];
+    const bf16x8 bk = *(const bf16x8*)&t.k[32 * bj + c][16 * s + 8 * hg];
+    acc = mfma32(a, bk, acc);
+  }
+  const int pj = 32 * bj + c;
+  const float gj = t.gl[pj];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int pi = 32 * bi + crow(i, hg);
+    const float dcy = fast_exp2(fminf(t.gl[pi] - gj, 0.f));
+    if (isq) t.p[pi][pj] = pj <= pi ? acc[i] * dcy : 0.f;
+    else t.ah[pi][pj] = pj < pi ? acc[i] * dcy : 0.f;
+  }
+}
+
+__device__ __forceinline__ void gd_ah_p_jobs(GdTiles& t, int w, int c, int hg) {
+  if (w == 0) { gd_ah_p_block(t, false, 1, 0, c, hg); gd_ah_p_block(t, true, 0, 0, c, hg); }
+  else if (w == 1) { gd_ah_p_block(t, true, 1, 0, c, hg); gd_ah_p_block(t, false, 0, 0, c, hg); }
+  else if (w == 2) gd_ah_p_block(t, false, 1, 1, c, hg);
+  else gd_ah_p_block(t, true, 1, 1, c, hg);
+}
+
+// Stages rows [t0, t0 + n) of Q and K (query/key head hk) and dO (value head
+// h) in the tiles, zero past n: 16-byte pieces, four per thread and tile.
+struct GdStage {
+  uint4 q[4], k[4], o[4];
+  float g, b;
+  __device__ __forceinline__ void fetch(const bf16* q_, const bf16* k_, const bf16* do_, const float* g_,
+                                        const float* beta_, int t0, int n, int H, int Hk, int h, int hk,
+                                        int tid) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + kGdThreads * it;
+      const int row = ch >> 4, col = (ch & 15) * 8;
+      q[it] = k[it] = o[it] = zero4();
+      if (row < n) {
+        const size_t oqk = ((size_t)(t0 + row) * Hk + hk) * kGdD + col;
+        const size_t oo = ((size_t)(t0 + row) * H + h) * kGdD + col;
+        q[it] = *(const uint4*)(q_ + oqk);
+        k[it] = *(const uint4*)(k_ + oqk);
+        o[it] = *(const uint4*)(do_ + oo);
+      }
+    }
+    g = b = 0.f;
+    if (tid < 64 && tid < n) {
+      const size_t idx = (size_t)(t0 + tid) * H + h;
+      g = g_[idx];
+      b = beta_[idx];
+    }
+  }
+  __device__ __forceinline__ void put(GdTiles& t, int tid) const {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + kGdThreads * it;
+      const int row = ch >> 4, col = (ch & 15) * 8;
+      *(uint4*)&t.q[row][col] = q[it];
+      *(uint4*)&t.k[row][col] = k[it];
+      *(uint4*)&t.dO[row][col] = o[it];
+    }
+  }
+};
+
+// Every workgroup checks the whole cu_seqlens before it writes anything.
+__device__ __forceinline__ bool gd_cu_bad(const int32_t* __restrict__ cu, int n_seg, int T, int* s_bad) {
+  if (threadIdx.x == 0) *s_bad = 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b < n_seg; b += blockDim.x)
+    if (cu[b + 1] < cu[b]) atomicOr(s_bad, 1);
+  if (threadIdx.x == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(s_bad, 1);
+  __syncthreads();
+  return *s_bad != 0;
+}
+
+struct GdChainSmem {
+  GdTiles t;
+  // A fragments of K^T and Q^T for the state-gradient update, [d_k block][k-step][lane]:
+  // element e of lane (c, hg) is K[kpos(s, e, hg)][32 r + c]
+  alignas(16) bf16x8 kt[4][4][64], qt[4][4][64];
+};
+
+// Pass 2: one workgroup per (slice, value head), chunks from the last to the
+// first.  Wave w owns value columns [32w, 32w + 32): dS stays in its registers
+// (C layout of four 32x32 blocks, rows = key dims), as the state does in the
+// forward.
 template <typename GradT>
 __global__ void __launch_bounds__(kGdThreads, 1)
-gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-                       const float* __restrict__ g, const float* __restrict__ beta,
-                       const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
-                       const bf16* __restrict__ dout, const float* __restrict__ dht,
-                       const float* __restrict__ ck_s, const float* __restrict__ ck_u, float* __restrict__ scratch,
-                       float* __restrict__ dq, float* __restrict__ dk, GradT* __restrict__ dv,
-                       float* __restrict__ dg, float* __restrict__ dbeta, float* __restrict__ dh0, bool atomic_qk) {
-  __shared__ GdBwdSmem sm;
+gd_bwd_chain_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+                    const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk,
+                    float scale, const bf16* __restrict__ dout, const float* __restrict__ dht,
+                    float* __restrict__ ck_ds, float* __restrict__ ck_dr, GradT* __restrict__ dv,
+                    float* __restrict__ dh0) {
+  __shared__ GdChainSmem sm;
   __shared__ int s_bad;
+  GdTiles& t = sm.t;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
-
-  // the recomputation pass reported a bad cu_seqlens; every workgroup checks
-  // it again before it writes anything
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  for (int b = tid; b < n_seg; b += kGdThreads)
-    if (cu[b + 1] < cu[b]) atomicOr(&s_bad, 1);
-  if (tid == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(&s_bad, 1);
-  __syncthreads();
-  if (s_bad || (int)blockIdx.x >= n_seg * H) return;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad) || (int)blockIdx.x >= n_seg * H) return;
 
   const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const int hk = h / (H / Hk);
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
-  float* sc = scratch + (size_t)blockIdx.x * kGdBwdScratch;
-  float* s_dS = sc;                                   // [128][128] gradient of the chunk's end state
-  float* s_KS = s_dS + kGdD * kGdD;                   // [64][128] K S0
-  float* s_QS = s_KS + kGdC * kGdD;                   // [64][128] Q S0
-  float* s_X = s_QS + kGdC * kGdD;                    // [64][128] V - diag(G) K S0
-  float* s_dR = s_X + kGdC * kGdD;                    // [64][128] dU, solved in place into dR
-  float* s_dKS = s_dR + kGdC * kGdD;                  // [64][128] -diag(G beta) dR
-  float* s_dKt = s_dKS + kGdC * kGdD;                 // [64][128] U dS^T
-  float* s_dA = s_dKt + kGdC * kGdD;                  // [64][64]
-  float* s_dP = s_dA + kGdC * kGdC;                   // [64][64]
+  const int n0 = 32 * w + c;
+  const size_t st_base = (size_t)(b * H + h) * kGdStateFloats;
 
-  const size_t st_base = (size_t)(b * H + h) * kGdD * kGdD;
-  for (int e = tid; e < kGdD * kGdD; e += kGdThreads) s_dS[e] = dht ? dht[st_base + e] : 0.f;
+  f32x16 dS[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      dS[r][i] = dht ? dht[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
 
   const int n_chunks = (L + kGdC - 1) / kGdC;
+  GdStage pf;
+  if (n_chunks > 0) {
+    const int c0 = (n_chunks - 1) * kGdC;
+    pf.fetch(q, k, dout, g, beta, seg0 + c0, L - c0, H, Hk, h, hk, tid);
+  }
   for (int ci = n_chunks - 1; ci >= 0; --ci) {
     const int t0 = seg0 + ci * kGdC;
     const int n = min(kGdC, L - ci * kGdC);
     const size_t slot = gd_ckpt_slot(seg0, b, ci);
-    const float* S0p = ck_s + (slot * H + h) * kGdD * kGdD;
-    const float* Up = ck_u + (slot * H + h) * kGdC * kGdD;
-    const HView Qv{q + ((size_t)t0 * Hk + hk) * kGdD, (int64_t)Hk * kGdD, 1, n, kGdD};
-    const HView Kv{k + ((size_t)t0 * Hk + hk) * kGdD, (int64_t)Hk * kGdD, 1, n, kGdD};
-    const HView KTv{Kv.p, 1, (int64_t)Hk * kGdD, kGdD, n};            // K^T [dk][pos]
-    const HView QTv{Qv.p, 1, (int64_t)Hk * kGdD, kGdD, n};
-    const bf16* Vp = v + ((size_t)t0 * H + h) * kGdD;
-    const bf16* dOp = dout + ((size_t)t0 * H + h) * kGdD;
-    const HView dOv{dOp, (int64_t)H * kGdD, 1, n, kGdD};
-    const FView S0v{S0p, kGdD, 1, kGdD, kGdD};                          // [dk][col]
-    const FView S0Tv{S0p, 1, kGdD, kGdD, kGdD};                         // [col][dk]
-    const FView Uv{Up, kGdD, 1, n, kGdD};                               // [pos][col]
-    const FView UTv{Up, 1, kGdD, kGdD, n};                              // [col][pos]
-    const FView dSv{s_dS, kGdD, 1, kGdD, kGdD};
-    const FView dSTv{s_dS, 1, kGdD, kGdD, kGdD};
-
-    __syncthreads();                                  // the previous chunk is done with LDS and scratch
-    // ---- gates (log2 units), chunk-local
-    if (w == 0) {
-      float x = lane < n ? g[(size_t)(t0 + lane) * H + h] : 0.f;
+    {
+      float* dst = ck_ds + (slot * H + h) * kGdStateFloats;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-      }
-      x *= kLog2e;
-      const float last = __shfl(x, n - 1, 64);
-      sm.gl[lane] = x;
-      sm.eg[lane] = fast_exp2(x);
-      sm.dec[lane] = fast_exp2(last - x);
-      sm.beta[lane] = lane < n ? beta[(size_t)(t0 + lane) * H + h] : 0.f;
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] = dS[r][i];
+    }
+    __syncthreads();                                  // the previous chunk's LDS reads are done
+    pf.put(t, tid);
+    if (w == 0) gd_gates(t, pf.g, pf.b, lane);
+    if (ci > 0) {
+      const int c0 = (ci - 1) * kGdC;
+      pf.fetch(q, k, dout, g, beta, seg0 + c0, kGdC, H, Hk, h, hk, tid);
     }
     __syncthreads();
 
-    // ---- Ah, P (LDS) and K S0, Q S0 (scratch): 8 + 16 block jobs
-    for (int job = w; job < 24; job += 4) {
-      if (job < 8) {
-        const bool isq = job >= 4;
-        const int jb = job & 3;                       // blocks (0,0), (1,0), (1,1), (0,1)
-        const int bi = jb == 0 ? 0 : (jb == 3 ? 0 : 1), bj = jb == 1 ? 0 : (jb == 3 ? 1 : bi);
-        float (*dst)[kLP] = isq ? sm.p : sm.ah;
-        f32x16 acc = {};
-        if (jb != 3) acc = isq ? gd_block_product<kGdD>(Qv, KTv, 32 * bi, 32 * bj, acc)
-                               : gd_block_product<kGdD>(Kv, KTv, 32 * bi, 32 * bj, acc);
+    gd_ah_p_jobs(t, w, c, hg);
+    // K^T and Q^T fragments, once for the four waves
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * bi + crow(i, hg), cc = 32 * bj + c;
-          const float gam = fast_exp2(fminf(sm.gl[r] - sm.gl[cc], 0.f));
-          const bool keep = isq ? cc <= r : cc < r;
-          dst[r][cc] = (jb != 3 && keep) ? gam * acc[i] : 0.f;
-        }
-      } else {
-        const int jj = job - 8, isq = jj >= 8, blk = jj & 7, rb = blk >> 2, cb = blk & 3;
-        f32x16 acc = {};
-        acc = isq ? gd_block_product<kGdD>(Qv, S0v, 32 * rb, 32 * cb, acc)
-                  : gd_block_product<kGdD>(Kv, S0v, 32 * rb, 32 * cb, acc);
-        float* dst = isq ? s_QS : s_KS;
+    for (int it = 0; it < 4; ++it) {
+      const int f = tid + kGdThreads * it;
+      const int r = f >> 8, s = (f >> 6) & 3, fl = f & 63, fc = fl & 31, fh = fl >> 5;
+      bf16x8 xk, xq;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(32 * rb + crow(i, hg)) * kGdD + 32 * cb + c] = acc[i];
+      for (int e = 0; e < 8; ++e) {
+        xk[e] = t.k[kpos(s, e, fh)][32 * r + fc];
+        xq[e] = t.q[kpos(s, e, fh)][32 * r + fc];
       }
+      sm.kt[r][s][fl] = xk;
+      sm.qt[r][s][fl] = xq;
     }
-    __syncthreads();
-
-    // ---- X = V - diag(G) K S0 and dU = scale P^T dO + diag(G_L / G) K dS
-    {
-      const int r = tid >> 2, c0 = (tid & 3) * 32;
-      for (int cc = c0; cc < c0 + 32; ++cc)
-        s_X[r * kGdD + cc] = r < n ? (float)Vp[(size_t)r * H * kGdD + cc] - sm.eg[r] * s_KS[r * kGdD + cc] : 0.f;
-    }
-    // dU in registers: wave w holds the two 32-row blocks of its 32 columns in
-    // the C layout (rows 32 rb + crow(i, hg), column 32 w + c)
-    f32x16 du[2];
-    {
-      const FView PTv{&sm.p[0][0], 1, kLP, kGdC, kGdC};                 // P^T
+    // dO of this wave's columns as B fragments (k-step s: positions kpos(s, e, hg))
+    bf16x8 dob[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dob[s][e] = t.dO[kpos(s, e, hg)][n0];
+    // K dS for this wave's columns (the state gradient as the B operand straight
+    // from its C layout, as the forward's K S0)
+    f32x16 du[2] = {}, kds[2] = {};
+#pragma unroll
+    for (int s = 0; s < kGdD / 16; ++s) {
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = dS[s >> 1][8 * (s & 1) + e];
+      bf16x8 shi, slo;
+      split8(sv, shi, slo);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        f32x16 a1 = {}, a2 = {};
-        a1 = gd_block_product<kGdC>(PTv, dOv, 32 * rb, 32 * w, a1);
-        a2 = gd_block_product<kGdD>(Kv, dSv, 32 * rb, 32 * w, a2);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) du[rb][i] = scale * a1[i] + sm.dec[32 * rb + crow(i, hg)] * a2[i];
+        const bf16* kr = &t.k[32 * rb + c][16 * s + 4 * hg];
+        const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
+        kds[rb] = mfma32(ka, shi, kds[rb]);
+        kds[rb] = mfma32(ka, slo, kds[rb]);
       }
     }
+    __syncthreads();                                  // Ah, P and the fragments are complete
+
+    // P^T dO: A element e of lane (c, hg) at k-step s is P[kpos(s, e, hg)][32 rb + c];
+    // P^T of row block 1 has no position below 32
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (rb == 1 && s < 2) continue;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = t.p[kpos(s, e, hg)][32 * rb + c];
+        bf16x8 ph, pl;
+        split8(x, ph, pl);
+        du[rb] = mfma32(ph, dob[s], du[rb]);
+        du[rb] = mfma32(pl, dob[s], du[rb]);
+      }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) du[rb][i] = scale * du[rb][i] + t.dec[32 * rb + crow(i, hg)] * kds[rb][i];
 
     // ---- dR = (I + A)^-T dU, A = diag(beta) Ah, in the C layout, blocked by
     // 32 rows from the bottom: the lower block's triangle, the upper block's
     // update by the matrix cores, the upper block's triangle.  Inside a block,
     // row jj is final when reached from the block's end; the lane holding it
-    // hands it across the half-waves and every row above it subtracts A_(jj, row)
-    // times it.
+    // hands it across the half-waves and every row above it subtracts
+    // A_(jj, row) times it.
     auto triangle_t = [&](auto rb_tag) {
       constexpr int RB = decltype(rb_tag)::value;
 #pragma unroll
@@ -744,11 +817,11 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
         const bool own = ((jj >> 2) & 1) == hg;
         const float x = du[RB][ij];
         const float other = swap_halves(x);
-        const float rj = (own ? x : other) * sm.beta[32 * RB + jj];
+        const float rj = (own ? x : other) * t.beta[32 * RB + jj];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           if (8 * m >= jj) continue;                  // every row of the group is at or below jj
-          const float4 a4 = *(const float4*)&sm.ah[32 * RB + jj][32 * RB + 8 * m + 4 * hg];
+          const float4 a4 = *(const float4*)&t.ah[32 * RB + jj][32 * RB + 8 * m + 4 * hg];
           const int r0 = 8 * m + 4 * hg;
           if (r0 + 0 < jj) du[RB][4 * m + 0] -= a4.x * rj;
           if (r0 + 1 < jj) du[RB][4 * m + 1] -= a4.y * rj;
@@ -758,199 +831,399 @@ gated_delta_bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, c
       }
     };
     triangle_t(std::integral_constant<int, 1>{});
-    {
-      // upper rows i: dU_i -= sum_{j in the lower block} A_ji dR_j; the lower
-      // block is the B operand straight from its C layout (k-step s: elements
-      // 8s + e, rows 32 + kpos(s, e, hg)), A_ji read in that order
+    // upper rows i: dU_i -= sum_{j in the lower block} A_ji dR_j; the lower
+    // block is the B operand straight from its C layout, A_ji read in that order
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float xa[8], xb[8];
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float xa[8], xb[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 32 + kpos(s2, e, hg);
-          xa[e] = -sm.beta[j] * sm.ah[j][c];
-          xb[e] = du[1][8 * s2 + e];
-        }
-        bf16x8 ah, al, bh, bl;
-        split8(xa, ah, al);
-        split8(xb, bh, bl);
-        du[0] = mfma32(ah, bh, du[0]);
-        du[0] = mfma32(ah, bl, du[0]);
-        du[0] = mfma32(al, bh, du[0]);
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 + kpos(s2, e, hg);
+        xa[e] = -t.beta[j] * t.ah[j][c];
+        xb[e] = du[1][8 * s2 + e];
       }
+      bf16x8 ah, al, bh, bl;
+      split8(xa, ah, al);
+      split8(xb, bh, bl);
+      du[0] = mfma32(ah, bh, du[0]);
+      du[0] = mfma32(ah, bl, du[0]);
+      du[0] = mfma32(al, bh, du[0]);
     }
     triangle_t(std::integral_constant<int, 0>{});
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s_dR[(32 * rb + crow(i, hg)) * kGdD + 32 * w + c] = du[rb][i];
-    __syncthreads();
 
-    // ---- dV = diag(beta) dR (stored), dKS = -diag(G) dV, and the per-row sums
-    // of dbeta (through X) and dG
+    // ---- dV = diag(beta) dR (stored), dR into its checkpoint, and the new
+    // dS = G_L dS + K^T dKS + scale Q^T diag(G) dO with dKS = -diag(G beta) dR
     {
-      const int r = tid >> 2, c0 = (tid & 3) * 32;
-      const float br = sm.beta[r], gr = sm.eg[r];
-      float sR = 0.f, sG = 0.f;
-      for (int cc = c0; cc < c0 + 32; ++cc) {
-        const int e = r * kGdD + cc;
-        const float dr = s_dR[e], dvv = br * dr;
-        const float dov = r < n ? (float)dOp[(size_t)r * H * kGdD + cc] : 0.f;
-        sR += dr * s_X[e];
-        sG += -dvv * s_KS[e] + scale * dov * s_QS[e];
-        s_dKS[e] = -gr * dvv;
-        if (r < n) dv[((size_t)(t0 + r) * H + h) * kGdD + cc] = out_cast<GradT>(dvv);
-      }
-      sR += __shfl_xor(sR, 1, 64);
-      sR += __shfl_xor(sR, 2, 64);
-      sG += __shfl_xor(sG, 1, 64);
-      sG += __shfl_xor(sG, 2, 64);
-      if ((tid & 3) == 0) {
-        sm.dbeta[r] = sR;
-        sm.dG[r] = sG;
-      }
-    }
-    // <dS, S0> over the whole state
-    {
-      float part = 0.f;
-      for (int e = tid; e < kGdD * kGdD; e += kGdThreads) part += s_dS[e] * S0p[e];
+      float* drp = ck_dr + (slot * H + h) * kGdChunkFloats;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-      if (lane == 0) sm.red[w] = part;
-    }
-    __syncthreads();
-
-    // ---- dKt = U dS^T, dA = -strict_lower(dR U^T), dP = scale lower(dO U^T)
-    {
-      const FView dRv{s_dR, kGdD, 1, kGdC, kGdD};
-      for (int job = w; job < 16; job += 4) {
-        if (job < 8) {
-          const int rb = job >> 2, cb = job & 3;
-          f32x16 acc = {};
-          acc = gd_block_product<kGdD>(Uv, dSTv, 32 * rb, 32 * cb, acc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s_dKt[(32 * rb + crow(i, hg)) * kGdD + 32 * cb + c] = acc[i];
-        } else {
-          const int jj = job - 8, isp = jj >= 4, jb = jj & 3;
-          const int bi = jb == 0 ? 0 : (jb == 3 ? 0 : 1), bj = jb == 1 ? 0 : (jb == 3 ? 1 : bi);
-          f32x16 acc = {};
-          if (jb != 3) acc = isp ? gd_block_product<kGdD>(dOv, UTv, 32 * bi, 32 * bj, acc)
-                                 : gd_block_product<kGdD>(dRv, UTv, 32 * bi, 32 * bj, acc);
-          float* dst = isp ? s_dP : s_dA;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = 32 * bi + crow(i, hg), cc = 32 * bj + c;
-            const bool keep = jb != 3 && (isp ? cc <= r : cc < r);
-            dst[r * kGdC + cc] = keep ? (isp ? scale * acc[i] : -acc[i]) : 0.f;
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- the new dS = K^T dKS + scale Q^T diag(G) dO + G_L dS (its own block
-    // of the old dS only), and the gate and write-strength gradients
-    {
-      const FView dKSv{s_dKS, kGdD, 1, kGdC, kGdD};
-      const HSView GdOv{dOp, (int64_t)H * kGdD, 1, n, kGdD, sm.eg};
-      const float gL = sm.eg[n - 1];
-      for (int job = w; job < 16; job += 4) {
-        const int rb = job >> 2, cb = job & 3;
-        f32x16 a1 = {}, a2 = {};
-        a1 = gd_block_product<kGdC>(KTv, dKSv, 32 * rb, 32 * cb, a1);
-        a2 = gd_block_product<kGdC>(QTv, GdOv, 32 * rb, 32 * cb, a2);
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int e = (32 * rb + crow(i, hg)) * kGdD + 32 * cb + c;
-          s_dS[e] = a1[i] + scale * a2[i] + gL * s_dS[e];
+          const int row = 32 * rb + crow(i, hg);
+          drp[(size_t)row * kGdD + n0] = du[rb][i];
+          if (row < n) dv[((size_t)(t0 + row) * H + h) * kGdD + n0] = out_cast<GradT>(t.beta[row] * du[rb][i]);
         }
-      }
     }
-    if (tid < kGdC) {
-      const int i = tid;
-      const float bi = sm.beta[i];
-      float rpa = 0.f, cpa = 0.f, rpp = 0.f, cpp = 0.f, dba = 0.f, kk = 0.f;
-      for (int j = 0; j < kGdC; ++j) {
-        const float a_ij = s_dA[i * kGdC + j] * sm.ah[i][j];            // dA_ij Ah_ij
-        dba += a_ij;
-        rpa += bi * a_ij;
-        cpa += sm.beta[j] * s_dA[j * kGdC + i] * sm.ah[j][i];
-        rpp += s_dP[i * kGdC + j] * sm.p[i][j];
-        cpp += s_dP[j * kGdC + i] * sm.p[j][i];
-      }
-      if (i < n)
-        for (int cc = 0; cc < kGdD; ++cc)
-          kk += s_dKt[i * kGdD + cc] * sm.dec[i] * (float)k[((size_t)(t0 + i) * Hk + hk) * kGdD + cc];
-      sm.dbeta[i] += dba;
-      sm.dgam[i] = rpp - cpp + rpa - cpa + sm.eg[i] * sm.dG[i] - kk;
-      // kk summed over all rows goes to the last position (with G_L <dS, S0>)
-      float tot = kk;
+    const float gL = t.eg[kGdC - 1];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
-      if (i == 0) sm.red[0] = tot + sm.eg[n - 1] * (sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]);
-    }
-    __syncthreads();
-    if (tid < kGdC) {
-      const int i = tid;
-      if (i == n - 1) sm.dgam[i] += sm.red[0];
-    }
-    __syncthreads();
-    if (tid < kGdC) {
-      const int i = tid;
-      // dg_i = sum over j >= i of dgamma_j (positions of this chunk only)
-      float s = 0.f;
-      for (int j = i; j < n; ++j) s += sm.dgam[j];
-      if (i < n) {
-        dg[(size_t)(t0 + i) * H + h] = s;
-        dbeta[(size_t)(t0 + i) * H + h] = sm.dbeta[i];
-      }
-    }
-    __syncthreads();
-    // ---- M = diag(beta) (Gam o dA) and N = Gam o dP into the LDS of Ah and P
-    for (int e = tid; e < kGdC * kGdC; e += kGdThreads) {
-      const int i = e / kGdC, j = e - (e / kGdC) * kGdC;
-      const float gam = fast_exp2(fminf(sm.gl[i] - sm.gl[j], 0.f));
-      sm.ah[i][j] = sm.beta[i] * gam * s_dA[e];
-      sm.p[i][j] = gam * s_dP[e];
-    }
-    __syncthreads();
-
-    // ---- dK = dKS S0^T + N^T Q + M K + M^T K + diag(G_L / G) dKt and
-    // dQ = scale diag(G) dO S0^T + N K
-    {
-      const FView dKSv{s_dKS, kGdD, 1, kGdC, kGdD};
-      const FView Mv{&sm.ah[0][0], kLP, 1, kGdC, kGdC}, MTv{&sm.ah[0][0], 1, kLP, kGdC, kGdC};
-      const FView Nv{&sm.p[0][0], kLP, 1, kGdC, kGdC}, NTv{&sm.p[0][0], 1, kLP, kGdC, kGdC};
-      for (int job = w; job < 16; job += 4) {
-        const bool isq = job >= 8;
-        const int rb = (job & 7) >> 2, cb = job & 3;
-        f32x16 a1 = {}, a2 = {};
-        if (isq) {
-          a1 = gd_block_product<kGdD>(dOv, S0Tv, 32 * rb, 32 * cb, a1);
-          a2 = gd_block_product<kGdC>(Nv, Kv, 32 * rb, 32 * cb, a2);
-        } else {
-          a1 = gd_block_product<kGdD>(dKSv, S0Tv, 32 * rb, 32 * cb, a1);
-          a2 = gd_block_product<kGdC>(NTv, Qv, 32 * rb, 32 * cb, a2);
-          a2 = gd_block_product<kGdC>(Mv, Kv, 32 * rb, 32 * cb, a2);
-          a2 = gd_block_product<kGdC>(MTv, Kv, 32 * rb, 32 * cb, a2);
-        }
-        float* outp = isq ? dq : dk;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * rb + crow(i, hg), cc = 32 * cb + c;
-          if (r >= n) continue;
-          const float val = isq ? scale * sm.eg[r] * a1[i] + a2[i]
-                                : a1[i] + a2[i] + sm.dec[r] * s_dKt[r * kGdD + cc];
-          float* dst = outp + ((size_t)(t0 + r) * Hk + hk) * kGdD + cc;
-          if (atomic_qk) atomicAdd(dst, val);
-          else *dst = val;
-        }
+      for (int i = 0; i < 16; ++i) dS[r][i] *= gL;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x1[8], x2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = kpos(s, e, hg);
+        const float gp = t.eg[pos];
+        x1[e] = -gp * t.beta[pos] * du[s >> 1][8 * (s & 1) + e];
+        x2[e] = scale * gp * (float)dob[s][e];
+      }
+      bf16x8 b1h, b1l, b2h, b2l;
+      split8(x1, b1h, b1l);
+      split8(x2, b2h, b2l);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16x8 ak = sm.kt[r][s][lane], aq = sm.qt[r][s][lane];
+        dS[r] = mfma32(ak, b1h, dS[r]);
+        dS[r] = mfma32(ak, b1l, dS[r]);
+        dS[r] = mfma32(aq, b2h, dS[r]);
+        dS[r] = mfma32(aq, b2l, dS[r]);
       }
     }
   }
+  if (dh0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dh0[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] = dS[r][i];
+  }
+}
+
+struct GdChunkSmem {
+  GdTiles t;
+  alignas(16) float da[kGdC][kFP];   // dA
+  alignas(16) float dp[kGdC][kFP];   // dP
+  float xr[4][kGdC], gr[4][kGdC], rk[4][kGdC];   // per-wave row partials
+  float part[2][4][kGdC];                        // row-sum partials over column quarters
+  float dgam[kGdC];
+  float red[4];
+};
+
+// Pass 3: one workgroup per (checkpoint slot, value head); slots that hold no
+// chunk return at once.  Wave w owns value columns [32w, 32w + 32) for the
+// row sums through K S0 and Q S0, and key dims [32w, 32w + 32) of dK and dQ.
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                    int n_seg, int T, int H, int Hk, float scale, const bf16* __restrict__ dout,
+                    const float* __restrict__ ck_s, const float* __restrict__ ck_u,
+                    const float* __restrict__ ck_ds, const float* __restrict__ ck_dr, float* __restrict__ dq,
+                    float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ dbeta, bool atomic_qk) {
+  __shared__ GdChunkSmem sm;
+  __shared__ int s_bad;
+  GdTiles& t = sm.t;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad) || n_seg == 0) return;
+
+  // slot -> (slice, chunk): the slice's first slot cu[b] / 64 + b rises strictly with b
+  const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] / kGdC + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo, seg0 = cu[b], L = cu[b + 1] - seg0;
+  const int ci = slot - (seg0 / kGdC + b);
+  if (ci < 0 || ci * kGdC >= L) return;
+  const int hk = h / (H / Hk);
+  const int t0 = seg0 + ci * kGdC, n = min(kGdC, L - ci * kGdC);
+  const float* S0p = ck_s + ((size_t)slot * H + h) * kGdStateFloats;
+  const float* dSp = ck_ds + ((size_t)slot * H + h) * kGdStateFloats;
+  const float* Up = ck_u + ((size_t)slot * H + h) * kGdChunkFloats;
+  const float* dRp = ck_dr + ((size_t)slot * H + h) * kGdChunkFloats;
+  const int n0 = 32 * w + c;                          // this lane's value column, and key dim
+
+  {
+    GdStage st;
+    st.fetch(q, k, dout, g, beta, t0, n, H, Hk, h, hk, tid);
+    st.put(t, tid);
+    if (w == 0) gd_gates(t, st.g, st.b, lane);
+  }
   __syncthreads();
-  if (dh0)
-    for (int e = tid; e < kGdD * kGdD; e += kGdThreads) dh0[st_base + e] = s_dS[e];
+
+  gd_ah_p_jobs(t, w, c, hg);
+  if (w == 3) {                                       // block (0, 1) of Ah and P is zero
+    for (int e = lane; e < 32 * 32; e += 64) {
+      t.ah[e >> 5][32 + (e & 31)] = 0.f;
+      t.p[e >> 5][32 + (e & 31)] = 0.f;
+    }
+  }
+  // ---- K S0 and Q S0 for this wave's value columns, then the row partials
+  // sum_c dR (V - G K S0) (for dbeta) and -beta sum_c dR K S0 + scale sum_c dO Q S0 (dG)
+  {
+    f32x16 S0c[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S0c[r][i] = S0p[(size_t)(32 * r + crow(i, hg)) * kGdD + n0];
+    f32x16 ks[2] = {}, qs[2] = {};
+#pragma unroll
+    for (int s = 0; s < kGdD / 16; ++s) {
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = S0c[s >> 1][8 * (s & 1) + e];
+      bf16x8 shi, slo;
+      split8(sv, shi, slo);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16* kr = &t.k[32 * rb + c][16 * s + 4 * hg];
+        const bf16* qr = &t.q[32 * rb + c][16 * s + 4 * hg];
+        const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
+        const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
+        ks[rb] = mfma32(ka, shi, ks[rb]);
+        ks[rb] = mfma32(ka, slo, ks[rb]);
+        qs[rb] = mfma32(qa, shi, qs[rb]);
+        qs[rb] = mfma32(qa, slo, qs[rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float xr[16], gr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * rb + crow(i, hg);
+        const float dr = dRp[(size_t)row * kGdD + n0];
+        const float vv = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
+        const float dov = (float)t.dO[row][n0];
+        xr[i] = dr * (vv - t.eg[row] * ks[rb][i]);
+        gr[i] = -t.beta[row] * dr * ks[rb][i] + scale * dov * qs[rb][i];
+      }
+      int idx;
+      const float sx = row_sum16(xr, c, idx);
+      const float sg = row_sum16(gr, c, idx);
+      if ((c & 1) == 0) {
+        const int row = 32 * rb + crow(idx, hg);
+        sm.xr[w][row] = sx;
+        sm.gr[w][row] = sg;
+      }
+    }
+  }
+  __syncthreads();                                    // Ah and P are complete
+
+  // ---- dA = -strict_lower(dR U^T) and dP = scale lower(dO U^T), contracted
+  // over all value columns (k index = column 16 s + 8 hg + e); block (0, 1) is zero
+  auto dadp_block = [&](bool isp, int bi, int bj) {
+    f32x16 acc = {};
+#pragma unroll 2
+    for (int s = 0; s < kGdD / 16; ++s) {
+      const int col = 16 * s + 8 * hg;
+      float xu[8];
+      load8f(Up + (size_t)(32 * bj + c) * kGdD + col, xu);
+      bf16x8 uh, ul;
+      split8(xu, uh, ul);
+      if (isp) {
+        const bf16x8 a = *(const bf16x8*)&t.dO[32 * bi + c][col];
+        acc = mfma32(a, uh, acc);
+        acc = mfma32(a, ul, acc);
+      } else {
+        float xr[8];
+        load8f(dRp + (size_t)(32 * bi + c) * kGdD + col, xr);
+        bf16x8 rh, rl;
+        split8(xr, rh, rl);
+        acc = mfma32(rh, uh, acc);
+        acc = mfma32(rh, ul, acc);
+        acc = mfma32(rl, uh, acc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * bi + crow(i, hg), cc = 32 * bj + c;
+      if (isp) sm.dp[r][cc] = cc <= r ? scale * acc[i] : 0.f;
+      else sm.da[r][cc] = cc < r ? -acc[i] : 0.f;
+    }
+  };
+  if (w == 0) { dadp_block(false, 1, 0); dadp_block(true, 0, 0); }
+  else if (w == 1) { dadp_block(false, 0, 0); dadp_block(true, 1, 1); }
+  else if (w == 2) { dadp_block(false, 1, 1); dadp_block(true, 1, 0); }
+  else {
+    for (int e = lane; e < 32 * 32; e += 64) {
+      sm.da[e >> 5][32 + (e & 31)] = 0.f;
+      sm.dp[e >> 5][32 + (e & 31)] = 0.f;
+    }
+  }
+
+  // ---- key dims [32w, 32w + 32) of dR S0^T, U dS^T (= dKt) and dO S0^T,
+  // contracted over all value columns; <dS, S0> over this wave's key dims; and
+  // the row partials sum_d dKt o Kt
+  f32x16 r1[2] = {}, kt1[2] = {}, q1[2] = {};
+  {
+    float sdot = 0.f;
+    for (int s = 0; s < kGdD / 16; ++s) {
+      const int col = 16 * s + 8 * hg;
+      float xs[8], xd[8];
+      load8f(S0p + (size_t)n0 * kGdD + col, xs);
+      load8f(dSp + (size_t)n0 * kGdD + col, xd);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sdot += xs[e] * xd[e];
+      bf16x8 sh, sl, dh, dl;
+      split8(xs, sh, sl);
+      split8(xd, dh, dl);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float xr[8], xu[8];
+        load8f(dRp + (size_t)(32 * rb + c) * kGdD + col, xr);
+        load8f(Up + (size_t)(32 * rb + c) * kGdD + col, xu);
+        bf16x8 rh, rl, uh, ul;
+        split8(xr, rh, rl);
+        split8(xu, uh, ul);
+        const bf16x8 oa = *(const bf16x8*)&t.dO[32 * rb + c][col];
+        r1[rb] = mfma32(rh, sh, r1[rb]);
+        r1[rb] = mfma32(rh, sl, r1[rb]);
+        r1[rb] = mfma32(rl, sh, r1[rb]);
+        kt1[rb] = mfma32(uh, dh, kt1[rb]);
+        kt1[rb] = mfma32(uh, dl, kt1[rb]);
+        kt1[rb] = mfma32(ul, dh, kt1[rb]);
+        q1[rb] = mfma32(oa, sh, q1[rb]);
+        q1[rb] = mfma32(oa, sl, q1[rb]);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 64);
+    if (lane == 0) sm.red[w] = sdot;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * rb + crow(i, hg);
+        x[i] = kt1[rb][i] * t.dec[row] * (float)t.k[row][n0];
+      }
+      int idx;
+      const float sx = row_sum16(x, c, idx);
+      if ((c & 1) == 0) sm.rk[w][32 * rb + crow(idx, hg)] = sx;
+    }
+  }
+  __syncthreads();                                    // dA, dP and the row partials are complete
+
+  // ---- row sums over quarters of the columns: thread (quarter w, row i)
+  {
+    const int i = lane, j0 = 16 * w;
+    const float bi = t.beta[i];
+    float dba = 0.f, rpp = 0.f, cpp = 0.f, rpa = 0.f, cpa = 0.f;
+#pragma unroll 4
+    for (int j = j0; j < j0 + 16; ++j) {
+      const float aij = sm.da[i][j] * t.ah[i][j];
+      dba += aij;
+      cpa += t.beta[j] * sm.da[j][i] * t.ah[j][i];
+      rpp += sm.dp[i][j] * t.p[i][j];
+      cpp += sm.dp[j][i] * t.p[j][i];
+    }
+    rpa = bi * dba;
+    sm.part[0][w][i] = dba;
+    sm.part[1][w][i] = rpp - cpp + rpa - cpa;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int i = lane;
+    float dba = sm.xr[0][i] + sm.xr[1][i] + sm.xr[2][i] + sm.xr[3][i];
+    float dgm = 0.f, dG = 0.f, rk = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      dba += sm.part[0][qq][i];
+      dgm += sm.part[1][qq][i];
+      dG += sm.gr[qq][i];
+      rk += sm.rk[qq][i];
+    }
+    dgm += t.eg[i] * dG - rk;
+    float tot = rk;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    if (i == n - 1) dgm += tot + t.eg[i] * (sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]);
+    if (i >= n) dgm = 0.f;
+    // dg_i = sum over j >= i of dgamma_j: a reversed inclusive scan
+    float x = dgm;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      if (i + off < 64) x += y;
+    }
+    if (i < n) {
+      dg[(size_t)(t0 + i) * H + h] = x;
+      dbeta[(size_t)(t0 + i) * H + h] = dba;
+    }
+  }
+  __syncthreads();                                    // Ah and P are read for the last time
+
+  // ---- M + M^T (M = diag(beta) (Gam o dA), strictly lower) into Ah's LDS and
+  // N = Gam o dP into P's
+  for (int e = tid; e < kGdC * kGdC; e += kGdThreads) {
+    const int i = e >> 6, j = e & 63;
+    const float gij = fast_exp2(fminf(t.gl[i] - t.gl[j], 0.f));
+    const float gji = fast_exp2(fminf(t.gl[j] - t.gl[i], 0.f));
+    t.ah[i][j] = j < i ? t.beta[i] * gij * sm.da[i][j] : (j > i ? t.beta[j] * gji * sm.da[j][i] : 0.f);
+    t.p[i][j] = gij * sm.dp[i][j];
+  }
+  __syncthreads();
+
+  // ---- dK = -diag(G beta) dR S0^T + diag(G_L / G) dKt + N^T Q + (M + M^T) K and
+  // dQ = scale diag(G) dO S0^T + N K for key dims [32w, 32w + 32); k index =
+  // position 16 s + 8 hg + e
+  {
+    f32x16 ka[2] = {}, qa[2] = {};
+#pragma unroll
+    for (int s = 0; s < kGdC / 16; ++s) {
+      const int p0 = 16 * s + 8 * hg;
+      bf16x8 bq, bk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bq[e] = t.q[p0 + e][n0];
+        bk[e] = t.k[p0 + e][n0];
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        bf16x8 hh, ll;
+        float x[8];
+        if (!(rb == 1 && s < 2)) {                    // N^T of row block 1 has no position below 32
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = t.p[p0 + e][32 * rb + c];
+          split8(x, hh, ll);
+          ka[rb] = mfma32(hh, bq, ka[rb]);
+          ka[rb] = mfma32(ll, bq, ka[rb]);
+        }
+        load8f(&t.ah[32 * rb + c][p0], x);
+        split8(x, hh, ll);
+        ka[rb] = mfma32(hh, bk, ka[rb]);
+        ka[rb] = mfma32(ll, bk, ka[rb]);
+        if (!(rb == 0 && s >= 2)) {                   // N of row block 0 has no position past 31
+          load8f(&t.p[32 * rb + c][p0], x);
+          split8(x, hh, ll);
+          qa[rb] = mfma32(hh, bk, qa[rb]);
+          qa[rb] = mfma32(ll, bk, qa[rb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * rb + crow(i, hg);
+        if (row >= n) continue;
+        const float gr = t.eg[row];
+        const float kv = -gr * t.beta[row] * r1[rb][i] + t.dec[row] * kt1[rb][i] + ka[rb][i];
+        const float qv = scale * gr * q1[rb][i] + qa[rb][i];
+        const size_t o = ((size_t)(t0 + row) * Hk + hk) * kGdD + n0;
+        if (atomic_qk) {
+          atomicAdd(dk + o, kv);
+          atomicAdd(dq + o, qv);
+        } else {
+          dk[o] = kv;
+          dq[o] = qv;
+        }
+      }
+  }
 }
 
 // Clears dQ and dK before value heads that share a query/key head add into
@@ -959,13 +1232,7 @@ __global__ void __launch_bounds__(256)
 gd_clear_kernel(float* __restrict__ a, float* __restrict__ b2, int64_t n, const int32_t* __restrict__ cu, int n_seg,
                 int T) {
   __shared__ int s_bad;
-  if (threadIdx.x == 0) s_bad = 0;
-  __syncthreads();
-  for (int s = threadIdx.x; s < n_seg; s += blockDim.x)
-    if (cu[s + 1] < cu[s]) atomicOr(&s_bad, 1);
-  if (threadIdx.x == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(&s_bad, 1);
-  __syncthreads();
-  if (s_bad) return;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad)) return;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     a[i] = 0.f;
     b2[i] = 0.f;
@@ -973,16 +1240,19 @@ gd_clear_kernel(float* __restrict__ a, float* __restrict__ b2, int64_t n, const 
 }
 
 struct GdBwdLayout {
-  size_t ck_s, ck_u, scratch, total;
+  size_t slots, ck_s, ck_u, ck_ds, ck_dr, total;
 };
 GdBwdLayout gd_bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t slots = (size_t)T / kGdC + (size_t)n_seg + 1;
   GdBwdLayout l;
+  l.slots = (size_t)T / kGdC + (size_t)n_seg + 1;
+  const size_t st = up(l.slots * H * kGdStateFloats * sizeof(float));
+  const size_t ch = up(l.slots * H * kGdChunkFloats * sizeof(float));
   l.ck_s = 0;
-  l.ck_u = up(slots * H * kGdD * kGdD * sizeof(float));
-  l.scratch = l.ck_u + up(slots * H * kGdC * kGdD * sizeof(float));
-  l.total = l.scratch + (size_t)std::max<int64_t>(1, (int64_t)n_seg * H) * kGdBwdScratch * sizeof(float);
+  l.ck_ds = st;
+  l.ck_u = 2 * st;
+  l.ck_dr = 2 * st + ch;
+  l.total = 2 * st + 2 * ch;
   return l;
 }
 
@@ -1012,9 +1282,10 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   if (grad_dtype != PVB_BF16 && grad_dtype != PVB_F32) return PVB_E_INVALID_ARG;
   if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != kGdD) return PVB_E_UNSUPPORTED;
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads))
-    return PVB_E_UNSUPPORTED;
   const GdBwdLayout lay = gd_bwd_layout(T, H, n_seg);
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads) ||
+      !grid_fits((uint64_t)lay.slots * H, kGdThreads))
+    return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
   if (hs != PVB_OK) return hs;
@@ -1022,7 +1293,8 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   char* ws = static_cast<char*>(workspace);
   float* ck_s = reinterpret_cast<float*>(ws + lay.ck_s);
   float* ck_u = reinterpret_cast<float*>(ws + lay.ck_u);
-  float* scr = reinterpret_cast<float*>(ws + lay.scratch);
+  float* ck_ds = reinterpret_cast<float*>(ws + lay.ck_ds);
+  float* ck_dr = reinterpret_cast<float*>(ws + lay.ck_dr);
   const bool atomic_qk = H != H_k;
   const int64_t nqk = (int64_t)T * H_k * d;
   if (atomic_qk && nqk > 0) {
@@ -1030,18 +1302,23 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
     gd_clear_kernel<<<blocks, 256, 0, s>>>(d_dq, d_dk, nqk, d_cu, n_seg, T);
   }
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
-  // recomputation pass: the chunk-start states and the U of every chunk (it
+  // pass 1, recomputation: the chunk-start states and the U of every chunk (it
   // also validates cu_seqlens and writes the status word)
   gated_delta_kernel<bf16, true><<<grid, kGdThreads, 0, s>>>(
       (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
       (bf16*)nullptr, nullptr, d_status, ck_s, ck_u);
+  // pass 2, the state-gradient chain: dS at every chunk's end, dR, dV, dh0
   if (grad_dtype == PVB_F32)
-    gated_delta_bwd_kernel<float><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
-        (const bf16*)d_dout, d_dht, ck_s, ck_u, scr, d_dq, d_dk, (float*)d_dv, d_dg, d_dbeta, d_dh0, atomic_qk);
+    gd_bwd_chain_kernel<float><<<grid, kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, (const bf16*)d_dout,
+        d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
   else
-    gated_delta_bwd_kernel<bf16><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
-        (const bf16*)d_dout, d_dht, ck_s, ck_u, scr, d_dq, d_dk, (bf16*)d_dv, d_dg, d_dbeta, d_dh0, atomic_qk);
+    gd_bwd_chain_kernel<bf16><<<grid, kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, (const bf16*)d_dout,
+        d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
+  // pass 3, chunk-parallel: dQ, dK, dg, dbeta
+  gd_bwd_chunk_kernel<<<(unsigned)(lay.slots * H), kGdThreads, 0, s>>>(
+      (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
+      (const bf16*)d_dout, ck_s, ck_u, ck_ds, ck_dr, d_dq, d_dk, d_dg, d_dbeta, atomic_qk);
   return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
 }
