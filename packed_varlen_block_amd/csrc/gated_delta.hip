@@ -84,16 +84,14 @@ __device__ __forceinline__ int crow(int i, int hg) { return 8 * (i >> 2) + 4 * h
 // state it stores, for every chunk, the state at the chunk's start and the
 // chunk's U (the solved right-hand side) in checkpoint slots (see
 // gd_ckpt_slot); the products that only feed O are skipped.
-template <typename OutT, bool CKPT = false>
-__global__ void __launch_bounds__(kGdThreads, 1)
-gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-                   const float* __restrict__ g, const float* __restrict__ beta,
-                   const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
-                   const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
-                   int32_t* __restrict__ status, float* __restrict__ ck_s = nullptr,
-                   float* __restrict__ ck_u = nullptr) {
-  __shared__ GdSmem sm;
-  __shared__ int s_bad;
+template <typename OutT, bool CKPT>
+__device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, const bf16* __restrict__ q,
+                                            const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                            const float* __restrict__ g, const float* __restrict__ beta,
+                                            const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
+                                            const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
+                                            int32_t* __restrict__ status, float* __restrict__ ck_s,
+                                            float* __restrict__ ck_u) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
 
@@ -104,10 +102,10 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
     if (cu[b + 1] < cu[b]) atomicOr(&s_bad, 1);
   if (tid == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(&s_bad, 1);
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0) *status = s_bad ? PVB_E_BAD_CU_SEQLENS : PVB_OK;
-  if (s_bad || (int)blockIdx.x >= n_seg * H) return;
+  if (blk == 0 && tid == 0) *status = s_bad ? PVB_E_BAD_CU_SEQLENS : PVB_OK;
+  if (s_bad || (int)blk >= n_seg * H) return;
 
-  const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int b = blk / H, h = blk - (blk / H) * H;
   const int hk = h / (H / Hk);                        // the query/key head of value head h
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
   const int n0 = 32 * w + c;                          // this lane's value column
@@ -436,6 +434,21 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
   }
 }
 
+
+template <typename OutT, bool CKPT = false>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                   const float* __restrict__ g, const float* __restrict__ beta,
+                   const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
+                   const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
+                   int32_t* __restrict__ status, float* __restrict__ ck_s = nullptr,
+                   float* __restrict__ ck_u = nullptr) {
+  __shared__ GdSmem sm;
+  __shared__ int s_bad;
+  gd_fwd_body<OutT, CKPT>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o, ht, status, ck_s,
+                          ck_u);
+}
+
 }  // namespace
 }  // namespace pvb
 
@@ -628,16 +641,18 @@ __device__ __forceinline__ void gd_ah_p_jobs(GdTiles& t, int w, int c, int hg) {
 }
 
 // Stages rows [t0, t0 + n) of Q and K (query/key head hk) and dO (value head
-// h) in the tiles, zero past n: 16-byte pieces, four per thread and tile.
+// h) in the tiles, zero past n: 16-byte pieces, 1024 / NT per thread and tile.
+template <int NT>
 struct GdStage {
-  uint4 q[4], k[4], o[4];
+  static constexpr int IT = 1024 / NT;
+  uint4 q[IT], k[IT], o[IT];
   float g, b;
   __device__ __forceinline__ void fetch(const bf16* q_, const bf16* k_, const bf16* do_, const float* g_,
                                         const float* beta_, int t0, int n, int H, int Hk, int h, int hk,
                                         int tid) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + kGdThreads * it;
+    for (int it = 0; it < IT; ++it) {
+      const int ch = tid + NT * it;
       const int row = ch >> 4, col = (ch & 15) * 8;
       q[it] = k[it] = o[it] = zero4();
       if (row < n) {
@@ -657,8 +672,8 @@ struct GdStage {
   }
   __device__ __forceinline__ void put(GdTiles& t, int tid) const {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + kGdThreads * it;
+    for (int it = 0; it < IT; ++it) {
+      const int ch = tid + NT * it;
       const int row = ch >> 4, col = (ch & 15) * 8;
       *(uint4*)&t.q[row][col] = q[it];
       *(uint4*)&t.k[row][col] = k[it];
@@ -690,20 +705,18 @@ struct GdChainSmem {
 // (C layout of four 32x32 blocks, rows = key dims), as the state does in the
 // forward.
 template <typename GradT>
-__global__ void __launch_bounds__(kGdThreads, 1)
-gd_bwd_chain_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+__device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, int blk, const bf16* __restrict__ q,
+                                                  const bf16* __restrict__ k, const float* __restrict__ g,
                     const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk,
                     float scale, const bf16* __restrict__ dout, const float* __restrict__ dht,
                     float* __restrict__ ck_ds, float* __restrict__ ck_dr, GradT* __restrict__ dv,
                     float* __restrict__ dh0) {
-  __shared__ GdChainSmem sm;
-  __shared__ int s_bad;
   GdTiles& t = sm.t;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
-  if (gd_cu_bad(cu, n_seg, T, &s_bad) || (int)blockIdx.x >= n_seg * H) return;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad) || (int)blk >= n_seg * H) return;
 
-  const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int b = blk / H, h = blk - (blk / H) * H;
   const int hk = h / (H / Hk);
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
   const int n0 = 32 * w + c;
@@ -717,7 +730,7 @@ gd_bwd_chain_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       dS[r][i] = dht ? dht[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
 
   const int n_chunks = (L + kGdC - 1) / kGdC;
-  GdStage pf;
+  GdStage<kGdThreads> pf;
   if (n_chunks > 0) {
     const int c0 = (n_chunks - 1) * kGdC;
     pf.fetch(q, k, dout, g, beta, seg0 + c0, L - c0, H, Hk, h, hk, tid);
@@ -900,20 +913,72 @@ gd_bwd_chain_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
   }
 }
 
+constexpr int kGdChunkThreads = 512;
+constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
+
+// Passes 1 and 2 in one launch: they do not depend on each other, so the
+// recomputation chain of a (slice, head) runs beside its state-gradient chain
+// on another CU.  Block 2j is the state-gradient chain of workgroup j, block
+// 2j + 1 its recomputation; the two share one LDS allocation.
+constexpr size_t kGdChainsLds = sizeof(GdSmem) > sizeof(GdChainSmem) ? sizeof(GdSmem) : sizeof(GdChainSmem);
+
+template <typename GradT>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_bwd_chains_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                     int n_seg, int T, int H, int Hk, float scale, const float* __restrict__ h0,
+                     int32_t* __restrict__ status, float* __restrict__ ck_s, float* __restrict__ ck_u,
+                     const bf16* __restrict__ dout, const float* __restrict__ dht, float* __restrict__ ck_ds,
+                     float* __restrict__ ck_dr, GradT* __restrict__ dv, float* __restrict__ dh0) {
+  __shared__ __align__(16) unsigned char raw[kGdChainsLds];
+  __shared__ int s_bad;
+  const int j = blockIdx.x >> 1;
+  if (blockIdx.x & 1)
+    gd_fwd_body<bf16, true>(*reinterpret_cast<GdSmem*>(raw), s_bad, j, q, k, v, g, beta, cu, n_seg, T, H, Hk,
+                            scale, h0, (bf16*)nullptr, nullptr, status, ck_s, ck_u);
+  else
+    gd_bwd_chain_body<GradT>(*reinterpret_cast<GdChainSmem*>(raw), s_bad, j, q, k, g, beta, cu, n_seg, T, H, Hk,
+                             scale, dout, dht, ck_ds, ck_dr, dv, dh0);
+}
+
 struct GdChunkSmem {
-  GdTiles t;
-  alignas(16) float da[kGdC][kFP];   // dA
-  alignas(16) float dp[kGdC][kFP];   // dP
-  float xr[4][kGdC], gr[4][kGdC], rk[4][kGdC];   // per-wave row partials
-  float part[2][4][kGdC];                        // row-sum partials over column quarters
-  float dgam[kGdC];
+  GdTiles t;                         // Ah and P become M and N in place
+  alignas(16) float u[kGdC][kUP];    // U
+  alignas(16) float dr[kGdC][kUP];   // dR
+  float xr[4][kGdC], gr[4][kGdC], rk[4][kGdC];   // row partials per column quarter
+  float rs[6][32], cs[6][32];                    // row and column partials of the dA / dP blocks
   float red[4];
+  int slice;
 };
 
-// Pass 3: one workgroup per (checkpoint slot, value head); slots that hold no
-// chunk return at once.  Wave w owns value columns [32w, 32w + 32) for the
-// row sums through K S0 and Q S0, and key dims [32w, 32w + 32) of dK and dQ.
-__global__ void __launch_bounds__(kGdThreads, 1)
+// Every workgroup checks the whole cu_seqlens before it writes anything; the
+// same pass finds the slice of checkpoint slot `slot`: the largest b whose
+// first slot cu[b] / 64 + b is at most slot (that first slot rises strictly
+// with b).
+__device__ __forceinline__ bool gd_cu_bad_find(const int32_t* __restrict__ cu, int n_seg, int T, int slot,
+                                               int* s_bad, int* s_b) {
+  if (threadIdx.x == 0) {
+    *s_bad = 0;
+    *s_b = 0;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < n_seg; b += blockDim.x) {
+    const int c0 = cu[b];
+    if (cu[b + 1] < c0) atomicOr(s_bad, 1);
+    if (c0 >= 0 && c0 / kGdC + b <= slot) atomicMax(s_b, b);
+  }
+  if (threadIdx.x == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(s_bad, 1);
+  __syncthreads();
+  return *s_bad != 0;
+}
+
+// Pass 3: one workgroup of 8 waves per (checkpoint slot, value head); slots
+// that hold no chunk return at once.  Wave w works on row block rb = w / 4
+// (positions [32 rb, 32 rb + 32)) and quarter cq = w % 4: value columns
+// [32 cq, 32 cq + 32) for the row sums through K S0 and Q S0, key dims
+// [32 cq, 32 cq + 32) of dK and dQ.  U and dR are staged in LDS once; S0 and
+// dS are read from the checkpoints where they are used, one k-step ahead.
+__global__ void __launch_bounds__(kGdChunkThreads, 1)
 gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
                     int n_seg, int T, int H, int Hk, float scale, const bf16* __restrict__ dout,
@@ -925,17 +990,10 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
   GdTiles& t = sm.t;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
-  if (gd_cu_bad(cu, n_seg, T, &s_bad) || n_seg == 0) return;
-
-  // slot -> (slice, chunk): the slice's first slot cu[b] / 64 + b rises strictly with b
+  const int rb = w >> 2, cq = w & 3;
   const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  int lo = 0, hi = n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] / kGdC + mid <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  const int b = lo, seg0 = cu[b], L = cu[b + 1] - seg0;
+  if (gd_cu_bad_find(cu, n_seg, T, slot, &s_bad, &sm.slice) || n_seg == 0) return;
+  const int b = sm.slice, seg0 = cu[b], L = cu[b + 1] - seg0;
   const int ci = slot - (seg0 / kGdC + b);
   if (ci < 0 || ci * kGdC >= L) return;
   const int hk = h / (H / Hk);
@@ -944,32 +1002,57 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
   const float* dSp = ck_ds + ((size_t)slot * H + h) * kGdStateFloats;
   const float* Up = ck_u + ((size_t)slot * H + h) * kGdChunkFloats;
   const float* dRp = ck_dr + ((size_t)slot * H + h) * kGdChunkFloats;
-  const int n0 = 32 * w + c;                          // this lane's value column, and key dim
+  const int n0 = 32 * cq + c;                         // this lane's value column, and key dim
 
   {
-    GdStage st;
+    GdStage<kGdChunkThreads> st;
     st.fetch(q, k, dout, g, beta, t0, n, H, Hk, h, hk, tid);
+    float4 xu[4], xd[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {                  // 16-byte pieces: row ch / 32, columns 4 (ch % 32)..
+      const int ch = tid + kGdChunkThreads * it;
+      xu[it] = *(const float4*)(Up + 4 * ch);
+      xd[it] = *(const float4*)(dRp + 4 * ch);
+    }
     st.put(t, tid);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + kGdChunkThreads * it;
+      *(float4*)&sm.u[ch >> 5][4 * (ch & 31)] = xu[it];
+      *(float4*)&sm.dr[ch >> 5][4 * (ch & 31)] = xd[it];
+    }
     if (w == 0) gd_gates(t, st.g, st.b, lane);
   }
+  // this wave's rows of V and its value columns of S0, in flight during the barrier
+  float vc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 32 * rb + crow(i, hg);
+    vc[i] = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
+  }
+  f32x16 S0c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S0c[r][i] = S0p[(size_t)(32 * r + crow(i, hg)) * kGdD + n0];
   __syncthreads();
 
-  gd_ah_p_jobs(t, w, c, hg);
-  if (w == 3) {                                       // block (0, 1) of Ah and P is zero
-    for (int e = lane; e < 32 * 32; e += 64) {
+  if (w < 6) {
+    // Ah and P blocks: KK (1,0), QK (0,0), QK (1,0), KK (0,0), KK (1,1), QK (1,1)
+    const bool isq = w == 1 || w == 2 || w == 5;
+    const int bi = (w == 1 || w == 3) ? 0 : 1, bj = (w == 4 || w == 5) ? 1 : 0;
+    gd_ah_p_block(t, isq, bi, bj, c, hg);
+  } else {                                            // block (0, 1) of Ah and P (then M and N) is zero
+    for (int e = tid - 384; e < 32 * 32; e += 128) {
       t.ah[e >> 5][32 + (e & 31)] = 0.f;
       t.p[e >> 5][32 + (e & 31)] = 0.f;
     }
   }
-  // ---- K S0 and Q S0 for this wave's value columns, then the row partials
-  // sum_c dR (V - G K S0) (for dbeta) and -beta sum_c dR K S0 + scale sum_c dO Q S0 (dG)
+  // ---- K S0 and Q S0 (row block rb, value columns of quarter cq), then the
+  // row partials sum_c dR (V - G K S0) (dbeta) and -beta sum_c dR K S0 +
+  // scale sum_c dO Q S0 (dG)
   {
-    f32x16 S0c[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S0c[r][i] = S0p[(size_t)(32 * r + crow(i, hg)) * kGdD + n0];
-    f32x16 ks[2] = {}, qs[2] = {};
+    f32x16 ks = {}, qs = {};
 #pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
       float sv[8];
@@ -977,51 +1060,49 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       for (int e = 0; e < 8; ++e) sv[e] = S0c[s >> 1][8 * (s & 1) + e];
       bf16x8 shi, slo;
       split8(sv, shi, slo);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16* kr = &t.k[32 * rb + c][16 * s + 4 * hg];
-        const bf16* qr = &t.q[32 * rb + c][16 * s + 4 * hg];
-        const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
-        const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
-        ks[rb] = mfma32(ka, shi, ks[rb]);
-        ks[rb] = mfma32(ka, slo, ks[rb]);
-        qs[rb] = mfma32(qa, shi, qs[rb]);
-        qs[rb] = mfma32(qa, slo, qs[rb]);
-      }
+      const bf16* kr = &t.k[32 * rb + c][16 * s + 4 * hg];
+      const bf16* qr = &t.q[32 * rb + c][16 * s + 4 * hg];
+      const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
+      const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
+      ks = mfma32(ka, shi, ks);
+      ks = mfma32(ka, slo, ks);
+      qs = mfma32(qa, shi, qs);
+      qs = mfma32(qa, slo, qs);
     }
+    float xr[16], gr[16];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float xr[16], gr[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * rb + crow(i, hg);
-        const float dr = dRp[(size_t)row * kGdD + n0];
-        const float vv = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
-        const float dov = (float)t.dO[row][n0];
-        xr[i] = dr * (vv - t.eg[row] * ks[rb][i]);
-        gr[i] = -t.beta[row] * dr * ks[rb][i] + scale * dov * qs[rb][i];
-      }
-      int idx;
-      const float sx = row_sum16(xr, c, idx);
-      const float sg = row_sum16(gr, c, idx);
-      if ((c & 1) == 0) {
-        const int row = 32 * rb + crow(idx, hg);
-        sm.xr[w][row] = sx;
-        sm.gr[w][row] = sg;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * rb + crow(i, hg);
+      const float dr = sm.dr[row][n0];
+      const float dov = (float)t.dO[row][n0];
+      xr[i] = dr * (vc[i] - t.eg[row] * ks[i]);
+      gr[i] = -t.beta[row] * dr * ks[i] + scale * dov * qs[i];
+    }
+    int idx;
+    const float sx = row_sum16(xr, c, idx);
+    const float sg = row_sum16(gr, c, idx);
+    if ((c & 1) == 0) {
+      const int row = 32 * rb + crow(idx, hg);
+      sm.xr[cq][row] = sx;
+      sm.gr[cq][row] = sg;
     }
   }
   __syncthreads();                                    // Ah and P are complete
 
   // ---- dA = -strict_lower(dR U^T) and dP = scale lower(dO U^T), contracted
-  // over all value columns (k index = column 16 s + 8 hg + e); block (0, 1) is zero
-  auto dadp_block = [&](bool isp, int bi, int bj) {
+  // over all value columns (k index = column 16 s + 8 hg + e), one block per
+  // wave: its row and column partials of dA o Ah (with beta of the row for the
+  // columns) and dP o P, then M = diag(beta) (Gam o dA) and N = Gam o dP
+  // written over Ah and P in place (each wave reads and writes its own block).
+  if (w < 6) {
+    const bool isp = w >= 3;
+    const int bi = (w == 1 || w == 3) ? 0 : 1, bj = (w == 2 || w == 5) ? 1 : 0;
     f32x16 acc = {};
-#pragma unroll 2
+#pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
       const int col = 16 * s + 8 * hg;
       float xu[8];
-      load8f(Up + (size_t)(32 * bj + c) * kGdD + col, xu);
+      load8f(&sm.u[32 * bj + c][col], xu);
       bf16x8 uh, ul;
       split8(xu, uh, ul);
       if (isp) {
@@ -1029,115 +1110,118 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
         acc = mfma32(a, uh, acc);
         acc = mfma32(a, ul, acc);
       } else {
-        float xr[8];
-        load8f(dRp + (size_t)(32 * bi + c) * kGdD + col, xr);
+        float xd[8];
+        load8f(&sm.dr[32 * bi + c][col], xd);
         bf16x8 rh, rl;
-        split8(xr, rh, rl);
+        split8(xd, rh, rl);
         acc = mfma32(rh, uh, acc);
         acc = mfma32(rh, ul, acc);
         acc = mfma32(rl, uh, acc);
       }
     }
+    const int cc = 32 * bj + c;
+    const float glc = t.gl[cc];
+    float rsum[16], csum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = 32 * bi + crow(i, hg), cc = 32 * bj + c;
-      if (isp) sm.dp[r][cc] = cc <= r ? scale * acc[i] : 0.f;
-      else sm.da[r][cc] = cc < r ? -acc[i] : 0.f;
+      const int r = 32 * bi + crow(i, hg);
+      const float gam = fast_exp2(fminf(t.gl[r] - glc, 0.f));
+      if (isp) {
+        const float dpv = cc <= r ? scale * acc[i] : 0.f;
+        const float prod = dpv * t.p[r][cc];
+        rsum[i] = prod;
+        csum += prod;
+        t.p[r][cc] = gam * dpv;
+      } else {
+        const float dav = cc < r ? -acc[i] : 0.f;
+        const float prod = dav * t.ah[r][cc];
+        const float br = t.beta[r];
+        rsum[i] = prod;
+        csum += br * prod;
+        t.ah[r][cc] = br * gam * dav;
+      }
     }
-  };
-  if (w == 0) { dadp_block(false, 1, 0); dadp_block(true, 0, 0); }
-  else if (w == 1) { dadp_block(false, 0, 0); dadp_block(true, 1, 1); }
-  else if (w == 2) { dadp_block(false, 1, 1); dadp_block(true, 1, 0); }
-  else {
-    for (int e = lane; e < 32 * 32; e += 64) {
-      sm.da[e >> 5][32 + (e & 31)] = 0.f;
-      sm.dp[e >> 5][32 + (e & 31)] = 0.f;
-    }
+    int idx;
+    const float rsv = row_sum16(rsum, c, idx);
+    csum += swap_halves(csum);
+    if ((c & 1) == 0) sm.rs[w][crow(idx, hg)] = rsv;
+    if (hg == 0) sm.cs[w][c] = csum;
   }
 
-  // ---- key dims [32w, 32w + 32) of dR S0^T, U dS^T (= dKt) and dO S0^T,
-  // contracted over all value columns; <dS, S0> over this wave's key dims; and
-  // the row partials sum_d dKt o Kt
-  f32x16 r1[2] = {}, kt1[2] = {}, q1[2] = {};
+  // ---- row block rb, key dims of quarter cq: dR S0^T, U dS^T (= dKt) and
+  // dO S0^T contracted over all value columns; <dS, S0> over these key dims
+  // (waves of row block 0); the row partials sum_d dKt o Kt
+  f32x16 r1 = {}, kt1 = {}, q1 = {};
   {
     float sdot = 0.f;
-    for (int s = 0; s < kGdD / 16; ++s) {
+    float xs[2][8], xds[2][8];
+    auto fetch = [&](int s, int buf) {
       const int col = 16 * s + 8 * hg;
-      float xs[8], xd[8];
-      load8f(S0p + (size_t)n0 * kGdD + col, xs);
-      load8f(dSp + (size_t)n0 * kGdD + col, xd);
+      load8f(S0p + (size_t)n0 * kGdD + col, xs[buf]);
+      load8f(dSp + (size_t)n0 * kGdD + col, xds[buf]);
+    };
+    fetch(0, 0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sdot += xs[e] * xd[e];
-      bf16x8 sh, sl, dh, dl;
-      split8(xs, sh, sl);
-      split8(xd, dh, dl);
+    for (int s = 0; s < kGdD / 16; ++s) {
+      const int cur = s & 1, col = 16 * s + 8 * hg;
+      if (s + 1 < kGdD / 16) fetch(s + 1, cur ^ 1);
+      if (rb == 0) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float xr[8], xu[8];
-        load8f(dRp + (size_t)(32 * rb + c) * kGdD + col, xr);
-        load8f(Up + (size_t)(32 * rb + c) * kGdD + col, xu);
-        bf16x8 rh, rl, uh, ul;
-        split8(xr, rh, rl);
-        split8(xu, uh, ul);
-        const bf16x8 oa = *(const bf16x8*)&t.dO[32 * rb + c][col];
-        r1[rb] = mfma32(rh, sh, r1[rb]);
-        r1[rb] = mfma32(rh, sl, r1[rb]);
-        r1[rb] = mfma32(rl, sh, r1[rb]);
-        kt1[rb] = mfma32(uh, dh, kt1[rb]);
-        kt1[rb] = mfma32(uh, dl, kt1[rb]);
-        kt1[rb] = mfma32(ul, dh, kt1[rb]);
-        q1[rb] = mfma32(oa, sh, q1[rb]);
-        q1[rb] = mfma32(oa, sl, q1[rb]);
+        for (int e = 0; e < 8; ++e) sdot += xs[cur][e] * xds[cur][e];
       }
+      float xr[8], xu[8];
+      load8f(&sm.dr[32 * rb + c][col], xr);
+      load8f(&sm.u[32 * rb + c][col], xu);
+      bf16x8 sh, sl, dh, dl, rh, rl, uh, ul;
+      split8(xs[cur], sh, sl);
+      split8(xds[cur], dh, dl);
+      split8(xr, rh, rl);
+      split8(xu, uh, ul);
+      const bf16x8 oa = *(const bf16x8*)&t.dO[32 * rb + c][col];
+      r1 = mfma32(rh, sh, r1);
+      r1 = mfma32(rh, sl, r1);
+      r1 = mfma32(rl, sh, r1);
+      kt1 = mfma32(uh, dh, kt1);
+      kt1 = mfma32(uh, dl, kt1);
+      kt1 = mfma32(ul, dh, kt1);
+      q1 = mfma32(oa, sh, q1);
+      q1 = mfma32(oa, sl, q1);
     }
+    if (rb == 0) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 64);
-    if (lane == 0) sm.red[w] = sdot;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * rb + crow(i, hg);
-        x[i] = kt1[rb][i] * t.dec[row] * (float)t.k[row][n0];
-      }
-      int idx;
-      const float sx = row_sum16(x, c, idx);
-      if ((c & 1) == 0) sm.rk[w][32 * rb + crow(idx, hg)] = sx;
+      for (int off = 32; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 64);
+      if (lane == 0) sm.red[cq] = sdot;
     }
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * rb + crow(i, hg);
+      x[i] = kt1[i] * t.dec[row] * (float)t.k[row][n0];
+    }
+    int idx;
+    const float sx = row_sum16(x, c, idx);
+    if ((c & 1) == 0) sm.rk[cq][32 * rb + crow(idx, hg)] = sx;
   }
-  __syncthreads();                                    // dA, dP and the row partials are complete
+  __syncthreads();                                    // M, N and every partial are complete
 
-  // ---- row sums over quarters of the columns: thread (quarter w, row i)
-  {
-    const int i = lane, j0 = 16 * w;
-    const float bi = t.beta[i];
-    float dba = 0.f, rpp = 0.f, cpp = 0.f, rpa = 0.f, cpa = 0.f;
-#pragma unroll 4
-    for (int j = j0; j < j0 + 16; ++j) {
-      const float aij = sm.da[i][j] * t.ah[i][j];
-      dba += aij;
-      cpa += t.beta[j] * sm.da[j][i] * t.ah[j][i];
-      rpp += sm.dp[i][j] * t.p[i][j];
-      cpp += sm.dp[j][i] * t.p[j][i];
-    }
-    rpa = bi * dba;
-    sm.part[0][w][i] = dba;
-    sm.part[1][w][i] = rpp - cpp + rpa - cpa;
-  }
-  __syncthreads();
+  // ---- dbeta and dg of the chunk's positions (wave 0, lane = position).  The
+  // dA blocks are waves 0 (1,0), 1 (0,0), 2 (1,1); the dP blocks waves 3 (0,0),
+  // 4 (1,0), 5 (1,1).
   if (w == 0) {
-    const int i = lane;
-    float dba = sm.xr[0][i] + sm.xr[1][i] + sm.xr[2][i] + sm.xr[3][i];
-    float dgm = 0.f, dG = 0.f, rk = 0.f;
+    const int i = lane, ii = i & 31;
+    const bool up = i >= 32;
+    const float rowA = up ? sm.rs[0][ii] + sm.rs[2][ii] : sm.rs[1][ii];
+    const float colA = up ? sm.cs[2][ii] : sm.cs[0][ii] + sm.cs[1][ii];
+    const float rowP = up ? sm.rs[4][ii] + sm.rs[5][ii] : sm.rs[3][ii];
+    const float colP = up ? sm.cs[5][ii] : sm.cs[3][ii] + sm.cs[4][ii];
+    float dba = rowA, dG = 0.f, rk = 0.f;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      dba += sm.part[0][qq][i];
-      dgm += sm.part[1][qq][i];
+      dba += sm.xr[qq][i];
       dG += sm.gr[qq][i];
       rk += sm.rk[qq][i];
     }
-    dgm += t.eg[i] * dG - rk;
+    float dgm = rowP - colP + t.beta[i] * rowA - colA + t.eg[i] * dG - rk;
     float tot = rk;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
@@ -1155,24 +1239,12 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       dbeta[(size_t)(t0 + i) * H + h] = dba;
     }
   }
-  __syncthreads();                                    // Ah and P are read for the last time
-
-  // ---- M + M^T (M = diag(beta) (Gam o dA), strictly lower) into Ah's LDS and
-  // N = Gam o dP into P's
-  for (int e = tid; e < kGdC * kGdC; e += kGdThreads) {
-    const int i = e >> 6, j = e & 63;
-    const float gij = fast_exp2(fminf(t.gl[i] - t.gl[j], 0.f));
-    const float gji = fast_exp2(fminf(t.gl[j] - t.gl[i], 0.f));
-    t.ah[i][j] = j < i ? t.beta[i] * gij * sm.da[i][j] : (j > i ? t.beta[j] * gji * sm.da[j][i] : 0.f);
-    t.p[i][j] = gij * sm.dp[i][j];
-  }
-  __syncthreads();
 
   // ---- dK = -diag(G beta) dR S0^T + diag(G_L / G) dKt + N^T Q + (M + M^T) K and
-  // dQ = scale diag(G) dO S0^T + N K for key dims [32w, 32w + 32); k index =
-  // position 16 s + 8 hg + e
+  // dQ = scale diag(G) dO S0^T + N K, row block rb, key dims of quarter cq;
+  // k index = position 16 s + 8 hg + e
   {
-    f32x16 ka[2] = {}, qa[2] = {};
+    f32x16 ka = {}, qa = {};
 #pragma unroll
     for (int s = 0; s < kGdC / 16; ++s) {
       const int p0 = 16 * s + 8 * hg;
@@ -1182,47 +1254,47 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
         bq[e] = t.q[p0 + e][n0];
         bk[e] = t.k[p0 + e][n0];
       }
+      bf16x8 hh, ll;
+      float x[8];
+      if (!(rb == 1 && s < 2)) {                      // N^T and M^T of row block 1 have no position below 32
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        bf16x8 hh, ll;
-        float x[8];
-        if (!(rb == 1 && s < 2)) {                    // N^T of row block 1 has no position below 32
+        for (int e = 0; e < 8; ++e) x[e] = t.p[p0 + e][32 * rb + c];
+        split8(x, hh, ll);
+        ka = mfma32(hh, bq, ka);
+        ka = mfma32(ll, bq, ka);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = t.p[p0 + e][32 * rb + c];
-          split8(x, hh, ll);
-          ka[rb] = mfma32(hh, bq, ka[rb]);
-          ka[rb] = mfma32(ll, bq, ka[rb]);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = t.ah[p0 + e][32 * rb + c];
+        split8(x, hh, ll);
+        ka = mfma32(hh, bk, ka);
+        ka = mfma32(ll, bk, ka);
+      }
+      if (!(rb == 0 && s >= 2)) {                     // N and M of row block 0 have no position past 31
         load8f(&t.ah[32 * rb + c][p0], x);
         split8(x, hh, ll);
-        ka[rb] = mfma32(hh, bk, ka[rb]);
-        ka[rb] = mfma32(ll, bk, ka[rb]);
-        if (!(rb == 0 && s >= 2)) {                   // N of row block 0 has no position past 31
-          load8f(&t.p[32 * rb + c][p0], x);
-          split8(x, hh, ll);
-          qa[rb] = mfma32(hh, bk, qa[rb]);
-          qa[rb] = mfma32(ll, bk, qa[rb]);
-        }
+        ka = mfma32(hh, bk, ka);
+        ka = mfma32(ll, bk, ka);
+        load8f(&t.p[32 * rb + c][p0], x);
+        split8(x, hh, ll);
+        qa = mfma32(hh, bk, qa);
+        qa = mfma32(ll, bk, qa);
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * rb + crow(i, hg);
-        if (row >= n) continue;
-        const float gr = t.eg[row];
-        const float kv = -gr * t.beta[row] * r1[rb][i] + t.dec[row] * kt1[rb][i] + ka[rb][i];
-        const float qv = scale * gr * q1[rb][i] + qa[rb][i];
-        const size_t o = ((size_t)(t0 + row) * Hk + hk) * kGdD + n0;
-        if (atomic_qk) {
-          atomicAdd(dk + o, kv);
-          atomicAdd(dq + o, qv);
-        } else {
-          dk[o] = kv;
-          dq[o] = qv;
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * rb + crow(i, hg);
+      if (row >= n) continue;
+      const float gr = t.eg[row];
+      const float kv = -gr * t.beta[row] * r1[i] + t.dec[row] * kt1[i] + ka[i];
+      const float qv = scale * gr * q1[i] + qa[i];
+      const size_t o = ((size_t)(t0 + row) * Hk + hk) * kGdD + n0;
+      if (atomic_qk) {
+        atomicAdd(dk + o, kv);
+        atomicAdd(dq + o, qv);
+      } else {
+        dk[o] = kv;
+        dq[o] = qv;
       }
+    }
   }
 }
 
@@ -1283,8 +1355,8 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != kGdD) return PVB_E_UNSUPPORTED;
   const GdBwdLayout lay = gd_bwd_layout(T, H, n_seg);
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads) ||
-      !grid_fits((uint64_t)lay.slots * H, kGdThreads))
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)2 * n_seg * H, kGdThreads) ||
+      !grid_fits((uint64_t)lay.slots * H, kGdChunkThreads))
     return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
@@ -1302,22 +1374,20 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
     gd_clear_kernel<<<blocks, 256, 0, s>>>(d_dq, d_dk, nqk, d_cu, n_seg, T);
   }
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
-  // pass 1, recomputation: the chunk-start states and the U of every chunk (it
-  // also validates cu_seqlens and writes the status word)
-  gated_delta_kernel<bf16, true><<<grid, kGdThreads, 0, s>>>(
-      (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-      (bf16*)nullptr, nullptr, d_status, ck_s, ck_u);
-  // pass 2, the state-gradient chain: dS at every chunk's end, dR, dV, dh0
+  // passes 1 and 2 side by side: the recomputation stores the chunk-start
+  // states and the U of every chunk (it also validates cu_seqlens and writes
+  // the status word); the state-gradient chain stores dS at every chunk's end
+  // and dR, and writes dV and dh0
   if (grad_dtype == PVB_F32)
-    gd_bwd_chain_kernel<float><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, (const bf16*)d_dout,
-        d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
+    gd_bwd_chains_kernel<float><<<2 * grid, kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+        d_status, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
   else
-    gd_bwd_chain_kernel<bf16><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, (const bf16*)d_dout,
-        d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
+    gd_bwd_chains_kernel<bf16><<<2 * grid, kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+        d_status, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
   // pass 3, chunk-parallel: dQ, dK, dg, dbeta
-  gd_bwd_chunk_kernel<<<(unsigned)(lay.slots * H), kGdThreads, 0, s>>>(
+  gd_bwd_chunk_kernel<<<(unsigned)(lay.slots * H), kGdChunkThreads, 0, s>>>(
       (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
       (const bf16*)d_dout, ck_s, ck_u, ck_ds, ck_dr, d_dq, d_dk, d_dg, d_dbeta, atomic_qk);
   return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
