@@ -91,7 +91,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
                                             const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
                                             const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
                                             int32_t* __restrict__ status, float* __restrict__ ck_s,
-                                            float* __restrict__ ck_u) {
+                                            float* __restrict__ ck_u, const float* __restrict__ ck_t) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
 
@@ -123,9 +123,17 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   // computed (and before its outputs are stored, so that waiting for them
   // never waits for those stores).
   uint4 pq[4], pk[4], pv[4];
+  float4 pt0, pt1, pt2, pt3;                          // CKPT: the chunk's T = (I + A)^-1
   float pg = 0.f, pb = 0.f;
   auto fetch = [&](int cc0) {
     const int nvv = min(kGdC, L - cc0);
+    if constexpr (CKPT) {
+      const float* tp = ck_t + (gd_ckpt_slot(seg0, b, cc0 / kGdC) * H + h) * (kGdC * kGdC) + 4 * tid;
+      pt0 = *(const float4*)tp;
+      pt1 = *(const float4*)(tp + 4 * kGdThreads);
+      pt2 = *(const float4*)(tp + 8 * kGdThreads);
+      pt3 = *(const float4*)(tp + 12 * kGdThreads);
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int ch = tid + kGdThreads * it;           // 16-byte chunk: row ch/16, columns 8(ch%16)..
@@ -168,6 +176,12 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       *(uint4*)&sm.q[row][col] = pq[it];
       *(uint4*)&sm.k[row][col] = pk[it];
       *(uint4*)&sm.v[row][col] = pv[it];
+    }
+    if constexpr (CKPT) {                             // T, row-major, in A^T's place
+      *(float4*)&sm.at[tid >> 4][4 * (tid & 15)] = pt0;
+      *(float4*)&sm.at[(tid >> 4) + 16][4 * (tid & 15)] = pt1;
+      *(float4*)&sm.at[(tid >> 4) + 32][4 * (tid & 15)] = pt2;
+      *(float4*)&sm.at[(tid >> 4) + 48][4 * (tid & 15)] = pt3;
     }
     if (w == 0) {
       float x = pg;                                   // inclusive sum over the chunk
@@ -222,10 +236,8 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
     };
     using KK = std::integral_constant<bool, false>;
     using QK = std::integral_constant<bool, true>;
-    if constexpr (CKPT) {                             // P only feeds O
-      if (w == 0) block(KK{}, 1, 0);
-      else if (w == 1) block(KK{}, 0, 0);
-      else if (w == 2) block(KK{}, 1, 1);
+    if constexpr (CKPT) {
+      // P only feeds O, and the solve takes T from the workspace
     } else {
       if (w == 0) { block(KK{}, 1, 0); block(QK{}, 0, 0); }
       else if (w == 1) { block(QK{}, 1, 0); block(KK{}, 0, 0); }
@@ -348,23 +360,53 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       for (int e = 0; e < 8; ++e) x[e] = ks[s >> 1][8 * (s & 1) + e];
       split8(x, uh[s], ul[s]);
     };
-    triangle(std::integral_constant<int, 0>{});
-    split_u(0);
-    split_u(1);
+    if constexpr (CKPT) {
+      // U = T rhs: A element e of lane (c, hg) at k-step s is T[32 rb + c][kpos(s, e, hg)]
+      // (two runs of four); row block 0 of T has no column past 31
+      f32x16 uu[2] = {};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float x[8];                                     // -A21 at row 32 + c, positions kpos(s, e, hg)
+      for (int s = 0; s < 4; ++s) {
+        float xb[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = -sm.at[kpos(s, e, hg)][32 + c];
-      bf16x8 ah, al;
-      split8(x, ah, al);
-      ks[1] = mfma32(ah, uh[s], ks[1]);
-      ks[1] = mfma32(ah, ul[s], ks[1]);
-      ks[1] = mfma32(al, uh[s], ks[1]);
+        for (int e = 0; e < 8; ++e) xb[e] = ks[s >> 1][8 * (s & 1) + e];
+        bf16x8 bh, bl;
+        split8(xb, bh, bl);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          if (rb == 0 && s >= 2) continue;
+          const float* tr = &sm.at[32 * rb + c][kpos(s, 0, hg)];
+          const float4 t0v = *(const float4*)tr, t1v = *(const float4*)(tr + 8);
+          const float xa[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+          bf16x8 ah, al;
+          split8(xa, ah, al);
+          uu[rb] = mfma32(ah, bh, uu[rb]);
+          uu[rb] = mfma32(ah, bl, uu[rb]);
+          uu[rb] = mfma32(al, bh, uu[rb]);
+        }
+      }
+      ks[0] = uu[0];
+      ks[1] = uu[1];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) split_u(s);
+    } else {
+      triangle(std::integral_constant<int, 0>{});
+      split_u(0);
+      split_u(1);
+  #pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        float x[8];                                     // -A21 at row 32 + c, positions kpos(s, e, hg)
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = -sm.at[kpos(s, e, hg)][32 + c];
+        bf16x8 ah, al;
+        split8(x, ah, al);
+        ks[1] = mfma32(ah, uh[s], ks[1]);
+        ks[1] = mfma32(ah, ul[s], ks[1]);
+        ks[1] = mfma32(al, uh[s], ks[1]);
+      }
+      triangle(std::integral_constant<int, 1>{});
+      split_u(2);
+      split_u(3);
     }
-    triangle(std::integral_constant<int, 1>{});
-    split_u(2);
-    split_u(3);
     if constexpr (CKPT) {
       float* cuu = ck_u + (slot * H + h) * kGdC * kGdD;
 #pragma unroll
@@ -442,11 +484,11 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
                    const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
                    const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
                    int32_t* __restrict__ status, float* __restrict__ ck_s = nullptr,
-                   float* __restrict__ ck_u = nullptr) {
+                   float* __restrict__ ck_u = nullptr, const float* __restrict__ ck_t = nullptr) {
   __shared__ GdSmem sm;
   __shared__ int s_bad;
   gd_fwd_body<OutT, CKPT>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o, ht, status, ck_s,
-                          ck_u);
+                          ck_u, ck_t);
 }
 
 }  // namespace
@@ -633,12 +675,7 @@ __device__ __forceinline__ void gd_ah_p_block(GdTiles& t, bool isq, int bi, int 
   }
 }
 
-__device__ __forceinline__ void gd_ah_p_jobs(GdTiles& t, int w, int c, int hg) {
-  if (w == 0) { gd_ah_p_block(t, false, 1, 0, c, hg); gd_ah_p_block(t, true, 0, 0, c, hg); }
-  else if (w == 1) { gd_ah_p_block(t, true, 1, 0, c, hg); gd_ah_p_block(t, false, 0, 0, c, hg); }
-  else if (w == 2) gd_ah_p_block(t, false, 1, 1, c, hg);
-  else gd_ah_p_block(t, true, 1, 1, c, hg);
-}
+
 
 // Stages rows [t0, t0 + n) of Q and K (query/key head hk) and dO (value head
 // h) in the tiles, zero past n: 16-byte pieces, 1024 / NT per thread and tile.
@@ -693,6 +730,27 @@ __device__ __forceinline__ bool gd_cu_bad(const int32_t* __restrict__ cu, int n_
   return *s_bad != 0;
 }
 
+// Every workgroup checks the whole cu_seqlens before it writes anything; the
+// same pass finds the slice of checkpoint slot `slot`: the largest b whose
+// first slot cu[b] / 64 + b is at most slot (that first slot rises strictly
+// with b).
+__device__ __forceinline__ bool gd_cu_bad_find(const int32_t* __restrict__ cu, int n_seg, int T, int slot,
+                                               int* s_bad, int* s_b) {
+  if (threadIdx.x == 0) {
+    *s_bad = 0;
+    *s_b = 0;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < n_seg; b += blockDim.x) {
+    const int c0 = cu[b];
+    if (cu[b + 1] < c0) atomicOr(s_bad, 1);
+    if (c0 >= 0 && c0 / kGdC + b <= slot) atomicMax(s_b, b);
+  }
+  if (threadIdx.x == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(s_bad, 1);
+  __syncthreads();
+  return *s_bad != 0;
+}
+
 struct GdChainSmem {
   GdTiles t;
   // A fragments of K^T and Q^T for the state-gradient update, [d_k block][k-step][lane]:
@@ -707,10 +765,12 @@ struct GdChainSmem {
 template <typename GradT>
 __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, int blk, const bf16* __restrict__ q,
                                                   const bf16* __restrict__ k, const float* __restrict__ g,
-                    const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk,
-                    float scale, const bf16* __restrict__ dout, const float* __restrict__ dht,
-                    float* __restrict__ ck_ds, float* __restrict__ ck_dr, GradT* __restrict__ dv,
-                    float* __restrict__ dh0) {
+                                                  const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                                                  int n_seg, int T, int H, int Hk, float scale,
+                                                  const bf16* __restrict__ dout, const float* __restrict__ dht,
+                                                  const float* __restrict__ ck_t, float* __restrict__ ck_ds,
+                                                  float* __restrict__ ck_dr, GradT* __restrict__ dv,
+                                                  float* __restrict__ dh0) {
   GdTiles& t = sm.t;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
@@ -731,9 +791,17 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
 
   const int n_chunks = (L + kGdC - 1) / kGdC;
   GdStage<kGdThreads> pf;
+  float4 ptm0, ptm1, ptm2, ptm3;                      // the chunk's T = (I + A)^-1, row-major
+  const float* tbase = ck_t + (gd_ckpt_slot(seg0, b, 0) * H + h) * (kGdC * kGdC) + 4 * tid;
+  const size_t tstep = (size_t)H * kGdC * kGdC;       // one checkpoint slot
   if (n_chunks > 0) {
     const int c0 = (n_chunks - 1) * kGdC;
     pf.fetch(q, k, dout, g, beta, seg0 + c0, L - c0, H, Hk, h, hk, tid);
+    const float* tp = tbase + (size_t)(n_chunks - 1) * tstep;
+    ptm0 = *(const float4*)tp;
+    ptm1 = *(const float4*)(tp + 4 * kGdThreads);
+    ptm2 = *(const float4*)(tp + 8 * kGdThreads);
+    ptm3 = *(const float4*)(tp + 12 * kGdThreads);
   }
   for (int ci = n_chunks - 1; ci >= 0; --ci) {
     const int t0 = seg0 + ci * kGdC;
@@ -748,14 +816,27 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
     }
     __syncthreads();                                  // the previous chunk's LDS reads are done
     pf.put(t, tid);
+    {                                                 // T into Ah's place
+      const int ch = tid;
+      *(float4*)&t.ah[ch >> 4][4 * (ch & 15)] = ptm0;
+      *(float4*)&t.ah[(ch >> 4) + 16][4 * (ch & 15)] = ptm1;
+      *(float4*)&t.ah[(ch >> 4) + 32][4 * (ch & 15)] = ptm2;
+      *(float4*)&t.ah[(ch >> 4) + 48][4 * (ch & 15)] = ptm3;
+    }
     if (w == 0) gd_gates(t, pf.g, pf.b, lane);
     if (ci > 0) {
       const int c0 = (ci - 1) * kGdC;
       pf.fetch(q, k, dout, g, beta, seg0 + c0, kGdC, H, Hk, h, hk, tid);
+      const float* tp = tbase + (size_t)(ci - 1) * tstep;
+      ptm0 = *(const float4*)tp;
+      ptm1 = *(const float4*)(tp + 4 * kGdThreads);
+      ptm2 = *(const float4*)(tp + 8 * kGdThreads);
+      ptm3 = *(const float4*)(tp + 12 * kGdThreads);
     }
     __syncthreads();
 
-    gd_ah_p_jobs(t, w, c, hg);
+    // the lower blocks of P: QK (0,0), (1,0), (1,1)
+    if (w < 3) gd_ah_p_block(t, true, w == 0 ? 0 : 1, w == 2 ? 1 : 0, c, hg);
     // K^T and Q^T fragments, once for the four waves
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -794,7 +875,7 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
         kds[rb] = mfma32(ka, slo, kds[rb]);
       }
     }
-    __syncthreads();                                  // Ah, P and the fragments are complete
+    __syncthreads();                                  // T, P and the fragments are complete
 
     // P^T dO: A element e of lane (c, hg) at k-step s is P[kpos(s, e, hg)][32 rb + c];
     // P^T of row block 1 has no position below 32
@@ -816,53 +897,33 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
 #pragma unroll
       for (int i = 0; i < 16; ++i) du[rb][i] = scale * du[rb][i] + t.dec[32 * rb + crow(i, hg)] * kds[rb][i];
 
-    // ---- dR = (I + A)^-T dU, A = diag(beta) Ah, in the C layout, blocked by
-    // 32 rows from the bottom: the lower block's triangle, the upper block's
-    // update by the matrix cores, the upper block's triangle.  Inside a block,
-    // row jj is final when reached from the block's end; the lane holding it
-    // hands it across the half-waves and every row above it subtracts
-    // A_(jj, row) times it.
-    auto triangle_t = [&](auto rb_tag) {
-      constexpr int RB = decltype(rb_tag)::value;
+    // ---- dR = (I + A)^-T dU = T^T dU: A element e of lane (c, hg) at k-step s
+    // is T[kpos(s, e, hg)][32 rb + c]; row block 1 of T^T has no column below 32
+    {
+      f32x16 dr[2] = {};
 #pragma unroll
-      for (int jj = 31; jj > 0; --jj) {
-        const int ij = 4 * (jj >> 3) + (jj & 3);    // element index of row jj
-        const bool own = ((jj >> 2) & 1) == hg;
-        const float x = du[RB][ij];
-        const float other = swap_halves(x);
-        const float rj = (own ? x : other) * t.beta[32 * RB + jj];
+      for (int s = 0; s < 4; ++s) {
+        float xb[8];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          if (8 * m >= jj) continue;                  // every row of the group is at or below jj
-          const float4 a4 = *(const float4*)&t.ah[32 * RB + jj][32 * RB + 8 * m + 4 * hg];
-          const int r0 = 8 * m + 4 * hg;
-          if (r0 + 0 < jj) du[RB][4 * m + 0] -= a4.x * rj;
-          if (r0 + 1 < jj) du[RB][4 * m + 1] -= a4.y * rj;
-          if (r0 + 2 < jj) du[RB][4 * m + 2] -= a4.z * rj;
-          if (r0 + 3 < jj) du[RB][4 * m + 3] -= a4.w * rj;
+        for (int e = 0; e < 8; ++e) xb[e] = du[s >> 1][8 * (s & 1) + e];
+        bf16x8 bh, bl;
+        split8(xb, bh, bl);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          if (rb == 1 && s < 2) continue;
+          float xa[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xa[e] = t.ah[kpos(s, e, hg)][32 * rb + c];
+          bf16x8 ah, al;
+          split8(xa, ah, al);
+          dr[rb] = mfma32(ah, bh, dr[rb]);
+          dr[rb] = mfma32(ah, bl, dr[rb]);
+          dr[rb] = mfma32(al, bh, dr[rb]);
         }
       }
-    };
-    triangle_t(std::integral_constant<int, 1>{});
-    // upper rows i: dU_i -= sum_{j in the lower block} A_ji dR_j; the lower
-    // block is the B operand straight from its C layout, A_ji read in that order
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float xa[8], xb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 + kpos(s2, e, hg);
-        xa[e] = -t.beta[j] * t.ah[j][c];
-        xb[e] = du[1][8 * s2 + e];
-      }
-      bf16x8 ah, al, bh, bl;
-      split8(xa, ah, al);
-      split8(xb, bh, bl);
-      du[0] = mfma32(ah, bh, du[0]);
-      du[0] = mfma32(ah, bl, du[0]);
-      du[0] = mfma32(al, bh, du[0]);
+      du[0] = dr[0];
+      du[1] = dr[1];
     }
-    triangle_t(std::integral_constant<int, 0>{});
 
     // ---- dV = diag(beta) dR (stored), dR into its checkpoint, and the new
     // dS = G_L dS + K^T dKS + scale Q^T diag(G) dO with dKS = -diag(G beta) dR
@@ -886,11 +947,16 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
     for (int s = 0; s < 4; ++s) {
       float x1[8], x2[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = kpos(s, e, hg);
-        const float gp = t.eg[pos];
-        x1[e] = -gp * t.beta[pos] * du[s >> 1][8 * (s & 1) + e];
-        x2[e] = scale * gp * (float)dob[s][e];
+      for (int hf = 0; hf < 2; ++hf) {                // positions kpos(s, 4 hf .. 4 hf + 3, hg): four in a row
+        const int p0 = kpos(s, 4 * hf, hg);
+        const float4 g4 = *(const float4*)&t.eg[p0], b4 = *(const float4*)&t.beta[p0];
+        const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int e = 4 * hf + e4;
+          x1[e] = -gv[e4] * bv[e4] * du[s >> 1][8 * (s & 1) + e];
+          x2[e] = scale * gv[e4] * (float)dob[s][e];
+        }
       }
       bf16x8 b1h, b1l, b2h, b2l;
       split8(x1, b1h, b1l);
@@ -916,6 +982,86 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
 constexpr int kGdChunkThreads = 512;
 constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
 
+// Pass 0: T = (I + A)^-1 of every chunk (A = diag(beta) strict_lower(Gam o K K^T),
+// which depends on no state), so that both chains apply the solve as a
+// product.  One wave per (checkpoint slot, value head): the three lower
+// blocks of K K^T on the matrix cores, then lane j takes column j of T by
+// forward substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj, in fp32.
+// Rows and columns past the chunk's end give the identity.
+struct GdTmatSmem {
+  alignas(16) bf16 k[kGdC][kKP];
+  alignas(16) float a[kGdC][kFP];
+  float gl[kGdC], beta[kGdC];
+};
+
+__global__ void __launch_bounds__(64)
+gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const float* __restrict__ beta,
+               const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float* __restrict__ ck_t) {
+  __shared__ GdTmatSmem sm;
+  __shared__ int s_bad, s_b;
+  const int lane = threadIdx.x, hg = lane >> 5, c = lane & 31;
+  const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  if (gd_cu_bad_find(cu, n_seg, T, slot, &s_bad, &s_b) || n_seg == 0) return;
+  const int b = s_b, seg0 = cu[b], L = cu[b + 1] - seg0;
+  const int ci = slot - (seg0 / kGdC + b);
+  if (ci < 0 || ci * kGdC >= L) return;
+  const int hk = h / (H / Hk);
+  const int t0 = seg0 + ci * kGdC, n = min(kGdC, L - ci * kGdC);
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int ch = lane + 64 * it, row = ch >> 4, col = (ch & 15) * 8;
+    *(uint4*)&sm.k[row][col] = row < n ? *(const uint4*)(k + ((size_t)(t0 + row) * Hk + hk) * kGdD + col) : zero4();
+  }
+  {
+    float x = lane < n ? g[(size_t)(t0 + lane) * H + h] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    sm.gl[lane] = x * kLog2e;
+    sm.beta[lane] = lane < n ? beta[(size_t)(t0 + lane) * H + h] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int blk = 0; blk < 3; ++blk) {                 // blocks (0,0), (1,0), (1,1)
+    const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < kGdD / 16; ++s) {
+      const bf16x8 a = *(const bf16x8*)&sm.k[32 * bi + c][16 * s + 8 * hg];
+      const bf16x8 bk = *(const bf16x8*)&sm.k[32 * bj + c][16 * s + 8 * hg];
+      acc = mfma32(a, bk, acc);
+    }
+    const int pj = 32 * bj + c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int pi = 32 * bi + crow(i, hg);
+      const float dcy = fast_exp2(fminf(sm.gl[pi] - sm.gl[pj], 0.f));
+      sm.a[pi][pj] = pj < pi ? sm.beta[pi] * acc[i] * dcy : 0.f;
+    }
+  }
+  for (int e = lane; e < 32 * 32; e += 64) sm.a[e >> 5][32 + (e & 31)] = 0.f;
+  __syncthreads();
+  float tc[kGdC];
+#pragma unroll
+  for (int i = 0; i < kGdC; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int l4 = 0; l4 < i; l4 += 4) {
+      const float4 a4 = *(const float4*)&sm.a[i][l4];
+      acc += a4.x * tc[l4];
+      if (l4 + 1 < i) acc += a4.y * tc[l4 + 1];
+      if (l4 + 2 < i) acc += a4.z * tc[l4 + 2];
+      if (l4 + 3 < i) acc += a4.w * tc[l4 + 3];
+    }
+    tc[i] = (i == lane ? 1.f : 0.f) - acc;
+  }
+  float* dst = ck_t + ((size_t)slot * H + h) * (kGdC * kGdC);
+#pragma unroll
+  for (int i = 0; i < kGdC; ++i) dst[i * kGdC + lane] = tc[i];
+}
+
 // Passes 1 and 2 in one launch: they do not depend on each other, so the
 // recomputation chain of a (slice, head) runs beside its state-gradient chain
 // on another CU.  Block 2j is the state-gradient chain of workgroup j, block
@@ -927,18 +1073,19 @@ __global__ void __launch_bounds__(kGdThreads, 1)
 gd_bwd_chains_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                      const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
                      int n_seg, int T, int H, int Hk, float scale, const float* __restrict__ h0,
-                     int32_t* __restrict__ status, float* __restrict__ ck_s, float* __restrict__ ck_u,
-                     const bf16* __restrict__ dout, const float* __restrict__ dht, float* __restrict__ ck_ds,
-                     float* __restrict__ ck_dr, GradT* __restrict__ dv, float* __restrict__ dh0) {
+                     int32_t* __restrict__ status, const float* __restrict__ ck_t, float* __restrict__ ck_s,
+                     float* __restrict__ ck_u, const bf16* __restrict__ dout, const float* __restrict__ dht,
+                     float* __restrict__ ck_ds, float* __restrict__ ck_dr, GradT* __restrict__ dv,
+                     float* __restrict__ dh0) {
   __shared__ __align__(16) unsigned char raw[kGdChainsLds];
   __shared__ int s_bad;
   const int j = blockIdx.x >> 1;
   if (blockIdx.x & 1)
     gd_fwd_body<bf16, true>(*reinterpret_cast<GdSmem*>(raw), s_bad, j, q, k, v, g, beta, cu, n_seg, T, H, Hk,
-                            scale, h0, (bf16*)nullptr, nullptr, status, ck_s, ck_u);
+                            scale, h0, (bf16*)nullptr, nullptr, status, ck_s, ck_u, ck_t);
   else
     gd_bwd_chain_body<GradT>(*reinterpret_cast<GdChainSmem*>(raw), s_bad, j, q, k, g, beta, cu, n_seg, T, H, Hk,
-                             scale, dout, dht, ck_ds, ck_dr, dv, dh0);
+                             scale, dout, dht, ck_t, ck_ds, ck_dr, dv, dh0);
 }
 
 struct GdChunkSmem {
@@ -950,27 +1097,6 @@ struct GdChunkSmem {
   float red[4];
   int slice;
 };
-
-// Every workgroup checks the whole cu_seqlens before it writes anything; the
-// same pass finds the slice of checkpoint slot `slot`: the largest b whose
-// first slot cu[b] / 64 + b is at most slot (that first slot rises strictly
-// with b).
-__device__ __forceinline__ bool gd_cu_bad_find(const int32_t* __restrict__ cu, int n_seg, int T, int slot,
-                                               int* s_bad, int* s_b) {
-  if (threadIdx.x == 0) {
-    *s_bad = 0;
-    *s_b = 0;
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < n_seg; b += blockDim.x) {
-    const int c0 = cu[b];
-    if (cu[b + 1] < c0) atomicOr(s_bad, 1);
-    if (c0 >= 0 && c0 / kGdC + b <= slot) atomicMax(s_b, b);
-  }
-  if (threadIdx.x == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(s_bad, 1);
-  __syncthreads();
-  return *s_bad != 0;
-}
 
 // Pass 3: one workgroup of 8 waves per (checkpoint slot, value head); slots
 // that hold no chunk return at once.  Wave w works on row block rb = w / 4
@@ -1312,7 +1438,7 @@ gd_clear_kernel(float* __restrict__ a, float* __restrict__ b2, int64_t n, const 
 }
 
 struct GdBwdLayout {
-  size_t slots, ck_s, ck_u, ck_ds, ck_dr, total;
+  size_t slots, ck_s, ck_u, ck_ds, ck_dr, ck_t, total;
 };
 GdBwdLayout gd_bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -1324,7 +1450,8 @@ GdBwdLayout gd_bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   l.ck_ds = st;
   l.ck_u = 2 * st;
   l.ck_dr = 2 * st + ch;
-  l.total = 2 * st + 2 * ch;
+  l.ck_t = 2 * st + 2 * ch;
+  l.total = l.ck_t + up(l.slots * H * kGdC * kGdC * sizeof(float));
   return l;
 }
 
@@ -1367,6 +1494,7 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   float* ck_u = reinterpret_cast<float*>(ws + lay.ck_u);
   float* ck_ds = reinterpret_cast<float*>(ws + lay.ck_ds);
   float* ck_dr = reinterpret_cast<float*>(ws + lay.ck_dr);
+  float* ck_t = reinterpret_cast<float*>(ws + lay.ck_t);
   const bool atomic_qk = H != H_k;
   const int64_t nqk = (int64_t)T * H_k * d;
   if (atomic_qk && nqk > 0) {
@@ -1374,6 +1502,9 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
     gd_clear_kernel<<<blocks, 256, 0, s>>>(d_dq, d_dk, nqk, d_cu, n_seg, T);
   }
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
+  // pass 0: T = (I + A)^-1 of every chunk
+  gd_tmat_kernel<<<(unsigned)(lay.slots * H), 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k,
+                                                          ck_t);
   // passes 1 and 2 side by side: the recomputation stores the chunk-start
   // states and the U of every chunk (it also validates cu_seqlens and writes
   // the status word); the state-gradient chain stores dS at every chunk's end
@@ -1381,11 +1512,11 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   if (grad_dtype == PVB_F32)
     gd_bwd_chains_kernel<float><<<2 * grid, kGdThreads, 0, s>>>(
         (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-        d_status, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
+        d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
   else
     gd_bwd_chains_kernel<bf16><<<2 * grid, kGdThreads, 0, s>>>(
         (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-        d_status, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
+        d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
   // pass 3, chunk-parallel: dQ, dK, dg, dbeta
   gd_bwd_chunk_kernel<<<(unsigned)(lay.slots * H), kGdChunkThreads, 0, s>>>(
       (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
