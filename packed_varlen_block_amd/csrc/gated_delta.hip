@@ -989,8 +989,10 @@ constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
 // forward substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj, in fp32.
 // Rows and columns past the chunk's end give the identity.
 struct GdTmatSmem {
-  alignas(16) bf16 k[kGdC][kKP];
-  alignas(16) float a[kGdC][kFP];
+  union {
+    alignas(16) bf16 k[kGdC][kKP];   // K, then A over it
+    alignas(16) float a[kGdC][kFP];
+  };
   float gl[kGdC], beta[kGdC];
 };
 
@@ -1023,22 +1025,28 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
     sm.beta[lane] = lane < n ? beta[(size_t)(t0 + lane) * H + h] : 0.f;
   }
   __syncthreads();
+  f32x16 kk[3];                                       // blocks (0,0), (1,0), (1,1) of K K^T
 #pragma unroll
-  for (int blk = 0; blk < 3; ++blk) {                 // blocks (0,0), (1,0), (1,1)
+  for (int blk = 0; blk < 3; ++blk) {
     const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
-    f32x16 acc = {};
+    kk[blk] = f32x16{};
 #pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
       const bf16x8 a = *(const bf16x8*)&sm.k[32 * bi + c][16 * s + 8 * hg];
       const bf16x8 bk = *(const bf16x8*)&sm.k[32 * bj + c][16 * s + 8 * hg];
-      acc = mfma32(a, bk, acc);
+      kk[blk] = mfma32(a, bk, kk[blk]);
     }
+  }
+  __syncthreads();                                    // K is read; A goes over it
+#pragma unroll
+  for (int blk = 0; blk < 3; ++blk) {
+    const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
     const int pj = 32 * bj + c;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int pi = 32 * bi + crow(i, hg);
       const float dcy = fast_exp2(fminf(sm.gl[pi] - sm.gl[pj], 0.f));
-      sm.a[pi][pj] = pj < pi ? sm.beta[pi] * acc[i] * dcy : 0.f;
+      sm.a[pi][pj] = pj < pi ? sm.beta[pi] * kk[blk][i] * dcy : 0.f;
     }
   }
   for (int e = lane; e < 32 * 32; e += 64) sm.a[e >> 5][32 + (e & 31)] = 0.f;
@@ -1046,16 +1054,16 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
   float tc[kGdC];
 #pragma unroll
   for (int i = 0; i < kGdC; ++i) {
-    float acc = 0.f;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;     // four partial sums shorten the dependent chain
 #pragma unroll
     for (int l4 = 0; l4 < i; l4 += 4) {
       const float4 a4 = *(const float4*)&sm.a[i][l4];
-      acc += a4.x * tc[l4];
-      if (l4 + 1 < i) acc += a4.y * tc[l4 + 1];
-      if (l4 + 2 < i) acc += a4.z * tc[l4 + 2];
-      if (l4 + 3 < i) acc += a4.w * tc[l4 + 3];
+      a0 += a4.x * tc[l4];
+      if (l4 + 1 < i) a1 += a4.y * tc[l4 + 1];
+      if (l4 + 2 < i) a2 += a4.z * tc[l4 + 2];
+      if (l4 + 3 < i) a3 += a4.w * tc[l4 + 3];
     }
-    tc[i] = (i == lane ? 1.f : 0.f) - acc;
+    tc[i] = (i == lane ? 1.f : 0.f) - ((a0 + a1) + (a2 + a3));
   }
   float* dst = ck_t + ((size_t)slot * H + h) * (kGdC * kGdC);
 #pragma unroll
