@@ -781,6 +781,12 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
   const int n0 = 32 * w + c;
   const size_t st_base = (size_t)(b * H + h) * kGdStateFloats;
+  // staging rows of this wave for row-piece stores: [64][kSP] fp32 in the Q/K/dO
+  // tiles, which hold nothing between a chunk's last product and the next
+  // chunk's staging; only this wave touches them
+  constexpr int kSP = 36;
+  float* stg = reinterpret_cast<float*>(&t.q[0][0]) + w * (kGdC * kSP);
+  auto wave_lds_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
 
   f32x16 dS[4];
 #pragma unroll
@@ -808,11 +814,26 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
     const int n = min(kGdC, L - ci * kGdC);
     const size_t slot = gd_ckpt_slot(seg0, b, ci);
     {
-      float* dst = ck_ds + (slot * H + h) * kGdStateFloats;
+      // dS at this chunk's end into its checkpoint: 64 rows at a time through
+      // this wave's staging rows, written as 32-byte row pieces
+      float* dst = ck_ds + (slot * H + h) * kGdStateFloats + 32 * w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] = dS[r][i];
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) stg[(32 * r2 + crow(i, hg)) * kSP + c] = dS[2 * half + r2][i];
+        wave_lds_fence();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int pc = lane + 64 * it, row = pc >> 2, q8 = pc & 3;
+          const float* src = stg + row * kSP + 8 * q8;
+          float* o = dst + (size_t)(64 * half + row) * kGdD + 8 * q8;
+          *(float4*)o = *(const float4*)src;
+          *(float4*)(o + 4) = *(const float4*)(src + 4);
+        }
+        wave_lds_fence();
+      }
     }
     __syncthreads();                                  // the previous chunk's LDS reads are done
     pf.put(t, tid);
@@ -925,19 +946,8 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
       du[1] = dr[1];
     }
 
-    // ---- dV = diag(beta) dR (stored), dR into its checkpoint, and the new
-    // dS = G_L dS + K^T dKS + scale Q^T diag(G) dO with dKS = -diag(G beta) dR
-    {
-      float* drp = ck_dr + (slot * H + h) * kGdChunkFloats;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 32 * rb + crow(i, hg);
-          drp[(size_t)row * kGdD + n0] = du[rb][i];
-          if (row < n) dv[((size_t)(t0 + row) * H + h) * kGdD + n0] = out_cast<GradT>(t.beta[row] * du[rb][i]);
-        }
-    }
+    // ---- the new dS = G_L dS + K^T dKS + scale Q^T diag(G) dO with
+    // dKS = -diag(G beta) dR
     const float gL = t.eg[kGdC - 1];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -969,6 +979,40 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
         dS[r] = mfma32(aq, b2h, dS[r]);
         dS[r] = mfma32(aq, b2l, dS[r]);
       }
+    }
+    // off the chain: dR into its checkpoint and dV = diag(beta) dR, through
+    // this wave's staging rows, written as 32-byte row pieces
+    {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) stg[(32 * rb + crow(i, hg)) * kSP + c] = du[rb][i];
+      wave_lds_fence();
+      float* drp = ck_dr + (slot * H + h) * kGdChunkFloats + 32 * w;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int pc = lane + 64 * it, row = pc >> 2, q8 = pc & 3;
+        const float* src = stg + row * kSP + 8 * q8;
+        const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+        float* o = drp + (size_t)row * kGdD + 8 * q8;
+        *(float4*)o = x0;
+        *(float4*)(o + 4) = x1;
+        if (row < n) {
+          const float bt = t.beta[row];
+          const float x[8] = {bt * x0.x, bt * x0.y, bt * x0.z, bt * x0.w, bt * x1.x, bt * x1.y, bt * x1.z, bt * x1.w};
+          GradT* od = dv + ((size_t)(t0 + row) * H + h) * kGdD + 32 * w + 8 * q8;
+          if constexpr (std::is_same_v<GradT, float>) {
+            *(float4*)od = make_float4(x[0], x[1], x[2], x[3]);
+            *(float4*)(od + 4) = make_float4(x[4], x[5], x[6], x[7]);
+          } else {
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = (bf16)x[e];
+            *(bf16x8*)od = pk;
+          }
+        }
+      }
+      wave_lds_fence();
     }
   }
   if (dh0) {
