@@ -426,10 +426,14 @@ pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void*
  * with respect to q, k, v, g, beta and the initial states, slice by slice
  * (nothing crosses a boundary; "Packing与 FlashAttention Varlen", section 6).
  * Exact in exact arithmetic: reverse-mode differentiation of the recurrence of
- * pvb_gated_delta_fwd.  The call first recomputes the forward, storing each
- * 64-token chunk's starting state and solved update in the workspace, then
- * walks every (slice, value head) back from its last chunk, carrying the
- * gradient of the state.
+ * pvb_gated_delta_fwd, evaluated on 64-token chunks.  The call enqueues on
+ * the stream (after clearing dq and dk when query/key heads are shared):
+ * T = (I + A)^-1 of every chunk; then, side by side,
+ * the forward's recomputation (each chunk's starting state and solved update)
+ * and the chain that carries the gradient of the state from each slice's last
+ * chunk to its first (with dv and dh0); then one pass over all chunks at once
+ * for dq, dk, dg and dbeta.  Products keep about 16 significant bits (two
+ * bf16 parts per fp32 operand); the rest is fp32.
  *   d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0
  *                  as in pvb_gated_delta_fwd_gqa (d_h0 nullable)
  *   d_dout         bf16 [T, H, d] gradient of O                         (device)
@@ -442,8 +446,8 @@ pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void*
  *   d_dg, d_dbeta  out fp32 [T, H]
  *   d_dh0          out fp32 [n_seg, H, d, d], nullable
  *   workspace      >= pvb_gated_delta_bwd_workspace_bytes(T, H, n_seg) bytes
- *                  (checkpoints: 96 KB per 64-token chunk and head; scratch:
- *                  288 KB per slice and head)                          (device)
+ *                  (208 KB per 64-token chunk slot and head, T/64 + n_seg + 1
+ *                  slots: about 3.7 GB at T = 32768, H = 32)           (device)
  * d = 128.  Device-detected error: PVB_E_BAD_CU_SEQLENS (then no gradient is
  * written). */
 size_t pvb_gated_delta_bwd_workspace_bytes(int32_t T, int32_t H, int32_t n_seg);
