@@ -149,3 +149,30 @@ def test_backward_long_mixed_pack_sampled_head():
     for name, a, bref in zip(("dq", "dk", "dv", "dg", "dbeta"), got, ref):
         _check(name, a.double().cpu().numpy(), bref)
     _check("dh0", dh0[:, h].double().cpu().numpy(), ref_h0)
+
+
+# Seeded random draws: chunk-edge and arbitrary slice lengths with zeros mixed
+# in, grouped heads, the gate and write-strength ranges, initial states and
+# final-state gradients, fp32 or bf16 dv, two scales.
+CHUNK_EDGES = [1, 63, 64, 65, 127, 128, 129, 192]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_backward_random_draws(case):
+    r = np.random.default_rng(6000 + case)
+    n = int(r.integers(1, 7))
+    lengths = [0 if (u := r.random()) < 0.12 else int(r.choice(CHUNK_EDGES)) if u < 0.5 else int(r.integers(1, 300))
+               for _ in range(n)]
+    if sum(lengths) == 0:
+        lengths[-1] = int(r.choice(CHUNK_EDGES))
+    Hk = int(r.integers(1, 4))
+    H = Hk * int(r.choice([1, 2, 4]))
+    g_range = [(0.0, 0.0), (-0.1, 0.0), (-1.0, 0.0), (-6.0, -2.0)][int(r.integers(0, 4))]
+    beta_range = [(0.05, 1.0), (0.9, 1.0), (0.0, 0.3)][int(r.integers(0, 3))]
+    h0, dht = bool(r.random() < 0.5), bool(r.random() < 0.5)
+    grad_dtype = "bf16" if r.random() < 0.3 else "f32"
+    scale = None if r.random() < 0.6 else 0.3
+    say(f"gated delta bwd random {case}: lengths={lengths} H={H} H_k={Hk} g={g_range} beta={beta_range} "
+        f"h0={h0} dht={dht} dv={grad_dtype} scale={scale}")
+    _case(6100 + case, lengths, H, Hk=Hk, g_range=g_range, beta_range=beta_range, h0=h0, dht=dht,
+          grad_dtype=grad_dtype, scale=scale)

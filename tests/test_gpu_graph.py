@@ -158,3 +158,65 @@ def test_gated_delta_graph_replays():
             say(f"  O max-abs {err_o:.3e}  state max-abs {err_s:.3e}")
             assert err_o <= 1e-3 * max(1.0, float(np.abs(ref_o).max()))
             assert err_s <= 1e-3 * max(1.0, float(np.abs(ref_s).max()))
+
+
+def test_gated_delta_backward_graph_replays():
+    """The gated delta backward recorded once into a HIP graph (its workspace
+    allocated before the capture; value and query/key heads one to one, so no
+    atomics and replays are bitwise repeatable) and replayed over two packs of
+    the same size; every replay equals an eager call bit for bit, and the
+    first two replays match O12."""
+    import packed_varlen_block_amd as pvb
+    import torch
+    packs = [[130, 0, 64, 257], [257, 64, 0, 130]]
+    H, d = 4, 128
+    T = int(np.sum(packs[0]))
+    sets = [W.random_gated_delta(2300 + i, p, H=H, initial_state=True) for i, p in enumerate(packs)]
+    r = np.random.default_rng(2310)
+    dos = [W.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32)) for _ in packs]
+    dev = torch.device("cuda:0")
+
+    def upload(w, do):
+        x = {n: (_bits(w[n]) if w[n].dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(w[n])))
+             for n in ("q", "k", "v", "g", "beta", "h0")}
+        x["do"] = _bits(do)
+        return x
+
+    st_in = {n: t.to(dev) for n, t in upload(sets[0], dos[0]).items()}
+    cu = torch.tensor(host_cu(packs[0]), dtype=torch.int32, device=dev)
+    ws = torch.empty(pvb.gated_delta_bwd_workspace_bytes(T, H, len(packs[0])), dtype=torch.uint8, device=dev)
+
+    def step(c, x):
+        return pvb.gated_delta_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], c, x["do"], initial_state=x["h0"],
+                                   workspace=ws)
+
+    out0 = step(cu, st_in)
+    pvb.check_status(out0[-1])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sout = step(cu, st_in)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+    for rep, i in enumerate([1, 0, 1]):
+        w = sets[i]
+        say(f"gated delta backward graph replay {rep}: pack {packs[i]}")
+        cu.copy_(torch.tensor(host_cu(packs[i]), dtype=torch.int32))
+        for n, t in upload(w, dos[i]).items():
+            st_in[n].copy_(t)
+        eager = step(cu.clone(), {n: t.clone() for n, t in st_in.items()})
+        pvb.check_status(eager[-1])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        pvb.check_status(sout[-1])
+        for n, a, b in zip(names, sout[:6], eager[:6]):
+            _same(n, a, b)
+        if rep < 2:
+            f = W.bf16_bits_to_f64
+            ref = LA.gated_delta_varlen_backward(f(w["q"]), f(w["k"]), f(w["v"]), w["g"].astype(np.float64),
+                                                 w["beta"].astype(np.float64), host_cu(packs[i]),
+                                                 1.0 / np.sqrt(d), f(dos[i]), w["h0"].astype(np.float64))
+            for n, a, b in zip(names, sout[:6], ref):
+                err = float(np.abs(a.double().cpu().numpy() - b).max())
+                say(f"  {n} max-abs {err:.3e}")
+                assert err <= 1e-3 * max(1.0, float(np.abs(b).max()))
