@@ -78,3 +78,77 @@ def test_packed_loss_past_2_to_the_32_elements():
     assert abs(float(out["loss"][0].item()) - total) <= 1e-6 * abs(total)
     del z, out
     torch.cuda.empty_cache()
+
+
+def test_gated_delta_forward_backward_at_the_element_limit():
+    """The gated delta rule, forward and backward, with T·H·d one token row short
+    of 2^31 elements in v, O, dO and dv (T = 262143, H = 64 value heads over 32
+    query/key heads, d = 128): byte offsets pass 4 GB, dq and dk are summed over
+    value-head pairs with atomics, and the backward's workspace is about 58 GB.
+    255 slices of 1024 tokens and a ragged last one of 1023, with initial states
+    and final-state gradients; slices at the start, in the middle and at the end
+    are compared with O11 and O12 on three value heads (and their query/key
+    heads, summed over both value heads that share each)."""
+    import packed_varlen_block_amd as pvb
+    import torch
+    from oracle import linear_attention as LA
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    T, H, Hk, d = 262143, 64, 32, 128
+    assert T * H * d < 2 ** 31 <= (T + 1) * H * d
+    lengths = [1024] * 255 + [1023]
+    B = len(lengths)
+    hc = host_cu(lengths)
+    dev = torch.device("cuda:0")
+    say(f"gated delta max size: T={T} H={H} H_k={Hk} d={d}, {B} slices")
+    q = W.device_unit_rows_bf16((T, Hk, d), 7101, dev)
+    k = W.device_unit_rows_bf16((T, Hk, d), 7102, dev)
+    v = W.device_normal_bf16((T, H, d), 7103, 1.0, dev)
+    do = W.device_normal_bf16((T, H, d), 7104, 1.0, dev)
+    g = W.device_uniform_f32((T, H), 7105, -0.1, 0.0, dev)
+    beta = W.device_uniform_f32((T, H), 7106, 0.05, 1.0, dev)
+    h0 = W.device_normal_bf16((B, H, d, d), 7107, 0.125, dev).float()
+    dht = W.device_normal_bf16((B, H, d, d), 7108, 0.125, dev).float()
+    cu = torch.tensor(hc).to(dev)
+    o, ht, st = pvb.gated_delta_fwd(q, k, v, g, beta, cu, h_cu=hc, initial_state=h0)
+    pvb.check_status(st)
+    dq, dk, dv, dg, db, dh0, st = pvb.gated_delta_bwd(q, k, v, g, beta, cu, do, h_cu=hc, initial_state=h0,
+                                                      dht=dht, grad_dtype=torch.bfloat16)
+    pvb.check_status(st)
+    sc = 1.0 / np.sqrt(d)
+
+    def bar(ref):
+        return 1e-3 * max(1.0, float(np.abs(ref).max()))
+    for b, heads in ((0, (0, 1)), (127, (36, 37)), (B - 1, (62, 63))):
+        a, e = int(hc[b]), int(hc[b + 1])
+        hk = heads[0] // 2
+        say(f"  slice {b}: rows [{a}, {e}), value heads {heads}, query/key head {hk}")
+        qo = q[a:e, hk].double().cpu().numpy()
+        ko = k[a:e, hk].double().cpu().numpy()
+        rdq, rdk = np.zeros((e - a, d)), np.zeros((e - a, d))
+        for h in heads:
+            vo = v[a:e, h].double().cpu().numpy()
+            go, bo = g[a:e, h].double().cpu().numpy(), beta[a:e, h].double().cpu().numpy()
+            s0 = h0[b, h].double().cpu().numpy()
+            ro, rs = LA.gated_delta_segment(qo, ko, vo, go, bo, sc, s0)
+            got = {"O": o[a:e, h].double().cpu().numpy(), "final state": ht[b, h].double().cpu().numpy()}
+            for name, ref in (("O", ro), ("final state", rs)):
+                err = float(np.abs(got[name] - ref).max())
+                extra = 2.0 ** -8 * float(np.abs(ref).max()) if name == "O" else 0.0
+                say(f"    h{h} {name}: max-abs {err:.3e}")
+                assert err <= bar(ref) + extra, name
+            r = LA.gated_delta_segment_backward(qo, ko, vo, go, bo, sc, do[a:e, h].double().cpu().numpy(), s0,
+                                                dht[b, h].double().cpu().numpy())
+            rdq += r[0]
+            rdk += r[1]
+            got = {"dv": dv[a:e, h], "dg": dg[a:e, h], "dbeta": db[a:e, h], "dh0": dh0[b, h]}
+            for name, ref in zip(("dv", "dg", "dbeta", "dh0"), r[2:]):
+                err = float(np.abs(got[name].double().cpu().numpy() - ref).max())
+                extra = 2.0 ** -8 * float(np.abs(ref).max()) if name == "dv" else 0.0
+                say(f"    h{h} {name}: max-abs {err:.3e}")
+                assert err <= bar(ref) + extra, name
+        for name, got, ref in (("dq", dq[a:e, hk], rdq), ("dk", dk[a:e, hk], rdk)):
+            err = float(np.abs(got.double().cpu().numpy() - ref).max())
+            say(f"    hk{hk} {name}: max-abs {err:.3e}")
+            assert err <= bar(ref), name
+    del q, k, v, do, o, ht, dq, dk, dv, dg, db, dh0
+    torch.cuda.empty_cache()

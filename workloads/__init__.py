@@ -282,3 +282,23 @@ def device_normal_bf16(shape, seed: int, scale: float, device):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return torch.randn(tuple(shape), generator=g, device=device, dtype=torch.bfloat16).mul_(scale)
+
+
+def device_unit_rows_bf16(shape, seed: int, device):
+    """Rows of unit norm (N(0,1) draws normalised over the last axis in float32,
+    then rounded to bf16), drawn on the device by torch's seeded generator, for
+    the gated delta rule's q and k at sizes too large for the host."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    x /= x.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    return x.to(torch.bfloat16)
+
+
+def device_uniform_f32(shape, seed: int, lo: float, hi: float, device):
+    """U(lo, hi) float32, drawn on the device by torch's seeded generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32).mul_(hi - lo).add_(lo)
