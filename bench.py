@@ -655,10 +655,12 @@ def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5, Hk=None):
     slice, then slices of 16-1024), H=32, d=128, bf16 O and fp32 final states,
     the state reset at every boundary; g ~ U(-0.1, 0), beta ~ U(0.05, 1), unit
     q and k (Hk query/key heads: H when None, else value heads share them in
-    groups).  Each (slice, head) is a chain of 64-token chunks, so the time is
-    set by the longest slice: reported per chunk of that chain, beside the
-    HBM rate of the algorithmic bytes (q, k, v, g, beta read once, O and the
-    final states written once).  Median of reps."""
+    groups).  Each (slice, head) is a chain of 64-token chunks; the default
+    evaluation cuts it into groups of 1024 tokens (the workspace call), and
+    `one_chain_ms` times the call without a workspace, one chain per (slice,
+    head), whose time is set by the longest slice.  Reported per chunk of that
+    slice, beside the HBM rate of the algorithmic bytes (q, k, v, g, beta read
+    once, O and the final states written once).  Median of reps."""
     lengths = W.lengths_cfg4(seed)
     T, B = int(lengths.sum()), len(lengths)
     g = torch.Generator(device=dev).manual_seed(seed + 11)
@@ -676,23 +678,29 @@ def gated_delta(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5, Hk=None):
     o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(2):
-        pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, status=st)
-    torch.cuda.synchronize()
-    ev = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, status=st)
-        e1.record(stream)
-        ev.append((e0, e1))
-    torch.cuda.synchronize()
-    pvb.check_status(st)
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ws = torch.empty(pvb.gated_delta_fwd_workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+
+    def timed(chain):
+        for _ in range(2):
+            pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, workspace=ws, chain=chain, status=st)
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, workspace=ws, chain=chain, status=st)
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        pvb.check_status(st)
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+    chain_ms = timed(True)
+    ms = timed(False)
     byts = (2 * Hk + 2 * H) * T * d * 2 + 2 * T * H * 4 + B * H * d * d * 4
     chain = int(-(-int(lengths.max()) // 64))
     name = "gdn_long_mixed_T32768_H32_d128" if Hk == H else f"gdn_long_mixed_T32768_H32_Hk{Hk}_d128"
-    return {"workload": name, "segments": B, "ms": round(ms, 4),
+    return {"workload": name, "segments": B, "ms": round(ms, 4), "one_chain_ms": round(chain_ms, 4),
+            "workspace_bytes": int(ws.numel()),
             "longest_chain_chunks": chain, "us_per_chunk": round(ms * 1e3 / chain, 3),
             "algorithmic_bytes": byts, "achieved_GBs": round(byts / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}

@@ -399,16 +399,28 @@ pvb_status pvb_varlen_cross_attn_bwd(const void* d_q, const void* d_k, const voi
  *   d_h0           fp32 [n_seg, H, d, d] initial states, nullable            (device)
  *   d_o            out [T, H, d], bf16 or fp32 per o_dtype                   (device)
  *   d_ht           out fp32 [n_seg, H, d, d] final states, nullable          (device)
+ *   workspace      >= pvb_gated_delta_fwd_workspace_bytes(T, H, n_seg) bytes
+ *                  (device), or null with workspace_bytes = 0
  *   d_status       out: device status word (required)                       (device)
- * d = 128 (else PVB_E_UNSUPPORTED).  No workspace.  The slices are computed in
- * chunks of 64 tokens (UT transform) in fp32 with matrix-core products whose
- * fp32 operands are split into two bf16 parts.  Device-detected error:
+ * d = 128 (else PVB_E_UNSUPPORTED).  The slices are computed in chunks of 64
+ * tokens (UT transform) in fp32 with matrix-core products whose fp32 operands
+ * are split into two bf16 parts.  With a workspace, the chain of chunks is cut
+ * into groups of 16 chunks (1024 tokens): T = (I + A)^-1 of every chunk first,
+ * then each group's map of its starting state (S_out = A_g S_in + Z_g, a
+ * product of the chunks' affine maps) for all groups at once, then each
+ * slice's group starting states in order, then every group's chunks from its
+ * starting state; a slice of n chunks then takes about 16 + n/16 + 16 serial
+ * steps instead of n.  Without one (null, 0), each (slice, head) walks its
+ * chunks in one chain, solving each chunk's triangle in place.  Both give the
+ * same results up to rounding.  A workspace smaller than required (or null
+ * with workspace_bytes > 0): PVB_E_WORKSPACE.  Device-detected error:
  * PVB_E_BAD_CU_SEQLENS (then O and ht are not written). */
+size_t pvb_gated_delta_fwd_workspace_bytes(int32_t T, int32_t H, int32_t n_seg);
 pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
                                const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
                                int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
                                const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
-                               int32_t* d_status, void* stream);
+                               void* workspace, size_t workspace_bytes, int32_t* d_status, void* stream);
 /* The same with grouped query/key heads: q and k are [T, H_k, d], v, g, beta,
  * O and the states carry H value heads, H a multiple of H_k, and value head h
  * reads query/key head h / (H / H_k) (the published Gated DeltaNet layers use
@@ -419,7 +431,8 @@ pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void*
                                    const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
                                    int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d,
                                    float scale, const float* d_h0, void* d_o, int32_t o_dtype,
-                                   float* d_ht, int32_t* d_status, void* stream);
+                                   float* d_ht, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                   void* stream);
 
 /* Backward of pvb_gated_delta_fwd_gqa: the gradients of
  *   sum_t o_t . dO_t + sum_b <ht[b], dht[b]>

@@ -37,8 +37,8 @@ STATUS_NAMES = {0: "PVB_OK", 1: "PVB_E_INVALID_ARG", 2: "PVB_E_OVERSIZED", 3: "P
 EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row", "pvb_boundaries_from_positions",
            "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
            "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
-           "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa", "pvb_gated_delta_bwd",
-           "pvb_gated_delta_bwd_workspace_bytes",
+           "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa", "pvb_gated_delta_fwd_workspace_bytes",
+           "pvb_gated_delta_bwd", "pvb_gated_delta_bwd_workspace_bytes",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_varlen_attn_bwd_noalloc", "pvb_status_string", "pvb_version")
 PVB_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of pvb_varlen_attn_bwd_noalloc
@@ -81,8 +81,11 @@ def lib() -> ctypes.CDLL:
                                           P, P, I32, P, SZ, P, P]
         L.pvb_gated_delta_bwd_workspace_bytes.argtypes = [I32, I32, I32]
         L.pvb_gated_delta_bwd_workspace_bytes.restype = SZ
-        L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, P]
-        L.pvb_gated_delta_fwd_gqa.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, I32, P, P, P]
+        L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, SZ, P, P]
+        L.pvb_gated_delta_fwd_gqa.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, I32, P, P, SZ,
+                                              P, P]
+        L.pvb_gated_delta_fwd_workspace_bytes.argtypes = [I32, I32, I32]
+        L.pvb_gated_delta_fwd_workspace_bytes.restype = SZ
         L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
         L.pvb_varlen_cross_attn_workspace_bytes.restype = SZ
         L.pvb_varlen_cross_attn_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F,
@@ -599,12 +602,18 @@ def varlen_cross_attn_bwd(q, k, v, o, do, lse, cu_q, cu_k, h_cu_q, h_cu_k, windo
     return dq, dk, dv, status
 
 
+def gated_delta_fwd_workspace_bytes(T: int, H: int, n_seg: int) -> int:
+    return int(lib().pvb_gated_delta_fwd_workspace_bytes(T, H, n_seg))
+
+
 def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=None, final_state=True,
-                    o_dtype=None, out=None, state_out=None, status=None):
+                    o_dtype=None, out=None, state_out=None, workspace=None, chain=False, status=None):
     """Gated delta rule over the packed stream, the state reset at every
     boundary of ``cu``.  q, k: contiguous bf16 CUDA [T, H_k, 128]; v: [T, H, 128]
     with H a multiple of H_k (value head h reads query/key head h // (H / H_k));
-    g, beta: fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].
+    g, beta: fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].  The
+    grouped evaluation takes a workspace (allocated when not given); chain=True
+    walks each slice's chunks in one chain without one.
     Returns (O [T, H, 128], final states [B, H, 128, 128] fp32 or None, status)."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, dim=3)
@@ -639,10 +648,15 @@ def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=N
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
         if hc.size != n_seg + 1:
             raise PvbError(1, "h_cu must have B+1 entries")
+    if chain:
+        wp, wb = None, 0
+    else:
+        workspace = _workspace_arg(workspace, gated_delta_fwd_workspace_bytes(T, H, n_seg), dev)
+        wp, wb = _ptr(workspace), workspace.numel() * workspace.element_size()
     rc = lib().pvb_gated_delta_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg,
                                        T, H, Hk, d, scale, _ptr(initial_state), _ptr(out), _dtype_code(out.dtype),
-                                       _ptr(ht) if ht is not None and ht.numel() > 0 else None, _ptr(status),
-                                       _stream(dev))
+                                       _ptr(ht) if ht is not None and ht.numel() > 0 else None, wp, wb,
+                                       _ptr(status), _stream(dev))
     _check(rc, "gated_delta_fwd")
     return out, ht, status
 

@@ -64,6 +64,15 @@ __host__ __device__ __forceinline__ size_t gd_ckpt_slot(int seg0, int b, int c) 
   return (size_t)(seg0 / 64) + (size_t)b + (size_t)c;
 }
 
+// Groups of 16 chunks (1024 tokens) for the grouped forward: group gi of
+// slice b (starting at token seg0) has slot seg0/1024 + b + gi, which never
+// collide for the same reason as the chunk slots; T/1024 + B + 1 slots.
+constexpr int kGdGrpTok = 1024;
+constexpr int kGdGrpChunks = kGdGrpTok / 64;
+__host__ __device__ __forceinline__ size_t gd_grp_slot(int seg0, int b, int gi) {
+  return (size_t)(seg0 / kGdGrpTok) + (size_t)b + (size_t)gi;
+}
+
 // Position of element e of a k-step s fragment whose k order follows the C
 // layout's rows (lane half hg): 16s + 8(e/4) + 4hg + e%4.
 __device__ __forceinline__ int kpos(int s, int e, int hg) { return 16 * s + 8 * (e >> 2) + 4 * hg + (e & 3); }
@@ -84,14 +93,16 @@ __device__ __forceinline__ int crow(int i, int hg) { return 8 * (i >> 2) + 4 * h
 // state it stores, for every chunk, the state at the chunk's start and the
 // chunk's U (the solved right-hand side) in checkpoint slots (see
 // gd_ckpt_slot); the products that only feed O are skipped.
-template <typename OutT, bool CKPT>
+template <typename OutT, bool CKPT, bool GROUPED = false>
 __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
                                             const float* __restrict__ g, const float* __restrict__ beta,
                                             const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
                                             const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
                                             int32_t* __restrict__ status, float* __restrict__ ck_s,
-                                            float* __restrict__ ck_u, const float* __restrict__ ck_t) {
+                                            float* __restrict__ ck_u, const float* __restrict__ ck_t,
+                                            const float* __restrict__ gstate = nullptr) {
+  constexpr bool USE_T = CKPT || GROUPED;            // the solve as U = T rhs, T from pass 0
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
 
@@ -103,21 +114,49 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   if (tid == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(&s_bad, 1);
   __syncthreads();
   if (blk == 0 && tid == 0) *status = s_bad ? PVB_E_BAD_CU_SEQLENS : PVB_OK;
-  if (s_bad || (int)blk >= n_seg * H) return;
+  if (s_bad) return;
 
-  const int b = blk / H, h = blk - (blk / H) * H;
+  // the (slice, value head) of this workgroup; GROUPED: a group of up to
+  // kGdGrpTok tokens of the slice, from its group slot (see gd_grp_slot)
+  int b, h, cbeg = 0;
+  size_t gslot = 0;
+  if constexpr (GROUPED) {
+    if (n_seg == 0) return;
+    gslot = (size_t)(blk / H);
+    h = blk - (blk / H) * H;
+    int lo = 0, hi = n_seg - 1;                       // the largest b with cu[b] / kGdGrpTok + b <= gslot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((size_t)(cu[mid] / kGdGrpTok + mid) <= gslot) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    const int gi = (int)(gslot - (size_t)(cu[b] / kGdGrpTok + b));
+    const int Lb = cu[b + 1] - cu[b];
+    if (gi < 0 || (gi > 0 && gi * kGdGrpTok >= Lb)) return;   // an empty slice keeps group 0
+    cbeg = gi * kGdGrpTok;
+  } else {
+    if ((int)blk >= n_seg * H) return;
+    b = blk / H;
+    h = blk - (blk / H) * H;
+  }
   const int hk = h / (H / Hk);                        // the query/key head of value head h
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
+  const int cend = GROUPED ? min(L, cbeg + kGdGrpTok) : L;
   const int n0 = 32 * w + c;                          // this lane's value column
   const size_t st_base = (size_t)(b * H + h) * kGdD * kGdD;
 
-  // the state, rows (key dims) 32r + crow(i, hg), column n0
+  // the state, rows (key dims) 32r + crow(i, hg), column n0; a group after the
+  // slice's first starts from the state the group scan left for it
+  const float* s_in = h0 ? h0 + st_base : nullptr;
+  if constexpr (GROUPED) {
+    if (cbeg > 0) s_in = gstate + (gslot * H + h) * kGdD * kGdD;
+  }
   f32x16 S[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      S[r][i] = h0 ? h0[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
+    for (int i = 0; i < 16; ++i) S[r][i] = s_in ? s_in[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
 
   // The inputs of chunk c + 1 are loaded into registers while chunk c is
   // computed (and before its outputs are stored, so that waiting for them
@@ -127,7 +166,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   float pg = 0.f, pb = 0.f;
   auto fetch = [&](int cc0) {
     const int nvv = min(kGdC, L - cc0);
-    if constexpr (CKPT) {
+    if constexpr (USE_T) {
       const float* tp = ck_t + (gd_ckpt_slot(seg0, b, cc0 / kGdC) * H + h) * (kGdC * kGdC) + 4 * tid;
       pt0 = *(const float4*)tp;
       pt1 = *(const float4*)(tp + 4 * kGdThreads);
@@ -154,9 +193,9 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       pb = beta[idx];
     }
   };
-  if (L > 0) fetch(0);
+  if (cbeg < cend) fetch(cbeg);
 
-  for (int c0 = 0; c0 < L; c0 += kGdC) {
+  for (int c0 = cbeg; c0 < cend; c0 += kGdC) {
     const int nv = min(kGdC, L - c0);
     const size_t slot = gd_ckpt_slot(seg0, b, c0 / kGdC);
     if constexpr (CKPT) {
@@ -177,7 +216,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       *(uint4*)&sm.k[row][col] = pk[it];
       *(uint4*)&sm.v[row][col] = pv[it];
     }
-    if constexpr (CKPT) {                             // T, row-major, in A^T's place
+    if constexpr (USE_T) {                            // T, row-major, in A^T's place
       *(float4*)&sm.at[tid >> 4][4 * (tid & 15)] = pt0;
       *(float4*)&sm.at[(tid >> 4) + 16][4 * (tid & 15)] = pt1;
       *(float4*)&sm.at[(tid >> 4) + 32][4 * (tid & 15)] = pt2;
@@ -197,7 +236,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       sm.dec[lane] = fast_exp2(last - x);
       sm.beta[lane] = pb;
     }
-    if (c0 + kGdC < L) fetch(c0 + kGdC);
+    if (c0 + kGdC < cend) fetch(c0 + kGdC);
     __syncthreads();
 
     // ---- A (for the solve, stored transposed) and P: the lower 32x32 blocks
@@ -238,6 +277,10 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
     using QK = std::integral_constant<bool, true>;
     if constexpr (CKPT) {
       // P only feeds O, and the solve takes T from the workspace
+    } else if constexpr (USE_T) {                     // P only: the solve takes T from the workspace
+      if (w == 0) block(QK{}, 0, 0);
+      else if (w == 1) block(QK{}, 1, 0);
+      else if (w == 2) block(QK{}, 1, 1);
     } else {
       if (w == 0) { block(KK{}, 1, 0); block(QK{}, 0, 0); }
       else if (w == 1) { block(QK{}, 1, 0); block(KK{}, 0, 0); }
@@ -360,7 +403,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       for (int e = 0; e < 8; ++e) x[e] = ks[s >> 1][8 * (s & 1) + e];
       split8(x, uh[s], ul[s]);
     };
-    if constexpr (CKPT) {
+    if constexpr (USE_T) {
       // U = T rhs: A element e of lane (c, hg) at k-step s is T[32 rb + c][kpos(s, e, hg)]
       // (two runs of four); row block 0 of T has no column past 31
       f32x16 uu[2] = {};
@@ -468,7 +511,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
     }
   }
 
-  if (!CKPT && ht) {
+  if (!CKPT && ht && cend == L) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -493,61 +536,6 @@ gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const
 
 }  // namespace
 }  // namespace pvb
-
-namespace pvb {
-namespace {
-pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
-                            const float* d_beta, const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
-                            int32_t T, int32_t H, int32_t H_k, int32_t d, float scale, const float* d_h0,
-                            void* d_o, int32_t o_dtype, float* d_ht, int32_t* d_status, void* stream) {
-  if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
-  if (H_k <= 0 || H % H_k != 0) return PVB_E_INVALID_ARG;
-  if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
-  if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_g == nullptr || d_beta == nullptr ||
-                d_o == nullptr))
-    return PVB_E_INVALID_ARG;
-  if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
-  if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
-  if (d != kGdD) return PVB_E_UNSUPPORTED;
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads))
-    return PVB_E_UNSUPPORTED;
-  const pvb_status hs = check_host_cu(h_cu, n_seg, T);
-  if (hs != PVB_OK) return hs;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // one workgroup per (slice, head); with no slice, one workgroup still checks
-  // cu_seqlens and writes the status
-  const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
-  if (o_dtype == PVB_F32)
-    gated_delta_kernel<float><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-        (float*)d_o, d_ht, d_status);
-  else
-    gated_delta_kernel<bf16><<<grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-        (bf16*)d_o, d_ht, d_status);
-  return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
-}
-}  // namespace
-}  // namespace pvb
-
-extern "C" pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
-                                          const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
-                                          int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
-                                          const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
-                                          int32_t* d_status, void* stream) {
-  return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H, d, scale, d_h0, d_o,
-                               o_dtype, d_ht, d_status, stream);
-}
-
-extern "C" pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
-                                              const float* d_g, const float* d_beta, const int32_t* d_cu,
-                                              const int32_t* h_cu, int32_t n_seg, int32_t T, int32_t H,
-                                              int32_t H_k, int32_t d, float scale, const float* d_h0,
-                                              void* d_o, int32_t o_dtype, float* d_ht, int32_t* d_status,
-                                              void* stream) {
-  return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_o,
-                               o_dtype, d_ht, d_status, stream);
-}
 
 namespace pvb {
 namespace {
@@ -1114,6 +1102,318 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
   for (int i = 0; i < kGdC; ++i) dst[i * kGdC + lane] = tc[i];
 }
 
+// ===========================================================================
+// The grouped forward: the chain of chunks cut into groups of 16.
+//
+// With T = (I + A)^-1 from pass 0, a chunk maps its starting state affinely,
+//   U = T diag(beta) V - T diag(beta G) K S0 = Ut - W S0,
+//   S_end = (G_L I - Kt^T W) S0 + Kt^T Ut = M S0 + B,   Kt = diag(G_L / G) K,
+// so a group of chunks maps it as S_out = A_g S_in + Z_g with A_g the product
+// of its chunks' M and Z_g the state it reaches from zero.  Pass 1 composes
+// (A_g, Z_g) for every group that another group follows, all groups at once;
+// pass 2 walks each slice's groups in order, S_(g+1) = A_g S_g + Z_g, leaving
+// every group's starting state; pass 3 (the forward kernel in GROUPED mode)
+// runs the chunks of every group from its starting state and writes O and
+// the final states.  The serial depth of a slice of n chunks goes from n
+// chunk steps to 16 + n/16 + 16 steps.  Every product splits its fp32
+// operands into bf16 hi + lo parts (three products), as the chunk kernels do.
+
+struct GdComposeSmem {
+  alignas(16) bf16 k[kGdC][kKP];
+  alignas(16) bf16 v[kGdC][kKP];
+  alignas(16) float tm[kGdC][kFP];                    // T, row-major
+  alignas(16) bf16x8 kth[4][4][64], ktl[4][4][64];    // Kt^T as split A fragments [d_k block][k-step][lane]
+  alignas(16) float m[kGdD][kGdD + 4];                // M, row-major
+  alignas(16) float eg[kGdC], dec[kGdC], beta[kGdC];
+};
+
+// Pass 1: one workgroup of 4 waves per (group slot, value head); groups that
+// are the last of their slice (or hold no chunk) return at once.  Wave w owns
+// columns [32w, 32w + 32) of A_g and Z_g (C layout, rows = key dims), and
+// forms M's columns [32w, 32w + 32) and B's before M is shared through LDS.
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
+                      const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H,
+                      int Hk, const float* __restrict__ ck_t, float* __restrict__ gA, float* __restrict__ gZ) {
+  __shared__ GdComposeSmem sm;
+  __shared__ int s_bad, s_b;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
+  const size_t gslot = blockIdx.x / H;
+  const int h = blockIdx.x - (blockIdx.x / H) * H;
+  if (tid == 0) {
+    s_bad = 0;
+    s_b = 0;
+  }
+  __syncthreads();
+  for (int b = tid; b < n_seg; b += kGdThreads) {
+    const int c0 = cu[b];
+    if (cu[b + 1] < c0) atomicOr(&s_bad, 1);
+    if (c0 >= 0 && (size_t)(c0 / kGdGrpTok + b) <= gslot) atomicMax(&s_b, b);
+  }
+  if (tid == 0 && (cu[0] != 0 || cu[n_seg] != T)) atomicOr(&s_bad, 1);
+  __syncthreads();
+  if (s_bad || n_seg == 0) return;
+  const int b = s_b, seg0 = cu[b], L = cu[b + 1] - seg0;
+  const int gi = (int)(gslot - gd_grp_slot(seg0, b, 0));
+  const int n_grp = (L + kGdGrpTok - 1) / kGdGrpTok;
+  if (gi < 0 || gi >= n_grp - 1) return;               // only full groups that another group follows
+  const int hk = h / (H / Hk);
+  const int n0 = 32 * w + c;
+
+  f32x16 Ac[4], Zc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      Ac[r][i] = 32 * r + crow(i, hg) == n0 ? 1.f : 0.f;
+      Zc[r][i] = 0.f;
+    }
+
+  for (int j = 0; j < kGdGrpChunks; ++j) {
+    const int ci = gi * kGdGrpChunks + j;
+    const int t0 = seg0 + ci * kGdC;                   // a full chunk: the group is not the slice's last
+    const float* tp = ck_t + (gd_ckpt_slot(seg0, b, ci) * H + h) * (kGdC * kGdC);
+    __syncthreads();                                   // the previous chunk's reads of LDS are done
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int ch = tid + kGdThreads * it;
+      const int row = ch >> 4, col = (ch & 15) * 8;
+      *(uint4*)&sm.k[row][col] = *(const uint4*)(k + ((size_t)(t0 + row) * Hk + hk) * kGdD + col);
+      *(uint4*)&sm.v[row][col] = *(const uint4*)(v + ((size_t)(t0 + row) * H + h) * kGdD + col);
+      *(float4*)&sm.tm[ch >> 4][4 * (ch & 15)] = *(const float4*)(tp + 4 * ch);
+    }
+    if (w == 0) {
+      float x = g[(size_t)(t0 + lane) * H + h];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      x *= kLog2e;
+      const float last = __shfl(x, 63, 64);
+      sm.eg[lane] = fast_exp2(x);
+      sm.dec[lane] = fast_exp2(last - x);
+      sm.beta[lane] = beta[(size_t)(t0 + lane) * H + h];
+    }
+    __syncthreads();
+    // Kt^T as split A fragments, once for the four waves
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int f = tid + kGdThreads * it;
+      const int r = f >> 8, s = (f >> 6) & 3, fl = f & 63, fc = fl & 31, fh = fl >> 5;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = kpos(s, e, fh);
+        x[e] = (float)sm.k[pos][32 * r + fc] * sm.dec[pos];
+      }
+      split8(x, sm.kth[r][s][fl], sm.ktl[r][s][fl]);
+    }
+    // W = T diag(beta G) K and Ut = T diag(beta) V, columns n0: A element e of
+    // lane (c, hg) at k-step s is T[32 rb + c][kpos(s, e, hg)]
+    f32x16 Wc[2] = {}, Uc[2] = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float xk[8], xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = kpos(s, e, hg);
+        const float bt = sm.beta[pos];
+        xk[e] = bt * sm.eg[pos] * (float)sm.k[pos][n0];
+        xv[e] = bt * (float)sm.v[pos][n0];
+      }
+      bf16x8 kh, kl, vh, vl;
+      split8(xk, kh, kl);
+      split8(xv, vh, vl);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        if (rb == 0 && s >= 2) continue;               // row block 0 of T has no column past 31
+        const float* tr = &sm.tm[32 * rb + c][kpos(s, 0, hg)];
+        const float4 a0 = *(const float4*)tr, a1 = *(const float4*)(tr + 8);
+        const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bf16x8 th, tl;
+        split8(xa, th, tl);
+        Wc[rb] = mfma32(th, kh, Wc[rb]);
+        Wc[rb] = mfma32(th, kl, Wc[rb]);
+        Wc[rb] = mfma32(tl, kh, Wc[rb]);
+        Uc[rb] = mfma32(th, vh, Uc[rb]);
+        Uc[rb] = mfma32(th, vl, Uc[rb]);
+        Uc[rb] = mfma32(tl, vh, Uc[rb]);
+      }
+    }
+    __syncthreads();                                   // the Kt^T fragments are complete
+    // M = G_L I - Kt^T W and B = Kt^T Ut, columns n0 (W and Ut as the B
+    // operand straight from their C layout)
+    f32x16 Mc[4] = {}, Bc[4] = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float xw[8], xu[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xw[e] = Wc[s >> 1][8 * (s & 1) + e];
+        xu[e] = Uc[s >> 1][8 * (s & 1) + e];
+      }
+      bf16x8 wh, wl, uh, ul;
+      split8(xw, wh, wl);
+      split8(xu, uh, ul);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16x8 ah = sm.kth[r][s][lane], al = sm.ktl[r][s][lane];
+        Mc[r] = mfma32(ah, wh, Mc[r]);
+        Mc[r] = mfma32(ah, wl, Mc[r]);
+        Mc[r] = mfma32(al, wh, Mc[r]);
+        Bc[r] = mfma32(ah, uh, Bc[r]);
+        Bc[r] = mfma32(ah, ul, Bc[r]);
+        Bc[r] = mfma32(al, uh, Bc[r]);
+      }
+    }
+    const float gL = sm.eg[kGdC - 1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * r + crow(i, hg);
+        sm.m[row][n0] = (row == n0 ? gL : 0.f) - Mc[r][i];
+      }
+    __syncthreads();                                   // M is complete
+    // Z <- M Z + B and A <- M A, columns n0: A element e of lane (c, hg) at
+    // k-step s is M[32 r + c][kpos(s, e, hg)]
+    f32x16 An[4] = {};
+#pragma unroll
+    for (int s = 0; s < kGdD / 16; ++s) {
+      float xz[8], xa[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xz[e] = Zc[s >> 1][8 * (s & 1) + e];
+        xa[e] = Ac[s >> 1][8 * (s & 1) + e];
+      }
+      bf16x8 zh, zl, ah2, al2;
+      split8(xz, zh, zl);
+      split8(xa, ah2, al2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float* mr = &sm.m[32 * r + c][kpos(s, 0, hg)];
+        const float4 m0 = *(const float4*)mr, m1 = *(const float4*)(mr + 8);
+        const float xm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        bf16x8 mh, ml;
+        split8(xm, mh, ml);
+        Bc[r] = mfma32(mh, zh, Bc[r]);
+        Bc[r] = mfma32(mh, zl, Bc[r]);
+        Bc[r] = mfma32(ml, zh, Bc[r]);
+        An[r] = mfma32(mh, ah2, An[r]);
+        An[r] = mfma32(mh, al2, An[r]);
+        An[r] = mfma32(ml, ah2, An[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Zc[r] = Bc[r];
+      Ac[r] = An[r];
+    }
+  }
+  float* pa = gA + (gslot * H + h) * kGdD * kGdD;
+  float* pz = gZ + (gslot * H + h) * kGdD * kGdD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const size_t e = (size_t)(32 * r + crow(i, hg)) * kGdD + n0;
+      pa[e] = Ac[r][i];
+      pz[e] = Zc[r][i];
+    }
+}
+
+// Pass 2: one workgroup per (slice, value head) with more than one group;
+// S_(g+1) = A_g S_g + Z_g from the initial state (zero when absent), stored
+// as group g+1's starting state.  Wave w owns value columns [32w, 32w + 32).
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, const float* __restrict__ h0,
+                   const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS) {
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad) || (int)blockIdx.x >= n_seg * H) return;
+  const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int seg0 = cu[b], L = cu[b + 1] - seg0;
+  const int n_grp = (L + kGdGrpTok - 1) / kGdGrpTok;
+  if (n_grp < 2) return;
+  const int n0 = 32 * w + c;
+  const size_t st_base = (size_t)(b * H + h) * kGdD * kGdD;
+  f32x16 S[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[r][i] = h0 ? h0[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
+  for (int gi = 0; gi + 1 < n_grp; ++gi) {
+    const size_t slot = gd_grp_slot(seg0, b, gi);
+    const float* pa = gA + (slot * H + h) * kGdD * kGdD;
+    const float* pz = gZ + (slot * H + h) * kGdD * kGdD;
+    f32x16 Sn[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Sn[r][i] = pz[(size_t)(32 * r + crow(i, hg)) * kGdD + n0];
+#pragma unroll
+    for (int s = 0; s < kGdD / 16; ++s) {
+      float xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = S[s >> 1][8 * (s & 1) + e];
+      bf16x8 sh, sl;
+      split8(xs, sh, sl);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float* ar = pa + (size_t)(32 * r + c) * kGdD + kpos(s, 0, hg);
+        const float4 a0 = *(const float4*)ar, a1 = *(const float4*)(ar + 8);
+        const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bf16x8 ah, al;
+        split8(xa, ah, al);
+        Sn[r] = mfma32(ah, sh, Sn[r]);
+        Sn[r] = mfma32(ah, sl, Sn[r]);
+        Sn[r] = mfma32(al, sh, Sn[r]);
+      }
+    }
+    float* ps = gS + ((slot + 1) * H + h) * kGdD * kGdD;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      S[r] = Sn[r];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] = S[r][i];
+    }
+  }
+}
+
+// Pass 3: the forward kernel on every group from its starting state.
+template <typename OutT>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_fwd_grouped_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                      const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                      int n_seg, int T, int H, int Hk, float scale, const float* __restrict__ h0,
+                      OutT* __restrict__ o, float* __restrict__ ht, int32_t* __restrict__ status,
+                      const float* __restrict__ ck_t, const float* __restrict__ gS) {
+  __shared__ GdSmem sm;
+  __shared__ int s_bad;
+  gd_fwd_body<OutT, false, true>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o, ht,
+                                 status, nullptr, nullptr, ck_t, gS);
+}
+
+struct GdFwdLayout {
+  size_t slots, gslots, ck_t, gA, gZ, gS, total;
+};
+GdFwdLayout gd_fwd_layout(int32_t T, int32_t H, int32_t n_seg) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  GdFwdLayout l;
+  l.slots = (size_t)T / kGdC + (size_t)n_seg + 1;
+  l.gslots = (size_t)T / kGdGrpTok + (size_t)n_seg + 1;
+  const size_t gs = up(l.gslots * H * kGdD * kGdD * sizeof(float));
+  l.ck_t = 0;
+  l.gA = up(l.slots * H * kGdC * kGdC * sizeof(float));
+  l.gZ = l.gA + gs;
+  l.gS = l.gZ + gs;
+  l.total = l.gS + gs;
+  return l;
+}
+
 // Passes 1 and 2 in one launch: they do not depend on each other, so the
 // recomputation chain of a (slice, head) runs beside its state-gradient chain
 // on another CU.  Block 2j is the state-gradient chain of workgroup j, block
@@ -1574,4 +1874,101 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
       (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
       (const bf16*)d_dout, ck_s, ck_u, ck_ds, ck_dr, d_dq, d_dk, d_dg, d_dbeta, atomic_qk);
   return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+
+namespace pvb {
+namespace {
+pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                            const float* d_beta, const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                            int32_t T, int32_t H, int32_t H_k, int32_t d, float scale, const float* d_h0,
+                            void* d_o, int32_t o_dtype, float* d_ht, void* workspace, size_t workspace_bytes,
+                            int32_t* d_status, void* stream) {
+  if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
+  if (H_k <= 0 || H % H_k != 0) return PVB_E_INVALID_ARG;
+  if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
+  if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_g == nullptr || d_beta == nullptr ||
+                d_o == nullptr))
+    return PVB_E_INVALID_ARG;
+  if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
+  if (d != kGdD) return PVB_E_UNSUPPORTED;
+  const GdFwdLayout lay = gd_fwd_layout(T, H, n_seg);
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads) ||
+      !grid_fits((uint64_t)lay.slots * H, kGdThreads))
+    return PVB_E_UNSUPPORTED;
+  const bool grouped = workspace != nullptr || workspace_bytes != 0;
+  if (grouped && (workspace == nullptr || workspace_bytes < lay.total)) return PVB_E_WORKSPACE;
+  const pvb_status hs = check_host_cu(h_cu, n_seg, T);
+  if (hs != PVB_OK) return hs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!grouped) {
+    // one chain per (slice, head); with no slice, one workgroup still checks
+    // cu_seqlens and writes the status
+    const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
+    if (o_dtype == PVB_F32)
+      gated_delta_kernel<float><<<grid, kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+          (float*)d_o, d_ht, d_status);
+    else
+      gated_delta_kernel<bf16><<<grid, kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+          (bf16*)d_o, d_ht, d_status);
+    return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* ck_t = reinterpret_cast<float*>(ws + lay.ck_t);
+  float* gA = reinterpret_cast<float*>(ws + lay.gA);
+  float* gZ = reinterpret_cast<float*>(ws + lay.gZ);
+  float* gS = reinterpret_cast<float*>(ws + lay.gS);
+  // pass 0: T of every chunk; passes 1 and 2 only when a slice spans more than
+  // one group (known without the host mirror only on the device)
+  bool multi = true;
+  if (h_cu != nullptr) {
+    multi = false;
+    for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
+  }
+  gd_tmat_kernel<<<(unsigned)(lay.slots * H), 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k,
+                                                          ck_t);
+  if (multi) {
+    gd_grp_compose_kernel<<<(unsigned)(lay.gslots * H), kGdThreads, 0, s>>>(
+        (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ);
+    gd_grp_scan_kernel<<<(unsigned)std::max<int64_t>(1, (int64_t)n_seg * H), kGdThreads, 0, s>>>(
+        d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
+  }
+  if (o_dtype == PVB_F32)
+    gd_fwd_grouped_kernel<float><<<(unsigned)(lay.gslots * H), kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+        (float*)d_o, d_ht, d_status, ck_t, gS);
+  else
+    gd_fwd_grouped_kernel<bf16><<<(unsigned)(lay.gslots * H), kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+        (bf16*)d_o, d_ht, d_status, ck_t, gS);
+  return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+}  // namespace
+}  // namespace pvb
+
+extern "C" size_t pvb_gated_delta_fwd_workspace_bytes(int32_t T, int32_t H, int32_t n_seg) {
+  if (T < 0 || H <= 0 || n_seg < 0) return 0;
+  return pvb::gd_fwd_layout(T, H, n_seg).total;
+}
+
+extern "C" pvb_status pvb_gated_delta_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                          const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                                          int32_t n_seg, int32_t T, int32_t H, int32_t d, float scale,
+                                          const float* d_h0, void* d_o, int32_t o_dtype, float* d_ht,
+                                          void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                          void* stream) {
+  return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H, d, scale, d_h0, d_o,
+                               o_dtype, d_ht, workspace, workspace_bytes, d_status, stream);
+}
+
+extern "C" pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void* d_v,
+                                              const float* d_g, const float* d_beta, const int32_t* d_cu,
+                                              const int32_t* h_cu, int32_t n_seg, int32_t T, int32_t H,
+                                              int32_t H_k, int32_t d, float scale, const float* d_h0,
+                                              void* d_o, int32_t o_dtype, float* d_ht, void* workspace,
+                                              size_t workspace_bytes, int32_t* d_status, void* stream) {
+  return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_o,
+                               o_dtype, d_ht, workspace, workspace_bytes, d_status, stream);
 }

@@ -267,7 +267,7 @@ def test_cross_workspace_sizes():
 def test_gated_delta_host_side_errors():
     L = pvb.lib()
     ok = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=2, d=128,
-              scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, status=FAKE)
+              scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, ws=None, ws_bytes=0, status=FAKE)
 
     def call(**kw):
         a = dict(ok, **kw)
@@ -288,12 +288,28 @@ def test_gated_delta_host_side_errors():
     assert call(h_cu=bad.ctypes.data) == 4
     dec = np.array([0, 6, 5, 8], np.int32)
     assert call(h_cu=dec.ctypes.data, n_seg=3) == 4
+    # the grouped evaluation's workspace: too small, or missing with a size
+    need = L.pvb_gated_delta_fwd_workspace_bytes(8, 2, 1)
+    assert call(ws=FAKE, ws_bytes=need - 1) == 5
+    assert call(ws=None, ws_bytes=need) == 5
+
+
+def test_gated_delta_forward_workspace_size():
+    """T of every 64-token chunk slot (16 KB per head) and, per 1024-token group
+    slot and head, the group map A_g, the state Z_g and the starting state
+    (64 KB each); slots: T/64 + B + 1 and T/1024 + B + 1."""
+    W = pvb.gated_delta_fwd_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    for T, H, B in ((8, 2, 1), (32768, 32, 32), (4096, 3, 600)):
+        slots, gslots = T // 64 + B + 1, T // 1024 + B + 1
+        assert W(T, H, B) == up(slots * H * 64 * 64 * 4) + 3 * up(gslots * H * 128 * 128 * 4)
+    assert W(-1, 2, 1) == 0 and W(8, 0, 1) == 0
 
 
 def test_gated_delta_grouped_heads_host_side_errors():
     L = pvb.lib()
     args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=6, H_k=4, d=128,
-                scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, status=FAKE)
+                scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, ws=None, ws_bytes=0, status=FAKE)
     assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 1          # 6 value heads over 4
     args.update(H_k=0)
     assert L.pvb_gated_delta_fwd_gqa(*args.values(), None) == 1
@@ -316,7 +332,7 @@ def test_counts_above_the_documented_maximum_are_refused_on_host():
     assert L.pvb_boundaries_from_positions(FAKE, big, 0, FAKE, 8, FAKE, None, FAKE, None) == 3
     assert L.pvb_packed_nll(FAKE, 0, 4, big, FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, None) == 3
     assert L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, big, 8, 1, 1, 128, 0.1, None,
-                                     FAKE, 1, None, FAKE, None) == 3
+                                     FAKE, 1, None, None, 0, FAKE, None) == 3
 
 
 def test_grids_of_2_to_the_32_work_items_are_refused_on_host():
@@ -335,7 +351,7 @@ def test_grids_of_2_to_the_32_work_items_are_refused_on_host():
     assert _fwd(T=128, n_seg=2 ** 16, H=256, d=64, ws_bytes=16) == 5
     assert L.pvb_packed_nll(FAKE, 0, 2 ** 24, 8, FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, None) == 6
     assert L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2 ** 16, 8, 256, 256, 128, 0.1,
-                                     None, FAKE, 1, None, FAKE, None) == 6
+                                     None, FAKE, 1, None, None, 0, FAKE, None) == 6
 
 
 def test_noalloc_backward_refuses_sizes_beyond_its_scratch_on_host():

@@ -211,3 +211,27 @@ def test_random_draws(case):
     w = W.random_gated_delta(5100 + case, lengths, H=H, Hk=Hk, g_range=g_range, beta_range=beta_range,
                              initial_state=init)
     _run(w, o_dtype, scale=scale)
+
+
+@pytest.mark.parametrize("Hk", [4, 2])
+def test_grouped_evaluation_equals_one_chain(Hk):
+    """Slices longer than one group of 1024 tokens (2.9 groups, exactly one and
+    two groups, one token more than a group, and short ones): the grouped
+    evaluation (the default, with a workspace) matches O11 on two heads, and
+    one chain per (slice, head) (no workspace) agrees with it within rounding."""
+    import torch
+
+    import packed_varlen_block_amd as pvb
+    lengths = [3000, 1024, 0, 2048, 1025, 100, 64]
+    H = 4
+    say(f"gated delta grouped vs chain: lengths {lengths}, H {H}, H_k {Hk}")
+    w = W.random_gated_delta(5300 + Hk, lengths, H=H, Hk=Hk, initial_state=True)
+    og, hg_ = _run(w, "f32", heads=[0, 3])
+    oc, hc_, sc = pvb.gated_delta_fwd(_dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]), _dev(w["beta"]),
+                                      _dev(host_cu(lengths)), initial_state=_dev(w["h0"]), o_dtype=torch.float32,
+                                      chain=True)
+    pvb.check_status(sc)
+    d_o = float((og - oc).abs().max())
+    d_s = float((hg_ - hc_).abs().max())
+    say(f"  grouped vs chain: O {d_o:.3e}, final states {d_s:.3e}")
+    assert d_o <= 1e-3 * max(1.0, float(oc.abs().max())) and d_s <= 1e-3 * max(1.0, float(hc_.abs().max()))
