@@ -1017,9 +1017,10 @@ constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
 // Pass 0: T = (I + A)^-1 of every chunk (A = diag(beta) strict_lower(Gam o K K^T),
 // which depends on no state), so that both chains apply the solve as a
 // product.  One wave per (checkpoint slot, value head): the three lower
-// blocks of K K^T on the matrix cores, then lane j takes column j of T by
-// forward substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj, in fp32.
-// Rows and columns past the chunk's end give the identity.
+// blocks of K K^T on the matrix cores; the diagonal blocks of T by forward
+// substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj in fp32, lane j taking
+// column j of T11 and lane 32 + j column j of T22; then T21 = -T22 A21 T11 on
+// the matrix cores.  Rows and columns past the chunk's end give the identity.
 struct GdTmatSmem {
   union {
     alignas(16) bf16 k[kGdC][kKP];   // K, then A over it
@@ -1083,23 +1084,79 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
   }
   for (int e = lane; e < 32 * 32; e += 64) sm.a[e >> 5][32 + (e & 31)] = 0.f;
   __syncthreads();
-  float tc[kGdC];
+  // the two diagonal 32x32 blocks by substitution, side by side: lanes 0-31
+  // take the columns of T11, lanes 32-63 those of T22
+  {
+    const int bb = lane >> 5, jl = lane & 31;
+    float tc[32];
 #pragma unroll
-  for (int i = 0; i < kGdC; ++i) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;     // four partial sums shorten the dependent chain
+    for (int i = 0; i < 32; ++i) {
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;   // four partial sums shorten the dependent chain
 #pragma unroll
-    for (int l4 = 0; l4 < i; l4 += 4) {
-      const float4 a4 = *(const float4*)&sm.a[i][l4];
-      a0 += a4.x * tc[l4];
-      if (l4 + 1 < i) a1 += a4.y * tc[l4 + 1];
-      if (l4 + 2 < i) a2 += a4.z * tc[l4 + 2];
-      if (l4 + 3 < i) a3 += a4.w * tc[l4 + 3];
+      for (int l4 = 0; l4 < i; l4 += 4) {
+        const float4 a4 = *(const float4*)&sm.a[32 * bb + i][32 * bb + l4];
+        a0 += a4.x * tc[l4];
+        if (l4 + 1 < i) a1 += a4.y * tc[l4 + 1];
+        if (l4 + 2 < i) a2 += a4.z * tc[l4 + 2];
+        if (l4 + 3 < i) a3 += a4.w * tc[l4 + 3];
+      }
+      tc[i] = (i == jl ? 1.f : 0.f) - ((a0 + a1) + (a2 + a3));
     }
-    tc[i] = (i == lane ? 1.f : 0.f) - ((a0 + a1) + (a2 + a3));
+    // T11 and T22 over A11 and A22 (every lane of the one wave has read them);
+    // A21 stays until T21 is formed
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      sm.a[32 * bb + i][32 * bb + jl] = tc[i];
+      sm.a[i][32 + jl] = 0.f;                           // T12 (written twice, zero)
+    }
   }
+  __syncthreads();
+  // T21 = -T22 (A21 T11): X = A21 T11, A element e of lane (c, hg) at k-step
+  // s is A21[c][kpos(s, e, hg)], B element T11[kpos(s, e, hg)][c]; then
+  // -T22 X with X as the B operand straight from its C layout
+  {
+    f32x16 x = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float* ar = &sm.a[32 + c][kpos(s, 0, hg)];
+      const float4 p0 = *(const float4*)ar, p1 = *(const float4*)(ar + 8);
+      const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      float xb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[e] = sm.a[kpos(s, e, hg)][c];
+      bf16x8 ah, al, bh, bl;
+      split8(xa, ah, al);
+      split8(xb, bh, bl);
+      x = mfma32(ah, bh, x);
+      x = mfma32(ah, bl, x);
+      x = mfma32(al, bh, x);
+    }
+    f32x16 y = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float* tr = &sm.a[32 + c][32 + kpos(s, 0, hg)];
+      const float4 p0 = *(const float4*)tr, p1 = *(const float4*)(tr + 8);
+      const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      float xb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[e] = x[8 * s + e];
+      bf16x8 ah, al, bh, bl;
+      split8(xa, ah, al);
+      split8(xb, bh, bl);
+      y = mfma32(ah, bh, y);
+      y = mfma32(ah, bl, y);
+      y = mfma32(al, bh, y);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.a[32 + crow(i, hg)][c] = -y[i];   // T21 over A21, read for X above
+  }
+  __syncthreads();
   float* dst = ck_t + ((size_t)slot * H + h) * (kGdC * kGdC);
 #pragma unroll
-  for (int i = 0; i < kGdC; ++i) dst[i * kGdC + lane] = tc[i];
+  for (int it = 0; it < 16; ++it) {
+    const int pc = lane + 64 * it, row = pc >> 4, c4 = pc & 15;
+    *(float4*)(dst + row * kGdC + 4 * c4) = *(const float4*)&sm.a[row][4 * c4];
+  }
 }
 
 // ===========================================================================
@@ -1123,14 +1180,15 @@ struct GdComposeSmem {
   alignas(16) bf16 v[kGdC][kKP];
   alignas(16) float tm[kGdC][kFP];                    // T, row-major
   alignas(16) bf16x8 kth[4][4][64], ktl[4][4][64];    // Kt^T as split A fragments [d_k block][k-step][lane]
-  alignas(16) float m[kGdD][kGdD + 4];                // M, row-major
+  alignas(16) float w[kGdC][kGdD + 4];                // W = T diag(beta G) K, row-major
   alignas(16) float eg[kGdC], dec[kGdC], beta[kGdC];
 };
 
 // Pass 1: one workgroup of 4 waves per (group slot, value head); groups that
 // are the last of their slice (or hold no chunk) return at once.  Wave w owns
-// columns [32w, 32w + 32) of A_g and Z_g (C layout, rows = key dims), and
-// forms M's columns [32w, 32w + 32) and B's before M is shared through LDS.
+// columns [32w, 32w + 32) of A_g and Z_g (C layout, rows = key dims).  M is
+// never formed: it is G_L I minus the rank-64 product Kt^T W, so
+// M X = G_L X - Kt^T (W X) takes two thin products; W goes through LDS.
 __global__ void __launch_bounds__(kGdThreads, 1)
 gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H,
@@ -1242,44 +1300,16 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
         Uc[rb] = mfma32(tl, vh, Uc[rb]);
       }
     }
-    __syncthreads();                                   // the Kt^T fragments are complete
-    // M = G_L I - Kt^T W and B = Kt^T Ut, columns n0 (W and Ut as the B
-    // operand straight from their C layout)
-    f32x16 Mc[4] = {}, Bc[4] = {};
+    // W into LDS (the A operand of W Z and W A, rows = positions)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float xw[8], xu[8];
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xw[e] = Wc[s >> 1][8 * (s & 1) + e];
-        xu[e] = Uc[s >> 1][8 * (s & 1) + e];
-      }
-      bf16x8 wh, wl, uh, ul;
-      split8(xw, wh, wl);
-      split8(xu, uh, ul);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bf16x8 ah = sm.kth[r][s][lane], al = sm.ktl[r][s][lane];
-        Mc[r] = mfma32(ah, wh, Mc[r]);
-        Mc[r] = mfma32(ah, wl, Mc[r]);
-        Mc[r] = mfma32(al, wh, Mc[r]);
-        Bc[r] = mfma32(ah, uh, Bc[r]);
-        Bc[r] = mfma32(ah, ul, Bc[r]);
-        Bc[r] = mfma32(al, uh, Bc[r]);
-      }
-    }
-    const float gL = sm.eg[kGdC - 1];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * r + crow(i, hg);
-        sm.m[row][n0] = (row == n0 ? gL : 0.f) - Mc[r][i];
-      }
-    __syncthreads();                                   // M is complete
-    // Z <- M Z + B and A <- M A, columns n0: A element e of lane (c, hg) at
-    // k-step s is M[32 r + c][kpos(s, e, hg)]
-    f32x16 An[4] = {};
+      for (int i = 0; i < 16; ++i) sm.w[32 * rb + crow(i, hg)][n0] = Wc[rb][i];
+    __syncthreads();                                   // W and the Kt^T fragments are complete
+    // M X = G_L X - Kt^T (W X): Y = W Z and W A for this wave's columns (A
+    // element e of lane (c, hg) at k-step s is W[32 rb + c][kpos(s, e, hg)];
+    // Z and A as the B operand straight from their C layout)
+    f32x16 Yz[2] = {}, Ya[2] = {};
 #pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
       float xz[8], xa[8];
@@ -1292,24 +1322,50 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
       split8(xz, zh, zl);
       split8(xa, ah2, al2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float* mr = &sm.m[32 * r + c][kpos(s, 0, hg)];
-        const float4 m0 = *(const float4*)mr, m1 = *(const float4*)(mr + 8);
-        const float xm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        bf16x8 mh, ml;
-        split8(xm, mh, ml);
-        Bc[r] = mfma32(mh, zh, Bc[r]);
-        Bc[r] = mfma32(mh, zl, Bc[r]);
-        Bc[r] = mfma32(ml, zh, Bc[r]);
-        An[r] = mfma32(mh, ah2, An[r]);
-        An[r] = mfma32(mh, al2, An[r]);
-        An[r] = mfma32(ml, ah2, An[r]);
+      for (int rb = 0; rb < 2; ++rb) {
+        const float* wr = &sm.w[32 * rb + c][kpos(s, 0, hg)];
+        const float4 m0 = *(const float4*)wr, m1 = *(const float4*)(wr + 8);
+        const float xw[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        bf16x8 wh, wl;
+        split8(xw, wh, wl);
+        Yz[rb] = mfma32(wh, zh, Yz[rb]);
+        Yz[rb] = mfma32(wh, zl, Yz[rb]);
+        Yz[rb] = mfma32(wl, zh, Yz[rb]);
+        Ya[rb] = mfma32(wh, ah2, Ya[rb]);
+        Ya[rb] = mfma32(wh, al2, Ya[rb]);
+        Ya[rb] = mfma32(wl, ah2, Ya[rb]);
       }
     }
+    // Z <- G_L Z + Kt^T (Ut - W Z) and A <- G_L A - Kt^T (W A)
+    const float gL = sm.eg[kGdC - 1];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      Zc[r] = Bc[r];
-      Ac[r] = An[r];
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        Zc[r][i] *= gL;
+        Ac[r][i] *= gL;
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float xr[8], xy[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xr[e] = Uc[s >> 1][8 * (s & 1) + e] - Yz[s >> 1][8 * (s & 1) + e];
+        xy[e] = -Ya[s >> 1][8 * (s & 1) + e];
+      }
+      bf16x8 rh, rl, yh, yl;
+      split8(xr, rh, rl);
+      split8(xy, yh, yl);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16x8 ah = sm.kth[r][s][lane], al = sm.ktl[r][s][lane];
+        Zc[r] = mfma32(ah, rh, Zc[r]);
+        Zc[r] = mfma32(ah, rl, Zc[r]);
+        Zc[r] = mfma32(al, rh, Zc[r]);
+        Ac[r] = mfma32(ah, yh, Ac[r]);
+        Ac[r] = mfma32(ah, yl, Ac[r]);
+        Ac[r] = mfma32(al, yh, Ac[r]);
+      }
     }
   }
   float* pa = gA + (gslot * H + h) * kGdD * kGdD;
