@@ -1380,63 +1380,94 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
     }
 }
 
-// Pass 2: one workgroup per (slice, value head) with more than one group;
-// S_(g+1) = A_g S_g + Z_g from the initial state (zero when absent), stored
-// as group g+1's starting state.  Wave w owns value columns [32w, 32w + 32).
+// Pass 2: four workgroups per (slice, value head) with more than one group,
+// one per block of 32 value columns (the columns of S_(g+1) = A_g S_g + Z_g
+// depend on the same columns of S_g only).  Block cb n_seg H + slice H + h
+// takes column block cb, so the four blocks of a (slice, head) share an XCD,
+// and its L2 copy of A_g, whenever n_seg H is a multiple of 8.  From the
+// initial state (zero when
+// absent), each S_(g+1) is stored as group g+1's starting state.  Wave w owns
+// rows [32w, 32w + 32) of the column block: its rows of A_g (row-major, the A
+// operand) and Z_g are loaded one group ahead, and the whole block of S_g, the
+// B operand, passes through LDS, double-buffered so that one barrier a group
+// suffices.  C-layout element i of wave w's row block is B element i % 8 of
+// k-step 2w + i / 8, so each wave's accumulator goes to LDS as it stands.
+constexpr int kGdScanPitch = 20;     // floats per lane in the exchange: b128 accesses free of bank conflicts
 __global__ void __launch_bounds__(kGdThreads, 1)
 gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, const float* __restrict__ h0,
                    const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS) {
+  __shared__ alignas(16) float xs[2][4][64][kGdScanPitch];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
-  if (gd_cu_bad(cu, n_seg, T, &s_bad) || (int)blockIdx.x >= n_seg * H) return;
-  const int b = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int nbh = n_seg * H;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad) || nbh == 0) return;
+  const int cb = (int)blockIdx.x / nbh, bh = (int)blockIdx.x - cb * nbh;
+  if (cb >= 4) return;
+  const int b = bh / H, h = bh - b * H;
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
   const int n_grp = (L + kGdGrpTok - 1) / kGdGrpTok;
   if (n_grp < 2) return;
-  const int n0 = 32 * w + c;
+  const int n0 = 32 * cb + c;
   const size_t st_base = (size_t)(b * H + h) * kGdD * kGdD;
-  f32x16 S[4];
+  {
+    f32x16 S0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+    for (int i = 0; i < 16; ++i) S0[i] = h0 ? h0[st_base + (size_t)(32 * w + crow(i, hg)) * kGdD + n0] : 0.f;
+    float* x = &xs[0][w][lane][0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[r][i] = h0 ? h0[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
+    for (int q = 0; q < 4; ++q) *(float4*)(x + 4 * q) = make_float4(S0[4 * q], S0[4 * q + 1], S0[4 * q + 2], S0[4 * q + 3]);
+  }
+  // group gi's rows: A element e of lane (c, hg) at k-step s is
+  // A_g[32w + c][kpos(s, e, hg)], two float4 a k-step
+#define GD_SCAN_LOAD(gi_, ra_, rz_)                                                                       \
+  {                                                                                                    \
+    const size_t sl_ = gd_grp_slot(seg0, b, (gi_));                                                     \
+    const float* pa_ = gA + (sl_ * H + h) * kGdD * kGdD + (size_t)(32 * w + c) * kGdD + 4 * hg;         \
+    const float* pz_ = gZ + (sl_ * H + h) * kGdD * kGdD + (size_t)(32 * w) * kGdD + n0;                 \
+    _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) {                                                  \
+      ra_[2 * s_] = *(const float4*)(pa_ + 16 * s_);                                                    \
+      ra_[2 * s_ + 1] = *(const float4*)(pa_ + 16 * s_ + 8);                                            \
+    }                                                                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) rz_[i_] = pz_[(size_t)crow(i_, hg) * kGdD];        \
+  }
+  float4 ca[16], na[16];
+  float cz[16], nz[16];
+  GD_SCAN_LOAD(0, ca, cz);
+  __syncthreads();
   for (int gi = 0; gi + 1 < n_grp; ++gi) {
-    const size_t slot = gd_grp_slot(seg0, b, gi);
-    const float* pa = gA + (slot * H + h) * kGdD * kGdD;
-    const float* pz = gZ + (slot * H + h) * kGdD * kGdD;
-    f32x16 Sn[4];
+    if (gi + 2 < n_grp) GD_SCAN_LOAD(gi + 1, na, nz);
+    f32x16 Sn;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Sn[r][i] = pz[(size_t)(32 * r + crow(i, hg)) * kGdD + n0];
+    for (int i = 0; i < 16; ++i) Sn[i] = cz[i];
 #pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
-      float xs[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xs[e] = S[s >> 1][8 * (s & 1) + e];
-      bf16x8 sh, sl;
-      split8(xs, sh, sl);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float* ar = pa + (size_t)(32 * r + c) * kGdD + kpos(s, 0, hg);
-        const float4 a0 = *(const float4*)ar, a1 = *(const float4*)(ar + 8);
-        const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        bf16x8 ah, al;
-        split8(xa, ah, al);
-        Sn[r] = mfma32(ah, sh, Sn[r]);
-        Sn[r] = mfma32(ah, sl, Sn[r]);
-        Sn[r] = mfma32(al, sh, Sn[r]);
-      }
+      const float* x = &xs[gi & 1][s >> 1][lane][8 * (s & 1)];
+      const float4 b0 = *(const float4*)x, b1 = *(const float4*)(x + 4);
+      const float xb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const float xa[8] = {ca[2 * s].x, ca[2 * s].y, ca[2 * s].z, ca[2 * s].w,
+                           ca[2 * s + 1].x, ca[2 * s + 1].y, ca[2 * s + 1].z, ca[2 * s + 1].w};
+      bf16x8 ah, al, sh, sl;
+      split8(xa, ah, al);
+      split8(xb, sh, sl);
+      Sn = mfma32(ah, sh, Sn);
+      Sn = mfma32(ah, sl, Sn);
+      Sn = mfma32(al, sh, Sn);
     }
-    float* ps = gS + ((slot + 1) * H + h) * kGdD * kGdD;
+    float* ps = gS + ((gd_grp_slot(seg0, b, gi) + 1) * H + h) * kGdD * kGdD + (size_t)(32 * w) * kGdD + n0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      S[r] = Sn[r];
+    for (int i = 0; i < 16; ++i) ps[(size_t)crow(i, hg) * kGdD] = Sn[i];
+    float* x = &xs[(gi + 1) & 1][w][lane][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ps[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] = S[r][i];
+    for (int q = 0; q < 4; ++q) *(float4*)(x + 4 * q) = make_float4(Sn[4 * q], Sn[4 * q + 1], Sn[4 * q + 2], Sn[4 * q + 3]);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ca[i] = na[i];
+      cz[i] = nz[i];
     }
   }
+#undef GD_SCAN_LOAD
 }
 
 // Pass 3: the forward kernel on every group from its starting state.
@@ -1949,7 +1980,7 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
   if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != kGdD) return PVB_E_UNSUPPORTED;
   const GdFwdLayout lay = gd_fwd_layout(T, H, n_seg);
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)n_seg * H, kGdThreads) ||
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits(4 * (uint64_t)n_seg * H, kGdThreads) ||
       !grid_fits((uint64_t)lay.slots * H, kGdThreads))
     return PVB_E_UNSUPPORTED;
   const bool grouped = workspace != nullptr || workspace_bytes != 0;
@@ -1988,7 +2019,7 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
   if (multi) {
     gd_grp_compose_kernel<<<(unsigned)(lay.gslots * H), kGdThreads, 0, s>>>(
         (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ);
-    gd_grp_scan_kernel<<<(unsigned)std::max<int64_t>(1, (int64_t)n_seg * H), kGdThreads, 0, s>>>(
+    gd_grp_scan_kernel<<<(unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H), kGdThreads, 0, s>>>(
         d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
   }
   if (o_dtype == PVB_F32)
