@@ -1175,30 +1175,42 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
 // chunk steps to 16 + n/16 + 16 steps.  Every product splits its fp32
 // operands into bf16 hi + lo parts (three products), as the chunk kernels do.
 
+#ifndef GD_CMP_OCC
+#define GD_CMP_OCC 2
+#endif
 struct GdComposeSmem {
   alignas(16) bf16 k[kGdC][kKP];
   alignas(16) bf16 v[kGdC][kKP];
   alignas(16) float tm[kGdC][kFP];                    // T, row-major
-  alignas(16) bf16x8 kth[4][4][64], ktl[4][4][64];    // Kt^T as split A fragments [d_k block][k-step][lane]
-  alignas(16) float w[kGdC][kGdD + 4];                // W = T diag(beta G) K, row-major
+  alignas(16) bf16x8 kt[4][4][64];                    // K^T as A fragments [d_k block][k-step][lane]
   alignas(16) float eg[kGdC], dec[kGdC], beta[kGdC];
 };
 
-// Pass 1: one workgroup of 4 waves per (group slot, value head); groups that
-// are the last of their slice (or hold no chunk) return at once.  Wave w owns
-// columns [32w, 32w + 32) of A_g and Z_g (C layout, rows = key dims).  M is
-// never formed: it is G_L I minus the rank-64 product Kt^T W, so
-// M X = G_L X - Kt^T (W X) takes two thin products; W goes through LDS.
-__global__ void __launch_bounds__(kGdThreads, 1)
+// Pass 1: two workgroups of 4 waves per (group slot, value head), one for
+// Z_g and one for A_g; groups that are the last of their slice (or hold no
+// chunk) return at once.  Block x n_gs + gslot H + h takes map x (0: Z, 1:
+// A), n_gs = gslots H, so the pair shares an XCD whenever n_gs is a multiple
+// of 8.  Wave w owns columns [32w, 32w + 32) of its map (C layout, rows = key
+// dims).  M is never formed: M X = G_L X - Kt^T T diag(beta G) K X, so every
+// chunk takes the map through the forward recurrence's own chunk step (K X,
+// the right-hand side, U = T rhs, the rank-64 update), Z with V and from
+// zero, A without V and from the identity.  The update is written
+// K^T (diag(G_L / G) U): K^T is exact in bf16, so only the scaled U is split
+// (two products, not three).  With one map per workgroup the registers and
+// LDS allow two workgroups per CU.
+__global__ void __launch_bounds__(kGdThreads, GD_CMP_OCC)
 gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H,
-                      int Hk, const float* __restrict__ ck_t, float* __restrict__ gA, float* __restrict__ gZ) {
+                      int Hk, const float* __restrict__ ck_t, float* __restrict__ gA, float* __restrict__ gZ,
+                      int n_gs) {
   __shared__ GdComposeSmem sm;
   __shared__ int s_bad, s_b;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
-  const size_t gslot = blockIdx.x / H;
-  const int h = blockIdx.x - (blockIdx.x / H) * H;
+  const bool is_a = (int)blockIdx.x >= n_gs;
+  const int bx = is_a ? (int)blockIdx.x - n_gs : (int)blockIdx.x;
+  const size_t gslot = bx / H;
+  const int h = bx - (bx / H) * H;
   if (tid == 0) {
     s_bad = 0;
     s_b = 0;
@@ -1218,31 +1230,63 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
   if (gi < 0 || gi >= n_grp - 1) return;               // only full groups that another group follows
   const int hk = h / (H / Hk);
   const int n0 = 32 * w + c;
+  // V enters Z only; both maps take the same path (one loop, not one per map)
+  const float vsc = is_a ? 0.f : 1.f;
 
-  f32x16 Ac[4], Zc[4];
+  f32x16 X[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      Ac[r][i] = 32 * r + crow(i, hg) == n0 ? 1.f : 0.f;
-      Zc[r][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) X[r][i] = 32 * r + 8 * (i >> 2) + (i & 3) == n0 - 4 * hg ? 1.f - vsc : 0.f;
 
+  // chunk j + 1's K, V (Z only), T and gates are loaded into registers while
+  // chunk j is computed (every chunk of a composed group is full); scalar
+  // registers, not arrays, which the compiler would move to LDS.  Thread tid
+  // takes rows tid/16 + 16 it, columns 8 (tid % 16) of K and V and the float4
+  // tid + 256 it of T, it = 0..3.
+  uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
+  float4 pt0, pt1, pt2, pt3;
+  float pg, pb;
+  const int frow = tid >> 4, fcol = (tid & 15) * 8;
+#define GD_CMP_FETCH(j_)                                                                                \
+  {                                                                                                    \
+    const int t0_ = seg0 + (gi * kGdGrpChunks + (j_)) * kGdC;                                           \
+    const float* tp_ = ck_t + (gd_ckpt_slot(seg0, b, gi * kGdGrpChunks + (j_)) * H + h) * (kGdC * kGdC) \
+                       + 4 * tid;                                                                       \
+    const bf16* kp_ = k + ((size_t)(t0_ + frow) * Hk + hk) * kGdD + fcol;                               \
+    pk0 = *(const uint4*)kp_;                                                                           \
+    pk1 = *(const uint4*)(kp_ + (size_t)16 * Hk * kGdD);                                                \
+    pk2 = *(const uint4*)(kp_ + (size_t)32 * Hk * kGdD);                                                \
+    pk3 = *(const uint4*)(kp_ + (size_t)48 * Hk * kGdD);                                                \
+    const bf16* vp_ = v + ((size_t)(t0_ + frow) * H + h) * kGdD + fcol;                                 \
+    pv0 = *(const uint4*)vp_;                                                                           \
+    pv1 = *(const uint4*)(vp_ + (size_t)16 * H * kGdD);                                                 \
+    pv2 = *(const uint4*)(vp_ + (size_t)32 * H * kGdD);                                                 \
+    pv3 = *(const uint4*)(vp_ + (size_t)48 * H * kGdD);                                                 \
+    pt0 = *(const float4*)tp_;                                                                          \
+    pt1 = *(const float4*)(tp_ + 4 * kGdThreads);                                                       \
+    pt2 = *(const float4*)(tp_ + 8 * kGdThreads);                                                       \
+    pt3 = *(const float4*)(tp_ + 12 * kGdThreads);                                                      \
+    pg = g[(size_t)(t0_ + lane) * H + h];                                                               \
+    pb = beta[(size_t)(t0_ + lane) * H + h];                                                            \
+  }
+  GD_CMP_FETCH(0);
   for (int j = 0; j < kGdGrpChunks; ++j) {
-    const int ci = gi * kGdGrpChunks + j;
-    const int t0 = seg0 + ci * kGdC;                   // a full chunk: the group is not the slice's last
-    const float* tp = ck_t + (gd_ckpt_slot(seg0, b, ci) * H + h) * (kGdC * kGdC);
     __syncthreads();                                   // the previous chunk's reads of LDS are done
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int ch = tid + kGdThreads * it;
-      const int row = ch >> 4, col = (ch & 15) * 8;
-      *(uint4*)&sm.k[row][col] = *(const uint4*)(k + ((size_t)(t0 + row) * Hk + hk) * kGdD + col);
-      *(uint4*)&sm.v[row][col] = *(const uint4*)(v + ((size_t)(t0 + row) * H + h) * kGdD + col);
-      *(float4*)&sm.tm[ch >> 4][4 * (ch & 15)] = *(const float4*)(tp + 4 * ch);
-    }
+    *(uint4*)&sm.k[frow][fcol] = pk0;
+    *(uint4*)&sm.k[frow + 16][fcol] = pk1;
+    *(uint4*)&sm.k[frow + 32][fcol] = pk2;
+    *(uint4*)&sm.k[frow + 48][fcol] = pk3;
+    *(uint4*)&sm.v[frow][fcol] = pv0;
+    *(uint4*)&sm.v[frow + 16][fcol] = pv1;
+    *(uint4*)&sm.v[frow + 32][fcol] = pv2;
+    *(uint4*)&sm.v[frow + 48][fcol] = pv3;
+    *(float4*)&sm.tm[frow][4 * (tid & 15)] = pt0;
+    *(float4*)&sm.tm[frow + 16][4 * (tid & 15)] = pt1;
+    *(float4*)&sm.tm[frow + 32][4 * (tid & 15)] = pt2;
+    *(float4*)&sm.tm[frow + 48][4 * (tid & 15)] = pt3;
     if (w == 0) {
-      float x = g[(size_t)(t0 + lane) * H + h];
+      float x = pg;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -1252,132 +1296,109 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
       const float last = __shfl(x, 63, 64);
       sm.eg[lane] = fast_exp2(x);
       sm.dec[lane] = fast_exp2(last - x);
-      sm.beta[lane] = beta[(size_t)(t0 + lane) * H + h];
+      sm.beta[lane] = pb;
     }
+    if (j + 1 < kGdGrpChunks) GD_CMP_FETCH(j + 1);
     __syncthreads();
-    // Kt^T as split A fragments, once for the four waves
+    // K^T as A fragments, once for the four waves (read after the next
+    // barrier): element e of fragment (r, s, lane (fc, fh)) is
+    // K[kpos(s, e, fh)][32 r + fc]
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int f = tid + kGdThreads * it;
       const int r = f >> 8, s = (f >> 6) & 3, fl = f & 63, fc = fl & 31, fh = fl >> 5;
-      float x[8];
+      bf16x8 x;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = kpos(s, e, fh);
-        x[e] = (float)sm.k[pos][32 * r + fc] * sm.dec[pos];
-      }
-      split8(x, sm.kth[r][s][fl], sm.ktl[r][s][fl]);
+      for (int e = 0; e < 8; ++e) x[e] = sm.k[kpos(s, e, fh)][32 * r + fc];
+      sm.kt[r][s][fl] = x;
     }
-    // W = T diag(beta G) K and Ut = T diag(beta) V, columns n0: A element e of
-    // lane (c, hg) at k-step s is T[32 rb + c][kpos(s, e, hg)]
-    f32x16 Wc[2] = {}, Uc[2] = {};
+    // K X: A element e of lane (c, hg) at k-step s is K[32 rb + c][kpos(s, e,
+    // hg)] (exact in bf16, so X alone is split); X is the B operand straight
+    // from its C layout
+    f32x16 kx[2] = {};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float xk[8], xv[8];
+    for (int s = 0; s < kGdD / 16; ++s) {
+      float xb[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = kpos(s, e, hg);
-        const float bt = sm.beta[pos];
-        xk[e] = bt * sm.eg[pos] * (float)sm.k[pos][n0];
-        xv[e] = bt * (float)sm.v[pos][n0];
-      }
-      bf16x8 kh, kl, vh, vl;
-      split8(xk, kh, kl);
-      split8(xv, vh, vl);
+      for (int e = 0; e < 8; ++e) xb[e] = X[s >> 1][8 * (s & 1) + e];
+      bf16x8 bh, bl;
+      split8(xb, bh, bl);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        if (rb == 0 && s >= 2) continue;               // row block 0 of T has no column past 31
+        const bf16* kr = &sm.k[32 * rb + c][16 * s + 4 * hg];
+        const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
+        kx[rb] = mfma32(ka, bh, kx[rb]);
+        kx[rb] = mfma32(ka, bl, kx[rb]);
+      }
+    }
+    // right-hand side beta ([V] - G K X), in place
+    {
+      // rows 32 rb + crow(i, hg): one lane-dependent base and constant offsets
+      const float* bp = &sm.beta[4 * hg];
+      const float* ep = &sm.eg[4 * hg];
+      const bf16* vp = &sm.v[4 * hg][n0];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ro = 32 * rb + 8 * (i >> 2) + (i & 3);
+          kx[rb][i] = bp[ro] * (vsc * (float)vp[ro * kKP] - ep[ro] * kx[rb][i]);
+        }
+    }
+    // U = T rhs: A element e of lane (c, hg) at k-step s is T[32 rb + c][kpos(s,
+    // e, hg)]; row block 0 of T has no column past 31
+    f32x16 uu[2] = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float xb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[e] = kx[s >> 1][8 * (s & 1) + e];
+      bf16x8 bh, bl;
+      split8(xb, bh, bl);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        if (rb == 0 && s >= 2) continue;
         const float* tr = &sm.tm[32 * rb + c][kpos(s, 0, hg)];
         const float4 a0 = *(const float4*)tr, a1 = *(const float4*)(tr + 8);
         const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         bf16x8 th, tl;
         split8(xa, th, tl);
-        Wc[rb] = mfma32(th, kh, Wc[rb]);
-        Wc[rb] = mfma32(th, kl, Wc[rb]);
-        Wc[rb] = mfma32(tl, kh, Wc[rb]);
-        Uc[rb] = mfma32(th, vh, Uc[rb]);
-        Uc[rb] = mfma32(th, vl, Uc[rb]);
-        Uc[rb] = mfma32(tl, vh, Uc[rb]);
+        uu[rb] = mfma32(th, bh, uu[rb]);
+        uu[rb] = mfma32(th, bl, uu[rb]);
+        uu[rb] = mfma32(tl, bh, uu[rb]);
       }
     }
-    // W into LDS (the A operand of W Z and W A, rows = positions)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.w[32 * rb + crow(i, hg)][n0] = Wc[rb][i];
-    __syncthreads();                                   // W and the Kt^T fragments are complete
-    // M X = G_L X - Kt^T (W X): Y = W Z and W A for this wave's columns (A
-    // element e of lane (c, hg) at k-step s is W[32 rb + c][kpos(s, e, hg)];
-    // Z and A as the B operand straight from their C layout)
-    f32x16 Yz[2] = {}, Ya[2] = {};
-#pragma unroll
-    for (int s = 0; s < kGdD / 16; ++s) {
-      float xz[8], xa[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xz[e] = Zc[s >> 1][8 * (s & 1) + e];
-        xa[e] = Ac[s >> 1][8 * (s & 1) + e];
-      }
-      bf16x8 zh, zl, ah2, al2;
-      split8(xz, zh, zl);
-      split8(xa, ah2, al2);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float* wr = &sm.w[32 * rb + c][kpos(s, 0, hg)];
-        const float4 m0 = *(const float4*)wr, m1 = *(const float4*)(wr + 8);
-        const float xw[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        bf16x8 wh, wl;
-        split8(xw, wh, wl);
-        Yz[rb] = mfma32(wh, zh, Yz[rb]);
-        Yz[rb] = mfma32(wh, zl, Yz[rb]);
-        Yz[rb] = mfma32(wl, zh, Yz[rb]);
-        Ya[rb] = mfma32(wh, ah2, Ya[rb]);
-        Ya[rb] = mfma32(wh, al2, Ya[rb]);
-        Ya[rb] = mfma32(wl, ah2, Ya[rb]);
-      }
-    }
-    // Z <- G_L Z + Kt^T (Ut - W Z) and A <- G_L A - Kt^T (W A)
+    __syncthreads();                                   // the K^T fragments are complete
+    // X <- G_L X + K^T (diag(G_L / G) U)
     const float gL = sm.eg[kGdC - 1];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        Zc[r][i] *= gL;
-        Ac[r][i] *= gL;
-      }
+      for (int i = 0; i < 16; ++i) X[r][i] *= gL;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float xr[8], xy[8];
+      const float4 d0 = *(const float4*)&sm.dec[32 * (s >> 1) + 16 * (s & 1) + 4 * hg];
+      const float4 d1 = *(const float4*)&sm.dec[32 * (s >> 1) + 16 * (s & 1) + 8 + 4 * hg];
+      const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      float xr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xr[e] = Uc[s >> 1][8 * (s & 1) + e] - Yz[s >> 1][8 * (s & 1) + e];
-        xy[e] = -Ya[s >> 1][8 * (s & 1) + e];
-      }
-      bf16x8 rh, rl, yh, yl;
+      for (int e = 0; e < 8; ++e) xr[e] = dd[e] * uu[s >> 1][8 * (s & 1) + e];
+      bf16x8 rh, rl;
       split8(xr, rh, rl);
-      split8(xy, yh, yl);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bf16x8 ah = sm.kth[r][s][lane], al = sm.ktl[r][s][lane];
-        Zc[r] = mfma32(ah, rh, Zc[r]);
-        Zc[r] = mfma32(ah, rl, Zc[r]);
-        Zc[r] = mfma32(al, rh, Zc[r]);
-        Ac[r] = mfma32(ah, yh, Ac[r]);
-        Ac[r] = mfma32(ah, yl, Ac[r]);
-        Ac[r] = mfma32(al, yh, Ac[r]);
+        const bf16x8 ka = sm.kt[r][s][lane];
+        X[r] = mfma32(ka, rh, X[r]);
+        X[r] = mfma32(ka, rl, X[r]);
       }
     }
   }
-  float* pa = gA + (gslot * H + h) * kGdD * kGdD;
-  float* pz = gZ + (gslot * H + h) * kGdD * kGdD;
+#undef GD_CMP_FETCH
+  float* px = (is_a ? gA : gZ) + (gslot * H + h) * kGdD * kGdD + (size_t)(4 * hg) * kGdD + n0;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const size_t e = (size_t)(32 * r + crow(i, hg)) * kGdD + n0;
-      pa[e] = Ac[r][i];
-      pz[e] = Zc[r][i];
-    }
+    for (int i = 0; i < 16; ++i) px[(32 * r + 8 * (i >> 2) + (i & 3)) * kGdD] = X[r][i];
 }
 
 // Pass 2: four workgroups per (slice, value head) with more than one group,
@@ -1981,7 +2002,7 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
   if (d != kGdD) return PVB_E_UNSUPPORTED;
   const GdFwdLayout lay = gd_fwd_layout(T, H, n_seg);
   if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits(4 * (uint64_t)n_seg * H, kGdThreads) ||
-      !grid_fits((uint64_t)lay.slots * H, kGdThreads))
+      !grid_fits((uint64_t)lay.slots * H, kGdThreads) || !grid_fits(2 * (uint64_t)lay.gslots * H, kGdThreads))
     return PVB_E_UNSUPPORTED;
   const bool grouped = workspace != nullptr || workspace_bytes != 0;
   if (grouped && (workspace == nullptr || workspace_bytes < lay.total)) return PVB_E_WORKSPACE;
@@ -2017,8 +2038,9 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
   gd_tmat_kernel<<<(unsigned)(lay.slots * H), 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k,
                                                           ck_t);
   if (multi) {
-    gd_grp_compose_kernel<<<(unsigned)(lay.gslots * H), kGdThreads, 0, s>>>(
-        (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ);
+    gd_grp_compose_kernel<<<(unsigned)(2 * lay.gslots * H), kGdThreads, 0, s>>>(
+        (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ,
+        (int)(lay.gslots * H));
     gd_grp_scan_kernel<<<(unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H), kGdThreads, 0, s>>>(
         d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
   }
