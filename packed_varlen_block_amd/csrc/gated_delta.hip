@@ -1016,147 +1016,235 @@ constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
 
 // Pass 0: T = (I + A)^-1 of every chunk (A = diag(beta) strict_lower(Gam o K K^T),
 // which depends on no state), so that both chains apply the solve as a
-// product.  One wave per (checkpoint slot, value head): the three lower
-// blocks of K K^T on the matrix cores; the diagonal blocks of T by forward
-// substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj in fp32, lane j taking
-// column j of T11 and lane 32 + j column j of T22; then T21 = -T22 A21 T11 on
-// the matrix cores.  Rows and columns past the chunk's end give the identity.
+// product.  Work items are (checkpoint slot, value head) pairs, slot-major;
+// each workgroup (one wave) takes a run of `per` consecutive items, `per`
+// chosen so that the grid is one round of resident workgroups, and loads the
+// next item's K and gates while it computes the current one.  Per
+// item: the three lower blocks of K K^T on the matrix cores, the K fragments
+// loaded straight into the operand layout (lane (c, hg) holds rows c and
+// 32 + c, dims 16 s + 8 hg .. + 7 at k-step s); the diagonal blocks of T by
+// forward substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj in fp32, lane j
+// taking column j of T11 and lane 32 + j column j of T22; then T21 = -T22 A21
+// T11 on the matrix cores.  Rows and columns past the chunk's end give the
+// identity.
+constexpr int kGdTmatPerCu = 8;       // resident workgroups per CU (LDS: 8 x 17.9 KB)
 struct GdTmatSmem {
-  union {
-    alignas(16) bf16 k[kGdC][kKP];   // K, then A over it
-    alignas(16) float a[kGdC][kFP];
-  };
-  float gl[kGdC], beta[kGdC];
+  alignas(16) float a[kGdC][kFP];    // A, then T over it
+  alignas(16) float gl[kGdC];
+  alignas(16) float beta[kGdC];
 };
 
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64, 2)
 gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const float* __restrict__ beta,
-               const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float* __restrict__ ck_t) {
+               const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float* __restrict__ ck_t, int per) {
   __shared__ GdTmatSmem sm;
-  __shared__ int s_bad, s_b;
+  __shared__ int s_bad;
   const int lane = threadIdx.x, hg = lane >> 5, c = lane & 31;
-  const int slot = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  if (gd_cu_bad_find(cu, n_seg, T, slot, &s_bad, &s_b) || n_seg == 0) return;
-  const int b = s_b, seg0 = cu[b], L = cu[b + 1] - seg0;
-  const int ci = slot - (seg0 / kGdC + b);
-  if (ci < 0 || ci * kGdC >= L) return;
-  const int hk = h / (H / Hk);
-  const int t0 = seg0 + ci * kGdC, n = min(kGdC, L - ci * kGdC);
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int ch = lane + 64 * it, row = ch >> 4, col = (ch & 15) * 8;
-    *(uint4*)&sm.k[row][col] = row < n ? *(const uint4*)(k + ((size_t)(t0 + row) * Hk + hk) * kGdD + col) : zero4();
-  }
+  if (gd_cu_bad(cu, n_seg, T, &s_bad) || n_seg == 0) return;
+  const int64_t n_items = ((int64_t)T / kGdC + n_seg + 1) * H;
+  const int64_t it_end = std::min<int64_t>(n_items, ((int64_t)blockIdx.x + 1) * per);
+  // the slice of the current slot: the largest b whose first slot cu[b]/64 + b
+  // is at most the slot (found once by bisection, then advanced)
+  int64_t it = (int64_t)blockIdx.x * per;
+  int b;
   {
-    float x = lane < n ? g[(size_t)(t0 + lane) * H + h] : 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
+    const int64_t slot = it / H;
+    int lo = 0, hi = n_seg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)(cu[mid] / kGdC + mid) <= slot) lo = mid;
+      else hi = mid - 1;
     }
-    sm.gl[lane] = x * kLog2e;
-    sm.beta[lane] = lane < n ? beta[(size_t)(t0 + lane) * H + h] : 0.f;
+    b = lo;
   }
-  __syncthreads();
-  f32x16 kk[3];                                       // blocks (0,0), (1,0), (1,1) of K K^T
-#pragma unroll
-  for (int blk = 0; blk < 3; ++blk) {
-    const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
-    kk[blk] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < kGdD / 16; ++s) {
-      const bf16x8 a = *(const bf16x8*)&sm.k[32 * bi + c][16 * s + 8 * hg];
-      const bf16x8 bk = *(const bf16x8*)&sm.k[32 * bj + c][16 * s + 8 * hg];
-      kk[blk] = mfma32(a, bk, kk[blk]);
-    }
+  // the next item at or after `it` whose slot holds a chunk; sets the item's
+  // chunk (t0, n) and heads, or it = it_end
+  int t0 = 0, n = 0, h = 0, hk = 0;
+  int64_t slot = 0;
+#define GD_TMAT_NEXT()                                                                                  \
+  for (; it < it_end; ++it) {                                                                           \
+    slot = it / H;                                                                                      \
+    while (b + 1 < n_seg && (int64_t)(cu[b + 1] / kGdC + b + 1) <= slot) ++b;                             \
+    const int seg0_ = cu[b], L_ = cu[b + 1] - seg0_;                                                    \
+    const int64_t ci_ = slot - (seg0_ / kGdC + b);                                                      \
+    if (ci_ >= 0 && ci_ * kGdC < L_) {                                                                  \
+      h = (int)(it - slot * H);                                                                         \
+      hk = h / (H / Hk);                                                                                \
+      t0 = seg0_ + (int)ci_ * kGdC;                                                                     \
+      n = min(kGdC, L_ - (int)ci_ * kGdC);                                                              \
+      break;                                                                                            \
+    }                                                                                                   \
+    it = (slot + 1) * H - 1;                          /* an empty slot: skip its heads */               \
   }
-  __syncthreads();                                    // K is read; A goes over it
-#pragma unroll
-  for (int blk = 0; blk < 3; ++blk) {
-    const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
-    const int pj = 32 * bj + c;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int pi = 32 * bi + crow(i, hg);
-      const float dcy = fast_exp2(fminf(sm.gl[pi] - sm.gl[pj], 0.f));
-      sm.a[pi][pj] = pj < pi ? sm.beta[pi] * kk[blk][i] * dcy : 0.f;
-    }
+  // K fragments and gates of the item, into registers (scalars, not arrays,
+  // which the compiler would move to LDS)
+  uint4 f00, f01, f02, f03, f04, f05, f06, f07, f10, f11, f12, f13, f14, f15, f16, f17;
+  float pg, pb;
+#define GD_TMAT_FETCH()                                                                                 \
+  {                                                                                                    \
+    const bf16* r0_ = k + ((size_t)(t0 + c) * Hk + hk) * kGdD + 8 * hg;                                 \
+    const bf16* r1_ = r0_ + (size_t)32 * Hk * kGdD;                                                     \
+    const bool v0_ = c < n, v1_ = 32 + c < n;                                                           \
+    f00 = v0_ ? *(const uint4*)(r0_ + 0) : zero4();                                                     \
+    f01 = v0_ ? *(const uint4*)(r0_ + 16) : zero4();                                                    \
+    f02 = v0_ ? *(const uint4*)(r0_ + 32) : zero4();                                                    \
+    f03 = v0_ ? *(const uint4*)(r0_ + 48) : zero4();                                                    \
+    f04 = v0_ ? *(const uint4*)(r0_ + 64) : zero4();                                                    \
+    f05 = v0_ ? *(const uint4*)(r0_ + 80) : zero4();                                                    \
+    f06 = v0_ ? *(const uint4*)(r0_ + 96) : zero4();                                                    \
+    f07 = v0_ ? *(const uint4*)(r0_ + 112) : zero4();                                                   \
+    f10 = v1_ ? *(const uint4*)(r1_ + 0) : zero4();                                                     \
+    f11 = v1_ ? *(const uint4*)(r1_ + 16) : zero4();                                                    \
+    f12 = v1_ ? *(const uint4*)(r1_ + 32) : zero4();                                                    \
+    f13 = v1_ ? *(const uint4*)(r1_ + 48) : zero4();                                                    \
+    f14 = v1_ ? *(const uint4*)(r1_ + 64) : zero4();                                                    \
+    f15 = v1_ ? *(const uint4*)(r1_ + 80) : zero4();                                                    \
+    f16 = v1_ ? *(const uint4*)(r1_ + 96) : zero4();                                                    \
+    f17 = v1_ ? *(const uint4*)(r1_ + 112) : zero4();                                                   \
+    pg = lane < n ? g[(size_t)(t0 + lane) * H + h] : 0.f;                                               \
+    pb = lane < n ? beta[(size_t)(t0 + lane) * H + h] : 0.f;                                            \
   }
-  for (int e = lane; e < 32 * 32; e += 64) sm.a[e >> 5][32 + (e & 31)] = 0.f;
-  __syncthreads();
-  // the two diagonal 32x32 blocks by substitution, side by side: lanes 0-31
-  // take the columns of T11, lanes 32-63 those of T22
-  {
-    const int bb = lane >> 5, jl = lane & 31;
-    float tc[32];
+  GD_TMAT_NEXT();
+  if (it >= it_end) return;
+  GD_TMAT_FETCH();
+  while (true) {
+    const int cur_n = n;
+    const int64_t cur_slot = slot;
+    const int cur_h = h;
+    {
+      float x = pg;                                   // inclusive sum (zero past the chunk's end)
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;   // four partial sums shorten the dependent chain
-#pragma unroll
-      for (int l4 = 0; l4 < i; l4 += 4) {
-        const float4 a4 = *(const float4*)&sm.a[32 * bb + i][32 * bb + l4];
-        a0 += a4.x * tc[l4];
-        if (l4 + 1 < i) a1 += a4.y * tc[l4 + 1];
-        if (l4 + 2 < i) a2 += a4.z * tc[l4 + 2];
-        if (l4 + 3 < i) a3 += a4.w * tc[l4 + 3];
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
       }
-      tc[i] = (i == jl ? 1.f : 0.f) - ((a0 + a1) + (a2 + a3));
+      sm.gl[lane] = x * kLog2e;
+      sm.beta[lane] = pb;
     }
-    // T11 and T22 over A11 and A22 (every lane of the one wave has read them);
-    // A21 stays until T21 is formed
+    // blocks (0,0), (1,0), (1,1) of K K^T: A operand row block bi, B operand
+    // row block bj, both from the fragments as loaded
+    f32x16 kk0 = {}, kk1 = {}, kk2 = {};
+    {
+      const uint4 r0[8] = {f00, f01, f02, f03, f04, f05, f06, f07};
+      const uint4 r1[8] = {f10, f11, f12, f13, f14, f15, f16, f17};
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      sm.a[32 * bb + i][32 * bb + jl] = tc[i];
-      sm.a[i][32 + jl] = 0.f;                           // T12 (written twice, zero)
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const bf16x8 x0 = __builtin_bit_cast(bf16x8, r0[s2]);
+        const bf16x8 x1 = __builtin_bit_cast(bf16x8, r1[s2]);
+        kk0 = mfma32(x0, x0, kk0);
+        kk1 = mfma32(x1, x0, kk1);
+        kk2 = mfma32(x1, x1, kk2);
+      }
     }
+    // the next item's loads go out while this one is computed
+    ++it;
+    GD_TMAT_NEXT();
+    const bool more = it < it_end;
+    if (more) GD_TMAT_FETCH();
+    __syncthreads();                                  // the gates are in LDS; the last item's T is stored
+    // A = diag(beta) strict_lower(Gam o K K^T) for the three blocks; rows
+    // 32 bi + 8 m + 4 hg + e of the C layout
+    {
+      const f32x16 kk[3] = {kk0, kk1, kk2};
+#pragma unroll
+      for (int blk = 0; blk < 3; ++blk) {
+        const int bi = blk == 0 ? 0 : 1, bj = blk == 2 ? 1 : 0;
+        const int pj = 32 * bj + c;
+        const float gj = sm.gl[pj];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int p0 = 32 * bi + 8 * m + 4 * hg;
+          const float4 gi4 = *(const float4*)&sm.gl[p0];
+          const float4 bt4 = *(const float4*)&sm.beta[p0];
+          const float gv[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+          const float bv[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int pi = p0 + e;
+            sm.a[pi][pj] = pj < pi ? bv[e] * kk[blk][4 * m + e] * fast_exp2(gv[e] - gj) : 0.f;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // the two diagonal 32x32 blocks by substitution, side by side: lanes 0-31
+    // take the columns of T11, lanes 32-63 those of T22
+    {
+      const int bb = lane >> 5, jl = lane & 31;
+      float tc[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;   // four partial sums shorten the dependent chain
+#pragma unroll
+        for (int l4 = 0; l4 < i; l4 += 4) {
+          const float4 a4 = *(const float4*)&sm.a[32 * bb + i][32 * bb + l4];
+          a0 += a4.x * tc[l4];
+          if (l4 + 1 < i) a1 += a4.y * tc[l4 + 1];
+          if (l4 + 2 < i) a2 += a4.z * tc[l4 + 2];
+          if (l4 + 3 < i) a3 += a4.w * tc[l4 + 3];
+        }
+        tc[i] = (i == jl ? 1.f : 0.f) - ((a0 + a1) + (a2 + a3));
+      }
+      // T11 and T22 over A11 and A22 (every lane of the one wave has read
+      // them); A21 stays until T21 is formed
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        sm.a[32 * bb + i][32 * bb + jl] = tc[i];
+        sm.a[i][32 + jl] = 0.f;                         // T12 (written twice, zero)
+      }
+    }
+    __syncthreads();
+    // T21 = -T22 (A21 T11): X = A21 T11, A element e of lane (c, hg) at
+    // k-step s is A21[c][kpos(s, e, hg)], B element T11[kpos(s, e, hg)][c];
+    // then -T22 X with X as the B operand straight from its C layout
+    {
+      f32x16 x = {};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const float* ar = &sm.a[32 + c][kpos(s2, 0, hg)];
+        const float4 p0 = *(const float4*)ar, p1 = *(const float4*)(ar + 8);
+        const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        float xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = sm.a[kpos(s2, e, hg)][c];
+        bf16x8 ah, al, bh, bl;
+        split8(xa, ah, al);
+        split8(xb, bh, bl);
+        x = mfma32(ah, bh, x);
+        x = mfma32(ah, bl, x);
+        x = mfma32(al, bh, x);
+      }
+      f32x16 y = {};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const float* tr = &sm.a[32 + c][32 + kpos(s2, 0, hg)];
+        const float4 p0 = *(const float4*)tr, p1 = *(const float4*)(tr + 8);
+        const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        float xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = x[8 * s2 + e];
+        bf16x8 ah, al, bh, bl;
+        split8(xa, ah, al);
+        split8(xb, bh, bl);
+        y = mfma32(ah, bh, y);
+        y = mfma32(ah, bl, y);
+        y = mfma32(al, bh, y);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.a[32 + crow(i, hg)][c] = -y[i];   // T21 over A21, read for X above
+    }
+    __syncthreads();
+    float* dst = ck_t + ((size_t)cur_slot * H + cur_h) * (kGdC * kGdC);
+#pragma unroll
+    for (int i2 = 0; i2 < 16; ++i2) {
+      const int pc = lane + 64 * i2, row = pc >> 4, c4 = pc & 15;
+      *(float4*)(dst + row * kGdC + 4 * c4) = *(const float4*)&sm.a[row][4 * c4];
+    }
+    (void)cur_n;
+    if (!more) break;
   }
-  __syncthreads();
-  // T21 = -T22 (A21 T11): X = A21 T11, A element e of lane (c, hg) at k-step
-  // s is A21[c][kpos(s, e, hg)], B element T11[kpos(s, e, hg)][c]; then
-  // -T22 X with X as the B operand straight from its C layout
-  {
-    f32x16 x = {};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float* ar = &sm.a[32 + c][kpos(s, 0, hg)];
-      const float4 p0 = *(const float4*)ar, p1 = *(const float4*)(ar + 8);
-      const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      float xb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xb[e] = sm.a[kpos(s, e, hg)][c];
-      bf16x8 ah, al, bh, bl;
-      split8(xa, ah, al);
-      split8(xb, bh, bl);
-      x = mfma32(ah, bh, x);
-      x = mfma32(ah, bl, x);
-      x = mfma32(al, bh, x);
-    }
-    f32x16 y = {};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float* tr = &sm.a[32 + c][32 + kpos(s, 0, hg)];
-      const float4 p0 = *(const float4*)tr, p1 = *(const float4*)(tr + 8);
-      const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      float xb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xb[e] = x[8 * s + e];
-      bf16x8 ah, al, bh, bl;
-      split8(xa, ah, al);
-      split8(xb, bh, bl);
-      y = mfma32(ah, bh, y);
-      y = mfma32(ah, bl, y);
-      y = mfma32(al, bh, y);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.a[32 + crow(i, hg)][c] = -y[i];   // T21 over A21, read for X above
-  }
-  __syncthreads();
-  float* dst = ck_t + ((size_t)slot * H + h) * (kGdC * kGdC);
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int pc = lane + 64 * it, row = pc >> 4, c4 = pc & 15;
-    *(float4*)(dst + row * kGdC + 4 * c4) = *(const float4*)&sm.a[row][4 * c4];
-  }
+#undef GD_TMAT_FETCH
+#undef GD_TMAT_NEXT
 }
 
 // ===========================================================================
@@ -1503,6 +1591,32 @@ gd_fwd_grouped_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
   __shared__ int s_bad;
   gd_fwd_body<OutT, false, true>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o, ht,
                                  status, nullptr, nullptr, ck_t, gS);
+}
+
+// CUs of the current device (cached per device; 256 if the query fails).
+int gd_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Pass 0's launch: items per workgroup so that the grid is one round of
+// resident workgroups.
+struct GdTmatLaunch {
+  unsigned grid;
+  int per;
+};
+GdTmatLaunch gd_tmat_launch(size_t slots, int H) {
+  const size_t items = slots * (size_t)H;
+  const size_t res = (size_t)gd_cu_count() * kGdTmatPerCu;
+  const size_t per = std::max<size_t>(1, (items + res - 1) / res);
+  return {(unsigned)std::max<size_t>(1, (items + per - 1) / per), (int)per};
 }
 
 struct GdFwdLayout {
@@ -1963,8 +2077,8 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   }
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
   // pass 0: T = (I + A)^-1 of every chunk
-  gd_tmat_kernel<<<(unsigned)(lay.slots * H), 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k,
-                                                          ck_t);
+  const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
+  gd_tmat_kernel<<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
   // passes 1 and 2 side by side: the recomputation stores the chunk-start
   // states and the U of every chunk (it also validates cu_seqlens and writes
   // the status word); the state-gradient chain stores dS at every chunk's end
@@ -2035,8 +2149,8 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
     multi = false;
     for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
   }
-  gd_tmat_kernel<<<(unsigned)(lay.slots * H), 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k,
-                                                          ck_t);
+  const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
+  gd_tmat_kernel<<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
   if (multi) {
     gd_grp_compose_kernel<<<(unsigned)(2 * lay.gslots * H), kGdThreads, 0, s>>>(
         (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ,
