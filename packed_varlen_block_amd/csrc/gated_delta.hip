@@ -44,11 +44,12 @@ struct GdSmem {
   alignas(16) bf16 v[kGdC][kKP];
   alignas(16) float at[kGdC][kFP];   // A^T: at[j][i] = A[i][j]
   alignas(16) float p[kGdC][kFP];    // P (row i, column j)
-  // A operands shared by the four waves, split once per chunk, in fragment
-  // order [..][lane]: the gated keys for the state update (key-dim block r,
-  // position step s) and P (row block rb, position step s; rb = 0 stops at
-  // s = 2).  Positions inside a step are in the order of the C layout's rows.
-  alignas(16) bf16x8 kth[4][4][64], ktl[4][4][64];
+  // A operands shared by the four waves, in fragment order [..][lane]: K^T
+  // for the state update (key-dim block r, position step s; exact in bf16)
+  // and P split once per chunk (row block rb, position step s; rb = 0 stops
+  // at s = 2).  Positions inside a step are in the order of the C layout's
+  // rows.
+  alignas(16) bf16x8 kt[4][4][64];
   alignas(16) bf16x8 ph[6][64], pl[6][64];
   alignas(16) float gl[kGdC];        // gamma_i log2(e)
   alignas(16) float eg[kGdC];        // exp(gamma_i)
@@ -162,7 +163,9 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   // computed (and before its outputs are stored, so that waiting for them
   // never waits for those stores).
   uint4 pq[4], pk[4], pv[4];
-  float4 pt0, pt1, pt2, pt3;                          // CKPT: the chunk's T = (I + A)^-1
+  // the chunk's T = (I + A)^-1: fp32 rows (CKPT) or its six split A
+  // fragments (GROUPED, 12 KB: three 16-byte pieces a thread)
+  float4 pt0, pt1, pt2, pt3;
   float pg = 0.f, pb = 0.f;
   auto fetch = [&](int cc0) {
     const int nvv = min(kGdC, L - cc0);
@@ -171,7 +174,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       pt0 = *(const float4*)tp;
       pt1 = *(const float4*)(tp + 4 * kGdThreads);
       pt2 = *(const float4*)(tp + 8 * kGdThreads);
-      pt3 = *(const float4*)(tp + 12 * kGdThreads);
+      if constexpr (CKPT) pt3 = *(const float4*)(tp + 12 * kGdThreads);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -216,11 +219,16 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       *(uint4*)&sm.k[row][col] = pk[it];
       *(uint4*)&sm.v[row][col] = pv[it];
     }
-    if constexpr (USE_T) {                            // T, row-major, in A^T's place
+    if constexpr (CKPT) {                             // T, row-major, in A^T's place
       *(float4*)&sm.at[tid >> 4][4 * (tid & 15)] = pt0;
       *(float4*)&sm.at[(tid >> 4) + 16][4 * (tid & 15)] = pt1;
       *(float4*)&sm.at[(tid >> 4) + 32][4 * (tid & 15)] = pt2;
       *(float4*)&sm.at[(tid >> 4) + 48][4 * (tid & 15)] = pt3;
+    } else if constexpr (GROUPED) {                   // T's fragments, as stored, in A^T's place
+      float4* tf = reinterpret_cast<float4*>(&sm.at[0][0]);
+      tf[tid] = pt0;
+      tf[tid + kGdThreads] = pt1;
+      tf[tid + 2 * kGdThreads] = pt2;
     }
     if (w == 0) {
       float x = pg;                                   // inclusive sum over the chunk
@@ -288,19 +296,16 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       else block(QK{}, 1, 1);
     }
 
-    // ---- the gated keys (diag(G_63 / G) K)^T as split A fragments, once for
-    // the four waves: fragment f = (r, s, lane) of a thread
+    // ---- K^T as A fragments (exact in bf16), once for the four waves:
+    // fragment (r, s, lane (fc, fh)) of thread tid is r = it, s = w, element
+    // e K[kpos(s, e, fh)][32 r + fc]; the gate G_63 / G goes with U instead
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int f = tid + kGdThreads * it;
-      const int r = f >> 8, s = (f >> 6) & 3, fl = f & 63, fc = fl & 31, fh = fl >> 5;
-      float x[8];
+      const bf16* kc = &sm.k[16 * w + 4 * hg][32 * it + c];
+      bf16x8 x;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = kpos(s, e, fh);
-        x[e] = (float)sm.k[pos][32 * r + fc] * sm.dec[pos];
-      }
-      split8(x, sm.kth[r][s][fl], sm.ktl[r][s][fl]);
+      for (int e = 0; e < 8; ++e) x[e] = kc[(8 * (e >> 2) + (e & 3)) * kKP];
+      sm.kt[it][w][lane] = x;
     }
 
     // ---- K S0 and Q S0 for this wave's columns.  The state is the B operand
@@ -417,11 +422,18 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           if (rb == 0 && s >= 2) continue;
-          const float* tr = &sm.at[32 * rb + c][kpos(s, 0, hg)];
-          const float4 t0v = *(const float4*)tr, t1v = *(const float4*)(tr + 8);
-          const float xa[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
           bf16x8 ah, al;
-          split8(xa, ah, al);
+          if constexpr (CKPT) {
+            const float* tr = &sm.at[32 * rb + c][kpos(s, 0, hg)];
+            const float4 t0v = *(const float4*)tr, t1v = *(const float4*)(tr + 8);
+            const float xa[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+            split8(xa, ah, al);
+          } else {                                      // fragment f = (rb, s) as pass 0 split it
+            const bf16x8* tf = reinterpret_cast<const bf16x8*>(&sm.at[0][0]);
+            const int f = rb == 0 ? s : 2 + s;
+            ah = tf[(2 * f) * 64 + lane];
+            al = tf[(2 * f + 1) * 64 + lane];
+          }
           uu[rb] = mfma32(ah, bh, uu[rb]);
           uu[rb] = mfma32(ah, bl, uu[rb]);
           uu[rb] = mfma32(al, bh, uu[rb]);
@@ -429,8 +441,10 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       }
       ks[0] = uu[0];
       ks[1] = uu[1];
+      if constexpr (!CKPT) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) split_u(s);
+        for (int s = 0; s < 4; ++s) split_u(s);
+      }
     } else {
       triangle(std::integral_constant<int, 0>{});
       split_u(0);
@@ -478,6 +492,19 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
           oacc[rb] = mfma32(a_lo, uh[s], oacc[rb]);
         }
     }
+    // the state update as K^T (diag(G_63 / G) U): K^T exact, the scaled U
+    // split (k-step s: positions kpos(s, e, hg))
+    bf16x8 dh[4], dl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float4 d0 = *(const float4*)&sm.dec[16 * s + 4 * hg];
+      const float4 d1 = *(const float4*)&sm.dec[16 * s + 8 + 4 * hg];
+      const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = dd[e] * ks[s >> 1][8 * (s & 1) + e];
+      split8(x, dh[s], dl[s]);
+    }
     const float glast = sm.eg[kGdC - 1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -485,10 +512,9 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       for (int i = 0; i < 16; ++i) S[r][i] *= glast;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 a_hi = sm.kth[r][s][lane], a_lo = sm.ktl[r][s][lane];
-        S[r] = mfma32(a_hi, uh[s], S[r]);
-        S[r] = mfma32(a_hi, ul[s], S[r]);
-        S[r] = mfma32(a_lo, uh[s], S[r]);
+        const bf16x8 ka = sm.kt[r][s][lane];
+        S[r] = mfma32(ka, dh[s], S[r]);
+        S[r] = mfma32(ka, dl[s], S[r]);
       }
     }
     if constexpr (CKPT) continue;                     // no O in the recomputation pass
@@ -1026,7 +1052,9 @@ constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
 // forward substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj in fp32, lane j
 // taking column j of T11 and lane 32 + j column j of T22; then T21 = -T22 A21
 // T11 on the matrix cores.  Rows and columns past the chunk's end give the
-// identity.
+// identity.  FRAG: T is stored as the six split A fragments that U = T rhs
+// takes (fragment f = (rb, s), rb = 0 for f < 2; [f][hi, lo][lane], 12 KB of
+// the item's 16 KB), else as fp32 rows.
 constexpr int kGdTmatPerCu = 8;       // resident workgroups per CU (LDS: 8 x 17.9 KB)
 struct GdTmatSmem {
   alignas(16) float a[kGdC][kFP];    // A, then T over it
@@ -1034,6 +1062,7 @@ struct GdTmatSmem {
   alignas(16) float beta[kGdC];
 };
 
+template <bool FRAG>
 __global__ void __launch_bounds__(64, 2)
 gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const float* __restrict__ beta,
                const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float* __restrict__ ck_t, int per) {
@@ -1235,10 +1264,26 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
     }
     __syncthreads();
     float* dst = ck_t + ((size_t)cur_slot * H + cur_h) * (kGdC * kGdC);
+    if constexpr (FRAG) {
+      // A element e of lane (c, hg) in fragment (rb, s) is T[32 rb + c][kpos(s, e, hg)]
+      bf16x8* fd = reinterpret_cast<bf16x8*>(dst);
 #pragma unroll
-    for (int i2 = 0; i2 < 16; ++i2) {
-      const int pc = lane + 64 * i2, row = pc >> 4, c4 = pc & 15;
-      *(float4*)(dst + row * kGdC + 4 * c4) = *(const float4*)&sm.a[row][4 * c4];
+      for (int f = 0; f < 6; ++f) {
+        const int rb = f < 2 ? 0 : 1, s2 = f < 2 ? f : f - 2;
+        const float* tr = &sm.a[32 * rb + c][kpos(s2, 0, hg)];
+        const float4 p0 = *(const float4*)tr, p1 = *(const float4*)(tr + 8);
+        const float xa[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        bf16x8 th, tl;
+        split8(xa, th, tl);
+        fd[(2 * f) * 64 + lane] = th;
+        fd[(2 * f + 1) * 64 + lane] = tl;
+      }
+    } else {
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) {
+        const int pc = lane + 64 * i2, row = pc >> 4, c4 = pc & 15;
+        *(float4*)(dst + row * kGdC + 4 * c4) = *(const float4*)&sm.a[row][4 * c4];
+      }
     }
     (void)cur_n;
     if (!more) break;
@@ -1269,7 +1314,7 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
 struct GdComposeSmem {
   alignas(16) bf16 k[kGdC][kKP];
   alignas(16) bf16 v[kGdC][kKP];
-  alignas(16) float tm[kGdC][kFP];                    // T, row-major
+  alignas(16) bf16x8 tf[12][64];                      // T's split A fragments, as pass 0 stores them
   alignas(16) bf16x8 kt[4][4][64];                    // K^T as A fragments [d_k block][k-step][lane]
   alignas(16) float eg[kGdC], dec[kGdC], beta[kGdC];
 };
@@ -1330,10 +1375,10 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
   // chunk j + 1's K, V (Z only), T and gates are loaded into registers while
   // chunk j is computed (every chunk of a composed group is full); scalar
   // registers, not arrays, which the compiler would move to LDS.  Thread tid
-  // takes rows tid/16 + 16 it, columns 8 (tid % 16) of K and V and the float4
-  // tid + 256 it of T, it = 0..3.
+  // takes rows tid/16 + 16 it, columns 8 (tid % 16) of K and V (it = 0..3)
+  // and the 16-byte pieces tid + 256 it of T's fragments (it = 0..2).
   uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
-  float4 pt0, pt1, pt2, pt3;
+  float4 pt0, pt1, pt2;
   float pg, pb;
   const int frow = tid >> 4, fcol = (tid & 15) * 8;
 #define GD_CMP_FETCH(j_)                                                                                \
@@ -1354,7 +1399,6 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
     pt0 = *(const float4*)tp_;                                                                          \
     pt1 = *(const float4*)(tp_ + 4 * kGdThreads);                                                       \
     pt2 = *(const float4*)(tp_ + 8 * kGdThreads);                                                       \
-    pt3 = *(const float4*)(tp_ + 12 * kGdThreads);                                                      \
     pg = g[(size_t)(t0_ + lane) * H + h];                                                               \
     pb = beta[(size_t)(t0_ + lane) * H + h];                                                            \
   }
@@ -1369,10 +1413,9 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
     *(uint4*)&sm.v[frow + 16][fcol] = pv1;
     *(uint4*)&sm.v[frow + 32][fcol] = pv2;
     *(uint4*)&sm.v[frow + 48][fcol] = pv3;
-    *(float4*)&sm.tm[frow][4 * (tid & 15)] = pt0;
-    *(float4*)&sm.tm[frow + 16][4 * (tid & 15)] = pt1;
-    *(float4*)&sm.tm[frow + 32][4 * (tid & 15)] = pt2;
-    *(float4*)&sm.tm[frow + 48][4 * (tid & 15)] = pt3;
+    reinterpret_cast<float4*>(&sm.tf[0][0])[tid] = pt0;
+    reinterpret_cast<float4*>(&sm.tf[0][0])[tid + kGdThreads] = pt1;
+    reinterpret_cast<float4*>(&sm.tf[0][0])[tid + 2 * kGdThreads] = pt2;
     if (w == 0) {
       float x = pg;
 #pragma unroll
@@ -1446,11 +1489,8 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         if (rb == 0 && s >= 2) continue;
-        const float* tr = &sm.tm[32 * rb + c][kpos(s, 0, hg)];
-        const float4 a0 = *(const float4*)tr, a1 = *(const float4*)(tr + 8);
-        const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        bf16x8 th, tl;
-        split8(xa, th, tl);
+        const int f = rb == 0 ? s : 2 + s;              // fragment (rb, s) as pass 0 split it
+        const bf16x8 th = sm.tf[2 * f][lane], tl = sm.tf[2 * f + 1][lane];
         uu[rb] = mfma32(th, bh, uu[rb]);
         uu[rb] = mfma32(th, bl, uu[rb]);
         uu[rb] = mfma32(tl, bh, uu[rb]);
@@ -2078,7 +2118,7 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
   // pass 0: T = (I + A)^-1 of every chunk
   const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
-  gd_tmat_kernel<<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
+  gd_tmat_kernel<false><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
   // passes 1 and 2 side by side: the recomputation stores the chunk-start
   // states and the U of every chunk (it also validates cu_seqlens and writes
   // the status word); the state-gradient chain stores dS at every chunk's end
@@ -2150,7 +2190,8 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
     for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
   }
   const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
-  gd_tmat_kernel<<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
+  gd_tmat_kernel<true><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t,
+                                              tl.per);
   if (multi) {
     gd_grp_compose_kernel<<<(unsigned)(2 * lay.gslots * H), kGdThreads, 0, s>>>(
         (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ,
