@@ -1071,10 +1071,15 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
   const int lane = threadIdx.x, hg = lane >> 5, c = lane & 31;
   if (gd_cu_bad(cu, n_seg, T, &s_bad) || n_seg == 0) return;
   const int64_t n_items = ((int64_t)T / kGdC + n_seg + 1) * H;
-  const int64_t it_end = std::min<int64_t>(n_items, ((int64_t)blockIdx.x + 1) * per);
+  // run r of workgroup x: consecutive runs on one XCD (x mod 8 with the grid a
+  // multiple of 8), so the heads of a slot read its g and beta lines through
+  // one L2
+  const int64_t run = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t it_end = std::min<int64_t>(n_items, (run + 1) * per);
   // the slice of the current slot: the largest b whose first slot cu[b]/64 + b
   // is at most the slot (found once by bisection, then advanced)
-  int64_t it = (int64_t)blockIdx.x * per;
+  int64_t it = run * per;
+  if (it >= it_end) return;
   int b;
   {
     const int64_t slot = it / H;
@@ -1656,7 +1661,8 @@ GdTmatLaunch gd_tmat_launch(size_t slots, int H) {
   const size_t items = slots * (size_t)H;
   const size_t res = (size_t)gd_cu_count() * kGdTmatPerCu;
   const size_t per = std::max<size_t>(1, (items + res - 1) / res);
-  return {(unsigned)std::max<size_t>(1, (items + per - 1) / per), (int)per};
+  const size_t runs = std::max<size_t>(1, (items + per - 1) / per);
+  return {(unsigned)((runs + 7) / 8 * 8), (int)per};   // a multiple of 8: runs map to XCDs in blocks
 }
 
 struct GdFwdLayout {
