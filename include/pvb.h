@@ -400,7 +400,10 @@ pvb_status pvb_varlen_cross_attn_bwd(const void* d_q, const void* d_k, const voi
  *   d_o            out [T, H, d], bf16 or fp32 per o_dtype                   (device)
  *   d_ht           out fp32 [n_seg, H, d, d] final states, nullable          (device)
  *   workspace      >= pvb_gated_delta_fwd_workspace_bytes(T, H, n_seg) bytes
- *                  (device), or null with workspace_bytes = 0
+ *                  (device), or null with workspace_bytes = 0: 12 KB per
+ *                  64-token chunk slot and head (T/64 + n_seg + 1 slots) and
+ *                  192 KB per 1024-token group slot and head (T/1024 + n_seg
+ *                  + 1 slots); about 0.62 GB at T = 32768, H = 32
  *   d_status       out: device status word (required)                       (device)
  * d = 128 (else PVB_E_UNSUPPORTED).  The slices are computed in chunks of 64
  * tokens (UT transform) in fp32 with matrix-core products whose fp32 operands
@@ -459,8 +462,8 @@ pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void*
  *   d_dg, d_dbeta  out fp32 [T, H]
  *   d_dh0          out fp32 [n_seg, H, d, d], nullable
  *   workspace      >= pvb_gated_delta_bwd_workspace_bytes(T, H, n_seg) bytes
- *                  (208 KB per 64-token chunk slot and head, T/64 + n_seg + 1
- *                  slots: about 3.7 GB at T = 32768, H = 32)           (device)
+ *                  (216 KB per 64-token chunk slot and head, T/64 + n_seg + 1
+ *                  slots: about 3.9 GB at T = 32768, H = 32)           (device)
  * d = 128.  Device-detected error: PVB_E_BAD_CU_SEQLENS (then no gradient is
  * written). */
 size_t pvb_gated_delta_bwd_workspace_bytes(int32_t T, int32_t H, int32_t n_seg);

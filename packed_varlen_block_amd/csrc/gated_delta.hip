@@ -35,6 +35,8 @@ namespace {
 constexpr int kGdD = 128;            // d_k = d_v
 constexpr int kGdC = 64;             // chunk length
 constexpr int kGdThreads = 256;
+// six split A fragments of a 64x64 matrix, [f][hi, lo][lane] x 16 bytes (12 KB)
+constexpr size_t kGdTFragFloats = 6 * 2 * 64 * 4;
 constexpr int kKP = kGdD + 8;        // bf16 row pitch of the Q, K, V tiles
 constexpr int kFP = kGdC + 4;        // fp32 row pitch of A^T and P
 
@@ -163,18 +165,18 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   // computed (and before its outputs are stored, so that waiting for them
   // never waits for those stores).
   uint4 pq[4], pk[4], pv[4];
-  // the chunk's T = (I + A)^-1: fp32 rows (CKPT) or its six split A
-  // fragments (GROUPED, 12 KB: three 16-byte pieces a thread)
-  float4 pt0, pt1, pt2, pt3;
+  // the chunk's T = (I + A)^-1 as its six split A fragments (12 KB, three
+  // 16-byte pieces a thread); the backward's slots also hold T^T's after them
+  float4 pt0, pt1, pt2;
   float pg = 0.f, pb = 0.f;
+  constexpr size_t kTStride = (CKPT ? 2 : 1) * kGdTFragFloats;
   auto fetch = [&](int cc0) {
     const int nvv = min(kGdC, L - cc0);
     if constexpr (USE_T) {
-      const float* tp = ck_t + (gd_ckpt_slot(seg0, b, cc0 / kGdC) * H + h) * (kGdC * kGdC) + 4 * tid;
+      const float* tp = ck_t + (gd_ckpt_slot(seg0, b, cc0 / kGdC) * H + h) * kTStride + 4 * tid;
       pt0 = *(const float4*)tp;
       pt1 = *(const float4*)(tp + 4 * kGdThreads);
       pt2 = *(const float4*)(tp + 8 * kGdThreads);
-      if constexpr (CKPT) pt3 = *(const float4*)(tp + 12 * kGdThreads);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -219,12 +221,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       *(uint4*)&sm.k[row][col] = pk[it];
       *(uint4*)&sm.v[row][col] = pv[it];
     }
-    if constexpr (CKPT) {                             // T, row-major, in A^T's place
-      *(float4*)&sm.at[tid >> 4][4 * (tid & 15)] = pt0;
-      *(float4*)&sm.at[(tid >> 4) + 16][4 * (tid & 15)] = pt1;
-      *(float4*)&sm.at[(tid >> 4) + 32][4 * (tid & 15)] = pt2;
-      *(float4*)&sm.at[(tid >> 4) + 48][4 * (tid & 15)] = pt3;
-    } else if constexpr (GROUPED) {                   // T's fragments, as stored, in A^T's place
+    if constexpr (USE_T) {                            // T's fragments, as stored, in A^T's place
       float4* tf = reinterpret_cast<float4*>(&sm.at[0][0]);
       tf[tid] = pt0;
       tf[tid + kGdThreads] = pt1;
@@ -422,18 +419,10 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           if (rb == 0 && s >= 2) continue;
-          bf16x8 ah, al;
-          if constexpr (CKPT) {
-            const float* tr = &sm.at[32 * rb + c][kpos(s, 0, hg)];
-            const float4 t0v = *(const float4*)tr, t1v = *(const float4*)(tr + 8);
-            const float xa[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
-            split8(xa, ah, al);
-          } else {                                      // fragment f = (rb, s) as pass 0 split it
-            const bf16x8* tf = reinterpret_cast<const bf16x8*>(&sm.at[0][0]);
-            const int f = rb == 0 ? s : 2 + s;
-            ah = tf[(2 * f) * 64 + lane];
-            al = tf[(2 * f + 1) * 64 + lane];
-          }
+          // fragment f = (rb, s) as pass 0 split it
+          const bf16x8* tf = reinterpret_cast<const bf16x8*>(&sm.at[0][0]);
+          const int f = rb == 0 ? s : 2 + s;
+          const bf16x8 ah = tf[(2 * f) * 64 + lane], al = tf[(2 * f + 1) * 64 + lane];
           uu[rb] = mfma32(ah, bh, uu[rb]);
           uu[rb] = mfma32(ah, bl, uu[rb]);
           uu[rb] = mfma32(al, bh, uu[rb]);
@@ -811,9 +800,9 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
 
   const int n_chunks = (L + kGdC - 1) / kGdC;
   GdStage<kGdThreads> pf;
-  float4 ptm0, ptm1, ptm2, ptm3;                      // the chunk's T = (I + A)^-1, row-major
-  const float* tbase = ck_t + (gd_ckpt_slot(seg0, b, 0) * H + h) * (kGdC * kGdC) + 4 * tid;
-  const size_t tstep = (size_t)H * kGdC * kGdC;       // one checkpoint slot
+  float4 ptm0, ptm1, ptm2;                            // the chunk's T^T fragments (12 KB)
+  const float* tbase = ck_t + (gd_ckpt_slot(seg0, b, 0) * H + h) * (2 * kGdTFragFloats) + kGdTFragFloats + 4 * tid;
+  const size_t tstep = (size_t)H * 2 * kGdTFragFloats;   // one checkpoint slot
   if (n_chunks > 0) {
     const int c0 = (n_chunks - 1) * kGdC;
     pf.fetch(q, k, dout, g, beta, seg0 + c0, L - c0, H, Hk, h, hk, tid);
@@ -821,7 +810,6 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
     ptm0 = *(const float4*)tp;
     ptm1 = *(const float4*)(tp + 4 * kGdThreads);
     ptm2 = *(const float4*)(tp + 8 * kGdThreads);
-    ptm3 = *(const float4*)(tp + 12 * kGdThreads);
   }
   for (int ci = n_chunks - 1; ci >= 0; --ci) {
     const int t0 = seg0 + ci * kGdC;
@@ -851,12 +839,11 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
     }
     __syncthreads();                                  // the previous chunk's LDS reads are done
     pf.put(t, tid);
-    {                                                 // T into Ah's place
-      const int ch = tid;
-      *(float4*)&t.ah[ch >> 4][4 * (ch & 15)] = ptm0;
-      *(float4*)&t.ah[(ch >> 4) + 16][4 * (ch & 15)] = ptm1;
-      *(float4*)&t.ah[(ch >> 4) + 32][4 * (ch & 15)] = ptm2;
-      *(float4*)&t.ah[(ch >> 4) + 48][4 * (ch & 15)] = ptm3;
+    {                                                 // T^T's fragments, as stored, into Ah's place
+      float4* tf = reinterpret_cast<float4*>(&t.ah[0][0]);
+      tf[tid] = ptm0;
+      tf[tid + kGdThreads] = ptm1;
+      tf[tid + 2 * kGdThreads] = ptm2;
     }
     if (w == 0) gd_gates(t, pf.g, pf.b, lane);
     if (ci > 0) {
@@ -866,7 +853,6 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
       ptm0 = *(const float4*)tp;
       ptm1 = *(const float4*)(tp + 4 * kGdThreads);
       ptm2 = *(const float4*)(tp + 8 * kGdThreads);
-      ptm3 = *(const float4*)(tp + 12 * kGdThreads);
     }
     __syncthreads();
 
@@ -933,7 +919,8 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
       for (int i = 0; i < 16; ++i) du[rb][i] = scale * du[rb][i] + t.dec[32 * rb + crow(i, hg)] * kds[rb][i];
 
     // ---- dR = (I + A)^-T dU = T^T dU: A element e of lane (c, hg) at k-step s
-    // is T[kpos(s, e, hg)][32 rb + c]; row block 1 of T^T has no column below 32
+    // is T[kpos(s, e, hg)][32 rb + c], fragment f = rb == 0 ? s : 2 + s as pass
+    // 0 split it; row block 1 of T^T has no column below 32
     {
       f32x16 dr[2] = {};
 #pragma unroll
@@ -946,11 +933,9 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           if (rb == 1 && s < 2) continue;
-          float xa[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xa[e] = t.ah[kpos(s, e, hg)][32 * rb + c];
-          bf16x8 ah, al;
-          split8(xa, ah, al);
+          const bf16x8* tf = reinterpret_cast<const bf16x8*>(&t.ah[0][0]);
+          const int f = rb == 0 ? s : 2 + s;
+          const bf16x8 ah = tf[(2 * f) * 64 + lane], al = tf[(2 * f + 1) * 64 + lane];
           dr[rb] = mfma32(ah, bh, dr[rb]);
           dr[rb] = mfma32(ah, bl, dr[rb]);
           dr[rb] = mfma32(al, bh, dr[rb]);
@@ -1052,9 +1037,10 @@ constexpr int kUP = kGdD + 4;        // fp32 row pitch of the staged U and dR
 // forward substitution, T_ij = [i = j] - sum_{l < i} A_il T_lj in fp32, lane j
 // taking column j of T11 and lane 32 + j column j of T22; then T21 = -T22 A21
 // T11 on the matrix cores.  Rows and columns past the chunk's end give the
-// identity.  FRAG: T is stored as the six split A fragments that U = T rhs
-// takes (fragment f = (rb, s), rb = 0 for f < 2; [f][hi, lo][lane], 12 KB of
-// the item's 16 KB), else as fp32 rows.
+// identity.  T is stored as the six split A fragments that U = T rhs takes
+// (fragment f = (rb, s): rb = 0, s = f for f < 2, else rb = 1, s = f - 2;
+// [f][hi, lo][lane], 12 KB); TT (the backward) adds after them the six of
+// T^T that dR = T^T dU takes (rb = 0, s = f for f < 4, else rb = 1, s = f - 2).
 constexpr int kGdTmatPerCu = 8;       // resident workgroups per CU (LDS: 8 x 17.9 KB)
 struct GdTmatSmem {
   alignas(16) float a[kGdC][kFP];    // A, then T over it
@@ -1062,7 +1048,7 @@ struct GdTmatSmem {
   alignas(16) float beta[kGdC];
 };
 
-template <bool FRAG>
+template <bool TT>
 __global__ void __launch_bounds__(64, 2)
 gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const float* __restrict__ beta,
                const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float* __restrict__ ck_t, int per) {
@@ -1268,8 +1254,8 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
       for (int i = 0; i < 16; ++i) sm.a[32 + crow(i, hg)][c] = -y[i];   // T21 over A21, read for X above
     }
     __syncthreads();
-    float* dst = ck_t + ((size_t)cur_slot * H + cur_h) * (kGdC * kGdC);
-    if constexpr (FRAG) {
+    float* dst = ck_t + ((size_t)cur_slot * H + cur_h) * ((TT ? 2 : 1) * kGdTFragFloats);
+    {
       // A element e of lane (c, hg) in fragment (rb, s) is T[32 rb + c][kpos(s, e, hg)]
       bf16x8* fd = reinterpret_cast<bf16x8*>(dst);
 #pragma unroll
@@ -1283,11 +1269,20 @@ gd_tmat_kernel(const bf16* __restrict__ k, const float* __restrict__ g, const fl
         fd[(2 * f) * 64 + lane] = th;
         fd[(2 * f + 1) * 64 + lane] = tl;
       }
-    } else {
+    }
+    if constexpr (TT) {
+      // A element e of lane (c, hg) in fragment (rb, s) of T^T is T[kpos(s, e, hg)][32 rb + c]
+      bf16x8* fd = reinterpret_cast<bf16x8*>(dst + kGdTFragFloats);
 #pragma unroll
-      for (int i2 = 0; i2 < 16; ++i2) {
-        const int pc = lane + 64 * i2, row = pc >> 4, c4 = pc & 15;
-        *(float4*)(dst + row * kGdC + 4 * c4) = *(const float4*)&sm.a[row][4 * c4];
+      for (int f = 0; f < 6; ++f) {
+        const int rb = f < 4 ? 0 : 1, s2 = f < 4 ? f : f - 2;
+        float xa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[e] = sm.a[kpos(s2, e, hg)][32 * rb + c];
+        bf16x8 th, tl;
+        split8(xa, th, tl);
+        fd[(2 * f) * 64 + lane] = th;
+        fd[(2 * f + 1) * 64 + lane] = tl;
       }
     }
     (void)cur_n;
@@ -1389,7 +1384,7 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
 #define GD_CMP_FETCH(j_)                                                                                \
   {                                                                                                    \
     const int t0_ = seg0 + (gi * kGdGrpChunks + (j_)) * kGdC;                                           \
-    const float* tp_ = ck_t + (gd_ckpt_slot(seg0, b, gi * kGdGrpChunks + (j_)) * H + h) * (kGdC * kGdC) \
+    const float* tp_ = ck_t + (gd_ckpt_slot(seg0, b, gi * kGdGrpChunks + (j_)) * H + h) * kGdTFragFloats \
                        + 4 * tid;                                                                       \
     const bf16* kp_ = k + ((size_t)(t0_ + frow) * Hk + hk) * kGdD + fcol;                               \
     pk0 = *(const uint4*)kp_;                                                                           \
@@ -1675,7 +1670,7 @@ GdFwdLayout gd_fwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   l.gslots = (size_t)T / kGdGrpTok + (size_t)n_seg + 1;
   const size_t gs = up(l.gslots * H * kGdD * kGdD * sizeof(float));
   l.ck_t = 0;
-  l.gA = up(l.slots * H * kGdC * kGdC * sizeof(float));
+  l.gA = up(l.slots * H * kGdTFragFloats * sizeof(float));
   l.gZ = l.gA + gs;
   l.gS = l.gZ + gs;
   l.total = l.gS + gs;
@@ -2071,7 +2066,7 @@ GdBwdLayout gd_bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   l.ck_u = 2 * st;
   l.ck_dr = 2 * st + ch;
   l.ck_t = 2 * st + 2 * ch;
-  l.total = l.ck_t + up(l.slots * H * kGdC * kGdC * sizeof(float));
+  l.total = l.ck_t + up(l.slots * H * 2 * kGdTFragFloats * sizeof(float));
   return l;
 }
 
@@ -2124,7 +2119,7 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
   // pass 0: T = (I + A)^-1 of every chunk
   const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
-  gd_tmat_kernel<false><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
+  gd_tmat_kernel<true><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
   // passes 1 and 2 side by side: the recomputation stores the chunk-start
   // states and the U of every chunk (it also validates cu_seqlens and writes
   // the status word); the state-gradient chain stores dS at every chunk's end
@@ -2196,8 +2191,8 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
     for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
   }
   const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
-  gd_tmat_kernel<true><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t,
-                                              tl.per);
+  gd_tmat_kernel<false><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t,
+                                               tl.per);
   if (multi) {
     gd_grp_compose_kernel<<<(unsigned)(2 * lay.gslots * H), kGdThreads, 0, s>>>(
         (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ,

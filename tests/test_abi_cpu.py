@@ -295,14 +295,15 @@ def test_gated_delta_host_side_errors():
 
 
 def test_gated_delta_forward_workspace_size():
-    """T of every 64-token chunk slot (16 KB per head) and, per 1024-token group
-    slot and head, the group map A_g, the state Z_g and the starting state
-    (64 KB each); slots: T/64 + B + 1 and T/1024 + B + 1."""
+    """T's six split fragments for every 64-token chunk slot (12 KB per head)
+    and, per 1024-token group slot and head, the group map A_g, the state Z_g
+    and the starting state (64 KB each); slots: T/64 + B + 1 and
+    T/1024 + B + 1."""
     W = pvb.gated_delta_fwd_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     for T, H, B in ((8, 2, 1), (32768, 32, 32), (4096, 3, 600)):
         slots, gslots = T // 64 + B + 1, T // 1024 + B + 1
-        assert W(T, H, B) == up(slots * H * 64 * 64 * 4) + 3 * up(gslots * H * 128 * 128 * 4)
+        assert W(T, H, B) == up(slots * H * 12288) + 3 * up(gslots * H * 128 * 128 * 4)
     assert W(-1, 2, 1) == 0 and W(8, 0, 1) == 0
 
 
