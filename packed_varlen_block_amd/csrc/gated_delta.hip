@@ -761,11 +761,18 @@ struct GdChainSmem {
   alignas(16) bf16x8 kt[4][4][64], qt[4][4][64];
 };
 
-// Pass 2: one workgroup per (slice, value head), chunks from the last to the
-// first.  Wave w owns value columns [32w, 32w + 32): dS stays in its registers
-// (C layout of four 32x32 blocks, rows = key dims), as the state does in the
-// forward.
-template <typename GradT>
+// Pass 2: the state-gradient chain, chunks from the last to the first.  Wave
+// w owns value columns [32w, 32w + 32): dS stays in its registers (C layout
+// of four 32x32 blocks, rows = key dims), as the state does in the forward.
+// MODE 0: one workgroup per (slice, value head) walks the whole slice from the
+// final-state gradient.  MODE 1 and 2 work on a group of 16 chunks (block =
+// group slot x H + head, as the grouped forward): dS of a group's start is
+// A_g^T dS of its end plus an offset F_g (A_g the forward's map of the group),
+// so MODE 1 walks the group from dS = 0 without storing anything and leaves
+// F_g in gF (groups after a slice's first); MODE 2 walks it from dS of its end
+// (gD, or the final-state gradient for the slice's last group) with every
+// store, and writes dh0 for the slice's first group.
+template <typename GradT, int MODE = 0>
 __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, int blk, const bf16* __restrict__ q,
                                                   const bf16* __restrict__ k, const float* __restrict__ g,
                                                   const float* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -773,17 +780,39 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
                                                   const bf16* __restrict__ dout, const float* __restrict__ dht,
                                                   const float* __restrict__ ck_t, float* __restrict__ ck_ds,
                                                   float* __restrict__ ck_dr, GradT* __restrict__ dv,
-                                                  float* __restrict__ dh0) {
+                                                  float* __restrict__ dh0, float* __restrict__ gF = nullptr,
+                                                  const float* __restrict__ gD = nullptr) {
   GdTiles& t = sm.t;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
-  if (gd_cu_bad(cu, n_seg, T, &s_bad) || (int)blk >= n_seg * H) return;
-
-  const int b = blk / H, h = blk - (blk / H) * H;
+  if (gd_cu_bad(cu, n_seg, T, &s_bad)) return;
+  int b, h, gi = 0, n_grp = 1;
+  size_t gslot = 0;
+  if constexpr (MODE == 0) {
+    if ((int)blk >= n_seg * H) return;
+    b = blk / H;
+    h = blk - (blk / H) * H;
+  } else {
+    if (n_seg == 0) return;
+    gslot = (size_t)(blk / H);
+    h = blk - (blk / H) * H;
+    int lo = 0, hi = n_seg - 1;                       // the largest b with cu[b] / kGdGrpTok + b <= gslot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((size_t)(cu[mid] / kGdGrpTok + mid) <= gslot) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    gi = (int)(gslot - (size_t)(cu[b] / kGdGrpTok + b));
+    const int Lb = cu[b + 1] - cu[b];
+    n_grp = std::max(1, (Lb + kGdGrpTok - 1) / kGdGrpTok);   // an empty slice keeps group 0
+    if (gi < 0 || gi >= n_grp || (MODE == 1 && gi == 0)) return;
+  }
   const int hk = h / (H / Hk);
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
   const int n0 = 32 * w + c;
   const size_t st_base = (size_t)(b * H + h) * kGdStateFloats;
+  const size_t gs_base = (gslot * H + h) * kGdStateFloats;
   // staging rows of this wave for row-piece stores: [64][kSP] fp32 in the Q/K/dO
   // tiles, which hold nothing between a chunk's last product and the next
   // chunk's staging; only this wave touches them
@@ -791,31 +820,35 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
   float* stg = reinterpret_cast<float*>(&t.q[0][0]) + w * (kGdC * kSP);
   auto wave_lds_fence = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
 
+  const float* ds_in = MODE == 1 ? nullptr : dht ? dht + st_base : nullptr;
+  if (MODE == 2 && gi + 1 < n_grp) ds_in = gD + gs_base;
   f32x16 dS[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      dS[r][i] = dht ? dht[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
+    for (int i = 0; i < 16; ++i) dS[r][i] = ds_in ? ds_in[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] : 0.f;
 
+  // the chunks [c_lo, c_hi) of this walk
   const int n_chunks = (L + kGdC - 1) / kGdC;
+  const int c_lo = MODE == 0 ? 0 : gi * kGdGrpChunks;
+  const int c_hi = MODE == 0 ? n_chunks : std::min(n_chunks, c_lo + kGdGrpChunks);
   GdStage<kGdThreads> pf;
   float4 ptm0, ptm1, ptm2;                            // the chunk's T^T fragments (12 KB)
   const float* tbase = ck_t + (gd_ckpt_slot(seg0, b, 0) * H + h) * (2 * kGdTFragFloats) + kGdTFragFloats + 4 * tid;
   const size_t tstep = (size_t)H * 2 * kGdTFragFloats;   // one checkpoint slot
-  if (n_chunks > 0) {
-    const int c0 = (n_chunks - 1) * kGdC;
+  if (c_hi > c_lo) {
+    const int c0 = (c_hi - 1) * kGdC;
     pf.fetch(q, k, dout, g, beta, seg0 + c0, L - c0, H, Hk, h, hk, tid);
-    const float* tp = tbase + (size_t)(n_chunks - 1) * tstep;
+    const float* tp = tbase + (size_t)(c_hi - 1) * tstep;
     ptm0 = *(const float4*)tp;
     ptm1 = *(const float4*)(tp + 4 * kGdThreads);
     ptm2 = *(const float4*)(tp + 8 * kGdThreads);
   }
-  for (int ci = n_chunks - 1; ci >= 0; --ci) {
+  for (int ci = c_hi - 1; ci >= c_lo; --ci) {
     const int t0 = seg0 + ci * kGdC;
     const int n = min(kGdC, L - ci * kGdC);
     const size_t slot = gd_ckpt_slot(seg0, b, ci);
-    {
+    if constexpr (MODE != 1) {
       // dS at this chunk's end into its checkpoint: 64 rows at a time through
       // this wave's staging rows, written as 32-byte row pieces
       float* dst = ck_ds + (slot * H + h) * kGdStateFloats + 32 * w;
@@ -846,7 +879,7 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
       tf[tid + 2 * kGdThreads] = ptm2;
     }
     if (w == 0) gd_gates(t, pf.g, pf.b, lane);
-    if (ci > 0) {
+    if (ci > c_lo) {
       const int c0 = (ci - 1) * kGdC;
       pf.fetch(q, k, dout, g, beta, seg0 + c0, kGdC, H, Hk, h, hk, tid);
       const float* tp = tbase + (size_t)(ci - 1) * tstep;
@@ -981,7 +1014,7 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
     }
     // off the chain: dR into its checkpoint and dV = diag(beta) dR, through
     // this wave's staging rows, written as 32-byte row pieces
-    {
+    if constexpr (MODE != 1) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -1014,11 +1047,12 @@ __device__ __forceinline__ void gd_bwd_chain_body(GdChainSmem& sm, int& s_bad, i
       wave_lds_fence();
     }
   }
-  if (dh0) {
+  float* ds_out = MODE == 1 ? gF + gs_base : (dh0 && gi == 0) ? dh0 + st_base : nullptr;
+  if (ds_out) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dh0[st_base + (size_t)(32 * r + crow(i, hg)) * kGdD + n0] = dS[r][i];
+      for (int i = 0; i < 16; ++i) ds_out[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] = dS[r][i];
   }
 }
 
@@ -1321,7 +1355,11 @@ struct GdComposeSmem {
 
 // Pass 1: two workgroups of 4 waves per (group slot, value head), one for
 // Z_g and one for A_g; groups that are the last of their slice (or hold no
-// chunk) return at once.  Block x n_gs + gslot H + h takes map x (0: Z, 1:
+// chunk) return at once, except that for the backward (BWD, whose reverse
+// walk needs A_g of every group after a slice's first) A_g is formed for every
+// group of a slice with more than one, the last group's partial chunks
+// included, and T's slots also hold T^T.  Block x n_gs + gslot H + h takes
+// map x (0: Z, 1:
 // A), n_gs = gslots H, so the pair shares an XCD whenever n_gs is a multiple
 // of 8.  Wave w owns columns [32w, 32w + 32) of its map (C layout, rows = key
 // dims).  M is never formed: M X = G_L X - Kt^T T diag(beta G) K X, so every
@@ -1331,11 +1369,13 @@ struct GdComposeSmem {
 // K^T (diag(G_L / G) U): K^T is exact in bf16, so only the scaled U is split
 // (two products, not three).  With one map per workgroup the registers and
 // LDS allow two workgroups per CU.
+template <bool BWD>
 __global__ void __launch_bounds__(kGdThreads, GD_CMP_OCC)
 gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H,
                       int Hk, const float* __restrict__ ck_t, float* __restrict__ gA, float* __restrict__ gZ,
                       int n_gs) {
+  constexpr size_t t_stride = (BWD ? 2 : 1) * kGdTFragFloats;
   __shared__ GdComposeSmem sm;
   __shared__ int s_bad, s_b;
   const int tid = threadIdx.x;
@@ -1360,7 +1400,10 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
   const int b = s_b, seg0 = cu[b], L = cu[b + 1] - seg0;
   const int gi = (int)(gslot - gd_grp_slot(seg0, b, 0));
   const int n_grp = (L + kGdGrpTok - 1) / kGdGrpTok;
-  if (gi < 0 || gi >= n_grp - 1) return;               // only full groups that another group follows
+  if (gi < 0 || n_grp < 2 || gi >= n_grp - ((BWD && is_a) ? 0 : 1)) return;
+  // chunks of the group: 16, fewer in a slice's last group, whose last chunk
+  // may be partial (its rows past the slice's end load as zero)
+  const int nch = BWD ? std::min(kGdGrpChunks, (L + kGdC - 1) / kGdC - gi * kGdGrpChunks) : kGdGrpChunks;
   const int hk = h / (H / Hk);
   const int n0 = 32 * w + c;
   // V enters Z only; both maps take the same path (one loop, not one per map)
@@ -1373,8 +1416,8 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
     for (int i = 0; i < 16; ++i) X[r][i] = 32 * r + 8 * (i >> 2) + (i & 3) == n0 - 4 * hg ? 1.f - vsc : 0.f;
 
   // chunk j + 1's K, V (Z only), T and gates are loaded into registers while
-  // chunk j is computed (every chunk of a composed group is full); scalar
-  // registers, not arrays, which the compiler would move to LDS.  Thread tid
+  // chunk j is computed; scalar registers, not arrays, which the compiler
+  // would move to LDS.  Thread tid
   // takes rows tid/16 + 16 it, columns 8 (tid % 16) of K and V (it = 0..3)
   // and the 16-byte pieces tid + 256 it of T's fragments (it = 0..2).
   uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
@@ -1384,26 +1427,27 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
 #define GD_CMP_FETCH(j_)                                                                                \
   {                                                                                                    \
     const int t0_ = seg0 + (gi * kGdGrpChunks + (j_)) * kGdC;                                           \
-    const float* tp_ = ck_t + (gd_ckpt_slot(seg0, b, gi * kGdGrpChunks + (j_)) * H + h) * kGdTFragFloats \
+    const int nr_ = BWD ? std::min(kGdC, seg0 + L - t0_) : kGdC;                                        \
+    const float* tp_ = ck_t + (gd_ckpt_slot(seg0, b, gi * kGdGrpChunks + (j_)) * H + h) * t_stride      \
                        + 4 * tid;                                                                       \
     const bf16* kp_ = k + ((size_t)(t0_ + frow) * Hk + hk) * kGdD + fcol;                               \
-    pk0 = *(const uint4*)kp_;                                                                           \
-    pk1 = *(const uint4*)(kp_ + (size_t)16 * Hk * kGdD);                                                \
-    pk2 = *(const uint4*)(kp_ + (size_t)32 * Hk * kGdD);                                                \
-    pk3 = *(const uint4*)(kp_ + (size_t)48 * Hk * kGdD);                                                \
+    pk0 = frow < nr_ ? *(const uint4*)kp_ : zero4();                                                    \
+    pk1 = frow + 16 < nr_ ? *(const uint4*)(kp_ + (size_t)16 * Hk * kGdD) : zero4();                    \
+    pk2 = frow + 32 < nr_ ? *(const uint4*)(kp_ + (size_t)32 * Hk * kGdD) : zero4();                    \
+    pk3 = frow + 48 < nr_ ? *(const uint4*)(kp_ + (size_t)48 * Hk * kGdD) : zero4();                    \
     const bf16* vp_ = v + ((size_t)(t0_ + frow) * H + h) * kGdD + fcol;                                 \
-    pv0 = *(const uint4*)vp_;                                                                           \
-    pv1 = *(const uint4*)(vp_ + (size_t)16 * H * kGdD);                                                 \
-    pv2 = *(const uint4*)(vp_ + (size_t)32 * H * kGdD);                                                 \
-    pv3 = *(const uint4*)(vp_ + (size_t)48 * H * kGdD);                                                 \
+    pv0 = frow < nr_ ? *(const uint4*)vp_ : zero4();                                                    \
+    pv1 = frow + 16 < nr_ ? *(const uint4*)(vp_ + (size_t)16 * H * kGdD) : zero4();                     \
+    pv2 = frow + 32 < nr_ ? *(const uint4*)(vp_ + (size_t)32 * H * kGdD) : zero4();                     \
+    pv3 = frow + 48 < nr_ ? *(const uint4*)(vp_ + (size_t)48 * H * kGdD) : zero4();                     \
     pt0 = *(const float4*)tp_;                                                                          \
     pt1 = *(const float4*)(tp_ + 4 * kGdThreads);                                                       \
     pt2 = *(const float4*)(tp_ + 8 * kGdThreads);                                                       \
-    pg = g[(size_t)(t0_ + lane) * H + h];                                                               \
-    pb = beta[(size_t)(t0_ + lane) * H + h];                                                            \
+    pg = lane < nr_ ? g[(size_t)(t0_ + lane) * H + h] : 0.f;                                            \
+    pb = lane < nr_ ? beta[(size_t)(t0_ + lane) * H + h] : 0.f;                                         \
   }
   GD_CMP_FETCH(0);
-  for (int j = 0; j < kGdGrpChunks; ++j) {
+  for (int j = 0; j < nch; ++j) {
     __syncthreads();                                   // the previous chunk's reads of LDS are done
     *(uint4*)&sm.k[frow][fcol] = pk0;
     *(uint4*)&sm.k[frow + 16][fcol] = pk1;
@@ -1429,7 +1473,7 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
       sm.dec[lane] = fast_exp2(last - x);
       sm.beta[lane] = pb;
     }
-    if (j + 1 < kGdGrpChunks) GD_CMP_FETCH(j + 1);
+    if (j + 1 < nch) GD_CMP_FETCH(j + 1);
     __syncthreads();
     // K^T as A fragments, once for the four waves (read after the next
     // barrier): element e of fragment (r, s, lane (fc, fh)) is
@@ -1541,7 +1585,11 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
 // B operand, passes through LDS, double-buffered so that one barrier a group
 // suffices.  C-layout element i of wave w's row block is B element i % 8 of
 // k-step 2w + i / 8, so each wave's accumulator goes to LDS as it stands.
+// REV (the backward's state-gradient walk): from the final-state gradient,
+// D_(g-1) = A_g^T D_g + F_g from the slice's last group back to its second,
+// stored as group g-1's end gradient; the A operand then takes A_g's columns.
 constexpr int kGdScanPitch = 20;     // floats per lane in the exchange: b128 accesses free of bank conflicts
+template <bool REV>
 __global__ void __launch_bounds__(kGdThreads, 1)
 gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, const float* __restrict__ h0,
                    const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS) {
@@ -1567,16 +1615,26 @@ gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, cons
 #pragma unroll
     for (int q = 0; q < 4; ++q) *(float4*)(x + 4 * q) = make_float4(S0[4 * q], S0[4 * q + 1], S0[4 * q + 2], S0[4 * q + 3]);
   }
-  // group gi's rows: A element e of lane (c, hg) at k-step s is
-  // A_g[32w + c][kpos(s, e, hg)], two float4 a k-step
-#define GD_SCAN_LOAD(gi_, ra_, rz_)                                                                       \
+  // step j takes group gi = j (forward) or n_grp - 1 - j (REV).  Its A
+  // operand: element e of lane (c, hg) at k-step s is A_g[32w + c][kpos(s, e,
+  // hg)] (two float4 a k-step), or for REV A_g[kpos(s, e, hg)][32w + c]
+#define GD_SCAN_LOAD(j_, ra_, rz_)                                                                        \
   {                                                                                                    \
-    const size_t sl_ = gd_grp_slot(seg0, b, (gi_));                                                     \
-    const float* pa_ = gA + (sl_ * H + h) * kGdD * kGdD + (size_t)(32 * w + c) * kGdD + 4 * hg;         \
+    const size_t sl_ = gd_grp_slot(seg0, b, REV ? n_grp - 1 - (j_) : (j_));                            \
     const float* pz_ = gZ + (sl_ * H + h) * kGdD * kGdD + (size_t)(32 * w) * kGdD + n0;                 \
-    _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) {                                                  \
-      ra_[2 * s_] = *(const float4*)(pa_ + 16 * s_);                                                    \
-      ra_[2 * s_ + 1] = *(const float4*)(pa_ + 16 * s_ + 8);                                            \
+    if constexpr (REV) {                                                                               \
+      const float* pa_ = gA + (sl_ * H + h) * kGdD * kGdD + (size_t)(4 * hg) * kGdD + 32 * w + c;       \
+      _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) {                                                \
+        const float* p_ = pa_ + (size_t)(16 * s_) * kGdD;                                               \
+        ra_[2 * s_] = make_float4(p_[0], p_[kGdD], p_[2 * kGdD], p_[3 * kGdD]);                          \
+        ra_[2 * s_ + 1] = make_float4(p_[8 * kGdD], p_[9 * kGdD], p_[10 * kGdD], p_[11 * kGdD]);         \
+      }                                                                                                 \
+    } else {                                                                                            \
+      const float* pa_ = gA + (sl_ * H + h) * kGdD * kGdD + (size_t)(32 * w + c) * kGdD + 4 * hg;       \
+      _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) {                                                \
+        ra_[2 * s_] = *(const float4*)(pa_ + 16 * s_);                                                  \
+        ra_[2 * s_ + 1] = *(const float4*)(pa_ + 16 * s_ + 8);                                          \
+      }                                                                                                 \
     }                                                                                                   \
     _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) rz_[i_] = pz_[(size_t)crow(i_, hg) * kGdD];        \
   }
@@ -1603,7 +1661,8 @@ gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, cons
       Sn = mfma32(ah, sl, Sn);
       Sn = mfma32(al, sh, Sn);
     }
-    float* ps = gS + ((gd_grp_slot(seg0, b, gi) + 1) * H + h) * kGdD * kGdD + (size_t)(32 * w) * kGdD + n0;
+    const size_t so = REV ? gd_grp_slot(seg0, b, n_grp - 2 - gi) : gd_grp_slot(seg0, b, gi) + 1;
+    float* ps = gS + (so * H + h) * kGdD * kGdD + (size_t)(32 * w) * kGdD + n0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ps[(size_t)crow(i, hg) * kGdD] = Sn[i];
     float* x = &xs[(gi + 1) & 1][w][lane][0];
@@ -1701,6 +1760,43 @@ gd_bwd_chains_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, con
   else
     gd_bwd_chain_body<GradT>(*reinterpret_cast<GdChainSmem*>(raw), s_bad, j, q, k, g, beta, cu, n_seg, T, H, Hk,
                              scale, dout, dht, ck_t, ck_ds, ck_dr, dv, dh0);
+}
+
+// The grouped chains (slices longer than one group).  Pass 1b: the offsets F_g
+// of the state-gradient walk, one workgroup per (group slot, value head) for
+// every group after a slice's first.
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_bwd_cgrp_compose_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+                           const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H,
+                           int Hk, float scale, const bf16* __restrict__ dout, const float* __restrict__ ck_t,
+                           float* __restrict__ gF) {
+  __shared__ GdChainSmem sm;
+  __shared__ int s_bad;
+  gd_bwd_chain_body<float, 1>(sm, s_bad, blockIdx.x, q, k, g, beta, cu, n_seg, T, H, Hk, scale, dout, nullptr, ck_t,
+                              nullptr, nullptr, (float*)nullptr, nullptr, gF, nullptr);
+}
+
+// Passes 1 and 2 on groups, side by side: block 2j is the state-gradient walk
+// of group slot x head j from its end gradient, block 2j + 1 the
+// recomputation of the same group from its starting state.
+template <typename GradT>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_bwd_grp_chains_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                         const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                         int n_seg, int T, int H, int Hk, float scale, const float* __restrict__ h0,
+                         int32_t* __restrict__ status, const float* __restrict__ ck_t, float* __restrict__ ck_s,
+                         float* __restrict__ ck_u, const bf16* __restrict__ dout, const float* __restrict__ dht,
+                         float* __restrict__ ck_ds, float* __restrict__ ck_dr, GradT* __restrict__ dv,
+                         float* __restrict__ dh0, const float* __restrict__ gS, const float* __restrict__ gD) {
+  __shared__ __align__(16) unsigned char raw[kGdChainsLds];
+  __shared__ int s_bad;
+  const int j = blockIdx.x >> 1;
+  if (blockIdx.x & 1)
+    gd_fwd_body<bf16, true, true>(*reinterpret_cast<GdSmem*>(raw), s_bad, j, q, k, v, g, beta, cu, n_seg, T, H, Hk,
+                                  scale, h0, (bf16*)nullptr, nullptr, status, ck_s, ck_u, ck_t, gS);
+  else
+    gd_bwd_chain_body<GradT, 2>(*reinterpret_cast<GdChainSmem*>(raw), s_bad, j, q, k, g, beta, cu, n_seg, T, H, Hk,
+                                scale, dout, dht, ck_t, ck_ds, ck_dr, dv, dh0, nullptr, gD);
 }
 
 struct GdChunkSmem {
@@ -2053,7 +2149,7 @@ gd_clear_kernel(float* __restrict__ a, float* __restrict__ b2, int64_t n, const 
 }
 
 struct GdBwdLayout {
-  size_t slots, ck_s, ck_u, ck_ds, ck_dr, ck_t, total;
+  size_t slots, ck_s, ck_u, ck_ds, ck_dr, ck_t, gslots, gA, gZ, gS, gF, gD, total;
 };
 GdBwdLayout gd_bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -2066,7 +2162,16 @@ GdBwdLayout gd_bwd_layout(int32_t T, int32_t H, int32_t n_seg) {
   l.ck_u = 2 * st;
   l.ck_dr = 2 * st + ch;
   l.ck_t = 2 * st + 2 * ch;
-  l.total = l.ck_t + up(l.slots * H * 2 * kGdTFragFloats * sizeof(float));
+  // per group slot and head: the map A_g, the state Z_g and starting state of
+  // the recomputation, the offset F_g and end gradient of the state-gradient walk
+  l.gslots = (size_t)T / kGdGrpTok + (size_t)n_seg + 1;
+  const size_t gs = up(l.gslots * H * kGdStateFloats * sizeof(float));
+  l.gA = l.ck_t + up(l.slots * H * 2 * kGdTFragFloats * sizeof(float));
+  l.gZ = l.gA + gs;
+  l.gS = l.gZ + gs;
+  l.gF = l.gS + gs;
+  l.gD = l.gF + gs;
+  l.total = l.gD + gs;
   return l;
 }
 
@@ -2097,8 +2202,8 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != kGdD) return PVB_E_UNSUPPORTED;
   const GdBwdLayout lay = gd_bwd_layout(T, H, n_seg);
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)2 * n_seg * H, kGdThreads) ||
-      !grid_fits((uint64_t)lay.slots * H, kGdChunkThreads))
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)4 * n_seg * H, kGdThreads) ||
+      !grid_fits((uint64_t)lay.slots * H, kGdChunkThreads) || !grid_fits((uint64_t)2 * lay.gslots * H, kGdThreads))
     return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
   const pvb_status hs = check_host_cu(h_cu, n_seg, T);
@@ -2123,15 +2228,49 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   // passes 1 and 2 side by side: the recomputation stores the chunk-start
   // states and the U of every chunk (it also validates cu_seqlens and writes
   // the status word); the state-gradient chain stores dS at every chunk's end
-  // and dR, and writes dV and dh0
-  if (grad_dtype == PVB_F32)
-    gd_bwd_chains_kernel<float><<<2 * grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-        d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
-  else
-    gd_bwd_chains_kernel<bf16><<<2 * grid, kGdThreads, 0, s>>>(
-        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
-        d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
+  // and dR, and writes dV and dh0.  A slice longer than one group of 1024
+  // tokens is walked in groups (whether one is, is known without the host
+  // mirror only on the device): the recomputation's group maps and starting
+  // states as in the grouped forward, the state-gradient walk's offsets, its
+  // group end gradients by the transposed maps, then both walks on every
+  // group at once.
+  bool multi = true;
+  if (h_cu != nullptr) {
+    multi = false;
+    for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
+  }
+  if (!multi) {
+    if (grad_dtype == PVB_F32)
+      gd_bwd_chains_kernel<float><<<2 * grid, kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+          d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0);
+    else
+      gd_bwd_chains_kernel<bf16><<<2 * grid, kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+          d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0);
+  } else {
+    float* gA = reinterpret_cast<float*>(ws + lay.gA);
+    float* gZ = reinterpret_cast<float*>(ws + lay.gZ);
+    float* gS = reinterpret_cast<float*>(ws + lay.gS);
+    float* gF = reinterpret_cast<float*>(ws + lay.gF);
+    float* gD = reinterpret_cast<float*>(ws + lay.gD);
+    const unsigned ggrid = (unsigned)(lay.gslots * H);
+    gd_grp_compose_kernel<true><<<2 * ggrid, kGdThreads, 0, s>>>(
+        (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ, (int)ggrid);
+    gd_bwd_cgrp_compose_kernel<<<ggrid, kGdThreads, 0, s>>>((const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu,
+                                                            n_seg, T, H, H_k, scale, (const bf16*)d_dout, ck_t, gF);
+    const unsigned sgrid = (unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H);
+    gd_grp_scan_kernel<false><<<sgrid, kGdThreads, 0, s>>>(d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
+    gd_grp_scan_kernel<true><<<sgrid, kGdThreads, 0, s>>>(d_cu, n_seg, T, H, d_dht, gA, gF, gD);
+    if (grad_dtype == PVB_F32)
+      gd_bwd_grp_chains_kernel<float><<<2 * ggrid, kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+          d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0, gS, gD);
+    else
+      gd_bwd_grp_chains_kernel<bf16><<<2 * ggrid, kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+          d_status, ck_t, ck_s, ck_u, (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0, gS, gD);
+  }
   // pass 3, chunk-parallel: dQ, dK, dg, dbeta
   gd_bwd_chunk_kernel<<<(unsigned)(lay.slots * H), kGdChunkThreads, 0, s>>>(
       (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
@@ -2194,10 +2333,10 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
   gd_tmat_kernel<false><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t,
                                                tl.per);
   if (multi) {
-    gd_grp_compose_kernel<<<(unsigned)(2 * lay.gslots * H), kGdThreads, 0, s>>>(
+    gd_grp_compose_kernel<false><<<(unsigned)(2 * lay.gslots * H), kGdThreads, 0, s>>>(
         (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ,
         (int)(lay.gslots * H));
-    gd_grp_scan_kernel<<<(unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H), kGdThreads, 0, s>>>(
+    gd_grp_scan_kernel<false><<<(unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H), kGdThreads, 0, s>>>(
         d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
   }
   if (o_dtype == PVB_F32)

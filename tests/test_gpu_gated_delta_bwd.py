@@ -42,7 +42,7 @@ def _check(name, got, ref, extra=0.0):
 
 
 def _case(seed, lengths, H, Hk=None, g_range=(-0.1, 0.0), beta_range=(0.05, 1.0), h0=False, dht=False,
-          grad_dtype="f32", scale=None):
+          grad_dtype="f32", scale=None, mirror=True):
     import torch
 
     import packed_varlen_block_amd as pvb
@@ -55,7 +55,8 @@ def _case(seed, lengths, H, Hk=None, g_range=(-0.1, 0.0), beta_range=(0.05, 1.0)
     hc = host_cu(lengths)
     gd = torch.float32 if grad_dtype == "f32" else torch.bfloat16
     dq, dk, dv, dg, db, dh0, st = pvb.gated_delta_bwd(
-        _dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]), _dev(w["beta"]), _dev(hc), _dev(do), h_cu=hc,
+        _dev(w["q"]), _dev(w["k"]), _dev(w["v"]), _dev(w["g"]), _dev(w["beta"]), _dev(hc), _dev(do),
+        h_cu=hc if mirror else None,
         scale=scale, initial_state=_dev(w["h0"]) if h0 else None, dht=_dev(dsf) if dht else None, grad_dtype=gd)
     pvb.check_status(st)
     f = W.bf16_bits_to_f64
@@ -97,6 +98,17 @@ def test_backward_bf16_dv_and_scale():
 def test_backward_long_slice_grouped():
     say("gated delta bwd: a 2100-token slice beside short ones, 4 value heads over 2, states")
     _case(504, [2100, 300, 0, 65], H=4, Hk=2, h0=True, dht=True)
+
+
+@pytest.mark.parametrize("with_mirror", [True, False])
+def test_backward_group_edges(with_mirror):
+    """Slices of exactly one group (1024 tokens), one token more, and 2.05
+    groups with a partial last chunk, beside an empty one: the walks in
+    groups of 1024 tokens (the recomputation's maps and the state-gradient
+    walk's offsets and transposed maps) against O12, with and without the
+    host mirror of cu_seqlens."""
+    say(f"gated delta bwd: group edges, host mirror {with_mirror}")
+    _case(508, [1024, 1025, 0, 2100], H=2, h0=True, dht=True, mirror=with_mirror)
 
 
 def test_backward_bad_cu_writes_nothing():
