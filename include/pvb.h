@@ -463,7 +463,9 @@ pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, const void*
  *   d_dh0          out fp32 [n_seg, H, d, d], nullable
  *   workspace      >= pvb_gated_delta_bwd_workspace_bytes(T, H, n_seg) bytes
  *                  (216 KB per 64-token chunk slot and head, T/64 + n_seg + 1
- *                  slots: about 3.9 GB at T = 32768, H = 32)           (device)
+ *                  slots, and 320 KB per 1024-token group slot and head,
+ *                  T/1024 + n_seg + 1 slots: about 4.5 GB at T = 32768,
+ *                  H = 32)                                              (device)
  * d = 128.  Device-detected error: PVB_E_BAD_CU_SEQLENS (then no gradient is
  * written). */
 size_t pvb_gated_delta_bwd_workspace_bytes(int32_t T, int32_t H, int32_t n_seg);
