@@ -184,7 +184,12 @@ def test_backward_random_draws(case):
     h0, dht = bool(r.random() < 0.5), bool(r.random() < 0.5)
     grad_dtype = "bf16" if r.random() < 0.3 else "f32"
     scale = None if r.random() < 0.6 else 0.3
+    # odd cases go without the host mirror (the walks in groups, on the device's
+    # decision); the last two add a slice longer than one group of 1024 tokens
+    mirror = case % 2 == 0
+    if case >= 10:
+        lengths.append(int(r.integers(1025, 2200)))
     say(f"gated delta bwd random {case}: lengths={lengths} H={H} H_k={Hk} g={g_range} beta={beta_range} "
-        f"h0={h0} dht={dht} dv={grad_dtype} scale={scale}")
+        f"h0={h0} dht={dht} dv={grad_dtype} scale={scale} mirror={mirror}")
     _case(6100 + case, lengths, H, Hk=Hk, g_range=g_range, beta_range=beta_range, h0=h0, dht=dht,
-          grad_dtype=grad_dtype, scale=scale)
+          grad_dtype=grad_dtype, scale=scale, mirror=mirror)
