@@ -164,11 +164,12 @@ def test_gated_delta_backward_graph_replays():
     """The gated delta backward recorded once into a HIP graph (its workspace
     allocated before the capture; value and query/key heads one to one, so no
     atomics and replays are bitwise repeatable) and replayed over two packs of
-    the same size; every replay equals an eager call bit for bit, and the
-    first two replays match O12."""
+    the same size, each with a slice longer than one group of 1024 tokens (so
+    the group maps, both walks and the group walks are recorded); every replay
+    equals an eager call bit for bit, and the first two replays match O12."""
     import packed_varlen_block_amd as pvb
     import torch
-    packs = [[130, 0, 64, 257], [257, 64, 0, 130]]
+    packs = [[1100, 0, 64, 257], [257, 64, 0, 1100]]
     H, d = 4, 128
     T = int(np.sum(packs[0]))
     sets = [W.random_gated_delta(2300 + i, p, H=H, initial_state=True) for i, p in enumerate(packs)]
