@@ -1860,18 +1860,13 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
     }
     if (w == 0) gd_gates(t, st.g, st.b, lane);
   }
-  // this wave's rows of V and its value columns of S0, in flight during the barrier
+  // this wave's rows of V in its value columns, in flight during the barrier
   float vc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int row = 32 * rb + crow(i, hg);
     vc[i] = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
   }
-  f32x16 S0c[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) S0c[r][i] = S0p[(size_t)(32 * r + crow(i, hg)) * kGdD + n0];
   __syncthreads();
 
   if (w < 6) {
@@ -1885,44 +1880,16 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       t.p[e >> 5][32 + (e & 31)] = 0.f;
     }
   }
-  // ---- K S0 and Q S0 (row block rb, value columns of quarter cq), then the
-  // row partials sum_c dR (V - G K S0) (dbeta) and -beta sum_c dR K S0 +
-  // scale sum_c dO Q S0 (dG)
+  // ---- the row partial sum_c dR V (dbeta) over this wave's value columns;
+  // the K S0 and Q S0 terms come later from dR S0^T and dO S0^T:
+  // sum_c dR (K S0) = sum_k K o (dR S0^T), sum_c dO (Q S0) = sum_k Q o (dO S0^T)
   {
-    f32x16 ks = {}, qs = {};
+    float xr[16];
 #pragma unroll
-    for (int s = 0; s < kGdD / 16; ++s) {
-      float sv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = S0c[s >> 1][8 * (s & 1) + e];
-      bf16x8 shi, slo;
-      split8(sv, shi, slo);
-      const bf16* kr = &t.k[32 * rb + c][16 * s + 4 * hg];
-      const bf16* qr = &t.q[32 * rb + c][16 * s + 4 * hg];
-      const bf16x8 ka = cat(*(const bf16x4*)kr, *(const bf16x4*)(kr + 8));
-      const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
-      ks = mfma32(ka, shi, ks);
-      ks = mfma32(ka, slo, ks);
-      qs = mfma32(qa, shi, qs);
-      qs = mfma32(qa, slo, qs);
-    }
-    float xr[16], gr[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * rb + crow(i, hg);
-      const float dr = sm.dr[row][n0];
-      const float dov = (float)t.dO[row][n0];
-      xr[i] = dr * (vc[i] - t.eg[row] * ks[i]);
-      gr[i] = -t.beta[row] * dr * ks[i] + scale * dov * qs[i];
-    }
+    for (int i = 0; i < 16; ++i) xr[i] = sm.dr[32 * rb + crow(i, hg)][n0] * vc[i];
     int idx;
     const float sx = row_sum16(xr, c, idx);
-    const float sg = row_sum16(gr, c, idx);
-    if ((c & 1) == 0) {
-      const int row = 32 * rb + crow(idx, hg);
-      sm.xr[cq][row] = sx;
-      sm.gr[cq][row] = sg;
-    }
+    if ((c & 1) == 0) sm.xr[cq][32 * rb + crow(idx, hg)] = sx;
   }
   __syncthreads();                                    // Ah and P are complete
 
@@ -1987,7 +1954,9 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
 
   // ---- row block rb, key dims of quarter cq: dR S0^T, U dS^T (= dKt) and
   // dO S0^T contracted over all value columns; <dS, S0> over these key dims
-  // (waves of row block 0); the row partials sum_d dKt o Kt
+  // (waves of row block 0); the row partials sum_d dKt o Kt, and over these
+  // key dims sum_d K o (dR S0^T) = sum_c dR (K S0) and
+  // sum_d Q o (dO S0^T) = sum_c dO (Q S0)
   f32x16 r1 = {}, kt1 = {}, q1 = {};
   {
     float sdot = 0.f;
@@ -2035,9 +2004,24 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       const int row = 32 * rb + crow(i, hg);
       x[i] = kt1[i] * t.dec[row] * (float)t.k[row][n0];
     }
+    float xb[16], xc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * rb + crow(i, hg);
+      xb[i] = (float)t.k[row][n0] * r1[i];
+      xc[i] = (float)t.q[row][n0] * q1[i];
+    }
     int idx;
     const float sx = row_sum16(x, c, idx);
-    if ((c & 1) == 0) sm.rk[cq][32 * rb + crow(idx, hg)] = sx;
+    const float sb = row_sum16(xb, c, idx);
+    const float sc = row_sum16(xc, c, idx);
+    if ((c & 1) == 0) {
+      const int row = 32 * rb + crow(idx, hg);
+      sm.rk[cq][row] = sx;
+      // this wave wrote sm.xr[cq][row] in the first phase (same lane, same row)
+      sm.xr[cq][row] -= t.eg[row] * sb;
+      sm.gr[cq][row] = -t.beta[row] * sb + scale * sc;
+    }
   }
   __syncthreads();                                    // M, N and every partial are complete
 
