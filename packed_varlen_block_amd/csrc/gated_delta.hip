@@ -17,14 +17,19 @@
 //   O = scale (diag(G) Q S0 + P U),               P_ij = (G_i/G_j) q_i.k_j       (j <= i),
 //   S_end = G_63 S0 + (diag(G_63/G) K)^T U.
 // The chunk products run on the matrix cores; every fp32 operand (the state,
-// P, U, the gated keys, A's off-diagonal block) is split into bf16 hi + lo
-// parts, so the products keep about 16 significant bits; the two 32-row
+// P, U, T = (I + A)^-1, A's off-diagonal block) is split into bf16 hi + lo
+// parts, so the products keep about 16 significant bits (the state update is
+// written K^T (diag(G_63/G) U), so that K^T stays exact); the two 32-row
 // triangles of the solve are fp32 on the vector unit.
 //
-// One workgroup of 4 waves per (slice, value head); the slices are
+// A chain is one workgroup of 4 waves per (slice, value head); the slices are
 // independent.  Value head h reads query/key head h / (H / H_k).  Wave w owns
 // value columns [32w, 32w + 32) of the state, which stays in its registers (C
-// layout of four 32x32 blocks) across the chunks of the slice.
+// layout of four 32x32 blocks) across the chunks.  Given a workspace, a slice
+// is cut into groups of 16 chunks: a chunk maps its starting state affinely,
+// so the groups' maps are composed in parallel, walked group by group, and
+// every group's chunks then run from their starting state (the forward, and
+// both walks of the backward, the state-gradient walk on the transposed maps).
 #include <type_traits>
 
 #include "pvb_device.hpp"
