@@ -711,7 +711,12 @@ def gated_delta_backward(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
     16384-token slice, then slices of 16-1024), H=32, d=128, fp32 gradients,
     dO ~ N(0,1) bf16 and a final-state gradient; inputs as in gated_delta.  One
     call recomputes the forward (storing chunk checkpoints) and walks the
-    chunks back; reported per chunk of the longest slice's chain, median of reps."""
+    chunks back; reported per chunk of the longest slice's chain, median of reps.
+    The training pair is timed beside it: the training forward, which leaves
+    the checkpoints in the backward's workspace, and the backward that reads
+    them (`train_forward_ms`, `after_forward_ms`), against the plain forward
+    (with its workspace) and backward, each pair run back to back
+    (`plain_pair_ms`, `train_pair_ms`)."""
     lengths = W.lengths_cfg4(seed)
     T, B = int(lengths.sum()), len(lengths)
     g = torch.Generator(device=dev).manual_seed(seed + 13)
@@ -728,24 +733,50 @@ def gated_delta_backward(torch, pvb, W, dev, stream, seed, H=32, d=128, reps=5):
     hc = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     cu = torch.from_numpy(hc).to(dev)
     ws = torch.empty(pvb.gated_delta_bwd_workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(pvb.gated_delta_fwd_workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(2):
+
+    def plain_fwd():
+        pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, workspace=wsf, status=st)
+
+    def plain_bwd():
         pvb.gated_delta_bwd(q, k, v, gg, bb, cu, do, dht=dht, workspace=ws, status=st)
-    torch.cuda.synchronize()
-    ev = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        pvb.gated_delta_bwd(q, k, v, gg, bb, cu, do, dht=dht, workspace=ws, status=st)
-        e1.record(stream)
-        ev.append((e0, e1))
-    torch.cuda.synchronize()
-    pvb.check_status(st)
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    def train_fwd():
+        pvb.gated_delta_fwd(q, k, v, gg, bb, cu, out=o, state_out=ht, workspace=ws, train=True, status=st)
+
+    def after_fwd():
+        pvb.gated_delta_bwd(q, k, v, gg, bb, cu, do, dht=dht, workspace=ws, after_fwd=True, status=st)
+
+    def timed(*fns):
+        for _ in range(2):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for fn in fns:
+                fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        pvb.check_status(st)
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ms = timed(plain_bwd)
+    plain_pair = timed(plain_fwd, plain_bwd)
+    train_pair = timed(train_fwd, after_fwd)
+    train_f = timed(train_fwd)
+    after_b = timed(after_fwd)              # the workspace holds the last training forward's checkpoints
     chain = int(-(-int(lengths.max()) // 64))
     return {"workload": "gdn_bwd_long_mixed_T32768_H32_d128", "segments": B, "ms": round(ms, 4),
             "longest_chain_chunks": chain, "us_per_chunk": round(ms * 1e3 / chain, 3),
-            "workspace_bytes": int(ws.numel())}
+            "workspace_bytes": int(ws.numel()), "train_forward_ms": round(train_f, 4),
+            "after_forward_ms": round(after_b, 4), "plain_pair_ms": round(plain_pair, 4),
+            "train_pair_ms": round(train_pair, 4)}
 
 
 def packed_loss(torch, pvb, dev, stream, seed, C=8192, V=32768, reps=20):

@@ -477,6 +477,37 @@ pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, const void* d_v
                                int32_t grad_dtype, void* workspace, size_t workspace_bytes,
                                int32_t* d_status, void* stream);
 
+/* Training pair: the forward of pvb_gated_delta_fwd_gqa (same arguments and
+ * the same O and ht up to rounding; "Packing与 FlashAttention Varlen",
+ * section 6, as above) that
+ * also leaves in the backward's workspace what pvb_gated_delta_bwd recomputes
+ * (T and T^T of every chunk, every chunk's starting state and solved update,
+ * the 1024-token groups' maps), and the backward that reads them instead.
+ *   workspace      >= pvb_gated_delta_bwd_workspace_bytes(T, H, n_seg) bytes
+ *                  (device), written by pvb_gated_delta_fwd_train
+ * pvb_gated_delta_bwd_after_fwd takes pvb_gated_delta_bwd's arguments; its
+ * workspace must hold what pvb_gated_delta_fwd_train left for the same q, k,
+ * v, g, beta, cu_seqlens, H, H_k and h0, untouched since (the call does not
+ * check this: other contents give wrong gradients, never an out-of-bounds
+ * access, as every index comes from cu_seqlens).  The forward always uses the
+ * grouped evaluation; the results equal pvb_gated_delta_fwd_gqa's with a
+ * workspace and pvb_gated_delta_bwd's up to rounding.  Errors as those two
+ * calls, with PVB_E_WORKSPACE for a workspace under the backward's size. */
+pvb_status pvb_gated_delta_fwd_train(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                     const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                                     int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d,
+                                     float scale, const float* d_h0, void* d_o, int32_t o_dtype,
+                                     float* d_ht, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                     void* stream);
+pvb_status pvb_gated_delta_bwd_after_fwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                         const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                                         int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d,
+                                         float scale, const float* d_h0, const void* d_dout,
+                                         const float* d_dht, float* d_dq, float* d_dk, void* d_dv,
+                                         float* d_dg, float* d_dbeta, float* d_dh0, int32_t grad_dtype,
+                                         void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                         void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* pvb_status_string(int32_t status);
 

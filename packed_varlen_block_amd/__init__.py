@@ -38,7 +38,8 @@ EXPORTS = ("pvb_pack_plan_nextfit", "pvb_pack_plan_bfd", "pvb_build_packed_row",
            "pvb_packed_nll", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
            "pvb_varlen_cross_attn_workspace_bytes", "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd",
            "pvb_gated_delta_fwd", "pvb_gated_delta_fwd_gqa", "pvb_gated_delta_fwd_workspace_bytes",
-           "pvb_gated_delta_bwd", "pvb_gated_delta_bwd_workspace_bytes",
+           "pvb_gated_delta_bwd", "pvb_gated_delta_bwd_workspace_bytes", "pvb_gated_delta_fwd_train",
+           "pvb_gated_delta_bwd_after_fwd",
            "pvb_varlen_attn_workspace_bytes", "pvb_varlen_attn_fwd", "pvb_varlen_attn_bwd",
            "pvb_varlen_attn_bwd_noalloc", "pvb_status_string", "pvb_version")
 PVB_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of pvb_varlen_attn_bwd_noalloc
@@ -79,11 +80,13 @@ def lib() -> ctypes.CDLL:
                                                   P, P, P, I32, I32, P, P]
         L.pvb_gated_delta_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, P, P, P, P, P,
                                           P, P, I32, P, SZ, P, P]
+        L.pvb_gated_delta_bwd_after_fwd.argtypes = L.pvb_gated_delta_bwd.argtypes
         L.pvb_gated_delta_bwd_workspace_bytes.argtypes = [I32, I32, I32]
         L.pvb_gated_delta_bwd_workspace_bytes.restype = SZ
         L.pvb_gated_delta_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F, P, P, I32, P, P, SZ, P, P]
         L.pvb_gated_delta_fwd_gqa.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, P, I32, P, P, SZ,
                                               P, P]
+        L.pvb_gated_delta_fwd_train.argtypes = L.pvb_gated_delta_fwd_gqa.argtypes
         L.pvb_gated_delta_fwd_workspace_bytes.argtypes = [I32, I32, I32]
         L.pvb_gated_delta_fwd_workspace_bytes.restype = SZ
         L.pvb_varlen_cross_attn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
@@ -97,7 +100,7 @@ def lib() -> ctypes.CDLL:
                      "pvb_varlen_attn_bwd", "pvb_varlen_attn_fwd_gqa", "pvb_varlen_attn_bwd_gqa",
                      "pvb_varlen_attn_bwd_noalloc",
                      "pvb_varlen_cross_attn_fwd", "pvb_varlen_cross_attn_bwd", "pvb_gated_delta_fwd",
-                     "pvb_gated_delta_bwd",
+                     "pvb_gated_delta_bwd", "pvb_gated_delta_bwd_after_fwd", "pvb_gated_delta_fwd_train",
                      "pvb_gated_delta_fwd_gqa"):
             getattr(L, name).restype = ctypes.c_int
         L.pvb_status_string.argtypes = [I32]
@@ -607,13 +610,17 @@ def gated_delta_fwd_workspace_bytes(T: int, H: int, n_seg: int) -> int:
 
 
 def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=None, final_state=True,
-                    o_dtype=None, out=None, state_out=None, workspace=None, chain=False, status=None):
+                    o_dtype=None, out=None, state_out=None, workspace=None, chain=False, status=None,
+                    train=False):
     """Gated delta rule over the packed stream, the state reset at every
     boundary of ``cu``.  q, k: contiguous bf16 CUDA [T, H_k, 128]; v: [T, H, 128]
     with H a multiple of H_k (value head h reads query/key head h // (H / H_k));
     g, beta: fp32 [T, H]; initial_state: optional fp32 [B, H, 128, 128].  The
     grouped evaluation takes a workspace (allocated when not given); chain=True
-    walks each slice's chunks in one chain without one.
+    walks each slice's chunks in one chain without one.  train=True runs the
+    training forward: the workspace is the backward's
+    (gated_delta_bwd_workspace_bytes) and is left holding what
+    gated_delta_bwd(..., after_fwd=True) reads.
     Returns (O [T, H, 128], final states [B, H, 128, 128] fp32 or None, status)."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, dim=3)
@@ -648,15 +655,18 @@ def gated_delta_fwd(q, k, v, g, beta, cu, h_cu=None, scale=None, initial_state=N
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
         if hc.size != n_seg + 1:
             raise PvbError(1, "h_cu must have B+1 entries")
+    if train and (chain or workspace is None):
+        raise PvbError(1, "the training forward takes the grouped evaluation and the backward's workspace")
     if chain:
         wp, wb = None, 0
     else:
-        workspace = _workspace_arg(workspace, gated_delta_fwd_workspace_bytes(T, H, n_seg), dev)
+        nbytes = (gated_delta_bwd_workspace_bytes if train else gated_delta_fwd_workspace_bytes)(T, H, n_seg)
+        workspace = _workspace_arg(workspace, nbytes, dev)
         wp, wb = _ptr(workspace), workspace.numel() * workspace.element_size()
-    rc = lib().pvb_gated_delta_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg,
-                                       T, H, Hk, d, scale, _ptr(initial_state), _ptr(out), _dtype_code(out.dtype),
-                                       _ptr(ht) if ht is not None and ht.numel() > 0 else None, wp, wb,
-                                       _ptr(status), _stream(dev))
+    fn = lib().pvb_gated_delta_fwd_train if train else lib().pvb_gated_delta_fwd_gqa
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg, T, H, Hk, d, scale,
+            _ptr(initial_state), _ptr(out), _dtype_code(out.dtype),
+            _ptr(ht) if ht is not None and ht.numel() > 0 else None, wp, wb, _ptr(status), _stream(dev))
     _check(rc, "gated_delta_fwd")
     return out, ht, status
 
@@ -666,9 +676,11 @@ def gated_delta_bwd_workspace_bytes(T: int, H: int, n_seg: int) -> int:
 
 
 def gated_delta_bwd(q, k, v, g, beta, cu, do, h_cu=None, scale=None, initial_state=None, dht=None,
-                    grad_dtype=None, dh0=True, workspace=None, status=None):
+                    grad_dtype=None, dh0=True, workspace=None, status=None, after_fwd=False):
     """Backward of gated_delta_fwd: the gradients of sum(O * do) + sum(ht * dht)
-    (dht: gradient of the final states, optional).  Returns (dq, dk [T, H_k, 128]
+    (dht: gradient of the final states, optional).  after_fwd=True: the
+    workspace holds what gated_delta_fwd(..., train=True) left for the same
+    inputs, and the recomputation is skipped.  Returns (dq, dk [T, H_k, 128]
     fp32, dv [T, H, 128] in grad_dtype (fp32 by default), dg, dbeta [T, H] fp32,
     dh0 [B, H, 128, 128] fp32 or None, status)."""
     torch = _torch()
@@ -699,6 +711,8 @@ def gated_delta_bwd(q, k, v, g, beta, cu, do, h_cu=None, scale=None, initial_sta
     db = torch.empty((T, H), dtype=torch.float32, device=dev)
     dh = torch.empty((max(n_seg, 0), H, d, d), dtype=torch.float32, device=dev) if dh0 else None
     nbytes = gated_delta_bwd_workspace_bytes(T, H, n_seg)
+    if after_fwd and workspace is None:
+        raise PvbError(5, "gated_delta_bwd(after_fwd=True) needs the training forward's workspace")
     workspace = _workspace_arg(workspace, nbytes, dev)
     status = _status_arg(status, dev)
     hc = None
@@ -706,10 +720,10 @@ def gated_delta_bwd(q, k, v, g, beta, cu, do, h_cu=None, scale=None, initial_sta
         hc = np.ascontiguousarray(np.asarray(h_cu, dtype=np.int32))
         if hc.size != n_seg + 1:
             raise PvbError(1, "h_cu must have B+1 entries")
-    rc = lib().pvb_gated_delta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg, T, H,
-                                   Hk, d, scale, _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
-                                   _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh) if dh is not None and dh.numel() else None,
-                                   gcode, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                   _ptr(status), _stream(dev))
+    fn = lib().pvb_gated_delta_bwd_after_fwd if after_fwd else lib().pvb_gated_delta_bwd
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(hc), n_seg, T, H, Hk, d, scale,
+            _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
+            _ptr(dh) if dh is not None and dh.numel() else None, gcode, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(status), _stream(dev))
     _check(rc, "gated_delta_bwd")
     return dq, dk, dv, dg, db, dh, status

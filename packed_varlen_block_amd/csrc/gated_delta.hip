@@ -101,7 +101,7 @@ __device__ __forceinline__ int crow(int i, int hg) { return 8 * (i >> 2) + 4 * h
 // state it stores, for every chunk, the state at the chunk's start and the
 // chunk's U (the solved right-hand side) in checkpoint slots (see
 // gd_ckpt_slot); the products that only feed O are skipped.
-template <typename OutT, bool CKPT, bool GROUPED = false>
+template <typename OutT, bool CKPT, bool GROUPED = false, bool TRAIN = false>
 __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k, const bf16* __restrict__ v,
                                             const float* __restrict__ g, const float* __restrict__ beta,
@@ -110,7 +110,11 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
                                             int32_t* __restrict__ status, float* __restrict__ ck_s,
                                             float* __restrict__ ck_u, const float* __restrict__ ck_t,
                                             const float* __restrict__ gstate = nullptr) {
-  constexpr bool USE_T = CKPT || GROUPED;            // the solve as U = T rhs, T from pass 0
+  // CKPT: checkpoints only (the backward's recomputation); TRAIN: the forward
+  // with O and the final states that also leaves the backward's checkpoints
+  constexpr bool STORE = CKPT || TRAIN;               // chunk-start states and U into ck_s, ck_u
+  constexpr bool WITH_O = !CKPT;
+  constexpr bool USE_T = STORE || GROUPED;            // the solve as U = T rhs, T from pass 0
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
 
@@ -174,7 +178,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   // 16-byte pieces a thread); the backward's slots also hold T^T's after them
   float4 pt0, pt1, pt2;
   float pg = 0.f, pb = 0.f;
-  constexpr size_t kTStride = (CKPT ? 2 : 1) * kGdTFragFloats;
+  constexpr size_t kTStride = (STORE ? 2 : 1) * kGdTFragFloats;
   auto fetch = [&](int cc0) {
     const int nvv = min(kGdC, L - cc0);
     if constexpr (USE_T) {
@@ -208,12 +212,16 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
   for (int c0 = cbeg; c0 < cend; c0 += kGdC) {
     const int nv = min(kGdC, L - c0);
     const size_t slot = gd_ckpt_slot(seg0, b, c0 / kGdC);
-    if constexpr (CKPT) {
-      float* cs = ck_s + (slot * H + h) * kGdD * kGdD;
+    if constexpr (STORE) {
+      // the lane's offset is made opaque here, so that the 64 store addresses
+      // are formed at the stores rather than kept live across the loop
+      int lo = 4 * hg * kGdD + n0;
+      asm volatile("" : "+v"(lo));
+      float* cs = ck_s + (slot * H + h) * kGdD * kGdD + lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) cs[(size_t)(32 * r + crow(i, hg)) * kGdD + n0] = S[r][i];
+        for (int i = 0; i < 16; ++i) cs[(size_t)(32 * r + 8 * (i >> 2) + (i & 3)) * kGdD] = S[r][i];
     }
     __syncthreads();                                  // the previous chunk's reads are done
 
@@ -285,7 +293,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
     };
     using KK = std::integral_constant<bool, false>;
     using QK = std::integral_constant<bool, true>;
-    if constexpr (CKPT) {
+    if constexpr (!WITH_O) {
       // P only feeds O, and the solve takes T from the workspace
     } else if constexpr (USE_T) {                     // P only: the solve takes T from the workspace
       if (w == 0) block(QK{}, 0, 0);
@@ -330,7 +338,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
         const bf16x8 qa = cat(*(const bf16x4*)qr, *(const bf16x4*)(qr + 8));
         ks[rb] = mfma32(ka, shi, ks[rb]);
         ks[rb] = mfma32(ka, slo, ks[rb]);
-        if constexpr (!CKPT) {
+        if constexpr (WITH_O) {
           oacc[rb] = mfma32(qa, shi, oacc[rb]);
           oacc[rb] = mfma32(qa, slo, oacc[rb]);
         }
@@ -352,7 +360,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
 
     // ---- P as split A fragments, once for the four waves (read after the
     // next barrier): fragment f = (rb, s, lane), rb = 0 with s < 2 only
-    for (int f = tid; f < (CKPT ? 0 : 6 * 64); f += kGdThreads) {
+    for (int f = tid; f < (WITH_O ? 6 * 64 : 0); f += kGdThreads) {
       const int fi = f >> 6, fl = f & 63, fc = fl & 31, fh = fl >> 5;
       const int rb = fi < 2 ? 0 : 1, s = fi < 2 ? fi : fi - 2;
       const float* src = &sm.p[32 * rb + fc][16 * s + 4 * fh];
@@ -435,7 +443,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       }
       ks[0] = uu[0];
       ks[1] = uu[1];
-      if constexpr (!CKPT) {
+      if constexpr (WITH_O) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) split_u(s);
       }
@@ -458,13 +466,15 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
       split_u(2);
       split_u(3);
     }
-    if constexpr (CKPT) {
-      float* cuu = ck_u + (slot * H + h) * kGdC * kGdD;
+    if constexpr (STORE) {
+      int lo = 4 * hg * kGdD + n0;                    // opaque, as for the state
+      asm volatile("" : "+v"(lo));
+      float* cuu = ck_u + (slot * H + h) * kGdC * kGdD + lo;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          cuu[(size_t)(32 * rb + crow(i, hg)) * kGdD + n0] = ks[rb][i];   // zero past the end
+          cuu[(size_t)(32 * rb + 8 * (i >> 2) + (i & 3)) * kGdD] = ks[rb][i];   // zero past the end
         }
     }
     __syncthreads();                                  // the P and key fragments are complete
@@ -473,7 +483,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
     // and S = G_63 S0 + (diag(G_63 / G) K)^T U: the matrix-core work of both
     // is issued first, then O is staged in the Q/K tiles (free by now) and
     // written with 16-byte stores.
-    if constexpr (!CKPT) {
+    if constexpr (WITH_O) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -511,7 +521,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
         S[r] = mfma32(ka, dl[s], S[r]);
       }
     }
-    if constexpr (CKPT) continue;                     // no O in the recomputation pass
+    if constexpr (!WITH_O) continue;                  // no O in the recomputation pass
     OutT* stg = reinterpret_cast<OutT*>(&sm.q[0][0]) + w * (kGdC * 32);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -531,7 +541,7 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
     }
   }
 
-  if (!CKPT && ht && cend == L) {
+  if (WITH_O && ht && cend == L) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -1804,6 +1814,43 @@ gd_bwd_grp_chains_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                 scale, dout, dht, ck_t, ck_ds, ck_dr, dv, dh0, nullptr, gD);
 }
 
+// The training forward's group pass: O and the final states as the grouped
+// forward, plus the backward's checkpoints (every chunk's starting state and
+// U), with T's fragments in the backward's slots.
+template <typename OutT>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_fwd_train_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                    int n_seg, int T, int H, int Hk, float scale, const float* __restrict__ h0,
+                    OutT* __restrict__ o, float* __restrict__ ht, int32_t* __restrict__ status,
+                    const float* __restrict__ ck_t, float* __restrict__ ck_s, float* __restrict__ ck_u,
+                    const float* __restrict__ gS) {
+  __shared__ GdSmem sm;
+  __shared__ int s_bad;
+  gd_fwd_body<OutT, false, true, true>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o,
+                                       ht, status, ck_s, ck_u, ck_t, gS);
+}
+
+// The backward after a training forward: the state-gradient walk alone on
+// every group (the recomputation's checkpoints are in the workspace); it
+// validates cu_seqlens and writes the status word.
+template <typename GradT>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_bwd_cwalk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+                    const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk,
+                    float scale, int32_t* __restrict__ status, const float* __restrict__ ck_t,
+                    const bf16* __restrict__ dout, const float* __restrict__ dht, float* __restrict__ ck_ds,
+                    float* __restrict__ ck_dr, GradT* __restrict__ dv, float* __restrict__ dh0,
+                    const float* __restrict__ gD) {
+  __shared__ GdChainSmem sm;
+  __shared__ int s_bad;
+  const bool bad = gd_cu_bad(cu, n_seg, T, &s_bad);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = bad ? PVB_E_BAD_CU_SEQLENS : PVB_OK;
+  if (bad) return;
+  gd_bwd_chain_body<GradT, 2>(sm, s_bad, blockIdx.x, q, k, g, beta, cu, n_seg, T, H, Hk, scale, dout, dht, ck_t,
+                              ck_ds, ck_dr, dv, dh0, nullptr, gD);
+}
+
 struct GdChunkSmem {
   GdTiles t;                         // Ah and P become M and N in place
   alignas(16) float u[kGdC][kUP];    // U
@@ -2172,14 +2219,16 @@ extern "C" size_t pvb_gated_delta_bwd_workspace_bytes(int32_t T, int32_t H, int3
   return pvb::gd_bwd_layout(T, H, n_seg).total;
 }
 
-extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
-                                          const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
-                                          int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d, float scale,
-                                          const float* d_h0, const void* d_dout, const float* d_dht, float* d_dq,
-                                          float* d_dk, void* d_dv, float* d_dg, float* d_dbeta, float* d_dh0,
-                                          int32_t grad_dtype, void* workspace, size_t workspace_bytes,
-                                          int32_t* d_status, void* stream) {
-  using namespace pvb;
+namespace pvb {
+namespace {
+// after_fwd: the workspace holds pvb_gated_delta_fwd_train's checkpoints for
+// the same inputs, so T's pass and the recomputation are skipped.
+pvb_status gated_delta_bwd_call(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                const float* d_beta, const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                int32_t T, int32_t H, int32_t H_k, int32_t d, float scale, const float* d_h0,
+                                const void* d_dout, const float* d_dht, float* d_dq, float* d_dk, void* d_dv,
+                                float* d_dg, float* d_dbeta, float* d_dh0, int32_t grad_dtype, void* workspace,
+                                size_t workspace_bytes, int32_t* d_status, void* stream, bool after_fwd) {
   if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
   if (H_k <= 0 || H % H_k != 0) return PVB_E_INVALID_ARG;
   if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
@@ -2212,8 +2261,11 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
   }
   const unsigned grid = (unsigned)std::max<int64_t>(1, (int64_t)n_seg * H);
   // pass 0: T = (I + A)^-1 of every chunk
-  const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
-  gd_tmat_kernel<true><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
+  if (!after_fwd) {
+    const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
+    gd_tmat_kernel<true><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t,
+                                                tl.per);
+  }
   // passes 1 and 2 side by side: the recomputation stores the chunk-start
   // states and the U of every chunk (it also validates cu_seqlens and writes
   // the status word); the state-gradient chain stores dS at every chunk's end
@@ -2228,7 +2280,29 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
     multi = false;
     for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
   }
-  if (!multi) {
+  if (after_fwd) {
+    // the state-gradient walk alone, in groups: the recomputation's group maps
+    // are in the workspace
+    float* gA = reinterpret_cast<float*>(ws + lay.gA);
+    float* gF = reinterpret_cast<float*>(ws + lay.gF);
+    float* gD = reinterpret_cast<float*>(ws + lay.gD);
+    const unsigned ggrid = (unsigned)(lay.gslots * H);
+    if (multi) {
+      gd_bwd_cgrp_compose_kernel<<<ggrid, kGdThreads, 0, s>>>((const bf16*)d_q, (const bf16*)d_k, d_g, d_beta,
+                                                              d_cu, n_seg, T, H, H_k, scale, (const bf16*)d_dout,
+                                                              ck_t, gF);
+      const unsigned sgrid = (unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H);
+      gd_grp_scan_kernel<true><<<sgrid, kGdThreads, 0, s>>>(d_cu, n_seg, T, H, d_dht, gA, gF, gD);
+    }
+    if (grad_dtype == PVB_F32)
+      gd_bwd_cwalk_kernel<float><<<std::max(1u, ggrid), kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_status, ck_t,
+          (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (float*)d_dv, d_dh0, gD);
+    else
+      gd_bwd_cwalk_kernel<bf16><<<std::max(1u, ggrid), kGdThreads, 0, s>>>(
+          (const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_status, ck_t,
+          (const bf16*)d_dout, d_dht, ck_ds, ck_dr, (bf16*)d_dv, d_dh0, gD);
+  } else if (!multi) {
     if (grad_dtype == PVB_F32)
       gd_bwd_chains_kernel<float><<<2 * grid, kGdThreads, 0, s>>>(
           (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
@@ -2265,6 +2339,33 @@ extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, cons
       (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale,
       (const bf16*)d_dout, ck_s, ck_u, ck_ds, ck_dr, d_dq, d_dk, d_dg, d_dbeta, atomic_qk);
   return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
+}  // namespace
+}  // namespace pvb
+
+extern "C" pvb_status pvb_gated_delta_bwd(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                          const float* d_beta, const int32_t* d_cu, const int32_t* h_cu,
+                                          int32_t n_seg, int32_t T, int32_t H, int32_t H_k, int32_t d, float scale,
+                                          const float* d_h0, const void* d_dout, const float* d_dht, float* d_dq,
+                                          float* d_dk, void* d_dv, float* d_dg, float* d_dbeta, float* d_dh0,
+                                          int32_t grad_dtype, void* workspace, size_t workspace_bytes,
+                                          int32_t* d_status, void* stream) {
+  return pvb::gated_delta_bwd_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_dout,
+                                   d_dht, d_dq, d_dk, d_dv, d_dg, d_dbeta, d_dh0, grad_dtype, workspace,
+                                   workspace_bytes, d_status, stream, false);
+}
+
+extern "C" pvb_status pvb_gated_delta_bwd_after_fwd(const void* d_q, const void* d_k, const void* d_v,
+                                                    const float* d_g, const float* d_beta, const int32_t* d_cu,
+                                                    const int32_t* h_cu, int32_t n_seg, int32_t T, int32_t H,
+                                                    int32_t H_k, int32_t d, float scale, const float* d_h0,
+                                                    const void* d_dout, const float* d_dht, float* d_dq, float* d_dk,
+                                                    void* d_dv, float* d_dg, float* d_dbeta, float* d_dh0,
+                                                    int32_t grad_dtype, void* workspace, size_t workspace_bytes,
+                                                    int32_t* d_status, void* stream) {
+  return pvb::gated_delta_bwd_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_dout,
+                                   d_dht, d_dq, d_dk, d_dv, d_dg, d_dbeta, d_dh0, grad_dtype, workspace,
+                                   workspace_bytes, d_status, stream, true);
 }
 
 namespace pvb {
@@ -2338,6 +2439,65 @@ pvb_status gated_delta_call(const void* d_q, const void* d_k, const void* d_v, c
         (bf16*)d_o, d_ht, d_status, ck_t, gS);
   return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
 }
+
+// The training forward: the grouped forward on the backward's workspace, which
+// it leaves holding T and T^T of every chunk, every chunk's starting state and
+// U, and the group maps, so that the backward can skip their recomputation.
+pvb_status gated_delta_train_call(const void* d_q, const void* d_k, const void* d_v, const float* d_g,
+                                  const float* d_beta, const int32_t* d_cu, const int32_t* h_cu, int32_t n_seg,
+                                  int32_t T, int32_t H, int32_t H_k, int32_t d, float scale, const float* d_h0,
+                                  void* d_o, int32_t o_dtype, float* d_ht, void* workspace, size_t workspace_bytes,
+                                  int32_t* d_status, void* stream) {
+  if (n_seg < 0 || T < 0 || H <= 0 || d_cu == nullptr || d_status == nullptr) return PVB_E_INVALID_ARG;
+  if (H_k <= 0 || H % H_k != 0) return PVB_E_INVALID_ARG;
+  if (n_seg > PVB_MAX_COUNT) return PVB_E_OVERFLOW;
+  if (T > 0 && (d_q == nullptr || d_k == nullptr || d_v == nullptr || d_g == nullptr || d_beta == nullptr ||
+                d_o == nullptr))
+    return PVB_E_INVALID_ARG;
+  if (o_dtype != PVB_BF16 && o_dtype != PVB_F32) return PVB_E_INVALID_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
+  if (d != kGdD) return PVB_E_UNSUPPORTED;
+  const GdBwdLayout lay = gd_bwd_layout(T, H, n_seg);
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)4 * n_seg * H, kGdThreads) ||
+      !grid_fits((uint64_t)lay.slots * H, kGdChunkThreads) || !grid_fits((uint64_t)2 * lay.gslots * H, kGdThreads))
+    return PVB_E_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
+  const pvb_status hs = check_host_cu(h_cu, n_seg, T);
+  if (hs != PVB_OK) return hs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* ck_s = reinterpret_cast<float*>(ws + lay.ck_s);
+  float* ck_u = reinterpret_cast<float*>(ws + lay.ck_u);
+  float* ck_t = reinterpret_cast<float*>(ws + lay.ck_t);
+  float* gA = reinterpret_cast<float*>(ws + lay.gA);
+  float* gZ = reinterpret_cast<float*>(ws + lay.gZ);
+  float* gS = reinterpret_cast<float*>(ws + lay.gS);
+  bool multi = true;
+  if (h_cu != nullptr) {
+    multi = false;
+    for (int32_t b = 0; b < n_seg && !multi; ++b) multi = h_cu[b + 1] - h_cu[b] > kGdGrpTok;
+  }
+  const GdTmatLaunch tl = gd_tmat_launch(lay.slots, H);
+  gd_tmat_kernel<true><<<tl.grid, 64, 0, s>>>((const bf16*)d_k, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, tl.per);
+  const unsigned ggrid = (unsigned)std::max<size_t>(1, lay.gslots * H);
+  if (multi) {
+    // the maps of every group, the last's too (the backward's transposed scan
+    // reads them all)
+    gd_grp_compose_kernel<true><<<2 * ggrid, kGdThreads, 0, s>>>(
+        (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, ck_t, gA, gZ, (int)ggrid);
+    gd_grp_scan_kernel<false><<<(unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H), kGdThreads, 0, s>>>(
+        d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
+  }
+  if (o_dtype == PVB_F32)
+    gd_fwd_train_kernel<float><<<ggrid, kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+        (float*)d_o, d_ht, d_status, ck_t, ck_s, ck_u, gS);
+  else
+    gd_fwd_train_kernel<bf16><<<ggrid, kGdThreads, 0, s>>>(
+        (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,
+        (bf16*)d_o, d_ht, d_status, ck_t, ck_s, ck_u, gS);
+  return hipGetLastError() == hipSuccess ? PVB_OK : PVB_E_HIP;
+}
 }  // namespace
 }  // namespace pvb
 
@@ -2364,4 +2524,14 @@ extern "C" pvb_status pvb_gated_delta_fwd_gqa(const void* d_q, const void* d_k, 
                                               size_t workspace_bytes, int32_t* d_status, void* stream) {
   return pvb::gated_delta_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_o,
                                o_dtype, d_ht, workspace, workspace_bytes, d_status, stream);
+}
+
+extern "C" pvb_status pvb_gated_delta_fwd_train(const void* d_q, const void* d_k, const void* d_v,
+                                                const float* d_g, const float* d_beta, const int32_t* d_cu,
+                                                const int32_t* h_cu, int32_t n_seg, int32_t T, int32_t H,
+                                                int32_t H_k, int32_t d, float scale, const float* d_h0, void* d_o,
+                                                int32_t o_dtype, float* d_ht, void* workspace,
+                                                size_t workspace_bytes, int32_t* d_status, void* stream) {
+  return pvb::gated_delta_train_call(d_q, d_k, d_v, d_g, d_beta, d_cu, h_cu, n_seg, T, H, H_k, d, scale, d_h0, d_o,
+                                     o_dtype, d_ht, workspace, workspace_bytes, d_status, stream);
 }

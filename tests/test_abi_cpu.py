@@ -307,6 +307,33 @@ def test_gated_delta_forward_workspace_size():
     assert W(-1, 2, 1) == 0 and W(8, 0, 1) == 0
 
 
+def test_gated_delta_training_forward_host_side_errors():
+    """The training forward checks the forward's arguments and needs the
+    backward's workspace (PVB_E_WORKSPACE, 5, below it, or without one)."""
+    L = pvb.lib()
+    need = L.pvb_gated_delta_bwd_workspace_bytes(8, 2, 1)
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=2, H_k=2, d=128,
+              scale=0.125, h0=None, o=FAKE, o_dtype=0, ht=None, ws=FAKE, ws_bytes=need, status=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.pvb_gated_delta_fwd_train(*a.values(), None)
+    assert call(ws=None, ws_bytes=0) == 5
+    assert call(ws_bytes=need - 1) == 5
+    assert call(ws_bytes=L.pvb_gated_delta_fwd_workspace_bytes(8, 2, 1)) == 5
+    assert call(d=64) == 6
+    assert call(H=0) == 1
+    assert call(H_k=3) == 1
+    assert call(o_dtype=3) == 1
+    assert call(scale=0.0) == 1
+    for name in ("q", "k", "v", "g", "b", "o", "cu", "status"):
+        assert call(**{name: None}) == 1, name
+    assert call(n_seg=pvb.PVB_MAX_COUNT + 1) == 3
+    assert call(T=2 ** 24, H=2 ** 7, H_k=2 ** 7, ws_bytes=1 << 40) == 6
+    bad = np.array([0, 9], np.int32)
+    assert call(h_cu=bad.ctypes.data) == 4
+
+
 def test_gated_delta_grouped_heads_host_side_errors():
     L = pvb.lib()
     args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=6, H_k=4, d=128,
@@ -377,7 +404,8 @@ def test_noalloc_backward_refuses_sizes_beyond_its_scratch_on_host():
     assert pvb.workspace_bytes(131072, 32, 128, 1, True) <= cap
 
 
-def test_gated_delta_backward_host_side_errors():
+@pytest.mark.parametrize("entry", ["pvb_gated_delta_bwd", "pvb_gated_delta_bwd_after_fwd"])
+def test_gated_delta_backward_host_side_errors(entry):
     L = pvb.lib()
     ok = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, cu=FAKE, h_cu=None, n_seg=1, T=8, H=2, H_k=2, d=128,
               scale=0.125, h0=None, do=FAKE, dht=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, db=FAKE, dh0=None,
@@ -385,7 +413,7 @@ def test_gated_delta_backward_host_side_errors():
 
     def call(**kw):
         a = dict(ok, **kw)
-        return L.pvb_gated_delta_bwd(*a.values(), None)
+        return getattr(L, entry)(*a.values(), None)
     assert call() == 5                                # the workspace is too small
     assert call(d=64) == 6
     assert call(H=0) == 1

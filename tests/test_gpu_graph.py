@@ -221,3 +221,67 @@ def test_gated_delta_backward_graph_replays():
                 err = float(np.abs(a.double().cpu().numpy() - b).max())
                 say(f"  {n} max-abs {err:.3e}")
                 assert err <= 1e-3 * max(1.0, float(np.abs(b).max()))
+
+
+def test_gated_delta_training_pair_graph_replays():
+    """The training pair (the forward that leaves the backward's checkpoints,
+    then the backward that reads them) recorded once into a HIP graph on one
+    workspace and replayed over two packs of the same size, each with a slice
+    longer than one group; every replay equals the plain forward and backward,
+    called eagerly on their own workspaces, bit for bit."""
+    import packed_varlen_block_amd as pvb
+    import torch
+    packs = [[1100, 0, 64, 257], [257, 64, 0, 1100]]
+    H, d = 4, 128
+    T, B = int(np.sum(packs[0])), len(packs[0])
+    sets = [W.random_gated_delta(2400 + i, p, H=H, initial_state=True) for i, p in enumerate(packs)]
+    r = np.random.default_rng(2410)
+    dos = [W.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32)) for _ in packs]
+    dev = torch.device("cuda:0")
+
+    def upload(w, do):
+        x = {n: (_bits(w[n]) if w[n].dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(w[n])))
+             for n in ("q", "k", "v", "g", "beta", "h0")}
+        x["do"] = _bits(do)
+        return x
+
+    st_in = {n: t.to(dev) for n, t in upload(sets[0], dos[0]).items()}
+    cu = torch.tensor(host_cu(packs[0]), dtype=torch.int32, device=dev)
+    ws = torch.empty(pvb.gated_delta_bwd_workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty_like(ws)
+
+    def pair(c, x):
+        a = (x["q"], x["k"], x["v"], x["g"], x["beta"], c)
+        o, ht, st = pvb.gated_delta_fwd(*a, initial_state=x["h0"], o_dtype=torch.float32, workspace=ws, train=True)
+        grads = pvb.gated_delta_bwd(*a, x["do"], initial_state=x["h0"], workspace=ws, after_fwd=True)
+        return (o, ht) + tuple(grads[:6]), (st, grads[-1])
+
+    def plain(c, x):
+        a = (x["q"], x["k"], x["v"], x["g"], x["beta"], c)
+        o, ht, st = pvb.gated_delta_fwd(*a, initial_state=x["h0"], o_dtype=torch.float32)
+        grads = pvb.gated_delta_bwd(*a, x["do"], initial_state=x["h0"], workspace=ws_e)
+        return (o, ht) + tuple(grads[:6]), (st, grads[-1])
+
+    out0, s0 = pair(cu, st_in)
+    for s in s0:
+        pvb.check_status(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sout, ss = pair(cu, st_in)
+    torch.cuda.synchronize()
+    names = ("O", "final state", "dq", "dk", "dv", "dg", "dbeta", "dh0")
+    for rep, i in enumerate([1, 0, 1]):
+        say(f"gated delta training pair graph replay {rep}: pack {packs[i]}")
+        cu.copy_(torch.tensor(host_cu(packs[i]), dtype=torch.int32))
+        for n, t in upload(sets[i], dos[i]).items():
+            st_in[n].copy_(t)
+        eager, es = plain(cu.clone(), {n: t.clone() for n, t in st_in.items()})
+        for s in es:
+            pvb.check_status(s)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in ss:
+            pvb.check_status(s)
+        for n, a, b in zip(names, sout, eager):
+            _same(n, a, b)
