@@ -30,6 +30,9 @@
 // so the groups' maps are composed in parallel, walked group by group, and
 // every group's chunks then run from their starting state (the forward, and
 // both walks of the backward, the state-gradient walk on the transposed maps).
+// The backward recomputes each chunk's starting state and U from the inputs;
+// a training forward can leave them (with T, T^T and the group maps) in the
+// backward's workspace instead, and the backward then skips that walk.
 #include <type_traits>
 
 #include "pvb_device.hpp"
