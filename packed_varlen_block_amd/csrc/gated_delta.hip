@@ -1896,6 +1896,9 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
   const float* dRp = ck_dr + ((size_t)slot * H + h) * kGdChunkFloats;
   const int n0 = 32 * cq + c;                         // this lane's value column, and key dim
 
+  // this wave's rows of V in its value columns, loaded with the tiles and in
+  // flight during the barrier
+  float vc[16];
   {
     GdStage<kGdChunkThreads> st;
     st.fetch(q, k, dout, g, beta, t0, n, H, Hk, h, hk, tid);
@@ -1906,6 +1909,11 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       xu[it] = *(const float4*)(Up + 4 * ch);
       xd[it] = *(const float4*)(dRp + 4 * ch);
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * rb + crow(i, hg);
+      vc[i] = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
+    }
     st.put(t, tid);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -1915,14 +1923,16 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
     }
     if (w == 0) gd_gates(t, st.g, st.b, lane);
   }
-  // this wave's rows of V in its value columns, in flight during the barrier
-  float vc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 32 * rb + crow(i, hg);
-    vc[i] = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
-  }
   __syncthreads();
+  // the first k-step of S0 and dS for the products after dA and dP (row n0,
+  // value columns 16 s + 8 hg ..), in flight during the blocks before them
+  float xs[2][8], xds[2][8];
+  auto fetch_s = [&](int s, int buf) {
+    const int col = 16 * s + 8 * hg;
+    load8f(S0p + (size_t)n0 * kGdD + col, xs[buf]);
+    load8f(dSp + (size_t)n0 * kGdD + col, xds[buf]);
+  };
+  fetch_s(0, 0);
 
   if (w < 6) {
     // Ah and P blocks: KK (1,0), QK (0,0), QK (1,0), KK (0,0), KK (1,1), QK (1,1)
@@ -2015,17 +2025,10 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
   f32x16 r1 = {}, kt1 = {}, q1 = {};
   {
     float sdot = 0.f;
-    float xs[2][8], xds[2][8];
-    auto fetch = [&](int s, int buf) {
-      const int col = 16 * s + 8 * hg;
-      load8f(S0p + (size_t)n0 * kGdD + col, xs[buf]);
-      load8f(dSp + (size_t)n0 * kGdD + col, xds[buf]);
-    };
-    fetch(0, 0);
 #pragma unroll
     for (int s = 0; s < kGdD / 16; ++s) {
       const int cur = s & 1, col = 16 * s + 8 * hg;
-      if (s + 1 < kGdD / 16) fetch(s + 1, cur ^ 1);
+      if (s + 1 < kGdD / 16) fetch_s(s + 1, cur ^ 1);
       if (rb == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sdot += xs[cur][e] * xds[cur][e];
