@@ -150,5 +150,24 @@ def test_gated_delta_forward_backward_at_the_element_limit():
             err = float(np.abs(got.double().cpu().numpy() - ref).max())
             say(f"    hk{hk} {name}: max-abs {err:.3e}")
             assert err <= bar(ref), name
+    # the training pair on the same inputs: the same results as the plain calls,
+    # bit for bit (dq and dk, summed over the value-head pairs with atomics in
+    # no fixed order, to 1e-6 of their largest magnitude)
+    say("  the training pair at the same size, against the plain calls")
+    ws = torch.empty(pvb.gated_delta_bwd_workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+    o2, ht2, st = pvb.gated_delta_fwd(q, k, v, g, beta, cu, h_cu=hc, initial_state=h0, workspace=ws, train=True)
+    pvb.check_status(st)
+    grads = pvb.gated_delta_bwd(q, k, v, g, beta, cu, do, h_cu=hc, initial_state=h0, dht=dht,
+                                grad_dtype=torch.bfloat16, workspace=ws, after_fwd=True)
+    pvb.check_status(grads[-1])
+    del ws
+    for name, a2, a1 in (("O", o2, o), ("final state", ht2, ht), ("dv", grads[2], dv), ("dg", grads[3], dg),
+                         ("dbeta", grads[4], db), ("dh0", grads[5], dh0)):
+        assert torch.equal(a2, a1), f"training pair {name} differs from the plain call"
+    for name, a2, a1 in (("dq", grads[0], dq), ("dk", grads[1], dk)):
+        err = float((a2 - a1).abs().max())
+        say(f"    training pair {name}: max-abs difference {err:.3e}")
+        assert err <= 1e-6 * max(1.0, float(a1.abs().max())), name
+    del o2, ht2, grads
     del q, k, v, do, o, ht, dq, dk, dv, dg, db, dh0
     torch.cuda.empty_cache()
