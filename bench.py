@@ -285,6 +285,12 @@ def main():
     def avg_ms(name):
         return float(np.mean([s.elapsed_time(e) for s, e in ev[name]]))
 
+    # each timed step's device time, packed-row build to the end of the
+    # backward (its host planning runs before and overlaps the previous step)
+    dev_ms = np.array([r[0].elapsed_time(b[1]) for r, b in zip(ev["row"], ev["bwd"])])
+    step_spread = {"median": round(float(np.median(dev_ms)), 4), "p10": round(float(np.percentile(dev_ms, 10)), 4),
+                   "p90": round(float(np.percentile(dev_ms, 90)), 4)}
+
     ms_step = elapsed / a.steps * 1e3
     F = useful_fwd_flops(wl.lengths, H, d)
     value = 3.5 * F / (ms_step * 1e-3) / 1e12
@@ -318,6 +324,7 @@ def main():
         "useful_flop_per_step": 3.5 * F,
         "breakdown_ms": {"host_bfd_plan": round(plan_ms, 4), "build_packed_row": round(row_ms, 4),
                          "varlen_attn_fwd": round(fwd_ms, 4), "varlen_attn_bwd": round(bwd_ms, 4)},
+        "step_device_ms": step_spread,
         "fwd_tflops": round(fwd_tflops, 2),
         "bwd_tflops": round(bwd_tflops, 2),
         "roofline": {"kernel": "varlen_attn_bwd", "bound": "mfma", "achieved": round(bwd_tflops, 2),
