@@ -135,6 +135,28 @@ def test_train_pair_long_slice_grouped_heads():
     _case(713, [2100, 300, 0, 65], H=4, Hk=2, h0=True, dht=True, mirror=False)
 
 
+def test_train_pair_zero_length_slices_and_empty_stream():
+    """Zero-length slices pass their initial state to their final state and
+    their final-state gradient to their initial-state gradient; an empty stream
+    (no token, no slice) runs both calls and writes nothing."""
+    import torch
+
+    import packed_varlen_block_amd as pvb
+    say("gated delta training pair: zero-length slices, an all-empty pack, an empty stream")
+    _case(720, [0, 5, 0], H=2, h0=True, dht=True)
+    _case(721, [0, 0], H=2, h0=True, dht=True)
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    zf = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    cu = torch.tensor([0], dtype=torch.int32, device="cuda")
+    ws = torch.empty(pvb.gated_delta_bwd_workspace_bytes(0, 2, 0), dtype=torch.uint8, device="cuda")
+    o, ht, st = pvb.gated_delta_fwd(z, z, z, zf, zf, cu, workspace=ws, train=True)
+    pvb.check_status(st)
+    assert o.numel() == 0 and ht.numel() == 0
+    grads = pvb.gated_delta_bwd(z, z, z, zf, zf, cu, z, workspace=ws, after_fwd=True)
+    pvb.check_status(grads[-1])
+    assert all(x.numel() == 0 for x in grads[:5])
+
+
 def test_train_pair_bad_cu_writes_nothing():
     import torch
 
