@@ -225,27 +225,41 @@ def main():
     st_row = torch.zeros(1, dtype=torch.int32, device=dev)
     st_f = torch.zeros(1, dtype=torch.int32, device=dev)
     st_b = torch.zeros(1, dtype=torch.int32, device=dev)
+    # Each step's pack lengths are planned on the host and uploaded on a copy
+    # stream one step ahead, while the previous step runs, so that the upload's
+    # latency stays off the compute stream; four pinned and device slots rotate.
     ring = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(4)]
-    ring_ev = [None] * 4
-    len_dev = torch.empty(B, dtype=torch.int32, device=dev)
+    ring_ev = [None] * 4                              # the slot's last upload
+    use_ev = [None] * 4                               # the slot's last packed-row build
+    len_dev = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
+    copy_stream = torch.cuda.Stream(dev)
 
     ev = {name: [] for name in ("row", "fwd", "bwd")}
 
-    def step(i, timed):
-        # host: plan, take the first pack, stage its lengths
+    def plan_and_upload(i):
+        # host: plan, take the first pack, stage its lengths for step i
         _, _, _, order_i, offs_i = pvb.pack_plan_bfd(raw, 8192)
         slot = i % 4
         if ring_ev[slot] is not None:
-            ring_ev[slot].synchronize()
+            ring_ev[slot].synchronize()               # step i - 4 is done with the slot
         ring[slot].numpy()[:] = raw[order_i[offs_i[0]:offs_i[1]]]
-        len_dev.copy_(ring[slot], non_blocking=True)
+        if use_ev[slot] is not None:
+            copy_stream.wait_event(use_ev[slot])      # step i - 4's packed-row build has read it
+        with torch.cuda.stream(copy_stream):
+            len_dev[slot].copy_(ring[slot], non_blocking=True)
         e = torch.cuda.Event()
-        e.record(stream)
+        e.record(copy_stream)
         ring_ev[slot] = e
+
+    def step(i, timed):
+        slot = i % 4
+        stream.wait_event(ring_ev[slot])              # step i's lengths have landed
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
         if timed:
             marks[0].record(stream)
-        row = pvb.build_packed_row(len_dev, capacity=T, status=st_row)
+        row = pvb.build_packed_row(len_dev[slot], capacity=T, status=st_row)
+        use_ev[slot] = torch.cuda.Event()
+        use_ev[slot].record(stream)
         if timed:
             marks[1].record(stream)
         pvb.varlen_attn_fwd(q, k, v, row["cu"], out=o, lse=lse, workspace=ws_f, status=st_f)
@@ -258,6 +272,7 @@ def main():
             ev["row"].append((marks[0], marks[1]))
             ev["fwd"].append((marks[1], marks[2]))
             ev["bwd"].append((marks[2], marks[3]))
+        plan_and_upload(i + 1)                        # the next step's pack, while this one runs
 
     if a.copy_mb > 0:
         src = torch.empty(a.copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -267,6 +282,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    plan_and_upload(0)
     for i in range(a.warmup):
         step(i, False)
     torch.cuda.synchronize()
