@@ -258,10 +258,9 @@ def main():
         if timed:
             marks[0].record(stream)
         row = pvb.build_packed_row(len_dev[slot], capacity=T, status=st_row)
-        use_ev[slot] = torch.cuda.Event()
+        # one event after the build: the timing mark, which also frees the slot
+        use_ev[slot] = marks[1] if timed else torch.cuda.Event()
         use_ev[slot].record(stream)
-        if timed:
-            marks[1].record(stream)
         pvb.varlen_attn_fwd(q, k, v, row["cu"], out=o, lse=lse, workspace=ws_f, status=st_f)
         if timed:
             marks[2].record(stream)
