@@ -553,18 +553,18 @@ __device__ __forceinline__ void gd_fwd_body(GdSmem& sm, int& s_bad, int blk, con
 }
 
 
-template <typename OutT, bool CKPT = false>
+// The forward without a workspace: one chain per (slice, value head).
+template <typename OutT>
 __global__ void __launch_bounds__(kGdThreads, 1)
 gated_delta_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const float* __restrict__ g, const float* __restrict__ beta,
                    const int32_t* __restrict__ cu, int n_seg, int T, int H, int Hk, float scale,
                    const float* __restrict__ h0, OutT* __restrict__ o, float* __restrict__ ht,
-                   int32_t* __restrict__ status, float* __restrict__ ck_s = nullptr,
-                   float* __restrict__ ck_u = nullptr, const float* __restrict__ ck_t = nullptr) {
+                   int32_t* __restrict__ status) {
   __shared__ GdSmem sm;
   __shared__ int s_bad;
-  gd_fwd_body<OutT, CKPT>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o, ht, status, ck_s,
-                          ck_u, ck_t);
+  gd_fwd_body<OutT, false>(sm, s_bad, blockIdx.x, q, k, v, g, beta, cu, n_seg, T, H, Hk, scale, h0, o, ht, status,
+                           nullptr, nullptr, nullptr);
 }
 
 }  // namespace
