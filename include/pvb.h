@@ -63,8 +63,9 @@ typedef enum pvb_status {
  * A launch also holds fewer than 2^32 work-items (the dispatch's grid size is
  * a 32-bit count): an attention call whose work list would need 2^24 or more
  * workgroups of 256 (about (T / 128 + min(B, T)) * H of them), a gated delta
- * call with B * H >= 2^24, or a loss over C >= 2^24 cells returns
- * PVB_E_UNSUPPORTED, again before anything is enqueued. */
+ * forward with B * H >= 2^22 or backward with B * H >= 2^21 (its group walks
+ * launch four and eight workgroups per slice and head), or a loss over
+ * C >= 2^24 cells returns PVB_E_UNSUPPORTED, again before anything is enqueued. */
 #define PVB_MAX_COUNT (2147483647 - 65535)
 
 typedef enum pvb_dtype { PVB_BF16 = 0, PVB_F32 = 1 } pvb_dtype;

@@ -1607,17 +1607,17 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
 // D_(g-1) = A_g^T D_g + F_g from the slice's last group back to its second,
 // stored as group g-1's end gradient; the A operand then takes A_g's columns.
 constexpr int kGdScanPitch = 20;     // floats per lane in the exchange: b128 accesses free of bank conflicts
+using GdScanLds = float[2][4][64][kGdScanPitch];
 template <bool REV>
-__global__ void __launch_bounds__(kGdThreads, 1)
-gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, const float* __restrict__ h0,
-                   const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS) {
-  __shared__ alignas(16) float xs[2][4][64][kGdScanPitch];
-  __shared__ int s_bad;
+__device__ __forceinline__ void gd_grp_scan_body(GdScanLds& xs, int& s_bad, int blk, const int32_t* __restrict__ cu,
+                                                 int n_seg, int T, int H, const float* __restrict__ h0,
+                                                 const float* __restrict__ gA, const float* __restrict__ gZ,
+                                                 float* __restrict__ gS) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, hg = lane >> 5, c = lane & 31;
   const int nbh = n_seg * H;
   if (gd_cu_bad(cu, n_seg, T, &s_bad) || nbh == 0) return;
-  const int cb = (int)blockIdx.x / nbh, bh = (int)blockIdx.x - cb * nbh;
+  const int cb = blk / nbh, bh = blk - cb * nbh;
   if (cb >= 4) return;
   const int b = bh / H, h = bh - b * H;
   const int seg0 = cu[b], L = cu[b + 1] - seg0;
@@ -1694,6 +1694,31 @@ gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, cons
     }
   }
 #undef GD_SCAN_LOAD
+}
+
+template <bool REV>
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, const float* __restrict__ h0,
+                   const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS) {
+  __shared__ alignas(16) GdScanLds xs;
+  __shared__ int s_bad;
+  gd_grp_scan_body<REV>(xs, s_bad, (int)blockIdx.x, cu, n_seg, T, H, h0, gA, gZ, gS);
+}
+
+// Both walks of the plain backward in one launch: blocks [0, nb) the forward
+// walk (starting states), blocks [nb, 2 nb) the reverse walk (end gradients);
+// nb = 4 n_seg H, a multiple of 8 when n_seg H is, so that each walk's four
+// column blocks of a (slice, head) stay on one XCD.
+__global__ void __launch_bounds__(kGdThreads, 1)
+gd_grp_scan2_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, int nb, const float* __restrict__ h0,
+                    const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS,
+                    const float* __restrict__ dht, const float* __restrict__ gF, float* __restrict__ gD) {
+  __shared__ alignas(16) GdScanLds xs;
+  __shared__ int s_bad;
+  if ((int)blockIdx.x < nb)
+    gd_grp_scan_body<false>(xs, s_bad, (int)blockIdx.x, cu, n_seg, T, H, h0, gA, gZ, gS);
+  else
+    gd_grp_scan_body<true>(xs, s_bad, (int)blockIdx.x - nb, cu, n_seg, T, H, dht, gA, gF, gD);
 }
 
 // Pass 3: the forward kernel on every group from its starting state.
@@ -2246,7 +2271,7 @@ pvb_status gated_delta_bwd_call(const void* d_q, const void* d_k, const void* d_
   if (!(scale > 0.f) || !(scale < INFINITY)) return PVB_E_INVALID_ARG;
   if (d != kGdD) return PVB_E_UNSUPPORTED;
   const GdBwdLayout lay = gd_bwd_layout(T, H, n_seg);
-  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)4 * n_seg * H, kGdThreads) ||
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31) || !grid_fits((uint64_t)8 * n_seg * H, kGdThreads) ||
       !grid_fits((uint64_t)lay.slots * H, kGdChunkThreads) || !grid_fits((uint64_t)2 * lay.gslots * H, kGdThreads))
     return PVB_E_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < lay.total) return PVB_E_WORKSPACE;
@@ -2329,8 +2354,8 @@ pvb_status gated_delta_bwd_call(const void* d_q, const void* d_k, const void* d_
     gd_bwd_cgrp_compose_kernel<<<ggrid, kGdThreads, 0, s>>>((const bf16*)d_q, (const bf16*)d_k, d_g, d_beta, d_cu,
                                                             n_seg, T, H, H_k, scale, (const bf16*)d_dout, ck_t, gF);
     const unsigned sgrid = (unsigned)std::max<int64_t>(1, 4 * (int64_t)n_seg * H);
-    gd_grp_scan_kernel<false><<<sgrid, kGdThreads, 0, s>>>(d_cu, n_seg, T, H, d_h0, gA, gZ, gS);
-    gd_grp_scan_kernel<true><<<sgrid, kGdThreads, 0, s>>>(d_cu, n_seg, T, H, d_dht, gA, gF, gD);
+    gd_grp_scan2_kernel<<<2 * sgrid, kGdThreads, 0, s>>>(d_cu, n_seg, T, H, (int)sgrid, d_h0, gA, gZ, gS, d_dht,
+                                                         gF, gD);
     if (grad_dtype == PVB_F32)
       gd_bwd_grp_chains_kernel<float><<<2 * ggrid, kGdThreads, 0, s>>>(
           (const bf16*)d_q, (const bf16*)d_k, (const bf16*)d_v, d_g, d_beta, d_cu, n_seg, T, H, H_k, scale, d_h0,

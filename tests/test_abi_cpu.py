@@ -382,6 +382,27 @@ def test_grids_of_2_to_the_32_work_items_are_refused_on_host():
                                      None, FAKE, 1, None, None, 0, FAKE, None) == 6
 
 
+def test_gated_delta_grid_limits_on_host():
+    """The gated delta group walks launch four workgroups of 256 per slice and
+    head (the backward's two walks together eight), so a forward with
+    B * H >= 2^22 or a backward with B * H >= 2^21 returns PVB_E_UNSUPPORTED
+    (6); one head fewer passes the grid checks and stops at the too-small
+    workspace (5)."""
+    L = pvb.lib()
+
+    def fwd(n_seg, H):
+        return L.pvb_gated_delta_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, n_seg, 8, H, H, 128, 0.1,
+                                         None, FAKE, 1, None, FAKE, 16, FAKE, None)
+
+    def bwd(n_seg, H):
+        return L.pvb_gated_delta_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, n_seg, 8, H, H, 128, 0.1, None,
+                                     FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, FAKE, 16, FAKE, None)
+    assert fwd(2 ** 16, 64) == 6 and fwd(2 ** 16, 63) == 5
+    assert bwd(2 ** 16, 32) == 6 and bwd(2 ** 16, 31) == 5
+    assert L.pvb_gated_delta_fwd_train(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2 ** 16, 8, 64, 64, 128, 0.1,
+                                       None, FAKE, 1, None, FAKE, 16, FAKE, None) == 6
+
+
 def test_noalloc_backward_refuses_sizes_beyond_its_scratch_on_host():
     """pvb_varlen_attn_bwd_noalloc serves sizes whose workspace fits its fixed
     scratch (PVB_STATIC_SCRATCH_BYTES); larger ones return PVB_E_WORKSPACE (5)
