@@ -1706,9 +1706,9 @@ gd_grp_scan_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, cons
 }
 
 // Both walks of the plain backward in one launch: blocks [0, nb) the forward
-// walk (starting states), blocks [nb, 2 nb) the reverse walk (end gradients);
-// nb = 4 n_seg H, a multiple of 8 when n_seg H is, so that each walk's four
-// column blocks of a (slice, head) stay on one XCD.
+// walk (starting states), blocks [nb, 2 nb) the reverse walk (end gradients),
+// nb = 4 n_seg H.  When n_seg H is a multiple of 8, each walk's four column
+// blocks of a (slice, head) stay on one XCD, as in the separate launches.
 __global__ void __launch_bounds__(kGdThreads, 1)
 gd_grp_scan2_kernel(const int32_t* __restrict__ cu, int n_seg, int T, int H, int nb, const float* __restrict__ h0,
                     const float* __restrict__ gA, const float* __restrict__ gZ, float* __restrict__ gS,
