@@ -1934,10 +1934,14 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
       xu[it] = *(const float4*)(Up + 4 * ch);
       xd[it] = *(const float4*)(dRp + 4 * ch);
     }
+    // rows past the chunk's end read its last row (always in bounds) and are
+    // then set to zero: a load under the row test would be a branch, which
+    // the compiler closes by waiting for the load, one round trip per row
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = 32 * rb + crow(i, hg);
-      vc[i] = row < n ? (float)v[((size_t)(t0 + row) * H + h) * kGdD + n0] : 0.f;
+      const float x = (float)v[((size_t)(t0 + min(row, n - 1)) * H + h) * kGdD + n0];
+      vc[i] = row < n ? x : 0.f;
     }
     st.put(t, tid);
 #pragma unroll
