@@ -1448,38 +1448,55 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
     const int nr_ = BWD ? std::min(kGdC, seg0 + L - t0_) : kGdC;                                        \
     const float* tp_ = ck_t + (gd_ckpt_slot(seg0, b, gi * kGdGrpChunks + (j_)) * H + h) * t_stride      \
                        + 4 * tid;                                                                       \
+    /* rows past the slice's end (BWD: a last chunk may be partial) load its */                        \
+    /* last row and are zeroed when staged: a load under the row test would */                          \
+    /* be a branch closed by a full wait, and so would a select right after */                          \
+    /* the loads.  o*_ are row offsets from row frow. */                                                \
+    const int o0_ = BWD ? std::min(0, nr_ - 1 - frow) : 0, o1_ = BWD ? std::min(16, nr_ - 1 - frow) : 16;  \
+    const int o2_ = BWD ? std::min(32, nr_ - 1 - frow) : 32, o3_ = BWD ? std::min(48, nr_ - 1 - frow) : 48; \
     const bf16* kp_ = k + ((size_t)(t0_ + frow) * Hk + hk) * kGdD + fcol;                               \
-    pk0 = frow < nr_ ? *(const uint4*)kp_ : zero4();                                                    \
-    pk1 = frow + 16 < nr_ ? *(const uint4*)(kp_ + (size_t)16 * Hk * kGdD) : zero4();                    \
-    pk2 = frow + 32 < nr_ ? *(const uint4*)(kp_ + (size_t)32 * Hk * kGdD) : zero4();                    \
-    pk3 = frow + 48 < nr_ ? *(const uint4*)(kp_ + (size_t)48 * Hk * kGdD) : zero4();                    \
     const bf16* vp_ = v + ((size_t)(t0_ + frow) * H + h) * kGdD + fcol;                                 \
-    pv0 = frow < nr_ ? *(const uint4*)vp_ : zero4();                                                    \
-    pv1 = frow + 16 < nr_ ? *(const uint4*)(vp_ + (size_t)16 * H * kGdD) : zero4();                     \
-    pv2 = frow + 32 < nr_ ? *(const uint4*)(vp_ + (size_t)32 * H * kGdD) : zero4();                     \
-    pv3 = frow + 48 < nr_ ? *(const uint4*)(vp_ + (size_t)48 * H * kGdD) : zero4();                     \
+    pk0 = *(const uint4*)(kp_ + (ptrdiff_t)o0_ * Hk * kGdD);                                            \
+    pk1 = *(const uint4*)(kp_ + (ptrdiff_t)o1_ * Hk * kGdD);                                            \
+    pk2 = *(const uint4*)(kp_ + (ptrdiff_t)o2_ * Hk * kGdD);                                            \
+    pk3 = *(const uint4*)(kp_ + (ptrdiff_t)o3_ * Hk * kGdD);                                            \
+    pv0 = *(const uint4*)(vp_ + (ptrdiff_t)o0_ * H * kGdD);                                             \
+    pv1 = *(const uint4*)(vp_ + (ptrdiff_t)o1_ * H * kGdD);                                             \
+    pv2 = *(const uint4*)(vp_ + (ptrdiff_t)o2_ * H * kGdD);                                             \
+    pv3 = *(const uint4*)(vp_ + (ptrdiff_t)o3_ * H * kGdD);                                             \
     pt0 = *(const float4*)tp_;                                                                          \
     pt1 = *(const float4*)(tp_ + 4 * kGdThreads);                                                       \
     pt2 = *(const float4*)(tp_ + 8 * kGdThreads);                                                       \
-    pg = lane < nr_ ? g[(size_t)(t0_ + lane) * H + h] : 0.f;                                            \
-    pb = lane < nr_ ? beta[(size_t)(t0_ + lane) * H + h] : 0.f;                                         \
+    const int rl_ = BWD ? std::min(lane, nr_ - 1) : lane;                                                \
+    pg = g[(size_t)(t0_ + rl_) * H + h];                                                                \
+    pb = beta[(size_t)(t0_ + rl_) * H + h];                                                             \
   }
   GD_CMP_FETCH(0);
   for (int j = 0; j < nch; ++j) {
+    // the lane's indices, made opaque per chunk (they shadow the ones above),
+    // so that the addresses formed from them are not hoisted out of the loop
+    // and kept in registers, which spilled
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, hg = lane >> 5, c = lane & 31;
+    const int frow = tid >> 4, fcol = (tid & 15) * 8;
+    const int n0 = 32 * w + c;
+    // rows of this chunk: 64, fewer in a partial last chunk (BWD only)
+    const int nr = BWD ? std::min(kGdC, L - (gi * kGdGrpChunks + j) * kGdC) : kGdC;
     __syncthreads();                                   // the previous chunk's reads of LDS are done
-    *(uint4*)&sm.k[frow][fcol] = pk0;
-    *(uint4*)&sm.k[frow + 16][fcol] = pk1;
-    *(uint4*)&sm.k[frow + 32][fcol] = pk2;
-    *(uint4*)&sm.k[frow + 48][fcol] = pk3;
-    *(uint4*)&sm.v[frow][fcol] = pv0;
-    *(uint4*)&sm.v[frow + 16][fcol] = pv1;
-    *(uint4*)&sm.v[frow + 32][fcol] = pv2;
-    *(uint4*)&sm.v[frow + 48][fcol] = pv3;
+    *(uint4*)&sm.k[frow][fcol] = frow < nr ? pk0 : zero4();
+    *(uint4*)&sm.k[frow + 16][fcol] = frow + 16 < nr ? pk1 : zero4();
+    *(uint4*)&sm.k[frow + 32][fcol] = frow + 32 < nr ? pk2 : zero4();
+    *(uint4*)&sm.k[frow + 48][fcol] = frow + 48 < nr ? pk3 : zero4();
+    *(uint4*)&sm.v[frow][fcol] = frow < nr ? pv0 : zero4();
+    *(uint4*)&sm.v[frow + 16][fcol] = frow + 16 < nr ? pv1 : zero4();
+    *(uint4*)&sm.v[frow + 32][fcol] = frow + 32 < nr ? pv2 : zero4();
+    *(uint4*)&sm.v[frow + 48][fcol] = frow + 48 < nr ? pv3 : zero4();
     reinterpret_cast<float4*>(&sm.tf[0][0])[tid] = pt0;
     reinterpret_cast<float4*>(&sm.tf[0][0])[tid + kGdThreads] = pt1;
     reinterpret_cast<float4*>(&sm.tf[0][0])[tid + 2 * kGdThreads] = pt2;
     if (w == 0) {
-      float x = pg;
+      float x = lane < nr ? pg : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -1489,7 +1506,7 @@ gd_grp_compose_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, co
       const float last = __shfl(x, 63, 64);
       sm.eg[lane] = fast_exp2(x);
       sm.dec[lane] = fast_exp2(last - x);
-      sm.beta[lane] = pb;
+      sm.beta[lane] = lane < nr ? pb : 0.f;
     }
     if (j + 1 < nch) GD_CMP_FETCH(j + 1);
     __syncthreads();
