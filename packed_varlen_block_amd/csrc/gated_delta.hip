@@ -599,13 +599,20 @@ namespace {
 //   dg_t = sum_{i >= t} dgamma_i  (inside the chunk).
 // Only the first three lines form a chain from chunk to chunk, and that chain
 // needs neither S0 nor U.  So the call runs three passes:
-//   1. the forward in its recomputation mode (gated_delta_kernel, CKPT): S0
-//      and U of every chunk into checkpoint slots;
-//   2. the state-gradient chain (gd_bwd_chain_kernel), one workgroup per
-//      (slice, value head) walking the chunks back: dS at every chunk's end
-//      and every chunk's dR into checkpoint slots, dV, and dh0;
+//   0. T = (I + A)^-1 of every chunk (gd_tmat_kernel), as split fragments of
+//      T and T^T;
+//   1. the recomputation walk, which stores S0 and U of every chunk into
+//      checkpoint slots, and
+//   2. the state-gradient walk back over the chunks, which stores dS at every
+//      chunk's end and every chunk's dR and writes dV and dh0; both walks run
+//      side by side in one launch (gd_bwd_chains_kernel), or, when a slice is
+//      longer than one group, on every group at once from the group maps and
+//      scans (gd_bwd_grp_chains_kernel);
 //   3. the chunk-parallel pass (gd_bwd_chunk_kernel), one workgroup per
 //      (chunk, value head): everything else, from the four checkpoints.
+// After the training forward (gd_fwd_train_kernel), which leaves T, S0, U and
+// the recomputation's group maps in the workspace, passes 0 and 1 are skipped
+// and pass 2 runs alone (gd_bwd_cwalk_kernel).
 // The products run on the matrix cores with fp32 operands split into bf16
 // hi + lo parts (about 16 significant bits); the transposed solve is fp32 on
 // the vector unit.  dQ and dK of a query/key head shared by several value
@@ -2004,127 +2011,137 @@ gd_bwd_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, cons
   }
   __syncthreads();                                    // Ah and P are complete
 
-  // ---- dA = -strict_lower(dR U^T) and dP = scale lower(dO U^T), contracted
-  // over all value columns (k index = column 16 s + 8 hg + e), one block per
-  // wave: its row and column partials of dA o Ah (with beta of the row for the
-  // columns) and dP o P, then M = diag(beta) (Gam o dA) and N = Gam o dP
-  // written over Ah and P in place (each wave reads and writes its own block).
-  if (w < 6) {
-    const bool isp = w >= 3;
-    const int bi = (w == 1 || w == 3) ? 0 : 1, bj = (w == 2 || w == 5) ? 1 : 0;
-    f32x16 acc = {};
-#pragma unroll
-    for (int s = 0; s < kGdD / 16; ++s) {
-      const int col = 16 * s + 8 * hg;
-      float xu[8];
-      load8f(&sm.u[32 * bj + c][col], xu);
-      bf16x8 uh, ul;
-      split8(xu, uh, ul);
-      if (isp) {
-        const bf16x8 a = *(const bf16x8*)&t.dO[32 * bi + c][col];
-        acc = mfma32(a, uh, acc);
-        acc = mfma32(a, ul, acc);
-      } else {
-        float xd[8];
-        load8f(&sm.dr[32 * bi + c][col], xd);
-        bf16x8 rh, rl;
-        split8(xd, rh, rl);
-        acc = mfma32(rh, uh, acc);
-        acc = mfma32(rh, ul, acc);
-        acc = mfma32(rl, uh, acc);
-      }
-    }
-    const int cc = 32 * bj + c;
-    const float glc = t.gl[cc];
-    float rsum[16], csum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * bi + crow(i, hg);
-      const float gam = fast_exp2(fminf(t.gl[r] - glc, 0.f));
-      if (isp) {
-        const float dpv = cc <= r ? scale * acc[i] : 0.f;
-        const float prod = dpv * t.p[r][cc];
-        rsum[i] = prod;
-        csum += prod;
-        t.p[r][cc] = gam * dpv;
-      } else {
-        const float dav = cc < r ? -acc[i] : 0.f;
-        const float prod = dav * t.ah[r][cc];
-        const float br = t.beta[r];
-        rsum[i] = prod;
-        csum += br * prod;
-        t.ah[r][cc] = br * gam * dav;
-      }
-    }
-    int idx;
-    const float rsv = row_sum16(rsum, c, idx);
-    csum += swap_halves(csum);
-    if ((c & 1) == 0) sm.rs[w][crow(idx, hg)] = rsv;
-    if (hg == 0) sm.cs[w][c] = csum;
-  }
-
-  // ---- row block rb, key dims of quarter cq: dR S0^T, U dS^T (= dKt) and
-  // dO S0^T contracted over all value columns; <dS, S0> over these key dims
-  // (waves of row block 0); the row partials sum_d dKt o Kt, and over these
-  // key dims sum_d K o (dR S0^T) = sum_c dR (K S0) and
-  // sum_d Q o (dO S0^T) = sum_c dO (Q S0)
   f32x16 r1 = {}, kt1 = {}, q1 = {};
-  {
-    float sdot = 0.f;
-#pragma unroll
-    for (int s = 0; s < kGdD / 16; ++s) {
-      const int cur = s & 1, col = 16 * s + 8 * hg;
-      if (s + 1 < kGdD / 16) fetch_s(s + 1, cur ^ 1);
-      if (rb == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sdot += xs[cur][e] * xds[cur][e];
+  // waves 2 and 3 take the S0 phase first, in step with waves 6 and 7 (the
+  // same quarters, the other row block), which have no dA / dP block: both row
+  // blocks then read the same S0 and dS lines at about the same time
+  const bool s0_first = w == 2 || w == 3;
+#pragma clang loop unroll(disable)
+  for (int ph = 0; ph < 2; ++ph) {
+    if ((ph == 0) != s0_first) {
+      // ---- dA = -strict_lower(dR U^T) and dP = scale lower(dO U^T), contracted
+      // over all value columns (k index = column 16 s + 8 hg + e), one block per
+      // wave: its row and column partials of dA o Ah (with beta of the row for the
+      // columns) and dP o P, then M = diag(beta) (Gam o dA) and N = Gam o dP
+      // written over Ah and P in place (each wave reads and writes its own block).
+      if (w < 6) {
+        const bool isp = w >= 3;
+        const int bi = (w == 1 || w == 3) ? 0 : 1, bj = (w == 2 || w == 5) ? 1 : 0;
+        f32x16 acc = {};
+    #pragma unroll
+        for (int s = 0; s < kGdD / 16; ++s) {
+          const int col = 16 * s + 8 * hg;
+          float xu[8];
+          load8f(&sm.u[32 * bj + c][col], xu);
+          bf16x8 uh, ul;
+          split8(xu, uh, ul);
+          if (isp) {
+            const bf16x8 a = *(const bf16x8*)&t.dO[32 * bi + c][col];
+            acc = mfma32(a, uh, acc);
+            acc = mfma32(a, ul, acc);
+          } else {
+            float xd[8];
+            load8f(&sm.dr[32 * bi + c][col], xd);
+            bf16x8 rh, rl;
+            split8(xd, rh, rl);
+            acc = mfma32(rh, uh, acc);
+            acc = mfma32(rh, ul, acc);
+            acc = mfma32(rl, uh, acc);
+          }
+        }
+        const int cc = 32 * bj + c;
+        const float glc = t.gl[cc];
+        float rsum[16], csum = 0.f;
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 32 * bi + crow(i, hg);
+          const float gam = fast_exp2(fminf(t.gl[r] - glc, 0.f));
+          if (isp) {
+            const float dpv = cc <= r ? scale * acc[i] : 0.f;
+            const float prod = dpv * t.p[r][cc];
+            rsum[i] = prod;
+            csum += prod;
+            t.p[r][cc] = gam * dpv;
+          } else {
+            const float dav = cc < r ? -acc[i] : 0.f;
+            const float prod = dav * t.ah[r][cc];
+            const float br = t.beta[r];
+            rsum[i] = prod;
+            csum += br * prod;
+            t.ah[r][cc] = br * gam * dav;
+          }
+        }
+        int idx;
+        const float rsv = row_sum16(rsum, c, idx);
+        csum += swap_halves(csum);
+        if ((c & 1) == 0) sm.rs[w][crow(idx, hg)] = rsv;
+        if (hg == 0) sm.cs[w][c] = csum;
       }
-      float xr[8], xu[8];
-      load8f(&sm.dr[32 * rb + c][col], xr);
-      load8f(&sm.u[32 * rb + c][col], xu);
-      bf16x8 sh, sl, dh, dl, rh, rl, uh, ul;
-      split8(xs[cur], sh, sl);
-      split8(xds[cur], dh, dl);
-      split8(xr, rh, rl);
-      split8(xu, uh, ul);
-      const bf16x8 oa = *(const bf16x8*)&t.dO[32 * rb + c][col];
-      r1 = mfma32(rh, sh, r1);
-      r1 = mfma32(rh, sl, r1);
-      r1 = mfma32(rl, sh, r1);
-      kt1 = mfma32(uh, dh, kt1);
-      kt1 = mfma32(uh, dl, kt1);
-      kt1 = mfma32(ul, dh, kt1);
-      q1 = mfma32(oa, sh, q1);
-      q1 = mfma32(oa, sl, q1);
-    }
-    if (rb == 0) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 64);
-      if (lane == 0) sm.red[cq] = sdot;
-    }
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * rb + crow(i, hg);
-      x[i] = kt1[i] * t.dec[row] * (float)t.k[row][n0];
-    }
-    float xb[16], xc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * rb + crow(i, hg);
-      xb[i] = (float)t.k[row][n0] * r1[i];
-      xc[i] = (float)t.q[row][n0] * q1[i];
-    }
-    int idx;
-    const float sx = row_sum16(x, c, idx);
-    const float sb = row_sum16(xb, c, idx);
-    const float sc = row_sum16(xc, c, idx);
-    if ((c & 1) == 0) {
-      const int row = 32 * rb + crow(idx, hg);
-      sm.rk[cq][row] = sx;
-      // this wave wrote sm.xr[cq][row] in the first phase (same lane, same row)
-      sm.xr[cq][row] -= t.eg[row] * sb;
-      sm.gr[cq][row] = -t.beta[row] * sb + scale * sc;
+
+    } else {
+      // ---- row block rb, key dims of quarter cq: dR S0^T, U dS^T (= dKt) and
+      // dO S0^T contracted over all value columns; <dS, S0> over these key dims
+      // (waves of row block 0); the row partials sum_d dKt o Kt, and over these
+      // key dims sum_d K o (dR S0^T) = sum_c dR (K S0) and
+      // sum_d Q o (dO S0^T) = sum_c dO (Q S0)
+      {
+        float sdot = 0.f;
+    #pragma unroll
+        for (int s = 0; s < kGdD / 16; ++s) {
+          const int cur = s & 1, col = 16 * s + 8 * hg;
+          if (s + 1 < kGdD / 16) fetch_s(s + 1, cur ^ 1);
+          if (rb == 0) {
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) sdot += xs[cur][e] * xds[cur][e];
+          }
+          float xr[8], xu[8];
+          load8f(&sm.dr[32 * rb + c][col], xr);
+          load8f(&sm.u[32 * rb + c][col], xu);
+          bf16x8 sh, sl, dh, dl, rh, rl, uh, ul;
+          split8(xs[cur], sh, sl);
+          split8(xds[cur], dh, dl);
+          split8(xr, rh, rl);
+          split8(xu, uh, ul);
+          const bf16x8 oa = *(const bf16x8*)&t.dO[32 * rb + c][col];
+          r1 = mfma32(rh, sh, r1);
+          r1 = mfma32(rh, sl, r1);
+          r1 = mfma32(rl, sh, r1);
+          kt1 = mfma32(uh, dh, kt1);
+          kt1 = mfma32(uh, dl, kt1);
+          kt1 = mfma32(ul, dh, kt1);
+          q1 = mfma32(oa, sh, q1);
+          q1 = mfma32(oa, sl, q1);
+        }
+        if (rb == 0) {
+    #pragma unroll
+          for (int off = 32; off > 0; off >>= 1) sdot += __shfl_xor(sdot, off, 64);
+          if (lane == 0) sm.red[cq] = sdot;
+        }
+        float x[16];
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * rb + crow(i, hg);
+          x[i] = kt1[i] * t.dec[row] * (float)t.k[row][n0];
+        }
+        float xb[16], xc[16];
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * rb + crow(i, hg);
+          xb[i] = (float)t.k[row][n0] * r1[i];
+          xc[i] = (float)t.q[row][n0] * q1[i];
+        }
+        int idx;
+        const float sx = row_sum16(x, c, idx);
+        const float sb = row_sum16(xb, c, idx);
+        const float sc = row_sum16(xc, c, idx);
+        if ((c & 1) == 0) {
+          const int row = 32 * rb + crow(idx, hg);
+          sm.rk[cq][row] = sx;
+          // this wave wrote sm.xr[cq][row] in the first phase (same lane, same row)
+          sm.xr[cq][row] -= t.eg[row] * sb;
+          sm.gr[cq][row] = -t.beta[row] * sb + scale * sc;
+        }
+      }
     }
   }
   __syncthreads();                                    // M, N and every partial are complete
